@@ -1,0 +1,339 @@
+/*
+ * gdn_oracle.c -- plain, sequential fp64 CPU oracle for the gated-delta-rule
+ * token mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * Every routine is the literal definition of the operation, evaluated one token
+ * at a time in IEEE double precision with libm.  There is no chunking, no
+ * blocking and no reordering beyond what the definition states, so each line
+ * can be checked against the mathematics by eye.
+ *
+ * Sources (cited by page title and section; the pages carry no equations for
+ * the rule itself, the equation below is the one the method is specified by):
+ *   - "Agnes-3.0-Flash" model card (ModelScope), Architecture table, row
+ *     "Delta-rule layers": 16 key heads / 48 value heads, head dim 128, causal
+ *     conv of kernel 4 in front, gated RMS-norm after, recurrent state in fp32.
+ *   - "Agnes-3.0-Flash Deep Dive: A 33B Hybrid-Attention Multimodal Model",
+ *     section "Attention Layer Details": the delta rule erases before it
+ *     writes, and a forget gate decays the state.
+ *   - Update rule:  S_t = S_{t-1} * a_t (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+ *                   o_t = scale * S_t q_t,  a_t = exp(g_t).
+ *     S is dv x dk (row index = value channel), so S k is a dv-vector.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   value head h reads key/query head h / (Hv/Hk) (contiguous groups);
+ *   conv: y_t = sum_i w[c][i] x_{t-3+i}, w[c][3] is the current token, history
+ *   before a sequence start comes from that sequence's conv state (oldest
+ *   first) or zeros; SiLU on every channel; L2 as y / sqrt(sum y^2 + eps) on
+ *   each q and k head; gated norm as (o / rms(o)) * w * silu(z).
+ *
+ * Parity pins: every exported routine here is pinned by the CPU tests against
+ * invariants, closed forms, a brute-force unrolled form, an independent chunked
+ * (WY) formulation, and library routines (torch conv1d / rms_norm in fp64).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_NOMEM (-2)
+
+int oracle_abi_version(void) { return 1; }
+
+/* ---------------------------------------------------------------------------
+ * Round a double to the nearest bfloat16 value, ties to even.
+ * bfloat16 has an 8-bit significand (7 stored + hidden), exponent range of
+ * binary32 (normal down to 2^-126, subnormal spacing 2^-133), max finite
+ * (2 - 2^-7) * 2^127.  Written from that definition with frexp/ldexp/nearbyint
+ * (nearbyint rounds half to even in the default rounding mode).
+ * ------------------------------------------------------------------------- */
+static double round_to_bf16(double x)
+{
+    if (!isfinite(x) || x == 0.0) return x;
+    double ax = fabs(x);
+    double r;
+    if (ax < ldexp(1.0, -126)) {
+        /* subnormal range: fixed spacing 2^-133 */
+        r = ldexp(nearbyint(ldexp(ax, 133)), -133);
+    } else {
+        int e;
+        double m = frexp(ax, &e);              /* ax = m * 2^e, m in [0.5, 1) */
+        r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+        double maxf = ldexp(2.0 - ldexp(1.0, -7), 127);
+        if (r > maxf) r = INFINITY;
+    }
+    return x < 0 ? -r : r;
+}
+
+double oracle_round_bf16(double x) { return round_to_bf16(x); }
+
+void oracle_round_bf16_array(const double* x, double* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = round_to_bf16(x[i]);
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+static double silu(double x) { return x * sigmoid(x); }
+
+/* Sequence bounds: explicit cu_seqlens, or n_seqs equal pieces of T_total. */
+static int seq_bounds(const int32_t* cu, int32_t n_seqs, int32_t T_total, int32_t n,
+                      int64_t* start, int64_t* end)
+{
+    if (cu) {
+        *start = cu[n];
+        *end = cu[n + 1];
+    } else {
+        if (n_seqs <= 0 || T_total % n_seqs) return ORACLE_ERR_ARG;
+        int64_t len = T_total / n_seqs;
+        *start = (int64_t)n * len;
+        *end = *start + len;
+    }
+    if (*start < 0 || *end < *start || *end > T_total) return ORACLE_ERR_ARG;
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * One token of the rule on one value head, in place on S (dv x dk, row-major):
+ *   a = exp(g);  S <- a S;  p = S k;  u = beta (v - p);  S <- S + u k^T;
+ *   o = scale * S q.
+ * Expanding: S_new = a S (I - beta k k^T) + beta v k^T, i.e. decay first, the
+ * erase uses the decayed state, and the output reads the updated state.
+ * ------------------------------------------------------------------------- */
+static void rule_step(double* S, const double* kk, const double* qq, const double* vv,
+                      double g, double beta, double* o_out, int32_t dk, int32_t dv,
+                      double scale)
+{
+    double a = exp(g);
+    for (int64_t i = 0; i < (int64_t)dv * dk; ++i) S[i] *= a;
+    for (int32_t i = 0; i < dv; ++i) {
+        double* row = S + (int64_t)i * dk;
+        double p = 0.0;
+        for (int32_t j = 0; j < dk; ++j) p += row[j] * kk[j];
+        double u = beta * (vv[i] - p);
+        for (int32_t j = 0; j < dk; ++j) row[j] += u * kk[j];
+    }
+    if (o_out) {
+        for (int32_t i = 0; i < dv; ++i) {
+            const double* row = S + (int64_t)i * dk;
+            double acc = 0.0;
+            for (int32_t j = 0; j < dk; ++j) acc += row[j] * qq[j];
+            o_out[i] = scale * acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Sequential recurrence over packed sequences.
+ *   q, k : [T_total, Hk, dk]      v : [T_total, Hv, dv]
+ *   g, beta : [T_total, Hv]       o : [T_total, Hv, dv]
+ *   h0 (nullable -> zeros), hT (nullable) : [n_seqs, Hv, dv, dk]
+ *   cu_seqlens : [n_seqs + 1] (nullable -> n_seqs equal lengths)
+ * Parallel over independent (sequence, value head) pairs only.
+ * ------------------------------------------------------------------------- */
+int oracle_gdn_recurrence(const double* q, const double* k, const double* v,
+                          const double* g, const double* beta,
+                          const double* h0, double* o, double* hT,
+                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                          int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                          double scale, int32_t n_threads)
+{
+    if (!q || !k || !v || !g || !beta || !o) return ORACLE_ERR_ARG;
+    if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk || dk <= 0 || dv <= 0)
+        return ORACLE_ERR_ARG;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        int64_t s0, s1;
+        if (seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1)) return ORACLE_ERR_ARG;
+    }
+    const int32_t group = Hv / Hk;
+    const int64_t units = (int64_t)n_seqs * Hv;
+    int err = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int32_t n = (int32_t)(unit / Hv);
+        const int32_t h = (int32_t)(unit % Hv);
+        const int32_t kh = h / group;
+        int64_t s0, s1;
+        seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1);
+        const int64_t ssz = (int64_t)dv * dk;
+        double* S = (double*)malloc(sizeof(double) * ssz);
+        if (!S) { err = ORACLE_ERR_NOMEM; continue; }
+        if (h0) memcpy(S, h0 + ((int64_t)n * Hv + h) * ssz, sizeof(double) * ssz);
+        else memset(S, 0, sizeof(double) * ssz);
+        for (int64_t t = s0; t < s1; ++t) {
+            rule_step(S, k + (t * Hk + kh) * dk, q + (t * Hk + kh) * dk,
+                      v + (t * Hv + h) * dv, g[t * Hv + h], beta[t * Hv + h],
+                      o + (t * Hv + h) * dv, dk, dv, scale);
+        }
+        if (hT) memcpy(hT + ((int64_t)n * Hv + h) * ssz, S, sizeof(double) * ssz);
+        free(S);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Decode: one token per sequence, state updated in place.
+ *   q, k : [N, Hk, dk]  v : [N, Hv, dv]  g, beta : [N, Hv]  o : [N, Hv, dv]
+ *   state : [n_slots, Hv, dv, dk]; sequence n uses slot state_slot[n]
+ *   (state_slot nullable -> slot n).
+ * ------------------------------------------------------------------------- */
+int oracle_gdn_decode(const double* q, const double* k, const double* v,
+                      const double* g, const double* beta, double* state,
+                      const int32_t* state_slot, int32_t n_slots, double* o,
+                      int32_t N, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                      double scale, int32_t n_threads)
+{
+    if (!q || !k || !v || !g || !beta || !state || !o) return ORACLE_ERR_ARG;
+    if (N < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk || dk <= 0 || dv <= 0) return ORACLE_ERR_ARG;
+    for (int32_t n = 0; n < N; ++n) {
+        int32_t slot = state_slot ? state_slot[n] : n;
+        if (slot < 0 || slot >= n_slots) return ORACLE_ERR_ARG;
+    }
+    const int32_t group = Hv / Hk;
+    const int64_t ssz = (int64_t)dv * dk;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t unit = 0; unit < (int64_t)N * Hv; ++unit) {
+        const int32_t n = (int32_t)(unit / Hv);
+        const int32_t h = (int32_t)(unit % Hv);
+        const int32_t kh = h / group;
+        const int32_t slot = state_slot ? state_slot[n] : n;
+        rule_step(state + ((int64_t)slot * Hv + h) * ssz,
+                  k + ((int64_t)n * Hk + kh) * dk, q + ((int64_t)n * Hk + kh) * dk,
+                  v + ((int64_t)n * Hv + h) * dv, g[(int64_t)n * Hv + h],
+                  beta[(int64_t)n * Hv + h], o + ((int64_t)n * Hv + h) * dv, dk, dv,
+                  scale);
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Causal depthwise conv (kernel 4) + SiLU + per-head L2 of the q/k channels.
+ *   x : [T_total, C]  w : [C, 4] (w[c][3] multiplies the current token)
+ *   bias : [C] nullable
+ *   conv_state_in : [n_seqs, C, 3] nullable (zeros), oldest first: it holds
+ *                   the three inputs that precede the sequence.
+ *   y : [T_total, C]
+ *   conv_state_out : [n_seqs, C, 3] nullable: the last three inputs of the
+ *                   sequence's history (state_in followed by the sequence).
+ *   Channels [0, n_l2_heads * head_dim) are L2-normalised per head of
+ *   head_dim channels: y <- y / sqrt(sum y^2 + eps).
+ *   stage_bf16 != 0 rounds every y to bf16 (the stored dtype); 0 keeps fp64.
+ * ------------------------------------------------------------------------- */
+int oracle_conv1d(const double* x, const double* w, const double* bias,
+                  const double* conv_state_in, double* y, double* conv_state_out,
+                  const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t C,
+                  int32_t n_l2_heads, int32_t head_dim, double l2_eps, int32_t stage_bf16,
+                  int32_t n_threads)
+{
+    const int K = 4;
+    if (!x || !w || !y || n_seqs < 0 || T_total < 0 || C <= 0 || n_l2_heads < 0 ||
+        head_dim <= 0 || (int64_t)n_l2_heads * head_dim > C)
+        return ORACLE_ERR_ARG;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        int64_t s0, s1;
+        if (seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1)) return ORACLE_ERR_ARG;
+    }
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        int64_t s0, s1;
+        seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1);
+        const int64_t len = s1 - s0;
+        /* conv + bias + SiLU on every channel */
+        for (int64_t t = s0; t < s1; ++t) {
+            for (int32_t c = 0; c < C; ++c) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i) {
+                    int64_t pos = t - (K - 1) + i;   /* absolute position */
+                    double xv;
+                    if (pos >= s0) xv = x[pos * C + c];
+                    else {
+                        int64_t back = s0 - pos;     /* 1..3 steps before the start */
+                        xv = conv_state_in
+                                 ? conv_state_in[((int64_t)n * C + c) * (K - 1) + (K - 1) - back]
+                                 : 0.0;
+                    }
+                    acc += w[(int64_t)c * K + i] * xv;
+                }
+                if (bias) acc += bias[c];
+                y[t * C + c] = silu(acc);
+            }
+            /* L2 over each q/k head */
+            for (int32_t hh = 0; hh < n_l2_heads; ++hh) {
+                double* yh = y + t * C + (int64_t)hh * head_dim;
+                double ss = 0.0;
+                for (int32_t j = 0; j < head_dim; ++j) ss += yh[j] * yh[j];
+                double inv = 1.0 / sqrt(ss + l2_eps);
+                for (int32_t j = 0; j < head_dim; ++j) yh[j] *= inv;
+            }
+            if (stage_bf16)
+                for (int32_t c = 0; c < C; ++c) y[t * C + c] = round_to_bf16(y[t * C + c]);
+        }
+        /* new conv state: last K-1 entries of (state_in ++ x[s0:s1]) */
+        if (conv_state_out) {
+            for (int32_t c = 0; c < C; ++c) {
+                double hist[3];
+                for (int i = 0; i < K - 1; ++i) {
+                    /* position relative to sequence end: len-3+i */
+                    int64_t rel = len - (K - 1) + i;
+                    if (rel >= 0) hist[i] = x[(s0 + rel) * C + c];
+                    else {
+                        int64_t back = -rel; /* 1..3 steps before the start */
+                        hist[i] = conv_state_in
+                                      ? conv_state_in[((int64_t)n * C + c) * (K - 1) + (K - 1) - back]
+                                      : 0.0;
+                    }
+                }
+                for (int i = 0; i < K - 1; ++i)
+                    conv_state_out[((int64_t)n * C + c) * (K - 1) + i] = hist[i];
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Gated RMSNorm per (row, value head):
+ *   r = sqrt(mean_i o_i^2 + eps);  out_i = (o_i / r) * w_i * z_i * sigmoid(z_i)
+ *   o, z, out : [rows, Hv, dv]   w : [dv] shared by all heads.
+ *   stage_bf16 != 0 rounds out to bf16.
+ * ------------------------------------------------------------------------- */
+int oracle_gated_rmsnorm(const double* o, const double* z, const double* w, double* out,
+                         int64_t rows, int32_t Hv, int32_t dv, double eps, int32_t stage_bf16,
+                         int32_t n_threads)
+{
+    if (!o || !z || !w || !out || rows < 0 || Hv <= 0 || dv <= 0) return ORACLE_ERR_ARG;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows * Hv; ++r) {
+        const double* oo = o + r * dv;
+        const double* zz = z + r * dv;
+        double* dst = out + r * dv;
+        double ss = 0.0;
+        for (int32_t i = 0; i < dv; ++i) ss += oo[i] * oo[i];
+        double rms = sqrt(ss / dv + eps);
+        for (int32_t i = 0; i < dv; ++i) {
+            double val = (oo[i] / rms) * w[i] * silu(zz[i]);
+            dst[i] = stage_bf16 ? round_to_bf16(val) : val;
+        }
+    }
+    return ORACLE_OK;
+}
