@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule mixer on one MI355X.
+
+Headline (the JSON `value`): chunked prefill throughput at T = 65,536 tokens,
+B = 1, 16 key heads / 48 value heads, head dim 128, random fp32 initial state,
+fp32 outputs and final state -- one `gdn_chunk_fwd` launch per step, inputs
+resident in HBM.  The same run also times, as extra legs in the same JSON line:
+  decode  one batched decode step, 256 sequences, fp32 state [256,48,128,128]
+          updated in place (state GB/s), plus the batch-mode conv-state update;
+  mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
+          RMSNorm;
+  varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
+`roofline` covers the prefill kernel: algorithmic bytes per launch over the
+launch duration measured with HIP events on the launch stream, against the
+8 TB/s HBM3E peak (the kernel's arithmetic intensity, ~136 flop/B, is below the
+MFMA ridge); `mfma` gives the same launch against the 2.5 PFLOP/s dense fp16/bf16
+MFMA peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded prefix of the
+same prefill input on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,...]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s @T=64K (% MFMA peak); decode-step state GB/s (% HBM)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0          # dense fp16 / bf16 MFMA, MI355X
+HK, HV, D, C = 16, 48, 128, 64
+# algorithmic work per token of the chunked rule (chunk 64): Gram products per
+# key head + (W, U~, intra-chunk O: 3 dv (C+1)) + (K S0^T, Q S0^T, S update: 6 dk dv)
+# per value head
+FLOP_PER_TOKEN = HK * 2 * D * C + HV * (3 * D * (C + 1) + 6 * D * D)      # 6,178,816
+# bytes per token: q, k, v bf16; g, beta fp32; o fp32
+BYTES_PER_TOKEN = HK * D * 2 * 2 + HV * D * 2 + HV * 4 * 2 + HV * D * 4   # 45,440
+STATE_BYTES = HV * D * D * 4                                              # 3,145,728
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_leg(fn, steps, warmup):
+    """Run fn `warmup` times, then `steps` times bracketed by HIP events on the
+    current stream.  Returns (mean event ms, wall ms per step)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sum(s.elapsed_time(e) for s, e in evs) / steps
+    return ev, wall
+
+
+def leg_prefill(args, ops, synth, torch):
+    T = 65536
+    log(f"[prefill] drawing inputs T={T}")
+    ci = synth.chunk_inputs_torch(1002, T, h0_std=0.02)
+    q, k, v, g, b, h0 = ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], ci["h0"]
+    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    fs = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0, final_state=fs, o=o, n_seqs=1)
+
+    ev, wall = time_leg(step, args.steps, args.warmup)
+    bytes_launch = T * BYTES_PER_TOKEN + 2 * STATE_BYTES
+    flops_launch = T * FLOP_PER_TOKEN
+    res = dict(tokens=T, event_ms=ev, wall_ms=wall, tokens_per_s=T / (wall * 1e-3),
+               alg_bytes=bytes_launch, alg_flops=flops_launch,
+               hbm_gbps=bytes_launch / (ev * 1e-3) / 1e9,
+               mfma_tflops=flops_launch / (ev * 1e-3) / 1e12)
+    log(f"[prefill] {ev:.3f} ms/launch, {res['tokens_per_s'] / 1e6:.2f} M tok/s, "
+        f"{res['hbm_gbps']:.0f} GB/s alg, {res['mfma_tflops']:.1f} TFLOP/s alg")
+    return res, ci
+
+
+def leg_decode(args, ops, synth, torch):
+    N = 256
+    log(f"[decode] drawing inputs N={N}")
+    di = synth.decode_inputs_torch(1003, N)
+    o = torch.empty((N, HV, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.gdn_decode_step(di["q"], di["k"], di["v"], di["g"], di["beta"], di["state"], o=o)
+
+    ev, wall = time_leg(step, args.steps, args.warmup)
+    sbytes = 2 * N * STATE_BYTES
+    y = torch.empty((N, HK * 2 * D + HV * D), dtype=torch.bfloat16, device="cuda")
+
+    def conv_step():
+        ops.gdn_conv1d_fwd(di["x"], di["conv_w"], y=y, conv_state=di["conv_state"], n_seqs=N,
+                           n_l2_heads=2 * HK)
+
+    cev, cwall = time_leg(conv_step, args.steps, args.warmup)
+    cbytes = N * y.shape[1] * 2 * 2 + N * y.shape[1] * 3 * 2 * 2 + y.shape[1] * 4 * 2
+    res = dict(n_seqs=N, event_ms=ev, wall_ms=wall, state_bytes=sbytes,
+               state_gbps=sbytes / (ev * 1e-3) / 1e9,
+               frac_hbm=sbytes / (ev * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               conv_event_ms=cev, conv_alg_bytes=cbytes, conv_gbps=cbytes / (cev * 1e-3) / 1e9)
+    log(f"[decode] {ev:.3f} ms/step, state {res['state_gbps']:.0f} GB/s "
+        f"({100 * res['frac_hbm']:.1f}% of HBM); conv update {cev * 1e3:.1f} us")
+    return res
+
+
+def leg_mixer(args, ops, synth, torch):
+    T = 8192
+    log(f"[mixer] drawing inputs T={T}")
+    mi = synth.mixer_inputs_torch(1001, T)
+    y = torch.empty((T, (2 * HK + HV) * D), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    fs = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
+    yv = y.view(T, 2 * HK + HV, D)
+
+    def step():
+        ops.gdn_conv1d_fwd(mi["x"], mi["conv_w"], y=y, n_seqs=1, n_l2_heads=2 * HK)
+        ops.gdn_chunk_fwd(yv[:, :HK], yv[:, HK:2 * HK], yv[:, 2 * HK:], mi["g"], mi["beta"],
+                          final_state=fs, o=o, n_seqs=1)
+        ops.gdn_gated_rmsnorm(o, mi["z"], mi["norm_w"], out=out)
+
+    ev, wall = time_leg(step, args.steps, args.warmup)
+    res = dict(tokens=T, event_ms=ev, wall_ms=wall, tokens_per_s=T / (wall * 1e-3))
+    log(f"[mixer] {ev:.3f} ms/step, {res['tokens_per_s'] / 1e6:.2f} M tok/s")
+    return res
+
+
+def leg_varlen(args, ops, synth, torch):
+    lens = synth.varlen_lengths(1004)
+    T = int(lens.sum())
+    log(f"[varlen] drawing inputs T={T} N={len(lens)}")
+    ci = synth.chunk_inputs_torch(1004, T, lengths=lens, h0_std=0.02)
+    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    fs = torch.empty((len(lens), HV, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_bytes(len(lens), T, HK, HV), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], initial_state=ci["h0"],
+                          final_state=fs, o=o, cu_seqlens=ci["cu_seqlens"], workspace=ws)
+
+    ev, wall = time_leg(step, max(2, args.steps // 2), max(1, args.warmup // 2))
+    bytes_launch = T * BYTES_PER_TOKEN + 2 * len(lens) * STATE_BYTES
+    res = dict(tokens=T, n_seqs=len(lens), event_ms=ev, wall_ms=wall,
+               tokens_per_s=T / (wall * 1e-3), hbm_gbps=bytes_launch / (ev * 1e-3) / 1e9,
+               mfma_tflops=T * FLOP_PER_TOKEN / (ev * 1e-3) / 1e12)
+    log(f"[varlen] {ev:.3f} ms/launch, {res['tokens_per_s'] / 1e6:.2f} M tok/s")
+    return res
+
+
+def cpu_baseline(ci, seconds, torch):
+    """The fp64 oracle on a prefix of the prefill input, all 48 heads."""
+    import numpy as np
+    import oracle
+
+    def host_bf16(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    threads = len(os.sched_getaffinity(0))
+    q, k, v = host_bf16(ci["q"]), host_bf16(ci["k"]), host_bf16(ci["v"])
+    g, b = ci["g"].cpu().numpy(), ci["beta"].cpu().numpy()
+    h0 = ci["h0"].cpu().numpy()
+    # calibrate on 256 tokens, then size the sample for ~`seconds` of work
+    t0 = time.perf_counter()
+    oracle.recurrence(q[:256], k[:256], v[:256], g[:256], b[:256], h0, n_threads=threads)
+    rate = 256 / (time.perf_counter() - t0)
+    Ts = int(min(q.shape[0], max(512, rate * seconds)))
+    Ts -= Ts % 64
+    log(f"[cpu] oracle on {Ts} tokens x {HV} heads, {threads} threads")
+    t0 = time.perf_counter()
+    oracle.recurrence(q[:Ts], k[:Ts], v[:Ts], g[:Ts], b[:Ts], h0, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {Ts} tokens of the T=65536 prefill input, all 48 value heads, "
+                      f"fp64 sequential recurrence, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="prefill,decode,mixer,varlen")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the mixer shards by heads or sequences with no "
+              "exchange, and this build runs and reports a single MI355X (--gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_09_amd import ops, synth
+    torch.cuda.set_device(0)
+    ops.lib()
+    legs = args.legs.split(",")
+    out = {}
+    ci = None
+    if "prefill" in legs:
+        out["prefill"], ci = leg_prefill(args, ops, synth, torch)
+    if "decode" in legs:
+        out["decode"] = leg_decode(args, ops, synth, torch)
+    if "mixer" in legs:
+        out["mixer"] = leg_mixer(args, ops, synth, torch)
+    if "varlen" in legs:
+        out["varlen"] = leg_varlen(args, ops, synth, torch)
+
+    pre = out.get("prefill")
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"] if pre else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["wall_ms"] if pre else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA operands, f32 accumulate, f32 state",
+        "data": "synthetic",
+        "config": {"workload": "chunked prefill B=1 T=65536 Hk=16 Hv=48 d=128, fp32 S0, "
+                               "fp32 o + final state", "tokens": 65536, "chunk": C,
+                   "parallelism": "single GPU"},
+    }
+    if pre:
+        line["roofline"] = {"bound": "hbm", "achieved": round(pre["hbm_gbps"], 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(pre["hbm_gbps"] / HBM_PEAK_GBPS, 4),
+                            "traffic": None, "kernel": "chunk_fwd_kernel",
+                            "launch_ms": round(pre["event_ms"], 4)}
+        line["mfma"] = {"achieved": round(pre["mfma_tflops"], 1), "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(pre["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+    if "decode" in out:
+        d = out["decode"]
+        line["decode"] = {"state_GBps": round(d["state_gbps"], 1),
+                          "frac_hbm": round(d["frac_hbm"], 4),
+                          "launch_ms": round(d["event_ms"], 4),
+                          "conv_update_ms": round(d["conv_event_ms"], 4)}
+    if "mixer" in out:
+        line["mixer_T8192"] = {"tokens_per_s": round(out["mixer"]["tokens_per_s"], 1),
+                               "ms": round(out["mixer"]["event_ms"], 4)}
+    if "varlen" in out:
+        vl = out["varlen"]
+        line["varlen_262144x24"] = {"tokens_per_s": round(vl["tokens_per_s"], 1),
+                                    "ms": round(vl["event_ms"], 4),
+                                    "hbm_frac": round(vl["hbm_gbps"] / HBM_PEAK_GBPS, 4),
+                                    "mfma_frac": round(vl["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+    if ci is not None and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

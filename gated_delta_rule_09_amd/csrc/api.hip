@@ -1,0 +1,323 @@
+// api.hip -- the C ABI of libgdn (include/gdn.h): argument validation, then
+// kernel launches on the caller's stream.  Every argument check runs on the
+// host before any HIP call, so invalid calls return without touching the
+// device (and can be exercised without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gdn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return GDN_OK;
+  return fail(GDN_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range [lo, hi) of a tensor with `rows` rows of `width` elements at a
+// row stride of `stride` elements.
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+};
+Range range_of(const void* p, int64_t rows, int64_t stride, int64_t width, size_t elem) {
+  Range r;
+  if (!p || rows <= 0 || width <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + static_cast<uintptr_t>(((rows - 1) * stride + width) * static_cast<int64_t>(elem));
+  return r;
+}
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool env_validate_seqlens() {
+  const char* v = std::getenv("GDN_VALIDATE_CU_SEQLENS");
+  return v && v[0] == '1';
+}
+
+// Sequence-count / length consistency when cu_seqlens is absent.
+gdn_status check_equal_split(int32_t n_seqs, int32_t T_total) {
+  if (n_seqs < 0 || T_total < 0) return fail(GDN_ERR_SHAPE, "negative n_seqs or T_total");
+  if (n_seqs == 0 && T_total != 0) return fail(GDN_ERR_SHAPE, "T_total > 0 with no sequences");
+  if (n_seqs > 0 && T_total % n_seqs != 0)
+    return fail(GDN_ERR_SHAPE, "T_total %d not divisible by n_seqs %d without cu_seqlens",
+                T_total, n_seqs);
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    case GDN_ERR_SEQLENS: return "GDN_ERR_SEQLENS";
+    default: return "GDN_ERR_UNKNOWN";
+  }
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                   void* stream) {
+  if (!cu_seqlens) return fail(GDN_ERR_NULL, "cu_seqlens is NULL");
+  if (n_seqs < 0 || T_total < 0) return fail(GDN_ERR_SHAPE, "negative n_seqs or T_total");
+  std::vector<int32_t> h(static_cast<size_t>(n_seqs) + 1);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn_status s = hip_status(hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t),
+                                           hipMemcpyDeviceToHost, st),
+                            "gdn_validate_cu_seqlens copy");
+  if (s) return s;
+  s = hip_status(hipStreamSynchronize(st), "gdn_validate_cu_seqlens sync");
+  if (s) return s;
+  if (h[0] != 0) return fail(GDN_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", h[0]);
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (h[i + 1] < h[i])
+      return fail(GDN_ERR_SEQLENS, "cu_seqlens decreases at %d (%d -> %d)", i, h[i], h[i + 1]);
+  if (h[n_seqs] != T_total)
+    return fail(GDN_ERR_SEQLENS, "cu_seqlens[%d] = %d, expected T_total %d", n_seqs, h[n_seqs],
+                T_total);
+  return GDN_OK;
+}
+
+gdn_status gdn_conv1d_fwd(const uint16_t* x, int64_t x_row_stride, const uint16_t* w,
+                          const float* bias, uint16_t* y, int64_t y_row_stride,
+                          uint16_t* conv_state, const int32_t* cu_seqlens, int32_t n_seqs,
+                          int32_t T_total, int32_t C, int32_t n_l2_heads, int32_t head_dim,
+                          float l2_eps, void* stream) {
+  if (T_total > 0 && (!x || !w || !y))
+    return fail(GDN_ERR_NULL, "gdn_conv1d_fwd: x, w and y are required");
+  if (n_seqs < 0 || T_total < 0 || C <= 0 || n_l2_heads < 0)
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: bad sizes");
+  if (head_dim != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_conv1d_fwd: head_dim must be 128");
+  if (C % 8) return fail(GDN_ERR_UNSUPPORTED, "gdn_conv1d_fwd: C must be a multiple of 8");
+  if (static_cast<int64_t>(n_l2_heads) * head_dim > C)
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: n_l2_heads * head_dim > C");
+  if (x_row_stride < C || y_row_stride < C || x_row_stride % 8 || y_row_stride % 8)
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: row strides must be >= C and multiples of 8");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) || !aligned(conv_state, 16) ||
+      !aligned(bias, 4) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: x, y, w, conv_state must be 16-byte aligned");
+  if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps))
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: l2_eps must be finite and >= 0");
+  if (!cu_seqlens) {
+    const gdn_status s = check_equal_split(n_seqs, T_total);
+    if (s) return s;
+  } else if (n_seqs == 0 && T_total != 0) {
+    return fail(GDN_ERR_SHAPE, "gdn_conv1d_fwd: T_total > 0 with no sequences");
+  }
+  const Range rx = range_of(x, T_total, x_row_stride, C, 2);
+  const Range ry = range_of(y, T_total, y_row_stride, C, 2);
+  const Range rs = range_of(conv_state, n_seqs, 3LL * C, 3LL * C, 2);
+  const Range rw = range_of(w, C, 4, 4, 2);
+  if (overlap(rx, ry) || overlap(ry, rs) || overlap(rx, rs) || overlap(rw, ry) || overlap(rw, rs))
+    return fail(GDN_ERR_ALIAS, "gdn_conv1d_fwd: x, y, w and conv_state must not overlap");
+  if (cu_seqlens && env_validate_seqlens()) {
+    const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (s) return s;
+  }
+  return hip_status(gdn::launch_conv1d(x, x_row_stride, w, bias, y, y_row_stride, conv_state,
+                                       cu_seqlens, n_seqs, T_total, C, n_l2_heads * head_dim,
+                                       l2_eps, static_cast<hipStream_t>(stream)),
+                    "gdn_conv1d_fwd launch");
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
+                                     int32_t d) {
+  (void)Hk;
+  (void)Hv;
+  (void)d;
+  if (n_seqs < 0 || T_total < 0) return 0;
+  return gdn::chunk_workspace_layout(n_seqs, T_total).total;
+}
+
+gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                         int32_t* order, int32_t* chunk_off, int32_t* chunk_tab, void* stream) {
+  if (!cu_seqlens || !order || !chunk_off || !chunk_tab)
+    return fail(GDN_ERR_NULL, "gdn_chunk_map: all pointers are required");
+  if (n_seqs < 0 || T_total < 0) return fail(GDN_ERR_SHAPE, "gdn_chunk_map: bad sizes");
+  if (!aligned(cu_seqlens, 4) || !aligned(order, 4) || !aligned(chunk_off, 4) ||
+      !aligned(chunk_tab, 4))
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_map: arrays must be 4-byte aligned");
+  if (env_validate_seqlens()) {
+    const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (s) return s;
+  }
+  return hip_status(gdn::launch_chunk_map(cu_seqlens, n_seqs, T_total, order, chunk_off,
+                                          chunk_tab, static_cast<hipStream_t>(stream)),
+                    "gdn_chunk_map launch");
+}
+
+gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                         int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                         const float* g, const float* beta, float* o,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                         int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDN_ERR_NULL, "gdn_chunk_fwd: q, k, v, g, beta and o are required");
+  if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: bad sizes or Hv %% Hk != 0");
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_fwd: dk = dv = 128 only");
+  if (q_tok_stride < static_cast<int64_t>(Hk) * dk || k_tok_stride < static_cast<int64_t>(Hk) * dk ||
+      v_tok_stride < static_cast<int64_t>(Hv) * dv || q_tok_stride % 8 || k_tok_stride % 8 ||
+      v_tok_stride % 8)
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: token strides too small or not multiples of 8");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: q, k, v, o and states must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: scale must be finite");
+  if (!cu_seqlens) {
+    const gdn_status s = check_equal_split(n_seqs, T_total);
+    if (s) return s;
+  } else if (n_seqs == 0 && T_total != 0) {
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: T_total > 0 with no sequences");
+  }
+  // grid size: ceil(n_seqs * Hk / 8) * 8 * (Hv / Hk) * 2 blocks
+  if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: too many (sequence, head) pairs");
+  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total);
+  if (cu_seqlens) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace of %zu bytes needed", ws.total);
+    if (!aligned(workspace, 256))
+      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace must be 256-byte aligned");
+  }
+  const Range rq = range_of(q, T_total, q_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rk = range_of(k, T_total, k_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rv = range_of(v, T_total, v_tok_stride, static_cast<int64_t>(Hv) * dv, 2);
+  const Range rg = range_of(g, T_total, Hv, Hv, 4);
+  const Range rb = range_of(beta, T_total, Hv, Hv, 4);
+  const Range ro = range_of(o, T_total, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, 4);
+  const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
+  const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
+  const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
+  const Range rw = cu_seqlens ? range_of(workspace, 1, 0, static_cast<int64_t>(ws.total), 1) : Range{};
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &r0})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: o overlaps an input");
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro})
+    if (overlap(*in, rT)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: final_state overlaps o or an input");
+  if (overlap(r0, rT) && initial_state != final_state)
+    return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: final_state partially overlaps initial_state");
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro, &r0, &rT})
+    if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: workspace overlaps a tensor");
+  if (cu_seqlens && env_validate_seqlens()) {
+    const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (s) return s;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* order = nullptr;
+  if (cu_seqlens) {
+    order = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + ws.order_off);
+    const gdn_status s = hip_status(gdn::launch_chunk_order(cu_seqlens, n_seqs, order, st),
+                                    "gdn_chunk_fwd schedule launch");
+    if (s) return s;
+  }
+  return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g,
+                                          beta, o, initial_state, final_state, cu_seqlens, order,
+                                          n_seqs, T_total, Hk, Hv, scale, st),
+                    "gdn_chunk_fwd launch");
+}
+
+gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                           int64_t k_stride, const uint16_t* v, int64_t v_stride, const float* g,
+                           const float* beta, float* state, const int32_t* state_slot,
+                           int32_t n_slots, float* o, int32_t n_seqs, int32_t Hk, int32_t Hv,
+                           int32_t dk, int32_t dv, float scale, void* stream) {
+  if (n_seqs > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+    return fail(GDN_ERR_NULL, "gdn_decode_step: q, k, v, g, beta, state and o are required");
+  if (n_seqs < 0 || n_slots < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_step: bad sizes or Hv %% Hk != 0");
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_step: dk = dv = 128 only");
+  if (!state_slot && n_slots < n_seqs)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_step: n_slots < n_seqs without a slot map");
+  if (q_stride < static_cast<int64_t>(Hk) * dk || k_stride < static_cast<int64_t>(Hk) * dk ||
+      v_stride < static_cast<int64_t>(Hv) * dv || q_stride % 8 || k_stride % 8 || v_stride % 8)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_step: strides too small or not multiples of 8");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) ||
+      !aligned(o, 4) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(state_slot, 4))
+    return fail(GDN_ERR_SHAPE, "gdn_decode_step: q, k, v and state must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "gdn_decode_step: scale must be finite");
+  if (static_cast<int64_t>(n_seqs) * Hv > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_step: too many (sequence, head) pairs");
+  const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
+  const Range rs = range_of(state, n_slots, ssz, ssz, 4);
+  const Range ro = range_of(o, n_seqs, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, 4);
+  const Range rq = range_of(q, n_seqs, q_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rk = range_of(k, n_seqs, k_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rv = range_of(v, n_seqs, v_stride, static_cast<int64_t>(Hv) * dv, 2);
+  const Range rg = range_of(g, n_seqs, Hv, Hv, 4);
+  const Range rb = range_of(beta, n_seqs, Hv, Hv, 4);
+  const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl, &rs})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_decode_step: o overlaps an input or the state");
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl})
+    if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_step: state overlaps an input");
+  return hip_status(gdn::launch_decode_step(q, q_stride, k, k_stride, v, v_stride, g, beta, state,
+                                            state_slot, o, n_seqs, Hk, Hv, scale,
+                                            static_cast<hipStream_t>(stream)),
+                    "gdn_decode_step launch");
+}
+
+gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
+                             const float* w, void* out, int32_t out_is_bf16, int64_t rows,
+                             int32_t Hv, int32_t dv, float eps, void* stream) {
+  if (rows > 0 && (!o || !z || !w || !out))
+    return fail(GDN_ERR_NULL, "gdn_gated_rmsnorm: all pointers are required");
+  if (rows < 0 || Hv <= 0) return fail(GDN_ERR_SHAPE, "gdn_gated_rmsnorm: bad sizes");
+  if (dv != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_gated_rmsnorm: dv must be 128");
+  if (z_row_stride < static_cast<int64_t>(Hv) * dv || z_row_stride % 8)
+    return fail(GDN_ERR_SHAPE, "gdn_gated_rmsnorm: z row stride too small or not a multiple of 8");
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(out, 16))
+    return fail(GDN_ERR_SHAPE, "gdn_gated_rmsnorm: pointers must be 16-byte aligned");
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(GDN_ERR_SHAPE, "gdn_gated_rmsnorm: eps must be finite and >= 0");
+  const int64_t width = static_cast<int64_t>(Hv) * dv;
+  const Range ro = range_of(o, rows, width, width, 4);
+  const Range rz = range_of(z, rows, z_row_stride, width, 2);
+  const Range rw = range_of(w, 1, dv, dv, 4);
+  const Range rout = range_of(out, rows, width, width, out_is_bf16 ? 2 : 4);
+  if (overlap(rout, rz) || overlap(rout, rw))
+    return fail(GDN_ERR_ALIAS, "gdn_gated_rmsnorm: out overlaps z or w");
+  if (overlap(rout, ro) && !(static_cast<const void*>(o) == out && !out_is_bf16))
+    return fail(GDN_ERR_ALIAS, "gdn_gated_rmsnorm: out may alias o only exactly and in fp32");
+  return hip_status(gdn::launch_gated_rmsnorm(o, z, z_row_stride, w, out, out_is_bf16 != 0, rows,
+                                              Hv, eps, static_cast<hipStream_t>(stream)),
+                    "gdn_gated_rmsnorm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// decode.hip -- one-token step of the gated delta rule with the fp32 state
+// updated in place.
+//
+// Per (sequence n, value head h), with a = exp(g), b = beta and S the 128x128
+// fp32 state (row i = value channel):
+//     S <- a S + b (v - a S k) k^T,      o = scale * S q
+// Row i of the new state is a*S_i + u_i k^T with u_i = b (v_i - a S_i.k), and
+// o_i = scale * (a S_i.q + u_i (k.q)), so both dot products come from the OLD
+// row and the state is read once and written once (the rule of the
+// "Delta-rule layers" row of the model card's Architecture table, T = 1).
+//
+// Mapping: one 256-thread work-group per (n, h).  Eight consecutive lanes share
+// a state row; lane p of the eight holds the float4 columns p, p+8, p+16, p+24
+// of that row, so every wave-wide load reads eight whole 128-byte row pieces.
+// Thread t owns rows t/8 + {0, 32, 64, 96}.  Row dot products are reduced
+// inside the 8-lane group with DPP.
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kD = 128;
+
+template <bool kSlots>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
+    int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    const int32_t* __restrict__ slots, float* __restrict__ o, int Hk, int Hv, float scale) {
+  const int n = blockIdx.x / Hv;
+  const int h = blockIdx.x - n * Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int p = tid & 7;
+  const int rg = tid >> 3;
+  const int slot = kSlots ? slots[n] : n;
+  float* S = state + (static_cast<int64_t>(slot) * Hv + h) * (kD * kD);
+
+  // Stream the four rows first so 256 bytes per thread are in flight.
+  floatx4 s[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s[r][j] = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(S + (rg + 32 * r) * kD + 4 * (p + 8 * j)));
+
+  const uint16_t* kp = k + n * k_stride + kh * kD;
+  const uint16_t* qp = q + n * q_stride + kh * kD;
+  float kk[16], qq[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint2 kb = *reinterpret_cast<const uint2*>(kp + 4 * (p + 8 * j));
+    const uint2 qb = *reinterpret_cast<const uint2*>(qp + 4 * (p + 8 * j));
+    kk[4 * j + 0] = __uint_as_float(kb.x << 16);
+    kk[4 * j + 1] = __uint_as_float(kb.x & 0xffff0000u);
+    kk[4 * j + 2] = __uint_as_float(kb.y << 16);
+    kk[4 * j + 3] = __uint_as_float(kb.y & 0xffff0000u);
+    qq[4 * j + 0] = __uint_as_float(qb.x << 16);
+    qq[4 * j + 1] = __uint_as_float(qb.x & 0xffff0000u);
+    qq[4 * j + 2] = __uint_as_float(qb.y << 16);
+    qq[4 * j + 3] = __uint_as_float(qb.y & 0xffff0000u);
+  }
+  float kq = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kq += kk[j] * qq[j];
+  kq = sum8(kq);
+
+  const float a = expf(g[static_cast<int64_t>(n) * Hv + h]);
+  const float b = beta[static_cast<int64_t>(n) * Hv + h];
+  const uint16_t* vp = v + n * v_stride + h * kD;
+  float* op = o + (static_cast<int64_t>(n) * Hv + h) * kD;
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = rg + 32 * r;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sk += s[r][j][0] * kk[4 * j] + s[r][j][1] * kk[4 * j + 1] + s[r][j][2] * kk[4 * j + 2] +
+            s[r][j][3] * kk[4 * j + 3];
+      sq += s[r][j][0] * qq[4 * j] + s[r][j][1] * qq[4 * j + 1] + s[r][j][2] * qq[4 * j + 2] +
+            s[r][j][3] * qq[4 * j + 3];
+    }
+    sk = sum8(sk);
+    sq = sum8(sq);
+    const float vi = bf16_to_f32(vp[row]);
+    const float u = b * (vi - a * sk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      floatx4 t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = a * s[r][j][i] + u * kk[4 * j + i];
+      __builtin_nontemporal_store(t, reinterpret_cast<floatx4*>(S + row * kD + 4 * (p + 8 * j)));
+    }
+    if (p == 0) op[row] = scale * (a * sq + u * kq);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                              int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                              const float* g, const float* beta, float* state,
+                              const int32_t* state_slot, float* o, int n_seqs, int Hk, int Hv,
+                              float scale, hipStream_t stream) {
+  if (n_seqs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv));
+  if (state_slot)
+    hipLaunchKernelGGL(decode_step_kernel<true>, grid, dim3(256), 0, stream, q, q_stride, k,
+                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+  else
+    hipLaunchKernelGGL(decode_step_kernel<false>, grid, dim3(256), 0, stream, q, q_stride, k,
+                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

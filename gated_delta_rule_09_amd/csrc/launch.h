@@ -1,0 +1,45 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to libgdn).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                              int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                              const float* g, const float* beta, float* state,
+                              const int32_t* state_slot, float* o, int n_seqs, int Hk, int Hv,
+                              float scale, hipStream_t stream);
+
+hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const float* bias,
+                         uint16_t* y, int64_t ys, uint16_t* conv_state, const int32_t* cu,
+                         int n_seqs, int T_total, int C, int n_l2_channels, float l2_eps,
+                         hipStream_t stream);
+
+hipError_t launch_gated_rmsnorm(const float* o, const uint16_t* z, int64_t zs, const float* w,
+                                void* out, bool out_bf16, int64_t rows, int Hv, float eps,
+                                hipStream_t stream);
+
+// Workspace of the chunked prefill: the longest-first sequence order (int32).
+struct ChunkWorkspace {
+  size_t order_off, total;
+};
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total);
+
+hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
+                            int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream);
+
+hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
+                            const uint16_t* v, int64_t vs, const float* g, const float* beta,
+                            float* o, const float* h0, float* hT, const int32_t* cu,
+                            const int32_t* order, int n_seqs, int T_total, int Hk, int Hv,
+                            float scale, hipStream_t stream);
+
+// Longest-first sequence order only (the part of the chunk map the prefill
+// schedule needs).
+hipError_t launch_chunk_order(const int32_t* cu, int n_seqs, int32_t* order, hipStream_t stream);
+
+}  // namespace gdn

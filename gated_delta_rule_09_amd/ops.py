@@ -1,0 +1,265 @@
+"""Python binding of libgdn (include/gdn.h): argument marshalling only.
+
+Each function takes torch tensors on the GPU, checks dtype, device and layout,
+passes raw device pointers and the current HIP stream to the C ABI entry point
+of the same name, and raises GdnError on a non-zero status.  Every step of the
+computation runs in the HIP kernels; there is no CPU fallback, and a missing
+libgdn.so raises at the first call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
+
+_c = ctypes
+_vp, _i32, _i64, _f32, _sz = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_float, _c.c_size_t
+
+_SIGS = {
+    "gdn_status_string": (_c.c_char_p, [_i32]),
+    "gdn_last_error": (_c.c_char_p, []),
+    "gdn_abi_version": (_i32, []),
+    "gdn_conv1d_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
+                              _i32, _f32, _vp]),
+    "gdn_chunk_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "gdn_chunk_fwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
+                               _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
+    "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
+}
+
+_lib_handle = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so with prototypes set (raises if it is not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(hipcc, gfx950) first")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/gdn.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gdn_\w+)\s*\(", txt, re.M)))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        h = lib()
+        raise GdnError(status, where, f"{h.gdn_status_string(status).decode()}: "
+                                      f"{h.gdn_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, dims: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _inner_contig(t: torch.Tensor, name: str):
+    # all dims but the first contiguous (row stride free, multiple of 8)
+    exp = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.stride(d) != exp:
+            raise ValueError(f"{name}: inner dims must be contiguous")
+        exp *= t.shape[d]
+
+
+def gdn_conv1d_fwd(x: torch.Tensor, w: torch.Tensor, *, y: Optional[torch.Tensor] = None,
+                   bias: Optional[torch.Tensor] = None, conv_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                   n_l2_heads: int = 32, head_dim: int = 128, l2_eps: float = 1e-6) -> torch.Tensor:
+    """x [T, C] bf16, w [C, 4] bf16 -> y [T, C] bf16; conv_state [N, C, 3] updated in place."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    T, C = x.shape
+    _inner_contig(x, "x")
+    w = w.contiguous()
+    if y is None:
+        y = torch.empty((T, C), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, 2)
+    _inner_contig(y, "y")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+    if conv_state is not None:
+        _need(conv_state, "conv_state", torch.bfloat16, 3)
+        if not conv_state.is_contiguous():
+            raise ValueError("conv_state must be contiguous")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = conv_state.shape[0] if conv_state is not None else 1
+    st = lib().gdn_conv1d_fwd(_ptr(x), x.stride(0), _ptr(w), _ptr(bias), _ptr(y), y.stride(0),
+                              _ptr(conv_state), _ptr(cu_seqlens), n_seqs, T, C, n_l2_heads,
+                              head_dim, l2_eps, _stream())
+    _check(st, "gdn_conv1d_fwd")
+    return y
+
+
+def gdn_chunk_fwd_workspace_bytes(n_seqs: int, T_total: int, Hk: int, Hv: int, d: int = 128) -> int:
+    return int(lib().gdn_chunk_fwd_workspace_bytes(n_seqs, T_total, Hk, Hv, d))
+
+
+def gdn_chunk_map(cu_seqlens: torch.Tensor, T_total: int):
+    """(order [N], chunk_off [N+1], chunk_tab [n_chunks_max, 3]) int32 on the GPU."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    N = cu_seqlens.shape[0] - 1
+    dev = cu_seqlens.device
+    order = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    off = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    tab = torch.empty((T_total // 64 + N, 3), dtype=torch.int32, device=dev)
+    st = lib().gdn_chunk_map(_ptr(cu_seqlens), N, T_total, _ptr(order), _ptr(off), _ptr(tab),
+                             _stream())
+    _check(st, "gdn_chunk_map")
+    return order[:N], off, tab
+
+
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, *, initial_state: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                  scale: float = 1.0, o: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill. q, k [T, Hk, 128], v [T, Hv, 128] bf16; g, beta [T, Hv] fp32.
+
+    Returns (o [T, Hv, 128] fp32, final_state [N, Hv, 128, 128] fp32 or None).
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+        _inner_contig(t, nm)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    if not (g.is_contiguous() and beta.is_contiguous()):
+        raise ValueError("g and beta must be contiguous")
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32, 3)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4)
+        if not initial_state.is_contiguous():
+            raise ValueError("initial_state must be contiguous")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n_seqs, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, 4)
+        if not final_state.is_contiguous():
+            raise ValueError("final_state must be contiguous")
+    ws_bytes = 0
+    if cu_seqlens is not None:
+        ws_bytes = gdn_chunk_fwd_workspace_bytes(n_seqs, T, Hk, Hv, dk)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel()
+    st = lib().gdn_chunk_fwd(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                             _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state), _ptr(final_state),
+                             _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv, scale, _ptr(workspace),
+                             ws_bytes, _stream())
+    _check(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor, *,
+                    state_slot: Optional[torch.Tensor] = None, scale: float = 1.0,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence; state [n_slots, Hv, 128, 128] fp32 updated in place."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+        _inner_contig(t, nm)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(state, "state", torch.float32, 4)
+    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
+        raise ValueError("g, beta and state must be contiguous")
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if state_slot is not None:
+        _need(state_slot, "state_slot", torch.int32, 1)
+    if o is None:
+        o = torch.empty((N, Hv, dv), dtype=torch.float32, device=q.device)
+    st = lib().gdn_decode_step(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                               _ptr(g), _ptr(beta), _ptr(state), _ptr(state_slot), state.shape[0],
+                               _ptr(o), N, Hk, Hv, dk, dv, scale, _stream())
+    _check(st, "gdn_decode_step")
+    return o
+
+
+def gdn_gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,
+                      out: Optional[torch.Tensor] = None, out_bf16: bool = False,
+                      eps: float = 1e-6) -> torch.Tensor:
+    """o [rows, Hv, 128] fp32, z [rows, Hv, 128] bf16, w [128] fp32 -> out."""
+    _need(o, "o", torch.float32, 3)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    rows, Hv, dv = o.shape
+    if z.dim() == 3:
+        _inner_contig(z, "z")
+        z2 = z.view(z.shape[0], -1) if z.is_contiguous() else z.reshape(z.shape[0], -1)
+    else:
+        z2 = z
+    _need(z2, "z", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 1)
+    if out is None:
+        out = torch.empty((rows, Hv, dv), dtype=torch.bfloat16 if out_bf16 else torch.float32,
+                          device=o.device)
+    st = lib().gdn_gated_rmsnorm(_ptr(o), _ptr(z2), z2.stride(0), _ptr(w.contiguous()), _ptr(out),
+                                 1 if out_bf16 else 0, rows, Hv, dv, eps, _stream())
+    _check(st, "gdn_gated_rmsnorm")
+    return out
+
+
+def gdn_validate_cu_seqlens(cu_seqlens: torch.Tensor, T_total: int) -> None:
+    """Opt-in host check of cu_seqlens (synchronises the stream)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    st = lib().gdn_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, T_total,
+                                       _stream())
+    _check(st, "gdn_validate_cu_seqlens")

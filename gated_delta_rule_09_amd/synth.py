@@ -176,3 +176,78 @@ def decode_inputs(seed: int, N: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_D
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------- on-device draws
+#
+# Same distributions as above, drawn with torch's seeded generator directly on
+# the GPU (a different random stream from numpy's PCG64).  Used for benchmark
+# inputs that are too large to draw on the host quickly; parity tests use the
+# numpy generators so the oracle sees the identical bytes.
+
+def _tgen(seed: int, device):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return gen
+
+
+def chunk_inputs_torch(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DIM,
+                       lengths=None, h0_std: Optional[float] = None, device="cuda"):
+    """dict of device tensors: q, k, v (bf16), g, beta (fp32), h0, cu_seqlens."""
+    import torch
+    gen = _tgen(seed, device)
+
+    def unit(shape):
+        a = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return (a / a.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q = unit((T, Hk, d))
+    k = unit((T, Hk, d))
+    v = torch.randn((T, Hv, d), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    g = torch.rand((T, Hv), generator=gen, device=device, dtype=torch.float32) * -0.1
+    beta = torch.sigmoid(torch.randn((T, Hv), generator=gen, device=device, dtype=torch.float32))
+    n = 1 if lengths is None else len(lengths)
+    cu = None
+    if lengths is not None:
+        cu = torch.from_numpy(cu_from_lengths(lengths)).to(device)
+    h0 = None
+    if h0_std is not None:
+        h0 = torch.randn((n, Hv, d, d), generator=gen, device=device, dtype=torch.float32) * h0_std
+    return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, n_seqs=n)
+
+
+def mixer_inputs_torch(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DIM,
+                       device="cuda"):
+    import torch
+    gen = _tgen(seed, device)
+    C = (2 * Hk + Hv) * d
+    g = torch.rand((T, Hv), generator=gen, device=device) * -0.1
+    beta = torch.sigmoid(torch.randn((T, Hv), generator=gen, device=device))
+    x = torch.randn((T, C), generator=gen, device=device).to(torch.bfloat16)
+    w = (torch.randn((C, CONV_K), generator=gen, device=device) * 0.5).to(torch.bfloat16)
+    z = torch.randn((T, Hv, d), generator=gen, device=device).to(torch.bfloat16)
+    nw = 1.0 + 0.02 * torch.randn((d,), generator=gen, device=device)
+    return dict(x=x, conv_w=w, g=g, beta=beta, z=z, norm_w=nw)
+
+
+def decode_inputs_torch(seed: int, N: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DIM,
+                        state_std: float = 0.02, device="cuda"):
+    import torch
+    gen = _tgen(seed, device)
+
+    def unit(shape):
+        a = torch.randn(shape, generator=gen, device=device)
+        return (a / a.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    C = (2 * Hk + Hv) * d
+    return dict(
+        q=unit((N, Hk, d)), k=unit((N, Hk, d)),
+        v=torch.randn((N, Hv, d), generator=gen, device=device).to(torch.bfloat16),
+        g=torch.rand((N, Hv), generator=gen, device=device) * -0.1,
+        beta=torch.sigmoid(torch.randn((N, Hv), generator=gen, device=device)),
+        state=torch.randn((N, Hv, d, d), generator=gen, device=device) * state_std,
+        x=torch.randn((N, C), generator=gen, device=device).to(torch.bfloat16),
+        conv_w=(torch.randn((C, CONV_K), generator=gen, device=device) * 0.5).to(torch.bfloat16),
+        conv_state=torch.randn((N, C, CONV_K - 1), generator=gen, device=device).to(torch.bfloat16),
+    )

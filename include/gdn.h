@@ -1,0 +1,215 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated-delta-rule token mixer library
+ * (libgdn.so).
+ *
+ * The operation is the gated delta rule of the "Delta-rule layers" row of the
+ * Architecture table on the "Agnes-3.0-Flash" model card (ModelScope): 16 key
+ * heads shared by 48 value heads, head dim 128, a kernel-4 causal conv in
+ * front, a gated RMS-norm after, and an fp32 recurrent state.  The rule itself
+ * (the "erase, then write" update with a forget gate described in the
+ * "Attention Layer Details" section of "Agnes-3.0-Flash Deep Dive: A 33B
+ * Hybrid-Attention Multimodal Model") is, per value head h with key head
+ * kh = h / (Hv / Hk):
+ *
+ *     S_t = S_{t-1} * alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t,        alpha_t = exp(g_t)
+ *
+ * S is dv x dk with the VALUE channel as row index (S k is a value vector).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, owned by the caller.  The library
+ *    allocates nothing, keeps no pointer after returning and has no global
+ *    mutable state apart from a thread-local error string.
+ *  - bf16 tensors travel as uint16_t bit patterns.
+ *  - Strides are in elements; the innermost (head-dim) dimension is contiguous.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; no call synchronises the host unless stated.
+ *  - Argument errors are detected before anything is enqueued: a negative
+ *    status is returned and no output is touched.  Launch failures return
+ *    GDN_ERR_HIP with detail text in gdn_last_error().  Device faults surface
+ *    at the caller's next synchronisation, as usual for HIP.
+ *  - Data pointers of tensors with no elements (T_total == 0, n_seqs == 0,
+ *    rows == 0) may be NULL.
+ *  - Supported domain: head dim 128 (dk = dv = 128), Hv % Hk == 0.
+ *  - Matrix products inside the prefill kernel take fp16 operands with fp32
+ *    accumulation (q and k are converted exactly from bf16 when their values
+ *    lie in the fp16 normal range, i.e. for L2-normalised q and k).  Values
+ *    of v, of the state and of intermediate products must stay below the fp16
+ *    maximum (65504) in magnitude; the conv front's L2 normalisation keeps q
+ *    and k at unit norm.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gdn_status;
+
+#define GDN_OK 0
+#define GDN_ERR_NULL (-1)        /* a required pointer is NULL                        */
+#define GDN_ERR_SHAPE (-2)       /* a size, stride or head count is invalid           */
+#define GDN_ERR_UNSUPPORTED (-3) /* valid but outside the supported domain (e.g. d)   */
+#define GDN_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required          */
+#define GDN_ERR_ALIAS (-5)       /* an input overlaps an output it must not overlap   */
+#define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
+#define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
+
+#define GDN_ABI_VERSION 1
+
+/* Human-readable name of a status code (static storage). */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail text of the last failure on the calling thread (empty if none). */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the built library. */
+int32_t gdn_abi_version(void);
+
+/*
+ * gdn_conv1d_fwd -- causal depthwise conv (kernel 4) + SiLU + per-head L2 norm.
+ *
+ * The "causal conv (kernel 4) in front" of the "Delta-rule layers" row of the
+ * model card's Architecture table, applied to the projected q|k|v channels:
+ *
+ *     y[t][c] = silu( sum_{i=0..3} w[c][i] * x[t-3+i][c]  + bias[c] )
+ *
+ * where x before the start of a sequence is read from that sequence's
+ * conv_state (oldest first) or is zero when conv_state is NULL.  Then every
+ * head of head_dim channels among the first n_l2_heads heads is normalised:
+ *     y <- y / sqrt(sum y^2 + l2_eps)
+ * Arithmetic is fp32; y is rounded to bf16 (nearest, ties to even).
+ *
+ *   x          [T_total, C] bf16, row stride x_row_stride (>= C)
+ *   w          [C, 4] bf16; w[c][3] multiplies the current token
+ *   bias       [C] fp32 or NULL
+ *   y          [T_total, C] bf16, row stride y_row_stride (>= C); must not
+ *              overlap x
+ *   conv_state [n_seqs, C, 3] bf16 or NULL.  In: the three inputs preceding
+ *              each sequence, oldest first.  Out (in place): the last three
+ *              inputs of (old state ++ sequence); an empty sequence keeps it.
+ *   cu_seqlens [n_seqs + 1] int32 device array or NULL.  NULL means n_seqs
+ *              sequences of T_total / n_seqs tokens each (T_total % n_seqs == 0;
+ *              decode is T_total == n_seqs).  Precondition: cu[0] = 0,
+ *              non-decreasing, cu[n_seqs] = T_total (checked only by
+ *              gdn_validate_cu_seqlens or when GDN_VALIDATE_CU_SEQLENS=1).
+ *   n_l2_heads heads [0, n_l2_heads) of head_dim channels are L2-normalised
+ *              (32 for the layer: 16 q heads then 16 k heads).
+ *   head_dim   must be 128.  C must be a multiple of 8.
+ */
+gdn_status gdn_conv1d_fwd(const uint16_t* x, int64_t x_row_stride, const uint16_t* w,
+                          const float* bias, uint16_t* y, int64_t y_row_stride,
+                          uint16_t* conv_state, const int32_t* cu_seqlens, int32_t n_seqs,
+                          int32_t T_total, int32_t C, int32_t n_l2_heads, int32_t head_dim,
+                          float l2_eps, void* stream);
+
+/*
+ * gdn_chunk_fwd -- chunked prefill of the rule over packed sequences.
+ *
+ * Computes exactly the sequential rule above for every token of every
+ * sequence (the state restarts at each sequence start from its initial state),
+ * organised in chunks of 64 tokens with the WY / UT form inside each chunk.
+ *
+ *   q, k           [T_total, Hk, dk] bf16, token strides q_tok_stride,
+ *                  k_tok_stride (>= Hk * dk)
+ *   v              [T_total, Hv, dv] bf16, token stride v_tok_stride (>= Hv * dv)
+ *   g, beta        [T_total, Hv] fp32, contiguous (alpha = exp(g))
+ *   o              [T_total, Hv, dv] fp32, contiguous; must not overlap q, k, v
+ *   initial_state  [n_seqs, Hv, dv, dk] fp32 or NULL (zeros)
+ *   final_state    [n_seqs, Hv, dv, dk] fp32 or NULL; may be the same buffer as
+ *                  initial_state (each block reads its slice before writing it)
+ *   cu_seqlens     [n_seqs + 1] int32 device array or NULL (n_seqs equal
+ *                  sequences, T_total % n_seqs == 0); same precondition as above
+ *   scale          multiplies o (1.0 for the plain rule)
+ *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes()
+ *                  bytes, 256-byte aligned, required when cu_seqlens is given
+ *                  (may be NULL otherwise).  It holds the per-call schedule:
+ *                  the sequences ordered longest first (the order of
+ *                  gdn_chunk_map), built on the device from cu_seqlens.  Chunk
+ *                  bounds are those gdn_chunk_map tabulates.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
+                                     int32_t d);
+
+gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                         int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                         const float* g, const float* beta, float* o,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                         int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_map -- the varlen chunk map used by gdn_chunk_fwd, exposed so its
+ * integer results can be checked bit for bit.  From cu_seqlens it writes
+ *   order      [n_seqs]      sequence ids sorted by length, longest first
+ *                            (ties by id)
+ *   chunk_off  [n_seqs + 1]  exclusive prefix sum of ceil(len / 64)
+ *   chunk_tab  [n_chunks, 3] (sequence id, first token, token count) per chunk,
+ *                            sequences in id order, chunks restart at each
+ *                            sequence start; n_chunks = chunk_off[n_seqs]
+ *                            <= T_total / 64 + n_seqs
+ * All arrays are device int32.  cu_seqlens must be non-NULL here.
+ */
+gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                         int32_t* order, int32_t* chunk_off, int32_t* chunk_tab, void* stream);
+
+/*
+ * gdn_decode_step -- one token per sequence, state updated in place.
+ *
+ * The rule above with T = 1: per (sequence n, value head h)
+ *     S <- alpha S + beta (v - alpha S k) k^T,   o = scale * S q
+ * computed in fp32 from one pass over the state.
+ *
+ *   q, k        [n_seqs, Hk, dk] bf16, sequence strides q_stride, k_stride
+ *   v           [n_seqs, Hv, dv] bf16, sequence stride v_stride
+ *   g, beta     [n_seqs, Hv] fp32, contiguous
+ *   state       [n_slots, Hv, dv, dk] fp32, read and written in place
+ *   state_slot  [n_seqs] int32 device array or NULL: sequence n uses slot
+ *               state_slot[n] (NULL: slot n).  Slots must be distinct and in
+ *               [0, n_slots); not checked on the device.
+ *   o           [n_seqs, Hv, dv] fp32; must not overlap state or the inputs
+ */
+gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                           int64_t k_stride, const uint16_t* v, int64_t v_stride, const float* g,
+                           const float* beta, float* state, const int32_t* state_slot,
+                           int32_t n_slots, float* o, int32_t n_seqs, int32_t Hk, int32_t Hv,
+                           int32_t dk, int32_t dv, float scale, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- the "gated RMS-norm" after the rule (model card,
+ * Architecture table, row "Delta-rule layers"), per (row, value head):
+ *     out_i = o_i / sqrt(mean_j o_j^2 + eps) * w_i * z_i * sigmoid(z_i)
+ *
+ *   o      [rows, Hv, dv] fp32, contiguous
+ *   z      [rows, Hv * dv] bf16, row stride z_row_stride (>= Hv * dv)
+ *   w      [dv] fp32, shared by all heads
+ *   out    [rows, Hv, dv], fp32 (out_is_bf16 == 0) or bf16 (out_is_bf16 != 0,
+ *          rounded to nearest, ties to even); may be the same buffer as o when
+ *          fp32
+ *   dv     must be 128
+ */
+gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
+                             const float* w, void* out, int32_t out_is_bf16, int64_t rows,
+                             int32_t Hv, int32_t dv, float eps, void* stream);
+
+/*
+ * gdn_validate_cu_seqlens -- opt-in host check of a device cu_seqlens array:
+ * cu[0] == 0, non-decreasing, cu[n_seqs] == T_total.  Copies the array to the
+ * host and therefore SYNCHRONISES the stream.  Returns GDN_OK or
+ * GDN_ERR_SEQLENS.  When the environment variable GDN_VALIDATE_CU_SEQLENS=1
+ * is set, gdn_conv1d_fwd and gdn_chunk_fwd call it before enqueuing.
+ */
+gdn_status gdn_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

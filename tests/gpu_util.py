@@ -1,0 +1,75 @@
+"""Helpers for the GPU parity tests: host <-> device transfer and the tolerance.
+
+Tolerance (the mixer's accuracy bar, per output tensor): relative L2 error
+<= 1e-3 and max |got - ref| <= 5e-3 * max |ref|, against the fp64 oracle.
+bf16 outputs are compared on the bf16 grid: every element within one bf16 ulp
+of the oracle's rounded value (both sides round once, from fp32 vs fp64).
+"""
+import sys
+
+import numpy as np
+import torch
+
+REL_L2 = 1e-3
+MAX_ABS = 5e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a_u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        u = t.cpu().view(torch.int16).numpy().view(np.uint16)
+        return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nr = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / nr if nr > 0 else np.linalg.norm(got - ref)
+    mx = np.max(np.abs(ref)) if ref.size else 0.0
+    mabs = np.max(np.abs(got - ref)) / mx if mx > 0 else (np.max(np.abs(got - ref)) if ref.size else 0.0)
+    return rel, mabs
+
+
+def assert_close(got, ref, name=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == np.shape(ref), f"{name}: shape {got.shape} vs {np.shape(ref)}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    rel, mabs = errors(got, ref)
+    log(f"  {name}: rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
+    assert rel <= REL_L2, f"{name}: rel-L2 {rel:.3e} > {REL_L2}"
+    assert mabs <= MAX_ABS, f"{name}: max-abs {mabs:.3e} > {MAX_ABS} * max|ref|"
+
+
+def bf16_ulp(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def assert_bf16_within_1ulp(got, ref, name=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = np.abs(got - ref)
+    bad = d > bf16_ulp(ref) * 1.0000001
+    frac = np.mean(got != ref) if got.size else 0.0
+    log(f"  {name}: bf16 mismatches {frac:.2e}, max |d|/ulp {np.max(d / bf16_ulp(ref)) if got.size else 0:.2f}")
+    assert not np.any(bad), f"{name}: {int(bad.sum())} elements differ by more than 1 bf16 ulp"

@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed): libgdn.so loads, exports every
+function include/gdn.h declares, and rejects invalid arguments synchronously,
+before any HIP call, with the documented status codes.  Pointers here are fake
+addresses; every call is built to fail validation, so none is dereferenced."""
+import ctypes
+import os
+
+import pytest
+
+from gated_delta_rule_09_amd import ops
+
+OK, NULL, SHAPE, UNSUP, WS, ALIAS = 0, -1, -2, -3, -4, -5
+
+A = 0x7f0000000000          # fake, 256-byte aligned "device" addresses
+MB = 1 << 20
+
+
+def P(i):
+    return A + i * 1024 * MB
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    return ops.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = ops.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gdn.h but not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
+                       (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
+                       (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
+        assert lib.gdn_status_string(code).decode() == name
+
+
+def chunk(lib, **kw):
+    a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), beta=P(4), o=P(5),
+             h0=None, hT=None, cu=None, N=1, T=64, Hk=16, Hv=48, dk=128, dv=128, scale=1.0,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                             a["beta"], a["o"], a["h0"], a["hT"], a["cu"], a["N"], a["T"],
+                             a["Hk"], a["Hv"], a["dk"], a["dv"], a["scale"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+def test_chunk_fwd_validation(lib):
+    assert chunk(lib, q=None) == NULL
+    assert chunk(lib, o=None) == NULL
+    assert chunk(lib, Hv=47) == SHAPE                 # Hv % Hk != 0
+    assert chunk(lib, dk=64) == UNSUP
+    assert chunk(lib, dv=256) == UNSUP
+    assert chunk(lib, qs=1000) == SHAPE               # stride < Hk * dk
+    assert chunk(lib, vs=6148) == SHAPE               # not a multiple of 8
+    assert chunk(lib, T=65, N=2) == SHAPE             # equal split impossible
+    assert chunk(lib, N=0, T=5) == SHAPE
+    assert chunk(lib, q=P(0) + 2) == SHAPE            # misaligned
+    assert chunk(lib, scale=float("inf")) == SHAPE
+    # varlen needs a workspace of the advertised size
+    need = lib.gdn_chunk_fwd_workspace_bytes(3, 64, 16, 48, 128)
+    assert need > 0
+    assert chunk(lib, cu=P(6), N=3) == WS
+    assert chunk(lib, cu=P(6), N=3, ws=P(7), wsb=need - 1) == WS
+    # o overlapping an input / final state overlapping o
+    assert chunk(lib, o=P(0) + 4096) == ALIAS
+    assert chunk(lib, hT=P(5)) == ALIAS
+    # final state partially overlapping the initial state
+    assert chunk(lib, h0=P(8), hT=P(8) + 4096) == ALIAS
+    assert b"overlap" in lib.gdn_last_error()
+
+
+def test_decode_validation(lib):
+    def dec(**kw):
+        a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), b=P(4), st=P(5),
+                 slot=None, nslots=4, o=P(6), N=4, Hk=16, Hv=48, dk=128, dv=128)
+        a.update(kw)
+        return lib.gdn_decode_step(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                   a["b"], a["st"], a["slot"], a["nslots"], a["o"], a["N"],
+                                   a["Hk"], a["Hv"], a["dk"], a["dv"], 1.0, None)
+    assert dec(st=None) == NULL
+    # an empty batch may pass NULL data pointers and enqueues nothing
+    assert dec(q=None, k=None, v=None, g=None, b=None, st=None, o=None, N=0, nslots=0) == OK
+    assert dec(nslots=3) == SHAPE                      # fewer slots than sequences, no map
+    assert dec(Hk=5) == SHAPE
+    assert dec(dk=96) == UNSUP
+    assert dec(o=P(5) + 64) == ALIAS                   # o inside the state
+    assert dec(st=P(2)) == ALIAS                       # state over v
+
+
+def test_conv_validation(lib):
+    def conv(**kw):
+        a = dict(x=P(0), xs=10240, w=P(1), bias=None, y=P(2), ys=10240, cs=None, cu=None, N=1,
+                 T=16, C=10240, nl2=32, hd=128, eps=1e-6)
+        a.update(kw)
+        return lib.gdn_conv1d_fwd(a["x"], a["xs"], a["w"], a["bias"], a["y"], a["ys"], a["cs"],
+                                  a["cu"], a["N"], a["T"], a["C"], a["nl2"], a["hd"], a["eps"],
+                                  None)
+    assert conv(x=None) == NULL
+    assert conv(hd=64) == UNSUP
+    assert conv(C=10244) == UNSUP
+    assert conv(nl2=81) == SHAPE
+    assert conv(xs=10000) == SHAPE
+    assert conv(y=P(0) + 16) == ALIAS
+    assert conv(eps=-1.0) == SHAPE
+
+
+def test_rmsnorm_validation(lib):
+    def rn(**kw):
+        a = dict(o=P(0), z=P(1), zs=6144, w=P(2), out=P(3), bf=0, rows=8, Hv=48, dv=128, eps=1e-6)
+        a.update(kw)
+        return lib.gdn_gated_rmsnorm(a["o"], a["z"], a["zs"], a["w"], a["out"], a["bf"],
+                                     a["rows"], a["Hv"], a["dv"], a["eps"], None)
+    assert rn(w=None) == NULL
+    assert rn(dv=64) == UNSUP
+    assert rn(zs=6000) == SHAPE
+    assert rn(out=P(1)) == ALIAS                      # out over z
+    assert rn(out=P(0), bf=1) == ALIAS                 # bf16 out cannot alias fp32 o
+    assert rn(out=P(0) + 512) == ALIAS                 # partial alias with o
+
+
+def test_chunk_map_and_seqlens_validation(lib):
+    assert lib.gdn_chunk_map(None, 1, 1, P(0), P(1), P(2), None) == NULL
+    assert lib.gdn_chunk_map(P(3), -1, 1, P(0), P(1), P(2), None) == SHAPE
+    assert lib.gdn_validate_cu_seqlens(None, 1, 1, None) == NULL
+    assert lib.gdn_validate_cu_seqlens(P(0), -2, 1, None) == SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ops, "_lib_handle", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        ops.lib()

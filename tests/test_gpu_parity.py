@@ -1,0 +1,237 @@
+"""GPU parity of every entry point against the fp64 oracle, at sizes the oracle
+finishes in seconds, spanning several chunks and ragged tails, plus edge cases
+(empty sequences, T = 1, partial chunks, slot maps)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_09_amd import ops, synth
+from tests.gpu_util import (assert_bf16_within_1ulp, assert_close, dev_bf16, dev_f32, dev_i32,
+                            host, log)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_chunk(ci: synth.ChunkInputs, scale=1.0, varlen=True):
+    cu = dev_i32(ci.cu_seqlens) if (varlen and ci.cu_seqlens is not None) else None
+    h0 = dev_f32(ci.h0) if ci.h0 is not None else None
+    o, hT = ops.gdn_chunk_fwd(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g),
+                              dev_f32(ci.beta), initial_state=h0, cu_seqlens=cu,
+                              n_seqs=ci.n_seqs, scale=scale)
+    return host(o), host(hT)
+
+
+def oracle_chunk(ci: synth.ChunkInputs, scale=1.0):
+    return oracle.recurrence(ci.q, ci.k, ci.v, ci.g, ci.beta, ci.h0, cu_seqlens=ci.cu_seqlens,
+                             n_seqs=ci.n_seqs, scale=scale)
+
+
+# ----------------------------------------------------------------- prefill
+
+@pytest.mark.parametrize("T", [1, 2, 3, 63, 64, 65, 127, 200])
+def test_chunk_single_sequence_lengths(T):
+    log(f"chunk_fwd T={T} Hk=16 Hv=48 h0")
+    ci = synth.chunk_inputs(2000 + T, T, h0_std=0.02)
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+@pytest.mark.parametrize("Hk,Hv", [(1, 1), (2, 6), (4, 8), (3, 12)])
+def test_chunk_head_groupings(Hk, Hv):
+    log(f"chunk_fwd T=150 Hk={Hk} Hv={Hv}")
+    ci = synth.chunk_inputs(2100 + Hv, 150, Hk=Hk, Hv=Hv, h0_std=0.1)
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+def test_chunk_zero_initial_state_and_scale():
+    log("chunk_fwd T=300 no h0 scale=128^-0.5")
+    ci = synth.chunk_inputs(2200, 300)
+    s = 128 ** -0.5
+    o, hT = run_chunk(ci, scale=s)
+    ro, rT = oracle_chunk(ci, scale=s)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+def test_chunk_equal_split_without_cu_seqlens():
+    log("chunk_fwd 3 equal sequences of 100, no cu_seqlens")
+    ci = synth.chunk_inputs(2300, 300, Hk=4, Hv=12, lengths=[100, 100, 100], h0_std=0.05)
+    o, hT = run_chunk(ci, varlen=False)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+def test_chunk_varlen_with_empty_sequences():
+    lens = [70, 0, 1, 64, 0, 129, 5]
+    log(f"chunk_fwd varlen {lens}")
+    ci = synth.chunk_inputs(2400, sum(lens), Hk=4, Hv=12, lengths=lens, h0_std=0.05)
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    for n in range(len(lens)):
+        assert_close(hT[n], rT[n], f"final_state[{n}]")
+    # empty sequences hand back their initial state exactly
+    np.testing.assert_array_equal(hT[1], ci.h0[1])
+    np.testing.assert_array_equal(hT[4], ci.h0[4])
+
+
+def test_chunk_strong_decay_and_beta_extremes():
+    log("chunk_fwd strong decay, beta in {0, 1}")
+    ci = synth.chunk_inputs(2500, 200, Hk=2, Hv=6, h0_std=0.05)
+    ci.g = (ci.g * 30.0).astype(np.float32)           # alpha down to exp(-3)
+    ci.beta[::3] = 1.0
+    ci.beta[1::3] = 0.0
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+# ----------------------------------------------------------------- chunk map
+
+@pytest.mark.parametrize("lens", [[5], [64, 64], [0, 0, 3], [100, 0, 65, 1, 64, 300, 0, 2],
+                                  list(np.random.default_rng(3).integers(0, 400, 300))])
+def test_chunk_map_bit_exact(lens):
+    log(f"chunk_map N={len(lens)}")
+    cu = synth.cu_from_lengths(lens)
+    T = int(cu[-1])
+    order, off, tab = ops.gdn_chunk_map(dev_i32(cu), T)
+    r_order, r_off, r_tab = oracle.chunk_map(cu)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(order.cpu().numpy(), r_order)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    n = int(r_off[-1])
+    np.testing.assert_array_equal(tab[:n].cpu().numpy(), r_tab)
+
+
+# ----------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("N", [1, 5, 33])
+def test_decode_step(N):
+    log(f"decode_step N={N}")
+    di = synth.decode_inputs(2600 + N, N, with_conv=False)
+    st = dev_f32(di.state)
+    o = ops.gdn_decode_step(dev_bf16(di.q), dev_bf16(di.k), dev_bf16(di.v), dev_f32(di.g),
+                            dev_f32(di.beta), st)
+    ro, rst = oracle.decode(di.q, di.k, di.v, di.g, di.beta, di.state)
+    assert_close(host(o), ro, "o")
+    assert_close(host(st), rst, "state")
+
+
+def test_decode_step_slot_map_and_scale():
+    N, slots_n = 6, 10
+    log("decode_step with slot map")
+    di = synth.decode_inputs(2700, N, with_conv=False)
+    pool = np.random.default_rng(5).standard_normal((slots_n, 48, 128, 128)).astype(np.float32) * 0.02
+    slots = np.array([7, 0, 3, 9, 4, 1], dtype=np.int32)
+    pool[slots] = di.state
+    st = dev_f32(pool)
+    o = ops.gdn_decode_step(dev_bf16(di.q), dev_bf16(di.k), dev_bf16(di.v), dev_f32(di.g),
+                            dev_f32(di.beta), st, state_slot=dev_i32(slots), scale=0.5)
+    ro, rst = oracle.decode(di.q, di.k, di.v, di.g, di.beta, pool, state_slot=slots, scale=0.5)
+    got = host(st)
+    assert_close(host(o), ro, "o")
+    assert_close(got[slots], rst[slots], "state (slots used)")
+    others = [i for i in range(slots_n) if i not in slots]
+    np.testing.assert_array_equal(got[others], pool[others])
+
+
+# ----------------------------------------------------------------- conv
+
+@pytest.mark.parametrize("lens", [[37], [1, 1, 1, 1], [10, 0, 2, 25, 1]])
+def test_conv1d_varlen_with_state(lens):
+    log(f"conv1d lens={lens}")
+    mi = synth.mixer_inputs(2800 + len(lens), sum(lens), conv_state_seqs=len(lens))
+    cu = synth.cu_from_lengths(lens)
+    cs = dev_bf16(mi.conv_state)
+    y = ops.gdn_conv1d_fwd(dev_bf16(mi.x), dev_bf16(mi.conv_w), conv_state=cs,
+                           cu_seqlens=dev_i32(cu), n_l2_heads=32)
+    ry, rcs = oracle.conv1d(mi.x, mi.conv_w, conv_state=mi.conv_state, cu_seqlens=cu,
+                            n_l2_heads=32, head_dim=128, l2_eps=1e-6, stage_bf16=True)
+    assert_bf16_within_1ulp(host(y), ry, "y")
+    np.testing.assert_array_equal(host(cs), rcs)
+
+
+def test_conv1d_no_state_equal_split_and_bias():
+    T, N = 96, 3
+    log("conv1d no state, equal split, bias")
+    mi = synth.mixer_inputs(2900, T)
+    bias = np.random.default_rng(9).standard_normal(mi.x.shape[1]).astype(np.float32) * 0.1
+    y = ops.gdn_conv1d_fwd(dev_bf16(mi.x), dev_bf16(mi.conv_w), bias=dev_f32(bias), n_seqs=N,
+                           n_l2_heads=32)
+    ry, _ = oracle.conv1d(mi.x, mi.conv_w, bias=bias, n_seqs=N, n_l2_heads=32, head_dim=128,
+                          l2_eps=1e-6, stage_bf16=True)
+    assert_bf16_within_1ulp(host(y), ry, "y")
+
+
+def test_conv1d_strided_rows():
+    T = 20
+    log("conv1d strided x and y rows")
+    mi = synth.mixer_inputs(3000, T)
+    C = mi.x.shape[1]
+    xb = torch.zeros((T, C + 64), dtype=torch.bfloat16, device="cuda")
+    xb[:, :C] = dev_bf16(mi.x)
+    yb = torch.full((T, C + 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    ops.gdn_conv1d_fwd(xb[:, :C], dev_bf16(mi.conv_w), y=yb[:, :C], n_l2_heads=32)
+    ry, _ = oracle.conv1d(mi.x, mi.conv_w, n_l2_heads=32, head_dim=128, stage_bf16=True)
+    got = host(yb)
+    assert_bf16_within_1ulp(got[:, :C], ry, "y")
+    assert np.all(got[:, C:] == 7.0), "padding columns of y were written"
+
+
+# ----------------------------------------------------------------- gated norm
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_gated_rmsnorm(out_bf16):
+    rows, Hv = 77, 48
+    log(f"gated_rmsnorm rows={rows} bf16_out={out_bf16}")
+    r = np.random.default_rng(11)
+    o = r.standard_normal((rows, Hv, 128)).astype(np.float32) * 0.3
+    z = synth.bf16_bits(r.standard_normal((rows, Hv, 128)).astype(np.float32))
+    w = (1 + 0.02 * r.standard_normal(128)).astype(np.float32)
+    out = ops.gdn_gated_rmsnorm(dev_f32(o), dev_bf16(z), dev_f32(w), out_bf16=out_bf16)
+    ref = oracle.gated_rmsnorm(o, z, w, eps=1e-6, stage_bf16=out_bf16)
+    if out_bf16:
+        assert_bf16_within_1ulp(host(out), ref, "out")
+    else:
+        assert_close(host(out), ref, "out")
+
+
+def test_gated_rmsnorm_in_place():
+    rows, Hv = 10, 4
+    log("gated_rmsnorm in place")
+    r = np.random.default_rng(12)
+    o = r.standard_normal((rows, Hv, 128)).astype(np.float32)
+    z = synth.bf16_bits(r.standard_normal((rows, Hv, 128)).astype(np.float32))
+    w = np.ones(128, dtype=np.float32)
+    od = dev_f32(o)
+    ops.gdn_gated_rmsnorm(od, dev_bf16(z), dev_f32(w), out=od)
+    assert_close(host(od), oracle.gated_rmsnorm(o, z, w), "out")
+
+
+# ----------------------------------------------------------------- full mixer
+
+def test_mixer_conv_chunk_norm():
+    """conv front -> chunked rule -> gated norm, as one layer's token mixer."""
+    T = 200
+    log(f"mixer T={T}")
+    mi = synth.mixer_inputs(3100, T)
+    y = ops.gdn_conv1d_fwd(dev_bf16(mi.x), dev_bf16(mi.conv_w), n_l2_heads=32)
+    yv = y.view(T, 80, 128)
+    q, k, v = yv[:, :16], yv[:, 16:32], yv[:, 32:]
+    o, hT = ops.gdn_chunk_fwd(q, k, v, dev_f32(mi.g), dev_f32(mi.beta))
+    out = ops.gdn_gated_rmsnorm(o, dev_bf16(mi.z), dev_f32(mi.norm_w))
+    ry, _ = oracle.conv1d(mi.x, mi.conv_w, n_l2_heads=32, head_dim=128, stage_bf16=True)
+    ry = ry.reshape(T, 80, 128)
+    ro, rT = oracle.recurrence(ry[:, :16], ry[:, 16:32], ry[:, 32:], mi.g, mi.beta)
+    rout = oracle.gated_rmsnorm(ro, mi.z, mi.norm_w)
+    assert_close(host(o), ro, "o")
+    assert_close(host(hT), rT, "final_state")
+    assert_close(host(out), rout, "norm out")

@@ -1,0 +1,142 @@
+"""Structural GPU checks: every output row written exactly where it belongs,
+nothing outside, packed == separate calls bit for bit, run-to-run determinism,
+resumable state (final -> initial), prefill + decode continuity."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_09_amd import ops, synth
+from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_i32, host, log
+
+pytestmark = pytest.mark.gpu
+
+LENS = [70, 0, 1, 64, 129, 5, 0, 200]
+
+
+def _dev(ci):
+    return (dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g), dev_f32(ci.beta))
+
+
+def test_outputs_land_in_their_rows_and_guards_untouched():
+    log("sentinel / guard bands")
+    ci = synth.chunk_inputs(4000, sum(LENS), Hk=2, Hv=6, lengths=LENS, h0_std=0.05)
+    T, N = sum(LENS), len(LENS)
+    q, k, v, g, b = _dev(ci)
+    guard = 64
+    obuf = torch.full((T + 2 * guard, 6, 128), float("nan"), device="cuda")
+    sbuf = torch.full((N + 2, 6, 128, 128), float("nan"), device="cuda")
+    o = obuf[guard:guard + T]
+    fs = sbuf[1:N + 1]
+    ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=dev_f32(ci.h0), final_state=fs,
+                      cu_seqlens=dev_i32(ci.cu_seqlens), o=o)
+    ob, sb = host(obuf), host(sbuf)
+    assert np.all(np.isnan(ob[:guard])) and np.all(np.isnan(ob[guard + T:])), "o guard written"
+    assert np.all(np.isnan(sb[0])) and np.all(np.isnan(sb[N + 1])), "state guard written"
+    assert np.all(np.isfinite(ob[guard:guard + T])), "an o row was not written"
+    assert np.all(np.isfinite(sb[1:N + 1])), "a final state was not written"
+
+
+def test_packed_equals_separate_calls_bitwise():
+    log("packed vs separate, bitwise")
+    ci = synth.chunk_inputs(4100, sum(LENS), Hk=4, Hv=12, lengths=LENS, h0_std=0.05)
+    q, k, v, g, b = _dev(ci)
+    h0 = dev_f32(ci.h0)
+    o, hT = ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0, cu_seqlens=dev_i32(ci.cu_seqlens))
+    cu = ci.cu_seqlens
+    for n in range(len(LENS)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        on, sn = ops.gdn_chunk_fwd(q[s:e], k[s:e], v[s:e], g[s:e].contiguous(),
+                                   b[s:e].contiguous(), initial_state=h0[n:n + 1].contiguous(),
+                                   n_seqs=1)
+        assert torch.equal(o[s:e], on), f"o of sequence {n} differs"
+        assert torch.equal(hT[n:n + 1], sn), f"final state of sequence {n} differs"
+
+
+def test_runs_are_bitwise_deterministic():
+    log("determinism")
+    ci = synth.chunk_inputs(4200, 777, h0_std=0.02)
+    args = _dev(ci)
+    h0 = dev_f32(ci.h0)
+    o1, s1 = ops.gdn_chunk_fwd(*args, initial_state=h0)
+    o2, s2 = ops.gdn_chunk_fwd(*args, initial_state=h0)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    di = synth.decode_inputs(4201, 7, with_conv=False)
+    st1, st2 = dev_f32(di.state), dev_f32(di.state)
+    d = (dev_bf16(di.q), dev_bf16(di.k), dev_bf16(di.v), dev_f32(di.g), dev_f32(di.beta))
+    a = ops.gdn_decode_step(*d, st1)
+    bq = ops.gdn_decode_step(*d, st2)
+    assert torch.equal(a, bq) and torch.equal(st1, st2)
+
+
+def test_split_call_resumes_bitwise_at_chunk_boundary():
+    """Running T1 tokens, then T2 more from the returned state, equals one call
+    over T1 + T2 bit for bit when T1 is a multiple of the chunk length."""
+    log("split continuation")
+    T1, T2 = 128, 100
+    ci = synth.chunk_inputs(4300, T1 + T2, Hk=4, Hv=12, h0_std=0.05)
+    q, k, v, g, b = _dev(ci)
+    h0 = dev_f32(ci.h0)
+    o, s = ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0)
+    oa, sa = ops.gdn_chunk_fwd(q[:T1], k[:T1], v[:T1], g[:T1].contiguous(), b[:T1].contiguous(),
+                               initial_state=h0)
+    ob, sb = ops.gdn_chunk_fwd(q[T1:], k[T1:], v[T1:], g[T1:].contiguous(), b[T1:].contiguous(),
+                               initial_state=sa)
+    assert torch.equal(torch.cat([oa, ob]), o)
+    assert torch.equal(sb, s)
+
+
+def test_final_state_may_alias_initial_state():
+    log("final_state aliases initial_state")
+    ci = synth.chunk_inputs(4400, 150, Hk=2, Hv=6, h0_std=0.05)
+    args = _dev(ci)
+    o1, s1 = ops.gdn_chunk_fwd(*args, initial_state=dev_f32(ci.h0))
+    st = dev_f32(ci.h0)
+    o2, s2 = ops.gdn_chunk_fwd(*args, initial_state=st, final_state=st)
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    log("prefill(T) + decode(1) vs prefill(T+1)")
+    T = 130
+    ci = synth.chunk_inputs(4500, T + 1, h0_std=0.02)
+    q, k, v, g, b = _dev(ci)
+    h0 = dev_f32(ci.h0)
+    o_full, s_full = ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0)
+    _, st = ops.gdn_chunk_fwd(q[:T], k[:T], v[:T], g[:T].contiguous(), b[:T].contiguous(),
+                              initial_state=h0)
+    o_last = ops.gdn_decode_step(q[T:], k[T:], v[T:], g[T:].contiguous(), b[T:].contiguous(), st)
+    ro, rs = oracle.recurrence(ci.q, ci.k, ci.v, ci.g, ci.beta, ci.h0)
+    assert_close(host(o_last)[0], ro[T], "decode o")
+    assert_close(host(o_full)[T], ro[T], "prefill o[T]")
+    assert_close(host(st), rs, "decode state")
+
+
+def test_conv_prefill_then_step_continuity():
+    """conv over T tokens then a batch-mode step with the carried state equals
+    conv over T + 1 tokens."""
+    log("conv state continuity")
+    T = 40
+    mi = synth.mixer_inputs(4600, T + 1, conv_state_seqs=1)
+    x = dev_bf16(mi.x)
+    w = dev_bf16(mi.conv_w)
+    cs_full = dev_bf16(mi.conv_state)
+    y_full = ops.gdn_conv1d_fwd(x, w, conv_state=cs_full, n_seqs=1, n_l2_heads=32)
+    cs = dev_bf16(mi.conv_state)
+    y_a = ops.gdn_conv1d_fwd(x[:T], w, conv_state=cs, n_seqs=1, n_l2_heads=32)
+    y_b = ops.gdn_conv1d_fwd(x[T:], w, conv_state=cs, n_seqs=1, n_l2_heads=32)
+    assert torch.equal(torch.cat([y_a, y_b]), y_full)
+    assert torch.equal(cs, cs_full)
+
+
+def test_empty_batch_is_a_no_op():
+    log("empty inputs")
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    zv = torch.empty((0, 6, 128), dtype=torch.bfloat16, device="cuda")
+    zg = torch.empty((0, 6), dtype=torch.float32, device="cuda")
+    h0 = torch.randn((2, 6, 128, 128), device="cuda")
+    o, s = ops.gdn_chunk_fwd(z, z, zv, zg, zg, initial_state=h0,
+                             cu_seqlens=torch.zeros(3, dtype=torch.int32, device="cuda"))
+    assert o.shape[0] == 0 and torch.equal(s, h0)
+    o = ops.gdn_decode_step(z, z, zv, zg, zg, torch.zeros((1, 6, 128, 128), device="cuda"))
+    assert o.shape[0] == 0
