@@ -156,11 +156,9 @@ gdn_status gdn_conv1d_fwd(const uint16_t* x, int64_t x_row_stride, const uint16_
 
 size_t gdn_chunk_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
                                      int32_t d) {
-  (void)Hk;
-  (void)Hv;
   (void)d;
-  if (n_seqs < 0 || T_total < 0) return 0;
-  return gdn::chunk_workspace_layout(n_seqs, T_total).total;
+  if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0) return 0;
+  return gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv).total;
 }
 
 gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
@@ -210,13 +208,7 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
   // grid size: ceil(n_seqs * Hk / 8) * 8 * (Hv / Hk) * 2 blocks
   if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
     return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: too many (sequence, head) pairs");
-  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total);
-  if (cu_seqlens) {
-    if (!workspace || workspace_bytes < ws.total)
-      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace of %zu bytes needed", ws.total);
-    if (!aligned(workspace, 256))
-      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace must be 256-byte aligned");
-  }
+  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
   const Range rq = range_of(q, T_total, q_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rk = range_of(k, T_total, k_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rv = range_of(v, T_total, v_tok_stride, static_cast<int64_t>(Hv) * dv, 2);
@@ -226,7 +218,7 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
   const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
   const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
   const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
-  const Range rw = cu_seqlens ? range_of(workspace, 1, 0, static_cast<int64_t>(ws.total), 1) : Range{};
+  const Range rw = range_of(workspace, 1, 0, static_cast<int64_t>(ws.total), 1);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &r0})
     if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: o overlaps an input");
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro})
@@ -235,21 +227,20 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
     return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: final_state partially overlaps initial_state");
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro, &r0, &rT})
     if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: workspace overlaps a tensor");
+  if (n_seqs > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace of %zu bytes needed", ws.total);
+    if (!aligned(workspace, 256))
+      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace must be 256-byte aligned");
+  }
   if (cu_seqlens && env_validate_seqlens()) {
     const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
     if (s) return s;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* order = nullptr;
-  if (cu_seqlens) {
-    order = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + ws.order_off);
-    const gdn_status s = hip_status(gdn::launch_chunk_order(cu_seqlens, n_seqs, order, st),
-                                    "gdn_chunk_fwd schedule launch");
-    if (s) return s;
-  }
   return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g,
-                                          beta, o, initial_state, final_state, cu_seqlens, order,
-                                          n_seqs, T_total, Hk, Hv, scale, st),
+                                          beta, o, initial_state, final_state, cu_seqlens,
+                                          n_seqs, T_total, Hk, Hv, scale, workspace, st),
                     "gdn_chunk_fwd launch");
 }
 

@@ -14,29 +14,32 @@
 // (unroll S_i = a_i S_{i-1} + u_i k_i^T with u_i = b_i (v_i - a_i S_{i-1} k_i)
 // inside the chunk; every exponent used is <= 0 for g <= 0).
 //
-// Work decomposition.  One 256-thread work-group per (sequence, value head,
-// half of the 128 value channels); each of its four waves owns 16 value
-// channels and carries their 16 x 128 slice of S^T in MFMA accumulator
-// registers across all chunks of the sequence.  Per chunk:
-//   1. all threads stage K, Q (bf16 -> fp16, row-major) and K^T in LDS;
-//   2. every wave scans g in registers (wave-private decay tables in LDS);
-//   3. the waves share the 20 lower 16x16 tiles of K K^T and Q K^T
-//      (fp16 MFMA, exact products of bf16 inputs) and turn them into -A
-//      (off-diagonal blocks, fp16), the diagonal blocks of A (fp32) and
-//      P = scale * E * Q K^T (fp16);
-//   4. wave w inverts diagonal block w of I + A by forward substitution in fp32;
-//   5. each wave runs its chain: X = K S0^T and Q S0^T (B operand straight from
-//      the S^T registers), R = b V - b gamma X, U by blockwise forward
-//      substitution (U_i = T_ii (R_i - sum_j<i A_ij U_j)), O = gamma Q S0^T + P U,
-//      then S^T <- gamma_L S^T + K^T (D U).
-// Only the fp32-valued operands are rounded to fp16 (S0, U, T_ii, A, P);
-// accumulation is fp32 throughout.
+// Two kernels, run back to back on the caller's stream:
 //
-// Differences from designs for other GPUs: no per-chunk state is written to
-// HBM (the whole chain for a value slice stays in one work-group), operand
-// layouts follow the 64-lane MFMA accumulator so three of the five products
-// take their B operand from registers, and work-groups that share a key head
-// are placed on the same XCD (L2) by the block-id mapping.
+//   prep (fully parallel over every chunk x key head): everything that does not
+//   depend on the state.  K and Q are converted to fp16 once and written with
+//   K^T in MFMA fragment order; the 20 lower 16x16 tiles of K K^T and Q K^T are
+//   formed once per key head on fp16 MFMA (exact products of bf16 inputs); for
+//   each of the key head's value heads the decay tables, -A, the inverses
+//   T_bb = (I + A_bb)^-1 of the four diagonal 16x16 blocks (fp32 forward
+//   substitution) and P = scale E * Q K^T are written, also in fragment order.
+//   Chunks come from the varlen chunk table, so they restart at every sequence
+//   start.
+//
+//   scan (one work-group per sequence x value head x half of the value
+//   channels): the sequential part.  Each of the four waves carries the
+//   16 x 128 slice of S^T for its 16 value channels in MFMA accumulator
+//   registers across all chunks.  Per chunk the work-group copies the chunk's
+//   fragments into LDS with 16-byte loads issued one chunk ahead, and each wave
+//   runs  X = K S0^T and Q S0^T (B operand straight from the S^T registers),
+//   R = b V - b gamma X, U by blockwise forward substitution
+//   (U_i = T_ii (R_i - sum_{j<i} A_ij U_j)), O = scale gamma Q S0^T + P U, and
+//   S^T <- gamma_L S^T + K^T (D U).
+//
+// Only the fp32-valued operands are rounded to fp16 (S0, U, T_ii, A, P);
+// accumulation is fp32 throughout.  The per-chunk state never leaves the
+// registers, and fragment reads are lane-contiguous 16-byte LDS loads.
+// Work-groups that share a key head get block ids on the same XCD (L2).
 #include "common.h"
 #include "launch.h"
 
@@ -46,57 +49,70 @@ namespace {
 
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kDvPerWg = 64;      // value channels per work-group
+constexpr int kThreads = 256;
+constexpr int kDvPerWg = 64;      // value channels per scan work-group
 constexpr int kHalves = kD / kDvPerWg;
 
-// LDS strides in halves (padding breaks power-of-two bank strides)
-constexpr int kKS = kD + 8;       // K, Q rows: 136 halves
-constexpr int kKTS = kC + 8;      // K^T rows: 72 halves
-constexpr int kAS = kC + 8;       // -A and P rows: 72 halves
-constexpr int kTS = 16 + 8;       // diagonal inverse rows: 24 halves
-constexpr int kVTS = kC + 8;      // V^T rows: 72 bf16
+// ---- fragment layout in the workspace -------------------------------------
+// An A32 fragment of a 16 x 32 block holds, for lane l (row l % 16, group
+// g = l / 16), the 8 halves at columns kappa(g, e) (see common.h): 16 bytes per
+// lane, lanes in order, 1 KB.  An A16 fragment (16 x 16) holds 4 halves at
+// columns 4g .. 4g+3: 8 bytes per lane, 512 B.
+constexpr int kFrag = 1024;
+constexpr int kFrag16 = 512;
+// Per (chunk, key head): K (tb*4+kb), Q (16 + tb*4+kb), K^T (32 + dt*2+kb).
+constexpr int kKQBytes = 48 * kFrag;
+// Per (chunk, value head):
+constexpr int kOffP = 0;                              // 6 A32: (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+constexpr int kOffT = kOffP + 6 * kFrag;              // 4 A16: T_bb
+constexpr int kOffAn10 = kOffT + 4 * kFrag16;         // A16: -A rows 16..31, cols 0..15
+constexpr int kOffAn2 = kOffAn10 + kFrag16;           // A32: -A rows 32..47, cols 0..31
+constexpr int kOffAn3 = kOffAn2 + kFrag;              // A32: -A rows 48..63, cols 0..31
+constexpr int kOffAn32 = kOffAn3 + kFrag;             // A16: -A rows 48..63, cols 32..47
+constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gamma, scale gamma, exp(G_L - G)
+constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
+constexpr int kVBytes = kOffGL + 256;                 // 12544
+constexpr int kStageBytes = kKQBytes + kVBytes;       // 61696
+constexpr int kStagePieces = kStageBytes / 16;        // 3856
+constexpr int kStageRounds = (kStagePieces + kThreads - 1) / kThreads;   // 16
+// Pieces in the last copy round (the rest of that round's lanes stay idle).
+constexpr int kStageTail = kStagePieces - (kStageRounds - 1) * kThreads;  // 16
 
-struct __align__(16) Smem {
+static_assert(kStageBytes % 16 == 0, "stage size");
+
+// ---- prep kernel LDS -------------------------------------------------------
+constexpr int kKS = kD + 8;       // K, Q rows (halves)
+constexpr int kAS = kC + 8;       // -A, P rows (halves)
+constexpr int kTS = 16 + 8;       // T_bb rows (halves)
+
+struct __align__(16) PrepSmem {
   _Float16 K[kC * kKS];
   _Float16 Q[kC * kKS];
-  _Float16 KT[kD * kKTS];
-  _Float16 An[kC * kAS];          // -A (only the off-diagonal 16x16 blocks are used)
-  _Float16 P[kC * kAS];           // scale * E * QK^T, lower incl. diagonal, zero above
-  _Float16 T[4 * 16 * kTS];       // (I + A_bb)^-1
-  uint16_t VT[kDvPerWg * kVTS];   // V^T of this work-group's 64 value channels (bf16 bits)
-  float Ad[4 * 16 * 16];          // diagonal blocks of A, strictly lower, fp32
-  // wave-private decay tables
-  float bet[kWaves][kC];          // b_i
-  float bg[kWaves][kC];           // b_i gamma_i
-  float sg[kWaves][kC];           // scale gamma_i
-  float dl[kWaves][kC];           // exp(G_last - G_i)
-  float G[kWaves][kC];            // G_i
+  _Float16 An[kC * kAS];
+  _Float16 P[kC * kAS];
+  _Float16 T[4 * 16 * kTS];
+  float Ad[4 * 16 * 16];
+  float G[kC];
+  float bet[kC];
 };
 
-struct Params {
-  const uint16_t* q; const uint16_t* k; const uint16_t* v;
-  int64_t qs, ks, vs;
+struct PrepParams {
+  const uint16_t* q; const uint16_t* k;
+  int64_t qs, ks;
   const float* g; const float* beta;
-  float* o;
-  const float* h0; float* hT;
-  const int32_t* cu;       // cu_seqlens or nullptr (equal lengths seq_len)
-  const int32_t* order;    // longest-first schedule (varlen only)
-  int n_seqs, seq_len, Hk, Hv, group;   // group = Hv / Hk
-  int n_chain_groups;                   // n_seqs * Hk
+  const int32_t* cu;          // nullptr: equal lengths seq_len
+  const int32_t* chunk_off;   // varlen chunk map (device)
+  const int32_t* chunk_tab;
+  unsigned char* kq;          // [max_chunks][Hk][kKQBytes]
+  unsigned char* vb;          // [max_chunks][Hv][kVBytes]
+  int n_seqs, seq_len, Hk, Hv, group;
   float scale;
 };
 
-// A operand (or B operand read from a row-major tile) for a 32-wide reduction
-// block starting at column kb: lane (row, grp) gets columns
-// kb + 4grp .. +3 and kb + 16 + 4grp .. +3.
 __device__ __forceinline__ half8 lds_a32(const _Float16* base, int stride, int row, int kb,
                                          int grp) {
   const _Float16* p = base + row * stride + kb + 4 * grp;
-  const half4 lo = *reinterpret_cast<const half4*>(p);
-  const half4 hi = *reinterpret_cast<const half4*>(p + 16);
-  return cat8(lo, hi);
+  return cat8(*reinterpret_cast<const half4*>(p), *reinterpret_cast<const half4*>(p + 16));
 }
 
 __device__ __forceinline__ half4 lds_a16(const _Float16* base, int stride, int row, int kb,
@@ -104,44 +120,218 @@ __device__ __forceinline__ half4 lds_a16(const _Float16* base, int stride, int r
   return *reinterpret_cast<const half4*>(base + row * stride + kb + 4 * grp);
 }
 
-// Raw global data of one chunk, held in registers while the previous chunk is
-// being computed.  Rows past the chunk end are clamped to its last row on load
-// (no divergent branches, so all loads of a chunk are in flight at once) and
-// zeroed when written to LDS.
-struct Stage {
-  uint4 k[4], q[4], v[2];
-  float g, b;
-};
+__device__ __forceinline__ void put16(unsigned char* dst, const half8 v) {
+  *reinterpret_cast<half8*>(dst) = v;
+}
+__device__ __forceinline__ void put8(unsigned char* dst, const half4 v) {
+  *reinterpret_cast<half4*>(dst) = v;
+}
 
-__device__ __forceinline__ void stage_load(Stage& st, const Params& p, int t0, int len, int kh,
-                                           int h, int half, int tid, int lane) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
+  __shared__ PrepSmem sm;
+  const int kh = blockIdx.y;
+  const int c = blockIdx.x;
+  int t0, len;
+  if (p.cu) {
+    if (c >= p.chunk_off[p.n_seqs]) return;
+    t0 = p.chunk_tab[3 * c + 1];
+    len = p.chunk_tab[3 * c + 2];
+  } else {
+    const int nc = (p.seq_len + kC - 1) / kC;
+    const int n = c / nc;
+    const int i = c - n * nc;
+    t0 = n * p.seq_len + i * kC;
+    len = min(kC, p.seq_len - i * kC);
+  }
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // ---- K, Q -> LDS (fp16), rows past the chunk end zeroed ------------------
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int piece = tid + kThreads * j;       // 64 rows x 16 pieces of 8 channels
-    const int r = min(piece >> 4, len - 1);
+    const int r = piece >> 4;
     const int c8 = (piece & 15) * 8;
-    st.k[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + r) * p.ks + kh * kD + c8);
-    st.q[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + r) * p.qs + kh * kD + c8);
-  }
+    const int rr = min(r, len - 1);
+    const uint4 kb = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
+    const uint4 qb = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
+    float fk[8], fq[8];
+    bf16x8_to_f32(kb, fk);
+    bf16x8_to_f32(qb, fq);
+    half8 hk, hq;
+    const bool ok = r < len;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int piece = tid + kThreads * j;       // 64 rows x 8 pieces of 8 value channels
-    const int r = min(piece >> 3, len - 1);
-    const int c8 = (piece & 7) * 8;
-    st.v[j] = *reinterpret_cast<const uint4*>(p.v + static_cast<int64_t>(t0 + r) * p.vs + h * kD +
-                                              half * kDvPerWg + c8);
+    for (int i = 0; i < 8; ++i) {
+      hk[i] = static_cast<_Float16>(ok ? fk[i] : 0.f);
+      hq[i] = static_cast<_Float16>(ok ? fq[i] : 0.f);
+    }
+    *reinterpret_cast<half8*>(&sm.K[r * kKS + c8]) = hk;
+    *reinterpret_cast<half8*>(&sm.Q[r * kKS + c8]) = hq;
   }
-  const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
-  st.g = p.g[gi];
-  st.b = p.beta[gi];
+  // P tiles above the diagonal blocks that the fragments (0,0) and (2,1) cover
+  for (int i = tid; i < 2 * 256; i += kThreads) {
+    const int t = i >> 8, rr = (i >> 4) & 15, cc = i & 15;
+    const int r0 = t ? 32 : 0;
+    sm.P[(r0 + rr) * kAS + r0 + 16 + cc] = static_cast<_Float16>(0.f);
+  }
+  lds_barrier();
+
+  // ---- K, Q, K^T fragments (written once per chunk and key head) -----------
+  unsigned char* kq = p.kq + (static_cast<int64_t>(c) * p.Hk + kh) * kKQBytes;
+#pragma unroll
+  for (int j = 0; j < 12; ++j) {
+    const int f = w * 12 + j;
+    half8 v;
+    if (f < 32) {
+      const _Float16* X = f < 16 ? sm.K : sm.Q;
+      const int ff = f & 15;
+      v = lds_a32(X, kKS, 16 * (ff >> 2) + col, 32 * (ff & 3), grp);
+    } else {
+      const int dt = (f - 32) >> 1, kb = (f - 32) & 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+        v[e] = sm.K[tok * kKS + 16 * dt + col];
+      }
+    }
+    put16(kq + f * kFrag + lane * 16, v);
+  }
+
+  // ---- Gram tiles: wave w owns lower tiles 5w .. 5w+4 of the list
+  // [K K^T (10 tiles), Q K^T (10 tiles)], tile t -> (b, j) in order
+  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
+  floatx4 gram[5];
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int job = 5 * w + jj;
+    const int t = job >= 10 ? job - 10 : job;
+    const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+    const int j = t - (b * (b + 1)) / 2;
+    const _Float16* X = job >= 10 ? sm.Q : sm.K;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < kD; kb += 32)
+      acc = mfma32(lds_a32(X, kKS, 16 * b + col, kb, grp), lds_a32(sm.K, kKS, 16 * j + col, kb, grp), acc);
+    gram[jj] = acc;
+  }
+
+  // ---- per value head of this key head -------------------------------------
+  for (int vh = 0; vh < p.group; ++vh) {
+    const int h = kh * p.group + vh;
+    unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
+    // decay tables: wave 0 scans g; everyone waits at the barrier below
+    if (w == 0) {
+      const bool valid = lane < len;
+      const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
+      const float gv = valid ? p.g[gi] : 0.f;
+      const float bv = valid ? p.beta[gi] : 0.f;
+      float G = gv;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float up = __shfl_up(G, d, 64);
+        if (lane >= d) G += up;
+      }
+      const float Glast = __shfl(G, 63, 64);
+      const float gam = __expf(G);
+      sm.G[lane] = G;
+      sm.bet[lane] = bv;
+      float* dec = reinterpret_cast<float*>(vb + kOffDecay);
+      dec[lane] = bv;
+      dec[64 + lane] = bv * gam;
+      dec[128 + lane] = p.scale * gam;
+      dec[192 + lane] = __expf(Glast - G);
+      if (lane == 0) *reinterpret_cast<float*>(vb + kOffGL) = __expf(Glast);
+    }
+    lds_barrier();   // G, bet ready; previous head's readers done with An/P/T
+
+#pragma unroll
+    for (int jj = 0; jj < 5; ++jj) {
+      const int job = 5 * w + jj;
+      const bool isq = job >= 10;
+      const int t = isq ? job - 10 : job;
+      const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+      const int j = t - (b * (b + 1)) / 2;
+      const int jc = 16 * j + col;
+      const float Gj = sm.G[jc];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * b + 4 * grp + e;
+        const float E = __expf(sm.G[i] - Gj);
+        if (isq) {
+          sm.P[i * kAS + jc] = static_cast<_Float16>((jc <= i) ? p.scale * E * gram[jj][e] : 0.f);
+        } else {
+          const float a = (jc < i) ? sm.bet[i] * E * gram[jj][e] : 0.f;
+          if (b == j) sm.Ad[(b * 16 + 4 * grp + e) * 16 + col] = a;
+          else sm.An[i * kAS + jc] = static_cast<_Float16>(-a);
+        }
+      }
+    }
+    lds_barrier();   // -A, A_diag, P ready
+
+    // T_ww = (I + A_ww)^-1 by forward substitution (lane = column)
+    if (lane < 16) {
+      const float* Ab = sm.Ad + w * 256;
+      float tt[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int kk = 0; kk < i; ++kk) acc = fmaf(-Ab[i * 16 + kk], tt[kk], acc);
+        tt[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.T[(w * 16 + i) * kTS + lane] = static_cast<_Float16>(tt[i]);
+    }
+    // same-wave LDS write then read: in order within the wave
+    put8(vb + kOffT + w * kFrag16 + lane * 8, lds_a16(sm.T, kTS, w * 16 + col, 0, grp));
+    // P and -A fragments
+    if (w < 3) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int f = 2 * w + j;   // (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+        const int tb = f < 2 ? f : (f < 4 ? 2 : 3);
+        const int kb = (f == 3 || f == 5) ? 32 : 0;
+        put16(vb + kOffP + f * kFrag + lane * 16, lds_a32(sm.P, kAS, 16 * tb + col, kb, grp));
+      }
+    } else {
+      put8(vb + kOffAn10 + lane * 8, lds_a16(sm.An, kAS, 16 + col, 0, grp));
+      put16(vb + kOffAn2 + lane * 16, lds_a32(sm.An, kAS, 32 + col, 0, grp));
+      put16(vb + kOffAn3 + lane * 16, lds_a32(sm.An, kAS, 48 + col, 0, grp));
+      put8(vb + kOffAn32 + lane * 8, lds_a16(sm.An, kAS, 48 + col, 32, grp));
+    }
+  }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
-  __shared__ Smem sm;
+// ---- scan kernel ------------------------------------------------------------
+
+struct ScanParams {
+  const uint16_t* v;
+  int64_t vs;
+  float* o;
+  const float* h0; float* hT;
+  const int32_t* cu;          // nullptr: equal lengths seq_len
+  const int32_t* order;       // longest-first schedule (varlen)
+  const int32_t* chunk_off;   // first chunk of each sequence (varlen)
+  const unsigned char* kq;
+  const unsigned char* vb;
+  int n_seqs, seq_len, Hk, Hv, group;
+  int n_chain_groups;         // n_seqs * Hk
+};
+
+// Two stage buffers: the chunk being computed and the one being copied in.
+struct __align__(16) ScanSmem {
+  unsigned char buf[2][kStageBytes];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
+  __shared__ ScanSmem sm;
 
   // ---- block id -> (sequence rank, value head, value half) -----------------
   // Chains sharing a key head (group * kHalves of them) get block ids that are
-  // congruent mod 8, i.e. land on the same XCD and share K/Q through its L2.
+  // congruent mod 8, i.e. land on the same XCD and share fragments through L2.
   const int members = p.group * kHalves;
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -162,255 +352,193 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
   const int grp = lane >> 4;
   const int dvc = half * kDvPerWg + 16 * w + col;   // this lane's value channel
 
-  // Token range of the sequence.  Chunks of 64 restart at the sequence start
-  // (the same chunking gdn_chunk_map tabulates); their bounds are derived here
-  // so the chunk loop issues no bookkeeping loads.
-  int seq_start, seq_len;
+  int seq_start, seq_len, chunk0;
   if (p.cu) {
     seq_start = p.cu[n];
     seq_len = p.cu[n + 1] - seq_start;
+    chunk0 = p.chunk_off[n];
   } else {
     seq_start = n * p.seq_len;
     seq_len = p.seq_len;
+    chunk0 = n * ((p.seq_len + kC - 1) / kC);
   }
   const int n_chunks = (seq_len + kC - 1) / kC;
 
   // ---- initial state slice: S^T tiles, dk rows 16dt + 4grp + e, column dvc --
   floatx4 sT[8];
-  {
-    const int64_t sbase = ((static_cast<int64_t>(n) * p.Hv + h) * kD + dvc) * kD;
-    if (p.h0) {
+  const int64_t sbase = ((static_cast<int64_t>(n) * p.Hv + h) * kD + dvc) * kD;
+  if (p.h0) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const float4 t = *reinterpret_cast<const float4*>(p.h0 + sbase + 16 * dt + 4 * grp);
-        sT[dt][0] = t.x; sT[dt][1] = t.y; sT[dt][2] = t.z; sT[dt][3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) sT[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) {
+      const float4 t = *reinterpret_cast<const float4*>(p.h0 + sbase + 16 * dt + 4 * grp);
+      sT[dt][0] = t.x; sT[dt][1] = t.y; sT[dt][2] = t.z; sT[dt][3] = t.w;
     }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) sT[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // P above the diagonal blocks is read by the O product but never written.
-  for (int i = tid; i < kC * kAS; i += kThreads) sm.P[i] = static_cast<_Float16>(0.f);
+  // The fragments of chunk ci + 1 are copied from the workspace straight into
+  // the other LDS buffer (global_load_lds: lane l of a wave writes 16 bytes at
+  // the wave's base + 16 l) while chunk ci is computed; this lane's 16 values
+  // of V for chunk ci + 1 are loaded into registers.  Piece i (16 bytes) of a
+  // chunk's stage is byte 16 i of [K/Q/K^T blob | value-head blob].
+  uint32_t vraw[16];
+  const unsigned char* kq_head = p.kq + static_cast<int64_t>(kh) * kKQBytes;
+  const unsigned char* vb_head = p.vb + static_cast<int64_t>(h) * kVBytes;
+  const int64_t kq_step = static_cast<int64_t>(p.Hk) * kKQBytes;
+  const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
+  const uint16_t* v_head = p.v + h * kD + dvc;
 
-  Stage st;
-  if (n_chunks > 0) stage_load(st, p, seq_start, min(kC, seq_len), kh, h, half, tid, lane);
-
-  for (int c = 0; c < n_chunks; ++c) {
-    const int t0 = seq_start + c * kC;
-    const int len = min(kC, seq_len - c * kC);
-
-    __syncthreads();   // previous chunk's readers are done with LDS
-
-    // ---- 1. staged registers -> LDS: K, Q (fp16, row-major), K^T, V^T -------
+  auto stage = [&](int ci, int buf) {
+    const int cb = chunk0 + ci;
+    const unsigned char* kqb = kq_head + cb * kq_step;
+    const unsigned char* vbb = vb_head + cb * vb_step;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kStageRounds; ++j) {
       const int piece = tid + kThreads * j;
-      const int r = piece >> 4;
-      const int c8 = (piece & 15) * 8;
-      const bool ok = r < len;
-      float fk[8], fq[8];
-      bf16x8_to_f32(st.k[j], fk);
-      bf16x8_to_f32(st.q[j], fq);
-      half8 hk, hq;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hk[i] = static_cast<_Float16>(ok ? fk[i] : 0.f);
-        hq[i] = static_cast<_Float16>(ok ? fq[i] : 0.f);
-      }
-      *reinterpret_cast<half8*>(&sm.K[r * kKS + c8]) = hk;
-      *reinterpret_cast<half8*>(&sm.Q[r * kKS + c8]) = hq;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.KT[(c8 + i) * kKTS + r] = hk[i];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int piece = tid + kThreads * j;
-      const int r = piece >> 3;
-      const int c8 = (piece & 7) * 8;
-      const bool ok = r < len;
-      const uint32_t w4[4] = {st.v[j].x, st.v[j].y, st.v[j].z, st.v[j].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm.VT[(c8 + 2 * i) * kVTS + r] = ok ? static_cast<uint16_t>(w4[i] & 0xffffu) : 0;
-        sm.VT[(c8 + 2 * i + 1) * kVTS + r] = ok ? static_cast<uint16_t>(w4[i] >> 16) : 0;
+      if (j < kStageRounds - 1 || tid < kStageTail) {
+        const unsigned char* src = piece * 16 < kKQBytes ? kqb + piece * 16
+                                                         : vbb + (piece * 16 - kKQBytes);
+        lds_dma16(src, sm.buf[buf] + (kThreads * j + 64 * w) * 16);
       }
     }
-
-    // ---- 2. decay tables (every wave, private copy) ---------------------------
-    {
-      const bool valid = lane < len;
-      const float gv = valid ? st.g : 0.f;
-      const float bv = valid ? st.b : 0.f;
-      float G = gv;
+    const int t0 = seq_start + ci * kC;
+    const int len = min(kC, seq_len - ci * kC);
+    const uint16_t* vcol = v_head + static_cast<int64_t>(t0) * p.vs;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float up = __shfl_up(G, d, 64);
-        if (lane >= d) G += up;
-      }
-      const float Glast = __shfl(G, 63, 64);
-      const float gam = expf(G);
-      sm.G[w][lane] = G;
-      sm.bet[w][lane] = bv;
-      sm.bg[w][lane] = bv * gam;
-      sm.sg[w][lane] = p.scale * gam;
-      sm.dl[w][lane] = expf(Glast - G);
+    for (int i = 0; i < 16; ++i) {
+      const int r = min(16 * (i >> 2) + 4 * grp + (i & 3), len - 1);
+      vraw[i] = vcol[static_cast<int64_t>(r) * p.vs];
     }
+  };
 
-    // next chunk's loads fly while this one is computed
-    if (c + 1 < n_chunks)
-      stage_load(st, p, t0 + kC, min(kC, seq_len - (c + 1) * kC), kh, h, half, tid, lane);
-    __syncthreads();   // K, Q, K^T, V^T staged
-
-    // ---- 3. K K^T and Q K^T lower tiles -> -A, A_diag, P -----------------------
-    {
-      // 20 tile jobs: jobs 0..9 are K K^T tiles, 10..19 Q K^T tiles, each over
-      // the lower tiles (b, j) in order (0,0) (1,0) (1,1) (2,0) ... (3,3).
+  // O of the previous chunk, stored after the next barrier so that the wait at
+  // the top of each chunk only covers work issued a whole chunk earlier.
+  floatx4 Oprev[4];
+  int o_t0 = 0, o_len = 0;
+  auto store_o = [&]() {
+    float* ocol = p.o + static_cast<int64_t>(o_t0) * p.Hv * kD + h * kD + dvc;
 #pragma unroll
-      for (int jj = 0; jj < 5; ++jj) {
-        const int job = 5 * w + jj;
-        const bool isq = job >= 10;
-        const int t = isq ? job - 10 : job;
-        const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-        const int j = t - (b * (b + 1)) / 2;
-        const _Float16* X = isq ? sm.Q : sm.K;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 4; ++tb) {
+      if (o_len == kC) {
 #pragma unroll
-        for (int kb = 0; kb < kD; kb += 32) {
-          const half8 a = lds_a32(X, kKS, 16 * b + col, kb, grp);
-          const half8 bb = lds_a32(sm.K, kKS, 16 * j + col, kb, grp);
-          acc = mfma32(a, bb, acc);
-        }
-        const int jc = 16 * j + col;                 // column token
-        const float Gj = sm.G[w][jc];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * b + 4 * grp + e;        // row token
-          const float E = expf(sm.G[w][i] - Gj);
-          if (isq) {
-            const float v = (jc <= i) ? p.scale * E * acc[e] : 0.f;
-            sm.P[i * kAS + jc] = static_cast<_Float16>(v);
-          } else {
-            const float a = (jc < i) ? sm.bet[w][i] * E * acc[e] : 0.f;
-            if (b == j) sm.Ad[(b * 16 + 4 * grp + e) * 16 + col] = a;
-            else sm.An[i * kAS + jc] = static_cast<_Float16>(-a);
-          }
-        }
-      }
-    }
-    __syncthreads();   // -A, A_diag, P ready
-
-    // ---- 4. T_bb = (I + A_bb)^-1, wave w takes block w ------------------------
-    if (lane < 16) {
-      const float* Ab = sm.Ad + w * 256;
-      float t[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < i; ++kk) acc = fmaf(-Ab[i * 16 + kk], t[kk], acc);
-        t[i] = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.T[(w * 16 + i) * kTS + lane] = static_cast<_Float16>(t[i]);
-    }
-    __syncthreads();   // T ready
-
-    // ---- 5. chain for this wave's 16 value channels ----------------------------
-    {
-      // B operands of S0^T over 32-row dk blocks, straight from registers.
-      half8 sB[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
-
-      floatx4 X[4], QS[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          X[tb] = mfma32(lds_a32(sm.K, kKS, 16 * tb + col, 32 * kb, grp), sB[kb], X[tb]);
-          QS[tb] = mfma32(lds_a32(sm.Q, kKS, 16 * tb + col, 32 * kb, grp), sB[kb], QS[tb]);
-        }
-      }
-
-      // R = b V - b gamma X   (rows = tokens 16tb + 4grp + e, column dvc)
-      floatx4 R[4];
-      const uint16_t* vrow = sm.VT + (16 * w + col) * kVTS + 4 * grp;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint2 vb = *reinterpret_cast<const uint2*>(vrow + 16 * tb);
-        const float vv[4] = {__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xffff0000u),
-                             __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xffff0000u)};
+        for (int e = 0; e < 4; ++e)
+          ocol[static_cast<int64_t>(16 * tb + 4 * grp + e) * p.Hv * kD] = Oprev[tb][e];
+      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * tb + 4 * grp + e;
-          R[tb][e] = sm.bet[w][i] * vv[e] - sm.bg[w][i] * X[tb][e];
+          if (i < o_len) ocol[static_cast<int64_t>(i) * p.Hv * kD] = Oprev[tb][e];
         }
       }
+    }
+  };
 
-      // U by blockwise forward substitution
-      const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-      floatx4 U[4];
-      U[0] = mfma16(lds_a16(sm.T, kTS, 0 * 16 + col, 0, grp), to_half4(R[0]), z4);
-      floatx4 rhs = mfma16(lds_a16(sm.An, kAS, 16 + col, 0, grp), to_half4(U[0]), R[1]);
-      U[1] = mfma16(lds_a16(sm.T, kTS, 1 * 16 + col, 0, grp), to_half4(rhs), z4);
-      const half8 u01 = to_half8(U[0], U[1]);
-      rhs = mfma32(lds_a32(sm.An, kAS, 32 + col, 0, grp), u01, R[2]);
-      U[2] = mfma16(lds_a16(sm.T, kTS, 2 * 16 + col, 0, grp), to_half4(rhs), z4);
-      rhs = mfma32(lds_a32(sm.An, kAS, 48 + col, 0, grp), u01, R[3]);
-      rhs = mfma16(lds_a16(sm.An, kAS, 48 + col, 32, grp), to_half4(U[2]), rhs);
-      U[3] = mfma16(lds_a16(sm.T, kTS, 3 * 16 + col, 0, grp), to_half4(rhs), z4);
+  if (n_chunks > 0) stage(0, 0);
 
-      // O = scale gamma Q S0^T + P U
-      const half8 u23 = to_half8(U[2], U[3]);
-      float* ocol = p.o + static_cast<int64_t>(t0) * p.Hv * kD + h * kD + dvc;
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    const int t0 = seq_start + ci * kC;
+    const int len = min(kC, seq_len - ci * kC);
+    const unsigned char* B = sm.buf[ci & 1];
+    auto frag = [&](int f) { return *reinterpret_cast<const half8*>(B + f * kFrag + lane * 16); };
+    auto frag16 = [&](int off) { return *reinterpret_cast<const half4*>(B + kKQBytes + off + lane * 8); };
+    auto vfrag = [&](int off) { return *reinterpret_cast<const half8*>(B + kKQBytes + off + lane * 16); };
+    auto table = [&](int tab, int tb) {
+      return *reinterpret_cast<const floatx4*>(B + kKQBytes + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
+    };
+
+    // this chunk's copy (and everything older) has landed; the other buffer's
+    // readers (chunk ci - 1) are done
+    dma_barrier();
+    if (ci > 0) store_o();
+    float vv[16];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        floatx4 O;
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 16 * (i >> 2) + 4 * grp + (i & 3);
+      vv[i] = tok < len ? bf16_to_f32(static_cast<uint16_t>(vraw[i])) : 0.f;
+    }
+    if (ci + 1 < n_chunks) stage(ci + 1, (ci + 1) & 1);
+
+    // B operands of S0^T over 32-row dk blocks, straight from registers.
+    half8 sB[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] = sm.sg[w][16 * tb + 4 * grp + e] * QS[tb][e];
-        O = mfma32(lds_a32(sm.P, kAS, 16 * tb + col, 0, grp), u01, O);
-        if (tb >= 2) O = mfma32(lds_a32(sm.P, kAS, 16 * tb + col, 32, grp), u23, O);
-        if (len == kC) {
+    for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
+
+    floatx4 X[4], QS[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            ocol[static_cast<int64_t>(16 * tb + 4 * grp + e) * p.Hv * kD] = O[e];
-        } else {
+    for (int tb = 0; tb < 4; ++tb) {
+      X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * tb + 4 * grp + e;
-            if (i < len) ocol[static_cast<int64_t>(i) * p.Hv * kD] = O[e];
-          }
-        }
+      for (int kb = 0; kb < 4; ++kb) {
+        X[tb] = mfma32(frag(tb * 4 + kb), sB[kb], X[tb]);
+        QS[tb] = mfma32(frag(16 + tb * 4 + kb), sB[kb], QS[tb]);
       }
+    }
 
-      // S^T <- gamma_L S^T + K^T (D U)
-      floatx4 DU[4];
+    // R = b V - b gamma X   (rows = tokens 16tb + 4grp + e, column dvc)
+    floatx4 R[4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 4; ++tb) {
+      const floatx4 bt = table(0, tb);
+      const floatx4 bg = table(1, tb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) DU[tb][e] = sm.dl[w][16 * tb + 4 * grp + e] * U[tb][e];
-      const half8 d01 = to_half8(DU[0], DU[1]);
-      const half8 d23 = to_half8(DU[2], DU[3]);
-      const float gl = expf(sm.G[w][63]);
+      for (int e = 0; e < 4; ++e) R[tb][e] = bt[e] * vv[4 * tb + e] - bg[e] * X[tb][e];
+    }
+
+    // U by blockwise forward substitution
+    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 U[4];
+    U[0] = mfma16(frag16(kOffT + 0 * kFrag16), to_half4(R[0]), z4);
+    floatx4 rhs = mfma16(frag16(kOffAn10), to_half4(U[0]), R[1]);
+    U[1] = mfma16(frag16(kOffT + 1 * kFrag16), to_half4(rhs), z4);
+    const half8 u01 = to_half8(U[0], U[1]);
+    rhs = mfma32(vfrag(kOffAn2), u01, R[2]);
+    U[2] = mfma16(frag16(kOffT + 2 * kFrag16), to_half4(rhs), z4);
+    rhs = mfma32(vfrag(kOffAn3), u01, R[3]);
+    rhs = mfma16(frag16(kOffAn32), to_half4(U[2]), rhs);
+    U[3] = mfma16(frag16(kOffT + 3 * kFrag16), to_half4(rhs), z4);
+    const half8 u23 = to_half8(U[2], U[3]);
+
+    // O = scale gamma Q S0^T + P U  (stored at the start of the next chunk)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        floatx4 s = sT[dt];
+    for (int tb = 0; tb < 4; ++tb) {
+      const floatx4 sg = table(2, tb);
+      floatx4 O;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] *= gl;
-        s = mfma32(lds_a32(sm.KT, kKTS, 16 * dt + col, 0, grp), d01, s);
-        s = mfma32(lds_a32(sm.KT, kKTS, 16 * dt + col, 32, grp), d23, s);
-        sT[dt] = s;
-      }
+      for (int e = 0; e < 4; ++e) O[e] = sg[e] * QS[tb][e];
+      O = mfma32(vfrag(kOffP + (tb < 2 ? tb : 2 * tb - 2) * kFrag), u01, O);
+      if (tb >= 2) O = mfma32(vfrag(kOffP + (2 * tb - 1) * kFrag), u23, O);
+      Oprev[tb] = O;
+    }
+    o_t0 = t0;
+    o_len = len;
+
+    // S^T <- gamma_L S^T + K^T (D U)
+    floatx4 DU[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const floatx4 dl = table(3, tb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DU[tb][e] = dl[e] * U[tb][e];
+    }
+    const half8 d01 = to_half8(DU[0], DU[1]);
+    const half8 d23 = to_half8(DU[2], DU[3]);
+    const float gl = *reinterpret_cast<const float*>(B + kKQBytes + kOffGL);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      floatx4 s = sT[dt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] *= gl;
+      s = mfma32(frag(32 + dt * 2 + 0), d01, s);
+      s = mfma32(frag(32 + dt * 2 + 1), d23, s);
+      sT[dt] = s;
     }
   }
 
-  // ---- final state ------------------------------------------------------------
+  if (n_chunks > 0) store_o();
   if (p.hT) {
-    const int64_t sbase = ((static_cast<int64_t>(n) * p.Hv + h) * kD + dvc) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<float4*>(p.hT + sbase + 16 * dt + 4 * grp) =
@@ -420,25 +548,58 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
 
 }  // namespace
 
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
+  auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  ChunkWorkspace ws;
+  ws.max_chunks = static_cast<size_t>(T_total) / kC + static_cast<size_t>(n_seqs);
+  ws.order_off = 0;
+  ws.chunk_off_off = up(sizeof(int32_t) * static_cast<size_t>(n_seqs));
+  ws.chunk_tab_off = ws.chunk_off_off + up(sizeof(int32_t) * (static_cast<size_t>(n_seqs) + 1));
+  ws.kq_off = ws.chunk_tab_off + up(sizeof(int32_t) * 3 * ws.max_chunks);
+  ws.v_off = ws.kq_off + up(ws.max_chunks * static_cast<size_t>(Hk) * kKQBytes);
+  ws.total = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
+  return ws;
+}
+
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const float* g, const float* beta,
                             float* o, const float* h0, float* hT, const int32_t* cu,
-                            const int32_t* order, int n_seqs, int T_total, int Hk, int Hv,
-                            float scale, hipStream_t stream) {
+                            int n_seqs, int T_total, int Hk, int Hv, float scale,
+                            void* workspace, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
-  Params p;
-  p.q = q; p.k = k; p.v = v; p.qs = qs; p.ks = ks; p.vs = vs;
-  p.g = g; p.beta = beta; p.o = o; p.h0 = h0; p.hT = hT;
-  p.cu = cu;
-  p.order = cu ? order : nullptr;
-  p.n_seqs = n_seqs;
-  p.seq_len = cu ? 0 : T_total / n_seqs;
-  p.Hk = Hk; p.Hv = Hv; p.group = Hv / Hk;
-  p.n_chain_groups = n_seqs * Hk;
-  p.scale = scale;
-  const int members = p.group * kHalves;
-  const int blocks = ((p.n_chain_groups + 7) / 8) * 8 * members;
-  hipLaunchKernelGGL(chunk_fwd_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
+  const ChunkWorkspace ws = chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  int32_t* order = reinterpret_cast<int32_t*>(base + ws.order_off);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(base + ws.chunk_off_off);
+  int32_t* chunk_tab = reinterpret_cast<int32_t*>(base + ws.chunk_tab_off);
+  const int seq_len = cu ? 0 : T_total / n_seqs;
+  int n_chunk_slots;   // grid of the prep kernel
+  if (cu) {
+    const hipError_t e = launch_chunk_map(cu, n_seqs, T_total, order, chunk_off, chunk_tab, stream);
+    if (e != hipSuccess) return e;
+    n_chunk_slots = static_cast<int>(ws.max_chunks);
+  } else {
+    n_chunk_slots = n_seqs * ((seq_len + kC - 1) / kC);
+  }
+  if (T_total > 0 && n_chunk_slots > 0) {
+    PrepParams pp;
+    pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = g; pp.beta = beta;
+    pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
+    pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
+    pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
+    pp.scale = scale;
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(n_chunk_slots, Hk), dim3(kThreads), 0, stream, pp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ScanParams sp;
+  sp.v = v; sp.vs = vs; sp.o = o; sp.h0 = h0; sp.hT = hT;
+  sp.cu = cu; sp.order = cu ? order : nullptr; sp.chunk_off = chunk_off;
+  sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
+  sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;
+  sp.n_chain_groups = n_seqs * Hk;
+  const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kHalves;
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(blocks), dim3(kThreads), 0, stream, sp);
   return hipGetLastError();
 }
 

@@ -78,22 +78,6 @@ __global__ __launch_bounds__(kThreads) void chunk_table_kernel(const int32_t* __
 
 }  // namespace
 
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total) {
-  (void)T_total;
-  ChunkWorkspace ws;
-  ws.order_off = 0;
-  ws.total = ((sizeof(int32_t) * static_cast<size_t>(n_seqs)) + 255) & ~static_cast<size_t>(255);
-  if (ws.total == 0) ws.total = 256;
-  return ws;
-}
-
-hipError_t launch_chunk_order(const int32_t* cu, int n_seqs, int32_t* order, hipStream_t stream) {
-  if (n_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(order_kernel, dim3((n_seqs + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, cu, n_seqs, order);
-  return hipGetLastError();
-}
-
 hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
                             int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream) {
   (void)T_total;

@@ -128,7 +128,30 @@ __device__ __forceinline__ half8 cat8(const half4 lo, const half4 hi) {
   return h;
 }
 
-// Device-side launch helpers.
+// Work-group barrier that orders LDS only: each wave waits for its own LDS
+// operations, then all waves meet.  Unlike __syncthreads() it does not wait for
+// global loads or stores in flight, so loads issued ahead (prefetch of the next
+// chunk) stay in flight across it.  Use only where the barrier guards LDS.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Asynchronous copy of 16 bytes per lane from global memory straight into LDS
+// (gfx950 global_load_lds_dwordx4): lane l's bytes land at lds_wave_base + 16 l,
+// where lds_wave_base must be the same for the whole wave.  Completion is
+// tracked by vmcnt only; wait with dma_barrier() before reading the data.
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((global_void*)(src), (lds_void*)(lds_wave_base), 16, 0, 0);
+}
+
+// Work-group barrier after all of this wave's vector memory operations (loads,
+// stores and LDS copies) and LDS operations have completed.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 constexpr int kWave = 64;
 
 }  // namespace gdn

@@ -23,11 +23,13 @@ hipError_t launch_gated_rmsnorm(const float* o, const uint16_t* z, int64_t zs, c
                                 void* out, bool out_bf16, int64_t rows, int Hv, float eps,
                                 hipStream_t stream);
 
-// Workspace of the chunked prefill: the longest-first sequence order (int32).
+// Workspace of the chunked prefill (each piece 256-byte aligned):
+//   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]
+//   | K/Q/K^T fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]
 struct ChunkWorkspace {
-  size_t order_off, total;
+  size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, total;
 };
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total);
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv);
 
 hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
                             int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream);
@@ -35,11 +37,7 @@ hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t*
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const float* g, const float* beta,
                             float* o, const float* h0, float* hT, const int32_t* cu,
-                            const int32_t* order, int n_seqs, int T_total, int Hk, int Hv,
-                            float scale, hipStream_t stream);
-
-// Longest-first sequence order only (the part of the chunk map the prefill
-// schedule needs).
-hipError_t launch_chunk_order(const int32_t* cu, int n_seqs, int32_t* order, hipStream_t stream);
+                            int n_seqs, int T_total, int Hk, int Hv, float scale,
+                            void* workspace, hipStream_t stream);
 
 }  // namespace gdn

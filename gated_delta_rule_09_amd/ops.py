@@ -194,10 +194,10 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         if not final_state.is_contiguous():
             raise ValueError("final_state must be contiguous")
     ws_bytes = 0
-    if cu_seqlens is not None:
-        ws_bytes = gdn_chunk_fwd_workspace_bytes(n_seqs, T, Hk, Hv, dk)
+    if n_seqs > 0:
         if workspace is None:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            workspace = torch.empty(gdn_chunk_fwd_workspace_bytes(n_seqs, T, Hk, Hv, dk),
+                                    dtype=torch.uint8, device=q.device)
         ws_bytes = workspace.numel()
     st = lib().gdn_chunk_fwd(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
                              _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state), _ptr(final_state),

@@ -127,11 +127,14 @@ gdn_status gdn_conv1d_fwd(const uint16_t* x, int64_t x_row_stride, const uint16_
  *                  sequences, T_total % n_seqs == 0); same precondition as above
  *   scale          multiplies o (1.0 for the plain rule)
  *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes()
- *                  bytes, 256-byte aligned, required when cu_seqlens is given
- *                  (may be NULL otherwise).  It holds the per-call schedule:
- *                  the sequences ordered longest first (the order of
- *                  gdn_chunk_map), built on the device from cu_seqlens.  Chunk
- *                  bounds are those gdn_chunk_map tabulates.
+ *                  bytes, 256-byte aligned (may be NULL only when n_seqs == 0),
+ *                  not overlapping any tensor.  Per call it receives the chunk
+ *                  map (as gdn_chunk_map), then the state-independent part of
+ *                  every chunk (fp16 K, Q, K^T, -A, the inverted diagonal
+ *                  blocks of I + A, the masked decayed Q K^T and the decay
+ *                  tables, in MFMA fragment order), which the sequential scan
+ *                  then reads.  About 21 KB per token for 16 key / 48 value
+ *                  heads.  Contents are scratch: nothing is kept across calls.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
                                      int32_t d);
