@@ -72,11 +72,17 @@ constexpr int kOffAn32 = kOffAn3 + kFrag;             // A16: -A rows 48..63, co
 constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gamma, scale gamma, exp(G_L - G)
 constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
 constexpr int kVBytes = kOffGL + 256;                 // 12544
-constexpr int kStageBytes = kKQBytes + kVBytes;       // 61696
-constexpr int kStagePieces = kStageBytes / 16;        // 3856
-constexpr int kStageRounds = (kStagePieces + kThreads - 1) / kThreads;   // 16
-// Pieces in the last copy round (the rest of that round's lanes stay idle).
-constexpr int kStageTail = kStagePieces - (kStageRounds - 1) * kThreads;  // 16
+// Per chunk the scan stages [K/Q/K^T blob | value-head blob | V tile] in LDS,
+// where the V tile is this work-group's 64 value channels of the chunk's 64
+// tokens, row-major bf16 (128 bytes per token).
+constexpr int kVTileBytes = kC * kDvPerWg * 2;                          // 8192
+constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;           // 69888
+constexpr int kStagePieces = kStageBytes / 16;                          // 4368
+constexpr int kStageRounds = (kStagePieces + kThreads - 1) / kThreads;  // 18
+constexpr int kKQRounds = kKQBytes / (16 * kThreads);                   // 12
+constexpr int kVBPieces = kVBytes / 16;                                 // 784
+constexpr int kVTilePieces = kVTileBytes / 16;                          // 512
+static_assert(kKQBytes % (16 * kThreads) == 0, "K/Q blob is whole copy rounds");
 
 static_assert(kStageBytes % 16 == 0, "stage size");
 
@@ -378,38 +384,39 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     for (int dt = 0; dt < 8; ++dt) sT[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // The fragments of chunk ci + 1 are copied from the workspace straight into
-  // the other LDS buffer (global_load_lds: lane l of a wave writes 16 bytes at
-  // the wave's base + 16 l) while chunk ci is computed; this lane's 16 values
-  // of V for chunk ci + 1 are loaded into registers.  Piece i (16 bytes) of a
-  // chunk's stage is byte 16 i of [K/Q/K^T blob | value-head blob].
-  uint32_t vraw[16];
+  // The stage of chunk ci + 1 is copied straight into the other LDS buffer
+  // (global_load_lds: lane l of a wave writes 16 bytes at the wave's base +
+  // 16 l) while chunk ci is computed.  Piece i is byte 16 i of the stage:
+  // K/Q/K^T blob (rounds 0..11), value-head blob (784 pieces), then the V tile
+  // (512 pieces: token r, channels 8 (i % 8) .. +7 of this work-group's 64).
   const unsigned char* kq_head = p.kq + static_cast<int64_t>(kh) * kKQBytes;
   const unsigned char* vb_head = p.vb + static_cast<int64_t>(h) * kVBytes;
   const int64_t kq_step = static_cast<int64_t>(p.Hk) * kKQBytes;
   const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
-  const uint16_t* v_head = p.v + h * kD + dvc;
+  const uint16_t* v_head = p.v + h * kD + half * kDvPerWg;
 
   auto stage = [&](int ci, int buf) {
     const int cb = chunk0 + ci;
     const unsigned char* kqb = kq_head + cb * kq_step;
     const unsigned char* vbb = vb_head + cb * vb_step;
+    unsigned char* dst = sm.buf[buf];
 #pragma unroll
-    for (int j = 0; j < kStageRounds; ++j) {
-      const int piece = tid + kThreads * j;
-      if (j < kStageRounds - 1 || tid < kStageTail) {
-        const unsigned char* src = piece * 16 < kKQBytes ? kqb + piece * 16
-                                                         : vbb + (piece * 16 - kKQBytes);
-        lds_dma16(src, sm.buf[buf] + (kThreads * j + 64 * w) * 16);
-      }
-    }
+    for (int j = 0; j < kKQRounds; ++j)
+      lds_dma16(kqb + (kThreads * j + tid) * 16, dst + (kThreads * j + 64 * w) * 16);
     const int t0 = seq_start + ci * kC;
     const int len = min(kC, seq_len - ci * kC);
-    const uint16_t* vcol = v_head + static_cast<int64_t>(t0) * p.vs;
+    const uint16_t* vrow0 = v_head + static_cast<int64_t>(t0) * p.vs;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = min(16 * (i >> 2) + 4 * grp + (i & 3), len - 1);
-      vraw[i] = vcol[static_cast<int64_t>(r) * p.vs];
+    for (int j = 0; j < kStageRounds - kKQRounds; ++j) {
+      const int q = kThreads * j + tid;             // piece index after the K/Q blob
+      unsigned char* d = dst + kKQBytes + (kThreads * j + 64 * w) * 16;
+      if (q < kVBPieces) {
+        lds_dma16(vbb + q * 16, d);
+      } else if (q < kVBPieces + kVTilePieces) {
+        const int vp = q - kVBPieces;
+        const int r = min(vp >> 3, len - 1);          // rows past the end re-read the last
+        lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp & 7) * 8, d);
+      }
     }
   };
 
@@ -417,21 +424,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
   // the top of each chunk only covers work issued a whole chunk earlier.
   floatx4 Oprev[4];
   int o_t0 = 0, o_len = 0;
+  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
   auto store_o = [&]() {
-    float* ocol = p.o + static_cast<int64_t>(o_t0) * p.Hv * kD + h * kD + dvc;
+    float* obase = p.o + static_cast<int64_t>(o_t0) * o_rs + h * kD;
+    if (o_len == kC) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      if (o_len == kC) {
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          ocol[static_cast<int64_t>(16 * tb + 4 * grp + e) * p.Hv * kD] = Oprev[tb][e];
-      } else {
+          obase[static_cast<uint32_t>((16 * tb + 4 * grp + e) * o_rs + dvc)] = Oprev[tb][e];
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * tb + 4 * grp + e;
-          if (i < o_len) ocol[static_cast<int64_t>(i) * p.Hv * kD] = Oprev[tb][e];
+          if (i < o_len) obase[static_cast<uint32_t>(i * o_rs + dvc)] = Oprev[tb][e];
         }
-      }
     }
   };
 
@@ -447,17 +456,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     auto table = [&](int tab, int tb) {
       return *reinterpret_cast<const floatx4*>(B + kKQBytes + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
     };
+    const uint16_t* vtile = reinterpret_cast<const uint16_t*>(B + kKQBytes + kVBytes);
 
     // this chunk's copy (and everything older) has landed; the other buffer's
     // readers (chunk ci - 1) are done
     dma_barrier();
     if (ci > 0) store_o();
-    float vv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = 16 * (i >> 2) + 4 * grp + (i & 3);
-      vv[i] = tok < len ? bf16_to_f32(static_cast<uint16_t>(vraw[i])) : 0.f;
-    }
     if (ci + 1 < n_chunks) stage(ci + 1, (ci + 1) & 1);
 
     // B operands of S0^T over 32-row dk blocks, straight from registers.
@@ -470,10 +474,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     for (int tb = 0; tb < 4; ++tb) {
       X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
       QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        X[tb] = mfma32(frag(tb * 4 + kb), sB[kb], X[tb]);
-        QS[tb] = mfma32(frag(16 + tb * 4 + kb), sB[kb], QS[tb]);
+    for (int kb = 0; kb < 4; ++kb) {
+      half8 fk[4], fq[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        fk[tb] = frag(tb * 4 + kb);
+        fq[tb] = frag(16 + tb * 4 + kb);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        X[tb] = mfma32(fk[tb], sB[kb], X[tb]);
+        QS[tb] = mfma32(fq[tb], sB[kb], QS[tb]);
       }
     }
 
@@ -484,7 +497,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
       const floatx4 bt = table(0, tb);
       const floatx4 bg = table(1, tb);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) R[tb][e] = bt[e] * vv[4 * tb + e] - bg[e] * X[tb][e];
+      for (int e = 0; e < 4; ++e) {
+        const float vv = bf16_to_f32(vtile[(16 * tb + 4 * grp + e) * kDvPerWg + 16 * w + col]);
+        R[tb][e] = bt[e] * vv - bg[e] * X[tb][e];
+      }
     }
 
     // U by blockwise forward substitution
@@ -527,13 +543,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     const half8 d23 = to_half8(DU[2], DU[3]);
     const float gl = *reinterpret_cast<const float*>(B + kKQBytes + kOffGL);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      floatx4 s = sT[dt];
+    for (int dh = 0; dh < 2; ++dh) {
+      half8 ft[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] *= gl;
-      s = mfma32(frag(32 + dt * 2 + 0), d01, s);
-      s = mfma32(frag(32 + dt * 2 + 1), d23, s);
-      sT[dt] = s;
+      for (int i = 0; i < 8; ++i) ft[i] = frag(32 + dh * 8 + i);
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        const int dt = dh * 4 + d4;
+        floatx4 s = sT[dt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] *= gl;
+        s = mfma32(ft[2 * d4], d01, s);
+        s = mfma32(ft[2 * d4 + 1], d23, s);
+        sT[dt] = s;
+      }
     }
   }
 
