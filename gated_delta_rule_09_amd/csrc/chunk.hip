@@ -26,8 +26,8 @@
 //   Chunks come from the varlen chunk table, so they restart at every sequence
 //   start.
 //
-//   scan (one work-group per sequence x value head x half of the value
-//   channels): the sequential part.  Each of the four waves carries the
+//   scan (one work-group per sequence x value head x quarter of the value
+//   channels): the sequential part.  Each of the two waves carries the
 //   16 x 128 slice of S^T for its 16 value channels in MFMA accumulator
 //   registers across all chunks.  Per chunk the work-group copies the chunk's
 //   fragments into LDS with 16-byte loads issued one chunk ahead, and each wave
@@ -49,9 +49,15 @@ namespace {
 
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
-constexpr int kThreads = 256;
-constexpr int kDvPerWg = 64;      // value channels per scan work-group
-constexpr int kHalves = kD / kDvPerWg;
+constexpr int kThreads = 256;    // prep work-group
+// Scan work-group: two compute waves (16 value channels each) and two loader
+// waves that copy the next chunk into LDS and store the previous chunk's O.
+constexpr int kScanComputeWaves = 2;
+constexpr int kScanLoaderWaves = 2;
+constexpr int kScanThreads = 64 * (kScanComputeWaves + kScanLoaderWaves);
+constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
+constexpr int kDvPerWg = 16 * kScanComputeWaves;   // value channels per scan work-group
+constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value head
 
 // ---- fragment layout in the workspace -------------------------------------
 // An A32 fragment of a 16 x 32 block holds, for lane l (row l % 16, group
@@ -73,16 +79,18 @@ constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gam
 constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
 constexpr int kVBytes = kOffGL + 256;                 // 12544
 // Per chunk the scan stages [K/Q/K^T blob | value-head blob | V tile] in LDS,
-// where the V tile is this work-group's 64 value channels of the chunk's 64
-// tokens, row-major bf16 (128 bytes per token).
-constexpr int kVTileBytes = kC * kDvPerWg * 2;                          // 8192
-constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;           // 69888
-constexpr int kStagePieces = kStageBytes / 16;                          // 4368
-constexpr int kStageRounds = (kStagePieces + kThreads - 1) / kThreads;  // 18
-constexpr int kKQRounds = kKQBytes / (16 * kThreads);                   // 12
-constexpr int kVBPieces = kVBytes / 16;                                 // 784
-constexpr int kVTilePieces = kVTileBytes / 16;                          // 512
-static_assert(kKQBytes % (16 * kThreads) == 0, "K/Q blob is whole copy rounds");
+// where the V tile is this work-group's value channels of the chunk's 64
+// tokens, row-major bf16 (2 kDvPerWg bytes per token).
+constexpr int kVTileBytes = kC * kDvPerWg * 2;                                  // 4096
+constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 65792
+constexpr int kStagePieces = kStageBytes / 16;                                  // 4112
+constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 33
+constexpr int kKQRounds = kKQBytes / (16 * kLoaderThreads);                     // 24
+constexpr int kVBPieces = kVBytes / 16;                                         // 784
+constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
+constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
+static_assert(kKQBytes % (16 * kLoaderThreads) == 0, "K/Q blob is whole copy rounds");
+static_assert((kC * kDvPerWg) % (4 * kLoaderThreads) == 0, "O tile is whole store rounds");
 
 static_assert(kStageBytes % 16 == 0, "stage size");
 
@@ -327,18 +335,21 @@ struct ScanParams {
   int n_chain_groups;         // n_seqs * Hk
 };
 
-// Two stage buffers: the chunk being computed and the one being copied in.
+// Two stage buffers (the chunk being computed, the one being copied in) and two
+// O tiles (the chunk being computed, the one being stored).
+constexpr int kOTileFloats = kC * kDvPerWg;
 struct __align__(16) ScanSmem {
   unsigned char buf[2][kStageBytes];
+  float obuf[2][kOTileFloats];
 };
 
-__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
+__global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams p) {
   __shared__ ScanSmem sm;
 
-  // ---- block id -> (sequence rank, value head, value half) -----------------
-  // Chains sharing a key head (group * kHalves of them) get block ids that are
+  // ---- block id -> (sequence rank, value head, value quarter) --------------
+  // Chains sharing a key head (group * kParts of them) get block ids that are
   // congruent mod 8, i.e. land on the same XCD and share fragments through L2.
-  const int members = p.group * kHalves;
+  const int members = p.group * kParts;
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
@@ -347,16 +358,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
   if (gi >= p.n_chain_groups) return;
   const int rank = gi / p.Hk;
   const int kh = gi - rank * p.Hk;
-  const int h = kh * p.group + member / kHalves;
-  const int half = member % kHalves;
+  const int h = kh * p.group + member / kParts;
+  const int part = member % kParts;
   const int n = p.order ? p.order[rank] : rank;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int dvc = half * kDvPerWg + 16 * w + col;   // this lane's value channel
+  const bool compute = w < kScanComputeWaves;
 
   int seq_start, seq_len, chunk0;
   if (p.cu) {
@@ -370,7 +379,78 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
   }
   const int n_chunks = (seq_len + kC - 1) / kC;
 
-  // ---- initial state slice: S^T tiles, dk rows 16dt + 4grp + e, column dvc --
+  if (!compute) {
+    // ---- loader waves: copy the stage of chunk ci + 1 into LDS and store the
+    // O tile of chunk ci - 1 while the compute waves work on chunk ci --------
+    const int lt = tid - 64 * kScanComputeWaves;          // 0 .. kLoaderThreads - 1
+    const int lw = w - kScanComputeWaves;
+    const unsigned char* kq_head = p.kq + static_cast<int64_t>(kh) * kKQBytes;
+    const unsigned char* vb_head = p.vb + static_cast<int64_t>(h) * kVBytes;
+    const int64_t kq_step = static_cast<int64_t>(p.Hk) * kKQBytes;
+    const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
+    const uint16_t* v_head = p.v + h * kD + part * kDvPerWg;
+    const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
+    float* o_head = p.o + h * kD + part * kDvPerWg;
+
+    // Piece i of the stage is its byte 16 i: the K/Q/K^T blob, the value-head
+    // blob, then the V tile (token i / kVPiecesPerRow, channels
+    // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDvPerWg).
+    auto stage = [&](int ci) {
+      const int cb = chunk0 + ci;
+      const unsigned char* kqb = kq_head + cb * kq_step;
+      const unsigned char* vbb = vb_head + cb * vb_step;
+      unsigned char* dst = sm.buf[ci & 1];
+#pragma unroll
+      for (int j = 0; j < kKQRounds; ++j)
+        lds_dma16(kqb + (kLoaderThreads * j + lt) * 16, dst + (kLoaderThreads * j + 64 * lw) * 16);
+      const int len = min(kC, seq_len - ci * kC);
+      const uint16_t* vrow0 = v_head + static_cast<int64_t>(seq_start + ci * kC) * p.vs;
+#pragma unroll
+      for (int j = 0; j < kStageRounds - kKQRounds; ++j) {
+        const int q = kLoaderThreads * j + lt;       // piece index after the K/Q blob
+        unsigned char* d = dst + kKQBytes + (kLoaderThreads * j + 64 * lw) * 16;
+        if (q < kVBPieces) {
+          lds_dma16(vbb + q * 16, d);
+        } else if (q < kVBPieces + kVTilePieces) {
+          const int vp = q - kVBPieces;
+          const int r = min(vp / kVPiecesPerRow, len - 1);   // rows past the end re-read the last
+          lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % kVPiecesPerRow) * 8, d);
+        }
+      }
+    };
+    // O tile of chunk ci: 16 bytes per lane, 8 lanes per token row
+    auto store_o = [&](int ci) {
+      const int len = min(kC, seq_len - ci * kC);
+      const float* src = sm.obuf[ci & 1];
+      float* dst = o_head + static_cast<int64_t>(seq_start + ci * kC) * o_rs;
+#pragma unroll
+      for (int j = 0; j < kOTileFloats / (4 * kLoaderThreads); ++j) {
+        const int i = kLoaderThreads * j + lt;
+        const int r = i / (kDvPerWg / 4);
+        const int c4 = (i % (kDvPerWg / 4)) * 4;
+        const floatx4 val = *reinterpret_cast<const floatx4*>(src + r * kDvPerWg + c4);
+        if (r < len) *reinterpret_cast<floatx4*>(dst + r * o_rs + c4) = val;
+      }
+    };
+
+    if (n_chunks > 0) stage(0);
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      dma_barrier();                       // stage ci landed, O tile ci - 1 written
+      if (ci + 1 < n_chunks) stage(ci + 1);
+      if (ci > 0) store_o(ci - 1);
+    }
+    lds_barrier();                         // O tile of the last chunk written
+    if (n_chunks > 0) store_o(n_chunks - 1);
+    return;
+  }
+
+  // ---- compute waves ---------------------------------------------------------
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int dvw = 16 * w + col;                        // channel inside the work-group
+  const int dvc = part * kDvPerWg + dvw;               // this lane's value channel
+
+  // initial state slice: S^T tiles, dk rows 16dt + 4grp + e, column dvc
   floatx4 sT[8];
   const int64_t sbase = ((static_cast<int64_t>(n) * p.Hv + h) * kD + dvc) * kD;
   if (p.h0) {
@@ -383,72 +463,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) sT[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // The stage of chunk ci + 1 is copied straight into the other LDS buffer
-  // (global_load_lds: lane l of a wave writes 16 bytes at the wave's base +
-  // 16 l) while chunk ci is computed.  Piece i is byte 16 i of the stage:
-  // K/Q/K^T blob (rounds 0..11), value-head blob (784 pieces), then the V tile
-  // (512 pieces: token r, channels 8 (i % 8) .. +7 of this work-group's 64).
-  const unsigned char* kq_head = p.kq + static_cast<int64_t>(kh) * kKQBytes;
-  const unsigned char* vb_head = p.vb + static_cast<int64_t>(h) * kVBytes;
-  const int64_t kq_step = static_cast<int64_t>(p.Hk) * kKQBytes;
-  const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
-  const uint16_t* v_head = p.v + h * kD + half * kDvPerWg;
-
-  auto stage = [&](int ci, int buf) {
-    const int cb = chunk0 + ci;
-    const unsigned char* kqb = kq_head + cb * kq_step;
-    const unsigned char* vbb = vb_head + cb * vb_step;
-    unsigned char* dst = sm.buf[buf];
-#pragma unroll
-    for (int j = 0; j < kKQRounds; ++j)
-      lds_dma16(kqb + (kThreads * j + tid) * 16, dst + (kThreads * j + 64 * w) * 16);
-    const int t0 = seq_start + ci * kC;
-    const int len = min(kC, seq_len - ci * kC);
-    const uint16_t* vrow0 = v_head + static_cast<int64_t>(t0) * p.vs;
-#pragma unroll
-    for (int j = 0; j < kStageRounds - kKQRounds; ++j) {
-      const int q = kThreads * j + tid;             // piece index after the K/Q blob
-      unsigned char* d = dst + kKQBytes + (kThreads * j + 64 * w) * 16;
-      if (q < kVBPieces) {
-        lds_dma16(vbb + q * 16, d);
-      } else if (q < kVBPieces + kVTilePieces) {
-        const int vp = q - kVBPieces;
-        const int r = min(vp >> 3, len - 1);          // rows past the end re-read the last
-        lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp & 7) * 8, d);
-      }
-    }
-  };
-
-  // O of the previous chunk, stored after the next barrier so that the wait at
-  // the top of each chunk only covers work issued a whole chunk earlier.
-  floatx4 Oprev[4];
-  int o_t0 = 0, o_len = 0;
-  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-  auto store_o = [&]() {
-    float* obase = p.o + static_cast<int64_t>(o_t0) * o_rs + h * kD;
-    if (o_len == kC) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          obase[static_cast<uint32_t>((16 * tb + 4 * grp + e) * o_rs + dvc)] = Oprev[tb][e];
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * tb + 4 * grp + e;
-          if (i < o_len) obase[static_cast<uint32_t>(i * o_rs + dvc)] = Oprev[tb][e];
-        }
-    }
-  };
-
-  if (n_chunks > 0) stage(0, 0);
+  // Nothing may be pending at the loop header: the compiler's wait insertion
+  // would otherwise keep a vmcnt(0) inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int ci = 0; ci < n_chunks; ++ci) {
-    const int t0 = seq_start + ci * kC;
-    const int len = min(kC, seq_len - ci * kC);
     const unsigned char* B = sm.buf[ci & 1];
     auto frag = [&](int f) { return *reinterpret_cast<const half8*>(B + f * kFrag + lane * 16); };
     auto frag16 = [&](int off) { return *reinterpret_cast<const half4*>(B + kKQBytes + off + lane * 8); };
@@ -457,18 +476,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
       return *reinterpret_cast<const floatx4*>(B + kKQBytes + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
     };
     const uint16_t* vtile = reinterpret_cast<const uint16_t*>(B + kKQBytes + kVBytes);
+    float* obuf = sm.obuf[ci & 1];
 
-    // this chunk's copy (and everything older) has landed; the other buffer's
-    // readers (chunk ci - 1) are done
-    dma_barrier();
-    if (ci > 0) store_o();
-    if (ci + 1 < n_chunks) stage(ci + 1, (ci + 1) & 1);
+    dma_barrier();                         // this chunk's stage is in LDS
 
     // B operands of S0^T over 32-row dk blocks, straight from registers.
     half8 sB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
 
+    half8 fk[16], fq[16];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      fk[f] = frag(f);
+      fq[f] = frag(16 + f);
+    }
     floatx4 X[4], QS[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -476,19 +498,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
       QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      half8 fk[4], fq[4];
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        fk[tb] = frag(tb * 4 + kb);
-        fq[tb] = frag(16 + tb * 4 + kb);
-      }
+      for (int tb = 0; tb < 4; ++tb) X[tb] = mfma32(fk[tb * 4 + kb], sB[kb], X[tb]);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        X[tb] = mfma32(fk[tb], sB[kb], X[tb]);
-        QS[tb] = mfma32(fq[tb], sB[kb], QS[tb]);
-      }
-    }
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + kb], sB[kb], QS[tb]);
 
     // R = b V - b gamma X   (rows = tokens 16tb + 4grp + e, column dvc)
     floatx4 R[4];
@@ -498,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
       const floatx4 bg = table(1, tb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float vv = bf16_to_f32(vtile[(16 * tb + 4 * grp + e) * kDvPerWg + 16 * w + col]);
+        const float vv = bf16_to_f32(vtile[(16 * tb + 4 * grp + e) * kDvPerWg + dvw]);
         R[tb][e] = bt[e] * vv - bg[e] * X[tb][e];
       }
     }
@@ -517,20 +533,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     U[3] = mfma16(frag16(kOffT + 3 * kFrag16), to_half4(rhs), z4);
     const half8 u23 = to_half8(U[2], U[3]);
 
-    // O = scale gamma Q S0^T + P U  (stored at the start of the next chunk)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const floatx4 sg = table(2, tb);
-      floatx4 O;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = sg[e] * QS[tb][e];
-      O = mfma32(vfrag(kOffP + (tb < 2 ? tb : 2 * tb - 2) * kFrag), u01, O);
-      if (tb >= 2) O = mfma32(vfrag(kOffP + (2 * tb - 1) * kFrag), u23, O);
-      Oprev[tb] = O;
-    }
-    o_t0 = t0;
-    o_len = len;
-
     // S^T <- gamma_L S^T + K^T (D U)
     floatx4 DU[4];
 #pragma unroll
@@ -542,25 +544,34 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(ScanParams p) {
     const half8 d01 = to_half8(DU[0], DU[1]);
     const half8 d23 = to_half8(DU[2], DU[3]);
     const float gl = *reinterpret_cast<const float*>(B + kKQBytes + kOffGL);
+    half8 ft[16];
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      half8 ft[8];
+    for (int i = 0; i < 16; ++i) ft[i] = frag(32 + i);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ft[i] = frag(32 + dh * 8 + i);
+    for (int dt = 0; dt < 8; ++dt) {
+      floatx4 s = sT[dt];
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) {
-        const int dt = dh * 4 + d4;
-        floatx4 s = sT[dt];
+      for (int e = 0; e < 4; ++e) s[e] *= gl;
+      s = mfma32(ft[2 * dt], d01, s);
+      s = mfma32(ft[2 * dt + 1], d23, s);
+      sT[dt] = s;
+    }
+
+    // O = scale gamma Q S0^T + P U  -> LDS tile, stored by the loader waves
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] *= gl;
-        s = mfma32(ft[2 * d4], d01, s);
-        s = mfma32(ft[2 * d4 + 1], d23, s);
-        sT[dt] = s;
-      }
+    for (int tb = 0; tb < 4; ++tb) {
+      const floatx4 sg = table(2, tb);
+      floatx4 O;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) O[e] = sg[e] * QS[tb][e];
+      O = mfma32(vfrag(kOffP + (tb < 2 ? tb : 2 * tb - 2) * kFrag), u01, O);
+      if (tb >= 2) O = mfma32(vfrag(kOffP + (2 * tb - 1) * kFrag), u23, O);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) obuf[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = O[e];
     }
   }
+  lds_barrier();                           // matches the loaders' final barrier
 
-  if (n_chunks > 0) store_o();
   if (p.hT) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -621,8 +632,8 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;
   sp.n_chain_groups = n_seqs * Hk;
-  const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kHalves;
-  hipLaunchKernelGGL(chunk_scan_kernel, dim3(blocks), dim3(kThreads), 0, stream, sp);
+  const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kParts;
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(blocks), dim3(kScanThreads), 0, stream, sp);
   return hipGetLastError();
 }
 
