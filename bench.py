@@ -10,16 +10,24 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm;
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
-`roofline` covers the prefill kernel: algorithmic bytes per launch over the
-launch duration measured with HIP events on the launch stream, against the
-8 TB/s HBM3E peak (the kernel's arithmetic intensity, ~136 flop/B, is below the
-MFMA ridge); `mfma` gives the same launch against the 2.5 PFLOP/s dense fp16/bf16
-MFMA peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded prefix of the
-same prefill input on this host's cores.
+`roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
+kernel, then the sequential scan kernel, back to back on one stream):
+algorithmic bytes per launch over the launch duration measured with HIP events
+on the launch stream, against the 8 TB/s HBM3E peak (the arithmetic intensity,
+~136 flop/B, is below the MFMA ridge); `mfma` gives the same launch against the
+2.5 PFLOP/s dense fp16/bf16 MFMA peak.  `traffic` is the HBM bytes per launch
+that rocprofv3's FETCH_SIZE + WRITE_SIZE counters recorded (scaled by the
+counters' reading for a plain 1 GiB copy), taken from profiles/ and reported
+only while the prefill source is the one they were taken on.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded prefix of the same prefill input on this
+host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,...]
+(`--legs copy` adds a plain 1 GiB device copy, the calibration kernel for the
+HBM byte counters.)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -73,9 +81,12 @@ def leg_prefill(args, ops, synth, torch):
     q, k, v, g, b, h0 = ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], ci["h0"]
     o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
     fs = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_bytes(1, T, HK, HV), dtype=torch.uint8,
+                     device="cuda")
 
     def step():
-        ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0, final_state=fs, o=o, n_seqs=1)
+        ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0, final_state=fs, o=o, n_seqs=1,
+                          workspace=ws)
 
     ev, wall = time_leg(step, args.steps, args.warmup)
     bytes_launch = T * BYTES_PER_TOKEN + 2 * STATE_BYTES
@@ -162,6 +173,42 @@ def leg_varlen(args, ops, synth, torch):
     return res
 
 
+def leg_copy(args, torch):
+    """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30
+    bytes each, the reference for scaling the HBM byte counters."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ev, wall = time_leg(lambda: dst.copy_(src), max(2, args.steps // 4), 1)
+    log(f"[copy] 1 GiB copy {ev:.3f} ms, {2 * n / (ev * 1e-3) / 1e9:.0f} GB/s")
+    return dict(bytes=2 * n, event_ms=ev)
+
+
+PREFILL_SOURCES = ("gated_delta_rule_09_amd/csrc/chunk.hip", "gated_delta_rule_09_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T65536_traffic.json")
+
+
+def prefill_source_sha():
+    h = hashlib.sha256()
+    for rel in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter runs, or None
+    when they were taken on different prefill sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != prefill_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(ci, seconds, torch):
     """The fp64 oracle on a prefix of the prefill input, all 48 heads."""
     import numpy as np
@@ -200,7 +247,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mixer shards by heads or sequences with no "
-              "exchange, and this build runs and reports a single MI355X (--gpus 1).",
+              "exchange; the figures here are for a single MI355X (--gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -219,6 +266,8 @@ def main():
         out["mixer"] = leg_mixer(args, ops, synth, torch)
     if "varlen" in legs:
         out["varlen"] = leg_varlen(args, ops, synth, torch)
+    if "copy" in legs:
+        out["copy"] = leg_copy(args, torch)
 
     pre = out.get("prefill")
     line = {
@@ -242,7 +291,8 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": round(pre["hbm_gbps"], 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(pre["hbm_gbps"] / HBM_PEAK_GBPS, 4),
-                            "traffic": None, "kernel": "chunk_fwd_kernel",
+                            "traffic": measured_traffic(),
+                            "kernel": "chunk_prep_kernel + chunk_scan_kernel (one gdn_chunk_fwd)",
                             "launch_ms": round(pre["event_ms"], 4)}
         line["mfma"] = {"achieved": round(pre["mfma_tflops"], 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}

@@ -469,71 +469,102 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const unsigned char* B = sm.buf[ci & 1];
+    const unsigned char* VB = B + kKQBytes;
     auto frag = [&](int f) { return *reinterpret_cast<const half8*>(B + f * kFrag + lane * 16); };
-    auto frag16 = [&](int off) { return *reinterpret_cast<const half4*>(B + kKQBytes + off + lane * 8); };
-    auto vfrag = [&](int off) { return *reinterpret_cast<const half8*>(B + kKQBytes + off + lane * 16); };
+    auto frag16 = [&](int off) { return *reinterpret_cast<const half4*>(VB + off + lane * 8); };
+    auto vfrag = [&](int off) { return *reinterpret_cast<const half8*>(VB + off + lane * 16); };
     auto table = [&](int tab, int tb) {
-      return *reinterpret_cast<const floatx4*>(B + kKQBytes + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
+      return *reinterpret_cast<const floatx4*>(VB + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
     };
-    const uint16_t* vtile = reinterpret_cast<const uint16_t*>(B + kKQBytes + kVBytes);
+    const uint16_t* vtile = reinterpret_cast<const uint16_t*>(VB + kVBytes);
     float* obuf = sm.obuf[ci & 1];
 
+    // The chunk runs in phases separated by scheduling fences; each phase
+    // issues the LDS reads of the next one, so read latency hides behind the
+    // products of the current phase.
     dma_barrier();                         // this chunk's stage is in LDS
 
-    // B operands of S0^T over 32-row dk blocks, straight from registers.
+    // phase 0: K fragments; B operands of S0^T straight from registers
+    half8 fk[16];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fk[f] = frag(f);
     half8 sB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    half8 fk[16], fq[16];
+    // phase 1: Q fragments | X = K S0^T
+    half8 fq[16];
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      fk[f] = frag(f);
-      fq[f] = frag(16 + f);
-    }
-    floatx4 X[4], QS[4];
+    for (int f = 0; f < 16; ++f) fq[f] = frag(16 + f);
+    floatx4 X[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int tb = 0; tb < 4; ++tb) X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) X[tb] = mfma32(fk[tb * 4 + kb], sB[kb], X[tb]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // phase 2: V, b, b gamma, T_bb, -A | QS = Q S0^T
+    float vv[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[tb][e] = bf16_to_f32(vtile[(16 * tb + 4 * grp + e) * kDvPerWg + dvw]);
+    floatx4 bt[4], bg[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      bt[tb] = table(0, tb);
+      bg[tb] = table(1, tb);
+    }
+    half4 tT[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tT[b] = frag16(kOffT + b * kFrag16);
+    const half4 an10 = frag16(kOffAn10);
+    const half8 an2 = vfrag(kOffAn2);
+    const half8 an3 = vfrag(kOffAn3);
+    const half4 an32 = frag16(kOffAn32);
+    floatx4 QS[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + kb], sB[kb], QS[tb]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // R = b V - b gamma X   (rows = tokens 16tb + 4grp + e, column dvc)
+    // phase 3: K^T fragments | R = b V - b gamma X, U by blockwise forward
+    // substitution (rows = tokens 16tb + 4grp + e, column dvc)
+    half8 ft[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ft[i] = frag(32 + i);
     floatx4 R[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const floatx4 bt = table(0, tb);
-      const floatx4 bg = table(1, tb);
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float vv = bf16_to_f32(vtile[(16 * tb + 4 * grp + e) * kDvPerWg + dvw]);
-        R[tb][e] = bt[e] * vv - bg[e] * X[tb][e];
-      }
-    }
-
-    // U by blockwise forward substitution
+      for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * vv[tb][e] - bg[tb][e] * X[tb][e];
     const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
     floatx4 U[4];
-    U[0] = mfma16(frag16(kOffT + 0 * kFrag16), to_half4(R[0]), z4);
-    floatx4 rhs = mfma16(frag16(kOffAn10), to_half4(U[0]), R[1]);
-    U[1] = mfma16(frag16(kOffT + 1 * kFrag16), to_half4(rhs), z4);
+    U[0] = mfma16(tT[0], to_half4(R[0]), z4);
+    floatx4 rhs = mfma16(an10, to_half4(U[0]), R[1]);
+    U[1] = mfma16(tT[1], to_half4(rhs), z4);
     const half8 u01 = to_half8(U[0], U[1]);
-    rhs = mfma32(vfrag(kOffAn2), u01, R[2]);
-    U[2] = mfma16(frag16(kOffT + 2 * kFrag16), to_half4(rhs), z4);
-    rhs = mfma32(vfrag(kOffAn3), u01, R[3]);
-    rhs = mfma16(frag16(kOffAn32), to_half4(U[2]), rhs);
-    U[3] = mfma16(frag16(kOffT + 3 * kFrag16), to_half4(rhs), z4);
+    rhs = mfma32(an2, u01, R[2]);
+    U[2] = mfma16(tT[2], to_half4(rhs), z4);
+    rhs = mfma32(an3, u01, R[3]);
+    rhs = mfma16(an32, to_half4(U[2]), rhs);
+    U[3] = mfma16(tT[3], to_half4(rhs), z4);
     const half8 u23 = to_half8(U[2], U[3]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // S^T <- gamma_L S^T + K^T (D U)
+    // phase 4: P, scale gamma, D, gamma_L | S^T <- gamma_L S^T + K^T (D U)
+    half8 fp[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) fp[f] = vfrag(kOffP + f * kFrag);
+    floatx4 sg[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) sg[tb] = table(2, tb);
     floatx4 DU[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -543,10 +574,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     }
     const half8 d01 = to_half8(DU[0], DU[1]);
     const half8 d23 = to_half8(DU[2], DU[3]);
-    const float gl = *reinterpret_cast<const float*>(B + kKQBytes + kOffGL);
-    half8 ft[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ft[i] = frag(32 + i);
+    const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       floatx4 s = sT[dt];
@@ -556,16 +584,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       s = mfma32(ft[2 * dt + 1], d23, s);
       sT[dt] = s;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // O = scale gamma Q S0^T + P U  -> LDS tile, stored by the loader waves
+    // phase 5: O = scale gamma Q S0^T + P U -> LDS tile, stored by the loaders
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const floatx4 sg = table(2, tb);
       floatx4 O;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = sg[e] * QS[tb][e];
-      O = mfma32(vfrag(kOffP + (tb < 2 ? tb : 2 * tb - 2) * kFrag), u01, O);
-      if (tb >= 2) O = mfma32(vfrag(kOffP + (2 * tb - 1) * kFrag), u23, O);
+      for (int e = 0; e < 4; ++e) O[e] = sg[tb][e] * QS[tb][e];
+      O = mfma32(fp[tb < 2 ? tb : 2 * tb - 2], u01, O);
+      if (tb >= 2) O = mfma32(fp[2 * tb - 1], u23, O);
 #pragma unroll
       for (int e = 0; e < 4; ++e) obuf[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = O[e];
     }
