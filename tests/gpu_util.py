@@ -2,8 +2,13 @@
 
 Tolerance (the mixer's accuracy bar, per output tensor): relative L2 error
 <= 1e-3 and max |got - ref| <= 5e-3 * max |ref|, against the fp64 oracle.
-bf16 outputs are compared on the bf16 grid: every element within one bf16 ulp
-of the oracle's rounded value (both sides round once, from fp32 vs fp64).
+bf16 outputs are held to the same tolerance and, in addition, compared on the
+bf16 grid: every element within one bf16 ulp of the oracle's rounded value
+(both sides round once, the kernel from fp32, the oracle from fp64), except
+where the kernel's fp32 arithmetic itself is off by more than that: a value
+that comes out of cancellation (a conv sum whose terms nearly cancel) carries
+an fp32 error of about 2^-24 of the cancelled terms, which can exceed one ulp
+of the small result.  Such elements must be within 2^-16 * max|ref| absolute.
 """
 import sys
 
@@ -65,11 +70,19 @@ def bf16_ulp(x):
     return 2.0 ** (e - 7)
 
 
+BF16_ABS_FLOOR = 2.0 ** -16
+
+
 def assert_bf16_within_1ulp(got, ref, name=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    assert_close(got, ref, name)
     d = np.abs(got - ref)
-    bad = d > bf16_ulp(ref) * 1.0000001
+    over = d > bf16_ulp(ref) * 1.0000001
+    mx = np.max(np.abs(ref)) if ref.size else 0.0
+    bad = over & (d > BF16_ABS_FLOOR * mx)
     frac = np.mean(got != ref) if got.size else 0.0
-    log(f"  {name}: bf16 mismatches {frac:.2e}, max |d|/ulp {np.max(d / bf16_ulp(ref)) if got.size else 0:.2f}")
+    log(f"  {name}: bf16 mismatches {frac:.2e}, over 1 ulp {int(over.sum())}, "
+        f"max |d|/ulp {np.max(d / bf16_ulp(ref)) if got.size else 0:.2f}, "
+        f"max |d| over 1 ulp / max|ref| {np.max(d[over]) / mx if over.any() else 0:.2e}")
     assert not np.any(bad), f"{name}: {int(bad.sum())} elements differ by more than 1 bf16 ulp"
