@@ -18,8 +18,10 @@
  *     "Delta-rule layers": 16 key heads / 48 value heads, head dim 128, causal
  *     conv of kernel 4 in front, gated RMS-norm after, recurrent state in fp32.
  *   - "Agnes-3.0-Flash Deep Dive: A 33B Hybrid-Attention Multimodal Model",
- *     section "Attention Layer Details": the delta rule erases before it
- *     writes, and a forget gate decays the state.
+ *     section "Attention Layer Details" (the same head geometry, conv, norm
+ *     and fp32 state), and its explanatory paragraph on the Gated Delta Rule
+ *     (after "Feed-Forward and Positional Encoding"): the delta rule erases
+ *     before it writes, and a forget gate decays the state.
  *   - Update rule:  S_t = S_{t-1} * a_t (I - b_t k_t k_t^T) + b_t v_t k_t^T,
  *                   o_t = scale * S_t q_t,  a_t = exp(g_t).
  *     S is dv x dk (row index = value channel), so S k is a dv-vector.

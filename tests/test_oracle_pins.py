@@ -333,3 +333,31 @@ def test_round_bf16_matches_torch_cast():
     got = oracle.round_bf16(x32.astype(np.float64))
     ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- chunk map
+
+@pytest.mark.parametrize("lens", [[5], [0], [64, 64], [65, 0, 1, 128, 63, 0, 200], [7, 7, 3, 7],
+                                  [300, 1, 64, 65, 129, 0, 0, 2]])
+def test_chunk_map_brute_force(lens):
+    """The varlen chunk map against a direct enumeration: every sequence cut into
+    64-token pieces from its own start (the last one partial), sequences ranked
+    longest first with ties broken by id."""
+    lens = np.asarray(lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    order, off, tab = oracle.chunk_map(cu)
+    ranked = sorted(range(len(lens)), key=lambda n: (-lens[n], n))
+    assert order.tolist() == ranked
+    rows, offs = [], [0]
+    for n, L in enumerate(lens):
+        start = int(cu[n])
+        for a in range(0, int(L), 64):
+            rows.append([n, start + a, min(64, int(L) - a)])
+        offs.append(len(rows))
+    assert off.tolist() == offs
+    assert tab.tolist() == rows
+    # each token belongs to exactly one chunk
+    covered = np.zeros(int(cu[-1]), dtype=np.int32)
+    for _, t0, ln in rows:
+        covered[t0:t0 + ln] += 1
+    assert np.all(covered == 1)
