@@ -189,10 +189,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T65536_traffic.json")
 
 
 def prefill_source_sha():
+    """Hash of the prefill sources' code: // comments and blank lines are
+    dropped, so a comment edit does not invalidate the counter figures."""
     h = hashlib.sha256()
     for rel in PREFILL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

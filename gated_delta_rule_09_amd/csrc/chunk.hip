@@ -27,14 +27,17 @@
 //   start.
 //
 //   scan (one work-group per sequence x value head x quarter of the value
-//   channels): the sequential part.  Each of the two waves carries the
-//   16 x 128 slice of S^T for its 16 value channels in MFMA accumulator
-//   registers across all chunks.  Per chunk the work-group copies the chunk's
-//   fragments into LDS with 16-byte loads issued one chunk ahead, and each wave
-//   runs  X = K S0^T and Q S0^T (B operand straight from the S^T registers),
+//   channels): the sequential part.  Two compute waves each carry the 16 x 128
+//   slice of S^T for their 16 value channels in MFMA accumulator registers
+//   across all chunks; two loader waves copy the next chunk's fragments and V
+//   tile into LDS (global_load_lds, one chunk ahead) and store the previous
+//   chunk's O tile from LDS, so the compute waves never issue a global memory
+//   instruction inside the loop.  Per chunk each compute wave runs
+//   X = K S0^T and Q S0^T (B operand straight from the S^T registers),
 //   R = b V - b gamma X, U by blockwise forward substitution
-//   (U_i = T_ii (R_i - sum_{j<i} A_ij U_j)), O = scale gamma Q S0^T + P U, and
-//   S^T <- gamma_L S^T + K^T (D U).
+//   (U_i = T_ii (R_i - sum_{j<i} A_ij U_j)), S^T <- gamma_L S^T + K^T (D U)
+//   and O = scale gamma Q S0^T + P U, in phases that each issue the LDS reads
+//   of the next phase.
 //
 // Only the fp32-valued operands are rounded to fp16 (S0, U, T_ii, A, P);
 // accumulation is fp32 throughout.  The per-chunk state never leaves the
