@@ -438,11 +438,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 
     if (n_chunks > 0) stage(0);
     for (int ci = 0; ci < n_chunks; ++ci) {
-      dma_barrier();                       // stage ci landed, O tile ci - 1 written
+      dma_barrier();                       // stage ci landed, O tile ci - 2 written
       if (ci + 1 < n_chunks) stage(ci + 1);
-      if (ci > 0) store_o(ci - 1);
+      if (ci > 1) store_o(ci - 2);
     }
-    lds_barrier();                         // O tile of the last chunk written
+    dma_barrier();                         // O tile n - 2 written, O n - 3 read
+    if (n_chunks > 1) store_o(n_chunks - 2);
+    lds_barrier();                         // O tile n - 1 written
     if (n_chunks > 0) store_o(n_chunks - 1);
     return;
   }
@@ -469,6 +471,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   // Nothing may be pending at the loop header: the compiler's wait insertion
   // would otherwise keep a vmcnt(0) inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
+  floatx4 Oprev[4];
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const unsigned char* B = sm.buf[ci & 1];
@@ -480,17 +483,24 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       return *reinterpret_cast<const floatx4*>(VB + kOffDecay + tab * 256 + (16 * tb + 4 * grp) * 4);
     };
     const uint16_t* vtile = reinterpret_cast<const uint16_t*>(VB + kVBytes);
-    float* obuf = sm.obuf[ci & 1];
 
     // The chunk runs in phases separated by scheduling fences; each phase
     // issues the LDS reads of the next one, so read latency hides behind the
     // products of the current phase.
     dma_barrier();                         // this chunk's stage is in LDS
 
-    // phase 0: K fragments; B operands of S0^T straight from registers
+    // phase 0: K fragments; B operands of S0^T straight from registers; the
+    // previous chunk's O tile (its products have long completed) to LDS
     half8 fk[16];
 #pragma unroll
     for (int f = 0; f < 16; ++f) fk[f] = frag(f);
+    if (ci > 0) {
+      float* ob = sm.obuf[(ci - 1) & 1];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = Oprev[tb][e];
+    }
     half8 sB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
@@ -589,7 +599,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 5: O = scale gamma Q S0^T + P U -> LDS tile, stored by the loaders
+    // phase 5: O = scale gamma Q S0^T + P U, kept in registers and written to
+    // the LDS tile at the start of the next chunk (stored by the loaders)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       floatx4 O;
@@ -597,11 +608,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       for (int e = 0; e < 4; ++e) O[e] = sg[tb][e] * QS[tb][e];
       O = mfma32(fp[tb < 2 ? tb : 2 * tb - 2], u01, O);
       if (tb >= 2) O = mfma32(fp[2 * tb - 1], u23, O);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) obuf[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = O[e];
+      Oprev[tb] = O;
     }
   }
-  lds_barrier();                           // matches the loaders' final barrier
+  lds_barrier();                           // the loaders are done with O tile n - 3
+  if (n_chunks > 0) {
+    float* ob = sm.obuf[(n_chunks - 1) & 1];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = Oprev[tb][e];
+  }
+  lds_barrier();                           // O tile n - 1 written
 
   if (p.hT) {
 #pragma unroll
