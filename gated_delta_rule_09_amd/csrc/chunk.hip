@@ -436,12 +436,48 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       }
     };
 
-    if (n_chunks > 0) stage(0);
-    for (int ci = 0; ci < n_chunks; ++ci) {
-      dma_barrier();                       // stage ci landed, O tile ci - 2 written
-      if (ci + 1 < n_chunks) stage(ci + 1);
-      if (ci > 1) store_o(ci - 2);
+    // L2 prefetch, two chunks ahead.  The copies are latency-bound (each CU
+    // keeps only so many line requests in flight), so they should hit L2.
+    // The `members` work-groups of a key head share its K/Q blob and the blobs
+    // of its value heads; member m pulls lines 64 m .. 64 m + 63 of that data
+    // (loader wave 0), and each work-group its own V rows (loader wave 1).  One
+    // dword per 128-byte line; the values go to `sink`, stored only under a
+    // condition that never holds.
+    const int kq_lines = kKQBytes / 128;
+    const int vb_lines = p.group * kVBytes / 128;
+    auto touch = [&](int ci) -> uint32_t {
+      const int cb = chunk0 + ci;
+      const unsigned char* a;
+      if (lw == 0) {
+        const int L = min(member * 64 + lane, kq_lines + vb_lines - 1);
+        a = L < kq_lines ? kq_head + cb * kq_step + L * 128
+                         : p.vb + (static_cast<int64_t>(cb) * p.Hv + kh * p.group) * kVBytes +
+                               (L - kq_lines) * 128;
+      } else {
+        const int r = min(lane, min(kC, seq_len - ci * kC) - 1);
+        a = reinterpret_cast<const unsigned char*>(
+            v_head + static_cast<int64_t>(seq_start + ci * kC + r) * p.vs);
+      }
+      return *reinterpret_cast<const uint32_t*>(a);
+    };
+    uint32_t sink = 0, tv = 0;
+
+    // Order per chunk: copies of chunk ci + 1, O stores, prefetch of chunk
+    // ci + 2.  The prefetch is the youngest memory operation, so the wait at
+    // the next barrier (vmcnt(1)) leaves only it in flight.
+    if (n_chunks > 0) {
+      stage(0);
+      tv = touch(min(1, n_chunks - 1));
     }
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (ci + 1 < n_chunks) stage(ci + 1);
+      sink ^= tv;                          // issued a chunk ago
+      if (ci > 1) store_o(ci - 2);
+      tv = touch(min(ci + 2, n_chunks - 1));
+    }
+    sink ^= tv;
+    if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
     dma_barrier();                         // O tile n - 2 written, O n - 3 read
     if (n_chunks > 1) store_o(n_chunks - 2);
     lds_barrier();                         // O tile n - 1 written
