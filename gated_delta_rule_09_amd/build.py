@@ -2,6 +2,11 @@
 
 Every source under csrc/ is compiled for gfx950 only, with packed-fp32 code
 generation disabled, and linked into gated_delta_rule_09_amd/libgdn.so.
+
+The build also checks that no kernel spills registers: the prefill scan is
+written to fit its registers, and a register allocation that spills vector
+registers into accumulator registers around its MFMA chains has produced wrong
+results on gfx950, so a spill is treated as a build error.
 """
 import concurrent.futures
 import glob
@@ -34,11 +39,30 @@ def _compile(src: str) -> str:
     return obj
 
 
+SPILL_MARKERS = ("Reload Reuse", "Spill", "Reload")
+
+
+def _check_no_spills(src: str) -> None:
+    """Compile `src` to gfx950 assembly and fail on any register spill or
+    reload the compiler annotates."""
+    asm = os.path.join(BUILD, os.path.basename(src) + ".s")
+    cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-S", src, "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    with open(asm) as f:
+        bad = [ln.strip() for ln in f if ";" in ln and any(m in ln.split(";", 1)[1] for m in SPILL_MARKERS)]
+    if bad:
+        raise RuntimeError(f"{os.path.basename(src)}: the compiler spilled registers "
+                           f"({len(bad)} spill/reload instructions, e.g. {bad[0]!r})")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
+        list(ex.map(_check_no_spills, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

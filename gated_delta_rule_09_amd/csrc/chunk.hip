@@ -101,16 +101,28 @@ static_assert(kStageBytes % 16 == 0, "stage size");
 constexpr int kKS = kD + 8;       // K, Q rows (halves)
 constexpr int kAS = kC + 8;       // -A, P rows (halves)
 constexpr int kTS = 16 + 8;       // T_bb rows (halves)
+constexpr int kHeadBatch = 3;     // value heads prepared together
 
-struct __align__(16) PrepSmem {
+// K and Q are only needed until the K/Q/K^T fragments and the Gram tiles are
+// formed; their space is then reused for the per-value-head matrices of a
+// batch of up to kHeadBatch value heads.
+struct PrepKQ {
   _Float16 K[kC * kKS];
   _Float16 Q[kC * kKS];
-  _Float16 An[kC * kAS];
-  _Float16 P[kC * kAS];
-  _Float16 T[4 * 16 * kTS];
-  float Ad[4 * 16 * 16];
-  float G[kC];
-  float bet[kC];
+};
+struct PrepHeads {
+  _Float16 An[kHeadBatch][kC * kAS];
+  _Float16 P[kHeadBatch][kC * kAS];
+  float Ad[kHeadBatch][4 * 16 * 16];
+  _Float16 T[kHeadBatch][4 * 16 * kTS];
+};
+struct __align__(16) PrepSmem {
+  union {
+    PrepKQ kq;
+    PrepHeads vh;
+  } u;
+  float G[kHeadBatch][kC];
+  float bet[kHeadBatch][kC];
 };
 
 struct PrepParams {
@@ -144,6 +156,58 @@ __device__ __forceinline__ void put8(unsigned char* dst, const half4 v) {
   *reinterpret_cast<half4*>(dst) = v;
 }
 
+// Gram tile t of the list (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1)
+// (3,2) (3,3): block row and block column.
+__host__ __device__ constexpr int gram_row(int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); }
+__host__ __device__ constexpr int gram_col(int t) { return t - (gram_row(t) * (gram_row(t) + 1)) / 2; }
+
+// Wave W's share of the elementwise step: its Gram tiles 5W .. 5W+4 of
+// [K K^T (10), Q K^T (10)] become, for each of the nb heads of the batch,
+//   K K^T, diagonal tile:   A  = strict_lower(b E * K K^T)      (fp32, LDS)
+//   K K^T, off-diagonal:   -A  = -(b E * K K^T)                 (fp16, LDS)
+//   Q K^T:                  P  = scale * lower(E * Q K^T)       (fp16, LDS)
+// with E_ij = exp(G_i - G_j).  Lane (col, grp) holds rows 4 grp .. +3 of
+// column col of a tile (MFMA accumulator layout).
+template <int W>
+__device__ __forceinline__ void prep_elementwise(PrepSmem& sm, const floatx4 (&gram)[5], int nb,
+                                                 int col, int grp, float scale) {
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    constexpr int kJobs = 5 * W;
+    const int job = kJobs + jj;
+    const bool isq = job >= 10;
+    const int t = isq ? job - 10 : job;
+    const int b = gram_row(t);
+    const int j = gram_col(t);
+    const int jc = 16 * j + col;
+    const int i0 = 16 * b + 4 * grp;
+#pragma unroll
+    for (int vh = 0; vh < kHeadBatch; ++vh) {
+      if (vh >= nb) break;
+      const floatx4 Gi = *reinterpret_cast<const floatx4*>(&sm.G[vh][i0]);
+      const float Gj = sm.G[vh][jc];
+      if (isq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = scale * __expf(Gi[e] - Gj) * gram[jj][e];
+          sm.u.vh.P[vh][(i0 + e) * kAS + jc] =
+              static_cast<_Float16>((b > j || jc <= i0 + e) ? v : 0.f);
+        }
+      } else {
+        const floatx4 Bi = *reinterpret_cast<const floatx4*>(&sm.bet[vh][i0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = Bi[e] * __expf(Gi[e] - Gj) * gram[jj][e];
+          if (b == j)
+            sm.u.vh.Ad[vh][(b * 16 + 4 * grp + e) * 16 + col] = (jc < i0 + e) ? a : 0.f;
+          else
+            sm.u.vh.An[vh][(i0 + e) * kAS + jc] = static_cast<_Float16>(-a);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
   const int kh = blockIdx.y;
@@ -161,23 +225,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     len = min(kC, p.seq_len - i * kC);
   }
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
 
+  // g and beta of the first head batch, one token per lane (wave w, head w);
+  // issued first so their latency overlaps the K/Q loads
+  auto load_gb = [&](int vh, float& gv, float& bv) {
+    const bool valid = lane < len;
+    const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + kh * p.group + vh;
+    gv = valid ? p.g[gi] : 0.f;
+    bv = valid ? p.beta[gi] : 0.f;
+  };
+  float gv = 0.f, bv = 0.f;
+  if (w < min(kHeadBatch, p.group)) load_gb(w, gv, bv);
+
   // ---- K, Q -> LDS (fp16), rows past the chunk end zeroed ------------------
+  // (64 rows x 16 pieces of 8 channels; all eight loads issued first)
+  uint4 kraw[4], qraw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int piece = tid + kThreads * j;       // 64 rows x 16 pieces of 8 channels
+    const int piece = tid + kThreads * j;
+    const int rr = min(piece >> 4, len - 1);
+    const int c8 = (piece & 15) * 8;
+    kraw[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
+    qraw[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int piece = tid + kThreads * j;
     const int r = piece >> 4;
     const int c8 = (piece & 15) * 8;
-    const int rr = min(r, len - 1);
-    const uint4 kb = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
-    const uint4 qb = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
     float fk[8], fq[8];
-    bf16x8_to_f32(kb, fk);
-    bf16x8_to_f32(qb, fq);
+    bf16x8_to_f32(kraw[j], fk);
+    bf16x8_to_f32(qraw[j], fq);
     half8 hk, hq;
     const bool ok = r < len;
 #pragma unroll
@@ -185,14 +267,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
       hk[i] = static_cast<_Float16>(ok ? fk[i] : 0.f);
       hq[i] = static_cast<_Float16>(ok ? fq[i] : 0.f);
     }
-    *reinterpret_cast<half8*>(&sm.K[r * kKS + c8]) = hk;
-    *reinterpret_cast<half8*>(&sm.Q[r * kKS + c8]) = hq;
-  }
-  // P tiles above the diagonal blocks that the fragments (0,0) and (2,1) cover
-  for (int i = tid; i < 2 * 256; i += kThreads) {
-    const int t = i >> 8, rr = (i >> 4) & 15, cc = i & 15;
-    const int r0 = t ? 32 : 0;
-    sm.P[(r0 + rr) * kAS + r0 + 16 + cc] = static_cast<_Float16>(0.f);
+    *reinterpret_cast<half8*>(&sm.u.kq.K[r * kKS + c8]) = hk;
+    *reinterpret_cast<half8*>(&sm.u.kq.Q[r * kKS + c8]) = hq;
   }
   lds_barrier();
 
@@ -203,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     const int f = w * 12 + j;
     half8 v;
     if (f < 32) {
-      const _Float16* X = f < 16 ? sm.K : sm.Q;
+      const _Float16* X = f < 16 ? sm.u.kq.K : sm.u.kq.Q;
       const int ff = f & 15;
       v = lds_a32(X, kKS, 16 * (ff >> 2) + col, 32 * (ff & 3), grp);
     } else {
@@ -211,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-        v[e] = sm.K[tok * kKS + 16 * dt + col];
+        v[e] = sm.u.kq.K[tok * kKS + 16 * dt + col];
       }
     }
     put16(kq + f * kFrag + lane * 16, v);
@@ -227,24 +303,24 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     const int t = job >= 10 ? job - 10 : job;
     const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
     const int j = t - (b * (b + 1)) / 2;
-    const _Float16* X = job >= 10 ? sm.Q : sm.K;
+    const _Float16* X = job >= 10 ? sm.u.kq.Q : sm.u.kq.K;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < kD; kb += 32)
-      acc = mfma32(lds_a32(X, kKS, 16 * b + col, kb, grp), lds_a32(sm.K, kKS, 16 * j + col, kb, grp), acc);
+      acc = mfma32(lds_a32(X, kKS, 16 * b + col, kb, grp), lds_a32(sm.u.kq.K, kKS, 16 * j + col, kb, grp), acc);
     gram[jj] = acc;
   }
+  lds_barrier();   // K and Q are no longer read: their space becomes the heads'
 
-  // ---- per value head of this key head -------------------------------------
-  for (int vh = 0; vh < p.group; ++vh) {
-    const int h = kh * p.group + vh;
-    unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
-    // decay tables: wave 0 scans g; everyone waits at the barrier below
-    if (w == 0) {
-      const bool valid = lane < len;
-      const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
-      const float gv = valid ? p.g[gi] : 0.f;
-      const float bv = valid ? p.beta[gi] : 0.f;
+  // ---- the key head's value heads, up to kHeadBatch at a time --------------
+  for (int vb0 = 0; vb0 < p.group; vb0 += kHeadBatch) {
+    const int nb = min(kHeadBatch, p.group - vb0);
+
+    // decay tables: wave w scans g of head vb0 + w (lane = token)
+    if (w < nb) {
+      if (vb0 > 0) load_gb(vb0 + w, gv, bv);
+      const int h = kh * p.group + vb0 + w;
+      unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
       float G = gv;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -253,8 +329,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
       }
       const float Glast = __shfl(G, 63, 64);
       const float gam = __expf(G);
-      sm.G[lane] = G;
-      sm.bet[lane] = bv;
+      sm.G[w][lane] = G;
+      sm.bet[w][lane] = bv;
       float* dec = reinterpret_cast<float*>(vb + kOffDecay);
       dec[lane] = bv;
       dec[64 + lane] = bv * gam;
@@ -262,63 +338,79 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
       dec[192 + lane] = __expf(Glast - G);
       if (lane == 0) *reinterpret_cast<float*>(vb + kOffGL) = __expf(Glast);
     }
-    lds_barrier();   // G, bet ready; previous head's readers done with An/P/T
-
-#pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int job = 5 * w + jj;
-      const bool isq = job >= 10;
-      const int t = isq ? job - 10 : job;
-      const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-      const int j = t - (b * (b + 1)) / 2;
-      const int jc = 16 * j + col;
-      const float Gj = sm.G[jc];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * b + 4 * grp + e;
-        const float E = __expf(sm.G[i] - Gj);
-        if (isq) {
-          sm.P[i * kAS + jc] = static_cast<_Float16>((jc <= i) ? p.scale * E * gram[jj][e] : 0.f);
-        } else {
-          const float a = (jc < i) ? sm.bet[i] * E * gram[jj][e] : 0.f;
-          if (b == j) sm.Ad[(b * 16 + 4 * grp + e) * 16 + col] = a;
-          else sm.An[i * kAS + jc] = static_cast<_Float16>(-a);
-        }
-      }
+    // P tiles above the diagonal blocks that the fragments (0,0) and (2,1)
+    // cover are zero
+    for (int i = tid; i < kHeadBatch * 2 * 256; i += kThreads) {
+      const int vh = i >> 9, t = (i >> 8) & 1, rr = (i >> 4) & 15, cc = i & 15;
+      const int r0 = t ? 32 : 0;
+      sm.u.vh.P[vh][(r0 + rr) * kAS + r0 + 16 + cc] = static_cast<_Float16>(0.f);
     }
-    lds_barrier();   // -A, A_diag, P ready
+    lds_barrier();   // G, bet of the batch ready
 
-    // T_ww = (I + A_ww)^-1 by forward substitution (lane = column)
-    if (lane < 16) {
-      const float* Ab = sm.Ad + w * 256;
+    // -A (off-diagonal tiles, fp16), A (diagonal tiles, fp32) and P for every
+    // head of the batch from this wave's Gram tiles (tile list fixed per wave
+    // at compile time)
+    switch (w) {
+      case 0: prep_elementwise<0>(sm, gram, nb, col, grp, p.scale); break;
+      case 1: prep_elementwise<1>(sm, gram, nb, col, grp, p.scale); break;
+      case 2: prep_elementwise<2>(sm, gram, nb, col, grp, p.scale); break;
+      default: prep_elementwise<3>(sm, gram, nb, col, grp, p.scale); break;
+    }
+    lds_barrier();   // -A, A_diag, P of the batch ready
+
+    if (w < nb) {
+      // T_bb = (I + A_bb)^-1 of head vb0 + w by forward substitution: lane =
+      // 16 blk + column, all four diagonal blocks at once
+      const int h = kh * p.group + vb0 + w;
+      unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
+      const int blk = lane >> 4;
+      const float* Ab = sm.u.vh.Ad[w] + blk * 256;
       float tt[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float acc = (i == lane) ? 1.f : 0.f;
+        float acc = (i == col) ? 1.f : 0.f;
 #pragma unroll
         for (int kk = 0; kk < i; ++kk) acc = fmaf(-Ab[i * 16 + kk], tt[kk], acc);
         tt[i] = acc;
       }
+      _Float16* Tw = sm.u.vh.T[w];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.T[(w * 16 + i) * kTS + lane] = static_cast<_Float16>(tt[i]);
-    }
-    // same-wave LDS write then read: in order within the wave
-    put8(vb + kOffT + w * kFrag16 + lane * 8, lds_a16(sm.T, kTS, w * 16 + col, 0, grp));
-    // P and -A fragments
-    if (w < 3) {
+      for (int i = 0; i < 16; ++i) Tw[(blk * 16 + i) * kTS + col] = static_cast<_Float16>(tt[i]);
+      // T (same-wave LDS write then read: in order within the wave) and -A
+      // fragments of this head
+      half4 tf[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = 2 * w + j;   // (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
-        const int tb = f < 2 ? f : (f < 4 ? 2 : 3);
-        const int kb = (f == 3 || f == 5) ? 32 : 0;
-        put16(vb + kOffP + f * kFrag + lane * 16, lds_a32(sm.P, kAS, 16 * tb + col, kb, grp));
-      }
+      for (int bb = 0; bb < 4; ++bb) tf[bb] = lds_a16(Tw, kTS, bb * 16 + col, 0, grp);
+      const _Float16* An = sm.u.vh.An[w];
+      const half4 a10 = lds_a16(An, kAS, 16 + col, 0, grp);
+      const half8 a2 = lds_a32(An, kAS, 32 + col, 0, grp);
+      const half8 a3 = lds_a32(An, kAS, 48 + col, 0, grp);
+      const half4 a32 = lds_a16(An, kAS, 48 + col, 32, grp);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) put8(vb + kOffT + bb * kFrag16 + lane * 8, tf[bb]);
+      put8(vb + kOffAn10 + lane * 8, a10);
+      put16(vb + kOffAn2 + lane * 16, a2);
+      put16(vb + kOffAn3 + lane * 16, a3);
+      put8(vb + kOffAn32 + lane * 8, a32);
     } else {
-      put8(vb + kOffAn10 + lane * 8, lds_a16(sm.An, kAS, 16 + col, 0, grp));
-      put16(vb + kOffAn2 + lane * 16, lds_a32(sm.An, kAS, 32 + col, 0, grp));
-      put16(vb + kOffAn3 + lane * 16, lds_a32(sm.An, kAS, 48 + col, 0, grp));
-      put8(vb + kOffAn32 + lane * 8, lds_a16(sm.An, kAS, 48 + col, 32, grp));
+      // the other waves write the P fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
+      // of the batch, one head at a time
+      for (int vh = w - nb; vh < nb; vh += 4 - nb) {
+        const int h = kh * p.group + vb0 + vh;
+        unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
+        const _Float16* P = sm.u.vh.P[vh];
+        half8 pf[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+          const int tb = f < 2 ? f : (f < 4 ? 2 : 3);
+          const int kb = (f == 3 || f == 5) ? 32 : 0;
+          pf[f] = lds_a32(P, kAS, 16 * tb + col, kb, grp);
+        }
+#pragma unroll
+        for (int f = 0; f < 6; ++f) put16(vb + kOffP + f * kFrag + lane * 16, pf[f]);
+      }
     }
+    if (vb0 + kHeadBatch < p.group) lds_barrier();   // before the next batch overwrites
   }
 }
 
@@ -542,20 +634,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 1: Q fragments | X = K S0^T
+    // phase 1: Q fragments, V, tables, T_bb, -A | X = K S0^T
     half8 fq[16];
 #pragma unroll
     for (int f = 0; f < 16; ++f) fq[f] = frag(16 + f);
-    floatx4 X[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) X[tb] = mfma32(fk[tb * 4 + kb], sB[kb], X[tb]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // phase 2: V, b, b gamma, T_bb, -A | QS = Q S0^T
     float vv[4][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -574,17 +656,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     const half8 an2 = vfrag(kOffAn2);
     const half8 an3 = vfrag(kOffAn3);
     const half4 an32 = frag16(kOffAn32);
-    floatx4 QS[4];
+    floatx4 X[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 4; ++tb) X[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + kb], sB[kb], QS[tb]);
+      for (int tb = 0; tb < 4; ++tb) X[tb] = mfma32(fk[tb * 4 + kb], sB[kb], X[tb]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 3: K^T fragments | R = b V - b gamma X, U by blockwise forward
-    // substitution (rows = tokens 16tb + 4grp + e, column dvc)
+    // phase 2: K^T fragments, P, tables | R = b V - b gamma X, U by blockwise
+    // forward substitution (rows = tokens 16tb + 4grp + e, column dvc), with
+    // QS = Q S0^T filling the gaps of that dependent chain
     half8 ft[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) ft[i] = frag(32 + i);
@@ -594,36 +677,50 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 #pragma unroll
       for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * vv[tb][e] - bg[tb][e] * X[tb][e];
     const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 QS[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = z4;
     floatx4 U[4];
     U[0] = mfma16(tT[0], to_half4(R[0]), z4);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 0], sB[0], QS[tb]);
     floatx4 rhs = mfma16(an10, to_half4(U[0]), R[1]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 1], sB[1], QS[tb]);
     U[1] = mfma16(tT[1], to_half4(rhs), z4);
     const half8 u01 = to_half8(U[0], U[1]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 2], sB[2], QS[tb]);
     rhs = mfma32(an2, u01, R[2]);
     U[2] = mfma16(tT[2], to_half4(rhs), z4);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 3], sB[3], QS[tb]);
     rhs = mfma32(an3, u01, R[3]);
     rhs = mfma16(an32, to_half4(U[2]), rhs);
     U[3] = mfma16(tT[3], to_half4(rhs), z4);
     const half8 u23 = to_half8(U[2], U[3]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 4: P, scale gamma, D, gamma_L | S^T <- gamma_L S^T + K^T (D U)
+    // phase 3: S^T <- gamma_L S^T + K^T (D U), and O = scale gamma Q S0^T + P U
+    // (kept in registers, written to the LDS tile at the start of the next
+    // chunk and stored by the loaders)
     half8 fp[6];
 #pragma unroll
     for (int f = 0; f < 6; ++f) fp[f] = vfrag(kOffP + f * kFrag);
-    floatx4 sg[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) sg[tb] = table(2, tb);
-    floatx4 DU[4];
+    floatx4 sg[4], dl[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const floatx4 dl = table(3, tb);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) DU[tb][e] = dl[e] * U[tb][e];
+      sg[tb] = table(2, tb);
+      dl[tb] = table(3, tb);
     }
+    const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
+    floatx4 DU[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DU[tb][e] = dl[tb][e] * U[tb][e];
     const half8 d01 = to_half8(DU[0], DU[1]);
     const half8 d23 = to_half8(DU[2], DU[3]);
-    const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       floatx4 s = sT[dt];
@@ -633,10 +730,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       s = mfma32(ft[2 * dt + 1], d23, s);
       sT[dt] = s;
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // phase 5: O = scale gamma Q S0^T + P U, kept in registers and written to
-    // the LDS tile at the start of the next chunk (stored by the loaders)
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       floatx4 O;
