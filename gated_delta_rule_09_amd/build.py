@@ -3,14 +3,19 @@
 Every source under csrc/ is compiled for gfx950 only, with packed-fp32 code
 generation disabled, and linked into gated_delta_rule_09_amd/libgdn.so.
 
-The build also checks that no kernel spills registers: the prefill scan is
-written to fit its registers, and a register allocation that spills vector
-registers into accumulator registers around its MFMA chains has produced wrong
-results on gfx950, so a spill is treated as a build error.
+The build also compiles every source to gfx950 assembly and checks it:
+  * no register spills (the kernels are written to fit their registers);
+  * no MFMA whose accumulator input is the result of a recent MFMA of a
+    different shape (say v_mfma_f32_16x16x32_f16 feeding
+    v_mfma_f32_16x16x16_f16).  With only one or two wait states between such a
+    pair, the second has read stale accumulator values on gfx950; the kernels
+    route such results through VGPRs, which gives the producer its full
+    result latency.
 """
 import concurrent.futures
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -42,19 +47,61 @@ def _compile(src: str) -> str:
 SPILL_MARKERS = ("Reload Reuse", "Spill", "Reload")
 
 
-def _check_no_spills(src: str) -> None:
-    """Compile `src` to gfx950 assembly and fail on any register spill or
-    reload the compiler annotates."""
+_MFMA = re.compile(r"\s*(v_mfma_\w+)\s+([av]\[\d+:\d+\]),\s*[^,]+,\s*[^,]+,\s*([av]\[\d+:\d+\])")
+_DEST = re.compile(r"\s*(v_\w+)\s+([av](?:\d+|\[\d+:\d+\]))")
+
+
+def _regs(tok: str) -> set:
+    m = re.fullmatch(r"([av])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    return {tok}
+
+
+def mixed_mfma_chains(lines, window: int = 24) -> list:
+    """Instructions where an MFMA takes as accumulator input the result of an
+    MFMA of another shape issued at most `window` instructions earlier, with
+    no other write of those registers in between."""
+    found = []
+    for i, ln in enumerate(lines):
+        m = _MFMA.match(ln)
+        if not m:
+            continue
+        op, srcc = m.group(1), _regs(m.group(3))
+        for j in range(i - 1, max(-1, i - 1 - window), -1):
+            prev = lines[j].split(";", 1)[0]
+            if re.match(r"\s*(\.L|s_cbranch|s_branch|s_setpc)", prev):
+                break
+            pm = _MFMA.match(prev)
+            if pm and _regs(pm.group(2)) & srcc:
+                if pm.group(1) != op:
+                    found.append(f"{prev.strip()}  ->  {ln.strip()}")
+                break
+            dm = _DEST.match(prev)
+            if dm and not dm.group(1).startswith(("v_cmp", "v_mfma")) and _regs(dm.group(2)) & srcc:
+                break
+    return found
+
+
+def _check_asm(src: str) -> None:
+    """Compile `src` to gfx950 assembly; fail on register spills and on
+    mixed-shape MFMA accumulator chains."""
     asm = os.path.join(BUILD, os.path.basename(src) + ".s")
     cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-S", src, "-o", asm]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
     with open(asm) as f:
-        bad = [ln.strip() for ln in f if ";" in ln and any(m in ln.split(";", 1)[1] for m in SPILL_MARKERS)]
+        lines = f.read().splitlines()
+    bad = [ln.strip() for ln in lines
+           if ";" in ln and any(m in ln.split(";", 1)[1] for m in SPILL_MARKERS)]
     if bad:
         raise RuntimeError(f"{os.path.basename(src)}: the compiler spilled registers "
                            f"({len(bad)} spill/reload instructions, e.g. {bad[0]!r})")
+    chains = mixed_mfma_chains(lines)
+    if chains:
+        raise RuntimeError(f"{os.path.basename(src)}: MFMA accumulator fed directly by an "
+                           f"MFMA of another shape: {chains[0]}")
 
 
 def build(verbose: bool = False) -> str:
@@ -62,7 +109,7 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-        list(ex.map(_check_no_spills, srcs))
+        list(ex.map(_check_asm, srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -17,8 +17,8 @@
 // Two kernels, run back to back on the caller's stream:
 //
 //   prep (fully parallel over every chunk x key head): everything that does not
-//   depend on the state.  K and Q are converted to fp16 once and written with
-//   K^T in MFMA fragment order; the 20 lower 16x16 tiles of K K^T and Q K^T are
+//   depend on the state.  K and Q are converted to fp16 once (K as rows, Q in
+//   MFMA fragment order); the 20 lower 16x16 tiles of K K^T and Q K^T are
 //   formed once per key head on fp16 MFMA (exact products of bf16 inputs); for
 //   each of the key head's value heads the decay tables, -A, the inverses
 //   T_bb = (I + A_bb)^-1 of the four diagonal 16x16 blocks (fp32 forward
@@ -69,8 +69,13 @@ constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value
 // columns 4g .. 4g+3: 8 bytes per lane, 512 B.
 constexpr int kFrag = 1024;
 constexpr int kFrag16 = 512;
-// Per (chunk, key head): K (tb*4+kb), Q (16 + tb*4+kb), K^T (32 + dt*2+kb).
-constexpr int kKQBytes = 48 * kFrag;
+// Per (chunk, key head): K row-major in fp16 (row = token; 288-byte rows, the
+// padding spreads the rows over the LDS banks), then the 16 Q fragments
+// (tb*4+kb).  The scan reads K fragments from the rows with two 8-byte loads
+// and K^T fragments with gfx950's transposing LDS load.
+constexpr int kKRowBytes = 288;
+constexpr int kOffQ = kC * kKRowBytes;                // 18432
+constexpr int kKQBytes = kOffQ + 16 * kFrag;          // 34816
 // Per (chunk, value head):
 constexpr int kOffP = 0;                              // 6 A32: (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
 constexpr int kOffT = kOffP + 6 * kFrag;              // 4 A16: T_bb
@@ -81,19 +86,18 @@ constexpr int kOffAn32 = kOffAn3 + kFrag;             // A16: -A rows 48..63, co
 constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gamma, scale gamma, exp(G_L - G)
 constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
 constexpr int kVBytes = kOffGL + 256;                 // 12544
-// Per chunk the scan stages [K/Q/K^T blob | value-head blob | V tile] in LDS,
+// Per chunk the scan stages [K/Q blob | value-head blob | V tile] in LDS,
 // where the V tile is this work-group's value channels of the chunk's 64
 // tokens, row-major bf16 (2 kDvPerWg bytes per token).
 constexpr int kVTileBytes = kC * kDvPerWg * 2;                                  // 4096
-constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 65792
-constexpr int kStagePieces = kStageBytes / 16;                                  // 4112
-constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 33
-constexpr int kKQRounds = kKQBytes / (16 * kLoaderThreads);                     // 24
+constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 51456
+constexpr int kStagePieces = kStageBytes / 16;                                  // 3216
+constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 26
+constexpr int kKQRounds = kKQBytes / (16 * kLoaderThreads);                     // 17
 constexpr int kVBPieces = kVBytes / 16;                                         // 784
 constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
 constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
 static_assert(kKQBytes % (16 * kLoaderThreads) == 0, "K/Q blob is whole copy rounds");
-static_assert((kC * kDvPerWg) % (4 * kLoaderThreads) == 0, "O tile is whole store rounds");
 
 static_assert(kStageBytes % 16 == 0, "stage size");
 
@@ -272,25 +276,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   }
   lds_barrier();
 
-  // ---- K, Q, K^T fragments (written once per chunk and key head) -----------
+  // ---- K rows and Q fragments (written once per chunk and key head) --------
   unsigned char* kq = p.kq + (static_cast<int64_t>(c) * p.Hk + kh) * kKQBytes;
 #pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int f = w * 12 + j;
-    half8 v;
-    if (f < 32) {
-      const _Float16* X = f < 16 ? sm.u.kq.K : sm.u.kq.Q;
-      const int ff = f & 15;
-      v = lds_a32(X, kKS, 16 * (ff >> 2) + col, 32 * (ff & 3), grp);
-    } else {
-      const int dt = (f - 32) >> 1, kb = (f - 32) & 1;
+  for (int j = 0; j < 4; ++j) {
+    const int piece = tid + kThreads * j;       // 64 rows x 16 pieces of 8 channels
+    const int r = piece >> 4;
+    const int c8 = (piece & 15) * 8;
+    put16(kq + r * kKRowBytes + c8 * 2, *reinterpret_cast<const half8*>(&sm.u.kq.K[r * kKS + c8]));
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 32 * kb + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-        v[e] = sm.u.kq.K[tok * kKS + 16 * dt + col];
-      }
-    }
-    put16(kq + f * kFrag + lane * 16, v);
+  for (int j = 0; j < 4; ++j) {
+    const int f = w * 4 + j;
+    put16(kq + kOffQ + f * kFrag + lane * 16,
+          lds_a32(sm.u.kq.Q, kKS, 16 * (f >> 2) + col, 32 * (f & 3), grp));
   }
 
   // ---- Gram tiles: wave w owns lower tiles 5w .. 5w+4 of the list
@@ -430,13 +429,23 @@ struct ScanParams {
   int n_chain_groups;         // n_seqs * Hk
 };
 
-// Two stage buffers (the chunk being computed, the one being copied in) and two
-// O tiles (the chunk being computed, the one being stored).
-constexpr int kOTileFloats = kC * kDvPerWg;
+// Two stage buffers: the chunk being computed and the one being copied in.
 struct __align__(16) ScanSmem {
   unsigned char buf[2][kStageBytes];
-  float obuf[2][kOTileFloats];
 };
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+// gfx950 transposing LDS load (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j reads the four 16-bit values at its own address a_j; lane i of
+// the group then receives a_{4e + i/4}[i % 4] for e = 0..3.  If lane j points
+// at row r0 + j/4, column c0 + 4 (j % 4) of a row-major 16-bit matrix, lane i
+// receives column c0 + i of rows r0 .. r0 + 3: a column slice, as an MFMA
+// operand needs it.
+__device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
+  return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
+}
 
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams p) {
   __shared__ ScanSmem sm;
@@ -475,8 +484,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   const int n_chunks = (seq_len + kC - 1) / kC;
 
   if (!compute) {
-    // ---- loader waves: copy the stage of chunk ci + 1 into LDS and store the
-    // O tile of chunk ci - 1 while the compute waves work on chunk ci --------
+    // ---- loader waves: copy the stage of chunk ci + 1 into LDS while the
+    // compute waves work on chunk ci ---------------------------------------------
     const int lt = tid - 64 * kScanComputeWaves;          // 0 .. kLoaderThreads - 1
     const int lw = w - kScanComputeWaves;
     const unsigned char* kq_head = p.kq + static_cast<int64_t>(kh) * kKQBytes;
@@ -484,10 +493,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     const int64_t kq_step = static_cast<int64_t>(p.Hk) * kKQBytes;
     const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
     const uint16_t* v_head = p.v + h * kD + part * kDvPerWg;
-    const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-    float* o_head = p.o + h * kD + part * kDvPerWg;
 
-    // Piece i of the stage is its byte 16 i: the K/Q/K^T blob, the value-head
+    // Piece i of the stage is its byte 16 i: the K/Q blob, the value-head
     // blob, then the V tile (token i / kVPiecesPerRow, channels
     // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDvPerWg).
     auto stage = [&](int ci) {
@@ -511,20 +518,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
           const int r = min(vp / kVPiecesPerRow, len - 1);   // rows past the end re-read the last
           lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % kVPiecesPerRow) * 8, d);
         }
-      }
-    };
-    // O tile of chunk ci: 16 bytes per lane, 8 lanes per token row
-    auto store_o = [&](int ci) {
-      const int len = min(kC, seq_len - ci * kC);
-      const float* src = sm.obuf[ci & 1];
-      float* dst = o_head + static_cast<int64_t>(seq_start + ci * kC) * o_rs;
-#pragma unroll
-      for (int j = 0; j < kOTileFloats / (4 * kLoaderThreads); ++j) {
-        const int i = kLoaderThreads * j + lt;
-        const int r = i / (kDvPerWg / 4);
-        const int c4 = (i % (kDvPerWg / 4)) * 4;
-        const floatx4 val = *reinterpret_cast<const floatx4*>(src + r * kDvPerWg + c4);
-        if (r < len) *reinterpret_cast<floatx4*>(dst + r * o_rs + c4) = val;
       }
     };
 
@@ -554,9 +547,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     };
     uint32_t sink = 0, tv = 0;
 
-    // Order per chunk: copies of chunk ci + 1, O stores, prefetch of chunk
-    // ci + 2.  The prefetch is the youngest memory operation, so the wait at
-    // the next barrier (vmcnt(1)) leaves only it in flight.
+    // Order per chunk: copies of chunk ci + 1, then the prefetch of chunk
+    // ci + 2, the youngest memory operation, so the wait at the next barrier
+    // (vmcnt(1)) leaves only it in flight.
     if (n_chunks > 0) {
       stage(0);
       tv = touch(min(1, n_chunks - 1));
@@ -565,15 +558,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (ci + 1 < n_chunks) stage(ci + 1);
       sink ^= tv;                          // issued a chunk ago
-      if (ci > 1) store_o(ci - 2);
       tv = touch(min(ci + 2, n_chunks - 1));
     }
     sink ^= tv;
     if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
-    dma_barrier();                         // O tile n - 2 written, O n - 3 read
-    if (n_chunks > 1) store_o(n_chunks - 2);
-    lds_barrier();                         // O tile n - 1 written
-    if (n_chunks > 0) store_o(n_chunks - 1);
     return;
   }
 
@@ -599,12 +587,38 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   // Nothing may be pending at the loop header: the compiler's wait insertion
   // would otherwise keep a vmcnt(0) inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
-  floatx4 Oprev[4];
+
+  // O is computed transposed (lane = token, registers = four value channels
+  // 4grp .. 4grp+3 of this wave's sixteen), so each lane stores 16 bytes per
+  // token; the tile of chunk ci is stored at the start of chunk ci + 1.
+  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
+  float* o_col = p.o + h * kD + part * kDvPerWg + 16 * w + 4 * grp;
+  floatx4 Ot[4];
+  int o_t0 = 0, o_len = 0;
+  auto store_o = [&]() {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int r = 16 * tb + col;
+      if (r < o_len) *reinterpret_cast<floatx4*>(o_col + static_cast<int64_t>(o_t0 + r) * o_rs) = Ot[tb];
+    }
+  };
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const unsigned char* B = sm.buf[ci & 1];
     const unsigned char* VB = B + kKQBytes;
-    auto frag = [&](int f) { return *reinterpret_cast<const half8*>(B + f * kFrag + lane * 16); };
+    // K A-fragment (rows 16 tb .. +15 = tokens, 32 dk columns of block kb)
+    // from the K rows: the columns kappa(grp, e) are two runs of four
+    auto kfrag = [&](int tb, int kb) {
+      const unsigned char* r = B + (16 * tb + col) * kKRowBytes + (32 * kb + 4 * grp) * 2;
+      return cat8(*reinterpret_cast<const half4*>(r), *reinterpret_cast<const half4*>(r + 32));
+    };
+    // K^T A-fragment (rows 16 dt .. +15 = dk, 32 tokens of block kb): two
+    // transposing loads over token rows 32 kb + 4 grp .. and 32 kb + 16 + 4 grp ..
+    auto ktfrag = [&](int dt, int kb) {
+      const unsigned char* r = B + (32 * kb + 4 * grp + (col >> 2)) * kKRowBytes + (16 * dt + 4 * (col & 3)) * 2;
+      return cat8(lds_read_tr(r), lds_read_tr(r + 16 * kKRowBytes));
+    };
+    auto qfrag = [&](int f) { return *reinterpret_cast<const half8*>(B + kOffQ + f * kFrag + lane * 16); };
     auto frag16 = [&](int off) { return *reinterpret_cast<const half4*>(VB + off + lane * 8); };
     auto vfrag = [&](int off) { return *reinterpret_cast<const half8*>(VB + off + lane * 16); };
     auto table = [&](int tab, int tb) {
@@ -615,29 +629,25 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     // The chunk runs in phases separated by scheduling fences; each phase
     // issues the LDS reads of the next one, so read latency hides behind the
     // products of the current phase.
-    dma_barrier();                         // this chunk's stage is in LDS
+    lds_barrier();                         // this chunk's stage is in LDS
 
     // phase 0: K fragments; B operands of S0^T straight from registers; the
-    // previous chunk's O tile (its products have long completed) to LDS
+    // previous chunk's O tile (its products have long completed) to HBM
     half8 fk[16];
 #pragma unroll
-    for (int f = 0; f < 16; ++f) fk[f] = frag(f);
-    if (ci > 0) {
-      float* ob = sm.obuf[(ci - 1) & 1];
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ob[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = Oprev[tb][e];
-    }
+      for (int kb = 0; kb < 4; ++kb) fk[tb * 4 + kb] = kfrag(tb, kb);
     half8 sB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
+    if (ci > 0) store_o();
     __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: Q fragments, V, tables, T_bb, -A | X = K S0^T
     half8 fq[16];
 #pragma unroll
-    for (int f = 0; f < 16; ++f) fq[f] = frag(16 + f);
+    for (int f = 0; f < 16; ++f) fq[f] = qfrag(f);
     float vv[4][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -665,60 +675,65 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       for (int tb = 0; tb < 4; ++tb) X[tb] = mfma32(fk[tb * 4 + kb], sB[kb], X[tb]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 2: K^T fragments, P, tables | R = b V - b gamma X, U by blockwise
-    // forward substitution (rows = tokens 16tb + 4grp + e, column dvc), with
-    // QS = Q S0^T filling the gaps of that dependent chain
+    // phase 2: K^T fragments | R = b V - b gamma X, U by blockwise forward
+    // substitution (rows = tokens 16tb + 4grp + e, column dvc), with the
+    // transposed (Q S0^T)^T = S0 Q^T filling the gaps of that dependent chain
     half8 ft[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ft[i] = frag(32 + i);
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ft[2 * dt + kb] = ktfrag(dt, kb);
     floatx4 R[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) R[tb][e] = bt[tb][e] * vv[tb][e] - bg[tb][e] * X[tb][e];
     const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-    floatx4 QS[4];
+    floatx4 QSt[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = z4;
+    for (int tb = 0; tb < 4; ++tb) QSt[tb] = z4;
     floatx4 U[4];
     U[0] = mfma16(tT[0], to_half4(R[0]), z4);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 0], sB[0], QS[tb]);
+    for (int tb = 0; tb < 4; ++tb) QSt[tb] = mfma32(sB[0], fq[tb * 4 + 0], QSt[tb]);
     floatx4 rhs = mfma16(an10, to_half4(U[0]), R[1]);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 1], sB[1], QS[tb]);
+    for (int tb = 0; tb < 4; ++tb) QSt[tb] = mfma32(sB[1], fq[tb * 4 + 1], QSt[tb]);
     U[1] = mfma16(tT[1], to_half4(rhs), z4);
     const half8 u01 = to_half8(U[0], U[1]);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 2], sB[2], QS[tb]);
+    for (int tb = 0; tb < 4; ++tb) QSt[tb] = mfma32(sB[2], fq[tb * 4 + 2], QSt[tb]);
     rhs = mfma32(an2, u01, R[2]);
     U[2] = mfma16(tT[2], to_half4(rhs), z4);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) QS[tb] = mfma32(fq[tb * 4 + 3], sB[3], QS[tb]);
+    for (int tb = 0; tb < 4; ++tb) QSt[tb] = mfma32(sB[3], fq[tb * 4 + 3], QSt[tb]);
     rhs = mfma32(an3, u01, R[3]);
+    // The 16x16x32 result feeds the 16x16x16 product below as its accumulator.
+    // Routed through VGPRs: with the two MFMAs scheduled close together, the
+    // accumulator read of the second has been observed to see stale values.
+    asm volatile("" : "+v"(rhs));
     rhs = mfma16(an32, to_half4(U[2]), rhs);
     U[3] = mfma16(tT[3], to_half4(rhs), z4);
     const half8 u23 = to_half8(U[2], U[3]);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 3: S^T <- gamma_L S^T + K^T (D U), and O = scale gamma Q S0^T + P U
-    // (kept in registers, written to the LDS tile at the start of the next
-    // chunk and stored by the loaders)
+    // phase 3: S^T <- gamma_L S^T + K^T (D U), and O^T = scale gamma^T (S0 Q^T)
+    // + U^T P^T (the P fragments serve as B operands of the transposed product)
     half8 fp[6];
 #pragma unroll
     for (int f = 0; f < 6; ++f) fp[f] = vfrag(kOffP + f * kFrag);
-    floatx4 sg[4], dl[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      sg[tb] = table(2, tb);
-      dl[tb] = table(3, tb);
-    }
-    const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
-    floatx4 DU[4];
+    float sgl[4];                          // scale gamma of token 16 tb + col
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
+      sgl[tb] = *reinterpret_cast<const float*>(VB + kOffDecay + 2 * 256 + (16 * tb + col) * 4);
+    floatx4 DU[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) DU[tb][e] = dl[tb][e] * U[tb][e];
+    for (int tb = 0; tb < 4; ++tb) {
+      const floatx4 dl = table(3, tb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DU[tb][e] = dl[e] * U[tb][e];
+    }
+    const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
     const half8 d01 = to_half8(DU[0], DU[1]);
     const half8 d23 = to_half8(DU[2], DU[3]);
 #pragma unroll
@@ -734,21 +749,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     for (int tb = 0; tb < 4; ++tb) {
       floatx4 O;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = sg[tb][e] * QS[tb][e];
-      O = mfma32(fp[tb < 2 ? tb : 2 * tb - 2], u01, O);
-      if (tb >= 2) O = mfma32(fp[2 * tb - 1], u23, O);
-      Oprev[tb] = O;
+      for (int e = 0; e < 4; ++e) O[e] = sgl[tb] * QSt[tb][e];
+      O = mfma32(u01, fp[tb < 2 ? tb : 2 * tb - 2], O);
+      if (tb >= 2) O = mfma32(u23, fp[2 * tb - 1], O);
+      Ot[tb] = O;
     }
+    o_t0 = seq_start + ci * kC;
+    o_len = min(kC, seq_len - ci * kC);
   }
-  lds_barrier();                           // the loaders are done with O tile n - 3
-  if (n_chunks > 0) {
-    float* ob = sm.obuf[(n_chunks - 1) & 1];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ob[(16 * tb + 4 * grp + e) * kDvPerWg + dvw] = Oprev[tb][e];
-  }
-  lds_barrier();                           // O tile n - 1 written
+  if (n_chunks > 0) store_o();
 
   if (p.hT) {
 #pragma unroll
