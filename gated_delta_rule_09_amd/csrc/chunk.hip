@@ -69,13 +69,16 @@ constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value
 // columns 4g .. 4g+3: 8 bytes per lane, 512 B.
 constexpr int kFrag = 1024;
 constexpr int kFrag16 = 512;
-// Per (chunk, key head): K row-major in fp16 (row = token; 288-byte rows, the
-// padding spreads the rows over the LDS banks), then the 16 Q fragments
-// (tb*4+kb).  The scan reads K fragments from the rows with two 8-byte loads
-// and K^T fragments with gfx950's transposing LDS load.
-constexpr int kKRowBytes = 288;
-constexpr int kOffQ = kC * kKRowBytes;                // 18432
-constexpr int kKQBytes = kOffQ + 16 * kFrag;          // 34816
+// Per (chunk, key head): K as fp16 rows (row = token, 272 bytes: the padding
+// spreads the rows over the LDS banks), then the 16 Q fragments (tb*4+kb).
+// Within each 32-column block of a row the eight runs of four columns are
+// stored in the order 0 4 1 5 2 6 3 7, so that the 16 bytes at block offset
+// 16 m are the columns kappa(m, 0..7): a K fragment is one 16-byte LDS load
+// per lane, and K^T fragments come from gfx950's transposing LDS load over the
+// rows (any order of the four-column runs works for it).
+constexpr int kKRowBytes = 272;
+constexpr int kOffQ = kC * kKRowBytes;                // 17408
+constexpr int kKQBytes = kOffQ + 16 * kFrag;          // 33792
 // Per (chunk, value head):
 constexpr int kOffP = 0;                              // 6 A32: (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
 constexpr int kOffT = kOffP + 6 * kFrag;              // 4 A16: T_bb
@@ -90,14 +93,19 @@ constexpr int kVBytes = kOffGL + 256;                 // 12544
 // where the V tile is this work-group's value channels of the chunk's 64
 // tokens, row-major bf16 (2 kDvPerWg bytes per token).
 constexpr int kVTileBytes = kC * kDvPerWg * 2;                                  // 4096
-constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 51456
-constexpr int kStagePieces = kStageBytes / 16;                                  // 3216
-constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 26
-constexpr int kKQRounds = kKQBytes / (16 * kLoaderThreads);                     // 17
+constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 50432
+constexpr int kStagePieces = kStageBytes / 16;                                  // 3152
+constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 25
+constexpr int kKQPieces = kKQBytes / 16;                                        // 2112
 constexpr int kVBPieces = kVBytes / 16;                                         // 784
 constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
 constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
-static_assert(kKQBytes % (16 * kLoaderThreads) == 0, "K/Q blob is whole copy rounds");
+// O tile of a chunk in LDS: 64 tokens x kDvPerWg fp32, rows padded to 36 floats
+constexpr int kORow = kDvPerWg + 4;
+constexpr int kOTileFloats = kC * kORow;
+constexpr int kOPieces = kC * kDvPerWg / 4;                                     // 512
+static_assert(kOPieces % kLoaderThreads == 0, "O tile is whole store rounds");
+static_assert(kStagePieces == kKQPieces + kVBPieces + kVTilePieces, "stage = K/Q blob + value blob + V tile");
 
 static_assert(kStageBytes % 16 == 0, "stage size");
 
@@ -280,10 +288,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   unsigned char* kq = p.kq + (static_cast<int64_t>(c) * p.Hk + kh) * kKQBytes;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int piece = tid + kThreads * j;       // 64 rows x 16 pieces of 8 channels
+    const int piece = tid + kThreads * j;       // 64 rows x 4 blocks x 4 runs of 16 bytes
     const int r = piece >> 4;
-    const int c8 = (piece & 15) * 8;
-    put16(kq + r * kKRowBytes + c8 * 2, *reinterpret_cast<const half8*>(&sm.u.kq.K[r * kKS + c8]));
+    const int kb = (piece >> 2) & 3, m = piece & 3;
+    put16(kq + r * kKRowBytes + kb * 64 + m * 16, lds_a32(sm.u.kq.K, kKS, r, 32 * kb, m));
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -429,9 +437,12 @@ struct ScanParams {
   int n_chain_groups;         // n_seqs * Hk
 };
 
-// Two stage buffers: the chunk being computed and the one being copied in.
+// Two stage buffers (the chunk being computed, the one being copied in) and
+// two O tiles (written by the compute waves a chunk late, stored by the loader
+// waves a chunk after that).
 struct __align__(16) ScanSmem {
   unsigned char buf[2][kStageBytes];
+  float obuf[2][kOTileFloats];
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -502,22 +513,37 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       const unsigned char* kqb = kq_head + cb * kq_step;
       const unsigned char* vbb = vb_head + cb * vb_step;
       unsigned char* dst = sm.buf[ci & 1];
-#pragma unroll
-      for (int j = 0; j < kKQRounds; ++j)
-        lds_dma16(kqb + (kLoaderThreads * j + lt) * 16, dst + (kLoaderThreads * j + 64 * lw) * 16);
       const int len = min(kC, seq_len - ci * kC);
       const uint16_t* vrow0 = v_head + static_cast<int64_t>(seq_start + ci * kC) * p.vs;
 #pragma unroll
-      for (int j = 0; j < kStageRounds - kKQRounds; ++j) {
-        const int q = kLoaderThreads * j + lt;       // piece index after the K/Q blob
-        unsigned char* d = dst + kKQBytes + (kLoaderThreads * j + 64 * lw) * 16;
-        if (q < kVBPieces) {
-          lds_dma16(vbb + q * 16, d);
-        } else if (q < kVBPieces + kVTilePieces) {
-          const int vp = q - kVBPieces;
+      for (int j = 0; j < kStageRounds; ++j) {
+        const int q = kLoaderThreads * j + lt;
+        unsigned char* d = dst + (kLoaderThreads * j + 64 * lw) * 16;
+        if (q < kKQPieces) {
+          lds_dma16(kqb + q * 16, d);
+        } else if (q < kKQPieces + kVBPieces) {
+          lds_dma16(vbb + (q - kKQPieces) * 16, d);
+        } else if (q < kStagePieces) {
+          const int vp = q - kKQPieces - kVBPieces;
           const int r = min(vp / kVPiecesPerRow, len - 1);   // rows past the end re-read the last
           lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % kVPiecesPerRow) * 8, d);
         }
+      }
+    };
+    // O tile of chunk ci: 16 bytes per lane, kDvPerWg / 4 lanes per token row
+    const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
+    float* o_head = p.o + h * kD + part * kDvPerWg;
+    auto store_o = [&](int ci) {
+      const int len = min(kC, seq_len - ci * kC);
+      const float* src = sm.obuf[ci & 1];
+      float* dst = o_head + static_cast<int64_t>(seq_start + ci * kC) * o_rs;
+#pragma unroll
+      for (int j = 0; j < kOPieces / kLoaderThreads; ++j) {
+        const int i = kLoaderThreads * j + lt;
+        const int r = i / (kDvPerWg / 4);
+        const int c4 = (i % (kDvPerWg / 4)) * 4;
+        const floatx4 val = *reinterpret_cast<const floatx4*>(src + r * kORow + c4);
+        if (r < len) *reinterpret_cast<floatx4*>(dst + r * o_rs + c4) = val;
       }
     };
 
@@ -547,9 +573,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     };
     uint32_t sink = 0, tv = 0;
 
-    // Order per chunk: copies of chunk ci + 1, then the prefetch of chunk
-    // ci + 2, the youngest memory operation, so the wait at the next barrier
-    // (vmcnt(1)) leaves only it in flight.
+    // Order per chunk: copies of chunk ci + 1, the O stores of chunk ci - 2,
+    // then the prefetch of chunk ci + 2, the youngest memory operation, so the
+    // wait at the next barrier (vmcnt(1)) leaves only it in flight.
     if (n_chunks > 0) {
       stage(0);
       tv = touch(min(1, n_chunks - 1));
@@ -558,10 +584,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (ci + 1 < n_chunks) stage(ci + 1);
       sink ^= tv;                          // issued a chunk ago
+      if (ci > 1) store_o(ci - 2);
       tv = touch(min(ci + 2, n_chunks - 1));
     }
     sink ^= tv;
     if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
+    dma_barrier();                         // O tile n - 2 written, O n - 3 read
+    if (n_chunks > 1) store_o(n_chunks - 2);
+    lds_barrier();                         // O tile n - 1 written
+    if (n_chunks > 0) store_o(n_chunks - 1);
     return;
   }
 
@@ -589,33 +620,30 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   __builtin_amdgcn_s_waitcnt(0);
 
   // O is computed transposed (lane = token, registers = four value channels
-  // 4grp .. 4grp+3 of this wave's sixteen), so each lane stores 16 bytes per
-  // token; the tile of chunk ci is stored at the start of chunk ci + 1.
-  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-  float* o_col = p.o + h * kD + part * kDvPerWg + 16 * w + 4 * grp;
+  // 4grp .. 4grp+3 of this wave's sixteen): one 16-byte LDS write per lane and
+  // tile, at the start of the next chunk, when its products have completed.
   floatx4 Ot[4];
-  int o_t0 = 0, o_len = 0;
-  auto store_o = [&]() {
+  auto write_o = [&](int ci) {
+    float* ob = sm.obuf[ci & 1] + 16 * w + 4 * grp;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int r = 16 * tb + col;
-      if (r < o_len) *reinterpret_cast<floatx4*>(o_col + static_cast<int64_t>(o_t0 + r) * o_rs) = Ot[tb];
-    }
+    for (int tb = 0; tb < 4; ++tb) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * kORow) = Ot[tb];
   };
 
   for (int ci = 0; ci < n_chunks; ++ci) {
     const unsigned char* B = sm.buf[ci & 1];
     const unsigned char* VB = B + kKQBytes;
-    // K A-fragment (rows 16 tb .. +15 = tokens, 32 dk columns of block kb)
-    // from the K rows: the columns kappa(grp, e) are two runs of four
+    // K A-fragment (rows 16 tb .. +15 = tokens, 32 dk columns of block kb):
+    // the columns kappa(grp, e) are stored together
     auto kfrag = [&](int tb, int kb) {
-      const unsigned char* r = B + (16 * tb + col) * kKRowBytes + (32 * kb + 4 * grp) * 2;
-      return cat8(*reinterpret_cast<const half4*>(r), *reinterpret_cast<const half4*>(r + 32));
+      return *reinterpret_cast<const half8*>(B + (16 * tb + col) * kKRowBytes + kb * 64 + grp * 16);
     };
     // K^T A-fragment (rows 16 dt .. +15 = dk, 32 tokens of block kb): two
-    // transposing loads over token rows 32 kb + 4 grp .. and 32 kb + 16 + 4 grp ..
+    // transposing loads over token rows 32 kb + 4 grp .. and 32 kb + 16 + 4 grp ..;
+    // lane col reads the run of dk columns 16 dt + 4 (col & 3) .. +3, stored at
+    // run slot 2 (col & 3) + (dt & 1) of 32-column block dt / 2
     auto ktfrag = [&](int dt, int kb) {
-      const unsigned char* r = B + (32 * kb + 4 * grp + (col >> 2)) * kKRowBytes + (16 * dt + 4 * (col & 3)) * 2;
+      const unsigned char* r = B + (32 * kb + 4 * grp + (col >> 2)) * kKRowBytes + (dt >> 1) * 64 +
+                               (2 * (col & 3) + (dt & 1)) * 8;
       return cat8(lds_read_tr(r), lds_read_tr(r + 16 * kKRowBytes));
     };
     auto qfrag = [&](int f) { return *reinterpret_cast<const half8*>(B + kOffQ + f * kFrag + lane * 16); };
@@ -632,7 +660,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     lds_barrier();                         // this chunk's stage is in LDS
 
     // phase 0: K fragments; B operands of S0^T straight from registers; the
-    // previous chunk's O tile (its products have long completed) to HBM
+    // previous chunk's O tile to LDS
     half8 fk[16];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -641,7 +669,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     half8 sB[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sB[kb] = to_half8(sT[2 * kb], sT[2 * kb + 1]);
-    if (ci > 0) store_o();
+    if (ci > 0) write_o(ci - 1);
     __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: Q fragments, V, tables, T_bb, -A | X = K S0^T
@@ -754,10 +782,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       if (tb >= 2) O = mfma32(u23, fp[2 * tb - 1], O);
       Ot[tb] = O;
     }
-    o_t0 = seq_start + ci * kC;
-    o_len = min(kC, seq_len - ci * kC);
   }
-  if (n_chunks > 0) store_o();
+  lds_barrier();                           // the loaders are done with O tile n - 3
+  if (n_chunks > 0) write_o(n_chunks - 1);
+  lds_barrier();                           // O tile n - 1 written
 
   if (p.hT) {
 #pragma unroll
