@@ -28,6 +28,10 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA results in VGPRs: the kernels run one wave per SIMD with room
+          # for all of them there, and AGPR results cost a move per register
+          # each time a VALU op touches an accumulator
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
