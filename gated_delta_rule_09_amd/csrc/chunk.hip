@@ -27,17 +27,16 @@
 //   start.
 //
 //   scan (one work-group per sequence x value head x quarter of the value
-//   channels): the sequential part.  Two compute waves each carry the 16 x 128
-//   slice of S^T for their 16 value channels in MFMA accumulator registers
-//   across all chunks; two loader waves copy the next chunk's fragments and V
-//   tile into LDS (global_load_lds, one chunk ahead) and store the previous
-//   chunk's O tile from LDS, so the compute waves never issue a global memory
-//   instruction inside the loop.  Per chunk each compute wave runs
-//   X = K S0^T and Q S0^T (B operand straight from the S^T registers),
-//   R = b V - b gamma X, U by blockwise forward substitution
-//   (U_i = T_ii (R_i - sum_{j<i} A_ij U_j)), S^T <- gamma_L S^T + K^T (D U)
-//   and O = scale gamma Q S0^T + P U, in phases that each issue the LDS reads
-//   of the next phase.
+//   channels): the sequential part.  A state wave carries the 32 x 128 slice
+//   of S^T for the work-group's 32 value channels in registers across all
+//   chunks and per chunk runs W = K S0^T (B operand straight from the S^T
+//   registers), R = b V - b gamma W, U by blockwise forward substitution
+//   (U_i = T_ii (R_i - sum_{j<i} A_ij U_j)) and S^T <- gamma_L S^T + K^T (D U),
+//   in phases that each issue the LDS reads of the next phase.  It leaves the
+//   fp16 S0 and U in LDS; an output wave forms O = scale (gamma Q S0^T + P U)
+//   from them a chunk later and stores it.  Two loader waves copy the next
+//   chunk's fragments and V tile into LDS (global_load_lds, one chunk ahead),
+//   so the state wave never issues a global memory instruction inside the loop.
 //
 // Only the fp32-valued operands are rounded to fp16 (S0, U, T_ii, A, P);
 // accumulation is fp32 throughout.  The per-chunk state never leaves the
@@ -54,8 +53,7 @@ constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
 constexpr int kThreads = 256;    // prep work-group
 // Scan work-group (32 value channels of one value head): a state wave, an
-// output wave, and two loader waves that copy the next chunk into LDS and
-// store finished O tiles.
+// output wave, and two loader waves that copy the next chunk into LDS.
 constexpr int kScanComputeWaves = 2;
 constexpr int kScanLoaderWaves = 2;
 constexpr int kScanThreads = 64 * (kScanComputeWaves + kScanLoaderWaves);
@@ -101,11 +99,6 @@ constexpr int kKQPieces = kKQBytes / 16;                                        
 constexpr int kVBPieces = kVBytes / 16;                                         // 784
 constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
 constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
-// O tile of a chunk in LDS: 64 tokens x kDvPerWg fp32, rows padded to 36 floats
-constexpr int kORow = kDvPerWg + 4;
-constexpr int kOTileFloats = kC * kORow;
-constexpr int kOPieces = kC * kDvPerWg / 4;                                     // 512
-static_assert(kOPieces % kLoaderThreads == 0, "O tile is whole store rounds");
 // Per chunk the state wave leaves the fp16 S0 (as B operands, tile t, block kb
 // at fragment 4 t + kb) and U (fragments 8 + 2 t, 9 + 2 t) for the output wave.
 constexpr int kXBytes = 12 * kFrag;
@@ -442,12 +435,11 @@ struct ScanParams {
 };
 
 // Two stage buffers (the chunk being computed, the one being copied in) and
-// two O tiles (written by the compute waves a chunk late, stored by the loader
-// waves a chunk after that).
+// two sets of the S0 / U fragments passed from the state wave to the output
+// wave.
 struct __align__(16) ScanSmem {
   unsigned char buf[2][kStageBytes];
   unsigned char xbuf[2][kXBytes];
-  float obuf[2][kOTileFloats];
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -535,34 +527,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
         }
       }
     };
-    // O tile of chunk ci: 16 bytes per lane, kDvPerWg / 4 lanes per token row
-    const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-    float* o_head = p.o + h * kD + part * kDvPerWg;
-    auto store_o = [&](int ci) {
-      const int len = min(kC, seq_len - ci * kC);
-      const float* src = sm.obuf[ci & 1];
-      float* dst = o_head + static_cast<int64_t>(seq_start + ci * kC) * o_rs;
-#pragma unroll
-      for (int j = 0; j < kOPieces / kLoaderThreads; ++j) {
-        const int i = kLoaderThreads * j + lt;
-        const int r = i / (kDvPerWg / 4);
-        const int c4 = (i % (kDvPerWg / 4)) * 4;
-        const floatx4 val = *reinterpret_cast<const floatx4*>(src + r * kORow + c4);
-        if (r < len) *reinterpret_cast<floatx4*>(dst + r * o_rs + c4) = val;
-      }
-    };
-
-    // Per chunk: copies of chunk ci + 1, then the O stores of chunk ci - 2.
+    // Per chunk: the copies of chunk ci + 1.
     if (n_chunks > 0) stage(0);
     for (int ci = 0; ci < n_chunks; ++ci) {
       dma_barrier();
       if (ci + 1 < n_chunks) stage(ci + 1);
-      if (ci > 1) store_o(ci - 2);
     }
-    dma_barrier();                         // O tile n - 2 written, O n - 3 read
-    if (n_chunks > 1) store_o(n_chunks - 2);
-    lds_barrier();                         // O tile n - 1 written
-    if (n_chunks > 0) store_o(n_chunks - 1);
+    lds_barrier();                         // the compute waves' last two barriers
+    lds_barrier();
     return;
   }
 
@@ -784,7 +756,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
         }
       }
     }
-    lds_barrier();                         // matches the output wave's last O tile
+    lds_barrier();                         // S0, U of the last chunk written
     lds_barrier();
 
     if (p.hT) {
@@ -799,6 +771,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   }
 
   // ---- output wave: O of chunk ci - 1 during chunk ci ------------------------
+  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
   // Q and P fragments and the per-token scale of a chunk are taken into
   // registers while its stage is in LDS; the next chunk's copy overwrites it.
   half8 fq[16], fp[6];
@@ -826,7 +799,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 #pragma unroll
       for (int j = 0; j < 2; ++j) u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
     }
-    float* ob = sm.obuf[ci & 1] + 4 * grp;
+    const int len = min(kC, seq_len - ci * kC);
+    float* ob = p.o + static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -839,7 +813,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
         for (int e = 0; e < 4; ++e) O[e] = sgl[tb] * qs[e];
         O = mfma32(u[t][0], fp[tb < 2 ? tb : 2 * tb - 2], O);
         if (tb >= 2) O = mfma32(u[t][1], fp[2 * tb - 1], O);
-        *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * kORow + 16 * t) = O;
+        if (16 * tb + col < len) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * o_rs + 16 * t) = O;
       }
   };
   uint32_t sink = 0, tv = 0, tv_prev = 0;
@@ -856,7 +830,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
   lds_barrier();                           // S0, U of the last chunk written
   if (n_chunks > 0) output(n_chunks - 1);
-  lds_barrier();                           // O tile n - 1 written
+  lds_barrier();
 }
 
 }  // namespace
