@@ -88,21 +88,27 @@ constexpr int kOffAn32 = kOffAn3 + kFrag;             // A16: -A rows 48..63, co
 constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gamma, scale gamma, exp(G_L - G)
 constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
 constexpr int kVBytes = kOffGL + 256;                 // 12544
-// Per chunk the scan stages [K/Q blob | value-head blob | V tile] in LDS,
-// where the V tile is this work-group's value channels of the chunk's 64
-// tokens, row-major bf16 (2 kDvPerWg bytes per token).
+// Per chunk the scan stages what the state wave reads in LDS: [K rows |
+// value-head blob from T_bb on | V tile], where the V tile is this
+// work-group's value channels of the chunk's 64 tokens, row-major bf16
+// (2 kDvPerWg bytes per token).  The output wave loads its Q and P fragments
+// from global memory into registers.
+constexpr int kVBStaged = kVBytes - kOffT;                                      // 6400
 constexpr int kVTileBytes = kC * kDvPerWg * 2;                                  // 4096
-constexpr int kStageBytes = kKQBytes + kVBytes + kVTileBytes;                   // 50432
-constexpr int kStagePieces = kStageBytes / 16;                                  // 3152
-constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 25
-constexpr int kKQPieces = kKQBytes / 16;                                        // 2112
-constexpr int kVBPieces = kVBytes / 16;                                         // 784
+constexpr int kStageVB = kOffQ;                                                 // 17408
+constexpr int kStageV = kStageVB + kVBStaged;                                   // 23808
+constexpr int kStageBytes = kStageV + kVTileBytes;                              // 27904
+constexpr int kStagePieces = kStageBytes / 16;                                  // 1744
+constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 14
+constexpr int kKPieces = kOffQ / 16;                                            // 1088
+constexpr int kVBPieces = kVBStaged / 16;                                       // 400
 constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
 constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
 // Per chunk the state wave leaves the fp16 S0 (as B operands, tile t, block kb
 // at fragment 4 t + kb) and U (fragments 8 + 2 t, 9 + 2 t) for the output wave.
 constexpr int kXBytes = 12 * kFrag;
-static_assert(kStagePieces == kKQPieces + kVBPieces + kVTilePieces, "stage = K/Q blob + value blob + V tile");
+static_assert(kStagePieces == kKPieces + kVBPieces + kVTilePieces, "stage = K rows + value blob + V tile");
+static_assert(kOffT % 16 == 0 && kOffQ % 16 == 0, "staged parts are whole pieces");
 
 static_assert(kStageBytes % 16 == 0, "stage size");
 
@@ -502,8 +508,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     const int64_t vb_step = static_cast<int64_t>(p.Hv) * kVBytes;
     const uint16_t* v_head = p.v + h * kD + part * kDvPerWg;
 
-    // Piece i of the stage is its byte 16 i: the K/Q blob, the value-head
-    // blob, then the V tile (token i / kVPiecesPerRow, channels
+    // Piece i of the stage is its byte 16 i: the K rows, the value-head blob
+    // from T_bb on, then the V tile (token i / kVPiecesPerRow, channels
     // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDvPerWg).
     auto stage = [&](int ci) {
       const int cb = chunk0 + ci;
@@ -516,12 +522,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       for (int j = 0; j < kStageRounds; ++j) {
         const int q = kLoaderThreads * j + lt;
         unsigned char* d = dst + (kLoaderThreads * j + 64 * lw) * 16;
-        if (q < kKQPieces) {
+        if (q < kKPieces) {
           lds_dma16(kqb + q * 16, d);
-        } else if (q < kKQPieces + kVBPieces) {
-          lds_dma16(vbb + (q - kKQPieces) * 16, d);
+        } else if (q < kKPieces + kVBPieces) {
+          lds_dma16(vbb + kOffT + (q - kKPieces) * 16, d);
         } else if (q < kStagePieces) {
-          const int vp = q - kKQPieces - kVBPieces;
+          const int vp = q - kKPieces - kVBPieces;
           const int r = min(vp / kVPiecesPerRow, len - 1);   // rows past the end re-read the last
           lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % kVPiecesPerRow) * 8, d);
         }
@@ -592,7 +598,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 
     for (int ci = 0; ci < n_chunks; ++ci) {
       const unsigned char* B = sm.buf[ci & 1];
-      const unsigned char* VB = B + kKQBytes;
+      // VB + kOffX is item X of the value-head blob (staged from T_bb on)
+      const unsigned char* VB = B + kStageVB - kOffT;
       unsigned char* X = sm.xbuf[ci & 1];
       // K A-fragment (rows 16 tb .. +15 = tokens, 32 dk columns of block kb):
       // the columns kappa(grp, e) are stored together
@@ -615,7 +622,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       };
       // V of tokens 16 tb + 4 grp + e, channel 16 t + col: a transposing load
       // over the row-major bf16 V tile
-      const unsigned char* vtile = VB + kVBytes;
+      const unsigned char* vtile = B + kStageV;
       auto vcol = [&](int t, int tb) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_short4*)(vtile + (16 * tb + 4 * grp + (col >> 2)) * (2 * kDvPerWg) + 32 * t + 8 * (col & 3)));
@@ -772,15 +779,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 
   // ---- output wave: O of chunk ci - 1 during chunk ci ------------------------
   const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-  // Q and P fragments and the per-token scale of a chunk are taken into
-  // registers while its stage is in LDS; the next chunk's copy overwrites it.
+  // Q and P fragments and the per-token scale of chunk ci come from global
+  // memory (L2, prefetched) straight into registers, a chunk before their use.
   half8 fq[16], fp[6];
   float sgl[4];                            // scale gamma of token 16 tb + col
   auto load_q = [&](int ci) {
-    const unsigned char* B = sm.buf[ci & 1];
-    const unsigned char* VB = B + kKQBytes;
+    const int cb = chunk0 + ci;
+    const unsigned char* Qb = p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + kOffQ;
+    const unsigned char* VB = p.vb + (static_cast<int64_t>(cb) * p.Hv + h) * kVBytes;
 #pragma unroll
-    for (int f = 0; f < 16; ++f) fq[f] = *reinterpret_cast<const half8*>(B + kOffQ + f * kFrag + lane * 16);
+    for (int f = 0; f < 16; ++f) fq[f] = *reinterpret_cast<const half8*>(Qb + f * kFrag + lane * 16);
 #pragma unroll
     for (int f = 0; f < 6; ++f) fp[f] = *reinterpret_cast<const half8*>(VB + kOffP + f * kFrag + lane * 16);
 #pragma unroll
