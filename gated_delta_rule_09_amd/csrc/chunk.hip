@@ -42,6 +42,8 @@
 // accumulation is fp32 throughout.  The per-chunk state never leaves the
 // registers, and fragment reads are lane-contiguous 16-byte LDS loads.
 // Work-groups that share a key head get block ids on the same XCD (L2).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -52,9 +54,9 @@ namespace {
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
 constexpr int kThreads = 256;    // prep work-group
-// Scan work-group (32 value channels of one value head): a state wave, an
-// output wave, and two loader waves that copy the next chunk into LDS.
-constexpr int kScanComputeWaves = 2;
+// Scan work-group (32 value channels of one value head): a state wave, two
+// output waves, and two loader waves that copy the next chunk into LDS.
+constexpr int kScanComputeWaves = 3;
 constexpr int kScanLoaderWaves = 2;
 constexpr int kScanThreads = 64 * (kScanComputeWaves + kScanLoaderWaves);
 constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
@@ -777,68 +779,84 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     return;
   }
 
-  // ---- output wave: O of chunk ci - 1 during chunk ci ------------------------
-  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
-  // Q and P fragments and the per-token scale of chunk ci come from global
+  // ---- output waves: O of chunk ci - 1 during chunk ci -----------------------
+  // Output wave ow (0 or 1) forms token blocks 2 ow and 2 ow + 1 of O^T =
+  // scale gamma^T (S0 Q^T) + U^T P^T (rows = value channels 4 grp + e of tile
+  // t, column = token 16 tb + col; the P fragments serve as B operands).  Its
+  // Q and P fragments and per-token scales of chunk ci come from global
   // memory (L2, prefetched) straight into registers, a chunk before their use.
-  half8 fq[16], fp[6];
-  float sgl[4];                            // scale gamma of token 16 tb + col
-  auto load_q = [&](int ci) {
-    const int cb = chunk0 + ci;
-    const unsigned char* Qb = p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + kOffQ;
-    const unsigned char* VB = p.vb + (static_cast<int64_t>(cb) * p.Hv + h) * kVBytes;
+  const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
+  auto output_wave = [&](auto ow_c) {
+    constexpr int ow = decltype(ow_c)::value;
+    constexpr int tb0 = 2 * ow;
+    constexpr int np = ow == 0 ? 2 : 4;    // P fragments of the two token blocks
+    constexpr int p0 = ow == 0 ? 0 : 2;    // first of them: (0,0)(1,0) | (2,0)(2,1)(3,0)(3,1)
+    half8 fq[8], fp[np];
+    float sgl[2];                          // scale gamma of token 16 (tb0 + i) + col
+    auto load_q = [&](int ci) {
+      const int cb = chunk0 + ci;
+      const unsigned char* Qb = p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + kOffQ;
+      const unsigned char* VB = p.vb + (static_cast<int64_t>(cb) * p.Hv + h) * kVBytes;
 #pragma unroll
-    for (int f = 0; f < 16; ++f) fq[f] = *reinterpret_cast<const half8*>(Qb + f * kFrag + lane * 16);
+      for (int f = 0; f < 8; ++f) fq[f] = *reinterpret_cast<const half8*>(Qb + (4 * tb0 + f) * kFrag + lane * 16);
 #pragma unroll
-    for (int f = 0; f < 6; ++f) fp[f] = *reinterpret_cast<const half8*>(VB + kOffP + f * kFrag + lane * 16);
+      for (int f = 0; f < np; ++f) fp[f] = *reinterpret_cast<const half8*>(VB + kOffP + (p0 + f) * kFrag + lane * 16);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      sgl[tb] = *reinterpret_cast<const float*>(VB + kOffDecay + 2 * 256 + (16 * tb + col) * 4);
-  };
-  // O^T = scale gamma^T (S0 Q^T) + U^T P^T: rows = value channels 4 grp + e of
-  // tile t, column = token 16 tb + col; the P fragments serve as B operands
-  auto output = [&](int ci) {
-    const unsigned char* X = sm.xbuf[ci & 1];
-    half8 sB[2][4], u[2][2];
+      for (int i = 0; i < 2; ++i)
+        sgl[i] = *reinterpret_cast<const float*>(VB + kOffDecay + 2 * 256 + (16 * (tb0 + i) + col) * 4);
+    };
+    auto output = [&](int ci) {
+      const unsigned char* X = sm.xbuf[ci & 1];
+      half8 sB[2][4], u[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sB[t][kb] = *reinterpret_cast<const half8*>(X + (4 * t + kb) * kFrag + lane * 16);
+        for (int kb = 0; kb < 4; ++kb) sB[t][kb] = *reinterpret_cast<const half8*>(X + (4 * t + kb) * kFrag + lane * 16);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
-    }
-    const int len = min(kC, seq_len - ci * kC);
-    float* ob = p.o + static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        floatx4 qs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qs = mfma32(sB[t][kb], fq[tb * 4 + kb], qs);
-        floatx4 O;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] = sgl[tb] * qs[e];
-        O = mfma32(u[t][0], fp[tb < 2 ? tb : 2 * tb - 2], O);
-        if (tb >= 2) O = mfma32(u[t][1], fp[2 * tb - 1], O);
-        if (16 * tb + col < len) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * o_rs + 16 * t) = O;
+        for (int j = 0; j < 1 + ow; ++j) u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
       }
+      const int len = min(kC, seq_len - ci * kC);
+      float* ob = p.o + static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int tb = tb0 + i;
+          floatx4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) qs = mfma32(sB[t][kb], fq[4 * i + kb], qs);
+          floatx4 O;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[e] = sgl[i] * qs[e];
+          if (ow == 0) {
+            O = mfma32(u[t][0], fp[i], O);
+          } else {
+            O = mfma32(u[t][0], fp[2 * i], O);
+            O = mfma32(u[t][1 % (1 + ow)], fp[(2 * i + 1) % np], O);
+          }
+          if (16 * tb + col < len) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * o_rs + 16 * t) = O;
+        }
+    };
+    uint32_t sink = 0, tv = 0, tv_prev = 0;
+    if (ow == 0 && n_chunks > 0) tv = touch(min(1, n_chunks - 1));
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      lds_barrier();                       // stage ci in LDS; S0, U of chunk ci - 1 written
+      if (ow == 0) {
+        sink ^= tv_prev;                   // issued two chunks ago
+        tv_prev = tv;
+        tv = touch(min(ci + 2, n_chunks - 1));
+      }
+      if (ci > 0) output(ci - 1);
+      load_q(ci);
+    }
+    sink ^= tv_prev ^ tv;
+    if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
+    lds_barrier();                         // S0, U of the last chunk written
+    if (n_chunks > 0) output(n_chunks - 1);
+    lds_barrier();
   };
-  uint32_t sink = 0, tv = 0, tv_prev = 0;
-  if (n_chunks > 0) tv = touch(min(1, n_chunks - 1));
-  for (int ci = 0; ci < n_chunks; ++ci) {
-    lds_barrier();                         // stage ci in LDS; S0, U of chunk ci - 1 written
-    sink ^= tv_prev;                       // issued two chunks ago
-    tv_prev = tv;
-    tv = touch(min(ci + 2, n_chunks - 1));
-    if (ci > 0) output(ci - 1);
-    load_q(ci);
-  }
-  sink ^= tv_prev ^ tv;
-  if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
-  lds_barrier();                           // S0, U of the last chunk written
-  if (n_chunks > 0) output(n_chunks - 1);
-  lds_barrier();
+  if (w == 1) output_wave(std::integral_constant<int, 0>{});
+  else output_wave(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
