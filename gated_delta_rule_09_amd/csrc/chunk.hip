@@ -652,7 +652,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
         }
       __builtin_amdgcn_sched_barrier(0);
 
-      // phase 1: V, tables | W = K S0^T
+      // phase 1: V, tables | W = K S0^T by token block, so that the solve
+      // below can start on block 0 while later blocks are still in the MFMA
+      // pipe (no fence between the two phases); gamma_L S^T in VALU meanwhile
       short4v vr[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -670,14 +672,23 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) W[t][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) W[t][tb] = mfma32(fk[tb * 4 + kb], sB[t][kb], W[t][tb]);
+      // gamma_L S^T, while the products run (S0 has been read as sB)
+      {
+        const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) W[t][tb] = mfma32(fk[tb * 4 + kb], sB[t][kb], W[t][tb]);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sT[t][dt][e] *= gl;
+      }
 
-      // phase 2: T_bb, -A, K^T fragments | R = b V - b gamma W, U by blockwise
+      // then T_bb, -A, K^T fragments | R = b V - b gamma W, U by blockwise
       // forward substitution (rows = tokens 16 tb + 4 grp + e, column 16 t +
       // col), the two tiles' dependent chains interleaved
       half4 tT[4];
@@ -740,11 +751,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // phase 3: S^T <- gamma_L S^T + K^T (D U)
+      // phase 2: S^T <- (gamma_L S^T) + K^T (D U)
       floatx4 dl[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) dl[tb] = table(3, tb);
-      const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         floatx4 DU[4];
@@ -757,8 +767,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           floatx4 s = sT[t][dt];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] *= gl;
           s = mfma32(ft[2 * dt], d01, s);
           s = mfma32(ft[2 * dt + 1], d23, s);
           sT[t][dt] = s;
