@@ -54,12 +54,12 @@ namespace {
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
 constexpr int kThreads = 256;    // prep work-group
-// Scan work-group (32 value channels of one value head): a state wave, two
-// output waves, and two loader waves that copy the next chunk into LDS.
-constexpr int kScanComputeWaves = 3;
+// Scan work-group (32 value channels of one value head): a state wave, one or
+// two output waves, and two loader waves that copy the next chunk into LDS.
 constexpr int kScanLoaderWaves = 2;
-constexpr int kScanThreads = 64 * (kScanComputeWaves + kScanLoaderWaves);
 constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
+template <int kOutWaves>
+constexpr int scan_threads() { return 64 * (1 + kOutWaves + kScanLoaderWaves); }
 constexpr int kDvPerWg = 32;                       // value channels per scan work-group
 constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value head
 
@@ -463,7 +463,12 @@ __device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
   return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
 }
 
-__global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams p) {
+// kOutWaves = 2 when the work-groups fit the CUs one each (shorter chunk
+// period); 1 when there are more work-groups than CUs, so that two fit on a
+// CU (LDS and 256 VGPRs per wave allow it).
+template <int kOutWaves>
+__global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
+  constexpr int kScanComputeWaves = 1 + kOutWaves;
   __shared__ ScanSmem sm;
 
   // ---- block id -> (sequence rank, value head, value quarter) --------------
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   }
 
   // ---- output waves: O of chunk ci - 1 during chunk ci -----------------------
-  // Output wave ow (0 or 1) forms token blocks 2 ow and 2 ow + 1 of O^T =
+  // Output wave ow forms token blocks tb0 .. tb0 + ntb - 1 of O^T =
   // scale gamma^T (S0 Q^T) + U^T P^T (rows = value channels 4 grp + e of tile
   // t, column = token 16 tb + col; the P fragments serve as B operands).  Its
   // Q and P fragments and per-token scales of chunk ci come from global
@@ -796,21 +801,26 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
   const int64_t o_rs = static_cast<int64_t>(p.Hv) * kD;   // o row stride (floats)
   auto output_wave = [&](auto ow_c) {
     constexpr int ow = decltype(ow_c)::value;
-    constexpr int tb0 = 2 * ow;
-    constexpr int np = ow == 0 ? 2 : 4;    // P fragments of the two token blocks
-    constexpr int p0 = ow == 0 ? 0 : 2;    // first of them: (0,0)(1,0) | (2,0)(2,1)(3,0)(3,1)
-    half8 fq[8], fp[np];
-    float sgl[2];                          // scale gamma of token 16 (tb0 + i) + col
+    constexpr int ntb = 4 / kOutWaves;
+    constexpr int tb0 = ntb * ow;
+    // P fragments in the blob: (0,0)(1,0)(2,0)(2,1)(3,0)(3,1); token block tb
+    // uses fragment tb (tb < 2) or 2 tb - 2 and 2 tb - 1
+    constexpr int p0 = tb0 < 2 ? tb0 : 2 * tb0 - 2;
+    constexpr int tbl = tb0 + ntb - 1;
+    constexpr int np = (tbl < 2 ? tbl : 2 * tbl - 1) - p0 + 1;
+    constexpr bool need_u23 = tbl >= 2;
+    half8 fq[4 * ntb], fp[np];
+    float sgl[ntb];                        // scale gamma of token 16 (tb0 + i) + col
     auto load_q = [&](int ci) {
       const int cb = chunk0 + ci;
       const unsigned char* Qb = p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + kOffQ;
       const unsigned char* VB = p.vb + (static_cast<int64_t>(cb) * p.Hv + h) * kVBytes;
 #pragma unroll
-      for (int f = 0; f < 8; ++f) fq[f] = *reinterpret_cast<const half8*>(Qb + (4 * tb0 + f) * kFrag + lane * 16);
+      for (int f = 0; f < 4 * ntb; ++f) fq[f] = *reinterpret_cast<const half8*>(Qb + (4 * tb0 + f) * kFrag + lane * 16);
 #pragma unroll
       for (int f = 0; f < np; ++f) fp[f] = *reinterpret_cast<const half8*>(VB + kOffP + (p0 + f) * kFrag + lane * 16);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < ntb; ++i)
         sgl[i] = *reinterpret_cast<const float*>(VB + kOffDecay + 2 * 256 + (16 * (tb0 + i) + col) * 4);
     };
     auto output = [&](int ci) {
@@ -821,14 +831,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) sB[t][kb] = *reinterpret_cast<const half8*>(X + (4 * t + kb) * kFrag + lane * 16);
 #pragma unroll
-        for (int j = 0; j < 1 + ow; ++j) u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
+        for (int j = 0; j < (need_u23 ? 2 : 1); ++j)
+          u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
       }
       const int len = min(kC, seq_len - ci * kC);
       float* ob = p.o + static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < ntb; ++i) {
           const int tb = tb0 + i;
           floatx4 qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -836,11 +847,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
           floatx4 O;
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[e] = sgl[i] * qs[e];
-          if (ow == 0) {
-            O = mfma32(u[t][0], fp[i], O);
+          if (tb < 2) {
+            O = mfma32(u[t][0], fp[tb - p0], O);
           } else {
-            O = mfma32(u[t][0], fp[2 * i], O);
-            O = mfma32(u[t][1 % (1 + ow)], fp[(2 * i + 1) % np], O);
+            O = mfma32(u[t][0], fp[2 * tb - 2 - p0], O);
+            O = mfma32(u[t][need_u23 ? 1 : 0], fp[2 * tb - 1 - p0], O);
           }
           if (16 * tb + col < len) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * o_rs + 16 * t) = O;
         }
@@ -863,8 +874,21 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_kernel(ScanParams 
     if (n_chunks > 0) output(n_chunks - 1);
     lds_barrier();
   };
-  if (w == 1) output_wave(std::integral_constant<int, 0>{});
-  else output_wave(std::integral_constant<int, 1>{});
+  if (kOutWaves == 1 || w == 1) output_wave(std::integral_constant<int, 0>{});
+  else output_wave(std::integral_constant<int, kOutWaves - 1>{});
+}
+
+// Compute units of the current device, looked up once per device.
+int compute_units() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -920,7 +944,10 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;
   sp.n_chain_groups = n_seqs * Hk;
   const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kParts;
-  hipLaunchKernelGGL(chunk_scan_kernel, dim3(blocks), dim3(kScanThreads), 0, stream, sp);
+  if (blocks <= compute_units())
+    hipLaunchKernelGGL(chunk_scan_kernel<2>, dim3(blocks), dim3(scan_threads<2>()), 0, stream, sp);
+  else
+    hipLaunchKernelGGL(chunk_scan_kernel<1>, dim3(blocks), dim3(scan_threads<1>()), 0, stream, sp);
   return hipGetLastError();
 }
 
