@@ -9,12 +9,14 @@
 // n_l2 heads of 128 channels (the q and k heads).  fp32 math, bf16 out.
 //
 // Mapping: a thread owns 8 adjacent channels (one 16-byte load per token) and a
-// run of kTile consecutive tokens, keeping the 3-token history in registers so
-// x is read once (plus a 3-token halo per run).  16 lanes cover one 128-channel
-// head, so the L2 sum is a 16-lane DPP reduction.  A work-group spans 2048
-// channels.  Sequence boundaries come from cu_seqlens (binary search at the
-// start of the run, then a forward walk).  The new conv state is written by a
-// second kernel after all reads of the old one are done.
+// run of consecutive tokens (8 for prefill, 1 for a decode batch of one token
+// per sequence), loading every input row of the run before any arithmetic and
+// keeping the 3-token history in registers, so x is read once (plus a 3-token
+// halo per run).  16 lanes cover one 128-channel head, so the L2 sum is a
+// 16-lane DPP reduction.  A work-group spans 2048 channels.  Sequence
+// boundaries come from cu_seqlens (binary search at the start of the run, then
+// a forward walk).  The new conv state is written by a second kernel after all
+// reads of the old one are done.
 #include "common.h"
 #include "launch.h"
 
@@ -22,7 +24,6 @@ namespace gdn {
 
 namespace {
 
-constexpr int kTile = 8;
 constexpr int kThreads = 256;
 constexpr int kChPerThread = 8;
 constexpr int kChPerBlock = kThreads * kChPerThread;
@@ -47,116 +48,136 @@ struct Seqs {
   }
 };
 
-__device__ __forceinline__ void load_x8(const uint16_t* p, float* f) {
-  bf16x8_to_f32(*reinterpret_cast<const uint4*>(p), f);
-}
-
-// History value `back` (1..3) tokens before the start of sequence n, channel
-// group c0: from the conv state (oldest first) or zero.
-__device__ __forceinline__ void load_hist(const uint16_t* conv_state, int n, int C, int c0,
-                                          int back, float* f) {
+// The conv state of sequence n, channels c0 .. c0+7: 24 bf16 (channel-major,
+// three taps oldest first) in three 16-byte loads; tap j of channel i goes to
+// st[j][i].  Zero without a conv state.
+__device__ __forceinline__ void load_state(const uint16_t* conv_state, int n, int C, int c0,
+                                           float (&st)[3][8]) {
   if (!conv_state) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = 0.f;
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st[j][i] = 0.f;
     return;
   }
-  const uint16_t* base = conv_state + (static_cast<int64_t>(n) * C + c0) * 3;
+  const uint4* base = reinterpret_cast<const uint4*>(conv_state + (static_cast<int64_t>(n) * C + c0) * 3);
+  float f[24];
+  bf16x8_to_f32(base[0], f);
+  bf16x8_to_f32(base[1], f + 8);
+  bf16x8_to_f32(base[2], f + 16);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = bf16_to_f32(base[i * 3 + (3 - back)]);
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[j][i] = f[3 * i + j];
 }
 
+// x / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each;
+// the result is rounded to bf16)
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+// Eight floats to eight bf16, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{f[2 * i], f[2 * i + 1]}, bf16x2));
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// A thread owns 8 adjacent channels and kTile consecutive tokens.  All kTile + 3
+// input rows it needs are loaded before any arithmetic, so their latencies
+// overlap; the 3-token history moves through registers.
+template <int kTile>
 __global__ __launch_bounds__(kThreads) void conv1d_kernel(
     const uint16_t* __restrict__ x, int64_t xs, const uint16_t* __restrict__ w,
     const float* __restrict__ bias, uint16_t* __restrict__ y, int64_t ys,
     const uint16_t* __restrict__ conv_state, Seqs seqs, int T_total, int C, int n_l2_ch,
     float l2_eps) {
+  // Lanes past C stay to the end (zero inputs, no stores): the L2 sum is a
+  // 16-lane DPP reduction.
   const int c0 = (blockIdx.y * kThreads + threadIdx.x) * kChPerThread;
   const bool active = c0 < C;
   const int t0 = blockIdx.x * kTile;
   const int t1 = min(t0 + kTile, T_total);
 
-  float wt[8][4], bs[8];
+  // rows t0 - 3 .. t1 - 1 (row j = token t0 - 3 + j); rows outside [0, T) are zero
+  uint4 raw[kTile + 3];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bs[i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wt[i][j] = 0.f;
+  for (int j = 0; j < kTile + 3; ++j) {
+    const int t = t0 - 3 + j;
+    raw[j] = (active && t >= 0 && t < t1) ? *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * xs + c0)
+                                          : uint4{0u, 0u, 0u, 0u};
   }
-  if (active) {
-    const uint4 w0 = *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * 4);
-    const uint4 w1 = *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * 4 + 8);
-    const uint4 w2 = *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * 4 + 16);
-    const uint4 w3 = *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * 4 + 24);
+
+  float wt[8][4], bs[8];
+  {
+    const uint4* wp = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * 4);
     float f[32];
-    bf16x8_to_f32(w0, f);
-    bf16x8_to_f32(w1, f + 8);
-    bf16x8_to_f32(w2, f + 16);
-    bf16x8_to_f32(w3, f + 24);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bf16x8_to_f32(active ? wp[q] : uint4{0u, 0u, 0u, 0u}, f + 8 * q);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) wt[i][j] = f[i * 4 + j];
-    if (bias) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bs[i] = bias[c0 + i];
-    }
+    for (int i = 0; i < 8; ++i) bs[i] = (bias && active) ? bias[c0 + i] : 0.f;
   }
-  const bool l2 = c0 < n_l2_ch;  // uniform over the 16 lanes of a head
+  const bool l2 = c0 < n_l2_ch;          // uniform over the 16 lanes of a head
 
-  // history h[0] = x[t-3], h[1] = x[t-2], h[2] = x[t-1]
+  // history h[0] = x[t-3], h[1] = x[t-2], h[2] = x[t-1] of the current token
   float hist[3][8];
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hist[j][i] = 0.f;
   int n = seqs.find(t0);
   int s = seqs.start(n);
   int e = seqs.end(n);
-  if (active) {
+  {
+    float st[3][8];
+    if (t0 - 3 < s) load_state(active ? conv_state : nullptr, n, C, c0, st);
 #pragma unroll
     for (int b = 1; b <= 3; ++b) {
       const int pos = t0 - b;
-      if (pos >= s) load_x8(x + static_cast<int64_t>(pos) * xs + c0, hist[3 - b]);
-      else load_hist(conv_state, n, C, c0, s - pos, hist[3 - b]);
+      if (pos >= s) {
+        bf16x8_to_f32(raw[3 - b], hist[3 - b]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hist[3 - b][i] = st[3 - (s - pos)][i];
+      }
     }
   }
 
-  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+  for (int j = 0; j < kTile; ++j) {
+    const int t = t0 + j;
+    if (t >= t1) break;
     if (t >= e) {
       // next non-empty sequence starts exactly at t
       do { ++n; } while (seqs.end(n) <= t);
       s = seqs.start(n);
       e = seqs.end(n);
-      if (active) {
-#pragma unroll
-        for (int b = 1; b <= 3; ++b) load_hist(conv_state, n, C, c0, b, hist[3 - b]);
-      }
+      load_state(active ? conv_state : nullptr, n, C, c0, hist);
     }
     float cur[8], out[8];
-    if (active) load_x8(x + static_cast<int64_t>(t) * xs + c0, cur);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cur[i] = 0.f;
-    }
+    bf16x8_to_f32(raw[j + 3], cur);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float acc = wt[i][0] * hist[0][i];
+      float acc = fmaf(wt[i][0], hist[0][i], bs[i]);
       acc = fmaf(wt[i][1], hist[1][i], acc);
       acc = fmaf(wt[i][2], hist[2][i], acc);
       acc = fmaf(wt[i][3], cur[i], acc);
-      acc += bs[i];
-      const float sv = acc / (1.f + expf(-acc));
-      out[i] = sv;
-      ss = fmaf(sv, sv, ss);
+      out[i] = silu(acc);
+      ss = fmaf(out[i], out[i], ss);
     }
     ss = sum16(ss);
     if (l2) {
-      const float inv = 1.f / sqrtf(ss + l2_eps);
+      const float inv = rsqrtf(ss + l2_eps);
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] *= inv;
     }
-    if (active) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * ys + c0) = f32_to_bf16x8(out);
+    if (active) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * ys + c0) = pack_bf16x8(out);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       hist[0][i] = hist[1][i];
@@ -225,9 +246,16 @@ hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const
                          hipStream_t stream) {
   Seqs seqs{cu, n_seqs, (cu || n_seqs == 0) ? 0 : T_total / n_seqs};
   if (T_total > 0) {
-    const dim3 grid((T_total + kTile - 1) / kTile, (C + kChPerBlock - 1) / kChPerBlock);
-    hipLaunchKernelGGL(conv1d_kernel, grid, dim3(kThreads), 0, stream, x, xs, w, bias, y, ys,
-                       conv_state, seqs, T_total, C, n_l2_channels, l2_eps);
+    // one token per sequence (a decode batch): one token per thread
+    const bool batch = n_seqs >= T_total;
+    const int tile = batch ? 1 : 8;
+    const dim3 grid((T_total + tile - 1) / tile, (C + kChPerBlock - 1) / kChPerBlock);
+    if (batch)
+      hipLaunchKernelGGL(conv1d_kernel<1>, grid, dim3(kThreads), 0, stream, x, xs, w, bias, y, ys,
+                         conv_state, seqs, T_total, C, n_l2_channels, l2_eps);
+    else
+      hipLaunchKernelGGL(conv1d_kernel<8>, grid, dim3(kThreads), 0, stream, x, xs, w, bias, y, ys,
+                         conv_state, seqs, T_total, C, n_l2_channels, l2_eps);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
