@@ -116,20 +116,17 @@ static_assert(kStageBytes % 16 == 0, "stage size");
 
 // ---- prep kernel LDS -------------------------------------------------------
 constexpr int kKS = kD + 8;       // K, Q rows (halves)
-constexpr int kAS = kC + 8;       // -A, P rows (halves)
 constexpr int kTS = 16 + 8;       // T_bb rows (halves)
 constexpr int kHeadBatch = 3;     // value heads prepared together
 
-// K and Q are only needed until the K/Q/K^T fragments and the Gram tiles are
-// formed; their space is then reused for the per-value-head matrices of a
-// batch of up to kHeadBatch value heads.
+// K and Q are only needed until the K rows, Q fragments and Gram tiles are
+// formed; their space is then reused for the diagonal blocks of A and the
+// inverses T_bb of a batch of up to kHeadBatch value heads.
 struct PrepKQ {
   _Float16 K[kC * kKS];
   _Float16 Q[kC * kKS];
 };
 struct PrepHeads {
-  _Float16 An[kHeadBatch][kC * kAS];
-  _Float16 P[kHeadBatch][kC * kAS];
   float Ad[kHeadBatch][4 * 16 * 16];
   _Float16 T[kHeadBatch][4 * 16 * kTS];
 };
@@ -173,62 +170,87 @@ __device__ __forceinline__ void put8(unsigned char* dst, const half4 v) {
   *reinterpret_cast<half4*>(dst) = v;
 }
 
-// Gram tile t of the list (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1)
-// (3,2) (3,3): block row and block column.
-__host__ __device__ constexpr int gram_row(int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); }
-__host__ __device__ constexpr int gram_col(int t) { return t - (gram_row(t) * (gram_row(t) + 1)) / 2; }
+// Gram tiles of a wave, in the transposed orientation C' = X_j Y_b^T, so
+// that lane (col, grp) holds (Y X^T)[16 b + col][16 j + 4 grp + e], e = 0..3:
+// the four values an MFMA A-operand fragment (row 16 b + col, columns
+// 16 j + 4 grp ..) takes.  Tile k of wave W: Q K^T (isq) or K K^T, block row b,
+// block column j.  The waves' lists complete whole fragments:
+//   wave 0: P (0,0) (1,0) (1,1) (2,2), A (0,0)
+//   wave 1: P (2,0) (2,1) (3,0) (3,1), A (1,1)
+//   wave 2: P (3,2) (3,3), A (1,0) (3,2) (2,2)
+//   wave 3: A (2,0) (2,1) (3,0) (3,1) (3,3)
+struct GramTile { bool isq; int b, j; };
+__host__ __device__ constexpr GramTile gram_tile(int W, int k) {
+  constexpr GramTile t[4][5] = {
+      {{true, 0, 0}, {true, 1, 0}, {true, 1, 1}, {true, 2, 2}, {false, 0, 0}},
+      {{true, 2, 0}, {true, 2, 1}, {true, 3, 0}, {true, 3, 1}, {false, 1, 1}},
+      {{true, 3, 2}, {true, 3, 3}, {false, 1, 0}, {false, 3, 2}, {false, 2, 2}},
+      {{false, 2, 0}, {false, 2, 1}, {false, 3, 0}, {false, 3, 1}, {false, 3, 3}}};
+  return t[W][k];
+}
 
-// Wave W's share of the elementwise step: its Gram tiles 5W .. 5W+4 of
-// [K K^T (10), Q K^T (10)] become, for each of the nb heads of the batch,
-//   K K^T, diagonal tile:   A  = strict_lower(b E * K K^T)      (fp32, LDS)
-//   K K^T, off-diagonal:   -A  = -(b E * K K^T)                 (fp16, LDS)
-//   Q K^T:                  P  = scale * lower(E * Q K^T)       (fp16, LDS)
-// with E_ij = exp(G_i - G_j).  Lane (col, grp) holds rows 4 grp .. +3 of
-// column col of a tile (MFMA accumulator layout).
+// Wave W's share of the elementwise step, for head vh of the batch (G, bet in
+// LDS), with E_il = exp(G_i - G_l), i = 16 b + col, l = 16 j + 4 grp + e:
+//   Q K^T:                  P  = scale * lower(E * Q K^T)  -> P fragments (global)
+//   K K^T, off-diagonal:   -A  = -(b E * K K^T)            -> -A fragments (global)
+//   K K^T, diagonal:        A  = strict_lower(b E * K K^T) -> Ad (fp32, LDS)
+// P fragment f covers block row tb, columns 32 kb .. +31: (0,0)(1,0)(2,0)(2,1)(3,0)(3,1).
 template <int W>
-__device__ __forceinline__ void prep_elementwise(PrepSmem& sm, const floatx4 (&gram)[5], int nb,
-                                                 int col, int grp, float scale) {
+__device__ __forceinline__ void prep_elementwise(PrepSmem& sm, const floatx4 (&gram)[5], int vh,
+                                                 unsigned char* vb, int lane, int col, int grp,
+                                                 float scale) {
+  half4 v[5];
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    constexpr int kJobs = 5 * W;
-    const int job = kJobs + jj;
-    const bool isq = job >= 10;
-    const int t = isq ? job - 10 : job;
-    const int b = gram_row(t);
-    const int j = gram_col(t);
-    const int jc = 16 * j + col;
-    const int i0 = 16 * b + 4 * grp;
+  for (int k = 0; k < 5; ++k) {
+    constexpr GramTile dummy = gram_tile(W, 0);
+    (void)dummy;
+    const GramTile t = gram_tile(W, k);
+    const int i = 16 * t.b + col;
+    const float Gi = sm.G[vh][i];
+    const floatx4 Gl = *reinterpret_cast<const floatx4*>(&sm.G[vh][16 * t.j + 4 * grp]);
+    if (t.isq) {
 #pragma unroll
-    for (int vh = 0; vh < kHeadBatch; ++vh) {
-      if (vh >= nb) break;
-      const floatx4 Gi = *reinterpret_cast<const floatx4*>(&sm.G[vh][i0]);
-      const float Gj = sm.G[vh][jc];
-      if (isq) {
+      for (int e = 0; e < 4; ++e) {
+        const float x = scale * __expf(Gi - Gl[e]) * gram[k][e];
+        v[k][e] = static_cast<_Float16>((t.b > t.j || 4 * grp + e <= col) ? x : 0.f);
+      }
+    } else {
+      const float bi = sm.bet[vh][i];
+      floatx4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = scale * __expf(Gi[e] - Gj) * gram[jj][e];
-          sm.u.vh.P[vh][(i0 + e) * kAS + jc] =
-              static_cast<_Float16>((b > j || jc <= i0 + e) ? v : 0.f);
-        }
+      for (int e = 0; e < 4; ++e) a[e] = bi * __expf(Gi - Gl[e]) * gram[k][e];
+      if (t.b == t.j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = (4 * grp + e < col) ? a[e] : 0.f;
+        *reinterpret_cast<floatx4*>(&sm.u.vh.Ad[vh][(t.b * 16 + col) * 16 + 4 * grp]) = a;
       } else {
-        const floatx4 Bi = *reinterpret_cast<const floatx4*>(&sm.bet[vh][i0]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = Bi[e] * __expf(Gi[e] - Gj) * gram[jj][e];
-          if (b == j)
-            sm.u.vh.Ad[vh][(b * 16 + 4 * grp + e) * 16 + col] = (jc < i0 + e) ? a : 0.f;
-          else
-            sm.u.vh.An[vh][(i0 + e) * kAS + jc] = static_cast<_Float16>(-a);
-        }
+        for (int e = 0; e < 4; ++e) v[k][e] = static_cast<_Float16>(-a[e]);
       }
     }
   }
+  const half4 z4 = {0, 0, 0, 0};
+  if (W == 0) {
+    put16(vb + kOffP + 0 * kFrag + lane * 16, cat8(v[0], z4));
+    put16(vb + kOffP + 1 * kFrag + lane * 16, cat8(v[1], v[2]));
+    put16(vb + kOffP + 3 * kFrag + lane * 16, cat8(v[3], z4));
+  } else if (W == 1) {
+    put16(vb + kOffP + 2 * kFrag + lane * 16, cat8(v[0], v[1]));
+    put16(vb + kOffP + 4 * kFrag + lane * 16, cat8(v[2], v[3]));
+  } else if (W == 2) {
+    put16(vb + kOffP + 5 * kFrag + lane * 16, cat8(v[0], v[1]));
+    put8(vb + kOffAn10 + lane * 8, v[2]);
+    put8(vb + kOffAn32 + lane * 8, v[3]);
+  } else {
+    put16(vb + kOffAn2 + lane * 16, cat8(v[0], v[1]));
+    put16(vb + kOffAn3 + lane * 16, cat8(v[2], v[3]));
+  }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
-  const int kh = blockIdx.y;
-  const int c = blockIdx.x;
+  const int kh = blockIdx.x;
+  const int c = blockIdx.y;
   int t0, len;
   if (p.cu) {
     if (c >= p.chunk_off[p.n_seqs]) return;
@@ -247,19 +269,40 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  // g and beta of the first head batch, one token per lane (wave w, head w);
-  // issued first so their latency overlaps the K/Q loads
+  // g and beta of value head vh, one token per lane
   auto load_gb = [&](int vh, float& gv, float& bv) {
     const bool valid = lane < len;
     const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + kh * p.group + vh;
     gv = valid ? p.g[gi] : 0.f;
     bv = valid ? p.beta[gi] : 0.f;
   };
-  float gv = 0.f, bv = 0.f;
-  if (w < min(kHeadBatch, p.group)) load_gb(w, gv, bv);
+  // decay tables of value head vb0 + w (wave w, lane = token): G = inclusive
+  // cumsum of g, then b, b gamma, scale gamma, exp(G_L - G) and gamma_L
+  auto decay = [&](int vb0, float gv, float bv) {
+    const int h = kh * p.group + vb0 + w;
+    unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
+    float G = gv;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float up = __shfl_up(G, d, 64);
+      if (lane >= d) G += up;
+    }
+    const float Glast = __shfl(G, 63, 64);
+    const float gam = __expf(G);
+    sm.G[w][lane] = G;
+    sm.bet[w][lane] = bv;
+    float* dec = reinterpret_cast<float*>(vb + kOffDecay);
+    dec[lane] = bv;
+    dec[64 + lane] = bv * gam;
+    dec[128 + lane] = p.scale * gam;
+    dec[192 + lane] = __expf(Glast - G);
+    if (lane == 0) *reinterpret_cast<float*>(vb + kOffGL) = __expf(Glast);
+  };
 
-  // ---- K, Q -> LDS (fp16), rows past the chunk end zeroed ------------------
-  // (64 rows x 16 pieces of 8 channels; all eight loads issued first)
+  // ---- K, Q loads (64 rows x 16 pieces of 8 channels), issued first --------
+  float gv = 0.f, bv = 0.f;
+  const int nb0 = min(kHeadBatch, p.group);
+  if (w < nb0) load_gb(w, gv, bv);
   uint4 kraw[4], qraw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -269,6 +312,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     kraw[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
     qraw[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
   }
+  // the first batch's decay tables while the K, Q loads are in flight
+  if (w < nb0) decay(0, gv, bv);
+  // ---- K, Q -> LDS (fp16), rows past the chunk end zeroed ------------------
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int piece = tid + kThreads * j;
@@ -305,122 +351,75 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
           lds_a32(sm.u.kq.Q, kKS, 16 * (f >> 2) + col, 32 * (f & 3), grp));
   }
 
-  // ---- Gram tiles: wave w owns lower tiles 5w .. 5w+4 of the list
-  // [K K^T (10 tiles), Q K^T (10 tiles)], tile t -> (b, j) in order
-  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3).
+  // ---- this wave's five Gram tiles, transposed orientation ------------------
   floatx4 gram[5];
+  auto gram_tiles = [&](auto w_c) {
+    constexpr int W = decltype(w_c)::value;
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int job = 5 * w + jj;
-    const int t = job >= 10 ? job - 10 : job;
-    const int b = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-    const int j = t - (b * (b + 1)) / 2;
-    const _Float16* X = job >= 10 ? sm.u.kq.Q : sm.u.kq.K;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 5; ++k) {
+      const GramTile t = gram_tile(W, k);
+      const _Float16* Y = t.isq ? sm.u.kq.Q : sm.u.kq.K;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < kD; kb += 32)
-      acc = mfma32(lds_a32(X, kKS, 16 * b + col, kb, grp), lds_a32(sm.u.kq.K, kKS, 16 * j + col, kb, grp), acc);
-    gram[jj] = acc;
+      for (int kb = 0; kb < kD; kb += 32)
+        acc = mfma32(lds_a32(sm.u.kq.K, kKS, 16 * t.j + col, kb, grp), lds_a32(Y, kKS, 16 * t.b + col, kb, grp), acc);
+      gram[k] = acc;
+    }
+  };
+  switch (w) {
+    case 0: gram_tiles(std::integral_constant<int, 0>{}); break;
+    case 1: gram_tiles(std::integral_constant<int, 1>{}); break;
+    case 2: gram_tiles(std::integral_constant<int, 2>{}); break;
+    default: gram_tiles(std::integral_constant<int, 3>{}); break;
   }
   lds_barrier();   // K and Q are no longer read: their space becomes the heads'
 
   // ---- the key head's value heads, up to kHeadBatch at a time --------------
   for (int vb0 = 0; vb0 < p.group; vb0 += kHeadBatch) {
     const int nb = min(kHeadBatch, p.group - vb0);
-
-    // decay tables: wave w scans g of head vb0 + w (lane = token)
-    if (w < nb) {
-      if (vb0 > 0) load_gb(vb0 + w, gv, bv);
-      const int h = kh * p.group + vb0 + w;
-      unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
-      float G = gv;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float up = __shfl_up(G, d, 64);
-        if (lane >= d) G += up;
+    if (vb0 > 0) {
+      if (w < nb) {
+        load_gb(vb0 + w, gv, bv);
+        decay(vb0, gv, bv);
       }
-      const float Glast = __shfl(G, 63, 64);
-      const float gam = __expf(G);
-      sm.G[w][lane] = G;
-      sm.bet[w][lane] = bv;
-      float* dec = reinterpret_cast<float*>(vb + kOffDecay);
-      dec[lane] = bv;
-      dec[64 + lane] = bv * gam;
-      dec[128 + lane] = p.scale * gam;
-      dec[192 + lane] = __expf(Glast - G);
-      if (lane == 0) *reinterpret_cast<float*>(vb + kOffGL) = __expf(Glast);
+      lds_barrier();   // G, bet of the batch ready
     }
-    // P tiles above the diagonal blocks that the fragments (0,0) and (2,1)
-    // cover are zero
-    for (int i = tid; i < kHeadBatch * 2 * 256; i += kThreads) {
-      const int vh = i >> 9, t = (i >> 8) & 1, rr = (i >> 4) & 15, cc = i & 15;
-      const int r0 = t ? 32 : 0;
-      sm.u.vh.P[vh][(r0 + rr) * kAS + r0 + 16 + cc] = static_cast<_Float16>(0.f);
-    }
-    lds_barrier();   // G, bet of the batch ready
 
-    // -A (off-diagonal tiles, fp16), A (diagonal tiles, fp32) and P for every
-    // head of the batch from this wave's Gram tiles (tile list fixed per wave
-    // at compile time)
-    switch (w) {
-      case 0: prep_elementwise<0>(sm, gram, nb, col, grp, p.scale); break;
-      case 1: prep_elementwise<1>(sm, gram, nb, col, grp, p.scale); break;
-      case 2: prep_elementwise<2>(sm, gram, nb, col, grp, p.scale); break;
-      default: prep_elementwise<3>(sm, gram, nb, col, grp, p.scale); break;
+    // P and -A fragments of every head of the batch from this wave's Gram
+    // tiles; A's diagonal blocks to LDS
+    for (int vh = 0; vh < nb; ++vh) {
+      unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + kh * p.group + vb0 + vh) * kVBytes;
+      switch (w) {
+        case 0: prep_elementwise<0>(sm, gram, vh, vb, lane, col, grp, p.scale); break;
+        case 1: prep_elementwise<1>(sm, gram, vh, vb, lane, col, grp, p.scale); break;
+        case 2: prep_elementwise<2>(sm, gram, vh, vb, lane, col, grp, p.scale); break;
+        default: prep_elementwise<3>(sm, gram, vh, vb, lane, col, grp, p.scale); break;
+      }
     }
-    lds_barrier();   // -A, A_diag, P of the batch ready
+    lds_barrier();   // A_diag of the batch ready
 
     if (w < nb) {
       // T_bb = (I + A_bb)^-1 of head vb0 + w by forward substitution: lane =
-      // 16 blk + column, all four diagonal blocks at once
+      // 16 blk + column, all four diagonal blocks at once.  Right-looking:
+      // once t_j is known it leaves every later row, each row still
+      // subtracting its terms in order j = 0, 1, ...
       const int h = kh * p.group + vb0 + w;
       unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
       const int blk = lane >> 4;
       const float* Ab = sm.u.vh.Ad[w] + blk * 256;
       float tt[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == col) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) tt[i] = (i == col) ? 1.f : 0.f;
 #pragma unroll
-        for (int kk = 0; kk < i; ++kk) acc = fmaf(-Ab[i * 16 + kk], tt[kk], acc);
-        tt[i] = acc;
-      }
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) tt[i] = fmaf(-Ab[i * 16 + j], tt[j], tt[i]);
       _Float16* Tw = sm.u.vh.T[w];
 #pragma unroll
       for (int i = 0; i < 16; ++i) Tw[(blk * 16 + i) * kTS + col] = static_cast<_Float16>(tt[i]);
-      // T (same-wave LDS write then read: in order within the wave) and -A
-      // fragments of this head
-      half4 tf[4];
+      // T fragments (same-wave LDS write then read: in order within the wave)
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) tf[bb] = lds_a16(Tw, kTS, bb * 16 + col, 0, grp);
-      const _Float16* An = sm.u.vh.An[w];
-      const half4 a10 = lds_a16(An, kAS, 16 + col, 0, grp);
-      const half8 a2 = lds_a32(An, kAS, 32 + col, 0, grp);
-      const half8 a3 = lds_a32(An, kAS, 48 + col, 0, grp);
-      const half4 a32 = lds_a16(An, kAS, 48 + col, 32, grp);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) put8(vb + kOffT + bb * kFrag16 + lane * 8, tf[bb]);
-      put8(vb + kOffAn10 + lane * 8, a10);
-      put16(vb + kOffAn2 + lane * 16, a2);
-      put16(vb + kOffAn3 + lane * 16, a3);
-      put8(vb + kOffAn32 + lane * 8, a32);
-    } else {
-      // the other waves write the P fragments (0,0)(1,0)(2,0)(2,1)(3,0)(3,1)
-      // of the batch, one head at a time
-      for (int vh = w - nb; vh < nb; vh += 4 - nb) {
-        const int h = kh * p.group + vb0 + vh;
-        unsigned char* vb = p.vb + (static_cast<int64_t>(c) * p.Hv + h) * kVBytes;
-        const _Float16* P = sm.u.vh.P[vh];
-        half8 pf[6];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) {
-          const int tb = f < 2 ? f : (f < 4 ? 2 : 3);
-          const int kb = (f == 3 || f == 5) ? 32 : 0;
-          pf[f] = lds_a32(P, kAS, 16 * tb + col, kb, grp);
-        }
-#pragma unroll
-        for (int f = 0; f < 6; ++f) put16(vb + kOffP + f * kFrag + lane * 16, pf[f]);
-      }
+      for (int bb = 0; bb < 4; ++bb) put8(vb + kOffT + bb * kFrag16 + lane * 8, lds_a16(Tw, kTS, bb * 16 + col, 0, grp));
     }
     if (vb0 + kHeadBatch < p.group) lds_barrier();   // before the next batch overwrites
   }
@@ -933,7 +932,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
     pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
     pp.scale = scale;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(n_chunk_slots, Hk), dim3(kThreads), 0, stream, pp);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
