@@ -6,7 +6,8 @@ B = 1, 16 key heads / 48 value heads, head dim 128, random fp32 initial state,
 fp32 outputs and final state -- one `gdn_chunk_fwd` launch per step, inputs
 resident in HBM.  The same run also times, as extra legs in the same JSON line:
   decode  one batched decode step, 256 sequences, fp32 state [256,48,128,128]
-          updated in place (state GB/s), plus the batch-mode conv-state update;
+          updated in place (state GB/s), plus the batch-mode conv-state update
+          and a 4-tokens-per-sequence step (gdn_decode_tokens);
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm;
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
@@ -119,12 +120,35 @@ def leg_decode(args, ops, synth, torch):
 
     cev, cwall = time_leg(conv_step, args.steps, args.warmup)
     cbytes = N * y.shape[1] * 2 * 2 + N * y.shape[1] * 3 * 2 * 2 + y.shape[1] * 4 * 2
+
+    # several tokens per sequence in one pass over the state (gdn_decode_tokens)
+    NT = 4
+    gen = torch.Generator(device="cuda").manual_seed(1005)
+
+    def unit(shape):
+        a = torch.randn(shape, generator=gen, device="cuda")
+        return (a / a.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    tq, tk = unit((N * NT, HK, D)), unit((N * NT, HK, D))
+    tv = torch.randn((N * NT, HV, D), generator=gen, device="cuda").to(torch.bfloat16)
+    tg = torch.rand((N * NT, HV), generator=gen, device="cuda") * -0.1
+    tb = torch.sigmoid(torch.randn((N * NT, HV), generator=gen, device="cuda"))
+    to = torch.empty((N * NT, HV, D), dtype=torch.float32, device="cuda")
+
+    def tokens_step():
+        ops.gdn_decode_tokens(tq, tk, tv, tg, tb, di["state"], NT, o=to)
+
+    tev, twall = time_leg(tokens_step, args.steps, args.warmup)
     res = dict(n_seqs=N, event_ms=ev, wall_ms=wall, state_bytes=sbytes,
                state_gbps=sbytes / (ev * 1e-3) / 1e9,
                frac_hbm=sbytes / (ev * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-               conv_event_ms=cev, conv_alg_bytes=cbytes, conv_gbps=cbytes / (cev * 1e-3) / 1e9)
+               conv_event_ms=cev, conv_alg_bytes=cbytes, conv_gbps=cbytes / (cev * 1e-3) / 1e9,
+               tokens_n=NT, tokens_event_ms=tev,
+               tokens_state_gbps=sbytes / (tev * 1e-3) / 1e9,
+               tokens_per_s=N * NT / (tev * 1e-3))
     log(f"[decode] {ev:.3f} ms/step, state {res['state_gbps']:.0f} GB/s "
-        f"({100 * res['frac_hbm']:.1f}% of HBM); conv update {cev * 1e3:.1f} us")
+        f"({100 * res['frac_hbm']:.1f}% of HBM); conv update {cev * 1e3:.1f} us; "
+        f"{NT} tokens/sequence: {tev:.3f} ms, {res['tokens_per_s'] / 1e6:.2f} M tok/s")
     return res
 
 
@@ -306,7 +330,10 @@ def main():
         line["decode"] = {"state_GBps": round(d["state_gbps"], 1),
                           "frac_hbm": round(d["frac_hbm"], 4),
                           "launch_ms": round(d["event_ms"], 4),
-                          "conv_update_ms": round(d["conv_event_ms"], 4)}
+                          "conv_update_ms": round(d["conv_event_ms"], 4),
+                          "tokens4": {"launch_ms": round(d["tokens_event_ms"], 4),
+                                      "tokens_per_s": round(d["tokens_per_s"], 1),
+                                      "state_GBps": round(d["tokens_state_gbps"], 1)}}
     if "mixer" in out:
         line["mixer_T8192"] = {"tokens_per_s": round(out["mixer"]["tokens_per_s"], 1),
                                "ms": round(out["mixer"]["event_ms"], 4)}

@@ -284,6 +284,50 @@ gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* 
                     "gdn_decode_step launch");
 }
 
+gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                             int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* state_slot, int32_t n_slots, float* o,
+                             int32_t n_seqs, int32_t n_tokens, int32_t Hk, int32_t Hv,
+                             int32_t dk, int32_t dv, float scale, void* stream) {
+  if (n_seqs > 0 && (!q || !k || !v || !g || !beta || !state || !o))
+    return fail(GDN_ERR_NULL, "gdn_decode_tokens: q, k, v, g, beta, state and o are required");
+  if (n_seqs < 0 || n_slots < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: bad sizes or Hv %% Hk != 0");
+  if (n_tokens < 1 || n_tokens > 8)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_tokens: n_tokens must be 1..8");
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_tokens: dk = dv = 128 only");
+  if (!state_slot && n_slots < n_seqs)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: n_slots < n_seqs without a slot map");
+  if (q_stride < static_cast<int64_t>(Hk) * dk || k_stride < static_cast<int64_t>(Hk) * dk ||
+      v_stride < static_cast<int64_t>(Hv) * dv || q_stride % 8 || k_stride % 8 || v_stride % 8)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: strides too small or not multiples of 8");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) ||
+      !aligned(o, 4) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(state_slot, 4))
+    return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: q, k, v and state must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: scale must be finite");
+  if (static_cast<int64_t>(n_seqs) * Hv > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_tokens: too many (sequence, head) pairs");
+  const int64_t rows = static_cast<int64_t>(n_seqs) * n_tokens;
+  const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
+  const Range rs = range_of(state, n_slots, ssz, ssz, 4);
+  const Range ro = range_of(o, rows, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, 4);
+  const Range rq = range_of(q, rows, q_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rk = range_of(k, rows, k_stride, static_cast<int64_t>(Hk) * dk, 2);
+  const Range rv = range_of(v, rows, v_stride, static_cast<int64_t>(Hv) * dv, 2);
+  const Range rg = range_of(g, rows, Hv, Hv, 4);
+  const Range rb = range_of(beta, rows, Hv, Hv, 4);
+  const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl, &rs})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_decode_tokens: o overlaps an input or the state");
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl})
+    if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_tokens: state overlaps an input");
+  return hip_status(gdn::launch_decode_tokens(q, q_stride, k, k_stride, v, v_stride, g, beta, state,
+                                              state_slot, o, n_seqs, n_tokens, Hk, Hv, scale,
+                                              static_cast<hipStream_t>(stream)),
+                    "gdn_decode_tokens launch");
+}
+
 gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
                              const float* w, void* out, int32_t out_is_bf16, int64_t rows,
                              int32_t Hv, int32_t dv, float eps, void* stream) {

@@ -103,7 +103,138 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   }
 }
 
+// kT consecutive tokens of each sequence in one pass over the state: the
+// thread's rows stay in registers while the tokens are applied in order, each
+// with the arithmetic above (both dot products from the row before that
+// token), so kT tokens cost one read and one write of the state.  Token t of
+// sequence n is row n * kT + t of q, k, v, g, beta and o.
+template <int kT, bool kSlots>
+__global__ __launch_bounds__(kThreads) void decode_tokens_kernel(
+    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
+    int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    const int32_t* __restrict__ slots, float* __restrict__ o, int Hk, int Hv, float scale) {
+  const int n = blockIdx.x / Hv;
+  const int h = blockIdx.x - n * Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int p = tid & 7;
+  const int rg = tid >> 3;
+  const int slot = kSlots ? slots[n] : n;
+  float* S = state + (static_cast<int64_t>(slot) * Hv + h) * (kD * kD);
+
+  floatx4 s[kRows][4];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s[r][j] = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(S + (rg + kRowStep * r) * kD + 4 * (p + 8 * j)));
+
+  // every token's k, q (this lane's 16 channels, bf16 pairs), g, beta and the
+  // thread's two v entries, all issued before the arithmetic
+  uint2 kb[kT][4], qb[kT][4];
+  float gt[kT], bt[kT], vt[kT][kRows];
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    const int64_t row = static_cast<int64_t>(n) * kT + t;
+    const uint16_t* kp = k + row * k_stride + kh * kD;
+    const uint16_t* qp = q + row * q_stride + kh * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kb[t][j] = *reinterpret_cast<const uint2*>(kp + 4 * (p + 8 * j));
+      qb[t][j] = *reinterpret_cast<const uint2*>(qp + 4 * (p + 8 * j));
+    }
+    gt[t] = g[row * Hv + h];
+    bt[t] = beta[row * Hv + h];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) vt[t][r] = bf16_to_f32(v[row * v_stride + h * kD + rg + kRowStep * r]);
+  }
+
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    float kk[16], qq[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kk[4 * j + 0] = __uint_as_float(kb[t][j].x << 16);
+      kk[4 * j + 1] = __uint_as_float(kb[t][j].x & 0xffff0000u);
+      kk[4 * j + 2] = __uint_as_float(kb[t][j].y << 16);
+      kk[4 * j + 3] = __uint_as_float(kb[t][j].y & 0xffff0000u);
+      qq[4 * j + 0] = __uint_as_float(qb[t][j].x << 16);
+      qq[4 * j + 1] = __uint_as_float(qb[t][j].x & 0xffff0000u);
+      qq[4 * j + 2] = __uint_as_float(qb[t][j].y << 16);
+      qq[4 * j + 3] = __uint_as_float(qb[t][j].y & 0xffff0000u);
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kq += kk[j] * qq[j];
+    kq = sum8(kq);
+    const float a = expf(gt[t]);
+    const float b = bt[t];
+    float* op = o + ((static_cast<int64_t>(n) * kT + t) * Hv + h) * kD;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int row = rg + kRowStep * r;
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sk += s[r][j][0] * kk[4 * j] + s[r][j][1] * kk[4 * j + 1] + s[r][j][2] * kk[4 * j + 2] +
+              s[r][j][3] * kk[4 * j + 3];
+        sq += s[r][j][0] * qq[4 * j] + s[r][j][1] * qq[4 * j + 1] + s[r][j][2] * qq[4 * j + 2] +
+              s[r][j][3] * qq[4 * j + 3];
+      }
+      sk = sum8(sk);
+      sq = sum8(sq);
+      const float u = b * (vt[t][r] - a * sk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[r][j][i] = a * s[r][j][i] + u * kk[4 * j + i];
+      if (p == 0) op[row] = scale * (a * sq + u * kq);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_nontemporal_store(s[r][j], reinterpret_cast<floatx4*>(S + (rg + kRowStep * r) * kD + 4 * (p + 8 * j)));
+}
+
+template <int kT>
+void launch_tokens(dim3 grid, hipStream_t stream, const uint16_t* q, int64_t q_stride,
+                   const uint16_t* k, int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                   const float* g, const float* beta, float* state, const int32_t* state_slot,
+                   float* o, int Hk, int Hv, float scale) {
+  if (state_slot)
+    hipLaunchKernelGGL((decode_tokens_kernel<kT, true>), grid, dim3(kThreads), 0, stream, q, q_stride, k,
+                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+  else
+    hipLaunchKernelGGL((decode_tokens_kernel<kT, false>), grid, dim3(kThreads), 0, stream, q, q_stride, k,
+                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+}
+
 }  // namespace
+
+hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                                int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                                const float* g, const float* beta, float* state,
+                                const int32_t* state_slot, float* o, int n_seqs, int n_tokens,
+                                int Hk, int Hv, float scale, hipStream_t stream) {
+  if (n_seqs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv));
+  switch (n_tokens) {
+    case 1: launch_tokens<1>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 2: launch_tokens<2>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 3: launch_tokens<3>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 4: launch_tokens<4>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 5: launch_tokens<5>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 6: launch_tokens<6>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 7: launch_tokens<7>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 8: launch_tokens<8>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
                               int64_t k_stride, const uint16_t* v, int64_t v_stride,

@@ -14,6 +14,12 @@ hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_
                               const int32_t* state_slot, float* o, int n_seqs, int Hk, int Hv,
                               float scale, hipStream_t stream);
 
+hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                                int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                                const float* g, const float* beta, float* state,
+                                const int32_t* state_slot, float* o, int n_seqs, int n_tokens,
+                                int Hk, int Hv, float scale, hipStream_t stream);
+
 hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const float* bias,
                          uint16_t* y, int64_t ys, uint16_t* conv_state, const int32_t* cu,
                          int n_seqs, int T_total, int C, int n_l2_channels, float l2_eps,
@@ -25,7 +31,7 @@ hipError_t launch_gated_rmsnorm(const float* o, const uint16_t* z, int64_t zs, c
 
 // Workspace of the chunked prefill (each piece 256-byte aligned):
 //   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]
-//   | K/Q/K^T fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]
+//   | K rows + Q fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]
 struct ChunkWorkspace {
   size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, total;
 };

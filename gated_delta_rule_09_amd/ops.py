@@ -34,6 +34,8 @@ _SIGS = {
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "gdn_decode_tokens": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
+                                 _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
 }
@@ -230,6 +232,35 @@ def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                                _ptr(g), _ptr(beta), _ptr(state), _ptr(state_slot), state.shape[0],
                                _ptr(o), N, Hk, Hv, dk, dv, scale, _stream())
     _check(st, "gdn_decode_step")
+    return o
+
+
+def gdn_decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, state: torch.Tensor, n_tokens: int, *,
+                      state_slot: Optional[torch.Tensor] = None, scale: float = 1.0,
+                      o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """n_tokens consecutive tokens per sequence (rows n * n_tokens + t of q, k, v,
+    g, beta and o); state [n_slots, Hv, 128, 128] fp32 updated in place."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+        _inner_contig(t, nm)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(state, "state", torch.float32, 4)
+    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
+        raise ValueError("g, beta and state must be contiguous")
+    rows, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if n_tokens < 1 or rows % n_tokens:
+        raise ValueError("rows must be a multiple of n_tokens")
+    if state_slot is not None:
+        _need(state_slot, "state_slot", torch.int32, 1)
+    if o is None:
+        o = torch.empty((rows, Hv, dv), dtype=torch.float32, device=q.device)
+    st = lib().gdn_decode_tokens(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                                 _ptr(g), _ptr(beta), _ptr(state), _ptr(state_slot), state.shape[0],
+                                 _ptr(o), rows // n_tokens, n_tokens, Hk, Hv, dk, dv, scale, _stream())
+    _check(st, "gdn_decode_tokens")
     return o
 
 

@@ -60,7 +60,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -183,6 +183,32 @@ gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* 
                            const float* beta, float* state, const int32_t* state_slot,
                            int32_t n_slots, float* o, int32_t n_seqs, int32_t Hk, int32_t Hv,
                            int32_t dk, int32_t dv, float scale, void* stream);
+
+/*
+ * gdn_decode_tokens -- n_tokens (1..8) consecutive tokens per sequence, state
+ * updated in place: the rule above applied to the tokens in order, as
+ * n_tokens successive gdn_decode_step calls would, but reading and writing
+ * each state once.  For serving steps that append several tokens to each
+ * cached sequence (e.g. verifying drafted tokens).  Token t of sequence n is
+ * row n * n_tokens + t of every per-token array:
+ *
+ *   q, k        [n_seqs * n_tokens, Hk, dk] bf16, row strides q_stride, k_stride
+ *   v           [n_seqs * n_tokens, Hv, dv] bf16, row stride v_stride
+ *   g, beta     [n_seqs * n_tokens, Hv] fp32, contiguous
+ *   state       [n_slots, Hv, dv, dk] fp32, read and written in place
+ *   state_slot  [n_seqs] int32 device array or NULL, as for gdn_decode_step
+ *   o           [n_seqs * n_tokens, Hv, dv] fp32; must not overlap state or
+ *               the inputs
+ *
+ * n_tokens outside 1..8 returns GDN_ERR_UNSUPPORTED; other errors as for
+ * gdn_decode_step.
+ */
+gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
+                             int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* state_slot, int32_t n_slots, float* o,
+                             int32_t n_seqs, int32_t n_tokens, int32_t Hk, int32_t Hv,
+                             int32_t dk, int32_t dv, float scale, void* stream);
 
 /*
  * gdn_gated_rmsnorm -- the "gated RMS-norm" after the rule (model card,

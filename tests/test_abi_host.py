@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -93,6 +93,26 @@ def test_decode_validation(lib):
     assert dec(dk=96) == UNSUP
     assert dec(o=P(5) + 64) == ALIAS                   # o inside the state
     assert dec(st=P(2)) == ALIAS                       # state over v
+
+
+def test_decode_tokens_validation(lib):
+    def dec(**kw):
+        a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), b=P(4), st=P(5),
+                 slot=None, nslots=4, o=P(6), N=4, nt=3, Hk=16, Hv=48, dk=128, dv=128)
+        a.update(kw)
+        return lib.gdn_decode_tokens(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                     a["b"], a["st"], a["slot"], a["nslots"], a["o"], a["N"],
+                                     a["nt"], a["Hk"], a["Hv"], a["dk"], a["dv"], 1.0, None)
+    assert dec(v=None) == NULL
+    assert dec(q=None, k=None, v=None, g=None, b=None, st=None, o=None, N=0, nslots=0) == OK
+    assert dec(nt=0) == UNSUP
+    assert dec(nt=9) == UNSUP
+    assert dec(nslots=3) == SHAPE
+    assert dec(vs=6148) == SHAPE
+    assert dec(q=P(0) + 8) == SHAPE                    # misaligned
+    assert dec(o=P(5) + 64) == ALIAS                   # o inside the state
+    # o's rows are N * n_tokens long: the last token row of o overlapping g
+    assert dec(o=P(3) - 4 * 48 * 128 * 12 + 4) == ALIAS
 
 
 def test_conv_validation(lib):

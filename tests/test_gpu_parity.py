@@ -143,6 +143,52 @@ def test_decode_step_slot_map_and_scale():
     np.testing.assert_array_equal(got[others], pool[others])
 
 
+@pytest.mark.parametrize("N,nt", [(1, 1), (3, 2), (5, 5), (17, 8)])
+def test_decode_tokens_against_oracle(N, nt):
+    """n_tokens tokens per sequence in one pass: the recurrence from each
+    sequence's state, o of every token and the final state."""
+    log(f"decode_tokens N={N} n_tokens={nt}")
+    ci = synth.chunk_inputs(2800 + 10 * N + nt, N * nt, lengths=[nt] * N, h0_std=0.02)
+    st = dev_f32(ci.h0)
+    o = ops.gdn_decode_tokens(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g),
+                              dev_f32(ci.beta), st, nt)
+    ro, rT = oracle.recurrence(ci.q, ci.k, ci.v, ci.g, ci.beta, ci.h0, cu_seqlens=ci.cu_seqlens,
+                               n_seqs=N)
+    assert_close(host(o), ro, "o")
+    assert_close(host(st), rT, "state")
+
+
+@pytest.mark.parametrize("nt", [1, 3, 8])
+def test_decode_tokens_equals_successive_steps(nt):
+    """The same per-token arithmetic as gdn_decode_step: n_tokens tokens in one
+    call agree with n_tokens successive one-token calls (slot map and scale
+    included)."""
+    N, slots_n = 6, 9
+    log(f"decode_tokens vs {nt} decode_step calls")
+    ci = synth.chunk_inputs(2900 + nt, N * nt, lengths=[nt] * N, h0_std=0.02)
+    pool = np.random.default_rng(6).standard_normal((slots_n, 48, 128, 128)).astype(np.float32) * 0.02
+    slots = np.array([8, 2, 0, 5, 3, 6], dtype=np.int32)
+    pool[slots] = ci.h0
+    q, k, v = dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v)
+    g, b = dev_f32(ci.g), dev_f32(ci.beta)
+    st1 = dev_f32(pool)
+    o1 = ops.gdn_decode_tokens(q, k, v, g, b, st1, nt, state_slot=dev_i32(slots), scale=0.7)
+    st2 = dev_f32(pool)
+    o2 = torch.empty_like(o1)
+    qv, kv, vv = q.view(N, nt, 16, 128), k.view(N, nt, 16, 128), v.view(N, nt, 48, 128)
+    gv, bv, o2v = g.view(N, nt, 48), b.view(N, nt, 48), o2.view(N, nt, 48, 128)
+    for t in range(nt):
+        o2v[:, t] = ops.gdn_decode_step(qv[:, t], kv[:, t], vv[:, t], gv[:, t].contiguous(),
+                                        bv[:, t].contiguous(), st2, state_slot=dev_i32(slots),
+                                        scale=0.7)
+    for name, a1, a2 in (("o", host(o1), host(o2)), ("state", host(st1), host(st2))):
+        err = np.abs(a1.astype(np.float64) - a2).max() / np.abs(a2).max()
+        log(f"  {name}: max|one call - successive calls| / max = {err:.3e}")
+        assert err <= 1e-6, name
+    others = [i for i in range(slots_n) if i not in slots]
+    np.testing.assert_array_equal(host(st1)[others], pool[others])
+
+
 # ----------------------------------------------------------------- conv
 
 @pytest.mark.parametrize("lens", [[37], [1, 1, 1, 1], [10, 0, 2, 25, 1]])
