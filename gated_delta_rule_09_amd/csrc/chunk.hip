@@ -58,8 +58,8 @@ constexpr int kThreads = 256;    // prep work-group
 // two output waves, and two loader waves that copy the next chunk into LDS.
 constexpr int kScanLoaderWaves = 2;
 constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
-template <int kOutWaves>
-constexpr int scan_threads() { return 64 * (1 + kOutWaves + kScanLoaderWaves); }
+template <int kOutWaves, int kStateWaves>
+constexpr int scan_threads() { return 64 * (kStateWaves + kOutWaves + kScanLoaderWaves); }
 constexpr int kDvPerWg = 32;                       // value channels per scan work-group
 constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value head
 
@@ -465,9 +465,9 @@ __device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
 // kOutWaves = 2 when the work-groups fit the CUs one each (shorter chunk
 // period); 1 when there are more work-groups than CUs, so that two fit on a
 // CU (LDS and 256 VGPRs per wave allow it).
-template <int kOutWaves>
-__global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
-  constexpr int kScanComputeWaves = 1 + kOutWaves;
+template <int kOutWaves, int kStateWaves>
+__global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
+  constexpr int kScanComputeWaves = kStateWaves + kOutWaves;
   __shared__ ScanSmem sm;
 
   // ---- block id -> (sequence rank, value head, value quarter) --------------
@@ -580,21 +580,24 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  if (w == 0) {
+  // State wave(s): kStateWaves waves share the work-group's two tiles; wave
+  // sw carries tiles t0 .. t0 + NT - 1.
+  auto state_wave = [&](auto nt_c, const int t0) {
+    constexpr int NT = decltype(nt_c)::value;
     // state tiles: S^T rows (dk) 16 dt + 4 grp + e, column (dv) 16 t + col
-    floatx4 sT[2][8];
+    floatx4 sT[NT][8];
     const int64_t sbase0 = ((static_cast<int64_t>(n) * p.Hv + h) * kD + part * kDvPerWg + col) * kD;
     if (p.h0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const float4 v = *reinterpret_cast<const float4*>(p.h0 + sbase0 + 16 * t * kD + 16 * dt + 4 * grp);
+          const float4 v = *reinterpret_cast<const float4*>(p.h0 + sbase0 + 16 * (t0 + t) * kD + 16 * dt + 4 * grp);
           sT[t][dt][0] = v.x; sT[t][dt][1] = v.y; sT[t][dt][2] = v.z; sT[t][dt][3] = v.w;
         }
     } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) sT[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -646,33 +649,33 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) fk[tb * 4 + kb] = kfrag(tb, kb);
-      half8 sB[2][4];
+      half8 sB[NT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           sB[t][kb] = to_half8(sT[t][2 * kb], sT[t][2 * kb + 1]);
-          *reinterpret_cast<half8*>(X + (4 * t + kb) * kFrag + lane * 16) = sB[t][kb];
+          *reinterpret_cast<half8*>(X + (4 * (t0 + t) + kb) * kFrag + lane * 16) = sB[t][kb];
         }
       __builtin_amdgcn_sched_barrier(0);
 
       // phase 1: V, tables | W = K S0^T by token block, so that the solve
       // below can start on block 0 while later blocks are still in the MFMA
       // pipe (no fence between the two phases); gamma_L S^T in VALU meanwhile
-      short4v vr[2][4];
+      short4v vr[NT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) vr[t][tb] = vcol(t, tb);
+        for (int tb = 0; tb < 4; ++tb) vr[t][tb] = vcol(t0 + t, tb);
       floatx4 bt[4], bg[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         bt[tb] = table(0, tb);
         bg[tb] = table(1, tb);
       }
-      floatx4 W[2][4];
+      floatx4 W[NT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) W[t][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -680,12 +683,12 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) W[t][tb] = mfma32(fk[tb * 4 + kb], sB[t][kb], W[t][tb]);
+          for (int t = 0; t < NT; ++t) W[t][tb] = mfma32(fk[tb * 4 + kb], sB[t][kb], W[t][tb]);
       // gamma_L S^T, while the products run (S0 has been read as sB)
       {
         const float gl = *reinterpret_cast<const float*>(VB + kOffGL);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -707,51 +710,51 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) ft[2 * dt + kb] = ktfrag(dt, kb);
-      floatx4 R[2][4];
+      floatx4 R[NT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             R[t][tb][e] = bt[tb][e] * bf16_to_f32(static_cast<uint16_t>(vr[t][tb][e])) - bg[tb][e] * W[t][tb][e];
       const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-      floatx4 U[2][4];
-      half8 u01[2], u23[2];
+      floatx4 U[NT][4];
+      half8 u01[NT], u23[NT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) U[t][0] = mfma16(tT[0], to_half4(R[t][0]), z4);
-      floatx4 rhs[2];
+      for (int t = 0; t < NT; ++t) U[t][0] = mfma16(tT[0], to_half4(R[t][0]), z4);
+      floatx4 rhs[NT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) rhs[t] = mfma16(an10, to_half4(U[t][0]), R[t][1]);
+      for (int t = 0; t < NT; ++t) rhs[t] = mfma16(an10, to_half4(U[t][0]), R[t][1]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         U[t][1] = mfma16(tT[1], to_half4(rhs[t]), z4);
         u01[t] = to_half8(U[t][0], U[t][1]);
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) rhs[t] = mfma32(an2, u01[t], R[t][2]);
+      for (int t = 0; t < NT; ++t) rhs[t] = mfma32(an2, u01[t], R[t][2]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) U[t][2] = mfma16(tT[2], to_half4(rhs[t]), z4);
+      for (int t = 0; t < NT; ++t) U[t][2] = mfma16(tT[2], to_half4(rhs[t]), z4);
       // The last block row's two products meet in a VALU add: a 16x16x32
       // result taken straight as the accumulator of a 16x16x16 product has
       // been observed to read stale values.
 #pragma unroll
-      for (int t = 0; t < 2; ++t) rhs[t] = mfma32(an3, u01[t], R[t][3]);
+      for (int t = 0; t < NT; ++t) rhs[t] = mfma32(an3, u01[t], R[t][3]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const floatx4 r2 = mfma16(an32, to_half4(U[t][2]), z4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) rhs[t][e] += r2[e];
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         U[t][3] = mfma16(tT[3], to_half4(rhs[t]), z4);
         u23[t] = to_half8(U[t][2], U[t][3]);
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        *reinterpret_cast<half8*>(X + (8 + 2 * t) * kFrag + lane * 16) = u01[t];
-        *reinterpret_cast<half8*>(X + (9 + 2 * t) * kFrag + lane * 16) = u23[t];
+      for (int t = 0; t < NT; ++t) {
+        *reinterpret_cast<half8*>(X + (8 + 2 * (t0 + t)) * kFrag + lane * 16) = u01[t];
+        *reinterpret_cast<half8*>(X + (9 + 2 * (t0 + t)) * kFrag + lane * 16) = u23[t];
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -760,7 +763,7 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) dl[tb] = table(3, tb);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         floatx4 DU[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
@@ -782,12 +785,16 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
 
     if (p.hT) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<float4*>(p.hT + sbase0 + 16 * t * kD + 16 * dt + 4 * grp) =
+          *reinterpret_cast<float4*>(p.hT + sbase0 + 16 * (t0 + t) * kD + 16 * dt + 4 * grp) =
               make_float4(sT[t][dt][0], sT[t][dt][1], sT[t][dt][2], sT[t][dt][3]);
     }
+  };
+  if (w < kStateWaves) {
+    if (kStateWaves == 1) state_wave(std::integral_constant<int, 2>{}, 0);
+    else state_wave(std::integral_constant<int, 1>{}, w);
     return;
   }
 
@@ -856,10 +863,11 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
         }
     };
     uint32_t sink = 0, tv = 0, tv_prev = 0;
-    if (ow == 0 && n_chunks > 0) tv = touch(min(1, n_chunks - 1));
+    constexpr bool prefetcher = ow == kOutWaves - 1;
+    if (prefetcher && n_chunks > 0) tv = touch(min(1, n_chunks - 1));
     for (int ci = 0; ci < n_chunks; ++ci) {
       lds_barrier();                       // stage ci in LDS; S0, U of chunk ci - 1 written
-      if (ow == 0) {
+      if (prefetcher) {
         sink ^= tv_prev;                   // issued two chunks ago
         tv_prev = tv;
         tv = touch(min(ci + 2, n_chunks - 1));
@@ -873,7 +881,7 @@ __global__ __launch_bounds__(scan_threads<kOutWaves>(), kOutWaves == 1 ? 2 : 1) 
     if (n_chunks > 0) output(n_chunks - 1);
     lds_barrier();
   };
-  if (kOutWaves == 1 || w == 1) output_wave(std::integral_constant<int, 0>{});
+  if (kOutWaves == 1 || w == kStateWaves) output_wave(std::integral_constant<int, 0>{});
   else output_wave(std::integral_constant<int, kOutWaves - 1>{});
 }
 
@@ -944,9 +952,9 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   sp.n_chain_groups = n_seqs * Hk;
   const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kParts;
   if (blocks <= compute_units())
-    hipLaunchKernelGGL(chunk_scan_kernel<2>, dim3(blocks), dim3(scan_threads<2>()), 0, stream, sp);
+    hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()), 0, stream, sp);
   else
-    hipLaunchKernelGGL(chunk_scan_kernel<1>, dim3(blocks), dim3(scan_threads<1>()), 0, stream, sp);
+    hipLaunchKernelGGL((chunk_scan_kernel<1, 1>), dim3(blocks), dim3(scan_threads<1, 1>()), 0, stream, sp);
   return hipGetLastError();
 }
 
