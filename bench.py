@@ -11,6 +11,7 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm;
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
+A second prefill timing writes o in bf16 (`prefill_bf16_o`, not the headline).
 `roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
 kernel, then the sequential scan kernel, back to back on one stream):
 algorithmic bytes per launch over the launch duration measured with HIP events
@@ -98,6 +99,17 @@ def leg_prefill(args, ops, synth, torch):
                mfma_tflops=flops_launch / (ev * 1e-3) / 1e12)
     log(f"[prefill] {ev:.3f} ms/launch, {res['tokens_per_s'] / 1e6:.2f} M tok/s, "
         f"{res['hbm_gbps']:.0f} GB/s alg, {res['mfma_tflops']:.1f} TFLOP/s alg")
+
+    # the same launch with o written in bf16 (gdn_chunk_fwd_bf16o); not the headline
+    o16 = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
+
+    def step16():
+        ops.gdn_chunk_fwd(q, k, v, g, b, initial_state=h0, final_state=fs, o=o16, n_seqs=1,
+                          workspace=ws)
+
+    ev16, _ = time_leg(step16, args.steps, args.warmup)
+    res.update(bf16o_event_ms=ev16, bf16o_tokens_per_s=T / (ev16 * 1e-3))
+    log(f"[prefill] bf16 o: {ev16:.3f} ms/launch, {res['bf16o_tokens_per_s'] / 1e6:.2f} M tok/s")
     return res, ci
 
 
@@ -325,6 +337,8 @@ def main():
                             "launch_ms": round(pre["event_ms"], 4)}
         line["mfma"] = {"achieved": round(pre["mfma_tflops"], 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+        line["prefill_bf16_o"] = {"launch_ms": round(pre["bf16o_event_ms"], 4),
+                                  "tokens_per_s": round(pre["bf16o_tokens_per_s"], 1)}
     if "decode" in out:
         d = out["decode"]
         line["decode"] = {"state_GBps": round(d["state_gbps"], 1),

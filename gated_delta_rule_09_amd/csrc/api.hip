@@ -178,13 +178,14 @@ gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_to
                     "gdn_chunk_map launch");
 }
 
-gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
-                         int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
-                         const float* g, const float* beta, float* o,
-                         const float* initial_state, float* final_state,
-                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
-                         int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Shared by gdn_chunk_fwd (fp32 o) and gdn_chunk_fwd_bf16o (bf16 o).
+static gdn_status chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                            int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                            const float* g, const float* beta, void* o, bool o_bf16,
+                            const float* initial_state, float* final_state,
+                            const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                            int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
     return fail(GDN_ERR_NULL, "gdn_chunk_fwd: q, k, v, g, beta and o are required");
   if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
@@ -214,7 +215,7 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
   const Range rv = range_of(v, T_total, v_tok_stride, static_cast<int64_t>(Hv) * dv, 2);
   const Range rg = range_of(g, T_total, Hv, Hv, 4);
   const Range rb = range_of(beta, T_total, Hv, Hv, 4);
-  const Range ro = range_of(o, T_total, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, 4);
+  const Range ro = range_of(o, T_total, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, o_bf16 ? 2 : 4);
   const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
   const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
   const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
@@ -239,9 +240,33 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g,
-                                          beta, o, initial_state, final_state, cu_seqlens,
+                                          beta, o, o_bf16, initial_state, final_state, cu_seqlens,
                                           n_seqs, T_total, Hk, Hv, scale, workspace, st),
                     "gdn_chunk_fwd launch");
+}
+
+gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                         int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                         const float* g, const float* beta, float* o,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                         int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta, o, false,
+                   initial_state, final_state, cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale,
+                   workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                               int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                               const float* g, const float* beta, uint16_t* o,
+                               const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                               int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta, o, true,
+                   initial_state, final_state, cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale,
+                   workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,

@@ -430,7 +430,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
 struct ScanParams {
   const uint16_t* v;
   int64_t vs;
-  float* o;
+  void* o;                    // fp32, or bf16 when o_bf16
+  int o_bf16;
   const float* h0; float* hT;
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* order;       // longest-first schedule (varlen)
@@ -450,6 +451,12 @@ struct __align__(16) ScanSmem {
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
+}
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 // gfx950 transposing LDS load (ds_read_b64_tr_b16).  Within each group of 16
@@ -841,7 +848,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
           u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
       }
       const int len = min(kC, seq_len - ci * kC);
-      float* ob = p.o + static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
+      const int64_t oe = static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -859,7 +866,13 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
             O = mfma32(u[t][0], fp[2 * tb - 2 - p0], O);
             O = mfma32(u[t][need_u23 ? 1 : 0], fp[2 * tb - 1 - p0], O);
           }
-          if (16 * tb + col < len) *reinterpret_cast<floatx4*>(ob + (16 * tb + col) * o_rs + 16 * t) = O;
+          if (16 * tb + col < len) {
+            const int64_t e = oe + (16 * tb + col) * o_rs + 16 * t;
+            if (p.o_bf16)   // round to nearest even (v_cvt_pk_bf16_f32)
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + e) = uint2{pack_bf16x2(O[0], O[1]), pack_bf16x2(O[2], O[3])};
+            else
+              *reinterpret_cast<floatx4*>(static_cast<float*>(p.o) + e) = O;
+          }
         }
     };
     uint32_t sink = 0, tv = 0, tv_prev = 0;
@@ -876,7 +889,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
       load_q(ci);
     }
     sink ^= tv_prev ^ tv;
-    if (sink == 0x9e3779b9u && p.n_seqs < 0) p.o[0] = 0.f;   // keeps the prefetch loads
+    if (sink == 0x9e3779b9u && p.n_seqs < 0) static_cast<float*>(p.o)[0] = 0.f;   // keeps the prefetch loads
     lds_barrier();                         // S0, U of the last chunk written
     if (n_chunks > 0) output(n_chunks - 1);
     lds_barrier();
@@ -915,7 +928,7 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
 
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const float* g, const float* beta,
-                            float* o, const float* h0, float* hT, const int32_t* cu,
+                            void* o, bool o_bf16, const float* h0, float* hT, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
@@ -945,7 +958,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     if (e != hipSuccess) return e;
   }
   ScanParams sp;
-  sp.v = v; sp.vs = vs; sp.o = o; sp.h0 = h0; sp.hT = hT;
+  sp.v = v; sp.vs = vs; sp.o = o; sp.o_bf16 = o_bf16 ? 1 : 0; sp.h0 = h0; sp.hT = hT;
   sp.cu = cu; sp.order = cu ? order : nullptr; sp.chunk_off = chunk_off;
   sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;

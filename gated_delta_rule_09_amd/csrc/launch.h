@@ -42,7 +42,7 @@ hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t*
 
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const float* g, const float* beta,
-                            float* o, const float* h0, float* hT, const int32_t* cu,
+                            void* o, bool o_bf16, const float* h0, float* hT, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream);
 

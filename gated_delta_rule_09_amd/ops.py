@@ -31,6 +31,8 @@ _SIGS = {
     "gdn_chunk_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "gdn_chunk_fwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gdn_chunk_fwd_bf16o": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
@@ -161,10 +163,12 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
                   scale: float = 1.0, o: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  workspace: Optional[torch.Tensor] = None,
+                  o_bf16: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill. q, k [T, Hk, 128], v [T, Hv, 128] bf16; g, beta [T, Hv] fp32.
 
-    Returns (o [T, Hv, 128] fp32, final_state [N, Hv, 128, 128] fp32 or None).
+    Returns (o [T, Hv, 128] fp32 -- bf16 with o_bf16 or a bf16 `o` --,
+    final_state [N, Hv, 128, 128] fp32 or None).
     """
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 3)
@@ -180,9 +184,12 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         n_seqs = cu_seqlens.shape[0] - 1
     elif n_seqs is None:
         n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    if o is not None and o.dtype == torch.bfloat16:
+        o_bf16 = True
+    odt = torch.bfloat16 if o_bf16 else torch.float32
     if o is None:
-        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", torch.float32, 3)
+        o = torch.empty((T, Hv, dv), dtype=odt, device=q.device)
+    _need(o, "o", odt, 3)
     if not o.is_contiguous():
         raise ValueError("o must be contiguous")
     if initial_state is not None:
@@ -201,11 +208,12 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             workspace = torch.empty(gdn_chunk_fwd_workspace_bytes(n_seqs, T, Hk, Hv, dk),
                                     dtype=torch.uint8, device=q.device)
         ws_bytes = workspace.numel()
-    st = lib().gdn_chunk_fwd(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
-                             _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state), _ptr(final_state),
-                             _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv, scale, _ptr(workspace),
-                             ws_bytes, _stream())
-    _check(st, "gdn_chunk_fwd")
+    fn = lib().gdn_chunk_fwd_bf16o if o_bf16 else lib().gdn_chunk_fwd
+    st = fn(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+            _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state), _ptr(final_state),
+            _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv, scale, _ptr(workspace),
+            ws_bytes, _stream())
+    _check(st, "gdn_chunk_fwd_bf16o" if o_bf16 else "gdn_chunk_fwd")
     return o, final_state
 
 

@@ -130,11 +130,12 @@ gdn_status gdn_conv1d_fwd(const uint16_t* x, int64_t x_row_stride, const uint16_
  *                  bytes, 256-byte aligned (may be NULL only when n_seqs == 0),
  *                  not overlapping any tensor.  Per call it receives the chunk
  *                  map (as gdn_chunk_map), then the state-independent part of
- *                  every chunk (fp16 K, Q, K^T, -A, the inverted diagonal
+ *                  every chunk (fp16 K rows and Q, -A, the inverted diagonal
  *                  blocks of I + A, the masked decayed Q K^T and the decay
- *                  tables, in MFMA fragment order), which the sequential scan
- *                  then reads.  About 21 KB per token for 16 key / 48 value
- *                  heads.  Contents are scratch: nothing is kept across calls.
+ *                  tables, mostly in MFMA fragment order), which the
+ *                  sequential scan then reads.  About 17.9 KB per token for
+ *                  16 key / 48 value heads.  Contents are scratch: nothing is
+ *                  kept across calls.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
                                      int32_t d);
@@ -146,6 +147,20 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_bf16o -- gdn_chunk_fwd with o written as bf16 (each element
+ * the fp32 result rounded to nearest, ties to even): half the output bytes.
+ * o is [T_total, Hv, dv] bf16, contiguous, 16-byte aligned; every other
+ * argument, the states and the errors are as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                               int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                               const float* g, const float* beta, uint16_t* o,
+                               const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                               int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gdn_chunk_map -- the varlen chunk map used by gdn_chunk_fwd, exposed so its

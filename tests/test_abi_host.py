@@ -77,6 +77,24 @@ def test_chunk_fwd_validation(lib):
     assert b"overlap" in lib.gdn_last_error()
 
 
+def test_chunk_fwd_bf16o_validation(lib):
+    def c16(**kw):
+        a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), beta=P(4), o=P(5),
+                 h0=None, hT=None, cu=None, N=1, T=64, Hk=16, Hv=48, dk=128, dv=128, scale=1.0,
+                 ws=None, wsb=0, stream=None)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_bf16o(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                       a["beta"], a["o"], a["h0"], a["hT"], a["cu"], a["N"], a["T"],
+                                       a["Hk"], a["Hv"], a["dk"], a["dv"], a["scale"], a["ws"],
+                                       a["wsb"], a["stream"])
+    assert c16(o=None) == NULL
+    assert c16(dk=64) == UNSUP
+    assert c16(o=P(5) + 8) == SHAPE                   # o must be 16-byte aligned
+    # a bf16 o of 64 x 48 x 128 elements is 786,432 bytes: ending 2 bytes into g overlaps it
+    assert c16(o=P(3) - 786432 + 16) == ALIAS
+    assert c16(o=P(3) - 786432) == WS                 # just below g: no overlap, no workspace
+
+
 def test_decode_validation(lib):
     def dec(**kw):
         a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), b=P(4), st=P(5),

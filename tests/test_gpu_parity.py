@@ -49,6 +49,33 @@ def test_chunk_head_groupings(Hk, Hv):
     assert_close(hT, rT, "final_state")
 
 
+@pytest.mark.parametrize("lens", [[150], [70, 0, 1, 64, 129, 5, 0, 200, 33]])
+def test_chunk_bf16_output(lens):
+    """gdn_chunk_fwd_bf16o: o is the fp32 result of gdn_chunk_fwd rounded to
+    bf16 (nearest, ties to even) bit for bit, and the final states agree
+    exactly; both paths against the oracle."""
+    log(f"chunk_fwd bf16 o lens={lens}")
+    ci = synth.chunk_inputs(2150 + len(lens), int(sum(lens)), Hk=4, Hv=12, lengths=lens, h0_std=0.05)
+    args = (dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g), dev_f32(ci.beta))
+    kw = dict(initial_state=dev_f32(ci.h0), cu_seqlens=dev_i32(ci.cu_seqlens))
+    o32, hT32 = ops.gdn_chunk_fwd(*args, **kw)
+    o16, hT16 = ops.gdn_chunk_fwd(*args, o_bf16=True, **kw)
+    assert o16.dtype == torch.bfloat16
+    np.testing.assert_array_equal(host(hT16), host(hT32))
+    want = oracle.round_bf16(host(o32))                 # fp64 values on the bf16 grid
+    got = o16.float().cpu().numpy().astype(np.float64)   # exact widening
+    np.testing.assert_array_equal(got, want)
+    # against the oracle: the fp32 bar, plus the bf16 rounding itself (relative
+    # error up to 2^-9 per element, so rel-L2 up to ~2^-9 on its own)
+    ro, _ = oracle_chunk(ci)
+    assert_close(host(o32), ro, "o (fp32)")
+    d = got - ro
+    rel = np.linalg.norm(d) / np.linalg.norm(ro)
+    mabs = np.abs(d).max() / np.abs(ro).max()
+    log(f"  o (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
+    assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+
+
 def test_chunk_zero_initial_state_and_scale():
     log("chunk_fwd T=300 no h0 scale=128^-0.5")
     ci = synth.chunk_inputs(2200, 300)
