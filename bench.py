@@ -6,8 +6,9 @@ B = 1, 16 key heads / 48 value heads, head dim 128, random fp32 initial state,
 fp32 outputs and final state -- one `gdn_chunk_fwd` launch per step, inputs
 resident in HBM.  The same run also times, as extra legs in the same JSON line:
   decode  one batched decode step, 256 sequences, fp32 state [256,48,128,128]
-          updated in place (state GB/s), plus the batch-mode conv-state update
-          and a 4-tokens-per-sequence step (gdn_decode_tokens);
+          updated in place (state GB/s), plus the batch-mode conv-state update,
+          a 4-tokens-per-sequence step (gdn_decode_tokens) and the whole mixer
+          step in one launch (gdn_decode_mixer_step);
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm;
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
@@ -151,16 +152,43 @@ def leg_decode(args, ops, synth, torch):
         ops.gdn_decode_tokens(tq, tk, tv, tg, tb, di["state"], NT, o=to)
 
     tev, twall = time_leg(tokens_step, args.steps, args.warmup)
+
+    # the whole mixer's decode step in one launch (gdn_decode_mixer_step) against
+    # the three launches it replaces (batch conv, decode step, gated norm)
+    z = torch.randn((N, HV, D), generator=gen, device="cuda").to(torch.bfloat16)
+    nw = 1.0 + 0.02 * torch.randn((D,), generator=gen, device="cuda")
+    mo = torch.empty((N, HV, D), dtype=torch.float32, device="cuda")
+    yv = y.view(N, 2 * HK + HV, D)
+
+    def fused_step():
+        ops.gdn_decode_mixer_step(di["x"], di["conv_w"], di["conv_state"], di["g"], di["beta"], z,
+                                  nw, di["state"], Hk=HK, out=mo)
+
+    def unfused_step():
+        ops.gdn_conv1d_fwd(di["x"], di["conv_w"], y=y, conv_state=di["conv_state"], n_seqs=N,
+                           n_l2_heads=2 * HK)
+        ops.gdn_decode_step(yv[:, :HK], yv[:, HK:2 * HK], yv[:, 2 * HK:], di["g"], di["beta"],
+                            di["state"], o=o)
+        ops.gdn_gated_rmsnorm(o, z, nw, out=mo)
+
+    fev, _ = time_leg(fused_step, args.steps, args.warmup)
+    uev, _ = time_leg(unfused_step, args.steps, args.warmup)
+    C = y.shape[1]
+    fbytes = sbytes + N * C * 2 + 2 * N * C * 3 * 2 + C * 4 * 2 + N * HV * D * (2 + 4) + 2 * N * HV * 4
     res = dict(n_seqs=N, event_ms=ev, wall_ms=wall, state_bytes=sbytes,
                state_gbps=sbytes / (ev * 1e-3) / 1e9,
                frac_hbm=sbytes / (ev * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                conv_event_ms=cev, conv_alg_bytes=cbytes, conv_gbps=cbytes / (cev * 1e-3) / 1e9,
                tokens_n=NT, tokens_event_ms=tev,
                tokens_state_gbps=sbytes / (tev * 1e-3) / 1e9,
-               tokens_per_s=N * NT / (tev * 1e-3))
+               tokens_per_s=N * NT / (tev * 1e-3),
+               fused_event_ms=fev, unfused_event_ms=uev, fused_alg_bytes=fbytes,
+               fused_gbps=fbytes / (fev * 1e-3) / 1e9)
     log(f"[decode] {ev:.3f} ms/step, state {res['state_gbps']:.0f} GB/s "
         f"({100 * res['frac_hbm']:.1f}% of HBM); conv update {cev * 1e3:.1f} us; "
-        f"{NT} tokens/sequence: {tev:.3f} ms, {res['tokens_per_s'] / 1e6:.2f} M tok/s")
+        f"{NT} tokens/sequence: {tev:.3f} ms, {res['tokens_per_s'] / 1e6:.2f} M tok/s; "
+        f"whole mixer step fused {fev:.3f} ms ({res['fused_gbps']:.0f} GB/s alg) vs "
+        f"three launches {uev:.3f} ms")
     return res
 
 
@@ -347,7 +375,10 @@ def main():
                           "conv_update_ms": round(d["conv_event_ms"], 4),
                           "tokens4": {"launch_ms": round(d["tokens_event_ms"], 4),
                                       "tokens_per_s": round(d["tokens_per_s"], 1),
-                                      "state_GBps": round(d["tokens_state_gbps"], 1)}}
+                                      "state_GBps": round(d["tokens_state_gbps"], 1)},
+                          "mixer_step": {"fused_ms": round(d["fused_event_ms"], 4),
+                                         "three_launches_ms": round(d["unfused_event_ms"], 4),
+                                         "alg_GBps": round(d["fused_gbps"], 1)}}
     if "mixer" in out:
         line["mixer_T8192"] = {"tokens_per_s": round(out["mixer"]["tokens_per_s"], 1),
                                "ms": round(out["mixer"]["event_ms"], 4)}

@@ -353,6 +353,59 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
                     "gdn_decode_tokens launch");
 }
 
+gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
+                                 const float* conv_bias, uint16_t* conv_state, const float* g,
+                                 const float* beta, const uint16_t* z, int64_t z_stride,
+                                 const float* norm_w, float* state, const int32_t* state_slot,
+                                 int32_t n_slots, void* out, int32_t out_is_bf16, int32_t n_seqs,
+                                 int32_t Hk, int32_t Hv, int32_t d, float scale, float l2_eps,
+                                 float norm_eps, void* stream) {
+  if (n_seqs > 0 && (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out))
+    return fail(GDN_ERR_NULL, "gdn_decode_mixer_step: all pointers but conv_bias and state_slot are required");
+  if (n_seqs < 0 || n_slots < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: bad sizes or Hv %% Hk != 0");
+  if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_mixer_step: d = 128 only");
+  if (Hv / Hk > 4) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_mixer_step: Hv / Hk must be at most 4");
+  if (!state_slot && n_slots < n_seqs)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: n_slots < n_seqs without a slot map");
+  const int64_t C = static_cast<int64_t>(2 * Hk + Hv) * d;
+  if (x_stride < C || z_stride < static_cast<int64_t>(Hv) * d)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: row strides too small");
+  if (!aligned(state, 16) || !aligned(x, 2) || !aligned(conv_w, 2) || !aligned(conv_state, 2) ||
+      !aligned(z, 2) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(norm_w, 4) ||
+      !aligned(conv_bias, 4) || !aligned(state_slot, 4) || !aligned(out, out_is_bf16 ? 2 : 4))
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: misaligned pointer (state needs 16 bytes)");
+  if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
+      !std::isfinite(norm_eps))
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: scale and eps must be finite, eps >= 0");
+  if (static_cast<int64_t>(n_seqs) * Hk > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: too many (sequence, head) pairs");
+  const int64_t ssz = static_cast<int64_t>(Hv) * d * d;
+  const Range rs = range_of(state, n_slots, ssz, ssz, 4);
+  const Range rc = range_of(conv_state, n_slots, C * 3, C * 3, 2);
+  const Range rx = range_of(x, n_seqs, x_stride, C, 2);
+  const Range rw = range_of(conv_w, 1, 0, C * 4, 2);
+  const Range rbias = range_of(conv_bias, 1, 0, C, 4);
+  const Range rg = range_of(g, n_seqs, Hv, Hv, 4);
+  const Range rb = range_of(beta, n_seqs, Hv, Hv, 4);
+  const Range rz = range_of(z, n_seqs, z_stride, static_cast<int64_t>(Hv) * d, 2);
+  const Range rn = range_of(norm_w, 1, 0, d, 4);
+  const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
+  const Range ro = range_of(out, n_seqs, static_cast<int64_t>(Hv) * d, static_cast<int64_t>(Hv) * d,
+                            out_is_bf16 ? 2 : 4);
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl, &rs, &rc})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: out overlaps another tensor");
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl, &rc})
+    if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: state overlaps another tensor");
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl})
+    if (overlap(*in, rc)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: conv_state overlaps an input");
+  return hip_status(gdn::launch_decode_mixer(x, x_stride, conv_w, conv_bias, conv_state, g, beta, z,
+                                             z_stride, norm_w, state, state_slot, out, out_is_bf16 != 0,
+                                             n_seqs, Hk, Hv, scale, l2_eps, norm_eps,
+                                             static_cast<hipStream_t>(stream)),
+                    "gdn_decode_mixer_step launch");
+}
+
 gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
                              const float* w, void* out, int32_t out_is_bf16, int64_t rows,
                              int32_t Hv, int32_t dv, float eps, void* stream) {

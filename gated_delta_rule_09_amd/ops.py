@@ -38,6 +38,9 @@ _SIGS = {
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "gdn_decode_tokens": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
+    "gdn_decode_mixer_step": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                     _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
+                                     _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
 }
@@ -270,6 +273,53 @@ def gdn_decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
                                  _ptr(o), rows // n_tokens, n_tokens, Hk, Hv, dk, dv, scale, _stream())
     _check(st, "gdn_decode_tokens")
     return o
+
+
+def gdn_decode_mixer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
+                          g: torch.Tensor, beta: torch.Tensor, z: torch.Tensor,
+                          norm_w: torch.Tensor, state: torch.Tensor, *, Hk: int = 16,
+                          conv_bias: Optional[torch.Tensor] = None,
+                          state_slot: Optional[torch.Tensor] = None, scale: float = 1.0,
+                          l2_eps: float = 1e-6, norm_eps: float = 1e-6, out_bf16: bool = False,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of the whole mixer (conv + SiLU + L2, the rule, the gated
+    RMSNorm) for the new tokens x [N, C] bf16; conv_state [n_slots, C, 3] bf16 and
+    state [n_slots, Hv, 128, 128] fp32 updated in place; z [N, Hv, 128] bf16.
+    Returns out [N, Hv, 128] (fp32, or bf16 with out_bf16)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, 2)
+    _need(conv_state, "conv_state", torch.bfloat16, 3)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(norm_w, "norm_w", torch.float32, 1)
+    _need(state, "state", torch.float32, 4)
+    for t, nm in ((conv_w, "conv_w"), (conv_state, "conv_state"), (g, "g"), (beta, "beta"),
+                  (norm_w, "norm_w"), (state, "state")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 else z
+    _need(z2, "z", torch.bfloat16, 2)
+    if z2.stride(1) != 1:
+        raise ValueError("z rows must be contiguous")
+    N = x.shape[0]
+    Hv, d = state.shape[1], state.shape[2]
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", torch.float32, 1)
+    if state_slot is not None:
+        _need(state_slot, "state_slot", torch.int32, 1)
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    if out is None:
+        out = torch.empty((N, Hv, d), dtype=odt, device=x.device)
+    _need(out, "out", odt, 3)
+    st = lib().gdn_decode_mixer_step(_ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_bias),
+                                     _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(z2), z2.stride(0),
+                                     _ptr(norm_w), _ptr(state), _ptr(state_slot), state.shape[0],
+                                     _ptr(out), 1 if out_bf16 else 0, N, Hk, Hv, d, scale, l2_eps,
+                                     norm_eps, _stream())
+    _check(st, "gdn_decode_mixer_step")
+    return out
 
 
 def gdn_gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,

@@ -226,6 +226,41 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
                              int32_t dk, int32_t dv, float scale, void* stream);
 
 /*
+ * gdn_decode_mixer_step -- one decode step of the whole mixer in one kernel
+ * (model card, Architecture table, row "Delta-rule layers": conv in front,
+ * the rule with its fp32 state, gated RMS-norm after).  Per sequence n and
+ * value head h, with the new token's projected channels x:
+ *     y = silu(conv4(conv_state, x) + bias)   (conv state shifted in place)
+ *     q, k = y / sqrt(sum y^2 + l2_eps) per head; q, k, v rounded to bf16
+ *     S <- alpha S + beta (v - alpha S k) k^T,  o = scale * S q
+ *     out = o / sqrt(mean(o^2) + norm_eps) * norm_w * z * sigmoid(z)
+ * i.e. gdn_conv1d_fwd in decode batch mode (n_l2_heads = Hk), gdn_decode_step
+ * and gdn_gated_rmsnorm in sequence, without the intermediate tensors.
+ *
+ *   x           [n_seqs, C] bf16, row stride x_stride >= C, C = (2 Hk + Hv) * d,
+ *               channels [q heads | k heads | v heads]
+ *   conv_w      [C, 4] bf16; conv_bias [C] fp32 or NULL
+ *   conv_state  [n_slots, C, 3] bf16, oldest first, updated in place
+ *   g, beta     [n_seqs, Hv] fp32, contiguous
+ *   z           [n_seqs, Hv * d] bf16, row stride z_stride >= Hv * d
+ *   norm_w      [d] fp32
+ *   state       [n_slots, Hv, d, d] fp32, updated in place
+ *   state_slot  [n_seqs] int32 device array or NULL: sequence n uses slot
+ *               state_slot[n] of both conv_state and state (NULL: slot n);
+ *               slots distinct and in [0, n_slots), not checked on the device
+ *   out         [n_seqs, Hv, d], fp32 (out_is_bf16 == 0) or bf16 (rounded to
+ *               nearest even); must not overlap any other tensor
+ *   d           must be 128; Hv / Hk must be 1, 2, 3 or 4
+ */
+gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
+                                 const float* conv_bias, uint16_t* conv_state, const float* g,
+                                 const float* beta, const uint16_t* z, int64_t z_stride,
+                                 const float* norm_w, float* state, const int32_t* state_slot,
+                                 int32_t n_slots, void* out, int32_t out_is_bf16, int32_t n_seqs,
+                                 int32_t Hk, int32_t Hv, int32_t d, float scale, float l2_eps,
+                                 float norm_eps, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- the "gated RMS-norm" after the rule (model card,
  * Architecture table, row "Delta-rule layers"), per (row, value head):
  *     out_i = o_i / sqrt(mean_j o_j^2 + eps) * w_i * z_i * sigmoid(z_i)

@@ -133,6 +133,31 @@ def test_decode_tokens_validation(lib):
     assert dec(o=P(3) - 4 * 48 * 128 * 12 + 4) == ALIAS
 
 
+def test_decode_mixer_step_validation(lib):
+    def mix(**kw):
+        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=P(2), g=P(3), b=P(4), z=P(5), zs=6144,
+                 nw=P(6), st=P(7), slot=None, nslots=4, out=P(8), bf=0, N=4, Hk=16, Hv=48, d=128,
+                 l2=1e-6, ne=1e-6)
+        a.update(kw)
+        return lib.gdn_decode_mixer_step(a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["g"],
+                                         a["b"], a["z"], a["zs"], a["nw"], a["st"], a["slot"],
+                                         a["nslots"], a["out"], a["bf"], a["N"], a["Hk"], a["Hv"],
+                                         a["d"], 1.0, a["l2"], a["ne"], None)
+    assert mix(z=None) == NULL
+    assert mix(x=None, w=None, cs=None, g=None, b=None, z=None, nw=None, st=None, out=None,
+               N=0) == OK
+    assert mix(d=64) == UNSUP
+    assert mix(Hk=8, Hv=48) == UNSUP                   # six value heads per key head
+    assert mix(Hv=40) == SHAPE                          # Hv not a multiple of Hk
+    assert mix(nslots=3) == SHAPE
+    assert mix(xs=10000) == SHAPE
+    assert mix(st=P(7) + 8) == SHAPE                    # state not 16-byte aligned
+    assert mix(l2=-1.0) == SHAPE
+    assert mix(out=P(7) + 64) == ALIAS                 # out inside the state
+    assert mix(cs=P(0) + 16) == ALIAS                  # conv state over x
+    assert mix(st=P(2) + 256) == ALIAS                 # state over the conv state
+
+
 def test_conv_validation(lib):
     def conv(**kw):
         a = dict(x=P(0), xs=10240, w=P(1), bias=None, y=P(2), ys=10240, cs=None, cu=None, N=1,

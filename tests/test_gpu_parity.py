@@ -289,6 +289,96 @@ def test_gated_rmsnorm_in_place():
     assert_close(host(od), oracle.gated_rmsnorm(o, z, w), "out")
 
 
+# ----------------------------------------------------------------- fused decode step
+
+def _mixer_step_case(seed, N, Hk, Hv, n_slots):
+    mi = synth.mixer_inputs(seed, N, Hk=Hk, Hv=Hv, conv_state_seqs=n_slots)
+    pool = synth.decode_inputs(seed + 1, n_slots, Hk=Hk, Hv=Hv, with_conv=False).state
+    return mi, pool
+
+
+def oracle_mixer_step(mi, pool, Hk, Hv, slots, bias=None, scale=1.0, out_bf16=False):
+    """conv (one token per sequence, history from its slot) -> L2 of q, k ->
+    one step of the rule on the slot's state -> gated RMSNorm, all in the oracle."""
+    N = mi.x.shape[0]
+    ry, rcs = oracle.conv1d(mi.x, mi.conv_w, bias=bias, conv_state=mi.conv_state[slots], n_seqs=N,
+                            n_l2_heads=2 * Hk, head_dim=128, l2_eps=1e-6, stage_bf16=True)
+    ry = ry.reshape(N, 2 * Hk + Hv, 128)
+    ro, rst = oracle.decode(ry[:, :Hk], ry[:, Hk:2 * Hk], ry[:, 2 * Hk:], mi.g, mi.beta, pool,
+                            state_slot=slots, scale=scale)
+    rout = oracle.gated_rmsnorm(ro, mi.z, mi.norm_w, eps=1e-6, stage_bf16=out_bf16)
+    return rout, rcs, rst
+
+
+@pytest.mark.parametrize("N,Hk,Hv,slotted,out_bf16", [
+    (1, 16, 48, False, False), (5, 16, 48, True, False), (3, 2, 2, False, True),
+    (4, 4, 8, True, True), (2, 2, 8, False, False), (7, 3, 9, True, False)])
+def test_decode_mixer_step_against_oracle(N, Hk, Hv, slotted, out_bf16):
+    """The fused step: normalised output, the conv window and the state of every
+    slot it used, against the oracle's conv -> rule -> norm; slots it did not
+    use are left as they were, bit for bit."""
+    n_slots = N + 3 if slotted else N
+    log(f"decode_mixer_step N={N} Hk={Hk} Hv={Hv} slotted={slotted} bf16_out={out_bf16}")
+    mi, pool = _mixer_step_case(3300 + 7 * N + Hv, N, Hk, Hv, n_slots)
+    r = np.random.default_rng(N + Hv)
+    slots = (r.permutation(n_slots)[:N] if slotted else np.arange(N)).astype(np.int32)
+    bias = (0.1 * r.standard_normal(mi.x.shape[1])).astype(np.float32) if slotted else None
+    scale = 0.6 if slotted else 1.0
+    cs, st = dev_bf16(mi.conv_state), dev_f32(pool)
+    out = ops.gdn_decode_mixer_step(dev_bf16(mi.x), dev_bf16(mi.conv_w), cs, dev_f32(mi.g),
+                                    dev_f32(mi.beta), dev_bf16(mi.z), dev_f32(mi.norm_w), st, Hk=Hk,
+                                    conv_bias=None if bias is None else dev_f32(bias),
+                                    state_slot=dev_i32(slots) if slotted else None, scale=scale,
+                                    out_bf16=out_bf16)
+    rout, rcs, rst = oracle_mixer_step(mi, pool, Hk, Hv, slots, bias=bias, scale=scale,
+                                       out_bf16=out_bf16)
+    if out_bf16:
+        assert out.dtype == torch.bfloat16
+        got = out.float().cpu().numpy().astype(np.float64)
+        d = got - rout
+        rel = np.linalg.norm(d) / np.linalg.norm(rout)
+        mabs = np.abs(d).max() / np.abs(rout).max()
+        log(f"  out (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
+        assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+    else:
+        assert_close(host(out), rout, "out")
+    got_cs, got_st = host(cs), host(st)
+    np.testing.assert_array_equal(got_cs[slots], rcs)
+    assert_close(got_st[slots], rst[slots], "state (slots used)")
+    others = [i for i in range(n_slots) if i not in slots]
+    cs_bits = cs.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(cs_bits[others], mi.conv_state[others])
+    np.testing.assert_array_equal(got_st[others], pool[others])
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_decode_mixer_step_matches_unfused(out_bf16):
+    """One fused call against the three separate calls it replaces (batch conv
+    with the conv window, gdn_decode_step, gdn_gated_rmsnorm) on the same
+    device inputs: identical conv windows, states and outputs up to the
+    reduction order of the two L2 norms."""
+    N, Hk, Hv = 33, 16, 48
+    log(f"decode_mixer_step vs conv + decode_step + gated_rmsnorm, N={N} bf16_out={out_bf16}")
+    mi, pool = _mixer_step_case(3400, N, Hk, Hv, N)
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    g, b = dev_f32(mi.g), dev_f32(mi.beta)
+    cs1, st1 = dev_bf16(mi.conv_state), dev_f32(pool)
+    out1 = ops.gdn_decode_mixer_step(x, w, cs1, g, b, z, nw, st1, Hk=Hk, scale=0.8,
+                                     out_bf16=out_bf16)
+    cs2, st2 = dev_bf16(mi.conv_state), dev_f32(pool)
+    y = ops.gdn_conv1d_fwd(x, w, conv_state=cs2, n_seqs=N, n_l2_heads=2 * Hk).view(N, 2 * Hk + Hv, 128)
+    o = ops.gdn_decode_step(y[:, :Hk], y[:, Hk:2 * Hk], y[:, 2 * Hk:], g, b, st2, scale=0.8)
+    out2 = ops.gdn_gated_rmsnorm(o, z, nw, out_bf16=out_bf16)
+    torch.cuda.synchronize()
+    assert torch.equal(cs1, cs2)
+    for name, a1, a2 in (("state", st1, st2), ("out", out1, out2)):
+        a1, a2 = a1.double(), a2.double()
+        err = ((a1 - a2).abs().max() / a2.abs().max()).item()
+        rel = ((a1 - a2).norm() / a2.norm()).item()
+        log(f"  {name}: max|fused - unfused| / max = {err:.3e}, rel_l2 = {rel:.3e}")
+        assert rel <= 1e-4 + (2.0 ** -9 if out_bf16 and name == "out" else 0.0), name
+
+
 # ----------------------------------------------------------------- full mixer
 
 def test_mixer_conv_chunk_norm():
