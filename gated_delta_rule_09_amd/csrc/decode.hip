@@ -9,12 +9,11 @@
 // row and the state is read once and written once (the rule of the
 // "Delta-rule layers" row of the model card's Architecture table, T = 1).
 //
-// Mapping: one 512-thread work-group per (n, h).  Eight consecutive lanes share
-// a state row; lane p of the eight holds the float4 columns p, p+8, p+16, p+24
-// of that row, so every wave-wide load reads eight whole 128-byte row pieces.
-// Thread t owns rows t/8 and t/8 + 64.  Row dot products are reduced inside the
-// 8-lane group with DPP.  (Per 64 KB state block, 512 threads with 128 bytes in
-// flight each stream faster than 256 threads with 256 bytes each.)
+// Mapping: one work-group per (n, h).  Eight consecutive lanes share a state
+// row; lane p of the eight holds the float4 columns p, p+8, p+16, p+24 of that
+// row, so every wave-wide load reads eight whole 128-byte row pieces.  With
+// kTh threads, thread t owns rows t/8 + i * kTh/8.  Row dot products are
+// reduced inside the 8-lane group with DPP.
 #include "common.h"
 #include "launch.h"
 
@@ -23,12 +22,21 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kThreads = 512;
-constexpr int kRowStep = kThreads / 8;       // rows between a thread's rows
-constexpr int kRows = kD / kRowStep;         // rows per thread
 
-template <bool kSlots>
-__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+// kTh threads per work-group, eight lanes per state row: a thread's rows are
+// kTh / 8 apart and it holds kD / (kTh / 8) of them.
+template <int kTh> constexpr int row_step() { return kTh / 8; }
+template <int kTh> constexpr int rows_per_thread() { return kD / (kTh / 8); }
+// One token: 1024 threads, one row each, 56 VGPRs, so two work-groups (32
+// waves) share a CU; at 256 sequences x 48 heads this streams the state 6 %
+// faster than 512 threads with two rows each.  Several tokens: the per-token
+// q/k registers grow with kT, and 512 threads with two rows each are faster
+// from two tokens on (and do not spill up to eight).
+constexpr int kStepThreads = 1024;
+constexpr int kTokThreads = 512;
+
+template <int kTh, bool kSlots>
+__global__ __launch_bounds__(kTh) void decode_step_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
     int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -36,6 +44,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   const int n = blockIdx.x / Hv;
   const int h = blockIdx.x - n * Hv;
   const int kh = h / (Hv / Hk);
+  constexpr int kRowStep = row_step<kTh>();
+  constexpr int kRows = rows_per_thread<kTh>();
   const int tid = threadIdx.x;
   const int p = tid & 7;
   const int rg = tid >> 3;
@@ -108,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 // with the arithmetic above (both dot products from the row before that
 // token), so kT tokens cost one read and one write of the state.  Token t of
 // sequence n is row n * kT + t of q, k, v, g, beta and o.
-template <int kT, bool kSlots>
-__global__ __launch_bounds__(kThreads) void decode_tokens_kernel(
+template <int kT, int kTh, bool kSlots>
+__global__ __launch_bounds__(kTh) void decode_tokens_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
     int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -117,6 +127,8 @@ __global__ __launch_bounds__(kThreads) void decode_tokens_kernel(
   const int n = blockIdx.x / Hv;
   const int h = blockIdx.x - n * Hv;
   const int kh = h / (Hv / Hk);
+  constexpr int kRowStep = row_step<kTh>();
+  constexpr int kRows = rows_per_thread<kTh>();
   const int tid = threadIdx.x;
   const int p = tid & 7;
   const int rg = tid >> 3;
@@ -206,10 +218,10 @@ void launch_tokens(dim3 grid, hipStream_t stream, const uint16_t* q, int64_t q_s
                    const float* g, const float* beta, float* state, const int32_t* state_slot,
                    float* o, int Hk, int Hv, float scale) {
   if (state_slot)
-    hipLaunchKernelGGL((decode_tokens_kernel<kT, true>), grid, dim3(kThreads), 0, stream, q, q_stride, k,
+    hipLaunchKernelGGL((decode_tokens_kernel<kT, kTokThreads, true>), grid, dim3(kTokThreads), 0, stream, q, q_stride, k,
                        k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
   else
-    hipLaunchKernelGGL((decode_tokens_kernel<kT, false>), grid, dim3(kThreads), 0, stream, q, q_stride, k,
+    hipLaunchKernelGGL((decode_tokens_kernel<kT, kTokThreads, false>), grid, dim3(kTokThreads), 0, stream, q, q_stride, k,
                        k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
 }
 
@@ -244,10 +256,10 @@ hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_
   if (n_seqs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv));
   if (state_slot)
-    hipLaunchKernelGGL(decode_step_kernel<true>, grid, dim3(kThreads), 0, stream, q, q_stride, k,
+    hipLaunchKernelGGL((decode_step_kernel<kStepThreads, true>), grid, dim3(kStepThreads), 0, stream, q, q_stride, k,
                        k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
   else
-    hipLaunchKernelGGL(decode_step_kernel<false>, grid, dim3(kThreads), 0, stream, q, q_stride, k,
+    hipLaunchKernelGGL((decode_step_kernel<kStepThreads, false>), grid, dim3(kStepThreads), 0, stream, q, q_stride, k,
                        k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
   return hipGetLastError();
 }
