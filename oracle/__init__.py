@@ -58,6 +58,9 @@ def _load():
     lib.oracle_gated_rmsnorm.restype = ctypes.c_int
     lib.oracle_chunk_map.argtypes = [_ip, ctypes.c_int32, ctypes.c_int32, _ip, _ip, _ip]
     lib.oracle_chunk_map.restype = ctypes.c_int
+    lib.oracle_gate_prep.argtypes = [_dp, ctypes.c_int64, _dp, ctypes.c_int64, _dp, _dp, _dp, _dp,
+                                     ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_gate_prep.restype = ctypes.c_int
     lib.oracle_round_bf16_array.argtypes = [_dp, _dp, ctypes.c_int64]
     lib.oracle_round_bf16_array.restype = None
     _lib = lib
@@ -166,6 +169,23 @@ def gated_rmsnorm(o, z, w, eps=1e-6, stage_bf16=False, n_threads=None):
     if rc:
         raise ValueError(f"oracle_gated_rmsnorm failed ({rc})")
     return out
+
+
+def gate_prep(a, b, A_log, dt_bias):
+    """g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b) per (token, value head).
+
+    a, b [T, Hv] (bf16 bits as uint16, or values); A_log, dt_bias [Hv]. Returns (g, beta) fp64.
+    """
+    lib = _load()
+    a, b, A_log, dt_bias = map(_f64, (a, b, A_log, dt_bias))
+    T, Hv = a.shape
+    g = np.zeros((T, Hv))
+    beta = np.zeros((T, Hv))
+    rc = lib.oracle_gate_prep(_ptr(a), Hv, _ptr(b), Hv, _ptr(A_log), _ptr(dt_bias), _ptr(g),
+                              _ptr(beta), T, Hv)
+    if rc:
+        raise ValueError(f"oracle_gate_prep failed ({rc})")
+    return g, beta
 
 
 def round_bf16(x):

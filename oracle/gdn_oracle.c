@@ -341,6 +341,36 @@ int oracle_gated_rmsnorm(const double* o, const double* z, const double* w, doub
 }
 
 /* ---------------------------------------------------------------------------
+ * Gate preparation from per-head projections.  The pages name a forget gate
+ * (the explanatory paragraph on the Gated Delta Rule in the Deep Dive article)
+ * but not its parametrisation; the reading taken here is a learned per-head
+ * decay rate A_h = exp(A_log[h]) times a data-dependent step
+ * softplus(a + dt_bias[h]):
+ *     g[t][h]    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *     beta[t][h] = sigmoid(b[t][h])
+ * so the decay exp(g) = (1 + e^{a + dt_bias})^{-A_h} lies in (0, 1].
+ *   a, b : [T, Hv] with row strides a_stride, b_stride (elements)
+ *   A_log, dt_bias : [Hv];  g, beta : [T, Hv] contiguous.
+ * softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^{-|x|}).
+ * ------------------------------------------------------------------------- */
+static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+int oracle_gate_prep(const double* a, int64_t a_stride, const double* b, int64_t b_stride,
+                     const double* A_log, const double* dt_bias, double* g, double* beta,
+                     int64_t T, int32_t Hv)
+{
+    if (!a || !b || !A_log || !dt_bias || !g || !beta || T < 0 || Hv <= 0 ||
+        a_stride < Hv || b_stride < Hv)
+        return ORACLE_ERR_ARG;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < Hv; ++h) {
+            g[t * Hv + h] = -exp(A_log[h]) * softplus(a[t * a_stride + h] + dt_bias[h]);
+            beta[t * Hv + h] = sigmoid(b[t * b_stride + h]);
+        }
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
  * Varlen chunk map (integer bookkeeping of the chunked prefill), from its
  * definition:
  *   order[r]     sequence ids sorted by length, longest first, ties by id

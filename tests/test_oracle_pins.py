@@ -361,3 +361,49 @@ def test_chunk_map_brute_force(lens):
     for _, t0, ln in rows:
         covered[t0:t0 + ln] += 1
     assert np.all(covered == 1)
+
+
+# ----------------------------------------------------------------- gate prep
+
+_A_LOG = np.log(np.array([0.5, 1.0, 2.0, 4.0, 8.0, 16.0]))
+_DT = np.array([0.0, 0.5, -1.0, 2.0, -3.0, 1.0])
+
+
+def test_gate_prep_closed_forms():
+    """a + dt_bias = 0 makes the step softplus(0) = ln 2, so g = -A ln 2 per head;
+    b = 0 gives beta = 1/2."""
+    Hv = _A_LOG.size
+    a = np.tile(-_DT, (3, 1))
+    g, beta = oracle.gate_prep(a, np.zeros((3, Hv)), _A_LOG, _DT)
+    np.testing.assert_allclose(g, np.tile(-np.exp(_A_LOG) * np.log(2.0), (3, 1)), rtol=1e-15)
+    assert np.all(beta == 0.5)
+
+
+def test_gate_prep_power_form_and_logit():
+    """The decay exp(g) equals (1 + e^(a + dt_bias))^(-exp(A_log)) -- the same
+    value written as a power -- head by head (a wrong head index, sign or
+    exponent fails it); beta / (1 - beta) = e^b; g < 0 and 0 < beta < 1."""
+    r = np.random.default_rng(41)
+    Hv = _A_LOG.size
+    a = r.normal(0.0, 2.0, (64, Hv))
+    b = r.normal(0.0, 3.0, (64, Hv))
+    g, beta = oracle.gate_prep(a, b, _A_LOG, _DT)
+    alpha = (1.0 + np.exp(a + _DT)) ** (-np.exp(_A_LOG))
+    np.testing.assert_allclose(np.exp(g), alpha, rtol=1e-12)
+    np.testing.assert_allclose(beta / (1.0 - beta), np.exp(b), rtol=1e-12)
+    assert np.all(g < 0) and np.all((beta > 0) & (beta < 1))
+
+
+def test_gate_prep_softplus_reflection_and_tails():
+    """softplus(x) - softplus(-x) = x; softplus(x) = x to rounding for large x
+    (no overflow at x = 800) and e^x for very negative x."""
+    x = np.array([[-800.0, -50.0, -3.0, 0.25, 7.0, 50.0, 800.0]])
+    Hv = x.shape[1]
+    zero = np.zeros(Hv)
+    gp, _ = oracle.gate_prep(x, np.zeros_like(x), zero, zero)    # A = 1: g = -softplus(x)
+    gm, _ = oracle.gate_prep(-x, np.zeros_like(x), zero, zero)
+    np.testing.assert_allclose(gm - gp, x, rtol=1e-15, atol=1e-15)
+    sp = -gp[0]
+    assert sp[-1] == 800.0 and abs(sp[-2] - 50.0) <= 1e-14
+    np.testing.assert_allclose(sp[1], np.exp(-50.0), rtol=1e-14)
+    assert sp[0] == 0.0 or sp[0] < 1e-300
