@@ -12,7 +12,8 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm;
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
-A second prefill timing writes o in bf16 (`prefill_bf16_o`, not the headline).
+Two more prefill timings, not the headline: o written in bf16
+(`prefill_bf16_o`) and the gates formed from bf16 projections (`prefill_gated`).
 `roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
 kernel, then the sequential scan kernel, back to back on one stream):
 algorithmic bytes per launch over the launch duration measured with HIP events
@@ -111,6 +112,20 @@ def leg_prefill(args, ops, synth, torch):
     ev16, _ = time_leg(step16, args.steps, args.warmup)
     res.update(bf16o_event_ms=ev16, bf16o_tokens_per_s=T / (ev16 * 1e-3))
     log(f"[prefill] bf16 o: {ev16:.3f} ms/launch, {res['bf16o_tokens_per_s'] / 1e6:.2f} M tok/s")
+
+    # the same launch with the gates formed from bf16 projections (gdn_chunk_fwd_gated)
+    gi = synth.gate_inputs(1007, T)
+    ga = torch.from_numpy(gi.a.view("int16")).view(torch.bfloat16).cuda()
+    gb = torch.from_numpy(gi.b.view("int16")).view(torch.bfloat16).cuda()
+    A_log, dt_bias = torch.from_numpy(gi.A_log).cuda(), torch.from_numpy(gi.dt_bias).cuda()
+
+    def step_gated():
+        ops.gdn_chunk_fwd_gated(q, k, v, ga, gb, A_log, dt_bias, initial_state=h0, final_state=fs,
+                                o=o, n_seqs=1, workspace=ws)
+
+    evg, _ = time_leg(step_gated, args.steps, args.warmup)
+    res.update(gated_event_ms=evg, gated_tokens_per_s=T / (evg * 1e-3))
+    log(f"[prefill] gates from projections: {evg:.3f} ms/launch")
     return res, ci
 
 
@@ -367,6 +382,8 @@ def main():
                         "unit": "TFLOP/s", "frac": round(pre["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
         line["prefill_bf16_o"] = {"launch_ms": round(pre["bf16o_event_ms"], 4),
                                   "tokens_per_s": round(pre["bf16o_tokens_per_s"], 1)}
+        line["prefill_gated"] = {"launch_ms": round(pre["gated_event_ms"], 4),
+                                 "tokens_per_s": round(pre["gated_tokens_per_s"], 1)}
     if "decode" in out:
         d = out["decode"]
         line["decode"] = {"state_GBps": round(d["state_gbps"], 1),

@@ -179,70 +179,99 @@ gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_to
 }
 
 // Shared by gdn_chunk_fwd (fp32 o) and gdn_chunk_fwd_bf16o (bf16 o).
-static gdn_status chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
-                            int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
-                            const float* g, const float* beta, void* o, bool o_bf16,
+// The common host side of the prefill entry points.  `gates` holds either g,
+// beta or the projections a, b with A_log, dt_bias; with `state_slot` the
+// initial and final states are one pool (h0 == hT) indexed per sequence.
+static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_stride,
+                            const uint16_t* k, int64_t k_tok_stride, const uint16_t* v,
+                            int64_t v_tok_stride, const gdn::GateInputs& gates, void* o, bool o_bf16,
                             const float* initial_state, float* final_state,
+                            const int32_t* state_slot, int32_t n_slots,
                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                             int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  if (T_total > 0 && (!q || !k || !v || !g || !beta || !o))
-    return fail(GDN_ERR_NULL, "gdn_chunk_fwd: q, k, v, g, beta and o are required");
+  const bool projected = gates.a != nullptr || gates.b != nullptr || gates.A_log != nullptr ||
+                         gates.dt_bias != nullptr;
+  const bool gates_given = projected ? (gates.a && gates.b && gates.A_log && gates.dt_bias)
+                                     : (gates.g && gates.beta);
+  if (T_total > 0 && (!q || !k || !v || !gates_given || !o))
+    return fail(GDN_ERR_NULL, "%s: q, k, v, the gates and o are required", fn);
+  if (state_slot && n_seqs > 0 && !initial_state)
+    return fail(GDN_ERR_NULL, "%s: the state pool is required", fn);
   if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
-    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: bad sizes or Hv %% Hk != 0");
-  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_fwd: dk = dv = 128 only");
+    return fail(GDN_ERR_SHAPE, "%s: bad sizes or Hv %% Hk != 0", fn);
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "%s: dk = dv = 128 only", fn);
   if (q_tok_stride < static_cast<int64_t>(Hk) * dk || k_tok_stride < static_cast<int64_t>(Hk) * dk ||
       v_tok_stride < static_cast<int64_t>(Hv) * dv || q_tok_stride % 8 || k_tok_stride % 8 ||
       v_tok_stride % 8)
-    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: token strides too small or not multiples of 8");
+    return fail(GDN_ERR_SHAPE, "%s: token strides too small or not multiples of 8", fn);
+  if (projected && (gates.a_stride < Hv || gates.b_stride < Hv))
+    return fail(GDN_ERR_SHAPE, "%s: a and b token strides must be at least Hv", fn);
+  if (state_slot && n_slots < 0) return fail(GDN_ERR_SHAPE, "%s: n_slots < 0", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(g, 4) ||
-      !aligned(beta, 4) || !aligned(cu_seqlens, 4))
-    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: q, k, v, o and states must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: scale must be finite");
+      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(gates.g, 4) ||
+      !aligned(gates.beta, 4) || !aligned(gates.a, 2) || !aligned(gates.b, 2) ||
+      !aligned(gates.A_log, 4) || !aligned(gates.dt_bias, 4) || !aligned(cu_seqlens, 4) ||
+      !aligned(state_slot, 4))
+    return fail(GDN_ERR_SHAPE,
+                "%s: misaligned pointer (q, k, v, o, states: 16 bytes; a, b: 2; the rest: 4)", fn);
+  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "%s: scale must be finite", fn);
   if (!cu_seqlens) {
     const gdn_status s = check_equal_split(n_seqs, T_total);
     if (s) return s;
   } else if (n_seqs == 0 && T_total != 0) {
-    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: T_total > 0 with no sequences");
+    return fail(GDN_ERR_SHAPE, "%s: T_total > 0 with no sequences", fn);
   }
   // grid size: ceil(n_seqs * Hk / 8) * 8 * (Hv / Hk) * 2 blocks
   if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
-    return fail(GDN_ERR_SHAPE, "gdn_chunk_fwd: too many (sequence, head) pairs");
+    return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
   const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
   const Range rq = range_of(q, T_total, q_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rk = range_of(k, T_total, k_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rv = range_of(v, T_total, v_tok_stride, static_cast<int64_t>(Hv) * dv, 2);
-  const Range rg = range_of(g, T_total, Hv, Hv, 4);
-  const Range rb = range_of(beta, T_total, Hv, Hv, 4);
+  const Range rg = range_of(gates.g, T_total, Hv, Hv, 4);
+  const Range rb = range_of(gates.beta, T_total, Hv, Hv, 4);
+  const Range ra = range_of(gates.a, T_total, gates.a_stride, Hv, 2);
+  const Range rb2 = range_of(gates.b, T_total, gates.b_stride, Hv, 2);
+  const Range rA = range_of(gates.A_log, 1, 0, Hv, 4);
+  const Range rdt = range_of(gates.dt_bias, 1, 0, Hv, 4);
+  const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
   const Range ro = range_of(o, T_total, static_cast<int64_t>(Hv) * dv, static_cast<int64_t>(Hv) * dv, o_bf16 ? 2 : 4);
   const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
-  const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
-  const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
+  const int32_t n_states = state_slot ? n_slots : n_seqs;
+  const Range r0 = range_of(initial_state, n_states, ssz, ssz, 4);
+  const Range rT = range_of(final_state, n_states, ssz, ssz, 4);
   const Range rw = range_of(workspace, 1, 0, static_cast<int64_t>(ws.total), 1);
-  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &r0})
-    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: o overlaps an input");
-  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro})
-    if (overlap(*in, rT)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: final_state overlaps o or an input");
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &r0})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: o overlaps an input", fn);
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro})
+    if (overlap(*in, rT)) return fail(GDN_ERR_ALIAS, "%s: final_state overlaps o or an input", fn);
   if (overlap(r0, rT) && initial_state != final_state)
-    return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: final_state partially overlaps initial_state");
-  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ro, &r0, &rT})
-    if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "gdn_chunk_fwd: workspace overlaps a tensor");
+    return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
+  for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro, &r0, &rT})
+    if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps a tensor", fn);
   if (n_seqs > 0) {
     if (!workspace || workspace_bytes < ws.total)
-      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace of %zu bytes needed", ws.total);
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, ws.total);
     if (!aligned(workspace, 256))
-      return fail(GDN_ERR_WORKSPACE, "gdn_chunk_fwd: workspace must be 256-byte aligned");
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   }
   if (cu_seqlens && env_validate_seqlens()) {
     const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
     if (s) return s;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g,
-                                          beta, o, o_bf16, initial_state, final_state, cu_seqlens,
-                                          n_seqs, T_total, Hk, Hv, scale, workspace, st),
-                    "gdn_chunk_fwd launch");
+  return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, gates,
+                                          o, o_bf16, initial_state, final_state, state_slot,
+                                          cu_seqlens, n_seqs, T_total, Hk, Hv, scale, workspace, st),
+                    "prefill launch");
+}
+
+static gdn::GateInputs given_gates(const float* g, const float* beta) {
+  gdn::GateInputs gi;
+  gi.g = g;
+  gi.beta = beta;
+  return gi;
 }
 
 gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
@@ -252,9 +281,10 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta, o, false,
-                   initial_state, final_state, cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale,
-                   workspace, workspace_bytes, stream);
+  return chunk_fwd("gdn_chunk_fwd", q, q_tok_stride, k, k_tok_stride, v, v_tok_stride,
+                   given_gates(g, beta), o, false, initial_state, final_state, nullptr, 0,
+                   cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale, workspace, workspace_bytes,
+                   stream);
 }
 
 gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
@@ -264,9 +294,43 @@ gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const ui
                                const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
                                int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta, o, true,
-                   initial_state, final_state, cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale,
-                   workspace, workspace_bytes, stream);
+  return chunk_fwd("gdn_chunk_fwd_bf16o", q, q_tok_stride, k, k_tok_stride, v, v_tok_stride,
+                   given_gates(g, beta), o, true, initial_state, final_state, nullptr, 0,
+                   cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale, workspace, workspace_bytes,
+                   stream);
+}
+
+gdn_status gdn_chunk_fwd_pooled(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                                int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                                const float* g, const float* beta, void* o, int32_t o_is_bf16,
+                                float* state, const int32_t* state_slot, int32_t n_slots,
+                                const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_seqs > 0 && !state_slot)
+    return fail(GDN_ERR_NULL, "gdn_chunk_fwd_pooled: state_slot is required");
+  return chunk_fwd("gdn_chunk_fwd_pooled", q, q_tok_stride, k, k_tok_stride, v, v_tok_stride,
+                   given_gates(g, beta), o, o_is_bf16 != 0, state, state,
+                   n_seqs > 0 ? state_slot : nullptr, n_slots, cu_seqlens, n_seqs, T_total, Hk, Hv,
+                   dk, dv, scale, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                               int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                               const uint16_t* a, int64_t a_tok_stride, const uint16_t* b,
+                               int64_t b_tok_stride, const float* A_log, const float* dt_bias,
+                               float* o, const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                               int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (T_total > 0 && (!a || !b || !A_log || !dt_bias))
+    return fail(GDN_ERR_NULL, "gdn_chunk_fwd_gated: a, b, A_log and dt_bias are required");
+  gdn::GateInputs gi;
+  gi.a = a; gi.a_stride = a_tok_stride; gi.b = b; gi.b_stride = b_tok_stride;
+  gi.A_log = A_log; gi.dt_bias = dt_bias;
+  return chunk_fwd("gdn_chunk_fwd_gated", q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, gi,
+                   o, false, initial_state, final_state, nullptr, 0, cu_seqlens, n_seqs, T_total,
+                   Hk, Hv, dk, dv, scale, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,

@@ -143,6 +143,11 @@ struct PrepParams {
   const uint16_t* q; const uint16_t* k;
   int64_t qs, ks;
   const float* g; const float* beta;
+  // gates from the per-head projections instead of g, beta (when ga != nullptr):
+  // g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)
+  const uint16_t* ga; const uint16_t* gb;
+  int64_t gas, gbs;
+  const float* A_log; const float* dt_bias;
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* chunk_off;   // varlen chunk map (device)
   const int32_t* chunk_tab;
@@ -247,6 +252,8 @@ __device__ __forceinline__ void prep_elementwise(PrepSmem& sm, const floatx4 (&g
   }
 }
 
+// kGated: the gates come from the projections (p.ga, p.gb, p.A_log, p.dt_bias).
+template <bool kGated>
 __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
   const int kh = blockIdx.x;
@@ -272,9 +279,20 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   // g and beta of value head vh, one token per lane
   auto load_gb = [&](int vh, float& gv, float& bv) {
     const bool valid = lane < len;
-    const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + kh * p.group + vh;
-    gv = valid ? p.g[gi] : 0.f;
-    bv = valid ? p.beta[gi] : 0.f;
+    if (kGated) {
+      // softplus(x) = max(x, 0) + log1p(e^-|x|), with the accurate libm forms
+      const int64_t t = t0 + min(lane, len - 1);
+      const int h = kh * p.group + vh;
+      const float x = bf16_to_f32(p.ga[t * p.gas + h]) + p.dt_bias[h];
+      const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+      const float y = bf16_to_f32(p.gb[t * p.gbs + h]);
+      gv = valid ? -expf(p.A_log[h]) * sp : 0.f;
+      bv = valid ? 1.f / (1.f + expf(-y)) : 0.f;
+    } else {
+      const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + kh * p.group + vh;
+      gv = valid ? p.g[gi] : 0.f;
+      bv = valid ? p.beta[gi] : 0.f;
+    }
   };
   // decay tables of value head vb0 + w (wave w, lane = token): G = inclusive
   // cumsum of g, then b, b gamma, scale gamma, exp(G_L - G) and gamma_L
@@ -433,6 +451,7 @@ struct ScanParams {
   void* o;                    // fp32, or bf16 when o_bf16
   int o_bf16;
   const float* h0; float* hT;
+  const int32_t* slots;       // nullptr: sequence n uses state n of h0 / hT
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* order;       // longest-first schedule (varlen)
   const int32_t* chunk_off;   // first chunk of each sequence (varlen)
@@ -492,6 +511,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   const int h = kh * p.group + member / kParts;
   const int part = member % kParts;
   const int n = p.order ? p.order[rank] : rank;
+  const int sn = p.slots ? p.slots[n] : n;    // state of sequence n
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -593,7 +613,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
     constexpr int NT = decltype(nt_c)::value;
     // state tiles: S^T rows (dk) 16 dt + 4 grp + e, column (dv) 16 t + col
     floatx4 sT[NT][8];
-    const int64_t sbase0 = ((static_cast<int64_t>(n) * p.Hv + h) * kD + part * kDvPerWg + col) * kD;
+    const int64_t sbase0 = ((static_cast<int64_t>(sn) * p.Hv + h) * kD + part * kDvPerWg + col) * kD;
     if (p.h0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -927,8 +947,9 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
 }
 
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
-                            const uint16_t* v, int64_t vs, const float* g, const float* beta,
-                            void* o, bool o_bf16, const float* h0, float* hT, const int32_t* cu,
+                            const uint16_t* v, int64_t vs, const GateInputs& gates,
+                            void* o, bool o_bf16, const float* h0, float* hT,
+                            const int32_t* state_slot, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
@@ -948,17 +969,23 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   }
   if (T_total > 0 && n_chunk_slots > 0) {
     PrepParams pp;
-    pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = g; pp.beta = beta;
+    pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = gates.g; pp.beta = gates.beta;
+    pp.ga = gates.a; pp.gb = gates.b; pp.gas = gates.a_stride; pp.gbs = gates.b_stride;
+    pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
     pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
     pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
     pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
     pp.scale = scale;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
+    if (gates.a)
+      hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
+    else
+      hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanParams sp;
   sp.v = v; sp.vs = vs; sp.o = o; sp.o_bf16 = o_bf16 ? 1 : 0; sp.h0 = h0; sp.hT = hT;
+  sp.slots = state_slot;
   sp.cu = cu; sp.order = cu ? order : nullptr; sp.chunk_off = chunk_off;
   sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;

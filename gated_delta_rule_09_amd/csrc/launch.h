@@ -47,9 +47,26 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv);
 hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
                             int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream);
 
+// The gates of the prefill: g, beta [T, Hv] fp32 as given, or (a != nullptr)
+// formed in the prep kernel from the bf16 projections a, b [T, Hv] (token
+// strides a_stride, b_stride) and the per-head A_log, dt_bias.
+struct GateInputs {
+  const float* g = nullptr;
+  const float* beta = nullptr;
+  const uint16_t* a = nullptr;
+  int64_t a_stride = 0;
+  const uint16_t* b = nullptr;
+  int64_t b_stride = 0;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
+};
+
+// state_slot != nullptr: sequence n reads h0[state_slot[n]] and writes
+// hT[state_slot[n]] (h0 == hT: a state pool updated in place).
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
-                            const uint16_t* v, int64_t vs, const float* g, const float* beta,
-                            void* o, bool o_bf16, const float* h0, float* hT, const int32_t* cu,
+                            const uint16_t* v, int64_t vs, const GateInputs& gates,
+                            void* o, bool o_bf16, const float* h0, float* hT,
+                            const int32_t* state_slot, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream);
 

@@ -33,6 +33,12 @@ _SIGS = {
                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "gdn_chunk_fwd_bf16o": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gdn_chunk_fwd_pooled": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
+                                    _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                    _vp, _sz, _vp]),
+    "gdn_chunk_fwd_gated": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _f32, _vp, _sz, _vp]),
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
@@ -217,6 +223,112 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv, scale, _ptr(workspace),
             ws_bytes, _stream())
     _check(st, "gdn_chunk_fwd_bf16o" if o_bf16 else "gdn_chunk_fwd")
+    return o, final_state
+
+
+def _qkv_checks(q, k, v):
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+        _inner_contig(t, nm)
+
+
+def _workspace(workspace, n_seqs, T, Hk, Hv, dk, device):
+    if n_seqs <= 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(gdn_chunk_fwd_workspace_bytes(n_seqs, T, Hk, Hv, dk),
+                                dtype=torch.uint8, device=device)
+    return workspace, workspace.numel()
+
+
+def gdn_chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                         beta: torch.Tensor, state: torch.Tensor, state_slot: torch.Tensor, *,
+                         cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                         scale: float = 1.0, o: Optional[torch.Tensor] = None,
+                         o_bf16: bool = False,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill continuing from a state pool: sequence n starts from
+    state[state_slot[n]] and leaves its final state there (in place).
+    state [n_slots, Hv, 128, 128] fp32; returns o [T, Hv, 128]."""
+    _qkv_checks(q, k, v)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(state, "state", torch.float32, 4)
+    _need(state_slot, "state_slot", torch.int32, 1)
+    if not (g.is_contiguous() and beta.is_contiguous() and state.is_contiguous()):
+        raise ValueError("g, beta and state must be contiguous")
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = state_slot.shape[0]
+    if o is not None and o.dtype == torch.bfloat16:
+        o_bf16 = True
+    odt = torch.bfloat16 if o_bf16 else torch.float32
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=odt, device=q.device)
+    _need(o, "o", odt, 3)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    workspace, ws_bytes = _workspace(workspace, n_seqs, T, Hk, Hv, dk, q.device)
+    st = lib().gdn_chunk_fwd_pooled(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v),
+                                    v.stride(0), _ptr(g), _ptr(beta), _ptr(o),
+                                    1 if o_bf16 else 0, _ptr(state), _ptr(state_slot),
+                                    state.shape[0], _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv,
+                                    scale, _ptr(workspace), ws_bytes, _stream())
+    _check(st, "gdn_chunk_fwd_pooled")
+    return o
+
+
+def gdn_chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                        b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor, *,
+                        initial_state: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True,
+                        cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                        scale: float = 1.0, o: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill with the gates formed in the prep kernel from the bf16
+    projections a, b [T, Hv] (token stride free, columns contiguous) and
+    A_log, dt_bias [Hv] fp32: g = -exp(A_log) softplus(a + dt_bias),
+    beta = sigmoid(b).  Returns (o fp32, final_state or None)."""
+    _qkv_checks(q, k, v)
+    for t, nm in ((a, "a"), (b, "b")):
+        _need(t, nm, torch.bfloat16, 2)
+        _inner_contig(t, nm)
+    for t, nm in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, nm, torch.float32, 1)
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32, 3)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n_seqs, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, 4)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    workspace, ws_bytes = _workspace(workspace, n_seqs, T, Hk, Hv, dk, q.device)
+    st = lib().gdn_chunk_fwd_gated(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v),
+                                   v.stride(0), _ptr(a), a.stride(0), _ptr(b), b.stride(0),
+                                   _ptr(A_log), _ptr(dt_bias), _ptr(o), _ptr(initial_state),
+                                   _ptr(final_state), _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv,
+                                   scale, _ptr(workspace), ws_bytes, _stream())
+    _check(st, "gdn_chunk_fwd_gated")
     return o, final_state
 
 

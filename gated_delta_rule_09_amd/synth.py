@@ -16,6 +16,8 @@ recipe of the mixer:
   x     ~ N(0, 1) bf16 (projected q|k|v channels before the conv)
   conv w ~ N(0, 0.5^2) bf16, layout [C, 4]
   z     ~ N(0, 1) bf16;  norm weight = 1 + N(0, 0.02^2) fp32
+  gate projections a, b ~ N(0, 1) bf16 [T, Hv]; per head A_log = log U(1, 16),
+  dt_bias ~ U(-7, -2.3) fp32 (a step of about 0.001 .. 0.1 at a = 0)
 All draws use numpy's PCG64 from one seed, in the order documented per function.
 """
 from __future__ import annotations
@@ -111,6 +113,24 @@ def chunk_inputs(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DI
     if h0_std is not None:
         h0 = (r.standard_normal((n, Hv, d, d), dtype=np.float32) * np.float32(h0_std))
     return ChunkInputs(q, k, v, g, beta, h0, cu, n, {"seed": seed, "T": T})
+
+
+@dataclass
+class GateInputs:
+    a: np.ndarray        # uint16 [T, Hv] (bf16 projection of the decay step)
+    b: np.ndarray        # uint16 [T, Hv] (bf16 projection of the write strength)
+    A_log: np.ndarray    # f32 [Hv]
+    dt_bias: np.ndarray  # f32 [Hv]
+
+
+def gate_inputs(seed: int, T: int, Hv: int = HV) -> GateInputs:
+    """Per-head gate projections and parameters. Draw order: a, b, A, dt_bias."""
+    r = rng(seed)
+    a = bf16_bits(r.standard_normal((T, Hv), dtype=np.float32))
+    b = bf16_bits(r.standard_normal((T, Hv), dtype=np.float32))
+    A_log = np.log(r.uniform(1.0, 16.0, size=Hv)).astype(np.float32)
+    dt_bias = r.uniform(-7.0, -2.3, size=Hv).astype(np.float32)
+    return GateInputs(a, b, A_log, dt_bias)
 
 
 @dataclass

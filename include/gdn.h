@@ -60,7 +60,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -158,6 +158,54 @@ gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const ui
                                int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
                                const float* g, const float* beta, uint16_t* o,
                                const float* initial_state, float* final_state,
+                               const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                               int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_pooled -- gdn_chunk_fwd for sequences that continue from, and
+ * return to, a pool of per-sequence states (continuous batching: one call may
+ * mix long prefills with sequences of one or a few new tokens), as serving
+ * many concurrent requests needs (the model card's Hardware Requirements
+ * table); the rule is that of gdn_chunk_fwd.
+ *   state       [n_slots, Hv, dv, dk] fp32, 16-byte aligned, read and written
+ *               in place: sequence n starts from state[state_slot[n]] and
+ *               leaves its final state there; an empty sequence leaves its
+ *               slot unchanged; slots not named are not touched
+ *   state_slot  [n_seqs] int32 device array, required when n_seqs > 0; slots
+ *               distinct and in [0, n_slots) (not checked on the device)
+ *   o           [T_total, Hv, dv] fp32 (o_is_bf16 == 0) or bf16 (as
+ *               gdn_chunk_fwd_bf16o), must not overlap the state pool
+ * Every other argument, the workspace and the errors as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_pooled(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                                int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                                const float* g, const float* beta, void* o, int32_t o_is_bf16,
+                                float* state, const int32_t* state_slot, int32_t n_slots,
+                                const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_gated -- gdn_chunk_fwd with the gates formed inside the prep
+ * kernel from the per-head projections instead of read as g and beta.  The
+ * Deep Dive article's paragraph on the Gated Delta Rule names a forget gate
+ * without its form; the form taken is a per-head decay rate times a
+ * data-dependent softplus step, and a sigmoid write strength:
+ *     g[t][h]    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *     beta[t][h] = sigmoid(b[t][h])
+ * (fp32 arithmetic on the bf16 inputs).
+ *   a, b         [T_total, Hv] bf16 with token strides a_tok_stride,
+ *                b_tok_stride (elements, >= Hv), 2-byte aligned; may be
+ *                columns of a wider projection output
+ *   A_log, dt_bias  [Hv] fp32
+ * Every other argument, the workspace and the errors as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                               int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                               const uint16_t* a, int64_t a_tok_stride, const uint16_t* b,
+                               int64_t b_tok_stride, const float* A_log, const float* dt_bias,
+                               float* o, const float* initial_state, float* final_state,
                                const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
                                int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
                                void* workspace, size_t workspace_bytes, void* stream);

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -156,6 +156,44 @@ def test_decode_mixer_step_validation(lib):
     assert mix(out=P(7) + 64) == ALIAS                 # out inside the state
     assert mix(cs=P(0) + 16) == ALIAS                  # conv state over x
     assert mix(st=P(2) + 256) == ALIAS                 # state over the conv state
+
+
+def test_chunk_pooled_validation(lib):
+    def pooled(**kw):
+        a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), b=P(4), o=P(5), bf=0,
+                 st=P(6), slot=P(7), nslots=8, cu=None, N=2, T=128, ws=P(9), wsb=1 << 30)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_pooled(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"],
+                                        a["b"], a["o"], a["bf"], a["st"], a["slot"], a["nslots"],
+                                        a["cu"], a["N"], a["T"], 16, 48, 128, 128, 1.0, a["ws"],
+                                        a["wsb"], None)
+    assert pooled(slot=None) == NULL
+    assert pooled(st=None) == NULL
+    assert pooled(nslots=-1) == SHAPE
+    assert pooled(slot=P(7) + 2) == SHAPE              # misaligned slot map
+    assert pooled(o=P(6) + 1024) == ALIAS              # o inside the pool
+    assert pooled(slot=P(6) + 4096) == ALIAS           # slot map inside the pool
+    assert pooled(wsb=16) == WS
+
+
+def test_chunk_gated_validation(lib):
+    def gated(**kw):
+        a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, a=P(3), as_=48, b=P(4),
+                 bs=48, A=P(5), dt=P(5) + 256, o=P(6), h0=None, hT=P(7), cu=None, N=1, T=128,
+                 ws=P(9), wsb=1 << 30)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_gated(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["a"],
+                                       a["as_"], a["b"], a["bs"], a["A"], a["dt"], a["o"],
+                                       a["h0"], a["hT"], a["cu"], a["N"], a["T"], 16, 48, 128,
+                                       128, 1.0, a["ws"], a["wsb"], None)
+    assert gated(a=None) == NULL
+    assert gated(dt=None) == NULL
+    assert gated(a=None, b=None, A=None, dt=None, q=None, k=None, v=None, o=None, hT=None,
+                 N=0, T=0) == OK
+    assert gated(as_=40) == SHAPE                       # a's token stride below Hv
+    assert gated(A=P(5) + 2) == SHAPE                   # misaligned A_log
+    assert gated(o=P(3) + 64) == ALIAS                  # o over a
+    assert gated(hT=P(4)) == ALIAS                      # final state over b
 
 
 def test_conv_validation(lib):

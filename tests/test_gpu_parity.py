@@ -76,6 +76,107 @@ def test_chunk_bf16_output(lens):
     assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
 
 
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_chunk_pooled_mixed_batch(out_bf16):
+    """A batch mixing prefills with one- and two-token sequences (and an empty
+    one), each continuing from its slot of a state pool and leaving its final
+    state there; unnamed slots untouched bit for bit."""
+    lens = [1, 300, 0, 1, 2, 65, 1, 129]
+    n_slots = 12
+    log(f"chunk_fwd_pooled lens={lens} bf16_o={out_bf16}")
+    ci = synth.chunk_inputs(3500, sum(lens), Hk=4, Hv=12, lengths=lens)
+    pool = np.random.default_rng(35).standard_normal((n_slots, 12, 128, 128)).astype(np.float32) * 0.05
+    slots = np.array([9, 2, 11, 0, 5, 7, 3, 10], dtype=np.int32)
+    st = dev_f32(pool)
+    o = ops.gdn_chunk_fwd_pooled(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g),
+                                 dev_f32(ci.beta), st, dev_i32(slots),
+                                 cu_seqlens=dev_i32(ci.cu_seqlens), scale=0.9, o_bf16=out_bf16)
+    ro, rT = oracle.recurrence(ci.q, ci.k, ci.v, ci.g, ci.beta, pool[slots],
+                               cu_seqlens=ci.cu_seqlens, n_seqs=len(lens), scale=0.9)
+    got = host(o)
+    if out_bf16:
+        d = got - ro
+        rel = np.linalg.norm(d) / np.linalg.norm(ro)
+        mabs = np.abs(d).max() / np.abs(ro).max()
+        log(f"  o (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
+        assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+    else:
+        assert_close(got, ro, "o")
+    got_st = host(st)
+    assert_close(got_st[slots], rT, "states (slots used)")
+    np.testing.assert_array_equal(got_st[slots[2]], pool[slots[2]])   # the empty sequence
+    others = [i for i in range(n_slots) if i not in slots]
+    np.testing.assert_array_equal(got_st[others], pool[others])
+
+
+def test_chunk_pooled_equals_gather_scatter():
+    """The pooled call computes exactly what gdn_chunk_fwd computes on the
+    gathered states (same kernels, same arithmetic): bit-identical o and
+    states."""
+    lens = [70, 1, 3, 200]
+    log(f"chunk_fwd_pooled vs gathered gdn_chunk_fwd lens={lens}")
+    ci = synth.chunk_inputs(3510, sum(lens), Hk=2, Hv=6, lengths=lens)
+    pool = np.random.default_rng(36).standard_normal((6, 6, 128, 128)).astype(np.float32) * 0.05
+    slots = np.array([4, 1, 5, 0], dtype=np.int32)
+    args = (dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g), dev_f32(ci.beta))
+    cu = dev_i32(ci.cu_seqlens)
+    st = dev_f32(pool)
+    o1 = ops.gdn_chunk_fwd_pooled(*args, st, dev_i32(slots), cu_seqlens=cu)
+    o2, hT = ops.gdn_chunk_fwd(*args, initial_state=dev_f32(pool[slots]), cu_seqlens=cu)
+    assert torch.equal(o1, o2)
+    np.testing.assert_array_equal(host(st)[slots], host(hT))
+
+
+@pytest.mark.parametrize("strided", [False, True])
+def test_chunk_gated_against_oracle(strided):
+    """Gates formed in the prep kernel from bf16 projections: against the
+    oracle's gate preparation followed by the recurrence.  With `strided`,
+    a and b are columns of a wider projection output."""
+    lens = [129, 0, 64, 7]
+    T, Hv = sum(lens), 12
+    log(f"chunk_fwd_gated lens={lens} strided={strided}")
+    ci = synth.chunk_inputs(3520, T, Hk=4, Hv=Hv, lengths=lens, h0_std=0.05)
+    gi = synth.gate_inputs(3521, T, Hv=Hv)
+    if strided:
+        wide = torch.zeros((T, 3 * Hv + 8), dtype=torch.bfloat16, device="cuda")
+        wide[:, 8:8 + Hv] = dev_bf16(gi.a)
+        wide[:, 8 + 2 * Hv:8 + 3 * Hv] = dev_bf16(gi.b)
+        a_d, b_d = wide[:, 8:8 + Hv], wide[:, 8 + 2 * Hv:8 + 3 * Hv]
+    else:
+        a_d, b_d = dev_bf16(gi.a), dev_bf16(gi.b)
+    o, hT = ops.gdn_chunk_fwd_gated(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), a_d, b_d,
+                                    dev_f32(gi.A_log), dev_f32(gi.dt_bias),
+                                    initial_state=dev_f32(ci.h0), cu_seqlens=dev_i32(ci.cu_seqlens))
+    g, beta = oracle.gate_prep(gi.a, gi.b, gi.A_log, gi.dt_bias)
+    log(f"  g in [{g.min():.3f}, {g.max():.4f}], beta in [{beta.min():.3f}, {beta.max():.3f}]")
+    ro, rT = oracle.recurrence(ci.q, ci.k, ci.v, g, beta, ci.h0, cu_seqlens=ci.cu_seqlens,
+                               n_seqs=len(lens))
+    assert_close(host(o), ro, "o")
+    assert_close(host(hT), rT, "final_state")
+
+
+def test_chunk_gated_equals_given_gates():
+    """The in-kernel gates against torch's fp32 softplus and sigmoid fed to
+    gdn_chunk_fwd: the same up to the fp32 rounding of the two gate
+    computations."""
+    T, Hv = 200, 12
+    log("chunk_fwd_gated vs gdn_chunk_fwd with torch-computed gates")
+    ci = synth.chunk_inputs(3530, T, Hk=4, Hv=Hv)
+    gi = synth.gate_inputs(3531, T, Hv=Hv)
+    a, b = dev_bf16(gi.a), dev_bf16(gi.b)
+    A_log, dt = dev_f32(gi.A_log), dev_f32(gi.dt_bias)
+    q, k, v = dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v)
+    o1, h1 = ops.gdn_chunk_fwd_gated(q, k, v, a, b, A_log, dt)
+    g = (-torch.exp(A_log) * torch.nn.functional.softplus(a.float() + dt)).contiguous()
+    beta = torch.sigmoid(b.float()).contiguous()
+    o2, h2 = ops.gdn_chunk_fwd(q, k, v, g, beta)
+    for name, x1, x2 in (("o", o1, o2), ("state", h1, h2)):
+        x1, x2 = x1.double(), x2.double()
+        rel = ((x1 - x2).norm() / x2.norm()).item()
+        log(f"  {name}: rel_l2 in-kernel vs torch gates = {rel:.3e}")
+        assert rel <= 1e-5, name
+
+
 def test_chunk_zero_initial_state_and_scale():
     log("chunk_fwd T=300 no h0 scale=128^-0.5")
     ci = synth.chunk_inputs(2200, 300)
