@@ -10,7 +10,8 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
           a 4-tokens-per-sequence step (gdn_decode_tokens) and the whole mixer
           step in one launch (gdn_decode_mixer_step);
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
-          RMSNorm;
+          RMSNorm, as four launches and as one gdn_mixer_fwd call (the conv
+          front inside the prep kernel);
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
 Two more prefill timings, not the headline: o written in bf16
 (`prefill_bf16_o`) and the gates formed from bf16 projections (`prefill_gated`).
@@ -224,8 +225,21 @@ def leg_mixer(args, ops, synth, torch):
         ops.gdn_gated_rmsnorm(o, mi["z"], mi["norm_w"], out=out)
 
     ev, wall = time_leg(step, args.steps, args.warmup)
-    res = dict(tokens=T, event_ms=ev, wall_ms=wall, tokens_per_s=T / (wall * 1e-3))
-    log(f"[mixer] {ev:.3f} ms/step, {res['tokens_per_s'] / 1e6:.2f} M tok/s")
+
+    # the same mixer in one call, the conv front inside the prep kernel (gdn_mixer_fwd)
+    ws = torch.empty(ops.gdn_mixer_fwd_workspace_bytes(1, T, HK, HV), dtype=torch.uint8,
+                     device="cuda")
+
+    def fused_step():
+        ops.gdn_mixer_fwd(mi["x"], mi["conv_w"], mi["g"], mi["beta"], mi["z"], mi["norm_w"], Hk=HK,
+                          final_state=fs, n_seqs=1, out=out, workspace=ws)
+
+    fev, fwall = time_leg(fused_step, args.steps, args.warmup)
+    res = dict(tokens=T, event_ms=ev, wall_ms=wall, tokens_per_s=T / (wall * 1e-3),
+               fused_event_ms=fev, fused_tokens_per_s=T / (fwall * 1e-3))
+    log(f"[mixer] {ev:.3f} ms/step, {res['tokens_per_s'] / 1e6:.2f} M tok/s; "
+        f"one call with the conv front fused: {fev:.3f} ms, "
+        f"{res['fused_tokens_per_s'] / 1e6:.2f} M tok/s")
     return res
 
 
@@ -398,7 +412,9 @@ def main():
                                          "alg_GBps": round(d["fused_gbps"], 1)}}
     if "mixer" in out:
         line["mixer_T8192"] = {"tokens_per_s": round(out["mixer"]["tokens_per_s"], 1),
-                               "ms": round(out["mixer"]["event_ms"], 4)}
+                               "ms": round(out["mixer"]["event_ms"], 4),
+                               "fused": {"tokens_per_s": round(out["mixer"]["fused_tokens_per_s"], 1),
+                                         "ms": round(out["mixer"]["fused_event_ms"], 4)}}
     if "varlen" in out:
         vl = out["varlen"]
         line["varlen_262144x24"] = {"tokens_per_s": round(vl["tokens_per_s"], 1),

@@ -4,7 +4,9 @@ Every source under csrc/ is compiled for gfx950 only, with packed-fp32 code
 generation disabled, and linked into gated_delta_rule_09_amd/libgdn.so.
 
 The build also compiles every source to gfx950 assembly and checks it:
-  * no register spills (the kernels are written to fit their registers);
+  * no register spills and no per-lane scratch memory at all (the kernels are
+    written to fit their registers; a register array indexed at run time
+    would also land in scratch);
   * no MFMA whose accumulator input is the result of a recent MFMA of a
     different shape (say v_mfma_f32_16x16x32_f16 feeding
     v_mfma_f32_16x16x16_f16).  With only one or two wait states between such a
@@ -102,6 +104,10 @@ def _check_asm(src: str) -> None:
     if bad:
         raise RuntimeError(f"{os.path.basename(src)}: the compiler spilled registers "
                            f"({len(bad)} spill/reload instructions, e.g. {bad[0]!r})")
+    scratch = [ln.strip() for ln in lines if re.search(r"\.private_segment_fixed_size:\s*[1-9]", ln)
+               or re.search(r"private_seg_size,\s*[1-9]", ln)]
+    if scratch:
+        raise RuntimeError(f"{os.path.basename(src)}: a kernel uses per-lane scratch memory: {scratch[0]!r}")
     chains = mixed_mfma_chains(lines)
     if chains:
         raise RuntimeError(f"{os.path.basename(src)}: MFMA accumulator fed directly by an "

@@ -470,6 +470,111 @@ gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint
                     "gdn_decode_mixer_step launch");
 }
 
+static size_t mixer_o_bytes(int32_t T_total, int32_t Hv, int32_t out_is_bf16) {
+  return out_is_bf16 ? ((static_cast<size_t>(T_total) * Hv * 128 * 4 + 255) & ~static_cast<size_t>(255)) : 0;
+}
+
+size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
+                                     int32_t d, int32_t out_is_bf16) {
+  (void)d;
+  if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0) return 0;
+  return gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv, true).total +
+         mixer_o_bytes(T_total, Hv, out_is_bf16);
+}
+
+gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
+                         const float* conv_bias, uint16_t* conv_state, const float* g,
+                         const float* beta, const uint16_t* z, int64_t z_stride,
+                         const float* norm_w, void* out, int32_t out_is_bf16,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                         int32_t Hv, int32_t d, float scale, float l2_eps, float norm_eps,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "gdn_mixer_fwd";
+  if (T_total > 0 && (!x || !conv_w || !g || !beta || !z || !norm_w || !out))
+    return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta, z, norm_w and out are required", fn);
+  if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "%s: bad sizes or Hv %% Hk != 0", fn);
+  if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "%s: d = 128 only", fn);
+  const int64_t C = static_cast<int64_t>(2 * Hk + Hv) * d;
+  const int64_t width = static_cast<int64_t>(Hv) * d;
+  if (x_stride < C || x_stride % 8 || z_stride < width || z_stride % 8)
+    return fail(GDN_ERR_SHAPE, "%s: x and z row strides too small or not multiples of 8", fn);
+  if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_bias, 16) ||
+      !aligned(conv_state, 16) || !aligned(z, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
+      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (16 bytes; g, beta, cu_seqlens: 4)", fn);
+  if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
+      !std::isfinite(norm_eps))
+    return fail(GDN_ERR_SHAPE, "%s: scale and eps must be finite, eps >= 0", fn);
+  if (!cu_seqlens) {
+    const gdn_status st = check_equal_split(n_seqs, T_total);
+    if (st) return st;
+  } else if (n_seqs == 0 && T_total != 0) {
+    return fail(GDN_ERR_SHAPE, "%s: T_total > 0 with no sequences", fn);
+  }
+  if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
+  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv, true);
+  const size_t need = ws.total + mixer_o_bytes(T_total, Hv, out_is_bf16);
+  const int64_t ssz = width * d;
+  const Range rx = range_of(x, T_total, x_stride, C, 2);
+  const Range rw = range_of(conv_w, 1, 0, C * 4, 2);
+  const Range rbias = range_of(conv_bias, 1, 0, C, 4);
+  const Range rcs = range_of(conv_state, n_seqs, 3 * C, 3 * C, 2);
+  const Range rg = range_of(g, T_total, Hv, Hv, 4);
+  const Range rb = range_of(beta, T_total, Hv, Hv, 4);
+  const Range rz = range_of(z, T_total, z_stride, width, 2);
+  const Range rn = range_of(norm_w, 1, 0, d, 4);
+  const Range rcu = range_of(cu_seqlens, 1, 0, static_cast<int64_t>(n_seqs) + 1, 4);
+  const Range ro = range_of(out, T_total, width, width, out_is_bf16 ? 2 : 4);
+  const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
+  const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
+  const Range rws = range_of(workspace, 1, 0, static_cast<int64_t>(need), 1);
+  for (const Range* in : {&rx, &rw, &rbias, &rcs, &rg, &rb, &rz, &rn, &rcu, &r0, &rT, &rws})
+    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: out overlaps another buffer", fn);
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rcu, &r0, &rT, &rws})
+    if (overlap(*in, rcs)) return fail(GDN_ERR_ALIAS, "%s: conv_state overlaps another buffer", fn);
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rcu, &rws})
+    if (overlap(*in, rT)) return fail(GDN_ERR_ALIAS, "%s: final_state overlaps an input or the workspace", fn);
+  if (overlap(r0, rT) && initial_state != final_state)
+    return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
+  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rcu, &r0})
+    if (overlap(*in, rws)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps a tensor", fn);
+  if (n_seqs > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (!aligned(workspace, 256))
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
+  if (cu_seqlens && env_validate_seqlens()) {
+    const gdn_status st = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (st) return st;
+  }
+  if (n_seqs == 0) return GDN_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // o: fp32 in out itself (normalised in place), or in the workspace for bf16 out
+  float* o = out_is_bf16 ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + ws.total)
+                         : static_cast<float*>(out);
+  gdn::ConvFront cf;
+  cf.x = x; cf.xs = x_stride; cf.w = conv_w; cf.bias = conv_bias; cf.state = conv_state;
+  cf.l2_eps = l2_eps;
+  gdn_status s = hip_status(gdn::launch_chunk_fwd(nullptr, 0, nullptr, 0, nullptr, 0,
+                                                  given_gates(g, beta), o, false, initial_state,
+                                                  final_state, nullptr, cu_seqlens, n_seqs,
+                                                  T_total, Hk, Hv, scale, workspace, st, &cf),
+                            "gdn_mixer_fwd prefill launch");
+  if (s) return s;
+  s = hip_status(gdn::launch_conv_state(x, x_stride, conv_state, cu_seqlens, n_seqs, T_total,
+                                        static_cast<int>(C), st),
+                 "gdn_mixer_fwd conv state launch");
+  if (s) return s;
+  return hip_status(gdn::launch_gated_rmsnorm(o, z, z_stride, norm_w, out, out_is_bf16 != 0, T_total,
+                                              Hv, norm_eps, st),
+                    "gdn_mixer_fwd norm launch");
+}
+
 gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
                              const float* w, void* out, int32_t out_is_bf16, int64_t rows,
                              int32_t Hv, int32_t dv, float eps, void* stream) {

@@ -139,6 +139,13 @@ struct __align__(16) PrepSmem {
   float bet[kHeadBatch][kC];
 };
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
+}
+
 struct PrepParams {
   const uint16_t* q; const uint16_t* k;
   int64_t qs, ks;
@@ -148,6 +155,12 @@ struct PrepParams {
   const uint16_t* ga; const uint16_t* gb;
   int64_t gas, gbs;
   const float* A_log; const float* dt_bias;
+  // conv front (kConv): q, k and v come from the causal conv + SiLU (+ L2 for
+  // q, k) of the pre-conv rows x [T, C]; v goes to vout [T, Hv, 128] bf16
+  const uint16_t* x; int64_t xs;
+  const uint16_t* conv_w; const float* conv_bias; const uint16_t* conv_state;
+  uint16_t* vout;
+  float l2_eps;
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* chunk_off;   // varlen chunk map (device)
   const int32_t* chunk_tab;
@@ -252,22 +265,120 @@ __device__ __forceinline__ void prep_elementwise(PrepSmem& sm, const floatx4 (&g
   }
 }
 
+// x / (1 + e^-x) with the hardware exp2 and reciprocal, as the conv front
+// of conv1d.hip computes it
+__device__ __forceinline__ float conv_silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+// Conv front of one task: chunk rows r0 .. r0 + 3 of the 8 channels ch0 ..
+// ch0 + 7 of x.  y = silu(sum_i w[c][i] x[t - 3 + i][c] + bias[c]), history
+// before the sequence start s0 from the conv state of sequence `seq` (oldest
+// first) or zero, then, with `l2`, y / sqrt(sum y^2 + eps) over the 128
+// channels that the 16 lanes of this DPP row hold.  The operations and their
+// order are those of conv1d_kernel, so every value equals the one the
+// separate conv call stores (bf16, round to nearest even).
+struct ConvRows {
+  uint4 raw[7];     // x rows r0 - 3 .. r0 + 3 (zero before s0 and at or past len)
+  uint4 wq[4];      // 4 taps of each of the 8 channels
+};
+
+__device__ __forceinline__ void conv_rows_load(const PrepParams& p, ConvRows& cr, int ch0, int t0,
+                                               int r0, int len, int s0) {
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const int rr = r0 - 3 + j;
+    const int t = t0 + rr;
+    cr.raw[j] = (rr < len && t >= s0)
+                    ? *reinterpret_cast<const uint4*>(p.x + static_cast<int64_t>(t) * p.xs + ch0)
+                    : uint4{0u, 0u, 0u, 0u};
+  }
+  const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + static_cast<int64_t>(ch0) * 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cr.wq[q] = wp[q];
+}
+
+__device__ __forceinline__ void conv_rows(const PrepParams& p, const ConvRows& cr, int ch0, int t0,
+                                          int r0, int s0, int seq, int C, bool l2,
+                                          float (&out)[4][8]) {
+  float xin[7][8];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) bf16x8_to_f32(cr.raw[k], xin[k]);
+  if (t0 + r0 - 3 < s0 && p.conv_state) {
+    // Rows before the sequence start: chunks start at s0 + 64 i and tasks at
+    // multiples of 4, so this is the sequence's first chunk, r0 = 0, and input
+    // rows 0, 1, 2 are the tokens s0 - 3, s0 - 2, s0 - 1: state taps 0, 1, 2.
+    float st[24];
+    const uint4* sp = reinterpret_cast<const uint4*>(p.conv_state + (static_cast<int64_t>(seq) * C + ch0) * 3);
+    bf16x8_to_f32(sp[0], st);
+    bf16x8_to_f32(sp[1], st + 8);
+    bf16x8_to_f32(sp[2], st + 16);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xin[k][i] = st[3 * i + k];
+  }
+  float wt[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bf16x8_to_f32(cr.wq[q], wt + 8 * q);
+  float bias[8];
+  if (p.conv_bias) {
+    const float4 b0 = *reinterpret_cast<const float4*>(p.conv_bias + ch0);
+    const float4 b1 = *reinterpret_cast<const float4*>(p.conv_bias + ch0 + 4);
+    bias[0] = b0.x; bias[1] = b0.y; bias[2] = b0.z; bias[3] = b0.w;
+    bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bias[i] = 0.f;
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = fmaf(wt[4 * i], xin[jj][i], bias[i]);
+      acc = fmaf(wt[4 * i + 1], xin[jj + 1][i], acc);
+      acc = fmaf(wt[4 * i + 2], xin[jj + 2][i], acc);
+      acc = fmaf(wt[4 * i + 3], xin[jj + 3][i], acc);
+      out[jj][i] = conv_silu(acc);
+      ss = fmaf(out[jj][i], out[jj][i], ss);
+    }
+    if (l2) {
+      ss = sum16(ss);
+      const float inv = rsqrtf(ss + p.l2_eps);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[jj][i] *= inv;
+    }
+    // round to bf16 as the stored conv output is
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const uint32_t b = pack_bf16x2(out[jj][i], out[jj][i + 1]);
+      out[jj][i] = __uint_as_float(b << 16);
+      out[jj][i + 1] = __uint_as_float(b & 0xffff0000u);
+    }
+  }
+}
+
 // kGated: the gates come from the projections (p.ga, p.gb, p.A_log, p.dt_bias).
-template <bool kGated>
+// kConv: q, k, v come from the conv front over p.x (v written to p.vout).
+template <bool kGated, bool kConv>
 __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
   const int kh = blockIdx.x;
   const int c = blockIdx.y;
-  int t0, len;
+  int t0, len, seq, s0;
   if (p.cu) {
     if (c >= p.chunk_off[p.n_seqs]) return;
+    seq = kConv ? p.chunk_tab[3 * c] : 0;
     t0 = p.chunk_tab[3 * c + 1];
     len = p.chunk_tab[3 * c + 2];
+    s0 = kConv ? p.cu[seq] : 0;
   } else {
     const int nc = (p.seq_len + kC - 1) / kC;
-    const int n = c / nc;
-    const int i = c - n * nc;
-    t0 = n * p.seq_len + i * kC;
+    seq = c / nc;
+    const int i = c - seq * nc;
+    s0 = seq * p.seq_len;
+    t0 = s0 + i * kC;
     len = min(kC, p.seq_len - i * kC);
   }
   const int tid = threadIdx.x;
@@ -321,35 +432,61 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   float gv = 0.f, bv = 0.f;
   const int nb0 = min(kHeadBatch, p.group);
   if (w < nb0) load_gb(w, gv, bv);
-  uint4 kraw[4], qraw[4];
+  const int C = (2 * p.Hk + p.Hv) * kD;        // channels of x (kConv)
+  const int r0 = (tid >> 4) * 4;                 // kConv task: rows r0 .. r0 + 3
+  const int g8 = (tid & 15) * 8;                 //   and channels g8 .. g8 + 7 of a head
+  if (kConv) {
+    // K then Q: load the task's rows, conv, L2, bf16 rounding, fp16 into LDS
+    ConvRows cr;
+    conv_rows_load(p, cr, p.Hk * kD + kh * kD + g8, t0, r0, len, s0);
+    // the first batch's decay tables while the x loads are in flight
+    if (w < nb0) decay(0, gv, bv);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int piece = tid + kThreads * j;
-    const int rr = min(piece >> 4, len - 1);
-    const int c8 = (piece & 15) * 8;
-    kraw[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
-    qraw[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
-  }
-  // the first batch's decay tables while the K, Q loads are in flight
-  if (w < nb0) decay(0, gv, bv);
-  // ---- K, Q -> LDS (fp16), rows past the chunk end zeroed ------------------
+    for (int m = 0; m < 2; ++m) {
+      if (m == 1) conv_rows_load(p, cr, kh * kD + g8, t0, r0, len, s0);
+      float y[4][8];
+      conv_rows(p, cr, m == 0 ? p.Hk * kD + kh * kD + g8 : kh * kD + g8, t0, r0, s0, seq, C, true, y);
+      _Float16* dst = m == 0 ? sm.u.kq.K : sm.u.kq.Q;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int piece = tid + kThreads * j;
-    const int r = piece >> 4;
-    const int c8 = (piece & 15) * 8;
-    float fk[8], fq[8];
-    bf16x8_to_f32(kraw[j], fk);
-    bf16x8_to_f32(qraw[j], fq);
-    half8 hk, hq;
-    const bool ok = r < len;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = r0 + jj;
+        half8 hv;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      hk[i] = static_cast<_Float16>(ok ? fk[i] : 0.f);
-      hq[i] = static_cast<_Float16>(ok ? fq[i] : 0.f);
+        for (int i = 0; i < 8; ++i) hv[i] = static_cast<_Float16>(r < len ? y[jj][i] : 0.f);
+        *reinterpret_cast<half8*>(&dst[r * kKS + g8]) = hv;
+      }
     }
-    *reinterpret_cast<half8*>(&sm.u.kq.K[r * kKS + c8]) = hk;
-    *reinterpret_cast<half8*>(&sm.u.kq.Q[r * kKS + c8]) = hq;
+  } else {
+    uint4 kraw[4], qraw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + kThreads * j;
+      const int rr = min(piece >> 4, len - 1);
+      const int c8 = (piece & 15) * 8;
+      kraw[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
+      qraw[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
+    }
+    // the first batch's decay tables while the K, Q loads are in flight
+    if (w < nb0) decay(0, gv, bv);
+    // K, Q -> LDS (fp16), rows past the chunk end zeroed
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + kThreads * j;
+      const int r = piece >> 4;
+      const int c8 = (piece & 15) * 8;
+      float fk[8], fq[8];
+      bf16x8_to_f32(kraw[j], fk);
+      bf16x8_to_f32(qraw[j], fq);
+      half8 hk, hq;
+      const bool ok = r < len;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hk[i] = static_cast<_Float16>(ok ? fk[i] : 0.f);
+        hq[i] = static_cast<_Float16>(ok ? fq[i] : 0.f);
+      }
+      *reinterpret_cast<half8*>(&sm.u.kq.K[r * kKS + c8]) = hk;
+      *reinterpret_cast<half8*>(&sm.u.kq.Q[r * kKS + c8]) = hq;
+    }
   }
   lds_barrier();
 
@@ -441,6 +578,24 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     }
     if (vb0 + kHeadBatch < p.group) lds_barrier();   // before the next batch overwrites
   }
+
+  if (kConv) {
+    // v of the key head's value heads: conv + SiLU (no L2), bf16 to vout
+    for (int vh = 0; vh < p.group; ++vh) {
+      const int h = kh * p.group + vh;
+      const int ch0 = 2 * p.Hk * kD + h * kD + g8;
+      ConvRows cv;
+      conv_rows_load(p, cv, ch0, t0, r0, len, s0);
+      float y[4][8];
+      conv_rows(p, cv, ch0, t0, r0, s0, seq, C, false, y);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (r0 + jj < len)
+          *reinterpret_cast<uint4*>(p.vout + static_cast<int64_t>(t0 + r0 + jj) * (p.Hv * kD) + h * kD + g8) =
+              uint4{pack_bf16x2(y[jj][0], y[jj][1]), pack_bf16x2(y[jj][2], y[jj][3]),
+                    pack_bf16x2(y[jj][4], y[jj][5]), pack_bf16x2(y[jj][6], y[jj][7])};
+    }
+  }
 }
 
 // ---- scan kernel ------------------------------------------------------------
@@ -470,12 +625,6 @@ struct __align__(16) ScanSmem {
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
-}
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 // gfx950 transposing LDS load (ds_read_b64_tr_b16).  Within each group of 16
@@ -933,7 +1082,7 @@ int compute_units() {
 
 }  // namespace
 
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, bool conv_v) {
   auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
   ChunkWorkspace ws;
   ws.max_chunks = static_cast<size_t>(T_total) / kC + static_cast<size_t>(n_seqs);
@@ -942,7 +1091,9 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
   ws.chunk_tab_off = ws.chunk_off_off + up(sizeof(int32_t) * (static_cast<size_t>(n_seqs) + 1));
   ws.kq_off = ws.chunk_tab_off + up(sizeof(int32_t) * 3 * ws.max_chunks);
   ws.v_off = ws.kq_off + up(ws.max_chunks * static_cast<size_t>(Hk) * kKQBytes);
-  ws.total = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
+  ws.conv_v_off = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
+  ws.total = ws.conv_v_off +
+             (conv_v ? up(static_cast<size_t>(T_total) * static_cast<size_t>(Hv) * kD * 2) : 0);
   return ws;
 }
 
@@ -951,9 +1102,9 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
                             void* o, bool o_bf16, const float* h0, float* hT,
                             const int32_t* state_slot, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, const ConvFront* conv) {
   if (n_seqs == 0) return hipSuccess;
-  const ChunkWorkspace ws = chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
+  const ChunkWorkspace ws = chunk_workspace_layout(n_seqs, T_total, Hk, Hv, conv != nullptr);
   unsigned char* base = static_cast<unsigned char*>(workspace);
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order_off);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + ws.chunk_off_off);
@@ -968,22 +1119,39 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     n_chunk_slots = n_seqs * ((seq_len + kC - 1) / kC);
   }
   if (T_total > 0 && n_chunk_slots > 0) {
-    PrepParams pp;
+    PrepParams pp{};
     pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = gates.g; pp.beta = gates.beta;
     pp.ga = gates.a; pp.gb = gates.b; pp.gas = gates.a_stride; pp.gbs = gates.b_stride;
     pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
+    if (conv) {
+      pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
+      pp.conv_state = conv->state; pp.l2_eps = conv->l2_eps;
+      pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
+    }
     pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
     pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
     pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
     pp.scale = scale;
-    if (gates.a)
-      hipLaunchKernelGGL(chunk_prep_kernel<true>, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
-    else
-      hipLaunchKernelGGL(chunk_prep_kernel<false>, dim3(Hk, n_chunk_slots), dim3(kThreads), 0, stream, pp);
+    const dim3 grid(Hk, n_chunk_slots);
+    if (conv) {
+      if (gates.a)
+        hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kThreads), 0, stream, pp);
+      else
+        hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kThreads), 0, stream, pp);
+    } else {
+      if (gates.a)
+        hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kThreads), 0, stream, pp);
+      else
+        hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kThreads), 0, stream, pp);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanParams sp;
+  if (conv) {
+    v = reinterpret_cast<const uint16_t*>(base + ws.conv_v_off);
+    vs = static_cast<int64_t>(Hv) * kD;
+  }
   sp.v = v; sp.vs = vs; sp.o = o; sp.o_bf16 = o_bf16 ? 1 : 0; sp.h0 = h0; sp.hT = hT;
   sp.slots = state_slot;
   sp.cu = cu; sp.order = cu ? order : nullptr; sp.chunk_off = chunk_off;

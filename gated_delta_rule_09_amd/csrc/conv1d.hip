@@ -142,8 +142,10 @@ __global__ __launch_bounds__(kThreads) void conv1d_kernel(
       if (pos >= s) {
         bf16x8_to_f32(raw[3 - b], hist[3 - b]);
       } else {
+        // state tap 3 - (s - pos), chosen by selects so that st stays in registers
+        const int tap = 3 - (s - pos);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hist[3 - b][i] = st[3 - (s - pos)][i];
+        for (int i = 0; i < 8; ++i) hist[3 - b][i] = tap == 0 ? st[0][i] : (tap == 1 ? st[1][i] : st[2][i]);
       }
     }
   }
@@ -259,14 +261,18 @@ hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (conv_state && n_seqs > 0) {
-    const int64_t work = static_cast<int64_t>(n_seqs) * (C / kChPerThread);
-    const dim3 grid(static_cast<unsigned>((work + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(conv_state_kernel, grid, dim3(kThreads), 0, stream, x, xs, conv_state,
-                       seqs, C);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return launch_conv_state(x, xs, conv_state, cu, n_seqs, T_total, C, stream);
+}
+
+hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state,
+                             const int32_t* cu, int n_seqs, int T_total, int C,
+                             hipStream_t stream) {
+  if (!conv_state || n_seqs <= 0) return hipSuccess;
+  Seqs seqs{cu, n_seqs, cu ? 0 : T_total / n_seqs};
+  const int64_t work = static_cast<int64_t>(n_seqs) * (C / kChPerThread);
+  const dim3 grid(static_cast<unsigned>((work + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(conv_state_kernel, grid, dim3(kThreads), 0, stream, x, xs, conv_state, seqs, C);
+  return hipGetLastError();
 }
 
 }  // namespace gdn

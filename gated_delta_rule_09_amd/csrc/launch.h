@@ -40,9 +40,10 @@ hipError_t launch_gated_rmsnorm(const float* o, const uint16_t* z, int64_t zs, c
 //   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]
 //   | K rows + Q fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]
 struct ChunkWorkspace {
-  size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, total;
+  size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, conv_v_off, total;
 };
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv);
+// conv_v: room for the conv front's v [T_total, Hv, 128] bf16 at conv_v_off.
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, bool conv_v = false);
 
 hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
                             int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream);
@@ -61,6 +62,20 @@ struct GateInputs {
   const float* dt_bias = nullptr;
 };
 
+// The conv front of the fused mixer prefill: the prep kernel computes q, k
+// (conv + SiLU + L2, bf16-rounded) and v (conv + SiLU, bf16, into the
+// workspace for the scan) from the pre-conv rows x [T, (2 Hk + Hv) 128], with
+// the same arithmetic as launch_conv1d.  The conv state is only read; the
+// caller shifts it afterwards (launch_conv_state).
+struct ConvFront {
+  const uint16_t* x = nullptr;
+  int64_t xs = 0;
+  const uint16_t* w = nullptr;
+  const float* bias = nullptr;
+  const uint16_t* state = nullptr;
+  float l2_eps = 1e-6f;
+};
+
 // state_slot != nullptr: sequence n reads h0[state_slot[n]] and writes
 // hT[state_slot[n]] (h0 == hT: a state pool updated in place).
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
@@ -68,6 +83,13 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
                             void* o, bool o_bf16, const float* h0, float* hT,
                             const int32_t* state_slot, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream,
+                            const ConvFront* conv = nullptr);
+
+// The new conv state [n_seqs, C, 3] (last three inputs of old state ++
+// sequence), after every read of the old one.
+hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state,
+                             const int32_t* cu, int n_seqs, int T_total, int C,
+                             hipStream_t stream);
 
 }  // namespace gdn

@@ -39,6 +39,10 @@ _SIGS = {
     "gdn_chunk_fwd_gated": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _f32, _vp, _sz, _vp]),
+    "gdn_mixer_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "gdn_mixer_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp,
+                             _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz,
+                             _vp]),
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
@@ -330,6 +334,82 @@ def gdn_chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: to
                                    scale, _ptr(workspace), ws_bytes, _stream())
     _check(st, "gdn_chunk_fwd_gated")
     return o, final_state
+
+
+def gdn_mixer_fwd_workspace_bytes(n_seqs: int, T_total: int, Hk: int, Hv: int, d: int = 128,
+                                  out_bf16: bool = False) -> int:
+    return int(lib().gdn_mixer_fwd_workspace_bytes(n_seqs, T_total, Hk, Hv, d, 1 if out_bf16 else 0))
+
+
+def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                  z: torch.Tensor, norm_w: torch.Tensor, *, Hk: int = 16,
+                  conv_bias: Optional[torch.Tensor] = None,
+                  conv_state: Optional[torch.Tensor] = None,
+                  initial_state: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                  scale: float = 1.0, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
+                  out_bf16: bool = False, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The whole mixer over a prefill: x [T, (2 Hk + Hv) 128] bf16 pre-conv rows,
+    conv_w [C, 4] bf16, g, beta [T, Hv] fp32, z [T, Hv, 128] bf16, norm_w [128]
+    fp32 -> (out [T, Hv, 128] fp32 or bf16, final_state or None); conv_state
+    [N, C, 3] bf16 updated in place."""
+    _need(x, "x", torch.bfloat16, 2)
+    _inner_contig(x, "x")
+    _need(conv_w, "conv_w", torch.bfloat16, 2)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(norm_w, "norm_w", torch.float32, 1)
+    for t, nm in ((conv_w, "conv_w"), (g, "g"), (beta, "beta"), (norm_w, "norm_w")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 else z
+    _need(z2, "z", torch.bfloat16, 2)
+    _inner_contig(z2, "z")
+    T = x.shape[0]
+    Hv = g.shape[1]
+    d = 128
+    if conv_bias is not None:
+        _need(conv_bias, "conv_bias", torch.float32, 1)
+    if conv_state is not None:
+        _need(conv_state, "conv_state", torch.bfloat16, 3)
+        if not conv_state.is_contiguous():
+            raise ValueError("conv_state must be contiguous")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    if out is None:
+        out = torch.empty((T, Hv, d), dtype=odt, device=x.device)
+    _need(out, "out", odt, 3)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, 4)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n_seqs, Hv, d, d), dtype=torch.float32, device=x.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, 4)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    ws_bytes = 0
+    if n_seqs > 0:
+        if workspace is None:
+            workspace = torch.empty(gdn_mixer_fwd_workspace_bytes(n_seqs, T, Hk, Hv, d, out_bf16),
+                                    dtype=torch.uint8, device=x.device)
+        ws_bytes = workspace.numel()
+    st = lib().gdn_mixer_fwd(_ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
+                             _ptr(g), _ptr(beta), _ptr(z2), z2.stride(0), _ptr(norm_w), _ptr(out),
+                             1 if out_bf16 else 0, _ptr(initial_state), _ptr(final_state),
+                             _ptr(cu_seqlens), n_seqs, T, Hk, Hv, d, scale, l2_eps, norm_eps,
+                             _ptr(workspace), ws_bytes, _stream())
+    _check(st, "gdn_mixer_fwd")
+    return out, final_state
 
 
 def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -211,6 +211,46 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_mixer_fwd -- the whole token mixer over a prefill in one call (the
+ * "Delta-rule layers" row of the model card's Architecture table: causal
+ * conv in front, the rule, gated RMS-norm after).  The causal conv (kernel 4)
+ * + SiLU + per-head L2 of q and k runs inside the chunk-prep kernel, so no
+ * conv output goes to HBM except v, which passes to the scan through the
+ * workspace; then the chunked rule, the conv-window update and the gated
+ * RMSNorm.  The result equals gdn_conv1d_fwd -> gdn_chunk_fwd ->
+ * gdn_gated_rmsnorm on the same inputs bit for bit (same operations in the
+ * same order).
+ *   x           [T_total, C] bf16 pre-conv rows [q | k | v], C = (2 Hk + Hv) d,
+ *               row stride x_stride (>= C, a multiple of 8)
+ *   conv_w      [C, 4] bf16, tap 3 = the current token; conv_bias [C] fp32 or NULL
+ *   conv_state  [n_seqs, C, 3] bf16 or NULL: the inputs before each sequence
+ *               (oldest first), replaced by each sequence's last three
+ *   g, beta     [T_total, Hv] fp32
+ *   z           [T_total, Hv, d] bf16 gate input, row stride z_stride (>= Hv d,
+ *               a multiple of 8); norm_w [d] fp32
+ *   out         [T_total, Hv, d] fp32 (out_is_bf16 == 0) or bf16, contiguous;
+ *               overlaps no other buffer
+ *   initial_state, final_state, cu_seqlens, n_seqs, scale: as gdn_chunk_fwd
+ *   l2_eps, norm_eps  the L2 and RMS epsilons (finite, >= 0)
+ *   workspace   gdn_mixer_fwd_workspace_bytes() bytes, 256-byte aligned: the
+ *               prefill workspace, v after the conv (T_total x Hv x d bf16)
+ *               and, for bf16 out, the fp32 o
+ * Every pointer 16-byte aligned except g, beta and cu_seqlens (4 bytes).
+ * d = 128.  Errors as for gdn_chunk_fwd.
+ */
+size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
+                                     int32_t d, int32_t out_is_bf16);
+
+gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
+                         const float* conv_bias, uint16_t* conv_state, const float* g,
+                         const float* beta, const uint16_t* z, int64_t z_stride,
+                         const float* norm_w, void* out, int32_t out_is_bf16,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                         int32_t Hv, int32_t d, float scale, float l2_eps, float norm_eps,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gdn_chunk_map -- the varlen chunk map used by gdn_chunk_fwd, exposed so its
  * integer results can be checked bit for bit.  From cu_seqlens it writes
  *   order      [n_seqs]      sequence ids sorted by length, longest first

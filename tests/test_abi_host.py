@@ -196,6 +196,28 @@ def test_chunk_gated_validation(lib):
     assert gated(hT=P(4)) == ALIAS                      # final state over b
 
 
+def test_mixer_fwd_validation(lib):
+    def mix(**kw):
+        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=None, g=P(2), b=P(3), z=P(4), zs=6144,
+                 nw=P(5), out=P(6), bf=0, h0=None, hT=P(7), cu=None, N=1, T=128, d=128,
+                 ws=P(9), wsb=1 << 30)
+        a.update(kw)
+        return lib.gdn_mixer_fwd(a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["g"], a["b"],
+                                 a["z"], a["zs"], a["nw"], a["out"], a["bf"], a["h0"], a["hT"],
+                                 a["cu"], a["N"], a["T"], 16, 48, a["d"], 1.0, 1e-6, 1e-6,
+                                 a["ws"], a["wsb"], None)
+    assert mix(z=None) == NULL
+    assert mix(d=64) == UNSUP
+    assert mix(xs=10000) == SHAPE
+    assert mix(bias=P(8) + 4) == SHAPE                 # bias must be 16-byte aligned
+    assert mix(out=P(0) + 4096) == ALIAS               # out over x
+    assert mix(cs=P(7) + 64) == ALIAS                  # conv state over the final state
+    assert mix(wsb=1024) == WS
+    need = lib.gdn_mixer_fwd_workspace_bytes(1, 128, 16, 48, 128, 1)
+    assert need > lib.gdn_mixer_fwd_workspace_bytes(1, 128, 16, 48, 128, 0)
+    assert mix(bf=1, wsb=need - 256) == WS
+
+
 def test_conv_validation(lib):
     def conv(**kw):
         a = dict(x=P(0), xs=10240, w=P(1), bias=None, y=P(2), ys=10240, cs=None, cu=None, N=1,

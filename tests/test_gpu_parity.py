@@ -390,6 +390,73 @@ def test_gated_rmsnorm_in_place():
     assert_close(host(od), oracle.gated_rmsnorm(o, z, w), "out")
 
 
+# ----------------------------------------------------------------- fused prefill mixer
+
+def _unfused_mixer(x, w, bias, cs, g, beta, z, nw, h0, cu, n_seqs, Hk, Hv, out_bf16, scale=1.0):
+    T = x.shape[0]
+    y = ops.gdn_conv1d_fwd(x, w, bias=bias, conv_state=cs, cu_seqlens=cu, n_seqs=n_seqs,
+                           n_l2_heads=2 * Hk).view(T, 2 * Hk + Hv, 128)
+    o, hT = ops.gdn_chunk_fwd(y[:, :Hk], y[:, Hk:2 * Hk], y[:, 2 * Hk:], g, beta,
+                              initial_state=h0, cu_seqlens=cu, n_seqs=n_seqs, scale=scale)
+    return ops.gdn_gated_rmsnorm(o, z, nw, out_bf16=out_bf16), hT
+
+
+@pytest.mark.parametrize("case", ["single", "varlen", "equal_split"])
+def test_mixer_fwd_equals_unfused(case):
+    """gdn_mixer_fwd (conv front inside the prep kernel) against the separate
+    conv, prefill and norm calls on the same inputs: out, final states and
+    the conv window identical bit for bit."""
+    if case == "single":
+        lens, Hk, Hv, out_bf16, with_cs, with_bias = [200], 16, 48, False, False, False
+    elif case == "varlen":
+        lens, Hk, Hv, out_bf16, with_cs, with_bias = [70, 0, 1, 130, 3, 64], 4, 12, True, True, True
+    else:
+        lens, Hk, Hv, out_bf16, with_cs, with_bias = [64, 64, 64], 2, 6, False, True, False
+    T, N = sum(lens), len(lens)
+    log(f"mixer_fwd vs unfused: {case} lens={lens} Hk={Hk} Hv={Hv} bf16_out={out_bf16}")
+    mi = synth.mixer_inputs(3600 + N, T, Hk=Hk, Hv=Hv, conv_state_seqs=N if with_cs else 0)
+    r = np.random.default_rng(37)
+    bias = dev_f32((0.1 * r.standard_normal(mi.x.shape[1])).astype(np.float32)) if with_bias else None
+    h0 = dev_f32((0.05 * r.standard_normal((N, Hv, 128, 128))).astype(np.float32))
+    cu = dev_i32(synth.cu_from_lengths(lens)) if case == "varlen" else None
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    g, b = dev_f32(mi.g), dev_f32(mi.beta)
+    cs1 = dev_bf16(mi.conv_state) if with_cs else None
+    cs2 = dev_bf16(mi.conv_state) if with_cs else None
+    out1, h1 = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=Hk, conv_bias=bias, conv_state=cs1,
+                                 initial_state=h0, cu_seqlens=cu, n_seqs=N, out_bf16=out_bf16)
+    out2, h2 = _unfused_mixer(x, w, bias, cs2, g, b, z, nw, h0, cu, N, Hk, Hv, out_bf16)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "out"
+    assert torch.equal(h1, h2), "final_state"
+    if with_cs:
+        assert torch.equal(cs1, cs2), "conv_state"
+
+
+def test_mixer_fwd_against_oracle():
+    """The fused mixer against the oracle's conv -> recurrence -> gated norm,
+    varlen with conv states, initial states and an empty sequence."""
+    lens, Hk, Hv = [90, 0, 5, 140], 4, 12
+    T, N = sum(lens), len(lens)
+    log(f"mixer_fwd vs oracle lens={lens}")
+    mi = synth.mixer_inputs(3650, T, Hk=Hk, Hv=Hv, conv_state_seqs=N)
+    h0 = (0.05 * np.random.default_rng(38).standard_normal((N, Hv, 128, 128))).astype(np.float32)
+    cu = synth.cu_from_lengths(lens)
+    cs = dev_bf16(mi.conv_state)
+    out, hT = ops.gdn_mixer_fwd(dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_f32(mi.g), dev_f32(mi.beta),
+                                dev_bf16(mi.z), dev_f32(mi.norm_w), Hk=Hk, conv_state=cs,
+                                initial_state=dev_f32(h0), cu_seqlens=dev_i32(cu))
+    ry, rcs = oracle.conv1d(mi.x, mi.conv_w, conv_state=mi.conv_state, cu_seqlens=cu,
+                            n_l2_heads=2 * Hk, head_dim=128, stage_bf16=True)
+    ry = ry.reshape(T, 2 * Hk + Hv, 128)
+    ro, rT = oracle.recurrence(ry[:, :Hk], ry[:, Hk:2 * Hk], ry[:, 2 * Hk:], mi.g, mi.beta, h0,
+                               cu_seqlens=cu, n_seqs=N)
+    rout = oracle.gated_rmsnorm(ro, mi.z, mi.norm_w)
+    assert_close(host(out), rout, "out")
+    assert_close(host(hT), rT, "final_state")
+    np.testing.assert_array_equal(host(cs), rcs)
+
+
 # ----------------------------------------------------------------- fused decode step
 
 def _mixer_step_case(seed, N, Hk, Hv, n_slots):
