@@ -8,6 +8,10 @@ oracle then recomputes outputs it can finish in seconds:
                                                              sampled value heads
   long prefill     B=1, T=65536, S0 ~ N(0, 0.02)             sampled value heads
   decode step      256 sequences x 1 token, state in place   every head
+  fused decode     the same batch through the whole mixer    every head
+                   step in one launch (conv window, state)
+  fused mixer      T=8192 in one gdn_mixer_fwd call          bit-identical to
+                                                             the four launches
   varlen prefill   262,144 tokens in 24 sequences            sampled (sequence,
                                                              value head) pairs
 A sampled value head h is recomputed on its own, with its key/query head
@@ -112,6 +116,41 @@ def test_full_decode_N256_every_head():
     ro, rS = oracle.decode(di.q, di.k, di.v, di.g, di.beta, di.state)
     assert_close(host(o), ro, "o")
     assert_close(host(state), rS, "state")
+
+
+def test_full_decode_mixer_step_N256_every_head():
+    N = 256
+    log(f"full fused decode step N={N}: conv window and state in place, every head")
+    mi = synth.mixer_inputs(1005, N, conv_state_seqs=N)
+    state0 = synth.decode_inputs(1006, N, with_conv=False).state
+    cs, state = dev_bf16(mi.conv_state), dev_f32(state0)
+    out = ops.gdn_decode_mixer_step(dev_bf16(mi.x), dev_bf16(mi.conv_w), cs, dev_f32(mi.g),
+                                    dev_f32(mi.beta), dev_bf16(mi.z), dev_f32(mi.norm_w), state,
+                                    Hk=HK)
+    log("  oracle conv -> decode -> norm")
+    ry, rcs = oracle.conv1d(mi.x, mi.conv_w, conv_state=mi.conv_state, n_seqs=N,
+                            n_l2_heads=2 * HK, head_dim=D, stage_bf16=True)
+    ry = ry.reshape(N, 2 * HK + HV, D)
+    ro, rS = oracle.decode(ry[:, :HK], ry[:, HK:2 * HK], ry[:, 2 * HK:], mi.g, mi.beta, state0)
+    rout = oracle.gated_rmsnorm(ro, mi.z, mi.norm_w)
+    assert_close(host(out), rout, "out")
+    assert_close(host(state), rS, "state")
+    np.testing.assert_array_equal(host(cs), rcs)
+
+
+def test_full_mixer_fwd_T8192_equals_four_launches():
+    T = 8192
+    log(f"full fused mixer T={T}: one gdn_mixer_fwd call against conv, prefill and norm")
+    mi = synth.mixer_inputs(1001, T)
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    g, b = dev_f32(mi.g), dev_f32(mi.beta)
+    out1, h1 = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=HK, n_seqs=1)
+    y = ops.gdn_conv1d_fwd(x, w, n_l2_heads=2 * HK).view(T, 2 * HK + HV, D)
+    o, h2 = ops.gdn_chunk_fwd(y[:, :HK], y[:, HK:2 * HK], y[:, 2 * HK:], g, b)
+    out2 = ops.gdn_gated_rmsnorm(o, z, nw)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "out"
+    assert torch.equal(h1, h2), "final_state"
 
 
 def test_full_varlen_262144_sampled_pairs():
