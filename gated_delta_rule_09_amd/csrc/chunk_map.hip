@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kChunk = 64;
 constexpr int kThreads = 256;
+constexpr int kLdsOffsets = 4096;   // chunk offsets kept in LDS for the table's searches
 
 // rank_i = #{ j : len_j > len_i  or  (len_j == len_i and j < i) }
 __global__ __launch_bounds__(kThreads) void order_kernel(const int32_t* __restrict__ cu,
@@ -40,6 +41,8 @@ __global__ __launch_bounds__(kThreads) void chunk_table_kernel(const int32_t* __
                                                                int32_t* __restrict__ chunk_tab) {
   __shared__ int32_t scan[kThreads];
   __shared__ int32_t carry;
+  __shared__ int32_t offs[kLdsOffsets];
+  __shared__ int32_t cus[kLdsOffsets + 1];
   const int tid = threadIdx.x;
   if (tid == 0) carry = 0;
   __syncthreads();
@@ -63,16 +66,31 @@ __global__ __launch_bounds__(kThreads) void chunk_table_kernel(const int32_t* __
   }
   if (tid == 0) chunk_off[n_seqs] = carry;
   __syncthreads();
-  // table: every thread walks the chunks of the sequences it owns
-  for (int n = tid; n < n_seqs; n += kThreads) {
-    const int s = cu[n];
-    const int len = cu[n + 1] - s;
-    int c = chunk_off[n];
-    for (int t = 0; t < len; t += kChunk, ++c) {
-      chunk_tab[3 * c + 0] = n;
-      chunk_tab[3 * c + 1] = s + t;
-      chunk_tab[3 * c + 2] = min(kChunk, len - t);
+  // table: the threads take the chunks in turn; chunk c belongs to the
+  // sequence n with chunk_off[n] <= c < chunk_off[n + 1] (binary search;
+  // empty sequences own no chunk), so a long sequence is not one thread's loop
+  // (the offsets searched in LDS when they fit)
+  const int total = carry;
+  const bool in_lds = n_seqs <= kLdsOffsets;
+  if (in_lds) {
+    for (int n = tid; n < n_seqs; n += kThreads) offs[n] = chunk_off[n];
+    for (int n = tid; n <= n_seqs; n += kThreads) cus[n] = cu[n];
+  }
+  __syncthreads();
+  const int32_t* off = in_lds ? offs : chunk_off;
+  const int32_t* cuv = in_lds ? cus : cu;
+  for (int c = tid; c < total; c += kThreads) {
+    int lo = 0, hi = n_seqs - 1;          // largest n with off[n] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= c) lo = mid; else hi = mid - 1;
     }
+    const int s = cuv[lo];
+    const int len = cuv[lo + 1] - s;
+    const int t = (c - off[lo]) * kChunk;
+    chunk_tab[3 * c + 0] = lo;
+    chunk_tab[3 * c + 1] = s + t;
+    chunk_tab[3 * c + 2] = min(kChunk, len - t);
   }
 }
 
