@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests must run in one process on the GPU machine; nothing to reorder here,
+    # GPU tests run in one process; nothing to reorder here,
     # but skip them cleanly when no GPU is visible so a CPU run never reaches HIP.
     try:
         import torch
