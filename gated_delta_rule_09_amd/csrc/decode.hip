@@ -135,6 +135,19 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
   const int slot = kSlots ? slots[n] : n;
   float* S = state + (static_cast<int64_t>(slot) * Hv + h) * (kD * kD);
 
+  // From two tokens on, every token's k and q rows of this key head are staged
+  // in LDS (loaded before the state rows, so the staging waits on them
+  // alone) and read back when the token is applied: held in registers
+  // instead, they cost 16 VGPRs per token and at four tokens leave one
+  // work-group per CU (338 against 257 us at 256 sequences x 4 tokens).
+  constexpr bool kStage = kT >= 2;
+  __shared__ uint2 kq_lds[kStage ? kT : 1][2][32];
+  if (kStage && tid < kT * 64) {
+    const int t = tid >> 6, which = (tid >> 5) & 1, idx = tid & 31;
+    const int64_t row = static_cast<int64_t>(n) * kT + t;
+    const uint16_t* src = which ? q + row * q_stride : k + row * k_stride;
+    kq_lds[t][which][idx] = *reinterpret_cast<const uint2*>(src + kh * kD + 4 * idx);
+  }
   floatx4 s[kRows][4];
 #pragma unroll
   for (int r = 0; r < kRows; ++r)
@@ -143,39 +156,51 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
       s[r][j] = __builtin_nontemporal_load(
           reinterpret_cast<const floatx4*>(S + (rg + kRowStep * r) * kD + 4 * (p + 8 * j)));
 
-  // every token's k, q (this lane's 16 channels, bf16 pairs), g, beta and the
-  // thread's two v entries, all issued before the arithmetic
-  uint2 kb[kT][4], qb[kT][4];
+  // every token's g, beta and the thread's v entries (and, without the LDS
+  // staging, k and q: this lane's 16 channels as bf16 pairs), all issued
+  // before the arithmetic
+  uint2 kb[kStage ? 1 : kT][4], qb[kStage ? 1 : kT][4];
   float gt[kT], bt[kT], vt[kT][kRows];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
     const int64_t row = static_cast<int64_t>(n) * kT + t;
-    const uint16_t* kp = k + row * k_stride + kh * kD;
-    const uint16_t* qp = q + row * q_stride + kh * kD;
+    if constexpr (!kStage) {
+      const uint16_t* kp = k + row * k_stride + kh * kD;
+      const uint16_t* qp = q + row * q_stride + kh * kD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kb[t][j] = *reinterpret_cast<const uint2*>(kp + 4 * (p + 8 * j));
-      qb[t][j] = *reinterpret_cast<const uint2*>(qp + 4 * (p + 8 * j));
+      for (int j = 0; j < 4; ++j) {
+        kb[t][j] = *reinterpret_cast<const uint2*>(kp + 4 * (p + 8 * j));
+        qb[t][j] = *reinterpret_cast<const uint2*>(qp + 4 * (p + 8 * j));
+      }
     }
     gt[t] = g[row * Hv + h];
     bt[t] = beta[row * Hv + h];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) vt[t][r] = bf16_to_f32(v[row * v_stride + h * kD + rg + kRowStep * r]);
   }
+  if (kStage) __syncthreads();
 
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
     float kk[16], qq[16];
+    const int tt = kStage ? 0 : t;
+    if constexpr (kStage) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kb[0][j] = kq_lds[t][0][p + 8 * j];
+        qb[0][j] = kq_lds[t][1][p + 8 * j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      kk[4 * j + 0] = __uint_as_float(kb[t][j].x << 16);
-      kk[4 * j + 1] = __uint_as_float(kb[t][j].x & 0xffff0000u);
-      kk[4 * j + 2] = __uint_as_float(kb[t][j].y << 16);
-      kk[4 * j + 3] = __uint_as_float(kb[t][j].y & 0xffff0000u);
-      qq[4 * j + 0] = __uint_as_float(qb[t][j].x << 16);
-      qq[4 * j + 1] = __uint_as_float(qb[t][j].x & 0xffff0000u);
-      qq[4 * j + 2] = __uint_as_float(qb[t][j].y << 16);
-      qq[4 * j + 3] = __uint_as_float(qb[t][j].y & 0xffff0000u);
+      kk[4 * j + 0] = __uint_as_float(kb[tt][j].x << 16);
+      kk[4 * j + 1] = __uint_as_float(kb[tt][j].x & 0xffff0000u);
+      kk[4 * j + 2] = __uint_as_float(kb[tt][j].y << 16);
+      kk[4 * j + 3] = __uint_as_float(kb[tt][j].y & 0xffff0000u);
+      qq[4 * j + 0] = __uint_as_float(qb[tt][j].x << 16);
+      qq[4 * j + 1] = __uint_as_float(qb[tt][j].x & 0xffff0000u);
+      qq[4 * j + 2] = __uint_as_float(qb[tt][j].y << 16);
+      qq[4 * j + 3] = __uint_as_float(qb[tt][j].y & 0xffff0000u);
     }
     float kq = 0.f;
 #pragma unroll
