@@ -417,53 +417,90 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
                     "gdn_decode_tokens launch");
 }
 
+// The gate source of a whole-mixer call: g and beta, or the projections a, b
+// with A_log and dt_bias (exactly one of the two sets).  Fills `gi` and the
+// byte ranges the aliasing checks use.
+static gdn_status mixer_gates(const char* fn, const float* g, const float* beta, const uint16_t* a,
+                              int64_t a_stride, const uint16_t* b, int64_t b_stride,
+                              const float* A_log, const float* dt_bias, int64_t rows, int32_t Hv,
+                              gdn::GateInputs& gi, Range (&r)[6]) {
+  const bool given = g || beta;
+  const bool projected = a || b || A_log || dt_bias;
+  if (rows > 0 && (given == projected || (given && !(g && beta)) ||
+                   (projected && !(a && b && A_log && dt_bias))))
+    return fail(GDN_ERR_NULL, "%s: pass either g and beta or a, b, A_log and dt_bias", fn);
+  if (projected && (a_stride < Hv || b_stride < Hv))
+    return fail(GDN_ERR_SHAPE, "%s: a and b token strides must be at least Hv", fn);
+  if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(a, 2) || !aligned(b, 2) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4))
+    return fail(GDN_ERR_SHAPE, "%s: misaligned gate pointer", fn);
+  gi.g = g; gi.beta = beta; gi.a = a; gi.a_stride = a_stride; gi.b = b; gi.b_stride = b_stride;
+  gi.A_log = A_log; gi.dt_bias = dt_bias;
+  r[0] = range_of(g, rows, Hv, Hv, 4);
+  r[1] = range_of(beta, rows, Hv, Hv, 4);
+  r[2] = range_of(a, rows, a_stride, Hv, 2);
+  r[3] = range_of(b, rows, b_stride, Hv, 2);
+  r[4] = range_of(A_log, 1, 0, Hv, 4);
+  r[5] = range_of(dt_bias, 1, 0, Hv, 4);
+  return GDN_OK;
+}
+
 gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
                                  const float* conv_bias, uint16_t* conv_state, const float* g,
-                                 const float* beta, const uint16_t* z, int64_t z_stride,
+                                 const float* beta, const uint16_t* a, int64_t a_stride,
+                                 const uint16_t* b, int64_t b_stride, const float* A_log,
+                                 const float* dt_bias, const uint16_t* z, int64_t z_stride,
                                  const float* norm_w, float* state, const int32_t* state_slot,
                                  int32_t n_slots, void* out, int32_t out_is_bf16, int32_t n_seqs,
                                  int32_t Hk, int32_t Hv, int32_t d, float scale, float l2_eps,
                                  float norm_eps, void* stream) {
-  if (n_seqs > 0 && (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out))
-    return fail(GDN_ERR_NULL, "gdn_decode_mixer_step: all pointers but conv_bias and state_slot are required");
+  const char* fn = "gdn_decode_mixer_step";
+  if (n_seqs > 0 && (!x || !conv_w || !conv_state || !z || !norm_w || !state || !out))
+    return fail(GDN_ERR_NULL, "%s: x, conv_w, conv_state, z, norm_w, state and out are required", fn);
   if (n_seqs < 0 || n_slots < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: bad sizes or Hv %% Hk != 0");
-  if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_mixer_step: d = 128 only");
-  if (Hv / Hk > 4) return fail(GDN_ERR_UNSUPPORTED, "gdn_decode_mixer_step: Hv / Hk must be at most 4");
+    return fail(GDN_ERR_SHAPE, "%s: bad sizes or Hv %% Hk != 0", fn);
+  gdn::GateInputs gi;
+  Range rgates[6];
+  {
+    const gdn_status st = mixer_gates(fn, g, beta, a, a_stride, b, b_stride, A_log, dt_bias, n_seqs, Hv,
+                                      gi, rgates);
+    if (st) return st;
+  }
+  if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "%s: d = 128 only", fn);
+  if (Hv / Hk > 4) return fail(GDN_ERR_UNSUPPORTED, "%s: Hv / Hk must be at most 4", fn);
   if (!state_slot && n_slots < n_seqs)
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: n_slots < n_seqs without a slot map");
+    return fail(GDN_ERR_SHAPE, "%s: n_slots < n_seqs without a slot map", fn);
   const int64_t C = static_cast<int64_t>(2 * Hk + Hv) * d;
   if (x_stride < C || z_stride < static_cast<int64_t>(Hv) * d)
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: row strides too small");
+    return fail(GDN_ERR_SHAPE, "%s: row strides too small", fn);
   if (!aligned(state, 16) || !aligned(x, 2) || !aligned(conv_w, 2) || !aligned(conv_state, 2) ||
-      !aligned(z, 2) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(norm_w, 4) ||
-      !aligned(conv_bias, 4) || !aligned(state_slot, 4) || !aligned(out, out_is_bf16 ? 2 : 4))
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: misaligned pointer (state needs 16 bytes)");
+      !aligned(z, 2) || !aligned(norm_w, 4) || !aligned(conv_bias, 4) || !aligned(state_slot, 4) ||
+      !aligned(out, out_is_bf16 ? 2 : 4))
+    return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (state needs 16 bytes)", fn);
   if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
       !std::isfinite(norm_eps))
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: scale and eps must be finite, eps >= 0");
+    return fail(GDN_ERR_SHAPE, "%s: scale and eps must be finite, eps >= 0", fn);
   if (static_cast<int64_t>(n_seqs) * Hk > 0x7fffffffLL)
-    return fail(GDN_ERR_SHAPE, "gdn_decode_mixer_step: too many (sequence, head) pairs");
+    return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
   const int64_t ssz = static_cast<int64_t>(Hv) * d * d;
   const Range rs = range_of(state, n_slots, ssz, ssz, 4);
   const Range rc = range_of(conv_state, n_slots, C * 3, C * 3, 2);
   const Range rx = range_of(x, n_seqs, x_stride, C, 2);
   const Range rw = range_of(conv_w, 1, 0, C * 4, 2);
   const Range rbias = range_of(conv_bias, 1, 0, C, 4);
-  const Range rg = range_of(g, n_seqs, Hv, Hv, 4);
-  const Range rb = range_of(beta, n_seqs, Hv, Hv, 4);
   const Range rz = range_of(z, n_seqs, z_stride, static_cast<int64_t>(Hv) * d, 2);
   const Range rn = range_of(norm_w, 1, 0, d, 4);
   const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
   const Range ro = range_of(out, n_seqs, static_cast<int64_t>(Hv) * d, static_cast<int64_t>(Hv) * d,
                             out_is_bf16 ? 2 : 4);
-  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl, &rs, &rc})
-    if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: out overlaps another tensor");
-  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl, &rc})
-    if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: state overlaps another tensor");
-  for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rsl})
-    if (overlap(*in, rc)) return fail(GDN_ERR_ALIAS, "gdn_decode_mixer_step: conv_state overlaps an input");
-  return hip_status(gdn::launch_decode_mixer(x, x_stride, conv_w, conv_bias, conv_state, g, beta, z,
+  const Range* inputs[] = {&rx, &rw, &rbias, &rz, &rn, &rsl, &rgates[0], &rgates[1], &rgates[2],
+                           &rgates[3], &rgates[4], &rgates[5]};
+  for (const Range* in : inputs)
+    if (overlap(*in, ro) || overlap(*in, rs) || overlap(*in, rc))
+      return fail(GDN_ERR_ALIAS, "%s: out, state or conv_state overlaps an input", fn);
+  if (overlap(ro, rs) || overlap(ro, rc) || overlap(rs, rc))
+    return fail(GDN_ERR_ALIAS, "%s: out, state and conv_state overlap", fn);
+  return hip_status(gdn::launch_decode_mixer(x, x_stride, conv_w, conv_bias, conv_state, gi, z,
                                              z_stride, norm_w, state, state_slot, out, out_is_bf16 != 0,
                                              n_seqs, Hk, Hv, scale, l2_eps, norm_eps,
                                              static_cast<hipStream_t>(stream)),
@@ -484,17 +521,26 @@ size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk
 
 gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
                          const float* conv_bias, uint16_t* conv_state, const float* g,
-                         const float* beta, const uint16_t* z, int64_t z_stride,
+                         const float* beta, const uint16_t* a, int64_t a_stride, const uint16_t* b,
+                         int64_t b_stride, const float* A_log, const float* dt_bias,
+                         const uint16_t* z, int64_t z_stride,
                          const float* norm_w, void* out, int32_t out_is_bf16,
                          const float* initial_state, float* final_state,
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t d, float scale, float l2_eps, float norm_eps,
                          void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_mixer_fwd";
-  if (T_total > 0 && (!x || !conv_w || !g || !beta || !z || !norm_w || !out))
-    return fail(GDN_ERR_NULL, "%s: x, conv_w, g, beta, z, norm_w and out are required", fn);
+  if (T_total > 0 && (!x || !conv_w || !z || !norm_w || !out))
+    return fail(GDN_ERR_NULL, "%s: x, conv_w, z, norm_w and out are required", fn);
   if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
     return fail(GDN_ERR_SHAPE, "%s: bad sizes or Hv %% Hk != 0", fn);
+  gdn::GateInputs gi;
+  Range rgates[6];
+  {
+    const gdn_status st = mixer_gates(fn, g, beta, a, a_stride, b, b_stride, A_log, dt_bias, T_total,
+                                      Hv, gi, rgates);
+    if (st) return st;
+  }
   if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "%s: d = 128 only", fn);
   const int64_t C = static_cast<int64_t>(2 * Hk + Hv) * d;
   const int64_t width = static_cast<int64_t>(Hv) * d;
@@ -502,9 +548,8 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
     return fail(GDN_ERR_SHAPE, "%s: x and z row strides too small or not multiples of 8", fn);
   if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_bias, 16) ||
       !aligned(conv_state, 16) || !aligned(z, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
-      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(g, 4) ||
-      !aligned(beta, 4) || !aligned(cu_seqlens, 4))
-    return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (16 bytes; g, beta, cu_seqlens: 4)", fn);
+      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (16 bytes; cu_seqlens: 4)", fn);
   if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
       !std::isfinite(norm_eps))
     return fail(GDN_ERR_SHAPE, "%s: scale and eps must be finite, eps >= 0", fn);
@@ -523,8 +568,8 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   const Range rw = range_of(conv_w, 1, 0, C * 4, 2);
   const Range rbias = range_of(conv_bias, 1, 0, C, 4);
   const Range rcs = range_of(conv_state, n_seqs, 3 * C, 3 * C, 2);
-  const Range rg = range_of(g, T_total, Hv, Hv, 4);
-  const Range rb = range_of(beta, T_total, Hv, Hv, 4);
+  const Range& rg = rgates[0];
+  const Range& rb = rgates[1];
   const Range rz = range_of(z, T_total, z_stride, width, 2);
   const Range rn = range_of(norm_w, 1, 0, d, 4);
   const Range rcu = range_of(cu_seqlens, 1, 0, static_cast<int64_t>(n_seqs) + 1, 4);
@@ -534,6 +579,10 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   const Range rws = range_of(workspace, 1, 0, static_cast<int64_t>(need), 1);
   for (const Range* in : {&rx, &rw, &rbias, &rcs, &rg, &rb, &rz, &rn, &rcu, &r0, &rT, &rws})
     if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: out overlaps another buffer", fn);
+  for (int i = 2; i < 6; ++i)
+    if (overlap(rgates[i], ro) || overlap(rgates[i], rcs) || overlap(rgates[i], rT) ||
+        overlap(rgates[i], rws))
+      return fail(GDN_ERR_ALIAS, "%s: a gate input overlaps an output or the workspace", fn);
   for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rcu, &r0, &rT, &rws})
     if (overlap(*in, rcs)) return fail(GDN_ERR_ALIAS, "%s: conv_state overlaps another buffer", fn);
   for (const Range* in : {&rx, &rw, &rbias, &rg, &rb, &rz, &rn, &rcu, &rws})
@@ -561,7 +610,7 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   cf.x = x; cf.xs = x_stride; cf.w = conv_w; cf.bias = conv_bias; cf.state = conv_state;
   cf.l2_eps = l2_eps;
   gdn_status s = hip_status(gdn::launch_chunk_fwd(nullptr, 0, nullptr, 0, nullptr, 0,
-                                                  given_gates(g, beta), o, false, initial_state,
+                                                  gi, o, false, initial_state,
                                                   final_state, nullptr, cu_seqlens, n_seqs,
                                                   T_total, Hk, Hv, scale, workspace, st, &cf),
                             "gdn_mixer_fwd prefill launch");

@@ -46,6 +46,10 @@ struct MixerParams {
   const uint16_t* conv_w; const float* conv_bias;
   uint16_t* conv_state;
   const float* g; const float* beta;
+  // gates from the per-head projections instead (ga != nullptr):
+  // g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)
+  const uint16_t* ga; const uint16_t* gb; int64_t gas, gbs;
+  const float* A_log; const float* dt_bias;
   const uint16_t* z; int64_t zs;
   const float* norm_w;
   float* state; const int32_t* slots;
@@ -74,7 +78,8 @@ __device__ __forceinline__ int channel(int c, int kh, int Hk, int G) {
                     : 2 * Hk * kD + kh * G * kD + (c - 2 * kD);
 }
 
-template <int G>
+// kGated: the gates come from the projections (p.ga, p.gb, p.A_log, p.dt_bias).
+template <int G, bool kGated>
 __global__ __launch_bounds__(kThreads) void decode_mixer_kernel(MixerParams p) {
   __shared__ float qk[2][kD];
   __shared__ float vv[G][kD];
@@ -173,8 +178,17 @@ __global__ __launch_bounds__(kThreads) void decode_mixer_kernel(MixerParams p) {
   for (int j = 0; j < G; ++j) {
     const int h = kh * G + j;
     float* S = p.state + (static_cast<int64_t>(slot) * p.Hv + h) * (kD * kD);
-    const float a = expf(p.g[static_cast<int64_t>(n) * p.Hv + h]);
-    const float b = p.beta[static_cast<int64_t>(n) * p.Hv + h];
+    float a, b;
+    if (kGated) {
+      // softplus(x) = max(x, 0) + log1p(e^-|x|), as the prefill's gate preparation
+      const float x = bf16_to_f32(p.ga[static_cast<int64_t>(n) * p.gas + h]) + p.dt_bias[h];
+      const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+      a = expf(-expf(p.A_log[h]) * sp);
+      b = 1.f / (1.f + expf(-bf16_to_f32(p.gb[static_cast<int64_t>(n) * p.gbs + h])));
+    } else {
+      a = expf(p.g[static_cast<int64_t>(n) * p.Hv + h]);
+      b = p.beta[static_cast<int64_t>(n) * p.Hv + h];
+    }
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       const int row = rg + kRowStep * r;
@@ -225,23 +239,30 @@ __global__ __launch_bounds__(kThreads) void decode_mixer_kernel(MixerParams p) {
 }  // namespace
 
 hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* conv_w,
-                               const float* conv_bias, uint16_t* conv_state, const float* g,
-                               const float* beta, const uint16_t* z, int64_t zs,
+                               const float* conv_bias, uint16_t* conv_state,
+                               const GateInputs& gates, const uint16_t* z, int64_t zs,
                                const float* norm_w, float* state, const int32_t* state_slot,
                                void* out, bool out_bf16, int n_seqs, int Hk, int Hv, float scale,
                                float l2_eps, float norm_eps, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
   MixerParams mp;
   mp.x = x; mp.xs = xs; mp.conv_w = conv_w; mp.conv_bias = conv_bias; mp.conv_state = conv_state;
-  mp.g = g; mp.beta = beta; mp.z = z; mp.zs = zs; mp.norm_w = norm_w;
+  mp.g = gates.g; mp.beta = gates.beta; mp.ga = gates.a; mp.gb = gates.b;
+  mp.gas = gates.a_stride; mp.gbs = gates.b_stride; mp.A_log = gates.A_log; mp.dt_bias = gates.dt_bias;
+  mp.z = z; mp.zs = zs; mp.norm_w = norm_w;
   mp.state = state; mp.slots = state_slot; mp.out = out; mp.out_bf16 = out_bf16 ? 1 : 0;
   mp.Hk = Hk; mp.Hv = Hv; mp.scale = scale; mp.l2_eps = l2_eps; mp.norm_eps = norm_eps;
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hk));
-  switch (Hv / Hk) {
-    case 1: hipLaunchKernelGGL(decode_mixer_kernel<1>, grid, dim3(kThreads), 0, stream, mp); break;
-    case 2: hipLaunchKernelGGL(decode_mixer_kernel<2>, grid, dim3(kThreads), 0, stream, mp); break;
-    case 3: hipLaunchKernelGGL(decode_mixer_kernel<3>, grid, dim3(kThreads), 0, stream, mp); break;
-    case 4: hipLaunchKernelGGL(decode_mixer_kernel<4>, grid, dim3(kThreads), 0, stream, mp); break;
+  const bool gated = gates.a != nullptr;
+  switch ((Hv / Hk) * 2 + (gated ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL((decode_mixer_kernel<1, false>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 3: hipLaunchKernelGGL((decode_mixer_kernel<1, true>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 4: hipLaunchKernelGGL((decode_mixer_kernel<2, false>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 5: hipLaunchKernelGGL((decode_mixer_kernel<2, true>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 6: hipLaunchKernelGGL((decode_mixer_kernel<3, false>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 7: hipLaunchKernelGGL((decode_mixer_kernel<3, true>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 8: hipLaunchKernelGGL((decode_mixer_kernel<4, false>), grid, dim3(kThreads), 0, stream, mp); break;
+    case 9: hipLaunchKernelGGL((decode_mixer_kernel<4, true>), grid, dim3(kThreads), 0, stream, mp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -20,13 +20,6 @@ hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint1
                                 const int32_t* state_slot, float* o, int n_seqs, int n_tokens,
                                 int Hk, int Hv, float scale, hipStream_t stream);
 
-hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* conv_w,
-                               const float* conv_bias, uint16_t* conv_state, const float* g,
-                               const float* beta, const uint16_t* z, int64_t zs,
-                               const float* norm_w, float* state, const int32_t* state_slot,
-                               void* out, bool out_bf16, int n_seqs, int Hk, int Hv, float scale,
-                               float l2_eps, float norm_eps, hipStream_t stream);
-
 hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const float* bias,
                          uint16_t* y, int64_t ys, uint16_t* conv_state, const int32_t* cu,
                          int n_seqs, int T_total, int C, int n_l2_channels, float l2_eps,
@@ -61,6 +54,15 @@ struct GateInputs {
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
 };
+
+// One decode step of the whole mixer (decode_mixer.hip), gates given or from
+// the projections.
+hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* conv_w,
+                               const float* conv_bias, uint16_t* conv_state,
+                               const GateInputs& gates, const uint16_t* z, int64_t zs,
+                               const float* norm_w, float* state, const int32_t* state_slot,
+                               void* out, bool out_bf16, int n_seqs, int Hk, int Hv, float scale,
+                               float l2_eps, float norm_eps, hipStream_t stream);
 
 // The conv front of the fused mixer prefill: the prep kernel computes q, k
 // (conv + SiLU + L2, bf16-rounded) and v (conv + SiLU, bf16, into the

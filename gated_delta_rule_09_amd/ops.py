@@ -40,17 +40,17 @@ _SIGS = {
                                    _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _f32, _vp, _sz, _vp]),
     "gdn_mixer_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "gdn_mixer_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp,
-                             _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz,
-                             _vp]),
+    "gdn_mixer_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
+                             _vp, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                             _i32, _f32, _f32, _f32, _vp, _sz, _vp]),
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "gdn_decode_tokens": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                  _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
-    "gdn_decode_mixer_step": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
-                                     _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
-                                     _vp]),
+    "gdn_decode_mixer_step": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                     _vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                     _i32, _i32, _f32, _f32, _f32, _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
 }
@@ -341,8 +341,10 @@ def gdn_mixer_fwd_workspace_bytes(n_seqs: int, T_total: int, Hk: int, Hv: int, d
     return int(lib().gdn_mixer_fwd_workspace_bytes(n_seqs, T_total, Hk, Hv, d, 1 if out_bf16 else 0))
 
 
-def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-                  z: torch.Tensor, norm_w: torch.Tensor, *, Hk: int = 16,
+def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tensor],
+                  beta: Optional[torch.Tensor], z: torch.Tensor, norm_w: torch.Tensor, *,
+                  Hk: int = 16, a: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
+                  A_log: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
                   conv_bias: Optional[torch.Tensor] = None,
                   conv_state: Optional[torch.Tensor] = None,
                   initial_state: Optional[torch.Tensor] = None,
@@ -355,21 +357,21 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: torch.Tensor, beta: 
     """The whole mixer over a prefill: x [T, (2 Hk + Hv) 128] bf16 pre-conv rows,
     conv_w [C, 4] bf16, g, beta [T, Hv] fp32, z [T, Hv, 128] bf16, norm_w [128]
     fp32 -> (out [T, Hv, 128] fp32 or bf16, final_state or None); conv_state
-    [N, C, 3] bf16 updated in place."""
+    [N, C, 3] bf16 updated in place.  The gates are g, beta [T, Hv] fp32, or
+    (g = beta = None) formed from the projections a, b [T, Hv] bf16 with A_log,
+    dt_bias [Hv] fp32."""
     _need(x, "x", torch.bfloat16, 2)
     _inner_contig(x, "x")
     _need(conv_w, "conv_w", torch.bfloat16, 2)
-    _need(g, "g", torch.float32, 2)
-    _need(beta, "beta", torch.float32, 2)
+    gate_args, Hv = _gate_args(g, beta, a, b, A_log, dt_bias)
     _need(norm_w, "norm_w", torch.float32, 1)
-    for t, nm in ((conv_w, "conv_w"), (g, "g"), (beta, "beta"), (norm_w, "norm_w")):
+    for t, nm in ((conv_w, "conv_w"), (norm_w, "norm_w")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
     z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 else z
     _need(z2, "z", torch.bfloat16, 2)
     _inner_contig(z2, "z")
     T = x.shape[0]
-    Hv = g.shape[1]
     d = 128
     if conv_bias is not None:
         _need(conv_bias, "conv_bias", torch.float32, 1)
@@ -404,7 +406,7 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: torch.Tensor, beta: 
                                     dtype=torch.uint8, device=x.device)
         ws_bytes = workspace.numel()
     st = lib().gdn_mixer_fwd(_ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
-                             _ptr(g), _ptr(beta), _ptr(z2), z2.stride(0), _ptr(norm_w), _ptr(out),
+                             *gate_args, _ptr(z2), z2.stride(0), _ptr(norm_w), _ptr(out),
                              1 if out_bf16 else 0, _ptr(initial_state), _ptr(final_state),
                              _ptr(cu_seqlens), n_seqs, T, Hk, Hv, d, scale, l2_eps, norm_eps,
                              _ptr(workspace), ws_bytes, _stream())
@@ -467,9 +469,32 @@ def gdn_decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torc
     return o
 
 
+def _gate_args(g, beta, a, b, A_log, dt_bias):
+    """(g, beta) given, or the projections (a, b bf16 [rows, Hv], A_log, dt_bias
+    fp32 [Hv]): the C arguments g, beta, a, a_stride, b, b_stride, A_log, dt_bias."""
+    if g is not None or beta is not None:
+        if a is not None or b is not None or A_log is not None or dt_bias is not None:
+            raise ValueError("pass either g and beta or a, b, A_log and dt_bias")
+        _need(g, "g", torch.float32, 2)
+        _need(beta, "beta", torch.float32, 2)
+        if not (g.is_contiguous() and beta.is_contiguous()):
+            raise ValueError("g and beta must be contiguous")
+        return (_ptr(g), _ptr(beta), None, 0, None, 0, None, None), g.shape[1]
+    for t, nm in ((a, "a"), (b, "b")):
+        _need(t, nm, torch.bfloat16, 2)
+        _inner_contig(t, nm)
+    for t, nm in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, nm, torch.float32, 1)
+    return (None, None, _ptr(a), a.stride(0), _ptr(b), b.stride(0), _ptr(A_log),
+            _ptr(dt_bias)), a.shape[1]
+
+
 def gdn_decode_mixer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
-                          g: torch.Tensor, beta: torch.Tensor, z: torch.Tensor,
+                          g: Optional[torch.Tensor], beta: Optional[torch.Tensor], z: torch.Tensor,
                           norm_w: torch.Tensor, state: torch.Tensor, *, Hk: int = 16,
+                          a: Optional[torch.Tensor] = None, b: Optional[torch.Tensor] = None,
+                          A_log: Optional[torch.Tensor] = None,
+                          dt_bias: Optional[torch.Tensor] = None,
                           conv_bias: Optional[torch.Tensor] = None,
                           state_slot: Optional[torch.Tensor] = None, scale: float = 1.0,
                           l2_eps: float = 1e-6, norm_eps: float = 1e-6, out_bf16: bool = False,
@@ -477,15 +502,16 @@ def gdn_decode_mixer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: tor
     """One decode step of the whole mixer (conv + SiLU + L2, the rule, the gated
     RMSNorm) for the new tokens x [N, C] bf16; conv_state [n_slots, C, 3] bf16 and
     state [n_slots, Hv, 128, 128] fp32 updated in place; z [N, Hv, 128] bf16.
-    Returns out [N, Hv, 128] (fp32, or bf16 with out_bf16)."""
+    Returns out [N, Hv, 128] (fp32, or bf16 with out_bf16).  The gates are g,
+    beta [N, Hv] fp32, or (g = beta = None) formed from the projections a, b
+    [N, Hv] bf16 with A_log, dt_bias [Hv] fp32."""
     _need(x, "x", torch.bfloat16, 2)
     _need(conv_w, "conv_w", torch.bfloat16, 2)
     _need(conv_state, "conv_state", torch.bfloat16, 3)
-    _need(g, "g", torch.float32, 2)
-    _need(beta, "beta", torch.float32, 2)
+    gate_args, _ = _gate_args(g, beta, a, b, A_log, dt_bias)
     _need(norm_w, "norm_w", torch.float32, 1)
     _need(state, "state", torch.float32, 4)
-    for t, nm in ((conv_w, "conv_w"), (conv_state, "conv_state"), (g, "g"), (beta, "beta"),
+    for t, nm in ((conv_w, "conv_w"), (conv_state, "conv_state"),
                   (norm_w, "norm_w"), (state, "state")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
@@ -506,7 +532,7 @@ def gdn_decode_mixer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: tor
         out = torch.empty((N, Hv, d), dtype=odt, device=x.device)
     _need(out, "out", odt, 3)
     st = lib().gdn_decode_mixer_step(_ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_bias),
-                                     _ptr(conv_state), _ptr(g), _ptr(beta), _ptr(z2), z2.stride(0),
+                                     _ptr(conv_state), *gate_args, _ptr(z2), z2.stride(0),
                                      _ptr(norm_w), _ptr(state), _ptr(state_slot), state.shape[0],
                                      _ptr(out), 1 if out_bf16 else 0, N, Hk, Hv, d, scale, l2_eps,
                                      norm_eps, _stream())

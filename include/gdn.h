@@ -60,7 +60,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -225,7 +225,10 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  *   conv_w      [C, 4] bf16, tap 3 = the current token; conv_bias [C] fp32 or NULL
  *   conv_state  [n_seqs, C, 3] bf16 or NULL: the inputs before each sequence
  *               (oldest first), replaced by each sequence's last three
- *   g, beta     [T_total, Hv] fp32
+ *   g, beta     [T_total, Hv] fp32, or both NULL and the gates formed from
+ *               the projections as in gdn_chunk_fwd_gated: a, b [T_total, Hv]
+ *               bf16 (token strides a_stride, b_stride >= Hv), A_log, dt_bias
+ *               [Hv] fp32 (pass NULL for these when g, beta are given)
  *   z           [T_total, Hv, d] bf16 gate input, row stride z_stride (>= Hv d,
  *               a multiple of 8); norm_w [d] fp32
  *   out         [T_total, Hv, d] fp32 (out_is_bf16 == 0) or bf16, contiguous;
@@ -235,7 +238,8 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  *   workspace   gdn_mixer_fwd_workspace_bytes() bytes, 256-byte aligned: the
  *               prefill workspace, v after the conv (T_total x Hv x d bf16)
  *               and, for bf16 out, the fp32 o
- * Every pointer 16-byte aligned except g, beta and cu_seqlens (4 bytes).
+ * Every pointer 16-byte aligned except g, beta, A_log, dt_bias and
+ * cu_seqlens (4 bytes) and a, b (2 bytes).
  * d = 128.  Errors as for gdn_chunk_fwd.
  */
 size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk, int32_t Hv,
@@ -243,7 +247,9 @@ size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk
 
 gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
                          const float* conv_bias, uint16_t* conv_state, const float* g,
-                         const float* beta, const uint16_t* z, int64_t z_stride,
+                         const float* beta, const uint16_t* a, int64_t a_stride, const uint16_t* b,
+                         int64_t b_stride, const float* A_log, const float* dt_bias,
+                         const uint16_t* z, int64_t z_stride,
                          const float* norm_w, void* out, int32_t out_is_bf16,
                          const float* initial_state, float* final_state,
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
@@ -329,7 +335,10 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
  *               channels [q heads | k heads | v heads]
  *   conv_w      [C, 4] bf16; conv_bias [C] fp32 or NULL
  *   conv_state  [n_slots, C, 3] bf16, oldest first, updated in place
- *   g, beta     [n_seqs, Hv] fp32, contiguous
+ *   g, beta     [n_seqs, Hv] fp32, contiguous; or both NULL and the gates
+ *               formed from the projections a, b [n_seqs, Hv] bf16 (token
+ *               strides a_stride, b_stride >= Hv) and A_log, dt_bias [Hv] fp32
+ *               as in gdn_chunk_fwd_gated (NULL when g, beta are given)
  *   z           [n_seqs, Hv * d] bf16, row stride z_stride >= Hv * d
  *   norm_w      [d] fp32
  *   state       [n_slots, Hv, d, d] fp32, updated in place
@@ -342,7 +351,9 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
  */
 gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint16_t* conv_w,
                                  const float* conv_bias, uint16_t* conv_state, const float* g,
-                                 const float* beta, const uint16_t* z, int64_t z_stride,
+                                 const float* beta, const uint16_t* a, int64_t a_stride,
+                                 const uint16_t* b, int64_t b_stride, const float* A_log,
+                                 const float* dt_bias, const uint16_t* z, int64_t z_stride,
                                  const float* norm_w, float* state, const int32_t* state_slot,
                                  int32_t n_slots, void* out, int32_t out_is_bf16, int32_t n_seqs,
                                  int32_t Hk, int32_t Hv, int32_t d, float scale, float l2_eps,

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -135,12 +135,13 @@ def test_decode_tokens_validation(lib):
 
 def test_decode_mixer_step_validation(lib):
     def mix(**kw):
-        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=P(2), g=P(3), b=P(4), z=P(5), zs=6144,
-                 nw=P(6), st=P(7), slot=None, nslots=4, out=P(8), bf=0, N=4, Hk=16, Hv=48, d=128,
-                 l2=1e-6, ne=1e-6)
+        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=P(2), g=P(3), b=P(4), pa=None, pas=48,
+                 pb=None, pbs=48, A=None, dt=None, z=P(5), zs=6144, nw=P(6), st=P(7), slot=None,
+                 nslots=4, out=P(8), bf=0, N=4, Hk=16, Hv=48, d=128, l2=1e-6, ne=1e-6)
         a.update(kw)
         return lib.gdn_decode_mixer_step(a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["g"],
-                                         a["b"], a["z"], a["zs"], a["nw"], a["st"], a["slot"],
+                                         a["b"], a["pa"], a["pas"], a["pb"], a["pbs"], a["A"],
+                                         a["dt"], a["z"], a["zs"], a["nw"], a["st"], a["slot"],
                                          a["nslots"], a["out"], a["bf"], a["N"], a["Hk"], a["Hv"],
                                          a["d"], 1.0, a["l2"], a["ne"], None)
     assert mix(z=None) == NULL
@@ -156,6 +157,11 @@ def test_decode_mixer_step_validation(lib):
     assert mix(out=P(7) + 64) == ALIAS                 # out inside the state
     assert mix(cs=P(0) + 16) == ALIAS                  # conv state over x
     assert mix(st=P(2) + 256) == ALIAS                 # state over the conv state
+    proj = dict(g=None, b=None, pa=P(3), pb=P(3) + 4096, A=P(4), dt=P(4) + 256)
+    assert mix(**dict(proj, g=P(9))) == NULL           # both gate sources
+    assert mix(**dict(proj, dt=None)) == NULL          # incomplete projections
+    assert mix(**dict(proj, pas=40)) == SHAPE          # a's stride below Hv
+    assert mix(**dict(proj, pa=P(8))) == ALIAS         # a inside out
 
 
 def test_chunk_pooled_validation(lib):
@@ -198,11 +204,12 @@ def test_chunk_gated_validation(lib):
 
 def test_mixer_fwd_validation(lib):
     def mix(**kw):
-        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=None, g=P(2), b=P(3), z=P(4), zs=6144,
-                 nw=P(5), out=P(6), bf=0, h0=None, hT=P(7), cu=None, N=1, T=128, d=128,
-                 ws=P(9), wsb=1 << 30)
+        a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=None, g=P(2), b=P(3), pa=None, pas=48,
+                 pb=None, pbs=48, A=None, dt=None, z=P(4), zs=6144, nw=P(5), out=P(6), bf=0,
+                 h0=None, hT=P(7), cu=None, N=1, T=128, d=128, ws=P(9), wsb=1 << 30)
         a.update(kw)
         return lib.gdn_mixer_fwd(a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["g"], a["b"],
+                                 a["pa"], a["pas"], a["pb"], a["pbs"], a["A"], a["dt"],
                                  a["z"], a["zs"], a["nw"], a["out"], a["bf"], a["h0"], a["hT"],
                                  a["cu"], a["N"], a["T"], 16, 48, a["d"], 1.0, 1e-6, 1e-6,
                                  a["ws"], a["wsb"], None)
@@ -216,6 +223,11 @@ def test_mixer_fwd_validation(lib):
     need = lib.gdn_mixer_fwd_workspace_bytes(1, 128, 16, 48, 128, 1)
     assert need > lib.gdn_mixer_fwd_workspace_bytes(1, 128, 16, 48, 128, 0)
     assert mix(bf=1, wsb=need - 256) == WS
+    proj = dict(g=None, b=None, pa=P(2), pb=P(2) + 65536, A=P(3), dt=P(3) + 256)
+    assert mix(**dict(proj, b=P(8))) == NULL           # both gate sources
+    assert mix(**dict(proj, A=None)) == NULL           # incomplete projections
+    assert mix(**dict(proj, pbs=47)) == SHAPE          # b's stride below Hv
+    assert mix(**dict(proj, pa=P(7))) == ALIAS         # a inside the final state
 
 
 def test_conv_validation(lib):

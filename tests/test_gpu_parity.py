@@ -433,6 +433,38 @@ def test_mixer_fwd_equals_unfused(case):
         assert torch.equal(cs1, cs2), "conv_state"
 
 
+def test_mixer_fwd_gates_from_projections():
+    """gdn_mixer_fwd with the gates formed from bf16 projections: bit-identical
+    to conv -> gdn_chunk_fwd_gated -> norm, and against the oracle's gate
+    preparation followed by conv -> recurrence -> gated norm."""
+    lens, Hk, Hv = [100, 1, 70], 4, 12
+    T, N = sum(lens), len(lens)
+    log(f"mixer_fwd, gates from projections, lens={lens}")
+    mi = synth.mixer_inputs(3750, T, Hk=Hk, Hv=Hv, conv_state_seqs=N)
+    gi = synth.gate_inputs(3751, T, Hv=Hv)
+    cu = synth.cu_from_lengths(lens)
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    ga, gb, A_log, dt = dev_bf16(gi.a), dev_bf16(gi.b), dev_f32(gi.A_log), dev_f32(gi.dt_bias)
+    cs1, cs2 = dev_bf16(mi.conv_state), dev_bf16(mi.conv_state)
+    out1, h1 = ops.gdn_mixer_fwd(x, w, None, None, z, nw, Hk=Hk, a=ga, b=gb, A_log=A_log,
+                                 dt_bias=dt, conv_state=cs1, cu_seqlens=dev_i32(cu))
+    y = ops.gdn_conv1d_fwd(x, w, conv_state=cs2, cu_seqlens=dev_i32(cu),
+                           n_l2_heads=2 * Hk).view(T, 2 * Hk + Hv, 128)
+    o, h2 = ops.gdn_chunk_fwd_gated(y[:, :Hk], y[:, Hk:2 * Hk], y[:, 2 * Hk:], ga, gb, A_log, dt,
+                                    cu_seqlens=dev_i32(cu))
+    out2 = ops.gdn_gated_rmsnorm(o, z, nw)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(h1, h2) and torch.equal(cs1, cs2)
+    g, beta = oracle.gate_prep(gi.a, gi.b, gi.A_log, gi.dt_bias)
+    ry, _ = oracle.conv1d(mi.x, mi.conv_w, conv_state=mi.conv_state, cu_seqlens=cu,
+                          n_l2_heads=2 * Hk, head_dim=128, stage_bf16=True)
+    ry = ry.reshape(T, 2 * Hk + Hv, 128)
+    ro, rT = oracle.recurrence(ry[:, :Hk], ry[:, Hk:2 * Hk], ry[:, 2 * Hk:], g, beta,
+                               cu_seqlens=cu, n_seqs=N)
+    assert_close(host(out1), oracle.gated_rmsnorm(ro, mi.z, mi.norm_w), "out")
+    assert_close(host(h1), rT, "final_state")
+
+
 def test_mixer_fwd_against_oracle():
     """The fused mixer against the oracle's conv -> recurrence -> gated norm,
     varlen with conv states, initial states and an empty sequence."""
@@ -517,6 +549,32 @@ def test_decode_mixer_step_against_oracle(N, Hk, Hv, slotted, out_bf16):
     cs_bits = cs.cpu().view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(cs_bits[others], mi.conv_state[others])
     np.testing.assert_array_equal(got_st[others], pool[others])
+
+
+def test_decode_mixer_step_gates_from_projections():
+    """The fused decode step with the gates formed from bf16 projections
+    (a, b as columns of a wider buffer) against the oracle's gate preparation
+    followed by conv -> rule -> norm, with a slot map."""
+    N, Hk, Hv, n_slots = 5, 4, 12, 8
+    log("decode_mixer_step, gates from projections")
+    mi, pool = _mixer_step_case(3700, N, Hk, Hv, n_slots)
+    gi = synth.gate_inputs(3701, N, Hv=Hv)
+    slots = np.array([6, 1, 3, 0, 7], dtype=np.int32)
+    wide = torch.zeros((N, 2 * Hv + 16), dtype=torch.bfloat16, device="cuda")
+    wide[:, 16:16 + Hv] = dev_bf16(gi.a)
+    wide[:, 16 + Hv:] = dev_bf16(gi.b)
+    cs, st = dev_bf16(mi.conv_state), dev_f32(pool)
+    out = ops.gdn_decode_mixer_step(dev_bf16(mi.x), dev_bf16(mi.conv_w), cs, None, None,
+                                    dev_bf16(mi.z), dev_f32(mi.norm_w), st, Hk=Hk,
+                                    a=wide[:, 16:16 + Hv], b=wide[:, 16 + Hv:],
+                                    A_log=dev_f32(gi.A_log), dt_bias=dev_f32(gi.dt_bias),
+                                    state_slot=dev_i32(slots))
+    g, beta = oracle.gate_prep(gi.a, gi.b, gi.A_log, gi.dt_bias)
+    mg = synth.MixerInputs(mi.x, mi.conv_w, g, beta, mi.z, mi.norm_w, mi.conv_state)
+    rout, rcs, rst = oracle_mixer_step(mg, pool, Hk, Hv, slots)
+    assert_close(host(out), rout, "out")
+    assert_close(host(st)[slots], rst[slots], "state (slots used)")
+    np.testing.assert_array_equal(host(cs)[slots], rcs)
 
 
 @pytest.mark.parametrize("out_bf16", [False, True])
