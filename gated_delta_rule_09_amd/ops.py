@@ -368,7 +368,7 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tenso
     for t, nm in ((conv_w, "conv_w"), (norm_w, "norm_w")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
-    z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 else z
+    z2 = z.reshape(z.shape[0], z.shape[1] * z.shape[2]) if z.dim() == 3 else z
     _need(z2, "z", torch.bfloat16, 2)
     _inner_contig(z2, "z")
     T = x.shape[0]
@@ -517,7 +517,7 @@ def gdn_decode_mixer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: tor
             raise ValueError(f"{nm} must be contiguous")
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous")
-    z2 = z.reshape(z.shape[0], -1) if z.dim() == 3 else z
+    z2 = z.reshape(z.shape[0], z.shape[1] * z.shape[2]) if z.dim() == 3 else z
     _need(z2, "z", torch.bfloat16, 2)
     if z2.stride(1) != 1:
         raise ValueError("z rows must be contiguous")
@@ -550,7 +550,7 @@ def gdn_gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,
     rows, Hv, dv = o.shape
     if z.dim() == 3:
         _inner_contig(z, "z")
-        z2 = z.view(z.shape[0], -1) if z.is_contiguous() else z.reshape(z.shape[0], -1)
+        z2 = z.view(z.shape[0], z.shape[1] * z.shape[2])   # inner dims contiguous: a view
     else:
         z2 = z
     _need(z2, "z", torch.bfloat16, 2)

@@ -140,3 +140,25 @@ def test_empty_batch_is_a_no_op():
     assert o.shape[0] == 0 and torch.equal(s, h0)
     o = ops.gdn_decode_step(z, z, zv, zg, zg, torch.zeros((1, 6, 128, 128), device="cuda"))
     assert o.shape[0] == 0
+    # the other entry points on empty batches: nothing written, states kept
+    pool = torch.randn((3, 6, 128, 128), device="cuda")
+    pool0 = pool.clone()
+    slots = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
+    o = ops.gdn_chunk_fwd_pooled(z, z, zv, zg, zg, pool, slots,
+                                 cu_seqlens=torch.zeros(3, dtype=torch.int32, device="cuda"))
+    assert o.shape[0] == 0 and torch.equal(pool, pool0)
+    o = ops.gdn_decode_tokens(z, z, zv, zg, zg, pool, 2)
+    assert o.shape[0] == 0 and torch.equal(pool, pool0)
+    C = (2 * 2 + 6) * 128
+    x0 = torch.empty((0, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.randn((C, 4), device="cuda").to(torch.bfloat16)
+    cs = torch.randn((2, C, 3), device="cuda").to(torch.bfloat16)
+    cs0 = cs.clone()
+    nw = torch.ones(128, device="cuda")
+    out, hT = ops.gdn_mixer_fwd(x0, w, zg, zg, zv, nw, Hk=2, conv_state=cs, initial_state=h0,
+                                cu_seqlens=torch.zeros(3, dtype=torch.int32, device="cuda"))
+    assert out.shape[0] == 0 and torch.equal(hT, h0) and torch.equal(cs, cs0)
+    cs3 = torch.randn((3, C, 3), device="cuda").to(torch.bfloat16)   # one window per state slot
+    cs30 = cs3.clone()
+    out = ops.gdn_decode_mixer_step(x0, w, cs3, zg, zg, zv, nw, pool, Hk=2)
+    assert out.shape[0] == 0 and torch.equal(pool, pool0) and torch.equal(cs3, cs30)
