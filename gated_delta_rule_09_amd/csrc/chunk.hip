@@ -146,6 +146,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 struct PrepParams {
   const uint16_t* q; const uint16_t* k;
   int64_t qs, ks;
@@ -181,11 +183,14 @@ __device__ __forceinline__ half4 lds_a16(const _Float16* base, int stride, int r
   return *reinterpret_cast<const half4*>(base + row * stride + kb + 4 * grp);
 }
 
+// Workspace writes of the prep are streamed past the caches (nontemporal): the
+// scan reads them long after they would have been evicted, and keeping them
+// out of L2 left the prefill launch 2 % faster.
 __device__ __forceinline__ void put16(unsigned char* dst, const half8 v) {
-  *reinterpret_cast<half8*>(dst) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<half8*>(dst));
 }
 __device__ __forceinline__ void put8(unsigned char* dst, const half4 v) {
-  *reinterpret_cast<half4*>(dst) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<half4*>(dst));
 }
 
 // Gram tiles of a wave, in the transposed orientation C' = X_j Y_b^T, so
@@ -421,10 +426,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     sm.G[w][lane] = G;
     sm.bet[w][lane] = bv;
     float* dec = reinterpret_cast<float*>(vb + kOffDecay);
-    dec[lane] = bv;
-    dec[64 + lane] = bv * gam;
-    dec[128 + lane] = p.scale * gam;
-    dec[192 + lane] = __expf(Glast - G);
+    __builtin_nontemporal_store(bv, &dec[lane]);
+    __builtin_nontemporal_store(bv * gam, &dec[64 + lane]);
+    __builtin_nontemporal_store(p.scale * gam, &dec[128 + lane]);
+    __builtin_nontemporal_store(__expf(Glast - G), &dec[192 + lane]);
     if (lane == 0) *reinterpret_cast<float*>(vb + kOffGL) = __expf(Glast);
   };
 
@@ -463,8 +468,13 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
       const int piece = tid + kThreads * j;
       const int rr = min(piece >> 4, len - 1);
       const int c8 = (piece & 15) * 8;
-      kraw[j] = *reinterpret_cast<const uint4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8);
-      qraw[j] = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8);
+      // q and k are read once: streamed (nontemporal)
+      const u32x4 kt = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(p.k + static_cast<int64_t>(t0 + rr) * p.ks + kh * kD + c8));
+      const u32x4 qt = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(p.q + static_cast<int64_t>(t0 + rr) * p.qs + kh * kD + c8));
+      kraw[j] = uint4{kt[0], kt[1], kt[2], kt[3]};
+      qraw[j] = uint4{qt[0], qt[1], qt[2], qt[3]};
     }
     // the first batch's decay tables while the K, Q loads are in flight
     if (w < nb0) decay(0, gv, bv);
@@ -591,9 +601,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         if (r0 + jj < len)
-          *reinterpret_cast<uint4*>(p.vout + static_cast<int64_t>(t0 + r0 + jj) * (p.Hv * kD) + h * kD + g8) =
-              uint4{pack_bf16x2(y[jj][0], y[jj][1]), pack_bf16x2(y[jj][2], y[jj][3]),
-                    pack_bf16x2(y[jj][4], y[jj][5]), pack_bf16x2(y[jj][6], y[jj][7])};
+          __builtin_nontemporal_store(
+              u32x4{pack_bf16x2(y[jj][0], y[jj][1]), pack_bf16x2(y[jj][2], y[jj][3]),
+                    pack_bf16x2(y[jj][4], y[jj][5]), pack_bf16x2(y[jj][6], y[jj][7])},
+              reinterpret_cast<u32x4*>(p.vout + static_cast<int64_t>(t0 + r0 + jj) * (p.Hv * kD) + h * kD + g8));
     }
   }
 }
