@@ -77,6 +77,8 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Eight floats to eight bf16, round to nearest even (v_cvt_pk_bf16_f32).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -179,7 +181,11 @@ __global__ __launch_bounds__(kThreads) void conv1d_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] *= inv;
     }
-    if (active) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * ys + c0) = pack_bf16x8(out);
+    if (active) {   // y is written once and read by another kernel: streamed (nontemporal)
+      const uint4 pk = pack_bf16x8(out);
+      __builtin_nontemporal_store(u32x4{pk.x, pk.y, pk.z, pk.w},
+                                  reinterpret_cast<u32x4*>(y + static_cast<int64_t>(t) * ys + c0));
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       hist[0][i] = hist[1][i];
