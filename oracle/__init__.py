@@ -61,6 +61,12 @@ def _load():
     lib.oracle_gate_prep.argtypes = [_dp, ctypes.c_int64, _dp, ctypes.c_int64, _dp, _dp, _dp, _dp,
                                      ctypes.c_int64, ctypes.c_int32]
     lib.oracle_gate_prep.restype = ctypes.c_int
+    lib.oracle_gdn_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp,
+                                        ctypes.c_int32]
+    lib.oracle_gdn_backward.restype = ctypes.c_int
     lib.oracle_round_bf16_array.argtypes = [_dp, _dp, ctypes.c_int64]
     lib.oracle_round_bf16_array.restype = None
     _lib = lib
@@ -116,6 +122,32 @@ def recurrence(q, k, v, g, beta, h0=None, cu_seqlens=None, n_seqs=1, scale=1.0,
     if rc:
         raise ValueError(f"oracle_gdn_recurrence failed ({rc})")
     return o, hT
+
+
+def backward(q, k, v, g, beta, d_o, h0=None, dhT=None, cu_seqlens=None, n_seqs=1, scale=1.0,
+             n_threads=None):
+    """Gradients of L = sum(d_o * o) + sum(dhT * hT) of the recurrence.
+
+    Shapes as recurrence(); d_o like o, dhT like the final state (or None).
+    Returns dict(dq, dk, dv, dg, dbeta, dh0) in fp64.
+    """
+    lib = _load()
+    q, k, v, g, beta, d_o, h0, dhT = map(_f64, (q, k, v, g, beta, d_o, h0, dhT))
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    cu = _i32(cu_seqlens)
+    if cu is not None:
+        n_seqs = cu.shape[0] - 1
+    out = dict(dq=np.zeros((T, Hk, dk)), dk=np.zeros((T, Hk, dk)), dv=np.zeros((T, Hv, dv)),
+               dg=np.zeros((T, Hv)), dbeta=np.zeros((T, Hv)), dh0=np.zeros((n_seqs, Hv, dv, dk)))
+    rc = lib.oracle_gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                 _ptr(d_o), _ptr(dhT), _ptr(cu, _ip), n_seqs, T, Hk, Hv, dk, dv,
+                                 float(scale), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+                                 _threads(n_threads))
+    if rc:
+        raise ValueError(f"oracle_gdn_backward failed ({rc})")
+    return out
 
 
 def decode(q, k, v, g, beta, state, state_slot=None, scale=1.0, n_threads=None):

@@ -185,6 +185,154 @@ int oracle_gdn_recurrence(const double* q, const double* k, const double* v,
 }
 
 /* ---------------------------------------------------------------------------
+ * Backward of the recurrence: the derivatives of the loss
+ *   L = sum(d_o * o) + sum(dhT * hT)
+ * with respect to q, k, v, g, beta and h0, by the chain rule through the
+ * operations of rule_step taken in reverse order.  Forward, per token:
+ *   a = e^g;  Sh = a S_prev;  p = Sh k;  u = beta (v - p);  S = Sh + u k^T;
+ *   o = scale S q.
+ * Backward, with D = dL/dS (from dhT, or zero, after the last token):
+ *   D  += scale d_o q^T           dq += scale S^T d_o
+ *   du  = D k                     dk += D^T u
+ *   dv  = beta du                 dbeta = (v - p) . du
+ *   dp  = -beta du
+ *   dSh = D + dp k^T              dk += Sh^T dp
+ *   dg  = a (S_prev : dSh)        D   = a dSh      (dL/dS_prev)
+ * and dh0 is the D left after the first token.  dq and dk of a key head sum
+ * over the value heads that share it.  Every forward state is kept (one per
+ * token), so this is for small sizes.  Layouts as oracle_gdn_recurrence;
+ * d_o like o, dhT and dh0 like the states (dhT, dh0 nullable).
+ * ------------------------------------------------------------------------- */
+int oracle_gdn_backward(const double* q, const double* k, const double* v, const double* g,
+                        const double* beta, const double* h0, const double* d_o,
+                        const double* dhT, const int32_t* cu_seqlens, int32_t n_seqs,
+                        int32_t T_total, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv,
+                        double scale, double* dq, double* dkey, double* dval, double* dg,
+                        double* dbeta, double* dh0, int32_t n_threads)
+{
+    if (!q || !k || !v || !g || !beta || !d_o || !dq || !dkey || !dval || !dg || !dbeta)
+        return ORACLE_ERR_ARG;
+    if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk || dk <= 0 || dv <= 0)
+        return ORACLE_ERR_ARG;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        int64_t s0, s1;
+        if (seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1)) return ORACLE_ERR_ARG;
+    }
+    const int32_t group = Hv / Hk;
+    const int64_t ssz = (int64_t)dv * dk;
+    const int64_t units = (int64_t)n_seqs * Hk;      /* (sequence, key head): owns dq, dk rows */
+    int err = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int64_t unit = 0; unit < units; ++unit) {
+        const int32_t n = (int32_t)(unit / Hk);
+        const int32_t kh = (int32_t)(unit % Hk);
+        int64_t s0, s1;
+        seq_bounds(cu_seqlens, n_seqs, T_total, n, &s0, &s1);
+        const int64_t len = s1 - s0;
+        for (int64_t t = s0; t < s1; ++t) {
+            memset(dq + (t * Hk + kh) * dk, 0, sizeof(double) * dk);
+            memset(dkey + (t * Hk + kh) * dk, 0, sizeof(double) * dk);
+        }
+        double* Sall = (double*)malloc(sizeof(double) * ssz * (len + 1));
+        double* D = (double*)malloc(sizeof(double) * ssz);
+        double* dSh = (double*)malloc(sizeof(double) * ssz);
+        double* work = (double*)malloc(sizeof(double) * 3 * dv);
+        if (!Sall || !D || !dSh || !work) {
+            free(Sall); free(D); free(dSh); free(work);
+            err = ORACLE_ERR_NOMEM;
+            continue;
+        }
+        double* p = work;
+        double* u = work + dv;
+        double* du = work + 2 * dv;
+        for (int32_t j = 0; j < group; ++j) {
+            const int32_t h = kh * group + j;
+            /* forward, every state kept: Sall[i] = state before token s0 + i */
+            if (h0) memcpy(Sall, h0 + ((int64_t)n * Hv + h) * ssz, sizeof(double) * ssz);
+            else memset(Sall, 0, sizeof(double) * ssz);
+            for (int64_t i = 0; i < len; ++i) {
+                const int64_t t = s0 + i;
+                memcpy(Sall + (i + 1) * ssz, Sall + i * ssz, sizeof(double) * ssz);
+                rule_step(Sall + (i + 1) * ssz, k + (t * Hk + kh) * dk, q + (t * Hk + kh) * dk,
+                          v + (t * Hv + h) * dv, g[t * Hv + h], beta[t * Hv + h], NULL, dk, dv,
+                          scale);
+            }
+            /* backward */
+            if (dhT) memcpy(D, dhT + ((int64_t)n * Hv + h) * ssz, sizeof(double) * ssz);
+            else memset(D, 0, sizeof(double) * ssz);
+            for (int64_t i = len - 1; i >= 0; --i) {
+                const int64_t t = s0 + i;
+                const double* Sp = Sall + i * ssz;          /* S_prev */
+                const double* S = Sall + (i + 1) * ssz;     /* S after the token */
+                const double* kk = k + (t * Hk + kh) * dk;
+                const double* qq = q + (t * Hk + kh) * dk;
+                const double* vv = v + (t * Hv + h) * dv;
+                const double* dout = d_o + (t * Hv + h) * dv;
+                double* dqt = dq + (t * Hk + kh) * dk;
+                double* dkt = dkey + (t * Hk + kh) * dk;
+                const double a = exp(g[t * Hv + h]);
+                const double b = beta[t * Hv + h];
+                /* o = scale S q */
+                for (int32_t r = 0; r < dv; ++r)
+                    for (int32_t c = 0; c < dk; ++c) D[(int64_t)r * dk + c] += scale * dout[r] * qq[c];
+                for (int32_t c = 0; c < dk; ++c) {
+                    double acc = 0.0;
+                    for (int32_t r = 0; r < dv; ++r) acc += S[(int64_t)r * dk + c] * dout[r];
+                    dqt[c] += scale * acc;
+                }
+                /* p and u of the forward step (Sh = a S_prev) */
+                for (int32_t r = 0; r < dv; ++r) {
+                    double acc = 0.0;
+                    for (int32_t c = 0; c < dk; ++c) acc += a * Sp[(int64_t)r * dk + c] * kk[c];
+                    p[r] = acc;
+                    u[r] = b * (vv[r] - acc);
+                }
+                /* S = Sh + u k^T */
+                for (int32_t r = 0; r < dv; ++r) {
+                    double acc = 0.0;
+                    for (int32_t c = 0; c < dk; ++c) acc += D[(int64_t)r * dk + c] * kk[c];
+                    du[r] = acc;
+                }
+                for (int32_t c = 0; c < dk; ++c) {
+                    double acc = 0.0;
+                    for (int32_t r = 0; r < dv; ++r) acc += D[(int64_t)r * dk + c] * u[r];
+                    dkt[c] += acc;
+                }
+                /* u = beta (v - p) */
+                double db = 0.0;
+                for (int32_t r = 0; r < dv; ++r) {
+                    dval[(t * Hv + h) * dv + r] = b * du[r];
+                    db += (vv[r] - p[r]) * du[r];
+                }
+                dbeta[t * Hv + h] = db;
+                /* p = Sh k, with dp = -beta du */
+                for (int32_t r = 0; r < dv; ++r) {
+                    const double dp = -b * du[r];
+                    for (int32_t c = 0; c < dk; ++c)
+                        dSh[(int64_t)r * dk + c] = D[(int64_t)r * dk + c] + dp * kk[c];
+                }
+                for (int32_t c = 0; c < dk; ++c) {
+                    double acc = 0.0;
+                    for (int32_t r = 0; r < dv; ++r) acc += a * Sp[(int64_t)r * dk + c] * (-b * du[r]);
+                    dkt[c] += acc;
+                }
+                /* Sh = a S_prev, a = e^g */
+                double da = 0.0;
+                for (int64_t e = 0; e < ssz; ++e) da += Sp[e] * dSh[e];
+                dg[t * Hv + h] = a * da;
+                for (int64_t e = 0; e < ssz; ++e) D[e] = a * dSh[e];
+            }
+            if (dh0) memcpy(dh0 + ((int64_t)n * Hv + h) * ssz, D, sizeof(double) * ssz);
+        }
+        free(Sall); free(D); free(dSh); free(work);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------------------------
  * Decode: one token per sequence, state updated in place.
  *   q, k : [N, Hk, dk]  v : [N, Hv, dv]  g, beta : [N, Hv]  o : [N, Hv, dv]
  *   state : [n_slots, Hv, dv, dk]; sequence n uses slot state_slot[n]

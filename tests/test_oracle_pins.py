@@ -407,3 +407,70 @@ def test_gate_prep_softplus_reflection_and_tails():
     assert sp[-1] == 800.0 and abs(sp[-2] - 50.0) <= 1e-14
     np.testing.assert_allclose(sp[1], np.exp(-50.0), rtol=1e-14)
     assert sp[0] == 0.0 or sp[0] < 1e-300
+
+
+# ----------------------------------------------------------------- backward
+
+def _bwd_case(seed, T, Hk, Hv, dk, dv, n_states):
+    r = np.random.default_rng(seed)
+    k = r.standard_normal((T, Hk, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    return dict(q=r.standard_normal((T, Hk, dk)), k=k, v=r.standard_normal((T, Hv, dv)),
+                g=-r.uniform(0.0, 0.5, (T, Hv)), beta=r.uniform(0.1, 0.9, (T, Hv)),
+                h0=0.3 * r.standard_normal((n_states, Hv, dv, dk))), \
+        r.standard_normal((T, Hv, dv)), r.standard_normal((n_states, Hv, dv, dk))
+
+
+def test_backward_central_differences():
+    """Every element of every input: the oracle's gradient of
+    L = sum(d_o * o) + sum(dhT * hT) against a central finite difference of L
+    computed with the forward oracle (varlen, two value heads on one key
+    head, scale != 1)."""
+    cu = np.array([0, 4, 6], dtype=np.int32)
+    x, d_o, dhT = _bwd_case(51, 6, 1, 2, 3, 2, 2)
+
+    def loss(x):
+        o, hT = oracle.recurrence(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"],
+                                  cu_seqlens=cu, n_seqs=2, scale=0.7)
+        return float(np.sum(d_o * o) + np.sum(dhT * hT))
+
+    grad = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, h0=x["h0"], dhT=dhT,
+                           cu_seqlens=cu, scale=0.7)
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", h0="dh0")
+    eps = 1e-6
+    for name, gname in names.items():
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {kk: vv.copy() for kk, vv in x.items()}
+            xm = {kk: vv.copy() for kk, vv in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        np.testing.assert_allclose(grad[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_backward_matches_torch_autograd_fp64():
+    """The hand-derived reverse recurrence against torch autograd through the
+    forward definition in fp64 (equal-length sequences, two value heads per
+    key head, dv != dk)."""
+    T, Hk, Hv, dk, dv, N = 12, 2, 4, 5, 3, 2
+    x, d_o, dhT = _bwd_case(52, T, Hk, Hv, dk, dv, N)
+    grad = oracle.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], d_o, h0=x["h0"], dhT=dhT,
+                           n_seqs=N, scale=1.3)
+    tx = {kk: torch.tensor(vv, dtype=torch.float64, requires_grad=True) for kk, vv in x.items()}
+    L = T // N
+    loss = torch.zeros((), dtype=torch.float64)
+    for n in range(N):
+        for h in range(Hv):
+            kh = h // (Hv // Hk)
+            S = tx["h0"][n, h]
+            for t in range(n * L, (n + 1) * L):
+                kt, qt = tx["k"][t, kh], tx["q"][t, kh]
+                a, b = torch.exp(tx["g"][t, h]), tx["beta"][t, h]
+                S = a * S + torch.outer(b * (tx["v"][t, h] - a * (S @ kt)), kt)
+                loss = loss + torch.dot(torch.as_tensor(d_o[t, h]), 1.3 * (S @ qt))
+            loss = loss + torch.sum(torch.as_tensor(dhT[n, h]) * S)
+    loss.backward()
+    for name, gname in dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", h0="dh0").items():
+        np.testing.assert_allclose(grad[gname], tx[name].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=gname)
