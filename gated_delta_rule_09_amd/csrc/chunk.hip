@@ -42,6 +42,7 @@
 // accumulation is fp32 throughout.  The per-chunk state never leaves the
 // registers, and fragment reads are lane-contiguous 16-byte LDS loads.
 // Work-groups that share a key head get block ids on the same XCD (L2).
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1078,17 +1079,18 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   else output_wave(std::integral_constant<int, kOutWaves - 1>{});
 }
 
-// Compute units of the current device, looked up once per device.
+// Compute units of the current device, looked up once per device (calls from
+// several host threads may race to fill an entry; they store the same value).
 int compute_units() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace
