@@ -148,6 +148,16 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
     const uint16_t* src = which ? q + row * q_stride : k + row * k_stride;
     kq_lds[t][which][idx] = *reinterpret_cast<const uint2*>(src + kh * kD + 4 * idx);
   }
+  // and every token's v row of this head (held in registers, the v entries
+  // of eight tokens alone kept the kernel above 128 VGPRs: 448 against
+  // 343 us at 256 sequences x 8 tokens)
+  constexpr bool kStageV = kStage;
+  __shared__ uint2 v_lds[kStageV ? kT : 1][32];
+  if (kStageV && tid < kT * 32) {
+    const int t = tid >> 5, idx = tid & 31;
+    const int64_t row = static_cast<int64_t>(n) * kT + t;
+    v_lds[t][idx] = *reinterpret_cast<const uint2*>(v + row * v_stride + h * kD + 4 * idx);
+  }
   floatx4 s[kRows][4];
 #pragma unroll
   for (int r = 0; r < kRows; ++r)
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
   // staging, k and q: this lane's 16 channels as bf16 pairs), all issued
   // before the arithmetic
   uint2 kb[kStage ? 1 : kT][4], qb[kStage ? 1 : kT][4];
-  float gt[kT], bt[kT], vt[kT][kRows];
+  float gt[kT], bt[kT], vt[kStageV ? 1 : kT][kRows];
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
     const int64_t row = static_cast<int64_t>(n) * kT + t;
@@ -176,9 +186,10 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
     gt[t] = g[row * Hv + h];
     bt[t] = beta[row * Hv + h];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) vt[t][r] = bf16_to_f32(v[row * v_stride + h * kD + rg + kRowStep * r]);
+    for (int r = 0; r < kRows; ++r)
+      if constexpr (!kStageV) vt[t][r] = bf16_to_f32(v[row * v_stride + h * kD + rg + kRowStep * r]);
   }
-  if (kStage) __syncthreads();
+  if (kStage || kStageV) __syncthreads();
 
 #pragma unroll
   for (int t = 0; t < kT; ++t) {
@@ -222,7 +233,10 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
       }
       sk = sum8(sk);
       sq = sum8(sq);
-      const float u = b * (vt[t][r] - a * sk);
+      float vv;
+      if constexpr (kStageV) vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(v_lds[t])[row]);
+      else vv = vt[t][r];
+      const float u = b * (vv - a * sk);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
