@@ -7,7 +7,10 @@ oracle then recomputes outputs it can finish in seconds:
   full mixer       B=1, T=8192 (conv -> rule -> gated norm)  all conv channels,
                                                              sampled value heads
   long prefill     B=1, T=65536, S0 ~ N(0, 0.02)             sampled value heads
+  long prefill,    bf16 o (= fp32 o rounded) and gates from  bit-exact /
+  other forms      projections (oracle)                       sampled heads
   decode step      256 sequences x 1 token, state in place   every head
+  multi-token      256 sequences x 4 tokens, one pass        every head
   fused decode     the same batch through the whole mixer    every head
                    step in one launch (conv window, state)
   fused mixer      T=8192 in one gdn_mixer_fwd call          bit-identical to
@@ -106,6 +109,35 @@ def test_full_prefill_T65536_sampled_heads():
     assert_close(host(fs[:, heads]), rT, "final_state")
 
 
+def test_full_prefill_T65536_bf16_o_and_gated():
+    """The two other prefill launch forms the benchmark times, at T=65536: o in
+    bf16 is the fp32 o rounded (nearest even) bit for bit with identical final
+    states; the gates formed from projections against the oracle's gate
+    preparation and recurrence on sampled value heads."""
+    T = 65536
+    heads = [5, 29]
+    log(f"full prefill T={T}: bf16 o, and gates from projections (oracle on heads {heads})")
+    ci = synth.chunk_inputs_torch(1002, T, h0_std=0.02)
+    args = (ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"])
+    o32, s32 = ops.gdn_chunk_fwd(*args, initial_state=ci["h0"], n_seqs=1)
+    o16, s16 = ops.gdn_chunk_fwd(*args, initial_state=ci["h0"], n_seqs=1, o_bf16=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s16, s32), "final states differ"
+    assert torch.equal(o16, o32.to(torch.bfloat16)), "bf16 o is not the fp32 o rounded"
+    del o16, s16
+    gi = synth.gate_inputs(1007, T)
+    og, sg = ops.gdn_chunk_fwd_gated(ci["q"], ci["k"], ci["v"], dev_bf16(gi.a), dev_bf16(gi.b),
+                                     dev_f32(gi.A_log), dev_f32(gi.dt_bias),
+                                     initial_state=ci["h0"], n_seqs=1)
+    g, beta = oracle.gate_prep(gi.a[:, heads], gi.b[:, heads], gi.A_log[heads], gi.dt_bias[heads])
+    kh = key_heads(heads)
+    log("  oracle")
+    ro, rT = oracle.recurrence(bits(ci["q"][:, kh]), bits(ci["k"][:, kh]), bits(ci["v"][:, heads]),
+                               g, beta, f32(ci["h0"][:, heads]))
+    assert_close(host(og[:, heads]), ro, "o (gated)")
+    assert_close(host(sg[:, heads]), rT, "final_state (gated)")
+
+
 def test_full_decode_N256_every_head():
     N = 256
     log(f"full decode step N={N}, state in place")
@@ -116,6 +148,21 @@ def test_full_decode_N256_every_head():
     ro, rS = oracle.decode(di.q, di.k, di.v, di.g, di.beta, di.state)
     assert_close(host(o), ro, "o")
     assert_close(host(state), rS, "state")
+
+
+def test_full_decode_tokens4_N256_every_head():
+    """256 sequences x 4 tokens in one pass over the states (the multi-token
+    decode the benchmark times): o of every token and the states, every head."""
+    N, nt = 256, 4
+    log(f"full multi-token decode N={N} x {nt} tokens, every head")
+    ci = synth.chunk_inputs(1008, N * nt, lengths=[nt] * N, h0_std=0.02)
+    state = dev_f32(ci.h0)
+    o = ops.gdn_decode_tokens(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g),
+                              dev_f32(ci.beta), state, nt)
+    ro, rT = oracle.recurrence(ci.q, ci.k, ci.v, ci.g, ci.beta, ci.h0, cu_seqlens=ci.cu_seqlens,
+                               n_seqs=N)
+    assert_close(host(o), ro, "o")
+    assert_close(host(state), rT, "state")
 
 
 def test_full_decode_mixer_step_N256_every_head():

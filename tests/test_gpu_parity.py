@@ -271,7 +271,7 @@ def test_decode_step_slot_map_and_scale():
     np.testing.assert_array_equal(got[others], pool[others])
 
 
-@pytest.mark.parametrize("N,nt", [(1, 1), (3, 2), (5, 5), (17, 8)])
+@pytest.mark.parametrize("N,nt", [(1, 1), (3, 2), (6, 3), (4, 4), (5, 5), (4, 6), (2, 7), (17, 8)])
 def test_decode_tokens_against_oracle(N, nt):
     """n_tokens tokens per sequence in one pass: the recurrence from each
     sequence's state, o of every token and the final state."""
