@@ -13,6 +13,9 @@
 //            to bf16, as the separate conv call stores them
 //   S_h   <- a S_h + b (v_h - a S_h k) k^T,  o_h = scale * S_h q   (a = exp(g))
 //   out_h  = o_h / sqrt(mean(o_h^2) + norm_eps) * w * z_h * sigmoid(z_h)
+// with g, b given per (n, h), or formed from the projections a, b as the
+// prefill's gate preparation does: g = -exp(A_log) softplus(a + dt_bias),
+// b = sigmoid(b_proj) (the kGated instances).
 //
 // Mapping: one 1024-thread work-group per (n, kh), so the conv channels and
 // the states it updates belong to it alone and the in-place updates race with
