@@ -526,10 +526,15 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
                          const uint16_t* z, int64_t z_stride,
                          const float* norm_w, void* out, int32_t out_is_bf16,
                          const float* initial_state, float* final_state,
+                         const int32_t* state_slot, int32_t n_slots,
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t d, float scale, float l2_eps, float norm_eps,
                          void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "gdn_mixer_fwd";
+  if (state_slot && n_seqs > 0 && (!initial_state || initial_state != final_state))
+    return fail(GDN_ERR_SHAPE, "%s: with a slot map, initial_state and final_state must be the same pool", fn);
+  if (state_slot && n_slots < 0) return fail(GDN_ERR_SHAPE, "%s: n_slots < 0", fn);
+  const int32_t n_rows = state_slot ? n_slots : n_seqs;   // rows of the state and conv-state buffers
   if (T_total > 0 && (!x || !conv_w || !z || !norm_w || !out))
     return fail(GDN_ERR_NULL, "%s: x, conv_w, z, norm_w and out are required", fn);
   if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
@@ -548,7 +553,8 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
     return fail(GDN_ERR_SHAPE, "%s: x and z row strides too small or not multiples of 8", fn);
   if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(conv_bias, 16) ||
       !aligned(conv_state, 16) || !aligned(z, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
-      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
+      !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4) ||
+      !aligned(state_slot, 4))
     return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (16 bytes; cu_seqlens: 4)", fn);
   if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
       !std::isfinite(norm_eps))
@@ -567,16 +573,20 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   const Range rx = range_of(x, T_total, x_stride, C, 2);
   const Range rw = range_of(conv_w, 1, 0, C * 4, 2);
   const Range rbias = range_of(conv_bias, 1, 0, C, 4);
-  const Range rcs = range_of(conv_state, n_seqs, 3 * C, 3 * C, 2);
+  const Range rcs = range_of(conv_state, n_rows, 3 * C, 3 * C, 2);
+  const Range rsl = range_of(state_slot, n_seqs, 1, 1, 4);
   const Range& rg = rgates[0];
   const Range& rb = rgates[1];
   const Range rz = range_of(z, T_total, z_stride, width, 2);
   const Range rn = range_of(norm_w, 1, 0, d, 4);
   const Range rcu = range_of(cu_seqlens, 1, 0, static_cast<int64_t>(n_seqs) + 1, 4);
   const Range ro = range_of(out, T_total, width, width, out_is_bf16 ? 2 : 4);
-  const Range r0 = range_of(initial_state, n_seqs, ssz, ssz, 4);
-  const Range rT = range_of(final_state, n_seqs, ssz, ssz, 4);
+  const Range r0 = range_of(initial_state, n_rows, ssz, ssz, 4);
+  const Range rT = range_of(final_state, n_rows, ssz, ssz, 4);
   const Range rws = range_of(workspace, 1, 0, static_cast<int64_t>(need), 1);
+  for (const Range* in : {&rsl})
+    if (overlap(*in, rcs) || overlap(*in, rT) || overlap(*in, rws))
+      return fail(GDN_ERR_ALIAS, "%s: state_slot overlaps a state or the workspace", fn);
   for (const Range* in : {&rx, &rw, &rbias, &rcs, &rg, &rb, &rz, &rn, &rcu, &r0, &rT, &rws})
     if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: out overlaps another buffer", fn);
   for (int i = 2; i < 6; ++i)
@@ -608,15 +618,16 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
                          : static_cast<float*>(out);
   gdn::ConvFront cf;
   cf.x = x; cf.xs = x_stride; cf.w = conv_w; cf.bias = conv_bias; cf.state = conv_state;
+  cf.slots = state_slot;
   cf.l2_eps = l2_eps;
   gdn_status s = hip_status(gdn::launch_chunk_fwd(nullptr, 0, nullptr, 0, nullptr, 0,
                                                   gi, o, false, initial_state,
-                                                  final_state, nullptr, cu_seqlens, n_seqs,
+                                                  final_state, state_slot, cu_seqlens, n_seqs,
                                                   T_total, Hk, Hv, scale, workspace, st, &cf),
                             "gdn_mixer_fwd prefill launch");
   if (s) return s;
   s = hip_status(gdn::launch_conv_state(x, x_stride, conv_state, cu_seqlens, n_seqs, T_total,
-                                        static_cast<int>(C), st),
+                                        static_cast<int>(C), st, state_slot),
                  "gdn_mixer_fwd conv state launch");
   if (s) return s;
   return hip_status(gdn::launch_gated_rmsnorm(o, z, z_stride, norm_w, out, out_is_bf16 != 0, T_total,

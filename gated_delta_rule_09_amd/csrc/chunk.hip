@@ -162,6 +162,7 @@ struct PrepParams {
   // q, k) of the pre-conv rows x [T, C]; v goes to vout [T, Hv, 128] bf16
   const uint16_t* x; int64_t xs;
   const uint16_t* conv_w; const float* conv_bias; const uint16_t* conv_state;
+  const int32_t* conv_slots;  // nullptr: sequence n uses conv_state row n
   uint16_t* vout;
   float l2_eps;
   const int32_t* cu;          // nullptr: equal lengths seq_len
@@ -315,7 +316,8 @@ __device__ __forceinline__ void conv_rows(const PrepParams& p, const ConvRows& c
     // multiples of 4, so this is the sequence's first chunk, r0 = 0, and input
     // rows 0, 1, 2 are the tokens s0 - 3, s0 - 2, s0 - 1: state taps 0, 1, 2.
     float st[24];
-    const uint4* sp = reinterpret_cast<const uint4*>(p.conv_state + (static_cast<int64_t>(seq) * C + ch0) * 3);
+    const int64_t row = p.conv_slots ? p.conv_slots[seq] : seq;
+    const uint4* sp = reinterpret_cast<const uint4*>(p.conv_state + (row * C + ch0) * 3);
     bf16x8_to_f32(sp[0], st);
     bf16x8_to_f32(sp[1], st + 8);
     bf16x8_to_f32(sp[2], st + 16);
@@ -1138,7 +1140,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
     if (conv) {
       pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
-      pp.conv_state = conv->state; pp.l2_eps = conv->l2_eps;
+      pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.l2_eps = conv->l2_eps;
       pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
     }
     pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;

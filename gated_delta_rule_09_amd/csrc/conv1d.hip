@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void conv1d_kernel(
 // and 8-channel group.  Runs after conv1d_kernel on the same stream.
 __global__ __launch_bounds__(kThreads) void conv_state_kernel(
     const uint16_t* __restrict__ x, int64_t xs, uint16_t* __restrict__ conv_state, Seqs seqs,
-    int C) {
+    int C, const int32_t* __restrict__ slots) {
   const int groups = C / kChPerThread;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (idx >= static_cast<int64_t>(seqs.n_seqs) * groups) return;
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void conv_state_kernel(
   const int s = seqs.start(n);
   const int len = seqs.end(n) - s;
   if (len == 0) return;
-  uint16_t* st = conv_state + (static_cast<int64_t>(n) * C + c0) * 3;
+  const int64_t row = slots ? slots[n] : n;     // the conv state row of sequence n
+  uint16_t* st = conv_state + (row * C + c0) * 3;
   uint16_t old[24];
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
@@ -272,12 +273,13 @@ hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const
 
 hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state,
                              const int32_t* cu, int n_seqs, int T_total, int C,
-                             hipStream_t stream) {
+                             hipStream_t stream, const int32_t* slots) {
   if (!conv_state || n_seqs <= 0) return hipSuccess;
   Seqs seqs{cu, n_seqs, cu ? 0 : T_total / n_seqs};
   const int64_t work = static_cast<int64_t>(n_seqs) * (C / kChPerThread);
   const dim3 grid(static_cast<unsigned>((work + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(conv_state_kernel, grid, dim3(kThreads), 0, stream, x, xs, conv_state, seqs, C);
+  hipLaunchKernelGGL(conv_state_kernel, grid, dim3(kThreads), 0, stream, x, xs, conv_state, seqs, C,
+                     slots);
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ struct ConvFront {
   const uint16_t* w = nullptr;
   const float* bias = nullptr;
   const uint16_t* state = nullptr;
+  const int32_t* slots = nullptr;   // nullptr: sequence n uses conv state row n
   float l2_eps = 1e-6f;
 };
 
@@ -92,6 +93,6 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
 // sequence), after every read of the old one.
 hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state,
                              const int32_t* cu, int n_seqs, int T_total, int C,
-                             hipStream_t stream);
+                             hipStream_t stream, const int32_t* slots = nullptr);
 
 }  // namespace gdn

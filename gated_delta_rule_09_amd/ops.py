@@ -41,8 +41,8 @@ _SIGS = {
                                    _f32, _vp, _sz, _vp]),
     "gdn_mixer_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "gdn_mixer_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
-                             _vp, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                             _i32, _f32, _f32, _f32, _vp, _sz, _vp]),
+                             _vp, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                             _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz, _vp]),
     "gdn_chunk_map": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "gdn_decode_step": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
@@ -349,6 +349,7 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tenso
                   conv_state: Optional[torch.Tensor] = None,
                   initial_state: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  state_slot: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
                   scale: float = 1.0, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
                   out_bf16: bool = False, out: Optional[torch.Tensor] = None,
@@ -359,11 +360,18 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tenso
     fp32 -> (out [T, Hv, 128] fp32 or bf16, final_state or None); conv_state
     [N, C, 3] bf16 updated in place.  The gates are g, beta [T, Hv] fp32, or
     (g = beta = None) formed from the projections a, b [T, Hv] bf16 with A_log,
-    dt_bias [Hv] fp32."""
+    dt_bias [Hv] fp32.  With state_slot [N] int32, initial_state is a pool
+    [n_slots, Hv, 128, 128] updated in place (returned as the final state) and
+    conv_state a pool [n_slots, C, 3]; sequence n uses row state_slot[n]."""
     _need(x, "x", torch.bfloat16, 2)
     _inner_contig(x, "x")
     _need(conv_w, "conv_w", torch.bfloat16, 2)
     gate_args, Hv = _gate_args(g, beta, a, b, A_log, dt_bias)
+    if state_slot is not None:
+        _need(state_slot, "state_slot", torch.int32, 1)
+        if initial_state is None:
+            raise ValueError("state_slot needs the state pool as initial_state")
+        final_state = initial_state
     _need(norm_w, "norm_w", torch.float32, 1)
     for t, nm in ((conv_w, "conv_w"), (norm_w, "norm_w")):
         if not t.is_contiguous():
@@ -383,7 +391,10 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tenso
         _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
         n_seqs = cu_seqlens.shape[0] - 1
     elif n_seqs is None:
-        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+        if state_slot is not None:
+            n_seqs = state_slot.shape[0]
+        else:
+            n_seqs = initial_state.shape[0] if initial_state is not None else 1
     odt = torch.bfloat16 if out_bf16 else torch.float32
     if out is None:
         out = torch.empty((T, Hv, d), dtype=odt, device=x.device)
@@ -408,6 +419,8 @@ def gdn_mixer_fwd(x: torch.Tensor, conv_w: torch.Tensor, g: Optional[torch.Tenso
     st = lib().gdn_mixer_fwd(_ptr(x), x.stride(0), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
                              *gate_args, _ptr(z2), z2.stride(0), _ptr(norm_w), _ptr(out),
                              1 if out_bf16 else 0, _ptr(initial_state), _ptr(final_state),
+                             _ptr(state_slot),
+                             initial_state.shape[0] if state_slot is not None else 0,
                              _ptr(cu_seqlens), n_seqs, T, Hk, Hv, d, scale, l2_eps, norm_eps,
                              _ptr(workspace), ws_bytes, _stream())
     _check(st, "gdn_mixer_fwd")

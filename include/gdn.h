@@ -60,7 +60,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -234,6 +234,12 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  *   out         [T_total, Hv, d] fp32 (out_is_bf16 == 0) or bf16, contiguous;
  *               overlaps no other buffer
  *   initial_state, final_state, cu_seqlens, n_seqs, scale: as gdn_chunk_fwd
+ *   state_slot  [n_seqs] int32 device array or NULL.  With it, states and conv
+ *               windows are pools of n_slots rows updated in place (serving):
+ *               initial_state == final_state = [n_slots, Hv, d, d] and
+ *               conv_state [n_slots, C, 3]; sequence n uses row
+ *               state_slot[n] of both (distinct, in [0, n_slots), not checked
+ *               on the device), other rows are not touched
  *   l2_eps, norm_eps  the L2 and RMS epsilons (finite, >= 0)
  *   workspace   gdn_mixer_fwd_workspace_bytes() bytes, 256-byte aligned: the
  *               prefill workspace, v after the conv (T_total x Hv x d bf16)
@@ -252,6 +258,7 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
                          const uint16_t* z, int64_t z_stride,
                          const float* norm_w, void* out, int32_t out_is_bf16,
                          const float* initial_state, float* final_state,
+                         const int32_t* state_slot, int32_t n_slots,
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t d, float scale, float l2_eps, float norm_eps,
                          void* workspace, size_t workspace_bytes, void* stream);

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -206,11 +206,13 @@ def test_mixer_fwd_validation(lib):
     def mix(**kw):
         a = dict(x=P(0), xs=10240, w=P(1), bias=None, cs=None, g=P(2), b=P(3), pa=None, pas=48,
                  pb=None, pbs=48, A=None, dt=None, z=P(4), zs=6144, nw=P(5), out=P(6), bf=0,
-                 h0=None, hT=P(7), cu=None, N=1, T=128, d=128, ws=P(9), wsb=1 << 30)
+                 h0=None, hT=P(7), slot=None, nslots=0, cu=None, N=1, T=128, d=128, ws=P(9),
+                 wsb=1 << 30)
         a.update(kw)
         return lib.gdn_mixer_fwd(a["x"], a["xs"], a["w"], a["bias"], a["cs"], a["g"], a["b"],
                                  a["pa"], a["pas"], a["pb"], a["pbs"], a["A"], a["dt"],
                                  a["z"], a["zs"], a["nw"], a["out"], a["bf"], a["h0"], a["hT"],
+                                 a["slot"], a["nslots"],
                                  a["cu"], a["N"], a["T"], 16, 48, a["d"], 1.0, 1e-6, 1e-6,
                                  a["ws"], a["wsb"], None)
     assert mix(z=None) == NULL
@@ -228,6 +230,9 @@ def test_mixer_fwd_validation(lib):
     assert mix(**dict(proj, A=None)) == NULL           # incomplete projections
     assert mix(**dict(proj, pbs=47)) == SHAPE          # b's stride below Hv
     assert mix(**dict(proj, pa=P(7))) == ALIAS         # a inside the final state
+    assert mix(slot=P(8), nslots=4, h0=P(7), hT=P(7) + 1024 * 1024) == SHAPE  # not one pool
+    assert mix(slot=P(8) + 2, nslots=4, h0=P(7), hT=P(7)) == SHAPE       # misaligned slot map
+    assert mix(slot=P(7) + 64, nslots=4, h0=P(7), hT=P(7)) == ALIAS      # slot map inside the pool
 
 
 def test_conv_validation(lib):

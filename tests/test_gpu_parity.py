@@ -465,6 +465,34 @@ def test_mixer_fwd_gates_from_projections():
     assert_close(host(h1), rT, "final_state")
 
 
+def test_mixer_fwd_with_state_pools():
+    """gdn_mixer_fwd over pools of states and conv windows (slot map, in place)
+    equals the call on the gathered rows, scattered back, bit for bit; pool
+    rows no sequence names are untouched."""
+    lens, Hk, Hv, n_slots = [90, 0, 1, 70], 2, 6, 7
+    T, N = sum(lens), len(lens)
+    log(f"mixer_fwd with state pools, lens={lens}")
+    mi = synth.mixer_inputs(3800, T, Hk=Hk, Hv=Hv, conv_state_seqs=n_slots)
+    pool = (0.05 * np.random.default_rng(39).standard_normal((n_slots, Hv, 128, 128))).astype(np.float32)
+    slots = np.array([5, 0, 3, 6], dtype=np.int32)
+    cu = dev_i32(synth.cu_from_lengths(lens))
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    g, b = dev_f32(mi.g), dev_f32(mi.beta)
+    cs_pool, st_pool = dev_bf16(mi.conv_state), dev_f32(pool)
+    out1, _ = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=Hk, conv_state=cs_pool, initial_state=st_pool,
+                                state_slot=dev_i32(slots), cu_seqlens=cu)
+    cs_g, st_g = dev_bf16(mi.conv_state[slots]), dev_f32(pool[slots])
+    out2, hT = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=Hk, conv_state=cs_g, initial_state=st_g,
+                                 cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    idx = torch.from_numpy(slots.astype(np.int64)).cuda()
+    assert torch.equal(st_pool[idx], hT) and torch.equal(cs_pool[idx], cs_g)
+    others = [i for i in range(n_slots) if i not in slots]
+    np.testing.assert_array_equal(host(st_pool)[others], pool[others])
+    assert torch.equal(cs_pool[others], dev_bf16(mi.conv_state)[others])
+
+
 def test_mixer_fwd_against_oracle():
     """The fused mixer against the oracle's conv -> recurrence -> gated norm,
     varlen with conv states, initial states and an empty sequence."""
