@@ -662,4 +662,83 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
                     "gdn_gated_rmsnorm launch");
 }
 
+size_t gdn_backward_workspace_bytes(int32_t T_total, int32_t Hv) {
+  if (T_total <= 0 || Hv <= 0) return 0;
+  return gdn::backward_workspace_bytes(T_total, Hv);
+}
+
+gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                        int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                        const float* g, const float* beta, const float* initial_state,
+                        const float* grad_o, const float* grad_final_state,
+                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                        int32_t Hv, int32_t dk, int32_t dv, float scale, float* grad_q,
+                        float* grad_k, float* grad_v, float* grad_g, float* grad_beta,
+                        float* grad_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const char* fn = "gdn_backward";
+  if (T_total > 0 && (!q || !k || !v || !g || !beta || !grad_o || !grad_q || !grad_k || !grad_v ||
+                      !grad_g || !grad_beta))
+    return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta, grad_o and the token gradients are required", fn);
+  if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk)
+    return fail(GDN_ERR_SHAPE, "%s: bad sizes or Hv %% Hk != 0", fn);
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_UNSUPPORTED, "%s: dk = dv = 128 only", fn);
+  if (q_tok_stride < static_cast<int64_t>(Hk) * dk || k_tok_stride < static_cast<int64_t>(Hk) * dk ||
+      v_tok_stride < static_cast<int64_t>(Hv) * dv || q_tok_stride % 8 || k_tok_stride % 8 ||
+      v_tok_stride % 8)
+    return fail(GDN_ERR_SHAPE, "%s: token strides too small or not multiples of 8", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(initial_state, 16) ||
+      !aligned(grad_final_state, 16) || !aligned(grad_initial_state, 16) || !aligned(grad_o, 4) ||
+      !aligned(grad_q, 4) || !aligned(grad_k, 4) || !aligned(grad_v, 4) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(grad_g, 4) || !aligned(grad_beta, 4) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_SHAPE, "%s: misaligned pointer (q, k, v, states: 16 bytes; the rest: 4)", fn);
+  if (!std::isfinite(scale)) return fail(GDN_ERR_SHAPE, "%s: scale must be finite", fn);
+  if (!cu_seqlens) {
+    const gdn_status s = check_equal_split(n_seqs, T_total);
+    if (s) return s;
+  } else if (n_seqs == 0 && T_total != 0) {
+    return fail(GDN_ERR_SHAPE, "%s: T_total > 0 with no sequences", fn);
+  }
+  if (static_cast<int64_t>(n_seqs) * Hv > 0x7fffffffLL)
+    return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
+  const size_t need = gdn_backward_workspace_bytes(T_total, Hv);
+  const int64_t wk = static_cast<int64_t>(Hk) * dk, wv = static_cast<int64_t>(Hv) * dv;
+  const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
+  const Range in_ranges[] = {
+      range_of(q, T_total, q_tok_stride, wk, 2), range_of(k, T_total, k_tok_stride, wk, 2),
+      range_of(v, T_total, v_tok_stride, wv, 2), range_of(g, T_total, Hv, Hv, 4),
+      range_of(beta, T_total, Hv, Hv, 4),        range_of(initial_state, n_seqs, ssz, ssz, 4),
+      range_of(grad_o, T_total, wv, wv, 4),      range_of(grad_final_state, n_seqs, ssz, ssz, 4),
+      range_of(cu_seqlens, 1, 0, static_cast<int64_t>(n_seqs) + 1, 4)};
+  const Range out_ranges[] = {
+      range_of(grad_q, T_total, wk, wk, 4),   range_of(grad_k, T_total, wk, wk, 4),
+      range_of(grad_v, T_total, wv, wv, 4),   range_of(grad_g, T_total, Hv, Hv, 4),
+      range_of(grad_beta, T_total, Hv, Hv, 4), range_of(grad_initial_state, n_seqs, ssz, ssz, 4),
+      range_of(workspace, 1, 0, static_cast<int64_t>(need), 1)};
+  const int n_out = sizeof(out_ranges) / sizeof(out_ranges[0]);
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& r : in_ranges)
+      if (overlap(out_ranges[i], r)) return fail(GDN_ERR_ALIAS, "%s: an output or the workspace overlaps an input", fn);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(out_ranges[i], out_ranges[j]))
+        return fail(GDN_ERR_ALIAS, "%s: outputs (or the workspace) overlap each other", fn);
+  }
+  if (T_total > 0 || (n_seqs > 0 && grad_initial_state)) {
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (!aligned(workspace, 256))
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
+  if (cu_seqlens && env_validate_seqlens()) {
+    const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (s) return s;
+  }
+  return hip_status(gdn::launch_backward(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta,
+                                         initial_state, grad_o, grad_final_state, cu_seqlens,
+                                         n_seqs, T_total, Hk, Hv, scale, grad_q, grad_k, grad_v,
+                                         grad_g, grad_beta, grad_initial_state, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    "gdn_backward launch");
+}
+
 }  // extern "C"

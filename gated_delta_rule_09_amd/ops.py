@@ -53,6 +53,10 @@ _SIGS = {
                                      _i32, _i32, _f32, _f32, _f32, _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
+    "gdn_backward_workspace_bytes": (_sz, [_i32, _i32]),
+    "gdn_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                            _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _sz, _vp]),
 }
 
 _lib_handle = None
@@ -583,3 +587,61 @@ def gdn_validate_cu_seqlens(cu_seqlens: torch.Tensor, T_total: int) -> None:
     st = lib().gdn_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, T_total,
                                        _stream())
     _check(st, "gdn_validate_cu_seqlens")
+
+
+def gdn_backward_workspace_bytes(T_total: int, Hv: int) -> int:
+    return int(lib().gdn_backward_workspace_bytes(T_total, Hv))
+
+
+def gdn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                 beta: torch.Tensor, grad_o: torch.Tensor, *,
+                 initial_state: Optional[torch.Tensor] = None,
+                 grad_final_state: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                 scale: float = 1.0, grad_initial_state: bool = True,
+                 workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of sum(grad_o * o) + sum(grad_final_state * S_T) of the rule.
+
+    Inputs as gdn_chunk_fwd; grad_o [T, Hv, 128] fp32, grad_final_state
+    [N, Hv, 128, 128] fp32 or None.  Returns a dict of fp32 tensors dq, dk
+    [T, Hk, 128], dv [T, Hv, 128], dg, dbeta [T, Hv] and dh0 [N, Hv, 128, 128]
+    (None unless grad_initial_state).  The workspace holds T x Hv x 64 KB.
+    """
+    _qkv_checks(q, k, v)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(grad_o, "grad_o", torch.float32, 3)
+    if not (g.is_contiguous() and beta.is_contiguous() and grad_o.is_contiguous()):
+        raise ValueError("g, beta and grad_o must be contiguous")
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    for t, nm in ((initial_state, "initial_state"), (grad_final_state, "grad_final_state")):
+        if t is not None:
+            _need(t, nm, torch.float32, 4)
+            if not t.is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+    dev = q.device
+    out = dict(dq=torch.empty((T, Hk, dk), dtype=torch.float32, device=dev),
+               dk=torch.empty((T, Hk, dk), dtype=torch.float32, device=dev),
+               dv=torch.empty((T, Hv, dv), dtype=torch.float32, device=dev),
+               dg=torch.empty((T, Hv), dtype=torch.float32, device=dev),
+               dbeta=torch.empty((T, Hv), dtype=torch.float32, device=dev),
+               dh0=(torch.empty((n_seqs, Hv, dv, dk), dtype=torch.float32, device=dev)
+                    if grad_initial_state else None))
+    if workspace is None:
+        need = gdn_backward_workspace_bytes(T, Hv)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().gdn_backward(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                            _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(grad_o),
+                            _ptr(grad_final_state), _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv,
+                            scale, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+                            _ptr(workspace), ws_bytes, _stream())
+    _check(st, "gdn_backward")
+    return out

@@ -116,6 +116,23 @@ def chunk_inputs(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DI
 
 
 @dataclass
+class BackwardSeeds:
+    d_o: np.ndarray             # f32 [T, Hv, d]: gradient of the outputs
+    dhT: Optional[np.ndarray]   # f32 [N, Hv, d, d]: gradient of the final states, or None
+
+
+def backward_seeds(seed: int, T: int, n_seqs: int, Hv: int = HV, d: int = HEAD_DIM,
+                   dhT_std: Optional[float] = 0.05) -> BackwardSeeds:
+    """Upstream gradients for the backward. Draw order: d_o, dhT."""
+    r = rng(seed)
+    d_o = r.standard_normal((T, Hv, d), dtype=np.float32)
+    dhT = None
+    if dhT_std is not None:
+        dhT = r.standard_normal((n_seqs, Hv, d, d), dtype=np.float32) * np.float32(dhT_std)
+    return BackwardSeeds(d_o, dhT)
+
+
+@dataclass
 class GateInputs:
     a: np.ndarray        # uint16 [T, Hv] (bf16 projection of the decay step)
     b: np.ndarray        # uint16 [T, Hv] (bf16 projection of the write strength)

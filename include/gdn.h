@@ -60,7 +60,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -382,6 +382,45 @@ gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint
 gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_stride,
                              const float* w, void* out, int32_t out_is_bf16, int64_t rows,
                              int32_t Hv, int32_t dv, float eps, void* stream);
+
+/*
+ * gdn_backward -- gradients of the rule for training: the derivatives of
+ *     L = sum(grad_o * o) + sum(grad_final_state * S_T)
+ * (o and S_T as gdn_chunk_fwd computes them from the same inputs) with
+ * respect to q, k, v, g, beta and the initial states.  The chain rule is
+ * taken through each token's erase-then-write update of the "Attention Layer
+ * Details" section of the deep-dive page, in reverse token order, in fp32:
+ * one kernel re-runs the recurrence and records the state before every
+ * token in the workspace, a second walks the tokens backwards holding
+ * dL/dS, a third sums dq and dk over the value heads of each key head.
+ * Memory-hungry by design (64 KB of workspace per token and value head), so
+ * meant for training-sized batches, not long-context prefill.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, n_seqs, T_total, sizes
+ *                     as gdn_chunk_fwd (initial_state NULL = zeros)
+ *   grad_o            [T_total, Hv, dv] fp32, contiguous
+ *   grad_final_state  [n_seqs, Hv, dv, dk] fp32 or NULL (= zeros)
+ *   grad_q, grad_k    [T_total, Hk, dk] fp32, contiguous
+ *   grad_v            [T_total, Hv, dv] fp32, contiguous
+ *   grad_g, grad_beta [T_total, Hv] fp32, contiguous (grad_g is dL/dg, g
+ *                     being the log of the decay alpha)
+ *   grad_initial_state [n_seqs, Hv, dv, dk] fp32 or NULL (not written)
+ *   workspace         >= gdn_backward_workspace_bytes(T_total, Hv) bytes,
+ *                     256-byte aligned, contents ignored on entry
+ *
+ * No output may overlap an input, another output or the workspace
+ * (GDN_ERR_ALIAS).  Errors as gdn_chunk_fwd.
+ */
+size_t gdn_backward_workspace_bytes(int32_t T_total, int32_t Hv);
+gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                        int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                        const float* g, const float* beta, const float* initial_state,
+                        const float* grad_o, const float* grad_final_state,
+                        const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
+                        int32_t Hv, int32_t dk, int32_t dv, float scale, float* grad_q,
+                        float* grad_k, float* grad_v, float* grad_g, float* grad_beta,
+                        float* grad_initial_state, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * gdn_validate_cu_seqlens -- opt-in host check of a device cu_seqlens array:

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -233,6 +233,38 @@ def test_mixer_fwd_validation(lib):
     assert mix(slot=P(8), nslots=4, h0=P(7), hT=P(7) + 1024 * 1024) == SHAPE  # not one pool
     assert mix(slot=P(8) + 2, nslots=4, h0=P(7), hT=P(7)) == SHAPE       # misaligned slot map
     assert mix(slot=P(7) + 64, nslots=4, h0=P(7), hT=P(7)) == ALIAS      # slot map inside the pool
+
+
+def backward(lib, **kw):
+    a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), beta=P(4), h0=None,
+             do=P(5), dhT=None, cu=None, N=1, T=64, Hk=16, Hv=48, dk=128, dv=128, scale=1.0,
+             dq=P(6), dkk=P(7), dvv=P(8), dg=P(9), db=P(10), dh0=None, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.gdn_backward(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"], a["beta"],
+                            a["h0"], a["do"], a["dhT"], a["cu"], a["N"], a["T"], a["Hk"], a["Hv"],
+                            a["dk"], a["dv"], a["scale"], a["dq"], a["dkk"], a["dvv"], a["dg"],
+                            a["db"], a["dh0"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_backward_validation(lib):
+    need = lib.gdn_backward_workspace_bytes(64, 48)
+    assert need == 64 * 48 * 128 * 128 * 4 + 2 * 64 * 48 * 128 * 4
+    assert lib.gdn_backward_workspace_bytes(0, 48) == 0
+    assert backward(lib, do=None) == NULL
+    assert backward(lib, dg=None) == NULL
+    assert backward(lib, Hv=40) == SHAPE
+    assert backward(lib, dk=64) == UNSUP
+    assert backward(lib, ks=1000) == SHAPE
+    assert backward(lib, T=65, N=2) == SHAPE
+    assert backward(lib, q=P(0) + 8) == SHAPE
+    assert backward(lib, scale=float("nan")) == SHAPE
+    assert backward(lib) == WS
+    assert backward(lib, ws=P(11), wsb=need - 1) == WS
+    assert backward(lib, ws=P(11) + 64, wsb=need) == WS          # not 256-byte aligned
+    assert backward(lib, dq=P(0) + 4096, ws=P(11), wsb=need) == ALIAS   # output over an input
+    assert backward(lib, dkk=P(6) + 4096, ws=P(11), wsb=need) == ALIAS  # two outputs overlap
+    assert backward(lib, ws=P(10), wsb=need) == ALIAS                   # workspace over an output
 
 
 def test_conv_validation(lib):

@@ -1,0 +1,84 @@
+"""GPU parity of gdn_backward (the rule's gradients) against the fp64
+oracle's backward, itself pinned by central differences and by autograd of
+the fp64 rule on the CPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_09_amd import ops, synth
+from tests.gpu_util import assert_close, dev_bf16, dev_f32, dev_i32, host, log
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _run(ci, bs, scale, Hk):
+    dhT = None if bs.dhT is None else dev_f32(bs.dhT)
+    h0 = None if ci.h0 is None else dev_f32(ci.h0)
+    cu = None if ci.cu_seqlens is None else dev_i32(ci.cu_seqlens)
+    got = ops.gdn_backward(dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g),
+                           dev_f32(ci.beta), dev_f32(bs.d_o), initial_state=h0,
+                           grad_final_state=dhT, cu_seqlens=cu, n_seqs=ci.n_seqs, scale=scale)
+    ref = oracle.backward(synth.bf16_value(ci.q), synth.bf16_value(ci.k), synth.bf16_value(ci.v),
+                          ci.g, ci.beta, bs.d_o, h0=ci.h0, dhT=bs.dhT, cu_seqlens=ci.cu_seqlens,
+                          n_seqs=ci.n_seqs, scale=scale)
+    return {n: host(got[n]) for n in NAMES}, ref
+
+
+def _check(got, ref, tag):
+    for n in NAMES:
+        assert_close(got[n], ref[n], f"{tag} {n}")
+
+
+def test_backward_equal_lengths_with_states():
+    log("backward: 2 x 70 tokens, Hk 2, Hv 6, h0 and dhT")
+    ci = synth.chunk_inputs(7000, 140, Hk=2, Hv=6, lengths=[70, 70], h0_std=0.05)
+    ci.cu_seqlens = None          # equal split without cu_seqlens
+    bs = synth.backward_seeds(7001, 140, 2, Hv=6)
+    got, ref = _run(ci, bs, 128 ** -0.5, 2)
+    _check(got, ref, "equal")
+
+
+def test_backward_varlen_ragged_and_empty_sequences():
+    lens = [70, 0, 1, 64, 129, 5, 0, 200]
+    log(f"backward: varlen {lens}, Hk 2, Hv 4, zero h0 and dhT")
+    ci = synth.chunk_inputs(7100, sum(lens), Hk=2, Hv=4, lengths=lens)
+    bs = synth.backward_seeds(7101, sum(lens), len(lens), Hv=4, dhT_std=None)
+    got, ref = _run(ci, bs, 1.0, 2)
+    _check(got, ref, "varlen")
+    assert np.all(got["dh0"][1] == 0) and np.all(got["dh0"][6] == 0)
+
+
+def test_backward_full_head_layout():
+    log("backward: T 96, Hk 16, Hv 48")
+    ci = synth.chunk_inputs(7200, 96, h0_std=0.02)
+    bs = synth.backward_seeds(7201, 96, 1)
+    got, ref = _run(ci, bs, 128 ** -0.5, 16)
+    _check(got, ref, "full heads")
+
+
+def test_backward_no_tokens_passes_state_gradient_through():
+    log("backward: no tokens, dh0 = dhT")
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    zv = torch.empty((0, 6, 128), dtype=torch.bfloat16, device="cuda")
+    zg = torch.empty((0, 6), dtype=torch.float32, device="cuda")
+    zo = torch.empty((0, 6, 128), dtype=torch.float32, device="cuda")
+    dhT = torch.randn((2, 6, 128, 128), device="cuda")
+    out = ops.gdn_backward(z, z, zv, zg, zg, zo, grad_final_state=dhT,
+                           cu_seqlens=torch.zeros(3, dtype=torch.int32, device="cuda"))
+    assert torch.equal(out["dh0"], dhT) and out["dq"].shape[0] == 0
+
+
+def test_backward_is_deterministic():
+    log("backward: determinism")
+    ci = synth.chunk_inputs(7300, 100, Hk=2, Hv=6, h0_std=0.05)
+    bs = synth.backward_seeds(7301, 100, 1, Hv=6)
+    args = (dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g), dev_f32(ci.beta),
+            dev_f32(bs.d_o))
+    kw = dict(initial_state=dev_f32(ci.h0), grad_final_state=dev_f32(bs.dhT))
+    a = ops.gdn_backward(*args, **kw)
+    b = ops.gdn_backward(*args, **kw)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
