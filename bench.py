@@ -29,7 +29,8 @@ host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,...]
 (`--legs copy` adds a plain 1 GiB device copy, the calibration kernel for the
-HBM byte counters.)
+HBM byte counters; `--legs backward` times gdn_backward on 8 sequences of 1024
+tokens, whose state record takes 26 GB of workspace.)
 """
 import argparse
 import hashlib
@@ -266,6 +267,38 @@ def leg_varlen(args, ops, synth, torch):
     return res
 
 
+def leg_backward(args, ops, synth, torch):
+    """gdn_backward over a training-shaped batch: 8 sequences of 1024 tokens."""
+    N, L = 8, 1024
+    T = N * L
+    log(f"[backward] drawing inputs T={T} N={N}")
+    ci = synth.chunk_inputs_torch(1008, T, lengths=[L] * N, h0_std=0.02)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1009)
+    d_o = torch.randn((T, HV, D), device="cuda", generator=gen)
+    dhT = torch.randn((N, HV, D, D), device="cuda", generator=gen) * 0.05
+    ws = torch.empty(ops.gdn_backward_workspace_bytes(T, HV), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], d_o,
+                         initial_state=ci["h0"], grad_final_state=dhT,
+                         cu_seqlens=ci["cu_seqlens"], workspace=ws)
+
+    ev, wall = time_leg(step, max(2, args.steps // 4), 1)
+    # algorithmic bytes: q, k, v, g, beta and d_o in; dq, dk, dv, dg, dbeta out;
+    # h0, dhT in and dh0 out
+    per_tok = HK * D * 2 * 2 + HV * D * 2 + HV * 4 * 2 + HV * D * 4 + HK * D * 4 * 2 + HV * D * 4 \
+        + HV * 4 * 2
+    alg = T * per_tok + 3 * N * STATE_BYTES
+    recorded = 2 * T * STATE_BYTES          # the per-token state record, written and read once
+    res = dict(tokens=T, n_seqs=N, event_ms=ev, wall_ms=wall, tokens_per_s=T / (ev * 1e-3),
+               alg_gbps=alg / (ev * 1e-3) / 1e9,
+               with_record_gbps=(alg + recorded) / (ev * 1e-3) / 1e9)
+    log(f"[backward] {ev:.3f} ms/call, {res['tokens_per_s'] / 1e6:.3f} M tok/s, "
+        f"{res['with_record_gbps']:.0f} GB/s counting the state record")
+    return res
+
+
 def leg_copy(args, torch):
     """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30
     bytes each, the reference for scaling the HBM byte counters."""
@@ -364,6 +397,8 @@ def main():
         out["mixer"] = leg_mixer(args, ops, synth, torch)
     if "varlen" in legs:
         out["varlen"] = leg_varlen(args, ops, synth, torch)
+    if "backward" in legs:
+        out["backward"] = leg_backward(args, ops, synth, torch)
     if "copy" in legs:
         out["copy"] = leg_copy(args, torch)
 
@@ -421,6 +456,11 @@ def main():
                                     "ms": round(vl["event_ms"], 4),
                                     "hbm_frac": round(vl["hbm_gbps"] / HBM_PEAK_GBPS, 4),
                                     "mfma_frac": round(vl["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+    if "backward" in out:
+        bw = out["backward"]
+        line["backward_8x1024"] = {"ms": round(bw["event_ms"], 4),
+                                   "tokens_per_s": round(bw["tokens_per_s"], 1),
+                                   "GBps_with_state_record": round(bw["with_record_gbps"], 1)}
     if ci is not None and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds, torch)
     print(json.dumps(line), flush=True)

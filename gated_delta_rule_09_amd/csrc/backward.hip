@@ -52,16 +52,11 @@ __device__ __forceinline__ void seq_range(const BwdParams& p, int n, int& s0, in
   else { s0 = n * p.seq_len; s1 = s0 + p.seq_len; }
 }
 
-// this lane's 16 key channels of a bf16 head row
-__device__ __forceinline__ void load_cols(const uint16_t* row, int lp, float (&x)[16]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint2 b = *reinterpret_cast<const uint2*>(row + 4 * (lp + 8 * j));
-    x[4 * j + 0] = __uint_as_float(b.x << 16);
-    x[4 * j + 1] = __uint_as_float(b.x & 0xffff0000u);
-    x[4 * j + 2] = __uint_as_float(b.y << 16);
-    x[4 * j + 3] = __uint_as_float(b.y & 0xffff0000u);
-  }
+// a if the lane's mask m is all ones, b if it is zero; a bitwise blend of two
+// loaded values, so that the compiler cannot turn a choice between two
+// register arrays into an indexed (scratch) access
+__device__ __forceinline__ float blend(unsigned m, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
 }
 
 __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
@@ -81,6 +76,20 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * j + i] = x[i];
   }
+  // the next token's k row share, gates and v element are in flight while
+  // the current token is applied
+  uint2 kn[4] = {};
+  float gn = 0.f, bn = 0.f;
+  uint16_t vn = 0;
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      kn[j] = *reinterpret_cast<const uint2*>(p.k + static_cast<int64_t>(t) * p.ks + kh * kD + 4 * (lp + 8 * j));
+    gn = p.g[static_cast<int64_t>(t) * p.Hv + h];
+    bn = p.beta[static_cast<int64_t>(t) * p.Hv + h];
+    vn = p.v[static_cast<int64_t>(t) * p.vs + h * kD + row];
+  };
+  if (s1 > s0) fetch(s0);
   for (int t = s0; t < s1; ++t) {
     float* dst = p.dump + ((static_cast<int64_t>(t) * p.Hv + h) * kD + row) * kD;
 #pragma unroll
@@ -88,10 +97,17 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
       __builtin_nontemporal_store(floatx4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]},
                                   reinterpret_cast<floatx4*>(dst + 4 * (lp + 8 * j)));
     float kk[16];
-    load_cols(p.k + static_cast<int64_t>(t) * p.ks + kh * kD, lp, kk);
-    const float a = expf(p.g[static_cast<int64_t>(t) * p.Hv + h]);
-    const float b = p.beta[static_cast<int64_t>(t) * p.Hv + h];
-    const float vv = bf16_to_f32(p.v[static_cast<int64_t>(t) * p.vs + h * kD + row]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kk[4 * j + 0] = __uint_as_float(kn[j].x << 16);
+      kk[4 * j + 1] = __uint_as_float(kn[j].x & 0xffff0000u);
+      kk[4 * j + 2] = __uint_as_float(kn[j].y << 16);
+      kk[4 * j + 3] = __uint_as_float(kn[j].y & 0xffff0000u);
+    }
+    const float a = expf(gn);
+    const float b = bn;
+    const float vv = bf16_to_f32(vn);
+    if (t + 1 < s1) fetch(t + 1);
     float sk = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sk = fmaf(s[e], kk[e], sk);
@@ -102,9 +118,46 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
   }
 }
 
+// What one lane of the reverse walk reads for one token; the next token's
+// copy is in flight while the current one is processed.  k and q, shared by
+// all rows, travel through a double-buffered LDS stage instead.
+struct RevToken {
+  floatx4 s[4];     // this lane's 16 columns of the recorded state row
+  float g, beta, dout;
+  uint16_t v;
+};
+
+__device__ __forceinline__ void rev_load(const BwdParams& p, int t, int h, int kh, int row, int lp,
+                                         RevToken& x) {
+  const int64_t th = static_cast<int64_t>(t) * p.Hv + h;
+  const float* src = p.dump + (th * kD + row) * kD;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x.s[j] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4 * (lp + 8 * j)));
+  }
+  x.g = p.g[th];
+  x.beta = p.beta[th];
+  x.dout = p.d_o[th * kD + row];
+  x.v = p.v[static_cast<int64_t>(t) * p.vs + h * kD + row];
+}
+
+// wave 0's share of a token's k (lanes 0..31) and q (lanes 32..63): 4 bf16
+__device__ __forceinline__ uint2 kq_load(const BwdParams& p, int t, int kh, int lane) {
+  const uint16_t* base = lane < 32 ? p.k + static_cast<int64_t>(t) * p.ks
+                                   : p.q + static_cast<int64_t>(t) * p.qs;
+  return *reinterpret_cast<const uint2*>(base + kh * kD + 4 * (lane & 31));
+}
+
+__device__ __forceinline__ void kq_store(float (*buf)[kD], int lane, uint2 b) {
+  *reinterpret_cast<floatx4*>(&buf[lane >> 5][4 * (lane & 31)]) =
+      floatx4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+              __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
+}
+
 __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
-  __shared__ float part[kWaves][2][kD];   // per-wave column sums: dq_h, dk_h
+  __shared__ __align__(16) float part[kWaves][2][kD];   // per-wave column sums: dq_h, dk_h
   __shared__ float spart[kWaves][2];      // per-wave sums: <S_prev, dSh>, dbeta
+  __shared__ __align__(16) float kq[2][2][kD];          // k, q of a token, by token parity
   const int n = blockIdx.x / p.Hv;
   const int h = blockIdx.x - n * p.Hv;
   const int kh = h / (p.Hv / p.Hk);
@@ -123,22 +176,36 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) D[4 * j + i] = x[i];
   }
+  RevToken nxt;
+  if (s1 > s0) {
+    rev_load(p, s1 - 1, h, kh, row, lp, nxt);
+    if (w == 0) kq_store(kq[(s1 - 1) & 1], lane, kq_load(p, s1 - 1, kh, lane));
+  }
+  __syncthreads();
   for (int t = s1 - 1; t >= s0; --t) {
     const int64_t th = static_cast<int64_t>(t) * p.Hv + h;
+    const RevToken cur = nxt;
+    uint2 kq_next = {0u, 0u};
+    if (t > s0) {   // the next token's inputs are in flight during this one
+      rev_load(p, t - 1, h, kh, row, lp, nxt);
+      if (w == 0) kq_next = kq_load(p, t - 1, kh, lane);
+    }
     float Sp[16], kk[16], qq[16];
-    const float* src = p.dump + (th * kD + row) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const floatx4 x = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4 * (lp + 8 * j)));
+      const floatx4 kx = *reinterpret_cast<const floatx4*>(&kq[t & 1][0][4 * (lp + 8 * j)]);
+      const floatx4 qx = *reinterpret_cast<const floatx4*>(&kq[t & 1][1][4 * (lp + 8 * j)]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sp[4 * j + i] = x[i];
+      for (int i = 0; i < 4; ++i) {
+        Sp[4 * j + i] = cur.s[j][i];
+        kk[4 * j + i] = kx[i];
+        qq[4 * j + i] = qx[i];
+      }
     }
-    load_cols(p.k + static_cast<int64_t>(t) * p.ks + kh * kD, lp, kk);
-    load_cols(p.q + static_cast<int64_t>(t) * p.qs + kh * kD, lp, qq);
-    const float a = expf(p.g[th]);
-    const float b = p.beta[th];
-    const float vv = bf16_to_f32(p.v[static_cast<int64_t>(t) * p.vs + h * kD + row]);
-    const float dout = p.d_o[th * kD + row];
+    const float a = expf(cur.g);
+    const float b = cur.beta;
+    const float vv = bf16_to_f32(cur.v);
+    const float dout = cur.dout;
     // the forward step, recomputed
     float sk = 0.f;
 #pragma unroll
@@ -169,33 +236,45 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
     }
     if (lp == 0) p.dv[th * kD + row] = b * du;
     float bdot = lp == 0 ? (vv - pk) * du : 0.f;
-    // column sums over the wave's eight rows (lanes lp, lp + 8, ..., lp + 56)
+    // Column sums over the wave's eight rows (lanes lp, lp + 8, ..., lp + 56)
+    // by a butterfly reduce-scatter over lane bits 5, 4, 3: each exchange
+    // sends half of the remaining values to the partner lane and keeps the
+    // other half, so lane (b5 b4 b3, lp) ends with the four sums of values
+    // j = 16 b5 + 8 b4 + 4 b3 + i (j < 16: cq[j], else ck[j - 16]), i.e. the
+    // float4 of columns 4 (lp + 8 (2 b4 + b3)) .. + 3 of dq_h (b5 = 0) or
+    // dk_h (b5 = 1).  16 + 8 permutes and a DPP step instead of 96 permutes.
+    const unsigned m5 = (lane & 32) ? ~0u : 0u, m4 = (lane & 16) ? ~0u : 0u, m3 = (lane & 8) ? ~0u : 0u;
+    float y[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int i = 0; i < 16; ++i) y[i] = __shfl_xor(blend(m5, cq[i], ck[i]), 32, 64);
 #pragma unroll
-      for (int d = 8; d < 64; d <<= 1) {
-        cq[e] += __shfl_xor(cq[e], d, 64);
-        ck[e] += __shfl_xor(ck[e], d, 64);
-      }
-    }
+    for (int i = 0; i < 16; ++i) y[i] += blend(m5, ck[i], cq[i]);
+    float z[8];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      gdot += __shfl_xor(gdot, d, 64);
-      bdot += __shfl_xor(bdot, d, 64);
-    }
-    if (lane < 8) {
+    for (int i = 0; i < 8; ++i) z[i] = __shfl_xor(blend(m4, y[i], y[8 + i]), 16, 64);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 8; ++i) z[i] += blend(m4, y[8 + i], y[i]);
+    floatx4 r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          part[w][0][4 * (lp + 8 * j) + i] = cq[4 * j + i];
-          part[w][1][4 * (lp + 8 * j) + i] = ck[4 * j + i];
-        }
-    }
+    for (int i = 0; i < 4; ++i)   // DPP row_ror:8 reads lane ^ 8 inside each row of 16
+      r[i] = blend(m3, z[4 + i], z[i]) + dpp<0x128>(blend(m3, z[i], z[4 + i]));
+    *reinterpret_cast<floatx4*>(&part[w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
+    // <S_prev, dSh> and dbeta over the wave: the eight lanes of a row by DPP,
+    // then the eight rows
+    gdot = sum8(gdot);
+    bdot = sum8(bdot);
+    gdot += dpp<0x128>(gdot);
+    bdot += dpp<0x128>(bdot);
+    gdot += __shfl_xor(gdot, 16, 64);
+    bdot += __shfl_xor(bdot, 16, 64);
+    gdot += __shfl_xor(gdot, 32, 64);
+    bdot += __shfl_xor(bdot, 32, 64);
     if (lane == 0) {
       spart[w][0] = gdot;
       spart[w][1] = bdot;
     }
+    // buffer (t - 1) & 1 was last read by token t + 1, before its final barrier
+    if (w == 0 && t > s0) kq_store(kq[(t - 1) & 1], lane, kq_next);
     __syncthreads();
     if (tid < 2 * kD) {
       const int which = tid >> 7, c = tid & (kD - 1);
