@@ -273,10 +273,8 @@ def leg_backward(args, ops, synth, torch):
     T = N * L
     log(f"[backward] drawing inputs T={T} N={N}")
     ci = synth.chunk_inputs_torch(1008, T, lengths=[L] * N, h0_std=0.02)
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1009)
-    d_o = torch.randn((T, HV, D), device="cuda", generator=gen)
-    dhT = torch.randn((N, HV, D, D), device="cuda", generator=gen) * 0.05
+    bs = synth.backward_seeds_torch(1009, T, N)
+    d_o, dhT = bs["d_o"], bs["dhT"]
     ws = torch.empty(ops.gdn_backward_workspace_bytes(T, HV), dtype=torch.uint8, device="cuda")
 
     def step():

@@ -155,9 +155,13 @@ __device__ __forceinline__ void kq_store(float (*buf)[kD], int lane, uint2 b) {
 }
 
 __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
-  __shared__ __align__(16) float part[kWaves][2][kD];   // per-wave column sums: dq_h, dk_h
-  __shared__ float spart[kWaves][2];      // per-wave sums: <S_prev, dSh>, dbeta
-  __shared__ __align__(16) float kq[2][2][kD];          // k, q of a token, by token parity
+  // All three are double-buffered by token parity, so one barrier per token
+  // suffices: a buffer written by token t (before its barrier) is next written
+  // by token t - 2, after every thread has passed token t - 1's barrier, which
+  // each reader of token t's copy reaches only after its reads.
+  __shared__ __align__(16) float part[2][kWaves][2][kD];   // per-wave column sums: dq_h, dk_h
+  __shared__ float spart[2][kWaves][2];      // per-wave sums: <S_prev, dSh>, dbeta
+  __shared__ __align__(16) float kq[2][2][kD];             // k, q of a token
   const int n = blockIdx.x / p.Hv;
   const int h = blockIdx.x - n * p.Hv;
   const int kh = h / (p.Hv / p.Hk);
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)   // DPP row_ror:8 reads lane ^ 8 inside each row of 16
       r[i] = blend(m3, z[4 + i], z[i]) + dpp<0x128>(blend(m3, z[i], z[4 + i]));
-    *reinterpret_cast<floatx4*>(&part[w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
+    *reinterpret_cast<floatx4*>(&part[t & 1][w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
     // <S_prev, dSh> and dbeta over the wave: the eight lanes of a row by DPP,
     // then the eight rows
     gdot = sum8(gdot);
@@ -270,29 +274,28 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
     gdot += __shfl_xor(gdot, 32, 64);
     bdot += __shfl_xor(bdot, 32, 64);
     if (lane == 0) {
-      spart[w][0] = gdot;
-      spart[w][1] = bdot;
+      spart[t & 1][w][0] = gdot;
+      spart[t & 1][w][1] = bdot;
     }
-    // buffer (t - 1) & 1 was last read by token t + 1, before its final barrier
+    // buffer (t - 1) & 1 was last read by token t + 1, before its barrier
     if (w == 0 && t > s0) kq_store(kq[(t - 1) & 1], lane, kq_next);
     __syncthreads();
     if (tid < 2 * kD) {
       const int which = tid >> 7, c = tid & (kD - 1);
       float acc = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) acc += part[ww][which][c];
+      for (int ww = 0; ww < kWaves; ++ww) acc += part[t & 1][ww][which][c];
       (which ? p.dk_part : p.dq_part)[th * kD + c] = acc;
     } else if (tid == 2 * kD) {
       float gs = 0.f, bs = 0.f;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        gs += spart[ww][0];
-        bs += spart[ww][1];
+        gs += spart[t & 1][ww][0];
+        bs += spart[t & 1][ww][1];
       }
       p.dg[th] = a * gs;
       p.dbeta[th] = bs;
     }
-    __syncthreads();   // part and spart are rewritten by the next token
   }
   if (p.dh0) {
 #pragma unroll

@@ -254,6 +254,17 @@ def chunk_inputs_torch(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = H
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, n_seqs=n)
 
 
+def backward_seeds_torch(seed: int, T: int, n_seqs: int, Hv: int = HV, d: int = HEAD_DIM,
+                         dhT_std: float = 0.05, device="cuda"):
+    """dict of device tensors d_o [T, Hv, d], dhT [n_seqs, Hv, d, d] (fp32), the
+    distributions of backward_seeds."""
+    import torch
+    gen = _tgen(seed, device)
+    d_o = torch.randn((T, Hv, d), generator=gen, device=device, dtype=torch.float32)
+    dhT = torch.randn((n_seqs, Hv, d, d), generator=gen, device=device, dtype=torch.float32) * dhT_std
+    return dict(d_o=d_o, dhT=dhT)
+
+
 def mixer_inputs_torch(seed: int, T: int, Hk: int = HK, Hv: int = HV, d: int = HEAD_DIM,
                        device="cuda"):
     import torch

@@ -227,3 +227,34 @@ def test_full_varlen_262144_sampled_pairs():
                                    h0_all[n:n + 1, h:h + 1])
         assert_close(host(o[a:b, h:h + 1]), ro, "o")
         assert_close(host(fs[n:n + 1, h:h + 1]), rT, "final_state")
+
+
+def test_full_backward_8x1024_sampled_groups():
+    """gdn_backward on the benchmark's backward batch (8 sequences x 1024
+    tokens, all 48 value heads, h0 and dS_T given): for sampled (sequence, key
+    head) pairs, dq, dk of the key head and dv, dg, dbeta, dh0 of its three
+    value heads against the oracle run on that slice alone."""
+    N, L = 8, 1024
+    T = N * L
+    log(f"full backward {N} x {L} tokens (benchmark inputs, seeds 1008/1009)")
+    ci = synth.chunk_inputs_torch(1008, T, lengths=[L] * N, h0_std=0.02)
+    bs = synth.backward_seeds_torch(1009, T, N)
+    got = ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], bs["d_o"],
+                           initial_state=ci["h0"], grad_final_state=bs["dhT"],
+                           cu_seqlens=ci["cu_seqlens"])
+    torch.cuda.synchronize()
+    for n, kh in ((0, 3), (5, 14)):
+        t0, t1 = n * L, (n + 1) * L
+        hs = slice(kh * GROUP, (kh + 1) * GROUP)
+        log(f"  oracle: sequence {n}, key head {kh}")
+        ref = oracle.backward(bits(ci["q"][t0:t1, kh:kh + 1]), bits(ci["k"][t0:t1, kh:kh + 1]),
+                              bits(ci["v"][t0:t1, hs]), f32(ci["g"][t0:t1, hs]),
+                              f32(ci["beta"][t0:t1, hs]), f32(bs["d_o"][t0:t1, hs]),
+                              h0=f32(ci["h0"][n:n + 1, hs]), dhT=f32(bs["dhT"][n:n + 1, hs]))
+        tag = f"seq {n} kh {kh}"
+        assert_close(host(got["dq"][t0:t1, kh:kh + 1]), ref["dq"], f"{tag} dq")
+        assert_close(host(got["dk"][t0:t1, kh:kh + 1]), ref["dk"], f"{tag} dk")
+        assert_close(host(got["dv"][t0:t1, hs]), ref["dv"], f"{tag} dv")
+        assert_close(host(got["dg"][t0:t1, hs]), ref["dg"], f"{tag} dg")
+        assert_close(host(got["dbeta"][t0:t1, hs]), ref["dbeta"], f"{tag} dbeta")
+        assert_close(host(got["dh0"][n:n + 1, hs]), ref["dh0"], f"{tag} dh0")
