@@ -662,9 +662,9 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
                     "gdn_gated_rmsnorm launch");
 }
 
-size_t gdn_backward_workspace_bytes(int32_t T_total, int32_t Hv) {
-  if (T_total <= 0 || Hv <= 0) return 0;
-  return gdn::backward_workspace_bytes(T_total, Hv);
+size_t gdn_backward_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hv) {
+  if (n_seqs <= 0 || T_total <= 0 || Hv <= 0) return 0;
+  return gdn::backward_workspace_bytes(n_seqs, T_total, Hv);
 }
 
 gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
@@ -701,7 +701,7 @@ gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t*
   }
   if (static_cast<int64_t>(n_seqs) * Hv > 0x7fffffffLL)
     return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
-  const size_t need = gdn_backward_workspace_bytes(T_total, Hv);
+  const size_t need = gdn_backward_workspace_bytes(n_seqs, T_total, Hv);
   const int64_t wk = static_cast<int64_t>(Hk) * dk, wv = static_cast<int64_t>(Hv) * dv;
   const int64_t ssz = static_cast<int64_t>(Hv) * dv * dk;
   const Range in_ranges[] = {

@@ -4,23 +4,24 @@
 // "Delta-rule layers" row of the model card's Architecture table,
 //     S <- a S + b (v - a S k) k^T,   o = scale S q,   a = exp(g).
 //
-// A plain per-token design, separate from the inference kernels:
+// A per-token design with checkpoints, separate from the inference kernels.
 // backward_fwd_kernel runs the recurrence and records the state before every
-// token (T x Hv x 64 KB of workspace); backward_rev_kernel walks the tokens
-// in reverse with D = dL/dS in registers and takes the chain rule through one
-// token's operations (S_prev read back from the record):
+// kSeg-th token of each sequence (the segment starts).  backward_rev_kernel
+// walks the segments of a sequence in reverse with D = dL/dS in registers: it
+// stages a segment's k, q, v, dO and gates in LDS, and for each of its tokens,
+// last first, rebuilds the state before that token from the segment's
+// checkpoint (up to kSeg - 1 forward steps, cheap next to a 64 KB record read)
+// and takes the chain rule through the token's operations:
 //     p = a S_prev k,  u = b (v - p),  S = a S_prev + u k^T
 //     D  += scale do q^T                dq_h += scale S^T do
 //     du  = D k                         dk_h += D^T u
 //     dv  = b du                        dbeta = (v - p) . du
 //     dSh = D - b du k^T                dk_h += a S_prev^T (-b du)
 //     dg  = a <S_prev, dSh>             D    = a dSh
-// and backward_sum_kernel adds the value heads' dq_h, dk_h into their key
+// backward_sum_kernel then adds the value heads' dq_h, dk_h into their key
 // head's dq, dk.  Both per-token kernels use one 1024-thread work-group per
-// (sequence, value head) with the decode step's layout: eight lanes per
-// state row, lane p holding the float4 columns p, p+8, p+16, p+24.  The
-// column sums over the 128 rows (dq_h, dk_h) go through lane shuffles inside
-// each wave, then LDS across the 16 waves.
+// (sequence, value head) with the decode step's layout: eight lanes per state
+// row, lane p holding the float4 columns p, p+8, p+16, p+24.
 #include "common.h"
 #include "launch.h"
 
@@ -31,6 +32,8 @@ namespace {
 constexpr int kD = 128;
 constexpr int kTh = 1024;
 constexpr int kWaves = kTh / 64;
+constexpr int kSeg = 8;   // tokens per checkpoint segment
+static_assert(kSeg * kD == kTh, "one staged element per thread");
 
 struct BwdParams {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
@@ -40,7 +43,7 @@ struct BwdParams {
   const float* d_o;           // [T, Hv, 128]
   const float* dhT;           // gradient of the final states or nullptr
   const int32_t* cu;          // nullptr: equal lengths seq_len
-  float* dump;                // [T, Hv, 128, 128]: the state before each token
+  float* ckpt;                // [T / kSeg + n_seqs, Hv, 128, 128]: states at segment starts
   float* dq_part; float* dk_part;   // [T, Hv, 128] per value head
   float* dv; float* dg; float* dbeta; float* dh0;
   int n_seqs, seq_len, Hk, Hv;
@@ -50,6 +53,13 @@ struct BwdParams {
 __device__ __forceinline__ void seq_range(const BwdParams& p, int n, int& s0, int& s1) {
   if (p.cu) { s0 = p.cu[n]; s1 = p.cu[n + 1]; }
   else { s0 = n * p.seq_len; s1 = s0 + p.seq_len; }
+}
+
+// Record slot of the checkpoint at token t (a segment start) of sequence n:
+// t / kSeg + n grows by one per segment inside a sequence and jumps by at
+// least one between sequences, so slots are distinct and below T / kSeg + N.
+__device__ __forceinline__ int64_t ckpt_row(const BwdParams& p, int t, int n, int h, int row) {
+  return ((static_cast<int64_t>(t / kSeg + n) * p.Hv + h) * kD + row) * kD;
 }
 
 // a if the lane's mask m is all ones, b if it is zero; a bitwise blend of two
@@ -91,11 +101,13 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
   };
   if (s1 > s0) fetch(s0);
   for (int t = s0; t < s1; ++t) {
-    float* dst = p.dump + ((static_cast<int64_t>(t) * p.Hv + h) * kD + row) * kD;
+    if ((t - s0) % kSeg == 0) {
+      float* dst = p.ckpt + ckpt_row(p, t, n, h, row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_nontemporal_store(floatx4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]},
-                                  reinterpret_cast<floatx4*>(dst + 4 * (lp + 8 * j)));
+      for (int j = 0; j < 4; ++j)
+        __builtin_nontemporal_store(floatx4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]},
+                                    reinterpret_cast<floatx4*>(dst + 4 * (lp + 8 * j)));
+    }
     float kk[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -118,50 +130,70 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
   }
 }
 
-// What one lane of the reverse walk reads for one token; the next token's
-// copy is in flight while the current one is processed.  k and q, shared by
-// all rows, travel through a double-buffered LDS stage instead.
-struct RevToken {
-  floatx4 s[4];     // this lane's 16 columns of the recorded state row
-  float g, beta, dout;
-  uint16_t v;
+// A segment's inputs in LDS: token i of the segment, channel c.
+struct SegStage {
+  float k[kSeg][kD], q[kSeg][kD], v[kSeg][kD], d_o[kSeg][kD];
+  float a[kSeg], beta[kSeg];
 };
 
-__device__ __forceinline__ void rev_load(const BwdParams& p, int t, int h, int kh, int row, int lp,
-                                         RevToken& x) {
-  const int64_t th = static_cast<int64_t>(t) * p.Hv + h;
-  const float* src = p.dump + (th * kD + row) * kD;
+// What thread (i = tid / 128, c = tid % 128) loads of a segment: token c0 + i.
+struct SegLoad {
+  uint16_t k, q, v;
+  float d_o, g, beta;
+};
+
+__device__ __forceinline__ void seg_load(const BwdParams& p, int c0, int len, int h, int kh, int tid,
+                                         SegLoad& x) {
+  const int i = tid >> 7, c = tid & (kD - 1);
+  if (i >= len) return;
+  const int64_t t = c0 + i;
+  x.k = p.k[t * p.ks + kh * kD + c];
+  x.q = p.q[t * p.qs + kh * kD + c];
+  x.v = p.v[t * p.vs + h * kD + c];
+  x.d_o = p.d_o[(t * p.Hv + h) * kD + c];
+  if (c == 0) {
+    x.g = p.g[t * p.Hv + h];
+    x.beta = p.beta[t * p.Hv + h];
+  }
+}
+
+__device__ __forceinline__ void seg_store(SegStage& st, int len, int tid, const SegLoad& x) {
+  const int i = tid >> 7, c = tid & (kD - 1);
+  if (i >= len) return;
+  st.k[i][c] = bf16_to_f32(x.k);
+  st.q[i][c] = bf16_to_f32(x.q);
+  st.v[i][c] = bf16_to_f32(x.v);
+  st.d_o[i][c] = x.d_o;
+  if (c == 0) {
+    st.a[i] = expf(x.g);
+    st.beta[i] = x.beta;
+  }
+}
+
+__device__ __forceinline__ void ckpt_load(const BwdParams& p, int c0, int n, int h, int row, int lp,
+                                          float (&x)[16]) {
+  const float* src = p.ckpt + ckpt_row(p, c0, n, h, row);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    x.s[j] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4 * (lp + 8 * j)));
+    const floatx4 y = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4 * (lp + 8 * j)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * j + i] = y[i];
   }
-  x.g = p.g[th];
-  x.beta = p.beta[th];
-  x.dout = p.d_o[th * kD + row];
-  x.v = p.v[static_cast<int64_t>(t) * p.vs + h * kD + row];
-}
-
-// wave 0's share of a token's k (lanes 0..31) and q (lanes 32..63): 4 bf16
-__device__ __forceinline__ uint2 kq_load(const BwdParams& p, int t, int kh, int lane) {
-  const uint16_t* base = lane < 32 ? p.k + static_cast<int64_t>(t) * p.ks
-                                   : p.q + static_cast<int64_t>(t) * p.qs;
-  return *reinterpret_cast<const uint2*>(base + kh * kD + 4 * (lane & 31));
-}
-
-__device__ __forceinline__ void kq_store(float (*buf)[kD], int lane, uint2 b) {
-  *reinterpret_cast<floatx4*>(&buf[lane >> 5][4 * (lane & 31)]) =
-      floatx4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
-              __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
 }
 
 __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
-  // All three are double-buffered by token parity, so one barrier per token
-  // suffices: a buffer written by token t (before its barrier) is next written
-  // by token t - 2, after every thread has passed token t - 1's barrier, which
-  // each reader of token t's copy reaches only after its reads.
+  // part and spart are double-buffered by token parity, so one barrier per
+  // token suffices: a buffer written by one token (before its barrier) is
+  // next written two tokens later, after every thread has passed the barrier
+  // in between, which each reader reaches only after its reads.  The segment
+  // stage is double-buffered by segment parity on the same argument.
   __shared__ __align__(16) float part[2][kWaves][2][kD];   // per-wave column sums: dq_h, dk_h
-  __shared__ float spart[2][kWaves][2];      // per-wave sums: <S_prev, dSh>, dbeta
-  __shared__ __align__(16) float kq[2][2][kD];             // k, q of a token
+  __shared__ float spart[2][kWaves][2];                    // per-wave sums: <S_prev, dSh>, dbeta
+  __shared__ __align__(16) SegStage stage[2];
+  // The state before the current segment's first token: lane tid's 16 values
+  // as four float4 at [j][tid].  Each lane reads back only what it wrote, so
+  // no barrier guards it.
+  __shared__ __align__(16) floatx4 ckpt_lds[4][kTh];
   const int n = blockIdx.x / p.Hv;
   const int h = blockIdx.x - n * p.Hv;
   const int kh = h / (p.Hv / p.Hk);
@@ -180,127 +212,177 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) D[4 * j + i] = x[i];
   }
-  RevToken nxt;
-  if (s1 > s0) {
-    rev_load(p, s1 - 1, h, kh, row, lp, nxt);
-    if (w == 0) kq_store(kq[(s1 - 1) & 1], lane, kq_load(p, s1 - 1, kh, lane));
+  const int n_seg = (s1 - s0 + kSeg - 1) / kSeg;
+  if (n_seg > 0) {
+    const int c0 = s0 + (n_seg - 1) * kSeg;
+    SegLoad x;
+    float cn[16];
+    seg_load(p, c0, s1 - c0, h, kh, tid, x);
+    ckpt_load(p, c0, n, h, row, lp, cn);
+    seg_store(stage[(n_seg - 1) & 1], s1 - c0, tid, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ckpt_lds[j][tid] = floatx4{cn[4 * j], cn[4 * j + 1], cn[4 * j + 2], cn[4 * j + 3]};
   }
   __syncthreads();
-  for (int t = s1 - 1; t >= s0; --t) {
-    const int64_t th = static_cast<int64_t>(t) * p.Hv + h;
-    const RevToken cur = nxt;
-    uint2 kq_next = {0u, 0u};
-    if (t > s0) {   // the next token's inputs are in flight during this one
-      rev_load(p, t - 1, h, kh, row, lp, nxt);
-      if (w == 0) kq_next = kq_load(p, t - 1, kh, lane);
-    }
-    float Sp[16], kk[16], qq[16];
+  int tpar = 0;   // parity of the token count processed so far (selects part, spart)
+  for (int sg = n_seg - 1; sg >= 0; --sg) {
+    const int c0 = s0 + sg * kSeg;
+    const int len = min(kSeg, s1 - c0);
+    const SegStage& st = stage[sg & 1];
+    // the previous segment's inputs are in flight during this segment
+    SegLoad xn = {};
+    if (sg > 0) seg_load(p, c0 - kSeg, kSeg, h, kh, tid, xn);
+    for (int ti = len - 1; ti >= 0; --ti) {
+      const int t = c0 + ti;
+      const int64_t th = static_cast<int64_t>(t) * p.Hv + h;
+      // the state before token t, from the checkpoint
+      float Sp[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const floatx4 kx = *reinterpret_cast<const floatx4*>(&kq[t & 1][0][4 * (lp + 8 * j)]);
-      const floatx4 qx = *reinterpret_cast<const floatx4*>(&kq[t & 1][1][4 * (lp + 8 * j)]);
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 x = ckpt_lds[j][tid];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Sp[4 * j + i] = cur.s[j][i];
-        kk[4 * j + i] = kx[i];
-        qq[4 * j + i] = qx[i];
+        for (int i = 0; i < 4; ++i) Sp[4 * j + i] = x[i];
       }
-    }
-    const float a = expf(cur.g);
-    const float b = cur.beta;
-    const float vv = bf16_to_f32(cur.v);
-    const float dout = cur.dout;
-    // the forward step, recomputed
-    float sk = 0.f;
+      for (int j = 0; j < ti; ++j) {
+        float kj[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sk = fmaf(Sp[e], kk[e], sk);
-    sk = sum8(sk);
-    const float pk = a * sk;
-    const float u = b * (vv - pk);
-    // o = scale S q
-    float cq[16], ck[16];
+        for (int jj = 0; jj < 4; ++jj) {
+          const floatx4 kx = *reinterpret_cast<const floatx4*>(&st.k[j][4 * (lp + 8 * jj)]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      D[e] = fmaf(p.scale * dout, qq[e], D[e]);
-      cq[e] = p.scale * dout * fmaf(a, Sp[e], u * kk[e]);
-    }
-    // S = Sh + u k^T
-    float du = 0.f;
+          for (int ii = 0; ii < 4; ++ii) kj[4 * jj + ii] = kx[ii];
+        }
+        const float aj = st.a[j];
+        float sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) du = fmaf(D[e], kk[e], du);
-    du = sum8(du);
-    const float dp = -b * du;
-    float gdot = 0.f;
+        for (int e = 0; e < 16; ++e) sk = fmaf(Sp[e], kj[e], sk);
+        sk = sum8(sk);
+        const float uj = st.beta[j] * (st.v[j][row] - aj * sk);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      ck[e] = fmaf(D[e], u, a * Sp[e] * dp);
-      const float dsh = fmaf(dp, kk[e], D[e]);
-      gdot = fmaf(Sp[e], dsh, gdot);
-      D[e] = a * dsh;
-    }
-    if (lp == 0) p.dv[th * kD + row] = b * du;
-    float bdot = lp == 0 ? (vv - pk) * du : 0.f;
-    // Column sums over the wave's eight rows (lanes lp, lp + 8, ..., lp + 56)
-    // by a butterfly reduce-scatter over lane bits 5, 4, 3: each exchange
-    // sends half of the remaining values to the partner lane and keeps the
-    // other half, so lane (b5 b4 b3, lp) ends with the four sums of values
-    // j = 16 b5 + 8 b4 + 4 b3 + i (j < 16: cq[j], else ck[j - 16]), i.e. the
-    // float4 of columns 4 (lp + 8 (2 b4 + b3)) .. + 3 of dq_h (b5 = 0) or
-    // dk_h (b5 = 1).  16 + 8 permutes and a DPP step instead of 96 permutes.
-    const unsigned m5 = (lane & 32) ? ~0u : 0u, m4 = (lane & 16) ? ~0u : 0u, m3 = (lane & 8) ? ~0u : 0u;
-    float y[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = __shfl_xor(blend(m5, cq[i], ck[i]), 32, 64);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] += blend(m5, ck[i], cq[i]);
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = __shfl_xor(blend(m4, y[i], y[8 + i]), 16, 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] += blend(m4, y[8 + i], y[i]);
-    floatx4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)   // DPP row_ror:8 reads lane ^ 8 inside each row of 16
-      r[i] = blend(m3, z[4 + i], z[i]) + dpp<0x128>(blend(m3, z[i], z[4 + i]));
-    *reinterpret_cast<floatx4*>(&part[t & 1][w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
-    // <S_prev, dSh> and dbeta over the wave: the eight lanes of a row by DPP,
-    // then the eight rows
-    gdot = sum8(gdot);
-    bdot = sum8(bdot);
-    gdot += dpp<0x128>(gdot);
-    bdot += dpp<0x128>(bdot);
-    gdot += __shfl_xor(gdot, 16, 64);
-    bdot += __shfl_xor(bdot, 16, 64);
-    gdot += __shfl_xor(gdot, 32, 64);
-    bdot += __shfl_xor(bdot, 32, 64);
-    if (lane == 0) {
-      spart[t & 1][w][0] = gdot;
-      spart[t & 1][w][1] = bdot;
-    }
-    // buffer (t - 1) & 1 was last read by token t + 1, before its barrier
-    if (w == 0 && t > s0) kq_store(kq[(t - 1) & 1], lane, kq_next);
-    __syncthreads();
-    if (tid < 2 * kD) {
-      const int which = tid >> 7, c = tid & (kD - 1);
-      float acc = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) acc += part[t & 1][ww][which][c];
-      (which ? p.dk_part : p.dq_part)[th * kD + c] = acc;
-    } else if (tid == 2 * kD) {
-      float gs = 0.f, bs = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        gs += spart[t & 1][ww][0];
-        bs += spart[t & 1][ww][1];
+        for (int e = 0; e < 16; ++e) Sp[e] = fmaf(aj, Sp[e], uj * kj[e]);
       }
-      p.dg[th] = a * gs;
-      p.dbeta[th] = bs;
+      float kk[16];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const floatx4 kx = *reinterpret_cast<const floatx4*>(&st.k[ti][4 * (lp + 8 * jj)]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) kk[4 * jj + ii] = kx[ii];
+      }
+      const float a = st.a[ti];
+      const float b = st.beta[ti];
+      const float vv = st.v[ti][row];
+      const float dout = st.d_o[ti][row];
+      // the forward step, recomputed
+      float sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sk = fmaf(Sp[e], kk[e], sk);
+      sk = sum8(sk);
+      const float pk = a * sk;
+      const float u = b * (vv - pk);
+      // o = scale S q: D += scale dout q^T (q read from the stage as used)
+      const float sd = p.scale * dout;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const floatx4 qx = *reinterpret_cast<const floatx4*>(&st.q[ti][4 * (lp + 8 * jj)]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) D[4 * jj + ii] = fmaf(sd, qx[ii], D[4 * jj + ii]);
+      }
+      // S = Sh + u k^T
+      float du = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) du = fmaf(D[e], kk[e], du);
+      du = sum8(du);
+      const float dp = -b * du;
+      float gdot = 0.f;
+      float cq[16], ck[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ck[e] = fmaf(D[e], u, a * Sp[e] * dp);
+        const float dsh = fmaf(dp, kk[e], D[e]);
+        gdot = fmaf(Sp[e], dsh, gdot);
+        D[e] = a * dsh;
+        cq[e] = sd * fmaf(a, Sp[e], u * kk[e]);   // scale dout S (the state after the token)
+      }
+      // the segment's first token (processed last) loads the previous
+      // segment's checkpoint; it replaces this one in ckpt_lds (already read
+      // by this token) before the barrier
+      float cn[16];
+      if (ti == 0 && sg > 0) ckpt_load(p, c0 - kSeg, n, h, row, lp, cn);
+      if (lp == 0) p.dv[th * kD + row] = b * du;
+      float bdot = lp == 0 ? (vv - pk) * du : 0.f;
+      // Column sums over the wave's eight rows (lanes lp, lp + 8, ..., lp + 56)
+      // by a butterfly reduce-scatter over lane bits 5, 4, 3: each exchange
+      // sends half of the remaining values to the partner lane and keeps the
+      // other half, so lane (b5 b4 b3, lp) ends with the four sums of values
+      // j = 16 b5 + 8 b4 + 4 b3 + i (j < 16: cq[j], else ck[j - 16]), i.e. the
+      // float4 of columns 4 (lp + 8 (2 b4 + b3)) .. + 3 of dq_h (b5 = 0) or
+      // dk_h (b5 = 1).  16 + 8 permutes and a DPP step instead of 96 permutes.
+      const unsigned m5 = (lane & 32) ? ~0u : 0u, m4 = (lane & 16) ? ~0u : 0u, m3 = (lane & 8) ? ~0u : 0u;
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = __shfl_xor(blend(m5, cq[i], ck[i]), 32, 64);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] += blend(m5, ck[i], cq[i]);
+      float z[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = __shfl_xor(blend(m4, y[i], y[8 + i]), 16, 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] += blend(m4, y[8 + i], y[i]);
+      floatx4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)   // DPP row_ror:8 reads lane ^ 8 inside each row of 16
+        r[i] = blend(m3, z[4 + i], z[i]) + dpp<0x128>(blend(m3, z[i], z[4 + i]));
+      *reinterpret_cast<floatx4*>(&part[tpar][w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
+      // <S_prev, dSh> and dbeta over the wave: the eight lanes of a row by DPP,
+      // then the eight rows
+      gdot = sum8(gdot);
+      bdot = sum8(bdot);
+      gdot += dpp<0x128>(gdot);
+      bdot += dpp<0x128>(bdot);
+      gdot += __shfl_xor(gdot, 16, 64);
+      bdot += __shfl_xor(bdot, 16, 64);
+      gdot += __shfl_xor(gdot, 32, 64);
+      bdot += __shfl_xor(bdot, 32, 64);
+      if (lane == 0) {
+        spart[tpar][w][0] = gdot;
+        spart[tpar][w][1] = bdot;
+      }
+      // the previous segment's inputs into the other stage buffer, last read
+      // by the segment before this one, ahead of its final barrier
+      if (ti == 0 && sg > 0) {
+        seg_store(stage[(sg - 1) & 1], kSeg, tid, xn);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ckpt_lds[j][tid] = floatx4{cn[4 * j], cn[4 * j + 1], cn[4 * j + 2], cn[4 * j + 3]};
+      }
+      __syncthreads();
+      if (tid < 2 * kD) {
+        const int which = tid >> 7, c = tid & (kD - 1);
+        float acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) acc += part[tpar][ww][which][c];
+        (which ? p.dk_part : p.dq_part)[th * kD + c] = acc;
+      } else if (tid == 2 * kD) {
+        float gs = 0.f, bs = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          gs += spart[tpar][ww][0];
+          bs += spart[tpar][ww][1];
+        }
+        p.dg[th] = a * gs;
+        p.dbeta[th] = bs;
+      }
+      tpar ^= 1;
     }
   }
   if (p.dh0) {
+    // the lane's offset is formed afresh here (the empty asm hides tid's
+    // provenance) rather than kept live in registers across the token loops
+    int tid2 = tid;
+    asm volatile("" : "+v"(tid2));
+    float* dst = p.dh0 + ((static_cast<int64_t>(n) * p.Hv + h) * kD + (tid2 >> 3)) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<floatx4*>(p.dh0 + ((static_cast<int64_t>(n) * p.Hv + h) * kD + row) * kD + 4 * (lp + 8 * j)) =
+      *reinterpret_cast<floatx4*>(dst + 4 * ((tid2 & 7) + 8 * j)) =
           floatx4{D[4 * j], D[4 * j + 1], D[4 * j + 2], D[4 * j + 3]};
   }
 }
@@ -329,10 +411,14 @@ __global__ __launch_bounds__(256) void backward_sum_kernel(const float* __restri
 
 }  // namespace
 
-size_t backward_workspace_bytes(int T_total, int Hv) {
-  const size_t dump = static_cast<size_t>(T_total) * Hv * kD * kD * sizeof(float);
-  const size_t parts = 2 * static_cast<size_t>(T_total) * Hv * kD * sizeof(float);
-  return dump + parts;
+// checkpoint slots: below T_total / kSeg + n_seqs (ckpt_row)
+static size_t ckpt_floats(int n_seqs, int T_total, int Hv) {
+  return (static_cast<size_t>(T_total / kSeg) + n_seqs) * Hv * kD * kD;
+}
+
+size_t backward_workspace_bytes(int n_seqs, int T_total, int Hv) {
+  const size_t parts = 2 * static_cast<size_t>(T_total) * Hv * kD;
+  return (ckpt_floats(n_seqs, T_total, Hv) + parts) * sizeof(float);
 }
 
 hipError_t launch_backward(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
@@ -346,8 +432,8 @@ hipError_t launch_backward(const uint16_t* q, int64_t qs, const uint16_t* k, int
   p.q = q; p.k = k; p.v = v; p.qs = qs; p.ks = ks; p.vs = vs; p.g = g; p.beta = beta;
   p.h0 = h0; p.d_o = d_o; p.dhT = dhT; p.cu = cu;
   float* ws = static_cast<float*>(workspace);
-  p.dump = ws;
-  p.dq_part = ws + static_cast<size_t>(T_total) * Hv * kD * kD;
+  p.ckpt = ws;
+  p.dq_part = ws + ckpt_floats(n_seqs, T_total, Hv);
   p.dk_part = p.dq_part + static_cast<size_t>(T_total) * Hv * kD;
   p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dh0 = dh0;
   p.n_seqs = n_seqs; p.seq_len = cu ? 0 : T_total / n_seqs; p.Hk = Hk; p.Hv = Hv; p.scale = scale;

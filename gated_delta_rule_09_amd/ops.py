@@ -53,7 +53,7 @@ _SIGS = {
                                      _i32, _i32, _f32, _f32, _f32, _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
-    "gdn_backward_workspace_bytes": (_sz, [_i32, _i32]),
+    "gdn_backward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "gdn_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
                             _vp, _sz, _vp]),
@@ -589,8 +589,8 @@ def gdn_validate_cu_seqlens(cu_seqlens: torch.Tensor, T_total: int) -> None:
     _check(st, "gdn_validate_cu_seqlens")
 
 
-def gdn_backward_workspace_bytes(T_total: int, Hv: int) -> int:
-    return int(lib().gdn_backward_workspace_bytes(T_total, Hv))
+def gdn_backward_workspace_bytes(n_seqs: int, T_total: int, Hv: int) -> int:
+    return int(lib().gdn_backward_workspace_bytes(n_seqs, T_total, Hv))
 
 
 def gdn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -605,7 +605,8 @@ def gdn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     Inputs as gdn_chunk_fwd; grad_o [T, Hv, 128] fp32, grad_final_state
     [N, Hv, 128, 128] fp32 or None.  Returns a dict of fp32 tensors dq, dk
     [T, Hk, 128], dv [T, Hv, 128], dg, dbeta [T, Hv] and dh0 [N, Hv, 128, 128]
-    (None unless grad_initial_state).  The workspace holds T x Hv x 64 KB.
+    (None unless grad_initial_state).  The workspace holds the state of every
+    8th token (T / 8 + N) x Hv x 64 KB and 1 KB per token and value head.
     """
     _qkv_checks(q, k, v)
     _need(g, "g", torch.float32, 2)
@@ -634,7 +635,7 @@ def gdn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
                dh0=(torch.empty((n_seqs, Hv, dv, dk), dtype=torch.float32, device=dev)
                     if grad_initial_state else None))
     if workspace is None:
-        need = gdn_backward_workspace_bytes(T, Hv)
+        need = gdn_backward_workspace_bytes(n_seqs, T, Hv)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel()
     st = lib().gdn_backward(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),

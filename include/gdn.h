@@ -391,10 +391,10 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  * taken through each token's erase-then-write update of the "Attention Layer
  * Details" section of the deep-dive page, in reverse token order, in fp32:
  * one kernel re-runs the recurrence and records the state before every
- * token in the workspace, a second walks the tokens backwards holding
- * dL/dS, a third sums dq and dk over the value heads of each key head.
- * Memory-hungry by design (64 KB of workspace per token and value head), so
- * meant for training-sized batches, not long-context prefill.
+ * 8th token of each sequence in the workspace, a second walks the tokens
+ * backwards holding dL/dS and rebuilding each token's state from the
+ * nearest record, a third sums dq and dk over the value heads of each key
+ * head.  The workspace holds about 8 KB per token and value head.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, n_seqs, T_total, sizes
  *                     as gdn_chunk_fwd (initial_state NULL = zeros)
@@ -405,13 +405,13 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  *   grad_g, grad_beta [T_total, Hv] fp32, contiguous (grad_g is dL/dg, g
  *                     being the log of the decay alpha)
  *   grad_initial_state [n_seqs, Hv, dv, dk] fp32 or NULL (not written)
- *   workspace         >= gdn_backward_workspace_bytes(T_total, Hv) bytes,
+ *   workspace         >= gdn_backward_workspace_bytes(n_seqs, T_total, Hv) bytes,
  *                     256-byte aligned, contents ignored on entry
  *
  * No output may overlap an input, another output or the workspace
  * (GDN_ERR_ALIAS).  Errors as gdn_chunk_fwd.
  */
-size_t gdn_backward_workspace_bytes(int32_t T_total, int32_t Hv);
+size_t gdn_backward_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hv);
 gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
                         int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
                         const float* g, const float* beta, const float* initial_state,
