@@ -288,7 +288,7 @@ def leg_backward(args, ops, synth, torch):
     per_tok = HK * D * 2 * 2 + HV * D * 2 + HV * 4 * 2 + HV * D * 4 + HK * D * 4 * 2 + HV * D * 4 \
         + HV * 4 * 2
     alg = T * per_tok + 3 * N * STATE_BYTES
-    recorded = 2 * (T // 8 + N) * STATE_BYTES   # the checkpointed states, written and read once
+    recorded = 2 * (T // 4 + N) * STATE_BYTES   # the checkpointed states, written and read once
     res = dict(tokens=T, n_seqs=N, event_ms=ev, wall_ms=wall, tokens_per_s=T / (ev * 1e-3),
                alg_gbps=alg / (ev * 1e-3) / 1e9,
                with_record_gbps=(alg + recorded) / (ev * 1e-3) / 1e9)

@@ -95,7 +95,7 @@ hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state
                              const int32_t* cu, int n_seqs, int T_total, int C,
                              hipStream_t stream, const int32_t* slots = nullptr);
 
-// Backward of the rule (backward.hip): workspace of (T_total / 8 + n_seqs) x
+// Backward of the rule (backward.hip): workspace of (T_total / 4 + n_seqs) x
 // Hv x 64 KB of checkpointed states plus 2 x T_total x Hv x 512 B of
 // per-value-head dq, dk.
 size_t backward_workspace_bytes(int n_seqs, int T_total, int Hv);

@@ -391,10 +391,10 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  * taken through each token's erase-then-write update of the "Attention Layer
  * Details" section of the deep-dive page, in reverse token order, in fp32:
  * one kernel re-runs the recurrence and records the state before every
- * 8th token of each sequence in the workspace, a second walks the tokens
+ * 4th token of each sequence in the workspace, a second walks the tokens
  * backwards holding dL/dS and rebuilding each token's state from the
  * nearest record, a third sums dq and dk over the value heads of each key
- * head.  The workspace holds about 8 KB per token and value head.
+ * head.  The workspace holds about 17 KB per token and value head.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, n_seqs, T_total, sizes
  *                     as gdn_chunk_fwd (initial_state NULL = zeros)
