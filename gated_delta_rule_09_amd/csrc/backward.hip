@@ -65,12 +65,18 @@ __device__ __forceinline__ int64_t ckpt_row(const BwdParams& p, int t, int n, in
   return ((static_cast<int64_t>(t / kSeg + n) * p.Hv + h) * kD + row) * kD;
 }
 
-// a if the lane's mask m is all ones, b if it is zero; a bitwise blend of two
-// loaded values, so that the compiler cannot turn a choice between two
-// register arrays into an indexed (scratch) access
-__device__ __forceinline__ float blend(unsigned m, float a, float b) {
-  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+// a where the lane's bit of the wave-wide mask m is set, else b: one
+// v_cndmask_b32.  Written as asm so that the compiler cannot turn a choice
+// between two register arrays into an indexed (scratch) access.
+__device__ __forceinline__ float lane_select(uint64_t m, float a, float b) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
 }
+// lanes whose index has bit 5, 4 or 3 set
+constexpr uint64_t kLaneBit5 = 0xFFFFFFFF00000000ull;
+constexpr uint64_t kLaneBit4 = 0xFFFF0000FFFF0000ull;
+constexpr uint64_t kLaneBit3 = 0xFF00FF00FF00FF00ull;
 
 __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
   const int n = blockIdx.x / p.Hv;
@@ -297,13 +303,14 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
       const float dp = -b * du;
       float gdot = 0.f;
       float cq[16], ck[16];
+      const float adp = a * dp, sda = sd * a, sdu = sd * u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        ck[e] = fmaf(D[e], u, a * Sp[e] * dp);
+        ck[e] = fmaf(D[e], u, adp * Sp[e]);
         const float dsh = fmaf(dp, kk[e], D[e]);
         gdot = fmaf(Sp[e], dsh, gdot);
         D[e] = a * dsh;
-        cq[e] = sd * fmaf(a, Sp[e], u * kk[e]);   // scale dout S (the state after the token)
+        cq[e] = fmaf(sda, Sp[e], sdu * kk[e]);   // scale dout S (the state after the token)
       }
       // the segment's first token (processed last) loads the previous
       // segment's checkpoint; it replaces this one in ckpt_lds (already read
@@ -319,21 +326,20 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
       // j = 16 b5 + 8 b4 + 4 b3 + i (j < 16: cq[j], else ck[j - 16]), i.e. the
       // float4 of columns 4 (lp + 8 (2 b4 + b3)) .. + 3 of dq_h (b5 = 0) or
       // dk_h (b5 = 1).  16 + 8 permutes and a DPP step instead of 96 permutes.
-      const unsigned m5 = (lane & 32) ? ~0u : 0u, m4 = (lane & 16) ? ~0u : 0u, m3 = (lane & 8) ? ~0u : 0u;
       float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = __shfl_xor(blend(m5, cq[i], ck[i]), 32, 64);
+      for (int i = 0; i < 16; ++i) y[i] = __shfl_xor(lane_select(kLaneBit5, cq[i], ck[i]), 32, 64);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] += blend(m5, ck[i], cq[i]);
+      for (int i = 0; i < 16; ++i) y[i] += lane_select(kLaneBit5, ck[i], cq[i]);
       float z[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = __shfl_xor(blend(m4, y[i], y[8 + i]), 16, 64);
+      for (int i = 0; i < 8; ++i) z[i] = __shfl_xor(lane_select(kLaneBit4, y[i], y[8 + i]), 16, 64);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] += blend(m4, y[8 + i], y[i]);
+      for (int i = 0; i < 8; ++i) z[i] += lane_select(kLaneBit4, y[8 + i], y[i]);
       floatx4 r;
 #pragma unroll
       for (int i = 0; i < 4; ++i)   // DPP row_ror:8 reads lane ^ 8 inside each row of 16
-        r[i] = blend(m3, z[4 + i], z[i]) + dpp<0x128>(blend(m3, z[i], z[4 + i]));
+        r[i] = lane_select(kLaneBit3, z[4 + i], z[i]) + dpp<0x128>(lane_select(kLaneBit3, z[i], z[4 + i]));
       *reinterpret_cast<floatx4*>(&part[tpar][w][(lane >> 5) & 1][4 * (lp + 8 * ((lane >> 3) & 3))]) = r;
       // <S_prev, dSh> and dbeta over the wave: the eight lanes of a row by DPP,
       // then the eight rows
