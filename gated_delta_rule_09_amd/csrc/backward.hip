@@ -78,7 +78,16 @@ constexpr uint64_t kLaneBit5 = 0xFFFFFFFF00000000ull;
 constexpr uint64_t kLaneBit4 = 0xFFFF0000FFFF0000ull;
 constexpr uint64_t kLaneBit3 = 0xFF00FF00FF00FF00ull;
 
+// The record kernel's inputs for kFwdTok tokens, staged in LDS by the whole
+// work-group (one element per thread and array), double-buffered.
+constexpr int kFwdTok = kTh / kD;
+struct FwdStage {
+  float k[kFwdTok][kD], v[kFwdTok][kD];
+  float a[kFwdTok], beta[kFwdTok];
+};
+
 __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
+  __shared__ __align__(16) FwdStage stage[2];
   const int n = blockIdx.x / p.Hv;
   const int h = blockIdx.x - n * p.Hv;
   const int kh = h / (p.Hv / p.Hk);
@@ -95,47 +104,69 @@ __global__ __launch_bounds__(kTh) void backward_fwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[4 * j + i] = x[i];
   }
-  // the next token's k row share, gates and v element are in flight while
-  // the current token is applied
-  uint2 kn[4] = {};
-  float gn = 0.f, bn = 0.f;
-  uint16_t vn = 0;
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      kn[j] = *reinterpret_cast<const uint2*>(p.k + static_cast<int64_t>(t) * p.ks + kh * kD + 4 * (lp + 8 * j));
-    gn = p.g[static_cast<int64_t>(t) * p.Hv + h];
-    bn = p.beta[static_cast<int64_t>(t) * p.Hv + h];
-    vn = p.v[static_cast<int64_t>(t) * p.vs + h * kD + row];
+  // thread (i, c) = (tid / 128, tid % 128) loads channel c of token b0 + i
+  const int si = tid >> 7, sc = tid & (kD - 1);
+  uint16_t lk = 0, lv = 0;
+  float lg = 0.f, lb = 0.f;
+  auto fetch = [&](int b0) {
+    const int64_t t = b0 + si;
+    if (t < s1) {
+      lk = p.k[t * p.ks + kh * kD + sc];
+      lv = p.v[t * p.vs + h * kD + sc];
+      if (sc == 0) {
+        lg = p.g[t * p.Hv + h];
+        lb = p.beta[t * p.Hv + h];
+      }
+    }
   };
-  if (s1 > s0) fetch(s0);
-  for (int t = s0; t < s1; ++t) {
-    if ((t - s0) % kSeg == 0) {
-      float* dst = p.ckpt + ckpt_row(p, t, n, h, row);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_nontemporal_store(floatx4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]},
-                                    reinterpret_cast<floatx4*>(dst + 4 * (lp + 8 * j)));
+  auto put = [&](FwdStage& st) {
+    st.k[si][sc] = bf16_to_f32(lk);
+    st.v[si][sc] = bf16_to_f32(lv);
+    if (sc == 0) {
+      st.a[si] = expf(lg);
+      st.beta[si] = lb;
     }
-    float kk[16];
+  };
+  if (s1 > s0) {
+    fetch(s0);
+    put(stage[0]);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int b0 = s0; b0 < s1; b0 += kFwdTok, buf ^= 1) {
+    const FwdStage& st = stage[buf];
+    const bool more = b0 + kFwdTok < s1;
+    if (more) fetch(b0 + kFwdTok);   // in flight during this batch
+    const int nb = min(kFwdTok, s1 - b0);
+    for (int i = 0; i < nb; ++i) {
+      const int t = b0 + i;
+      if ((t - s0) % kSeg == 0) {
+        float* dst = p.ckpt + ckpt_row(p, t, n, h, row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kk[4 * j + 0] = __uint_as_float(kn[j].x << 16);
-      kk[4 * j + 1] = __uint_as_float(kn[j].x & 0xffff0000u);
-      kk[4 * j + 2] = __uint_as_float(kn[j].y << 16);
-      kk[4 * j + 3] = __uint_as_float(kn[j].y & 0xffff0000u);
+        for (int j = 0; j < 4; ++j)
+          __builtin_nontemporal_store(floatx4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]},
+                                      reinterpret_cast<floatx4*>(dst + 4 * (lp + 8 * j)));
+      }
+      float kk[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 kx = *reinterpret_cast<const floatx4*>(&st.k[i][4 * (lp + 8 * j)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[4 * j + e] = kx[e];
+      }
+      const float a = st.a[i];
+      float sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sk = fmaf(s[e], kk[e], sk);
+      sk = sum8(sk);
+      const float u = st.beta[i] * (st.v[i][row] - a * sk);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = fmaf(a, s[e], u * kk[e]);
     }
-    const float a = expf(gn);
-    const float b = bn;
-    const float vv = bf16_to_f32(vn);
-    if (t + 1 < s1) fetch(t + 1);
-    float sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sk = fmaf(s[e], kk[e], sk);
-    sk = sum8(sk);
-    const float u = b * (vv - a * sk);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = fmaf(a, s[e], u * kk[e]);
+    // the other buffer was last read in the previous batch, which every
+    // thread finished before the barrier that ended it
+    if (more) put(stage[buf ^ 1]);
+    __syncthreads();
   }
 }
 

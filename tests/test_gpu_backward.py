@@ -51,6 +51,18 @@ def test_backward_varlen_ragged_and_empty_sequences():
     assert np.all(got["dh0"][1] == 0) and np.all(got["dh0"][6] == 0)
 
 
+@pytest.mark.parametrize("Hk,Hv", [(4, 4), (1, 4)])
+def test_backward_head_ratios_and_segment_edges(Hk, Hv):
+    """G = Hv / Hk of 1 and 4, lengths on either side of the checkpoint
+    segment (4 tokens) and of the record kernel's 8-token batches."""
+    lens = [3, 4, 5, 8, 9, 0, 13, 17]
+    log(f"backward: Hk {Hk}, Hv {Hv}, lengths {lens}")
+    ci = synth.chunk_inputs(7400 + Hk, sum(lens), Hk=Hk, Hv=Hv, lengths=lens, h0_std=0.05)
+    bs = synth.backward_seeds(7500 + Hk, sum(lens), len(lens), Hv=Hv)
+    got, ref = _run(ci, bs, 0.5, Hk)
+    _check(got, ref, f"Hk {Hk} Hv {Hv}")
+
+
 def test_backward_full_head_layout():
     log("backward: T 96, Hk 16, Hv 48")
     ci = synth.chunk_inputs(7200, 96, h0_std=0.02)
