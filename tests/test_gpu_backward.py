@@ -83,6 +83,23 @@ def test_backward_no_tokens_passes_state_gradient_through():
     assert torch.equal(out["dh0"], dhT) and out["dq"].shape[0] == 0
 
 
+def test_backward_without_initial_state_gradient():
+    """grad_initial_state=False passes no dh0 buffer; the other gradients are
+    unchanged bit for bit."""
+    log("backward: no dh0 requested")
+    ci = synth.chunk_inputs(7600, 70, Hk=2, Hv=4, lengths=[33, 37], h0_std=0.05)
+    bs = synth.backward_seeds(7601, 70, 2, Hv=4)
+    args = (dev_bf16(ci.q), dev_bf16(ci.k), dev_bf16(ci.v), dev_f32(ci.g), dev_f32(ci.beta),
+            dev_f32(bs.d_o))
+    kw = dict(initial_state=dev_f32(ci.h0), grad_final_state=dev_f32(bs.dhT),
+              cu_seqlens=dev_i32(ci.cu_seqlens))
+    full = ops.gdn_backward(*args, **kw)
+    part = ops.gdn_backward(*args, grad_initial_state=False, **kw)
+    assert part["dh0"] is None
+    for n in NAMES[:-1]:
+        assert torch.equal(full[n], part[n]), n
+
+
 def test_backward_is_deterministic():
     log("backward: determinism")
     ci = synth.chunk_inputs(7300, 100, Hk=2, Hv=6, h0_std=0.05)
