@@ -283,7 +283,9 @@ __global__ __launch_bounds__(kTh) void backward_rev_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Sp[4 * j + i] = x[i];
       }
-      for (int j = 0; j < ti; ++j) {
+#pragma unroll
+      for (int j = 0; j < kSeg - 1; ++j) {
+        if (j >= ti) break;   // uniform over the work-group
         float kj[16];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
