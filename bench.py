@@ -12,7 +12,8 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
   mixer   the full mixer at T = 8192: conv + SiLU + L2 -> chunked rule -> gated
           RMSNorm, as four launches and as one gdn_mixer_fwd call (the conv
           front inside the prep kernel);
-  varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens).
+  varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens);
+  backward  gdn_backward (the rule's gradients) on 8 sequences of 1024 tokens.
 Two more prefill timings, not the headline: o written in bf16
 (`prefill_bf16_o`) and the gates formed from bf16 projections (`prefill_gated`).
 `roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
@@ -29,8 +30,7 @@ host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs prefill,decode,...]
 (`--legs copy` adds a plain 1 GiB device copy, the calibration kernel for the
-HBM byte counters; `--legs backward` times gdn_backward on 8 sequences of 1024
-tokens.)
+HBM byte counters.)
 """
 import argparse
 import hashlib
@@ -370,7 +370,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,mixer,varlen")
+    ap.add_argument("--legs", default="prefill,decode,mixer,varlen,backward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
