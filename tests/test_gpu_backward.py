@@ -63,6 +63,27 @@ def test_backward_head_ratios_and_segment_edges(Hk, Hv):
     _check(got, ref, f"Hk {Hk} Hv {Hv}")
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_backward_random_shapes(case):
+    """Seeded random shapes: key heads 1-4, G = 1-4, 1-5 sequences of 0-40
+    tokens, with or without h0 and dS_T, a random scale."""
+    r = np.random.default_rng(9000 + case)
+    Hk = int(r.integers(1, 5))
+    Hv = Hk * int(r.integers(1, 5))
+    lens = [int(x) for x in r.integers(0, 41, size=int(r.integers(1, 6)))]
+    T = sum(lens)
+    with_h0, with_dhT = bool(r.integers(0, 2)), bool(r.integers(0, 2))
+    scale = float(r.uniform(0.05, 1.0))
+    log(f"backward random case {case}: Hk {Hk} Hv {Hv} lengths {lens} h0 {with_h0} "
+        f"dhT {with_dhT} scale {scale:.3f}")
+    ci = synth.chunk_inputs(9100 + case, T, Hk=Hk, Hv=Hv, lengths=lens,
+                            h0_std=0.05 if with_h0 else None)
+    bs = synth.backward_seeds(9200 + case, T, len(lens), Hv=Hv,
+                              dhT_std=0.05 if with_dhT else None)
+    got, ref = _run(ci, bs, scale, Hk)
+    _check(got, ref, f"random {case}")
+
+
 def test_backward_full_head_layout():
     log("backward: T 96, Hk 16, Hv 48")
     ci = synth.chunk_inputs(7200, 96, h0_std=0.02)
