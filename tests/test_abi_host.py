@@ -310,3 +310,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib_handle", None)
     with pytest.raises(RuntimeError, match="not built"):
         ops.lib()
+
+
+def test_backward_checkpoint_slots_fit_the_workspace():
+    """gdn_backward keeps the state before every 4th token of a sequence
+    (tokens s0, s0 + 4, ... of a sequence starting at s0) in slot t // 4 + n of
+    a workspace sized for T // 4 + N slots: over random packings with empty
+    and one-token sequences the slots are distinct and in range."""
+    import numpy as np
+    r = np.random.default_rng(31)
+    for _ in range(200):
+        lens = r.integers(0, 30, size=int(r.integers(1, 12)))
+        if r.integers(0, 3) == 0:
+            lens[r.integers(0, len(lens))] = 1
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        T, N = int(cu[-1]), len(lens)
+        slots = [t // 4 + n for n in range(N) for t in range(int(cu[n]), int(cu[n + 1]), 4)]
+        assert len(set(slots)) == len(slots)
+        assert all(0 <= s < T // 4 + N for s in slots)
