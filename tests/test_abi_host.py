@@ -249,7 +249,9 @@ def backward(lib, **kw):
 
 def test_backward_validation(lib):
     need = lib.gdn_backward_workspace_bytes(1, 64, 48)
-    assert need == (64 // 4 + 1) * 48 * 128 * 128 * 4 + 2 * 64 * 48 * 128 * 4
+    # checkpoints + per-(token, head, row group) parts of dq, dk, dg, dbeta; 48 (sequence,
+    # head) pairs get 4 row groups each
+    assert need == (64 // 4 + 1) * 48 * 128 * 128 * 4 + 2 * 64 * 48 * 4 * 129 * 4
     assert lib.gdn_backward_workspace_bytes(1, 0, 48) == 0
     assert backward(lib, do=None) == NULL
     assert backward(lib, dg=None) == NULL

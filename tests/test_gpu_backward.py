@@ -84,6 +84,20 @@ def test_backward_random_shapes(case):
     _check(got, ref, f"random {case}")
 
 
+@pytest.mark.parametrize("n_seqs", [17, 3, 12])
+def test_backward_row_group_layouts(n_seqs):
+    """Each (sequence, value head) is split over 1, 2 or 4 work-groups of
+    rows depending on how many pairs the batch has (more than 768, 129-768,
+    at most 128 at 48 heads): all three layouts against the oracle."""
+    r = np.random.default_rng(9300 + n_seqs)
+    lens = [int(x) for x in r.integers(0, 12, size=n_seqs)]
+    log(f"backward row groups: {n_seqs} sequences x 48 heads, lengths {lens}")
+    ci = synth.chunk_inputs(9400 + n_seqs, sum(lens), lengths=lens, h0_std=0.02)
+    bs = synth.backward_seeds(9500 + n_seqs, sum(lens), n_seqs)
+    got, ref = _run(ci, bs, 128 ** -0.5, 16)
+    _check(got, ref, f"{n_seqs} sequences")
+
+
 def test_backward_full_head_layout():
     log("backward: T 96, Hk 16, Hv 48")
     ci = synth.chunk_inputs(7200, 96, h0_std=0.02)
