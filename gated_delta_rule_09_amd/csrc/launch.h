@@ -96,8 +96,8 @@ hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state
                              hipStream_t stream, const int32_t* slots = nullptr);
 
 // Backward of the rule (backward.hip): workspace of (T_total / 4 + n_seqs) x
-// Hv x 64 KB of checkpointed states plus 2 x T_total x Hv x 512 B of
-// per-value-head dq, dk.
+// Hv x 64 KB of checkpointed states plus the partial dq, dk, dg, dbeta of
+// 1, 2 or 4 row groups per (token, value head).
 size_t backward_workspace_bytes(int n_seqs, int T_total, int Hv);
 hipError_t launch_backward(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                            const uint16_t* v, int64_t vs, const float* g, const float* beta,

@@ -606,7 +606,8 @@ def gdn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     [N, Hv, 128, 128] fp32 or None.  Returns a dict of fp32 tensors dq, dk
     [T, Hk, 128], dv [T, Hv, 128], dg, dbeta [T, Hv] and dh0 [N, Hv, 128, 128]
     (None unless grad_initial_state).  The workspace holds the state of every
-    4th token, (T / 4 + N) x Hv x 64 KB, and 1 KB per token and value head.
+    4th token, (T / 4 + N) x Hv x 64 KB, and 1-4 KB of partial sums per token
+    and value head.
     """
     _qkv_checks(q, k, v)
     _need(g, "g", torch.float32, 2)

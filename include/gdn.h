@@ -394,7 +394,9 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  * 4th token of each sequence in the workspace, a second walks the tokens
  * backwards holding dL/dS and rebuilding each token's state from the
  * nearest record, a third sums dq and dk over the value heads of each key
- * head.  The workspace holds about 17 KB per token and value head.
+ * head.  Small batches split each head's state rows over up to four
+ * work-groups.  The workspace holds about 16 KB of states plus 1-4 KB of
+ * partial sums per token and value head.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, n_seqs, T_total, sizes
  *                     as gdn_chunk_fwd (initial_state NULL = zeros)
