@@ -84,10 +84,10 @@ def test_backward_random_shapes(case):
     _check(got, ref, f"random {case}")
 
 
-@pytest.mark.parametrize("n_seqs", [17, 3, 12])
+@pytest.mark.parametrize("n_seqs", [33, 3, 12])
 def test_backward_row_group_layouts(n_seqs):
     """Each (sequence, value head) is split over 1, 2 or 4 work-groups of
-    rows depending on how many pairs the batch has (more than 768, 129-768,
+    rows depending on how many pairs the batch has (more than 1536, 129-1536,
     at most 128 at 48 heads): all three layouts against the oracle."""
     r = np.random.default_rng(9300 + n_seqs)
     lens = [int(x) for x in r.integers(0, 12, size=n_seqs)]
