@@ -253,6 +253,11 @@ def test_backward_validation(lib):
     # head) pairs get 4 row groups each
     assert need == (64 // 4 + 1) * 48 * 128 * 128 * 4 + 2 * 64 * 48 * 4 * 129 * 4
     assert lib.gdn_backward_workspace_bytes(1, 0, 48) == 0
+    # row groups per (sequence, head): 4 up to 128 pairs, 2 up to 1536, then 1
+    for n_seqs, R in ((2, 4), (3, 2), (32, 2), (33, 1)):
+        T = 40 * n_seqs
+        ck = (T // 4 + n_seqs) * 48 * 128 * 128 * 4
+        assert lib.gdn_backward_workspace_bytes(n_seqs, T, 48) == ck + 2 * T * 48 * R * 129 * 4, n_seqs
     assert backward(lib, do=None) == NULL
     assert backward(lib, dg=None) == NULL
     assert backward(lib, Hv=40) == SHAPE
