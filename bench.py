@@ -104,6 +104,8 @@ def leg_prefill(args, ops, synth, torch):
     log(f"[prefill] {ev:.3f} ms/launch, {res['tokens_per_s'] / 1e6:.2f} M tok/s, "
         f"{res['hbm_gbps']:.0f} GB/s alg, {res['mfma_tflops']:.1f} TFLOP/s alg")
 
+    if "bf16o" not in args.prefill_forms:
+        return res, ci
     # the same launch with o written in bf16 (gdn_chunk_fwd_bf16o); not the headline
     o16 = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
 
@@ -115,6 +117,8 @@ def leg_prefill(args, ops, synth, torch):
     res.update(bf16o_event_ms=ev16, bf16o_tokens_per_s=T / (ev16 * 1e-3))
     log(f"[prefill] bf16 o: {ev16:.3f} ms/launch, {res['bf16o_tokens_per_s'] / 1e6:.2f} M tok/s")
 
+    if "gated" not in args.prefill_forms:
+        return res, ci
     # the same launch with the gates formed from bf16 projections (gdn_chunk_fwd_gated)
     gi = synth.gate_inputs(1007, T)
     ga = torch.from_numpy(gi.a.view("int16")).view(torch.bfloat16).cuda()
@@ -371,6 +375,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="prefill,decode,mixer,varlen,backward")
+    ap.add_argument("--prefill-forms", default="fp32,bf16o,gated",
+                    help="prefill launch forms timed by the prefill leg (fp32 is always timed)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -427,10 +433,12 @@ def main():
                             "launch_ms": round(pre["event_ms"], 4)}
         line["mfma"] = {"achieved": round(pre["mfma_tflops"], 1), "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(pre["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
-        line["prefill_bf16_o"] = {"launch_ms": round(pre["bf16o_event_ms"], 4),
-                                  "tokens_per_s": round(pre["bf16o_tokens_per_s"], 1)}
-        line["prefill_gated"] = {"launch_ms": round(pre["gated_event_ms"], 4),
-                                 "tokens_per_s": round(pre["gated_tokens_per_s"], 1)}
+        if "bf16o_event_ms" in pre:
+            line["prefill_bf16_o"] = {"launch_ms": round(pre["bf16o_event_ms"], 4),
+                                      "tokens_per_s": round(pre["bf16o_tokens_per_s"], 1)}
+        if "gated_event_ms" in pre:
+            line["prefill_gated"] = {"launch_ms": round(pre["gated_event_ms"], 4),
+                                     "tokens_per_s": round(pre["gated_tokens_per_s"], 1)}
     if "decode" in out:
         d = out["decode"]
         line["decode"] = {"state_GBps": round(d["state_gbps"], 1),

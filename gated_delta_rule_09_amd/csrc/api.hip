@@ -222,10 +222,10 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   } else if (n_seqs == 0 && T_total != 0) {
     return fail(GDN_ERR_SHAPE, "%s: T_total > 0 with no sequences", fn);
   }
-  // grid size: ceil(n_seqs * Hk / 8) * 8 * (Hv / Hk) * 2 blocks
-  if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
+  // grid size: ceil(n_seqs * Hk / 8) * 8 * (Hv / Hk) * 4 blocks
+  if (static_cast<int64_t>(n_seqs) * Hv * 4 + 32LL * Hv > 0x7fffffffLL)
     return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
-  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
+  const size_t ws_total = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv).total;
   const Range rq = range_of(q, T_total, q_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rk = range_of(k, T_total, k_tok_stride, static_cast<int64_t>(Hk) * dk, 2);
   const Range rv = range_of(v, T_total, v_tok_stride, static_cast<int64_t>(Hv) * dv, 2);
@@ -241,7 +241,7 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   const int32_t n_states = state_slot ? n_slots : n_seqs;
   const Range r0 = range_of(initial_state, n_states, ssz, ssz, 4);
   const Range rT = range_of(final_state, n_states, ssz, ssz, 4);
-  const Range rw = range_of(workspace, 1, 0, static_cast<int64_t>(ws.total), 1);
+  const Range rw = range_of(workspace, 1, 0, static_cast<int64_t>(ws_total), 1);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &r0})
     if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: o overlaps an input", fn);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro})
@@ -251,8 +251,8 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro, &r0, &rT})
     if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps a tensor", fn);
   if (n_seqs > 0) {
-    if (!workspace || workspace_bytes < ws.total)
-      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, ws.total);
+    if (!workspace || workspace_bytes < ws_total)
+      return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, ws_total);
     if (!aligned(workspace, 256))
       return fail(GDN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   }
@@ -263,7 +263,8 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(gdn::launch_chunk_fwd(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, gates,
                                           o, o_bf16, initial_state, final_state, state_slot,
-                                          cu_seqlens, n_seqs, T_total, Hk, Hv, scale, workspace, st),
+                                          n_states, cu_seqlens, n_seqs, T_total, Hk, Hv, scale,
+                                          workspace, st),
                     "prefill launch");
 }
 
@@ -368,7 +369,7 @@ gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* 
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl})
     if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_step: state overlaps an input");
   return hip_status(gdn::launch_decode_step(q, q_stride, k, k_stride, v, v_stride, g, beta, state,
-                                            state_slot, o, n_seqs, Hk, Hv, scale,
+                                            state_slot, n_slots, o, n_seqs, Hk, Hv, scale,
                                             static_cast<hipStream_t>(stream)),
                     "gdn_decode_step launch");
 }
@@ -412,7 +413,7 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &rsl})
     if (overlap(*in, rs)) return fail(GDN_ERR_ALIAS, "gdn_decode_tokens: state overlaps an input");
   return hip_status(gdn::launch_decode_tokens(q, q_stride, k, k_stride, v, v_stride, g, beta, state,
-                                              state_slot, o, n_seqs, n_tokens, Hk, Hv, scale,
+                                              state_slot, n_slots, o, n_seqs, n_tokens, Hk, Hv, scale,
                                               static_cast<hipStream_t>(stream)),
                     "gdn_decode_tokens launch");
 }
@@ -501,7 +502,8 @@ gdn_status gdn_decode_mixer_step(const uint16_t* x, int64_t x_stride, const uint
   if (overlap(ro, rs) || overlap(ro, rc) || overlap(rs, rc))
     return fail(GDN_ERR_ALIAS, "%s: out, state and conv_state overlap", fn);
   return hip_status(gdn::launch_decode_mixer(x, x_stride, conv_w, conv_bias, conv_state, gi, z,
-                                             z_stride, norm_w, state, state_slot, out, out_is_bf16 != 0,
+                                             z_stride, norm_w, state, state_slot, n_slots, out,
+                                             out_is_bf16 != 0,
                                              n_seqs, Hk, Hv, scale, l2_eps, norm_eps,
                                              static_cast<hipStream_t>(stream)),
                     "gdn_decode_mixer_step launch");
@@ -619,15 +621,17 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   gdn::ConvFront cf;
   cf.x = x; cf.xs = x_stride; cf.w = conv_w; cf.bias = conv_bias; cf.state = conv_state;
   cf.slots = state_slot;
+  cf.n_slots = n_rows;
   cf.l2_eps = l2_eps;
   gdn_status s = hip_status(gdn::launch_chunk_fwd(nullptr, 0, nullptr, 0, nullptr, 0,
                                                   gi, o, false, initial_state,
-                                                  final_state, state_slot, cu_seqlens, n_seqs,
-                                                  T_total, Hk, Hv, scale, workspace, st, &cf),
+                                                  final_state, state_slot, n_rows, cu_seqlens,
+                                                  n_seqs, T_total, Hk, Hv, scale, workspace, st,
+                                                  &cf),
                             "gdn_mixer_fwd prefill launch");
   if (s) return s;
   s = hip_status(gdn::launch_conv_state(x, x_stride, conv_state, cu_seqlens, n_seqs, T_total,
-                                        static_cast<int>(C), st, state_slot),
+                                        static_cast<int>(C), st, state_slot, n_rows),
                  "gdn_mixer_fwd conv state launch");
   if (s) return s;
   return hip_status(gdn::launch_gated_rmsnorm(o, z, z_stride, norm_w, out, out_is_bf16 != 0, T_total,

@@ -163,6 +163,7 @@ struct PrepParams {
   const uint16_t* x; int64_t xs;
   const uint16_t* conv_w; const float* conv_bias; const uint16_t* conv_state;
   const int32_t* conv_slots;  // nullptr: sequence n uses conv_state row n
+  int conv_n_slots;           // rows of the conv-state pool (with conv_slots)
   uint16_t* vout;
   float l2_eps;
   const int32_t* cu;          // nullptr: equal lengths seq_len
@@ -311,12 +312,14 @@ __device__ __forceinline__ void conv_rows(const PrepParams& p, const ConvRows& c
   float xin[7][8];
 #pragma unroll
   for (int k = 0; k < 7; ++k) bf16x8_to_f32(cr.raw[k], xin[k]);
-  if (t0 + r0 - 3 < s0 && p.conv_state) {
+  const int64_t row = p.conv_slots ? p.conv_slots[seq] : seq;
+  // a slot outside the pool reads no history (zeros)
+  const bool has_row = !p.conv_slots || static_cast<uint64_t>(row) < static_cast<uint64_t>(p.conv_n_slots);
+  if (t0 + r0 - 3 < s0 && p.conv_state && has_row) {
     // Rows before the sequence start: chunks start at s0 + 64 i and tasks at
     // multiples of 4, so this is the sequence's first chunk, r0 = 0, and input
     // rows 0, 1, 2 are the tokens s0 - 3, s0 - 2, s0 - 1: state taps 0, 1, 2.
     float st[24];
-    const int64_t row = p.conv_slots ? p.conv_slots[seq] : seq;
     const uint4* sp = reinterpret_cast<const uint4*>(p.conv_state + (row * C + ch0) * 3);
     bf16x8_to_f32(sp[0], st);
     bf16x8_to_f32(sp[1], st + 8);
@@ -621,6 +624,7 @@ struct ScanParams {
   int o_bf16;
   const float* h0; float* hT;
   const int32_t* slots;       // nullptr: sequence n uses state n of h0 / hT
+  int n_slots;                // states in the pool (with slots)
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* order;       // longest-first schedule (varlen)
   const int32_t* chunk_off;   // first chunk of each sequence (varlen)
@@ -675,6 +679,9 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   const int part = member % kParts;
   const int n = p.order ? p.order[rank] : rank;
   const int sn = p.slots ? p.slots[n] : n;    // state of sequence n
+  // a slot outside the pool (say -1 for padding) names no state: the whole
+  // work-group skips the sequence (no state read or written, o not written)
+  if (p.slots && static_cast<unsigned>(sn) >= static_cast<unsigned>(p.n_slots)) return;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -1115,7 +1122,7 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, b
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const GateInputs& gates,
                             void* o, bool o_bf16, const float* h0, float* hT,
-                            const int32_t* state_slot, const int32_t* cu,
+                            const int32_t* state_slot, int n_slots, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream, const ConvFront* conv) {
   if (n_seqs == 0) return hipSuccess;
@@ -1140,7 +1147,8 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
     if (conv) {
       pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
-      pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.l2_eps = conv->l2_eps;
+      pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.conv_n_slots = conv->n_slots;
+      pp.l2_eps = conv->l2_eps;
       pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
     }
     pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
@@ -1169,6 +1177,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   }
   sp.v = v; sp.vs = vs; sp.o = o; sp.o_bf16 = o_bf16 ? 1 : 0; sp.h0 = h0; sp.hT = hT;
   sp.slots = state_slot;
+  sp.n_slots = n_slots;
   sp.cu = cu; sp.order = cu ? order : nullptr; sp.chunk_off = chunk_off;
   sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;

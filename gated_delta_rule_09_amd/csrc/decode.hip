@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kTh) void decode_step_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
     int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    const int32_t* __restrict__ slots, float* __restrict__ o, int Hk, int Hv, float scale) {
+    const int32_t* __restrict__ slots, int n_slots, float* __restrict__ o, int Hk, int Hv,
+    float scale) {
   const int n = blockIdx.x / Hv;
   const int h = blockIdx.x - n * Hv;
   const int kh = h / (Hv / Hk);
@@ -50,6 +51,9 @@ __global__ __launch_bounds__(kTh) void decode_step_kernel(
   const int p = tid & 7;
   const int rg = tid >> 3;
   const int slot = kSlots ? slots[n] : n;
+  // a slot outside the pool (say -1 for a padding row) names no state: the
+  // work-group leaves the pool and its output rows untouched
+  if (kSlots && static_cast<unsigned>(slot) >= static_cast<unsigned>(n_slots)) return;
   float* S = state + (static_cast<int64_t>(slot) * Hv + h) * (kD * kD);
 
   // Stream the thread's rows first so all its state bytes are in flight.
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k,
     int64_t k_stride, const uint16_t* __restrict__ v, int64_t v_stride,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    const int32_t* __restrict__ slots, float* __restrict__ o, int Hk, int Hv, float scale) {
+    const int32_t* __restrict__ slots, int n_slots, float* __restrict__ o, int Hk, int Hv,
+    float scale) {
   const int n = blockIdx.x / Hv;
   const int h = blockIdx.x - n * Hv;
   const int kh = h / (Hv / Hk);
@@ -133,6 +138,9 @@ __global__ __launch_bounds__(kTh) void decode_tokens_kernel(
   const int p = tid & 7;
   const int rg = tid >> 3;
   const int slot = kSlots ? slots[n] : n;
+  // a slot outside the pool (say -1 for a padding row) names no state: the
+  // work-group leaves the pool and its output rows untouched
+  if (kSlots && static_cast<unsigned>(slot) >= static_cast<unsigned>(n_slots)) return;
   float* S = state + (static_cast<int64_t>(slot) * Hv + h) * (kD * kD);
 
   // From two tokens on, every token's k and q rows of this key head are staged
@@ -255,13 +263,13 @@ template <int kT>
 void launch_tokens(dim3 grid, hipStream_t stream, const uint16_t* q, int64_t q_stride,
                    const uint16_t* k, int64_t k_stride, const uint16_t* v, int64_t v_stride,
                    const float* g, const float* beta, float* state, const int32_t* state_slot,
-                   float* o, int Hk, int Hv, float scale) {
+                   int n_slots, float* o, int Hk, int Hv, float scale) {
   if (state_slot)
     hipLaunchKernelGGL((decode_tokens_kernel<kT, kTokThreads, true>), grid, dim3(kTokThreads), 0, stream, q, q_stride, k,
-                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+                       k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale);
   else
     hipLaunchKernelGGL((decode_tokens_kernel<kT, kTokThreads, false>), grid, dim3(kTokThreads), 0, stream, q, q_stride, k,
-                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+                       k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale);
 }
 
 }  // namespace
@@ -269,19 +277,19 @@ void launch_tokens(dim3 grid, hipStream_t stream, const uint16_t* q, int64_t q_s
 hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
                                 int64_t k_stride, const uint16_t* v, int64_t v_stride,
                                 const float* g, const float* beta, float* state,
-                                const int32_t* state_slot, float* o, int n_seqs, int n_tokens,
-                                int Hk, int Hv, float scale, hipStream_t stream) {
+                                const int32_t* state_slot, int n_slots, float* o, int n_seqs,
+                                int n_tokens, int Hk, int Hv, float scale, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv));
   switch (n_tokens) {
-    case 1: launch_tokens<1>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 2: launch_tokens<2>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 3: launch_tokens<3>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 4: launch_tokens<4>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 5: launch_tokens<5>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 6: launch_tokens<6>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 7: launch_tokens<7>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
-    case 8: launch_tokens<8>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale); break;
+    case 1: launch_tokens<1>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 2: launch_tokens<2>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 3: launch_tokens<3>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 4: launch_tokens<4>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 5: launch_tokens<5>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 6: launch_tokens<6>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 7: launch_tokens<7>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
+    case 8: launch_tokens<8>(grid, stream, q, q_stride, k, k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -290,16 +298,16 @@ hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint1
 hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
                               int64_t k_stride, const uint16_t* v, int64_t v_stride,
                               const float* g, const float* beta, float* state,
-                              const int32_t* state_slot, float* o, int n_seqs, int Hk, int Hv,
-                              float scale, hipStream_t stream) {
+                              const int32_t* state_slot, int n_slots, float* o, int n_seqs,
+                              int Hk, int Hv, float scale, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv));
   if (state_slot)
     hipLaunchKernelGGL((decode_step_kernel<kStepThreads, true>), grid, dim3(kStepThreads), 0, stream, q, q_stride, k,
-                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+                       k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale);
   else
     hipLaunchKernelGGL((decode_step_kernel<kStepThreads, false>), grid, dim3(kStepThreads), 0, stream, q, q_stride, k,
-                       k_stride, v, v_stride, g, beta, state, state_slot, o, Hk, Hv, scale);
+                       k_stride, v, v_stride, g, beta, state, state_slot, n_slots, o, Hk, Hv, scale);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct MixerParams {
   const float* A_log; const float* dt_bias;
   const uint16_t* z; int64_t zs;
   const float* norm_w;
-  float* state; const int32_t* slots;
+  float* state; const int32_t* slots; int n_slots;
   void* out; int out_bf16;
   int Hk, Hv;
   float scale, l2_eps, norm_eps;
@@ -96,6 +96,9 @@ __global__ __launch_bounds__(kThreads) void decode_mixer_kernel(MixerParams p) {
   const int pl = tid & (kLpr - 1);
   const int rg = tid / kLpr;
   const int slot = p.slots ? p.slots[n] : n;
+  // a slot outside the pool (say -1 for a padding row) names no state or conv
+  // window: the work-group leaves both pools and its output rows untouched
+  if (p.slots && static_cast<unsigned>(slot) >= static_cast<unsigned>(p.n_slots)) return;
   const int C = (2 * p.Hk + p.Hv) * kD;
 
   // ---- the conv inputs of this thread's (at most two) channels -------------
@@ -245,7 +248,8 @@ hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* co
                                const float* conv_bias, uint16_t* conv_state,
                                const GateInputs& gates, const uint16_t* z, int64_t zs,
                                const float* norm_w, float* state, const int32_t* state_slot,
-                               void* out, bool out_bf16, int n_seqs, int Hk, int Hv, float scale,
+                               int n_slots, void* out, bool out_bf16, int n_seqs, int Hk, int Hv,
+                               float scale,
                                float l2_eps, float norm_eps, hipStream_t stream) {
   if (n_seqs == 0) return hipSuccess;
   MixerParams mp;
@@ -253,7 +257,8 @@ hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* co
   mp.g = gates.g; mp.beta = gates.beta; mp.ga = gates.a; mp.gb = gates.b;
   mp.gas = gates.a_stride; mp.gbs = gates.b_stride; mp.A_log = gates.A_log; mp.dt_bias = gates.dt_bias;
   mp.z = z; mp.zs = zs; mp.norm_w = norm_w;
-  mp.state = state; mp.slots = state_slot; mp.out = out; mp.out_bf16 = out_bf16 ? 1 : 0;
+  mp.state = state; mp.slots = state_slot; mp.n_slots = n_slots;
+  mp.out = out; mp.out_bf16 = out_bf16 ? 1 : 0;
   mp.Hk = Hk; mp.Hv = Hv; mp.scale = scale; mp.l2_eps = l2_eps; mp.norm_eps = norm_eps;
   const dim3 grid(static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hk));
   const bool gated = gates.a != nullptr;

@@ -11,14 +11,14 @@ namespace gdn {
 hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
                               int64_t k_stride, const uint16_t* v, int64_t v_stride,
                               const float* g, const float* beta, float* state,
-                              const int32_t* state_slot, float* o, int n_seqs, int Hk, int Hv,
-                              float scale, hipStream_t stream);
+                              const int32_t* state_slot, int n_slots, float* o, int n_seqs,
+                              int Hk, int Hv, float scale, hipStream_t stream);
 
 hipError_t launch_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t* k,
                                 int64_t k_stride, const uint16_t* v, int64_t v_stride,
                                 const float* g, const float* beta, float* state,
-                                const int32_t* state_slot, float* o, int n_seqs, int n_tokens,
-                                int Hk, int Hv, float scale, hipStream_t stream);
+                                const int32_t* state_slot, int n_slots, float* o, int n_seqs,
+                                int n_tokens, int Hk, int Hv, float scale, hipStream_t stream);
 
 hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const float* bias,
                          uint16_t* y, int64_t ys, uint16_t* conv_state, const int32_t* cu,
@@ -61,7 +61,8 @@ hipError_t launch_decode_mixer(const uint16_t* x, int64_t xs, const uint16_t* co
                                const float* conv_bias, uint16_t* conv_state,
                                const GateInputs& gates, const uint16_t* z, int64_t zs,
                                const float* norm_w, float* state, const int32_t* state_slot,
-                               void* out, bool out_bf16, int n_seqs, int Hk, int Hv, float scale,
+                               int n_slots, void* out, bool out_bf16, int n_seqs, int Hk, int Hv,
+                               float scale,
                                float l2_eps, float norm_eps, hipStream_t stream);
 
 // The conv front of the fused mixer prefill: the prep kernel computes q, k
@@ -76,24 +77,28 @@ struct ConvFront {
   const float* bias = nullptr;
   const uint16_t* state = nullptr;
   const int32_t* slots = nullptr;   // nullptr: sequence n uses conv state row n
+  int n_slots = 0;                  // rows of the conv-state pool (with slots)
   float l2_eps = 1e-6f;
 };
 
 // state_slot != nullptr: sequence n reads h0[state_slot[n]] and writes
-// hT[state_slot[n]] (h0 == hT: a state pool updated in place).
+// hT[state_slot[n]] (h0 == hT: a state pool of n_slots rows updated in place);
+// a sequence whose slot lies outside [0, n_slots) is skipped.
 hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
                             const uint16_t* v, int64_t vs, const GateInputs& gates,
                             void* o, bool o_bf16, const float* h0, float* hT,
-                            const int32_t* state_slot, const int32_t* cu,
+                            const int32_t* state_slot, int n_slots, const int32_t* cu,
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream,
                             const ConvFront* conv = nullptr);
 
 // The new conv state [n_seqs, C, 3] (last three inputs of old state ++
-// sequence), after every read of the old one.
+// sequence), after every read of the old one.  With slots, sequence n updates
+// row slots[n] of a pool of n_slots rows (none if the slot is outside it).
 hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state,
                              const int32_t* cu, int n_seqs, int T_total, int C,
-                             hipStream_t stream, const int32_t* slots = nullptr);
+                             hipStream_t stream, const int32_t* slots = nullptr,
+                             int n_slots = 0);
 
 // Backward of the rule (backward.hip): workspace of (T_total / 4 + n_seqs) x
 // Hv x 64 KB of checkpointed states plus the partial dq, dk, dg, dbeta of

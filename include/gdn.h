@@ -7,8 +7,9 @@
  * heads shared by 48 value heads, head dim 128, a kernel-4 causal conv in
  * front, a gated RMS-norm after, and an fp32 recurrent state.  The rule itself
  * (the "erase, then write" update with a forget gate described in the
- * "Attention Layer Details" section of "Agnes-3.0-Flash Deep Dive: A 33B
- * Hybrid-Attention Multimodal Model") is, per value head h with key head
+ * explanatory paragraph on the Gated Delta Rule that follows the
+ * "Feed-Forward and Positional Encoding" section of "Agnes-3.0-Flash Deep
+ * Dive: A 33B Hybrid-Attention Multimodal Model") is, per value head h with key head
  * kh = h / (Hv / Hk):
  *
  *     S_t = S_{t-1} * alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
@@ -172,8 +173,10 @@ gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const ui
  *               in place: sequence n starts from state[state_slot[n]] and
  *               leaves its final state there; an empty sequence leaves its
  *               slot unchanged; slots not named are not touched
- *   state_slot  [n_seqs] int32 device array, required when n_seqs > 0; slots
- *               distinct and in [0, n_slots) (not checked on the device)
+ *   state_slot  [n_seqs] int32 device array, required when n_seqs > 0; the
+ *               slots in [0, n_slots) must be distinct; a slot outside
+ *               [0, n_slots) (say -1) marks a padding sequence: no state is
+ *               read or written for it and its rows of o are not written
  *   o           [T_total, Hv, dv] fp32 (o_is_bf16 == 0) or bf16 (as
  *               gdn_chunk_fwd_bf16o), must not overlap the state pool
  * Every other argument, the workspace and the errors as for gdn_chunk_fwd.
@@ -238,8 +241,11 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  *               windows are pools of n_slots rows updated in place (serving):
  *               initial_state == final_state = [n_slots, Hv, d, d] and
  *               conv_state [n_slots, C, 3]; sequence n uses row
- *               state_slot[n] of both (distinct, in [0, n_slots), not checked
- *               on the device), other rows are not touched
+ *               state_slot[n] of both (slots in [0, n_slots) distinct), other
+ *               rows are not touched.  A slot outside [0, n_slots) (say -1)
+ *               marks a padding sequence: no state or conv-window row is read
+ *               or written for it (its conv history is taken as zeros) and its
+ *               rows of out are unspecified
  *   l2_eps, norm_eps  the L2 and RMS epsilons (finite, >= 0)
  *   workspace   gdn_mixer_fwd_workspace_bytes() bytes, 256-byte aligned: the
  *               prefill workspace, v after the conv (T_total x Hv x d bf16)
@@ -290,8 +296,10 @@ gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_to
  *   g, beta     [n_seqs, Hv] fp32, contiguous
  *   state       [n_slots, Hv, dv, dk] fp32, read and written in place
  *   state_slot  [n_seqs] int32 device array or NULL: sequence n uses slot
- *               state_slot[n] (NULL: slot n).  Slots must be distinct and in
- *               [0, n_slots); not checked on the device.
+ *               state_slot[n] (NULL: slot n).  Slots in [0, n_slots) must be
+ *               distinct; a slot outside [0, n_slots) (say -1 for a padding
+ *               row of a fixed-size batch) makes the kernel skip sequence n:
+ *               no state is read or written and its row of o is not written.
  *   o           [n_seqs, Hv, dv] fp32; must not overlap state or the inputs
  */
 gdn_status gdn_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
@@ -351,7 +359,9 @@ gdn_status gdn_decode_tokens(const uint16_t* q, int64_t q_stride, const uint16_t
  *   state       [n_slots, Hv, d, d] fp32, updated in place
  *   state_slot  [n_seqs] int32 device array or NULL: sequence n uses slot
  *               state_slot[n] of both conv_state and state (NULL: slot n);
- *               slots distinct and in [0, n_slots), not checked on the device
+ *               slots in [0, n_slots) distinct; a slot outside [0, n_slots)
+ *               (say -1) skips sequence n: neither pool is read or written and
+ *               its row of out is not written
  *   out         [n_seqs, Hv, d], fp32 (out_is_bf16 == 0) or bf16 (rounded to
  *               nearest even); must not overlap any other tensor
  *   d           must be 128; Hv / Hk must be 1, 2, 3 or 4
@@ -388,8 +398,8 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  *     L = sum(grad_o * o) + sum(grad_final_state * S_T)
  * (o and S_T as gdn_chunk_fwd computes them from the same inputs) with
  * respect to q, k, v, g, beta and the initial states.  The chain rule is
- * taken through each token's erase-then-write update of the "Attention Layer
- * Details" section of the deep-dive page, in reverse token order, in fp32:
+ * taken through each token's erase-then-write update (the deep-dive page's
+ * paragraph on the Gated Delta Rule), in reverse token order, in fp32:
  * one kernel re-runs the recurrence and records the state before every
  * 4th token of each sequence in the workspace, a second walks the tokens
  * backwards holding dL/dS and rebuilding each token's state from the

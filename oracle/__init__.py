@@ -14,7 +14,7 @@ Functions (each documented in gdn_oracle.c with its source):
   conv1d(...)         causal depthwise conv k=4 + SiLU + per-head L2
   gated_rmsnorm(...)  (o / rms(o)) * w * silu(z)
   round_bf16(...)     round-to-nearest-even onto the bfloat16 grid
-  chunk_map(...)      varlen schedule / chunk table (integer bookkeeping)
+  chunk_map(...)      varlen chunk offsets / chunk table (integer bookkeeping)
 """
 import ctypes
 import os
@@ -56,7 +56,7 @@ def _load():
                                          ctypes.c_int32, ctypes.c_double, ctypes.c_int32,
                                          ctypes.c_int32]
     lib.oracle_gated_rmsnorm.restype = ctypes.c_int
-    lib.oracle_chunk_map.argtypes = [_ip, ctypes.c_int32, ctypes.c_int32, _ip, _ip, _ip]
+    lib.oracle_chunk_map.argtypes = [_ip, ctypes.c_int32, ctypes.c_int32, _ip, _ip]
     lib.oracle_chunk_map.restype = ctypes.c_int
     lib.oracle_gate_prep.argtypes = [_dp, ctypes.c_int64, _dp, ctypes.c_int64, _dp, _dp, _dp, _dp,
                                      ctypes.c_int64, ctypes.c_int32]
@@ -230,17 +230,15 @@ def round_bf16(x):
 
 
 def chunk_map(cu_seqlens, chunk=64):
-    """(order [N], chunk_off [N+1], tab [n_chunks, 3]) as int32 numpy arrays."""
+    """(chunk_off [N+1], tab [n_chunks, 3]) as int32 numpy arrays."""
     lib = _load()
     cu = _i32(cu_seqlens)
     N = cu.shape[0] - 1
     lens = np.diff(cu.astype(np.int64))
     n_chunks = int(np.sum((lens + chunk - 1) // chunk))
-    order = np.zeros(max(N, 1), dtype=np.int32)
     off = np.zeros(N + 1, dtype=np.int32)
     tab = np.zeros((max(n_chunks, 1), 3), dtype=np.int32)
-    rc = lib.oracle_chunk_map(_ptr(cu, _ip), N, chunk, _ptr(order, _ip), _ptr(off, _ip),
-                              _ptr(tab, _ip))
+    rc = lib.oracle_chunk_map(_ptr(cu, _ip), N, chunk, _ptr(off, _ip), _ptr(tab, _ip))
     if rc:
         raise ValueError(f"oracle_chunk_map failed ({rc})")
-    return order[:N], off, tab[:n_chunks]
+    return off, tab[:n_chunks]

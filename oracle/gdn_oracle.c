@@ -521,28 +521,16 @@ int oracle_gate_prep(const double* a, int64_t a_stride, const double* b, int64_t
 /* ---------------------------------------------------------------------------
  * Varlen chunk map (integer bookkeeping of the chunked prefill), from its
  * definition:
- *   order[r]     sequence ids sorted by length, longest first, ties by id
  *   chunk_off[n] sum over m < n of ceil(len_m / C)
  *   tab[c]       (sequence, first token, token count) of chunk c, chunks of
  *                C tokens restarting at every sequence start
- * Plain insertion sort and loops.
+ * Plain loops.  (The order in which a kernel schedules the sequences is a
+ * performance choice, not part of the result, and is not defined here.)
  * ------------------------------------------------------------------------- */
-int oracle_chunk_map(const int32_t* cu, int32_t n_seqs, int32_t C, int32_t* order,
-                     int32_t* chunk_off, int32_t* tab)
+int oracle_chunk_map(const int32_t* cu, int32_t n_seqs, int32_t C, int32_t* chunk_off,
+                     int32_t* tab)
 {
     if (!cu || n_seqs < 0 || C <= 0) return ORACLE_ERR_ARG;
-    for (int32_t i = 0; i < n_seqs; ++i) order[i] = i;
-    for (int32_t i = 1; i < n_seqs; ++i) {
-        int32_t cur = order[i];
-        int32_t lc = cu[cur + 1] - cu[cur];
-        int32_t j = i - 1;
-        /* move while the earlier entry is shorter (stable: ties keep id order) */
-        while (j >= 0 && (cu[order[j] + 1] - cu[order[j]]) < lc) {
-            order[j + 1] = order[j];
-            --j;
-        }
-        order[j + 1] = cur;
-    }
     int32_t c = 0;
     for (int32_t n = 0; n < n_seqs; ++n) {
         chunk_off[n] = c;

@@ -341,13 +341,10 @@ def test_round_bf16_matches_torch_cast():
                                   [300, 1, 64, 65, 129, 0, 0, 2]])
 def test_chunk_map_brute_force(lens):
     """The varlen chunk map against a direct enumeration: every sequence cut into
-    64-token pieces from its own start (the last one partial), sequences ranked
-    longest first with ties broken by id."""
+    64-token pieces from its own start (the last one partial)."""
     lens = np.asarray(lens, dtype=np.int64)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    order, off, tab = oracle.chunk_map(cu)
-    ranked = sorted(range(len(lens)), key=lambda n: (-lens[n], n))
-    assert order.tolist() == ranked
+    off, tab = oracle.chunk_map(cu)
     rows, offs = [], [0]
     for n, L in enumerate(lens):
         start = int(cu[n])
