@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -178,6 +179,42 @@ gdn_status gdn_chunk_map(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_to
                     "gdn_chunk_map launch");
 }
 
+// ---- static workspace of gdn_chunk_fwd_noalloc ------------------------------
+// A file-scope device array stands in for the caller's workspace in the one
+// prefill entry point that allocates nothing.  Each GPU the library runs on
+// holds its own copy from module load until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address of the current GPU's copy comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is passed on.
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current GPU's copy of `scratch`.
+gdn_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gdn_chunk_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_fwd_noalloc: device %d beyond the %d supported", dev,
+                kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return hip_status(g_scratch_err[dev], "gdn_chunk_fwd_noalloc: hipGetSymbolAddress(scratch)");
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
 // Shared by gdn_chunk_fwd (fp32 o) and gdn_chunk_fwd_bf16o (bf16 o).
 // The common host side of the prefill entry points.  `gates` holds either g,
 // beta or the projections a, b with A_log, dt_bias; with `state_slot` the
@@ -189,7 +226,7 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
                             const int32_t* state_slot, int32_t n_slots,
                             const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                             int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool use_scratch = false) {
   const bool projected = gates.a != nullptr || gates.b != nullptr || gates.A_log != nullptr ||
                          gates.dt_bias != nullptr;
   const bool gates_given = projected ? (gates.a && gates.b && gates.A_log && gates.dt_bias)
@@ -241,7 +278,7 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   const int32_t n_states = state_slot ? n_slots : n_seqs;
   const Range r0 = range_of(initial_state, n_states, ssz, ssz, 4);
   const Range rT = range_of(final_state, n_states, ssz, ssz, 4);
-  const Range rw = range_of(workspace, 1, 0, static_cast<int64_t>(ws_total), 1);
+  const Range rw = range_of(use_scratch ? nullptr : workspace, 1, 0, static_cast<int64_t>(ws_total), 1);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &r0})
     if (overlap(*in, ro)) return fail(GDN_ERR_ALIAS, "%s: o overlaps an input", fn);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro})
@@ -250,7 +287,12 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
     return fail(GDN_ERR_ALIAS, "%s: final_state partially overlaps initial_state", fn);
   for (const Range* in : {&rq, &rk, &rv, &rg, &rb, &ra, &rb2, &rA, &rdt, &rsl, &ro, &r0, &rT})
     if (overlap(*in, rw)) return fail(GDN_ERR_ALIAS, "%s: workspace overlaps a tensor", fn);
-  if (n_seqs > 0) {
+  if (n_seqs > 0 && use_scratch) {
+    if (ws_total > kScratchBytes)
+      return fail(GDN_ERR_WORKSPACE,
+                  "%s: needs %zu bytes of workspace, the static buffer holds %zu (use gdn_chunk_fwd "
+                  "with a caller workspace)", fn, ws_total, kScratchBytes);
+  } else if (n_seqs > 0) {
     if (!workspace || workspace_bytes < ws_total)
       return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, ws_total);
     if (!aligned(workspace, 256))
@@ -258,6 +300,10 @@ static gdn_status chunk_fwd(const char* fn, const uint16_t* q, int64_t q_tok_str
   }
   if (cu_seqlens && env_validate_seqlens()) {
     const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
+    if (s) return s;
+  }
+  if (use_scratch && n_seqs > 0) {   // every argument is valid: only now touch the device
+    const gdn_status s = scratch_address(&workspace);
     if (s) return s;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -286,6 +332,18 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
                    given_gates(g, beta), o, false, initial_state, final_state, nullptr, 0,
                    cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale, workspace, workspace_bytes,
                    stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                                 int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                                 const float* g, const float* beta, float* o,
+                                 const float* initial_state, float* final_state,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                 int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                 void* stream) {
+  return chunk_fwd("gdn_chunk_fwd_noalloc", q, q_tok_stride, k, k_tok_stride, v, v_tok_stride,
+                   given_gates(g, beta), o, false, initial_state, final_state, nullptr, 0,
+                   cu_seqlens, n_seqs, T_total, Hk, Hv, dk, dv, scale, nullptr, 0, stream, true);
 }
 
 gdn_status gdn_chunk_fwd_bf16o(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,

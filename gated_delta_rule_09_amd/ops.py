@@ -31,6 +31,8 @@ _SIGS = {
     "gdn_chunk_fwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "gdn_chunk_fwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gdn_chunk_fwd_noalloc": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "gdn_chunk_fwd_bf16o": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "gdn_chunk_fwd_pooled": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _vp,
@@ -231,6 +233,43 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             _ptr(cu_seqlens), n_seqs, T, Hk, Hv, dk, dv, scale, _ptr(workspace),
             ws_bytes, _stream())
     _check(st, "gdn_chunk_fwd_bf16o" if o_bf16 else "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, o: torch.Tensor, *,
+                          initial_state: Optional[torch.Tensor] = None,
+                          final_state: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, n_seqs: Optional[int] = None,
+                          scale: float = 1.0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_chunk_fwd into caller-provided o (fp32) and final_state, with the
+    library's static device workspace instead of a workspace argument (nothing
+    is allocated, here or in the library).  Returns (o, final_state)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 3)
+        _inner_contig(t, nm)
+    _need(g, "g", torch.float32, 2)
+    _need(beta, "beta", torch.float32, 2)
+    _need(o, "o", torch.float32, 3)
+    if not (g.is_contiguous() and beta.is_contiguous() and o.is_contiguous()):
+        raise ValueError("g, beta and o must be contiguous")
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        n_seqs = cu_seqlens.shape[0] - 1
+    elif n_seqs is None:
+        n_seqs = initial_state.shape[0] if initial_state is not None else 1
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _need(t, nm, torch.float32, 4)
+            if not t.is_contiguous():
+                raise ValueError(f"{nm} must be contiguous")
+    st = lib().gdn_chunk_fwd_noalloc(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v),
+                                     v.stride(0), _ptr(g), _ptr(beta), _ptr(o),
+                                     _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens),
+                                     n_seqs, T, Hk, Hv, dk, dv, scale, _stream())
+    _check(st, "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

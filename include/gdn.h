@@ -61,7 +61,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -148,6 +148,33 @@ gdn_status gdn_chunk_fwd(const uint16_t* q, int64_t q_tok_stride, const uint16_t
                          const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total, int32_t Hk,
                          int32_t Hv, int32_t dk, int32_t dv, float scale, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * result and errors as gdn_chunk_fwd, without the workspace arguments; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call).
+ * The workspace is instead a static 64 MiB device array of the library, one
+ * copy per GPU, held from the library's load until the process ends:
+ *   - the call is rejected with GDN_ERR_WORKSPACE when
+ *     gdn_chunk_fwd_workspace_bytes(n_seqs, T_total, Hk, Hv, dk) exceeds
+ *     64 MiB (about 3,700 tokens at 16 key / 48 value heads);
+ *   - every call on one GPU uses that GPU's array, which keeps the last
+ *     call's contents (each call overwrites what it reads; nothing has to
+ *     start at zero), so calls that may run concurrently on one GPU (several
+ *     streams or host threads) race and must be ordered by the caller;
+ *   - the first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress) with that device current; argument errors are
+ *     found before that, as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_noalloc(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
+                                 int64_t k_tok_stride, const uint16_t* v, int64_t v_tok_stride,
+                                 const float* g, const float* beta, float* o,
+                                 const float* initial_state, float* final_state,
+                                 const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
+                                 int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                                 void* stream);
 
 /*
  * gdn_chunk_fwd_bf16o -- gdn_chunk_fwd with o written as bf16 (each element

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
