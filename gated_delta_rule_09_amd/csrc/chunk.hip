@@ -42,7 +42,9 @@
 // accumulation is fp32 throughout.  The per-chunk state never leaves the
 // registers, and fragment reads are lane-contiguous 16-byte LDS loads.
 // Work-groups that share a key head get block ids on the same XCD (L2).
+#include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -110,6 +112,16 @@ constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    
 // Per chunk the state wave leaves the fp16 S0 (as B operands, tile t, block kb
 // at fragment 4 t + kb) and U (fragments 8 + 2 t, 9 + 2 t) for the output wave.
 constexpr int kXBytes = 12 * kFrag;
+
+// The overlapped prefill: segments of kSegChunks chunks for sequences of at
+// least kSegMinChunks chunks, when the scan leaves kSegMinIdleCUs or more
+// compute units idle.  kScanLdsPad bytes of LDS added to each scan
+// work-group leave its compute unit too little for a prep work-group, so the
+// preps run on the idle units and take nothing from the scan's memory pipe.
+constexpr int kSegChunks = 256;
+constexpr int kSegMinChunks = 2 * kSegChunks;
+constexpr int kSegMinIdleCUs = 32;
+constexpr int kScanLdsPad = 48 * 1024;
 static_assert(kStagePieces == kKPieces + kVBPieces + kVTilePieces, "stage = K rows + value blob + V tile");
 static_assert(kOffT % 16 == 0 && kOffQ % 16 == 0, "staged parts are whole pieces");
 
@@ -172,6 +184,9 @@ struct PrepParams {
   unsigned char* kq;          // [max_chunks][Hk][kKQBytes]
   unsigned char* vb;          // [max_chunks][Hv][kVBytes]
   int n_seqs, seq_len, Hk, Hv, group;
+  // equal lengths: this launch prepares chunks seg_c0 .. seg_c0 + seg_nc - 1
+  // of every sequence (seg_nc = 0: all of them)
+  int seg_c0, seg_nc;
   float scale;
 };
 
@@ -376,7 +391,7 @@ template <bool kGated, bool kConv>
 __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
   const int kh = blockIdx.x;
-  const int c = blockIdx.y;
+  int c = blockIdx.y;     // chunk (index into the blob arrays)
   int t0, len, seq, s0;
   if (p.cu) {
     if (c >= p.chunk_off[p.n_seqs]) return;
@@ -386,8 +401,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     s0 = kConv ? p.cu[seq] : 0;
   } else {
     const int nc = (p.seq_len + kC - 1) / kC;
-    seq = c / nc;
-    const int i = c - seq * nc;
+    const int snc = p.seg_nc ? p.seg_nc : nc;
+    seq = c / snc;
+    const int i = p.seg_c0 + (c - seq * snc);
+    c = seq * nc + i;
     s0 = seq * p.seq_len;
     t0 = s0 + i * kC;
     len = min(kC, p.seq_len - i * kC);
@@ -632,6 +649,10 @@ struct ScanParams {
   const unsigned char* vb;
   int n_seqs, seq_len, Hk, Hv, group;
   int n_chain_groups;         // n_seqs * Hk
+  // equal lengths: this launch runs chunks c_base .. c_base + c_count - 1 of
+  // every sequence, from state h0 to state hT (c_base = 0 and c_count >= the
+  // chunks of a sequence: all of it)
+  int c_base, c_count;
 };
 
 // Two stage buffers (the chunk being computed, the one being copied in) and
@@ -694,9 +715,9 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
     seq_len = p.cu[n + 1] - seq_start;
     chunk0 = p.chunk_off[n];
   } else {
-    seq_start = n * p.seq_len;
-    seq_len = p.seq_len;
-    chunk0 = n * ((p.seq_len + kC - 1) / kC);
+    seq_start = n * p.seq_len + p.c_base * kC;
+    seq_len = min(p.seq_len - p.c_base * kC, p.c_count * kC);
+    chunk0 = n * ((p.seq_len + kC - 1) / kC) + p.c_base;
   }
   const int n_chunks = (seq_len + kC - 1) / kC;
 
@@ -1088,6 +1109,52 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   else output_wave(std::integral_constant<int, kOutWaves - 1>{});
 }
 
+static_assert(sizeof(ScanSmem) + kScanLdsPad <= 160 * 1024, "padded scan work-group fits a CU");
+static_assert(sizeof(ScanSmem) + kScanLdsPad + sizeof(PrepSmem) > 160 * 1024,
+              "no prep work-group fits beside a padded scan work-group");
+
+hipError_t launch_prep(const PrepParams& pp, dim3 grid, bool conv, hipStream_t stream) {
+  if (conv) {
+    if (pp.ga)
+      hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kThreads), 0, stream, pp);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kThreads), 0, stream, pp);
+  } else {
+    if (pp.ga)
+      hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kThreads), 0, stream, pp);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kThreads), 0, stream, pp);
+  }
+  return hipGetLastError();
+}
+
+// The second stream and the events of the overlapped prefill, one set per
+// device, made on first use (with that device current) and kept until the
+// process ends.  The lock keeps one call's records and waits together.
+struct Overlap {
+  std::mutex mu;
+  hipStream_t side = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t done[2] = {};
+};
+
+Overlap* overlap_of_current_device() {
+  static Overlap ov[64];
+  static std::once_flag once[64];
+  static bool ok[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::call_once(once[dev], [&] {
+    Overlap& o = ov[dev];
+    bool good = hipStreamCreateWithFlags(&o.side, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&o.start, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < 2 && good; ++i)
+      good = hipEventCreateWithFlags(&o.done[i], hipEventDisableTiming) == hipSuccess;
+    ok[dev] = good;
+  });
+  return ok[dev] ? &ov[dev] : nullptr;
+}
+
 // Compute units of the current device, looked up once per device (calls from
 // several host threads may race to fill an entry; they store the same value).
 int compute_units() {
@@ -1114,8 +1181,10 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, b
   ws.kq_off = ws.chunk_tab_off + up(sizeof(int32_t) * 3 * ws.max_chunks);
   ws.v_off = ws.kq_off + up(ws.max_chunks * static_cast<size_t>(Hk) * kKQBytes);
   ws.conv_v_off = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
-  ws.total = ws.conv_v_off +
-             (conv_v ? up(static_cast<size_t>(T_total) * static_cast<size_t>(Hv) * kD * 2) : 0);
+  ws.carry_off = ws.conv_v_off +
+                 (conv_v ? up(static_cast<size_t>(T_total) * static_cast<size_t>(Hv) * kD * 2) : 0);
+  const bool carry = n_seqs > 0 && T_total / n_seqs >= kSegMinChunks * kC;
+  ws.total = ws.carry_off + (carry ? static_cast<size_t>(n_seqs) * Hv * kD * kD * sizeof(float) : 0);
   return ws;
 }
 
@@ -1132,44 +1201,30 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + ws.chunk_off_off);
   int32_t* chunk_tab = reinterpret_cast<int32_t*>(base + ws.chunk_tab_off);
   const int seq_len = cu ? 0 : T_total / n_seqs;
+  const int nc = cu ? 0 : (seq_len + kC - 1) / kC;    // chunks per sequence (equal lengths)
   int n_chunk_slots;   // grid of the prep kernel
   if (cu) {
     const hipError_t e = launch_chunk_map(cu, n_seqs, T_total, order, chunk_off, chunk_tab, stream);
     if (e != hipSuccess) return e;
     n_chunk_slots = static_cast<int>(ws.max_chunks);
   } else {
-    n_chunk_slots = n_seqs * ((seq_len + kC - 1) / kC);
+    n_chunk_slots = n_seqs * nc;
   }
-  if (T_total > 0 && n_chunk_slots > 0) {
-    PrepParams pp{};
-    pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = gates.g; pp.beta = gates.beta;
-    pp.ga = gates.a; pp.gb = gates.b; pp.gas = gates.a_stride; pp.gbs = gates.b_stride;
-    pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
-    if (conv) {
-      pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
-      pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.conv_n_slots = conv->n_slots;
-      pp.l2_eps = conv->l2_eps;
-      pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
-    }
-    pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
-    pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
-    pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
-    pp.scale = scale;
-    const dim3 grid(Hk, n_chunk_slots);
-    if (conv) {
-      if (gates.a)
-        hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kThreads), 0, stream, pp);
-      else
-        hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kThreads), 0, stream, pp);
-    } else {
-      if (gates.a)
-        hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kThreads), 0, stream, pp);
-      else
-        hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kThreads), 0, stream, pp);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  PrepParams pp{};
+  pp.q = q; pp.k = k; pp.qs = qs; pp.ks = ks; pp.g = gates.g; pp.beta = gates.beta;
+  pp.ga = gates.a; pp.gb = gates.b; pp.gas = gates.a_stride; pp.gbs = gates.b_stride;
+  pp.A_log = gates.A_log; pp.dt_bias = gates.dt_bias;
+  if (conv) {
+    pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
+    pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.conv_n_slots = conv->n_slots;
+    pp.l2_eps = conv->l2_eps;
+    pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
   }
+  pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
+  pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
+  pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
+  pp.scale = scale;
+
   ScanParams sp;
   if (conv) {
     v = reinterpret_cast<const uint16_t*>(base + ws.conv_v_off);
@@ -1182,8 +1237,56 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   sp.kq = base + ws.kq_off; sp.vb = base + ws.v_off;
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;
   sp.n_chain_groups = n_seqs * Hk;
+  sp.c_base = 0; sp.c_count = nc;
   const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kParts;
-  if (blocks <= compute_units())
+  const int cus = compute_units();
+
+  // Long equal-length sequences whose scan leaves compute units idle: the
+  // prep of segment i + 1 runs on a second stream, on those idle units, while
+  // the scan works through segment i.
+  if (!cu && !state_slot && T_total > 0 && nc >= kSegMinChunks && blocks + kSegMinIdleCUs <= cus &&
+      ws.total > ws.carry_off) {
+    Overlap* ov = overlap_of_current_device();
+    if (ov) {
+      std::lock_guard<std::mutex> lock(ov->mu);
+      float* carry = reinterpret_cast<float*>(base + ws.carry_off);
+      const int n_seg = (nc + kSegChunks - 1) / kSegChunks;
+      auto prep_seg = [&](int s, hipStream_t st) {
+        pp.seg_c0 = s * kSegChunks;
+        pp.seg_nc = std::min(kSegChunks, nc - pp.seg_c0);
+        return launch_prep(pp, dim3(Hk, n_seqs * pp.seg_nc), conv != nullptr, st);
+      };
+      hipError_t e = prep_seg(0, stream);
+      if (e == hipSuccess) e = hipEventRecord(ov->start, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ov->side, ov->start, 0);
+      for (int s = 0; s < n_seg && e == hipSuccess; ++s) {
+        if (s + 1 < n_seg) {
+          // done[(s + 1) & 1] was last waited on (enqueued) in step s - 1
+          e = prep_seg(s + 1, ov->side);
+          if (e == hipSuccess) e = hipEventRecord(ov->done[(s + 1) & 1], ov->side);
+          if (e != hipSuccess) break;
+        }
+        if (s > 0) e = hipStreamWaitEvent(stream, ov->done[s & 1], 0);
+        if (e != hipSuccess) break;
+        sp.c_base = s * kSegChunks;
+        sp.c_count = kSegChunks;
+        sp.h0 = s == 0 ? h0 : carry;
+        sp.hT = s + 1 == n_seg ? hT : carry;
+        hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()),
+                           kScanLdsPad, stream, sp);
+        e = hipGetLastError();
+      }
+      return e;
+    }
+  }
+
+  if (T_total > 0 && n_chunk_slots > 0) {
+    pp.seg_c0 = 0;
+    pp.seg_nc = 0;
+    const hipError_t e = launch_prep(pp, dim3(Hk, n_chunk_slots), conv != nullptr, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (blocks <= cus)
     hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()), 0, stream, sp);
   else
     hipLaunchKernelGGL((chunk_scan_kernel<1, 1>), dim3(blocks), dim3(scan_threads<1, 1>()), 0, stream, sp);

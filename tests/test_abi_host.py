@@ -77,6 +77,18 @@ def test_chunk_fwd_validation(lib):
     assert b"overlap" in lib.gdn_last_error()
 
 
+def test_chunk_fwd_workspace_carries_state_for_long_sequences(lib):
+    """Sequences of 32768 tokens or more (T_total / n_seqs) get room for the
+    state carried between the segments of the overlapped launch."""
+    carry = 48 * 128 * 128 * 4
+    chunk_blobs = 16 * 33792 + 48 * 12544       # room for one more chunk
+    for n in (1, 2):
+        a = lib.gdn_chunk_fwd_workspace_bytes(n, n * 32767, 16, 48, 128)
+        b = lib.gdn_chunk_fwd_workspace_bytes(n, n * 32768, 16, 48, 128)
+        extra = b - a - n * carry
+        assert chunk_blobs <= extra <= chunk_blobs + 4096, (n, b - a)
+
+
 def test_chunk_fwd_bf16o_validation(lib):
     def c16(**kw):
         a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), beta=P(4), o=P(5),

@@ -2,23 +2,27 @@
 
 The GPU runs each workload whole, in the launch configuration the benchmark
 times (one call over every head and token, preallocated workspace); the fp64
-oracle then recomputes outputs it can finish in seconds:
+oracle then recomputes every output element, value heads in batches so the
+host copies stay a few GB:
   core recurrence  B=1, T=512, 16/48 heads, S0 = 0          every head
-  full mixer       B=1, T=8192 (conv -> rule -> gated norm)  all conv channels,
-                                                             sampled value heads
-  long prefill     B=1, T=65536, S0 ~ N(0, 0.02)             sampled value heads
+  full mixer       B=1, T=8192, one gdn_mixer_fwd call from  every head, end
+                   x (conv -> rule -> gated norm)            to end from x
+  long prefill     B=1, T=65536, S0 ~ N(0, 0.02), the        every head
+                   overlapped segmented launch
   long prefill,    bf16 o (= fp32 o rounded) and gates from  bit-exact /
   other forms      projections (oracle)                       sampled heads
+  ragged segments  B=1, T=49509: three whole segments, a      every head
+                   short last one and a partial last chunk
   decode step      256 sequences x 1 token, state in place   every head
   multi-token      256 sequences x 4 tokens, one pass        every head
   fused decode     the same batch through the whole mixer    every head
                    step in one launch (conv window, state)
   fused mixer      T=8192 in one gdn_mixer_fwd call          bit-identical to
                                                              the four launches
-  varlen prefill   262,144 tokens in 24 sequences            sampled (sequence,
-                                                             value head) pairs
-A sampled value head h is recomputed on its own, with its key/query head
-h // (Hv / Hk), so the check covers the head mapping too.
+  varlen prefill   262,144 tokens in 24 sequences            every (sequence,
+                                                             value head) pair
+A value head h is recomputed with its key/query head h // (Hv / Hk), so the
+check covers the head mapping too.
 """
 import numpy as np
 import pytest
@@ -61,38 +65,53 @@ def test_full_core_T512_every_head():
     assert_close(host(hT), rT, "final_state")
 
 
-def test_full_mixer_T8192_sampled_heads():
+def prefill_every_head(ci, o, fs, T, batch, cu=None, n_seqs=1):
+    """o and final states of every value head against the oracle, `batch`
+    value heads (and their key heads) at a time."""
+    g_all, beta_all = f32(ci["g"]), f32(ci["beta"])
+    h0_all = f32(ci["h0"]) if ci["h0"] is not None else None
+    for h0_ in range(0, HV, batch):
+        heads = list(range(h0_, min(HV, h0_ + batch)))
+        kh = key_heads(heads)
+        log(f"  oracle on value heads {heads[0]}..{heads[-1]}")
+        ro, rT = oracle.recurrence(bits(ci["q"][:, kh]), bits(ci["k"][:, kh]),
+                                   bits(ci["v"][:, heads]), g_all[:, heads], beta_all[:, heads],
+                                   h0_all[:, heads] if h0_all is not None else None,
+                                   cu_seqlens=cu, n_seqs=n_seqs)
+        assert_close(host(o[:, heads]), ro, f"o heads {heads[0]}..{heads[-1]}")
+        del ro
+        if fs is not None:
+            assert_close(host(fs[:, heads]), rT, f"final_state heads {heads[0]}..{heads[-1]}")
+
+
+def test_full_mixer_T8192_end_to_end_every_head():
+    """One gdn_mixer_fwd call at T=8192 from the pre-conv rows x against the
+    oracle's conv (bf16-staged, as the kernel stores it), recurrence and gated
+    norm, every value head; and the conv launch on its own against the
+    oracle's conv (every channel, one bf16 ulp)."""
     T = 8192
-    heads = [0, 19, 38, 47]
-    log(f"full mixer T={T}: conv all channels, rule + norm on value heads {heads}")
+    log(f"full mixer T={T}: gdn_mixer_fwd from x against oracle conv -> rule -> norm, every head")
     mi = synth.mixer_inputs(1001, T)
-    y = ops.gdn_conv1d_fwd(dev_bf16(mi.x), dev_bf16(mi.conv_w), n_l2_heads=2 * HK)
-    yv = y.view(T, 2 * HK + HV, D)
-    o, hT = ops.gdn_chunk_fwd(yv[:, :HK], yv[:, HK:2 * HK], yv[:, 2 * HK:], dev_f32(mi.g),
-                              dev_f32(mi.beta))
-    out = ops.gdn_gated_rmsnorm(o, dev_bf16(mi.z), dev_f32(mi.norm_w))
+    x, w = dev_bf16(mi.x), dev_bf16(mi.conv_w)
+    out, hT = ops.gdn_mixer_fwd(x, w, dev_f32(mi.g), dev_f32(mi.beta), dev_bf16(mi.z),
+                                dev_f32(mi.norm_w), Hk=HK, n_seqs=1)
+    y = ops.gdn_conv1d_fwd(x, w, n_l2_heads=2 * HK)
     log("  oracle conv")
     ry, _ = oracle.conv1d(mi.x, mi.conv_w, n_l2_heads=2 * HK, head_dim=D, stage_bf16=True)
     assert_bf16_within_1ulp(host(y), ry, "conv y")
-    # the rule and the norm take the GPU's conv output, so they are checked on
-    # their own inputs (the conv output was just checked against the oracle)
-    ybits = bits(y).reshape(T, 2 * HK + HV, D)
-    log("  oracle rule")
-    kh = key_heads(heads)
-    # one key head per value head: the oracle runs the chosen heads only
-    ro, rT = oracle.recurrence(ybits[:, kh], ybits[:, HK + np.array(kh)],
-                               ybits[:, 2 * HK + np.array(heads)], mi.g[:, heads],
-                               mi.beta[:, heads])
-    rout = oracle.gated_rmsnorm(ro, mi.z[:, heads], mi.norm_w)
-    assert_close(host(o)[:, heads], ro, "o")
-    assert_close(host(hT)[:, heads], rT, "final_state")
-    assert_close(host(out)[:, heads], rout, "norm out")
+    del y
+    ry = ry.reshape(T, 2 * HK + HV, D)
+    log("  oracle rule + norm")
+    ro, rT = oracle.recurrence(ry[:, :HK], ry[:, HK:2 * HK], ry[:, 2 * HK:], mi.g, mi.beta)
+    rout = oracle.gated_rmsnorm(ro, mi.z, mi.norm_w)
+    assert_close(host(out), rout, "mixer out")
+    assert_close(host(hT), rT, "final_state")
 
 
-def test_full_prefill_T65536_sampled_heads():
+@pytest.mark.timeout(600)
+def test_full_prefill_T65536_every_head():
     T = 65536
-    heads = [2, 24, 46]
-    log(f"full prefill T={T} (benchmark inputs, seed 1002), oracle on value heads {heads}")
+    log(f"full prefill T={T} (benchmark inputs, seed 1002), oracle on every value head")
     ci = synth.chunk_inputs_torch(1002, T, h0_std=0.02)
     o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
     fs = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
@@ -100,13 +119,27 @@ def test_full_prefill_T65536_sampled_heads():
                      device="cuda")
     ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], initial_state=ci["h0"],
                       final_state=fs, o=o, n_seqs=1, workspace=ws)
-    kh = key_heads(heads)
-    log("  oracle")
-    ro, rT = oracle.recurrence(bits(ci["q"][:, kh]), bits(ci["k"][:, kh]),
-                               bits(ci["v"][:, heads]), f32(ci["g"][:, heads]),
-                               f32(ci["beta"][:, heads]), f32(ci["h0"][:, heads]))
-    assert_close(host(o[:, heads]), ro, "o")
-    assert_close(host(fs[:, heads]), rT, "final_state")
+    prefill_every_head(ci, o, fs, T, batch=12)
+
+
+@pytest.mark.timeout(600)
+def test_segmented_prefill_ragged_tail_every_head():
+    """B=1, T = 3 * 16384 + 5 * 64 + 37: the overlapped launch runs three whole
+    16384-token segments and a short fourth one ending in a partial chunk,
+    with the state carried between segments; every value head against the
+    oracle.  Then without an initial or a final state (zero start, o only)."""
+    T = 3 * 16384 + 5 * 64 + 37
+    log(f"segmented prefill T={T}, every value head")
+    ci = synth.chunk_inputs_torch(1010, T, h0_std=0.05)
+    o, fs = ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"],
+                              initial_state=ci["h0"], n_seqs=1)
+    prefill_every_head(ci, o, fs, T, batch=16)
+    log("  no initial or final state")
+    o2, fs2 = ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], n_seqs=1,
+                                output_final_state=False)
+    assert fs2 is None
+    ci0 = dict(ci, h0=None)
+    prefill_every_head(ci0, o2, None, T, batch=24)
 
 
 def test_full_prefill_T65536_bf16_o_and_gated():
@@ -200,10 +233,11 @@ def test_full_mixer_fwd_T8192_equals_four_launches():
     assert torch.equal(h1, h2), "final_state"
 
 
-def test_full_varlen_262144_sampled_pairs():
+@pytest.mark.timeout(600)
+def test_full_varlen_262144_every_pair():
     lens = synth.varlen_lengths(1004)
     T = int(lens.sum())
-    log(f"full varlen prefill T={T} N={len(lens)} (benchmark inputs, seed 1004)")
+    log(f"full varlen prefill T={T} N={len(lens)} (benchmark inputs, seed 1004), every pair")
     ci = synth.chunk_inputs_torch(1004, T, lengths=lens, h0_std=0.02)
     o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
     fs = torch.empty((len(lens), HV, D, D), dtype=torch.float32, device="cuda")
@@ -211,22 +245,8 @@ def test_full_varlen_262144_sampled_pairs():
                      device="cuda")
     ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], initial_state=ci["h0"],
                       final_state=fs, o=o, cu_seqlens=ci["cu_seqlens"], workspace=ws)
-    cu = synth.cu_from_lengths(lens)
-    order = np.argsort(lens)
-    picks = [(int(order[0]), 5), (int(order[len(lens) // 2]), 30), (int(order[-1]), 47)]
-    g_all, beta_all = f32(ci["g"]), f32(ci["beta"])
-    h0_all = f32(ci["h0"])
-    for n, h in picks:
-        a, b = int(cu[n]), int(cu[n + 1])
-        kh = h // GROUP
-        log(f"  sequence {n} (length {b - a}), value head {h}")
-        q = bits(ci["q"][a:b, kh:kh + 1])
-        k = bits(ci["k"][a:b, kh:kh + 1])
-        v = bits(ci["v"][a:b, h:h + 1])
-        ro, rT = oracle.recurrence(q, k, v, g_all[a:b, h:h + 1], beta_all[a:b, h:h + 1],
-                                   h0_all[n:n + 1, h:h + 1])
-        assert_close(host(o[a:b, h:h + 1]), ro, "o")
-        assert_close(host(fs[n:n + 1, h:h + 1]), rT, "final_state")
+    del ws
+    prefill_every_head(ci, o, fs, T, batch=6, cu=synth.cu_from_lengths(lens), n_seqs=len(lens))
 
 
 def test_full_backward_8x1024_sampled_groups():

@@ -224,6 +224,51 @@ def test_chunk_strong_decay_and_beta_extremes():
 
 # ----------------------------------------------------------------- chunk map
 
+def scaled(ci: synth.ChunkInputs, e: int) -> synth.ChunkInputs:
+    """v and S0 times 2^e (exact: bf16 and fp32 keep every bit under a power
+    of two within their exponent range).  The rule is linear in (S0, v), so
+    o and the final state scale by 2^e too and the relative bar is the same."""
+    v = synth.bf16_bits(synth.bf16_value(ci.v) * np.float32(2.0 ** e))
+    assert np.array_equal(synth.bf16_value(v), synth.bf16_value(ci.v) * np.float32(2.0 ** e))
+    return synth.ChunkInputs(ci.q, ci.k, v, ci.g, ci.beta,
+                             None if ci.h0 is None else (ci.h0 * np.float32(2.0 ** e)),
+                             ci.cu_seqlens, ci.n_seqs)
+
+
+@pytest.mark.parametrize("T", [200, 1024])
+@pytest.mark.parametrize("e", [-12, -10, 6, 8])
+def test_chunk_value_and_state_scale(T, e):
+    """The prefill's matrix-unit operands S0, U (and the V tile) are fp16: the
+    relative bar must hold with v and S0 scaled by 2^e, from fp16's subnormal
+    end (2^-12: S0 ~ 5e-6) to 2^8 (|v| up to ~1500)."""
+    log(f"chunk_fwd T={T}, v and S0 times 2^{e}")
+    ci = scaled(synth.chunk_inputs(2300 + T, T, h0_std=0.02), e)
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+
+
+@pytest.mark.parametrize("T", [200, 1024])
+def test_chunk_value_outliers(T):
+    """One value head carries a dozen |v| ~ 200 entries among N(0, 1) values."""
+    log(f"chunk_fwd T={T}, |v| ~ 200 outliers on value head 7")
+    ci = synth.chunk_inputs(2400 + T, T, h0_std=0.02)
+    r = synth.rng(2401)
+    v = synth.bf16_value(ci.v).copy()
+    t = r.integers(0, T, 12)
+    c = r.integers(0, ci.v.shape[2], 12)
+    v[t, 7, c] = np.where(r.random(12) < 0.5, -1.0, 1.0) * r.uniform(150.0, 250.0, 12)
+    ci = synth.ChunkInputs(ci.q, ci.k, synth.bf16_bits(v), ci.g, ci.beta, ci.h0, ci.cu_seqlens,
+                           ci.n_seqs)
+    o, hT = run_chunk(ci)
+    ro, rT = oracle_chunk(ci)
+    assert_close(o, ro, "o")
+    assert_close(hT, rT, "final_state")
+    assert_close(o[:, 7], ro[:, 7], "o head 7")
+    assert_close(hT[:, 7], rT[:, 7], "final_state head 7")
+
+
 @pytest.mark.parametrize("lens", [[5], [64, 64], [0, 0, 3], [100, 0, 65, 1, 64, 300, 0, 2],
                                   list(np.random.default_rng(3).integers(0, 400, 300))])
 def test_chunk_map_bit_exact(lens):
