@@ -14,6 +14,10 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
           front inside the prep kernel);
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens);
   backward  gdn_backward (the rule's gradients) on 8 sequences of 1024 tokens.
+  latency   the core recurrence at T = 512 (zero state): median and min of
+          single launches;
+  ceilings  what this device sustains: a 1 GiB device copy and a dense
+          fp16 MFMA loop (gdn_calib_mfma_loop), beside the published peaks.
 Two more prefill timings, not the headline: o written in bf16
 (`prefill_bf16_o`) and the gates formed from bf16 projections (`prefill_gated`).
 `roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
@@ -312,6 +316,58 @@ def leg_copy(args, torch):
     return dict(bytes=2 * n, event_ms=ev)
 
 
+def leg_latency(args, ops, synth, torch):
+    """The core recurrence at T = 512 (B = 1, zero initial state, fp32 o and
+    final state): a latency figure, each launch bracketed by its own events."""
+    T = 512
+    log(f"[latency] drawing inputs T={T}")
+    ci = synth.chunk_inputs_torch(1000, T)
+    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    fs = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_bytes(1, T, HK, HV), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], final_state=fs, o=o,
+                          n_seqs=1, workspace=ws)
+
+    for _ in range(max(args.warmup, 3)):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for s, e in evs:
+        s.record()
+        step()
+        e.record()
+        e.synchronize()
+    ts = sorted(s.elapsed_time(e) for s, e in evs)
+    med, mn = ts[len(ts) // 2], ts[0]
+    bytes_launch = T * BYTES_PER_TOKEN + STATE_BYTES      # zero initial state: S_T only
+    res = dict(tokens=T, median_ms=med, min_ms=mn, tokens_per_s=T / (med * 1e-3),
+               hbm_frac=bytes_launch / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               mfma_frac=T * FLOP_PER_TOKEN / (med * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS)
+    log(f"[latency] T={T}: median {med * 1e3:.1f} us, min {mn * 1e3:.1f} us per launch")
+    return res
+
+
+def leg_ceilings(args, ops, torch):
+    """Measured ceilings of this device beside the published peaks: a 1 GiB
+    device copy (HBM) and the dense fp16 MFMA loop."""
+    cp = leg_copy(args, torch)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_blocks, n_iter = 4 * cus, 4096
+    out = torch.empty(4 * n_blocks, dtype=torch.float32, device="cuda")
+    flops = ops.gdn_calib_mfma_loop(n_iter, n_blocks, out)[1]
+    ev, _ = time_leg(lambda: ops.gdn_calib_mfma_loop(n_iter, n_blocks, out), 5, 2)
+    tflops = flops / (ev * 1e-3) / 1e12
+    log(f"[ceilings] copy {cp['bytes'] / (cp['event_ms'] * 1e-3) / 1e9:.0f} GB/s; "
+        f"MFMA loop {tflops:.0f} TFLOP/s ({n_blocks} x 4 waves x {n_iter} x 8 products)")
+    return dict(copy_gbps=cp["bytes"] / (cp["event_ms"] * 1e-3) / 1e9, copy_event_ms=cp["event_ms"],
+                mfma_tflops=tflops, mfma_event_ms=ev, mfma_blocks=n_blocks, mfma_iters=n_iter)
+
+
 PREFILL_SOURCES = ("gated_delta_rule_09_amd/csrc/chunk.hip", "gated_delta_rule_09_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_T65536_traffic.json")
 
@@ -364,7 +420,17 @@ def cpu_baseline(ci, seconds, torch):
     t0 = time.perf_counter()
     oracle.recurrence(q[:Ts], k[:Ts], v[:Ts], g[:Ts], b[:Ts], h0, n_threads=threads)
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"first {Ts} tokens of the T=65536 prefill input, all 48 value heads, "
                       f"fp64 sequential recurrence, {dt:.1f} s"}
 
@@ -374,7 +440,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,mixer,varlen,backward")
+    ap.add_argument("--legs", default="prefill,latency,decode,mixer,varlen,backward,ceilings")
     ap.add_argument("--prefill-forms", default="fp32,bf16o,gated",
                     help="prefill launch forms timed by the prefill leg (fp32 is always timed)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -395,6 +461,8 @@ def main():
     ci = None
     if "prefill" in legs:
         out["prefill"], ci = leg_prefill(args, ops, synth, torch)
+    if "latency" in legs:
+        out["latency"] = leg_latency(args, ops, synth, torch)
     if "decode" in legs:
         out["decode"] = leg_decode(args, ops, synth, torch)
     if "mixer" in legs:
@@ -405,6 +473,8 @@ def main():
         out["backward"] = leg_backward(args, ops, synth, torch)
     if "copy" in legs:
         out["copy"] = leg_copy(args, torch)
+    if "ceilings" in legs:
+        out["ceilings"] = leg_ceilings(args, ops, torch)
 
     pre = out.get("prefill")
     line = {
@@ -439,6 +509,19 @@ def main():
         if "gated_event_ms" in pre:
             line["prefill_gated"] = {"launch_ms": round(pre["gated_event_ms"], 4),
                                      "tokens_per_s": round(pre["gated_tokens_per_s"], 1)}
+    if "latency" in out:
+        la = out["latency"]
+        line["latency_T512"] = {"median_ms": round(la["median_ms"], 4),
+                                "min_ms": round(la["min_ms"], 4),
+                                "tokens_per_s": round(la["tokens_per_s"], 1),
+                                "hbm_frac": round(la["hbm_frac"], 4),
+                                "mfma_frac": round(la["mfma_frac"], 4)}
+    if "ceilings" in out:
+        ce = out["ceilings"]
+        line["ceilings"] = {"copy_GBps": round(ce["copy_gbps"], 1),
+                            "copy_frac_of_peak": round(ce["copy_gbps"] / HBM_PEAK_GBPS, 4),
+                            "mfma_loop_TFLOPs": round(ce["mfma_tflops"], 1),
+                            "mfma_loop_frac_of_peak": round(ce["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
     if "decode" in out:
         d = out["decode"]
         line["decode"] = {"state_GBps": round(d["state_gbps"], 1),

@@ -724,6 +724,21 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
                     "gdn_gated_rmsnorm launch");
 }
 
+double gdn_calib_mfma_loop_flops(int32_t n_iter, int32_t n_blocks) {
+  if (n_iter <= 0 || n_blocks <= 0) return 0.0;
+  return gdn::mfma_loop_flops(n_iter, n_blocks);
+}
+
+gdn_status gdn_calib_mfma_loop(int32_t n_iter, int32_t n_blocks, float* out, void* stream) {
+  if (!out) return fail(GDN_ERR_NULL, "gdn_calib_mfma_loop: out is NULL");
+  if (n_iter <= 0 || n_blocks <= 0 || n_blocks > (1 << 20))
+    return fail(GDN_ERR_SHAPE, "gdn_calib_mfma_loop: n_iter %d and n_blocks %d must be in 1 .. "
+                "and n_blocks <= 2^20", n_iter, n_blocks);
+  if (!aligned(out, 4)) return fail(GDN_ERR_SHAPE, "gdn_calib_mfma_loop: out misaligned");
+  return hip_status(gdn::launch_mfma_loop(n_iter, n_blocks, out, static_cast<hipStream_t>(stream)),
+                    "gdn_calib_mfma_loop launch");
+}
+
 size_t gdn_backward_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hv) {
   if (n_seqs <= 0 || T_total <= 0 || Hv <= 0) return 0;
   return gdn::backward_workspace_bytes(n_seqs, T_total, Hv);

@@ -115,4 +115,11 @@ hipError_t launch_backward(const uint16_t* q, int64_t qs, const uint16_t* k, int
                            float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                            void* workspace, hipStream_t stream);
 
+// Dense MFMA loop (calib.hip): n_blocks work-groups of 4 waves, each wave
+// n_iter rounds of 8 independent 16x16x32 fp16 products; one float per wave
+// to out (mfma_loop_waves(n_blocks) of them).
+double mfma_loop_flops(int n_iter, int n_blocks);
+int mfma_loop_waves(int n_blocks);
+hipError_t launch_mfma_loop(int n_iter, int n_blocks, float* out, hipStream_t stream);
+
 }  // namespace gdn

@@ -55,6 +55,8 @@ _SIGS = {
                                      _i32, _i32, _f32, _f32, _f32, _vp]),
     "gdn_gated_rmsnorm": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i64, _i32, _i32, _f32, _vp]),
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
+    "gdn_calib_mfma_loop_flops": (_c.c_double, [_i32, _i32]),
+    "gdn_calib_mfma_loop": (_i32, [_i32, _i32, _vp, _vp]),
     "gdn_backward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "gdn_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -626,6 +628,20 @@ def gdn_validate_cu_seqlens(cu_seqlens: torch.Tensor, T_total: int) -> None:
     st = lib().gdn_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.shape[0] - 1, T_total,
                                        _stream())
     _check(st, "gdn_validate_cu_seqlens")
+
+
+def gdn_calib_mfma_loop(n_iter: int, n_blocks: int,
+                        out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, float]:
+    """The dense fp16 MFMA loop (a measurement aid): returns (out [4 n_blocks]
+    fp32, the launch's flops)."""
+    if out is None:
+        out = torch.empty(4 * max(n_blocks, 0), dtype=torch.float32, device="cuda")
+    _need(out, "out", torch.float32, 1)
+    if out.numel() < 4 * n_blocks or not out.is_contiguous():
+        raise ValueError("out needs 4 * n_blocks contiguous floats")
+    h = lib()
+    _check(h.gdn_calib_mfma_loop(n_iter, n_blocks, _ptr(out), _stream()), "gdn_calib_mfma_loop")
+    return out, float(h.gdn_calib_mfma_loop_flops(n_iter, n_blocks))
 
 
 def gdn_backward_workspace_bytes(n_seqs: int, T_total: int, Hv: int) -> int:

@@ -72,7 +72,7 @@ typedef int32_t gdn_status;
 #define GDN_ERR_HIP (-6)         /* the HIP runtime reported an error                 */
 #define GDN_ERR_SEQLENS (-7)     /* cu_seqlens failed the opt-in host validation      */
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
@@ -493,6 +493,20 @@ gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t*
  */
 gdn_status gdn_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int32_t T_total,
                                    void* stream);
+
+/*
+ * gdn_calib_mfma_loop -- a measurement aid, not part of the rule: the dense
+ * fp16 matrix-unit ceiling of the running device, against which the prefill's
+ * matrix products are judged (beside the HBM ceiling a plain device copy
+ * gives).  n_blocks work-groups of 4 waves; every wave runs n_iter rounds of 8
+ * independent v_mfma_f32_16x16x32_f16 products and writes one float (the sum
+ * of its accumulators) to out[wave], so out holds 4 * n_blocks floats.
+ * gdn_calib_mfma_loop_flops gives the flops of such a launch (2*16*16*32 per
+ * product); divide by the launch time.  n_iter, n_blocks >= 1, n_blocks <=
+ * 2^20, out 4-byte aligned; GDN_ERR_SHAPE / GDN_ERR_NULL otherwise.
+ */
+double gdn_calib_mfma_loop_flops(int32_t n_iter, int32_t n_blocks);
+gdn_status gdn_calib_mfma_loop(int32_t n_iter, int32_t n_blocks, float* out, void* stream);
 
 #ifdef __cplusplus
 }

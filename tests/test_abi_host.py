@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 7
+    assert lib.gdn_abi_version() == 8
     for code, name in [(OK, "GDN_OK"), (NULL, "GDN_ERR_NULL"), (SHAPE, "GDN_ERR_SHAPE"),
                        (UNSUP, "GDN_ERR_UNSUPPORTED"), (WS, "GDN_ERR_WORKSPACE"),
                        (ALIAS, "GDN_ERR_ALIAS"), (-6, "GDN_ERR_HIP"), (-7, "GDN_ERR_SEQLENS")]:
@@ -87,6 +87,17 @@ def test_chunk_fwd_workspace_carries_state_for_long_sequences(lib):
         b = lib.gdn_chunk_fwd_workspace_bytes(n, n * 32768, 16, 48, 128)
         extra = b - a - n * carry
         assert chunk_blobs <= extra <= chunk_blobs + 4096, (n, b - a)
+
+
+def test_calib_mfma_loop_validation(lib):
+    assert lib.gdn_calib_mfma_loop(10, 4, None, None) == NULL
+    assert lib.gdn_calib_mfma_loop(0, 4, P(0), None) == SHAPE
+    assert lib.gdn_calib_mfma_loop(10, 0, P(0), None) == SHAPE
+    assert lib.gdn_calib_mfma_loop(10, (1 << 20) + 1, P(0), None) == SHAPE
+    assert lib.gdn_calib_mfma_loop(10, 4, P(0) + 2, None) == SHAPE
+    # 4 waves per block, 8 products of 2*16*16*32 flops per wave and round
+    assert lib.gdn_calib_mfma_loop_flops(10, 4) == 4 * 4 * 10 * 8 * 16384
+    assert lib.gdn_calib_mfma_loop_flops(0, 4) == 0.0
 
 
 def test_chunk_fwd_bf16o_validation(lib):
@@ -332,10 +343,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 
 def test_backward_checkpoint_slots_fit_the_workspace():
-    """gdn_backward keeps the state before every 4th token of a sequence
-    (tokens s0, s0 + 4, ... of a sequence starting at s0) in slot t // 4 + n of
-    a workspace sized for T // 4 + N slots: over random packings with empty
-    and one-token sequences the slots are distinct and in range."""
+    """The arithmetic claim behind gdn_backward's checkpoint record: keeping
+    the state before tokens s0, s0 + 4, ... of each sequence (starting at s0)
+    in slot t // 4 + n gives distinct slots below T // 4 + N, the count the
+    workspace holds, over random packings with empty and one-token sequences.
+    (This checks the scheme; the GPU tests run the kernel's own indexing on
+    such packings.)"""
     import numpy as np
     r = np.random.default_rng(31)
     for _ in range(200):

@@ -84,16 +84,31 @@ def test_backward_random_shapes(case):
     _check(got, ref, f"random {case}")
 
 
-@pytest.mark.parametrize("n_seqs", [33, 3, 12])
-def test_backward_row_group_layouts(n_seqs):
-    """Each (sequence, value head) is split over 1, 2 or 4 work-groups of
-    rows depending on how many pairs the batch has (more than 1536, 129-1536,
-    at most 128 at 48 heads): all three layouts against the oracle."""
+def row_groups_of(n_seqs, T, Hv=48):
+    """Row groups per (sequence, head) of a gdn_backward call, read back from
+    its workspace size: checkpoints (T // 4 + N slots of a 128 x 128 state per
+    head) plus two fp32 partial-sum arrays of 129 floats per (token, head,
+    row group)."""
+    need = ops.gdn_backward_workspace_bytes(n_seqs, T, Hv)
+    ck = (T // 4 + n_seqs) * Hv * 128 * 128 * 4
+    R, rem = divmod(need - ck, 2 * T * Hv * 129 * 4)
+    assert rem == 0, (need, ck)
+    return R
+
+
+@pytest.mark.parametrize("n_seqs,R", [(2, 4), (12, 2), (33, 1)])
+def test_backward_row_group_layouts(n_seqs, R):
+    """Each (sequence, value head) is split over 4, 2 or 1 work-groups of rows
+    depending on how many pairs the batch has (at most 128, 129-1536, more):
+    96, 576 and 1584 pairs at 48 heads take the three layouts (checked through
+    the workspace size), each against the oracle."""
     r = np.random.default_rng(9300 + n_seqs)
-    lens = [int(x) for x in r.integers(0, 12, size=n_seqs)]
-    log(f"backward row groups: {n_seqs} sequences x 48 heads, lengths {lens}")
-    ci = synth.chunk_inputs(9400 + n_seqs, sum(lens), lengths=lens, h0_std=0.02)
-    bs = synth.backward_seeds(9500 + n_seqs, sum(lens), n_seqs)
+    lens = [int(x) for x in r.integers(1, 12, size=n_seqs)]
+    T = sum(lens)
+    assert row_groups_of(n_seqs, T) == R
+    log(f"backward row groups: {n_seqs} sequences x 48 heads ({R} per pair), lengths {lens}")
+    ci = synth.chunk_inputs(9400 + n_seqs, T, lengths=lens, h0_std=0.02)
+    bs = synth.backward_seeds(9500 + n_seqs, T, n_seqs)
     got, ref = _run(ci, bs, 128 ** -0.5, 16)
     _check(got, ref, f"{n_seqs} sequences")
 

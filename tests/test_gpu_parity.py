@@ -7,8 +7,8 @@ import torch
 
 import oracle
 from gated_delta_rule_09_amd import ops, synth
-from tests.gpu_util import (assert_bf16_within_1ulp, assert_close, dev_bf16, dev_f32, dev_i32,
-                            host, log)
+from tests.gpu_util import (assert_bf16_rounded_close, assert_bf16_within_1ulp, assert_close,
+                            dev_bf16, dev_f32, dev_i32, host, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,15 +65,14 @@ def test_chunk_bf16_output(lens):
     want = oracle.round_bf16(host(o32))                 # fp64 values on the bf16 grid
     got = o16.float().cpu().numpy().astype(np.float64)   # exact widening
     np.testing.assert_array_equal(got, want)
-    # against the oracle: the fp32 bar, plus the bf16 rounding itself (relative
-    # error up to 2^-9 per element, so rel-L2 up to ~2^-9 on its own)
+    # against the oracle: the fp32 bar, plus the bf16 rounding itself.  The
+    # fp32 o carries the fp16-operand error (rel-L2 a few 1e-4, more than half
+    # a bf16 ulp on small elements), so no one-ulp check: by the triangle
+    # inequality the rounded o is within 1e-3 + 2^-9 (the rounding's largest
+    # relative step) in rel-L2
     ro, _ = oracle_chunk(ci)
     assert_close(host(o32), ro, "o (fp32)")
-    d = got - ro
-    rel = np.linalg.norm(d) / np.linalg.norm(ro)
-    mabs = np.abs(d).max() / np.abs(ro).max()
-    log(f"  o (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
-    assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+    assert_bf16_rounded_close(got, ro, "o (bf16)")
 
 
 @pytest.mark.parametrize("out_bf16", [False, True])
@@ -95,11 +94,7 @@ def test_chunk_pooled_mixed_batch(out_bf16):
                                cu_seqlens=ci.cu_seqlens, n_seqs=len(lens), scale=0.9)
     got = host(o)
     if out_bf16:
-        d = got - ro
-        rel = np.linalg.norm(d) / np.linalg.norm(ro)
-        mabs = np.abs(d).max() / np.abs(ro).max()
-        log(f"  o (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
-        assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+        assert_bf16_rounded_close(got, ro, "o (bf16)")
     else:
         assert_close(got, ro, "o")
     got_st = host(st)
@@ -611,13 +606,9 @@ def test_decode_mixer_step_against_oracle(N, Hk, Hv, slotted, out_bf16):
     rout, rcs, rst = oracle_mixer_step(mi, pool, Hk, Hv, slots, bias=bias, scale=scale,
                                        out_bf16=out_bf16)
     if out_bf16:
+        # both sides round once to bf16 (the oracle from fp64): one ulp apart at most
         assert out.dtype == torch.bfloat16
-        got = out.float().cpu().numpy().astype(np.float64)
-        d = got - rout
-        rel = np.linalg.norm(d) / np.linalg.norm(rout)
-        mabs = np.abs(d).max() / np.abs(rout).max()
-        log(f"  out (bf16): rel_l2={rel:.3e} max_abs/max_ref={mabs:.3e}")
-        assert rel <= 1e-3 + 2.0 ** -9 and mabs <= 5e-3
+        assert_bf16_within_1ulp(host(out), rout, "out (bf16)")
     else:
         assert_close(host(out), rout, "out")
     got_cs, got_st = host(cs), host(st)
@@ -676,11 +667,15 @@ def test_decode_mixer_step_matches_unfused(out_bf16):
     torch.cuda.synchronize()
     assert torch.equal(cs1, cs2)
     for name, a1, a2 in (("state", st1, st2), ("out", out1, out2)):
+        if out_bf16 and name == "out":
+            # each path rounds its fp32 result to bf16 once
+            assert_bf16_within_1ulp(host(a1), host(a2), "out (bf16), fused vs unfused")
+            continue
         a1, a2 = a1.double(), a2.double()
         err = ((a1 - a2).abs().max() / a2.abs().max()).item()
         rel = ((a1 - a2).norm() / a2.norm()).item()
         log(f"  {name}: max|fused - unfused| / max = {err:.3e}, rel_l2 = {rel:.3e}")
-        assert rel <= 1e-4 + (2.0 ** -9 if out_bf16 and name == "out" else 0.0), name
+        assert rel <= 1e-4, name
 
 
 # ----------------------------------------------------------------- full mixer
