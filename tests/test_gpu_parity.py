@@ -478,6 +478,23 @@ def test_mixer_fwd_equals_unfused(case):
         assert torch.equal(cs1, cs2), "conv_state"
 
 
+def test_mixer_fwd_long_segmented():
+    """B=1, T = 2 * 16384 + 100: gdn_mixer_fwd through the overlapped launch
+    (the conv front inside the prep of every segment, the last segment short)
+    against the four separate launches: out, final state bit for bit."""
+    T = 2 * 16384 + 100
+    log(f"mixer_fwd T={T} (segmented) against the four launches")
+    mi = synth.mixer_inputs_torch(3900, T)
+    x, w, z, nw, g, b = mi["x"], mi["conv_w"], mi["z"], mi["norm_w"], mi["g"], mi["beta"]
+    out1, h1 = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=16, n_seqs=1)
+    y = ops.gdn_conv1d_fwd(x, w, n_l2_heads=32).view(T, 80, 128)
+    o, h2 = ops.gdn_chunk_fwd(y[:, :16], y[:, 16:32], y[:, 32:], g, b)
+    out2 = ops.gdn_gated_rmsnorm(o, z, nw)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "out"
+    assert torch.equal(h1, h2), "final_state"
+
+
 def test_mixer_fwd_gates_from_projections():
     """gdn_mixer_fwd with the gates formed from bf16 projections: bit-identical
     to conv -> gdn_chunk_fwd_gated -> norm, and against the oracle's gate
