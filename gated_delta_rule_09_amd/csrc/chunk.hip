@@ -57,14 +57,13 @@ namespace {
 constexpr int kC = 64;            // chunk length
 constexpr int kD = 128;           // head dim (dk = dv)
 constexpr int kThreads = 256;    // prep work-group
-// Scan work-group (32 value channels of one value head): a state wave, one or
-// two output waves, and two loader waves that copy the next chunk into LDS.
+// Scan work-group (kTiles 16-channel tiles of one value head: 32 or 64 value
+// channels): state waves, output waves, and two loader waves that copy the
+// next chunk into LDS.
 constexpr int kScanLoaderWaves = 2;
 constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
 template <int kOutWaves, int kStateWaves>
 constexpr int scan_threads() { return 64 * (kStateWaves + kOutWaves + kScanLoaderWaves); }
-constexpr int kDvPerWg = 32;                       // value channels per scan work-group
-constexpr int kParts = kD / kDvPerWg;              // scan work-groups per value head
 
 // ---- fragment layout in the workspace -------------------------------------
 // An A32 fragment of a 16 x 32 block holds, for lane l (row l % 16, group
@@ -93,39 +92,46 @@ constexpr int kOffAn32 = kOffAn3 + kFrag;             // A16: -A rows 48..63, co
 constexpr int kOffDecay = kOffAn32 + kFrag16;         // 4 x 64 floats: b, b gamma, scale gamma, exp(G_L - G)
 constexpr int kOffGL = kOffDecay + 4 * 256;           // gamma_L
 constexpr int kVBytes = kOffGL + 256;                 // 12544
-// Per chunk the scan stages what the state wave reads in LDS: [K rows |
+// Per chunk the scan stages what the state waves read in LDS: [K rows |
 // value-head blob from T_bb on | V tile], where the V tile is this
 // work-group's value channels of the chunk's 64 tokens, row-major bf16
-// (2 kDvPerWg bytes per token).  The output wave loads its Q and P fragments
+// (2 kDv bytes per token).  The output waves load their Q and P fragments
 // from global memory into registers.
 constexpr int kVBStaged = kVBytes - kOffT;                                      // 6400
-constexpr int kVTileBytes = kC * kDvPerWg * 2;                                  // 4096
 constexpr int kStageVB = kOffQ;                                                 // 17408
 constexpr int kStageV = kStageVB + kVBStaged;                                   // 23808
-constexpr int kStageBytes = kStageV + kVTileBytes;                              // 27904
-constexpr int kStagePieces = kStageBytes / 16;                                  // 1744
-constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;  // 14
 constexpr int kKPieces = kOffQ / 16;                                            // 1088
 constexpr int kVBPieces = kVBStaged / 16;                                       // 400
-constexpr int kVTilePieces = kVTileBytes / 16;                                  // 256
-constexpr int kVPiecesPerRow = kDvPerWg / 8;                                    // 4
-// Per chunk the state wave leaves the fp16 S0 (as B operands, tile t, block kb
-// at fragment 4 t + kb) and U (fragments 8 + 2 t, 9 + 2 t) for the output wave.
-constexpr int kXBytes = 12 * kFrag;
+// Per chunk the state waves leave the fp16 S0 (as B operands, tile t, block
+// kb at fragment 4 t + kb) and U (fragments kU0 + 2 t, kU0 + 1 + 2 t) for the
+// output waves.
+template <int kTiles>
+struct ScanShape {
+  static constexpr int kDv = 16 * kTiles;                         // value channels per work-group
+  static constexpr int kParts = kD / kDv;                         // work-groups per value head
+  static constexpr int kVTileBytes = kC * kDv * 2;                // 4096 / 8192
+  static constexpr int kStageBytes = kStageV + kVTileBytes;       // 27904 / 32000
+  static constexpr int kStagePieces = kStageBytes / 16;
+  static constexpr int kStageRounds = (kStagePieces + kLoaderThreads - 1) / kLoaderThreads;
+  static constexpr int kVPiecesPerRow = kDv / 8;
+  static constexpr int kU0 = 4 * kTiles;
+  static constexpr int kXBytes = 6 * kTiles * kFrag;              // 12 / 24 KB
+  static_assert(kStagePieces == kKPieces + kVBPieces + kVTileBytes / 16, "stage = K rows + value blob + V tile");
+  static_assert(kStageBytes % 16 == 0, "stage size");
+};
 
 // The overlapped prefill: segments of kSegChunks chunks for sequences of at
 // least kSegMinChunks chunks, when the scan leaves kSegMinIdleCUs or more
-// compute units idle.  kScanLdsPad bytes of LDS added to each scan
-// work-group leave its compute unit too little for a prep work-group, so the
-// preps run on the idle units and take nothing from the scan's memory pipe.
+// compute units idle.  kScanLdsPad (kScanLdsPad4) bytes of LDS added to each
+// 32-channel (64-channel) scan work-group leave its compute unit too little
+// for a prep work-group, so the preps run on the idle units and take nothing
+// from the scan's memory pipe.
 constexpr int kSegChunks = 256;
 constexpr int kSegMinChunks = 2 * kSegChunks;
 constexpr int kSegMinIdleCUs = 32;
-constexpr int kScanLdsPad = 48 * 1024;
-static_assert(kStagePieces == kKPieces + kVBPieces + kVTilePieces, "stage = K rows + value blob + V tile");
+constexpr int kScanLdsPad = 48 * 1024;      // beside the 32-channel form
+constexpr int kScanLdsPad4 = 16 * 1024;     // beside the 64-channel form
 static_assert(kOffT % 16 == 0 && kOffQ % 16 == 0, "staged parts are whole pieces");
-
-static_assert(kStageBytes % 16 == 0, "stage size");
 
 // ---- prep kernel LDS -------------------------------------------------------
 constexpr int kKS = kD + 8;       // K, Q rows (halves)
@@ -658,9 +664,10 @@ struct ScanParams {
 // Two stage buffers (the chunk being computed, the one being copied in) and
 // two sets of the S0 / U fragments passed from the state wave to the output
 // wave.
+template <int kTiles>
 struct __align__(16) ScanSmem {
-  unsigned char buf[2][kStageBytes];
-  unsigned char xbuf[2][kXBytes];
+  unsigned char buf[2][ScanShape<kTiles>::kStageBytes];
+  unsigned char xbuf[2][ScanShape<kTiles>::kXBytes];
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -676,13 +683,20 @@ __device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
   return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p)));
 }
 
-// kOutWaves = 2 when the work-groups fit the CUs one each (shorter chunk
-// period); 1 when there are more work-groups than CUs, so that two fit on a
-// CU (LDS and 256 VGPRs per wave allow it).
-template <int kOutWaves, int kStateWaves>
+// <2, 2, 2>: 32 channels, one state wave per tile, two output waves; the
+// form for work-groups that fit the CUs one each (shortest chunk period).
+// <1, 1, 2>: one state and one output wave, two work-groups per CU (LDS and
+// 256 VGPRs per wave allow it).  <2, 2, 4>: 64 channels, two tiles per state
+// wave, one work-group per CU: a CU moves the chunk's shared K rows, Q and P
+// fragments and blob once for twice the channels.
+template <int kOutWaves, int kStateWaves, int kTiles = 2>
 __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
+  using Sh = ScanShape<kTiles>;
+  constexpr int kParts = Sh::kParts;
+  constexpr int kDvPerWg = Sh::kDv;
   constexpr int kScanComputeWaves = kStateWaves + kOutWaves;
-  __shared__ ScanSmem sm;
+  static_assert(kTiles % kStateWaves == 0, "tiles split evenly over the state waves");
+  __shared__ ScanSmem<kTiles> sm;
 
   // ---- block id -> (sequence rank, value head, value quarter) --------------
   // Chains sharing a key head (group * kParts of them) get block ids that are
@@ -734,7 +748,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
 
     // Piece i of the stage is its byte 16 i: the K rows, the value-head blob
     // from T_bb on, then the V tile (token i / kVPiecesPerRow, channels
-    // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDvPerWg).
+    // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDv).
     auto stage = [&](int ci) {
       const int cb = chunk0 + ci;
       const unsigned char* kqb = kq_head + cb * kq_step;
@@ -743,17 +757,17 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
       const int len = min(kC, seq_len - ci * kC);
       const uint16_t* vrow0 = v_head + static_cast<int64_t>(seq_start + ci * kC) * p.vs;
 #pragma unroll
-      for (int j = 0; j < kStageRounds; ++j) {
+      for (int j = 0; j < Sh::kStageRounds; ++j) {
         const int q = kLoaderThreads * j + lt;
         unsigned char* d = dst + (kLoaderThreads * j + 64 * lw) * 16;
         if (q < kKPieces) {
           lds_dma16(kqb + q * 16, d);
         } else if (q < kKPieces + kVBPieces) {
           lds_dma16(vbb + kOffT + (q - kKPieces) * 16, d);
-        } else if (q < kStagePieces) {
+        } else if (q < Sh::kStagePieces) {
           const int vp = q - kKPieces - kVBPieces;
-          const int r = min(vp / kVPiecesPerRow, len - 1);   // rows past the end re-read the last
-          lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % kVPiecesPerRow) * 8, d);
+          const int r = min(vp / Sh::kVPiecesPerRow, len - 1);   // rows past the end re-read the last
+          lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % Sh::kVPiecesPerRow) * 8, d);
         }
       }
     };
@@ -771,21 +785,25 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   // L2 prefetch, two chunks ahead, issued by the output wave: its misses
   // then hold up no copy (a wave's loads complete in order).  The `members`
   // work-groups of a key head share its K/Q blob and the blobs of its value
-  // heads; member m pulls lines 64 m .. 64 m + 63 of that data, and each
-  // work-group its own V rows.  One dword per 128-byte line; the values go to
-  // `sink`, stored only under a condition that never holds.
+  // heads; member m pulls lines 64 m .. 64 m + 63 of that data (with 64-channel
+  // work-groups also the lines 64 members further on), and each work-group
+  // its own V rows.  One dword per 128-byte line; the values go to `sink`,
+  // stored only under a condition that never holds.
   const int kq_lines = kKQBytes / 128;
   const int vb_lines = p.group * kVBytes / 128;
   auto touch = [&](int ci) -> uint32_t {
     const int cb = chunk0 + ci;
-    const int L = min(member * 64 + lane, kq_lines + vb_lines - 1);
-    const unsigned char* a =
-        L < kq_lines ? p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + L * 128
-                     : p.vb + (static_cast<int64_t>(cb) * p.Hv + kh * p.group) * kVBytes + (L - kq_lines) * 128;
+    auto line = [&](int L) {
+      L = min(L, kq_lines + vb_lines - 1);
+      return L < kq_lines ? p.kq + (static_cast<int64_t>(cb) * p.Hk + kh) * kKQBytes + L * 128
+                          : p.vb + (static_cast<int64_t>(cb) * p.Hv + kh * p.group) * kVBytes + (L - kq_lines) * 128;
+    };
     const int r = min(lane, min(kC, seq_len - ci * kC) - 1);
     const unsigned char* b = reinterpret_cast<const unsigned char*>(
         p.v + h * kD + part * kDvPerWg + static_cast<int64_t>(seq_start + ci * kC + r) * p.vs);
-    return *reinterpret_cast<const uint32_t*>(a) ^ *reinterpret_cast<const uint32_t*>(b);
+    uint32_t x = *reinterpret_cast<const uint32_t*>(line(member * 64 + lane)) ^ *reinterpret_cast<const uint32_t*>(b);
+    if (kTiles > 2) x ^= *reinterpret_cast<const uint32_t*>(line((member + members) * 64 + lane));
+    return x;
   };
 
   // ---- compute waves ---------------------------------------------------------
@@ -971,8 +989,8 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        *reinterpret_cast<half8*>(X + (8 + 2 * (t0 + t)) * kFrag + lane * 16) = u01[t];
-        *reinterpret_cast<half8*>(X + (9 + 2 * (t0 + t)) * kFrag + lane * 16) = u23[t];
+        *reinterpret_cast<half8*>(X + (Sh::kU0 + 2 * (t0 + t)) * kFrag + lane * 16) = u01[t];
+        *reinterpret_cast<half8*>(X + (Sh::kU0 + 1 + 2 * (t0 + t)) * kFrag + lane * 16) = u23[t];
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -1011,8 +1029,8 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
     }
   };
   if (w < kStateWaves) {
-    if (kStateWaves == 1) state_wave(std::integral_constant<int, 2>{}, 0);
-    else state_wave(std::integral_constant<int, 1>{}, w);
+    constexpr int kNT = kTiles / kStateWaves;
+    state_wave(std::integral_constant<int, kNT>{}, w * kNT);
     return;
   }
 
@@ -1049,19 +1067,19 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
     };
     auto output = [&](int ci) {
       const unsigned char* X = sm.xbuf[ci & 1];
-      half8 sB[2][4], u[2][2];
+      half8 sB[kTiles][4], u[kTiles][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) sB[t][kb] = *reinterpret_cast<const half8*>(X + (4 * t + kb) * kFrag + lane * 16);
 #pragma unroll
         for (int j = 0; j < (need_u23 ? 2 : 1); ++j)
-          u[t][j] = *reinterpret_cast<const half8*>(X + (8 + 2 * t + j) * kFrag + lane * 16);
+          u[t][j] = *reinterpret_cast<const half8*>(X + (Sh::kU0 + 2 * t + j) * kFrag + lane * 16);
       }
       const int len = min(kC, seq_len - ci * kC);
       const int64_t oe = static_cast<int64_t>(seq_start + ci * kC) * o_rs + h * kD + part * kDvPerWg + 4 * grp;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < kTiles; ++t)
 #pragma unroll
         for (int i = 0; i < ntb; ++i) {
           const int tb = tb0 + i;
@@ -1109,9 +1127,12 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   else output_wave(std::integral_constant<int, kOutWaves - 1>{});
 }
 
-static_assert(sizeof(ScanSmem) + kScanLdsPad <= 160 * 1024, "padded scan work-group fits a CU");
-static_assert(sizeof(ScanSmem) + kScanLdsPad + sizeof(PrepSmem) > 160 * 1024,
+static_assert(sizeof(ScanSmem<2>) + kScanLdsPad <= 160 * 1024, "padded scan work-group fits a CU");
+static_assert(sizeof(ScanSmem<2>) + kScanLdsPad + sizeof(PrepSmem) > 160 * 1024,
               "no prep work-group fits beside a padded scan work-group");
+static_assert(sizeof(ScanSmem<4>) + kScanLdsPad4 <= 160 * 1024, "padded 64-channel work-group fits a CU");
+static_assert(sizeof(ScanSmem<4>) + kScanLdsPad4 + sizeof(PrepSmem) > 160 * 1024,
+              "no prep work-group fits beside a padded 64-channel scan work-group");
 
 hipError_t launch_prep(const PrepParams& pp, dim3 grid, bool conv, hipStream_t stream) {
   if (conv) {
@@ -1238,13 +1259,19 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   sp.n_seqs = n_seqs; sp.seq_len = seq_len; sp.Hk = Hk; sp.Hv = Hv; sp.group = Hv / Hk;
   sp.n_chain_groups = n_seqs * Hk;
   sp.c_base = 0; sp.c_count = nc;
-  const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * kParts;
+  // work-groups of the 32- and 64-channel forms (the block map rounds the
+  // (sequence, key head) groups up to a multiple of the 8 XCDs)
+  const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * ScanShape<2>::kParts;
+  const int blocks4 = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * ScanShape<4>::kParts;
   const int cus = compute_units();
 
-  // Long equal-length sequences whose scan leaves compute units idle: the
-  // prep of segment i + 1 runs on a second stream, on those idle units, while
-  // the scan works through segment i.
-  if (!cu && !state_slot && T_total > 0 && nc >= kSegMinChunks && blocks + kSegMinIdleCUs <= cus &&
+  // Long equal-length sequences whose scan leaves compute units idle (in the
+  // 32-channel form, else in the 64-channel form): the prep of segment i + 1
+  // runs on a second stream, on those idle units, while the scan works
+  // through segment i.
+  const bool seg32 = blocks + kSegMinIdleCUs <= cus;
+  const bool seg64 = !seg32 && blocks4 + kSegMinIdleCUs <= cus;
+  if (!cu && !state_slot && T_total > 0 && nc >= kSegMinChunks && (seg32 || seg64) &&
       ws.total > ws.carry_off) {
     Overlap* ov = overlap_of_current_device();
     if (ov) {
@@ -1272,8 +1299,12 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
         sp.c_count = kSegChunks;
         sp.h0 = s == 0 ? h0 : carry;
         sp.hT = s + 1 == n_seg ? hT : carry;
-        hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()),
-                           kScanLdsPad, stream, sp);
+        if (seg32)
+          hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()),
+                             kScanLdsPad, stream, sp);
+        else
+          hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4>), dim3(blocks4), dim3(scan_threads<2, 2>()),
+                             kScanLdsPad4, stream, sp);
         e = hipGetLastError();
       }
       return e;
@@ -1286,10 +1317,12 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     const hipError_t e = launch_prep(pp, dim3(Hk, n_chunk_slots), conv != nullptr, stream);
     if (e != hipSuccess) return e;
   }
-  if (blocks <= cus)
+  if (blocks <= cus) {
     hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()), 0, stream, sp);
-  else
-    hipLaunchKernelGGL((chunk_scan_kernel<1, 1>), dim3(blocks), dim3(scan_threads<1, 1>()), 0, stream, sp);
+  } else {
+    // more work-groups than CUs: the 64-channel form, half as many
+    hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
+  }
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ host copies stay a few GB:
   long prefill,    bf16 o (= fp32 o rounded) and gates from  bit-exact /
   other forms      projections (oracle)                       every head
   ragged segments  B=1, T=49509: three whole segments, a      every head
-                   short last one and a partial last chunk
+                   short last one and a partial last chunk;
+                   B=2 x 32805 in the 64-channel scan form
   decode step      256 sequences x 1 token, state in place   every head
   multi-token      256 sequences x 4 tokens, one pass        every head
   fused decode     the same batch through the whole mixer    every head
@@ -142,6 +143,20 @@ def test_segmented_prefill_ragged_tail_every_head():
     assert fs2 is None
     ci0 = dict(ci, h0=None)
     prefill_every_head(ci0, o2, None, T, batch=24)
+
+
+@pytest.mark.timeout(600)
+def test_segmented_prefill_two_sequences_every_head():
+    """B=2 equal sequences of 2 * 16384 + 37 tokens with initial states: the
+    64-channel scan form (384 32-channel work-groups would not fit the CUs)
+    in the overlapped launch (segments of 16384 tokens, a last one of 37);
+    every value head of both sequences against the oracle."""
+    L = 2 * 16384 + 37
+    log(f"segmented prefill, 2 sequences of {L}, every value head")
+    ci = synth.chunk_inputs_torch(1011, 2 * L, lengths=[L, L], h0_std=0.05)
+    o, fs = ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"],
+                              initial_state=ci["h0"], n_seqs=2)
+    prefill_every_head(ci, o, fs, 2 * L, batch=16, cu=synth.cu_from_lengths([L, L]), n_seqs=2)
 
 
 @pytest.mark.timeout(600)
