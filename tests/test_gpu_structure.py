@@ -162,3 +162,74 @@ def test_empty_batch_is_a_no_op():
     cs30 = cs3.clone()
     out = ops.gdn_decode_mixer_step(x0, w, cs3, zg, zg, zv, nw, pool, Hk=2)
     assert out.shape[0] == 0 and torch.equal(pool, pool0) and torch.equal(cs3, cs30)
+
+
+@pytest.mark.parametrize("case", ["varlen", "segmented", "decode"])
+def test_graph_replay_matches_eager(case):
+    """A captured HIP graph of the call (after one eager warm-up), replayed
+    three times with eager work and synchronisations between the replays,
+    gives the eager call's bits every time.  `segmented` is a B = 1 prefill
+    of 32,868 tokens: the overlapped launch, whose second stream joins the
+    capture through its events."""
+    log(f"graph capture and replay: {case}")
+    if case == "varlen":
+        lens = [300, 1, 0, 129, 64]
+        ci = synth.chunk_inputs_torch(4100, sum(lens), lengths=lens, h0_std=0.05)
+        n = len(lens)
+    elif case == "segmented":
+        ci = synth.chunk_inputs_torch(4101, 2 * 16384 + 100, h0_std=0.05)
+        n = 1
+    else:
+        di = synth.decode_inputs_torch(4102, 8)
+    if case == "decode":
+        state0 = di["state"].clone()
+        o = torch.empty((8, 48, 128), dtype=torch.float32, device="cuda")
+        st = state0.clone()
+
+        def call():
+            ops.gdn_decode_step(di["q"], di["k"], di["v"], di["g"], di["beta"], st, o=o)
+
+        def reset():
+            st.copy_(state0)
+
+        outs = lambda: (o.clone(), st.clone())
+    else:
+        T = ci["q"].shape[0]
+        o = torch.empty((T, 48, 128), dtype=torch.float32, device="cuda")
+        fs = torch.empty((n, 48, 128, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ops.gdn_chunk_fwd_workspace_bytes(n, T, 16, 48), dtype=torch.uint8,
+                         device="cuda")
+
+        def call():
+            ops.gdn_chunk_fwd(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"],
+                              initial_state=ci["h0"], final_state=fs, o=o, n_seqs=n,
+                              cu_seqlens=ci["cu_seqlens"], workspace=ws)
+
+        def reset():
+            o.zero_()
+            fs.zero_()
+
+        outs = lambda: (o.clone(), fs.clone())
+    call()
+    torch.cuda.synchronize()
+    want = outs()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        call()               # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outs()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {r} differs from the eager call"
+        junk = torch.randn(1 << 16, device="cuda") * 2.0     # eager work between replays
+        del junk
