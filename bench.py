@@ -13,7 +13,7 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
           RMSNorm, as four launches and as one gdn_mixer_fwd call (the conv
           front inside the prep kernel);
   varlen  packed prefill of 262,144 tokens in 24 sequences (cu_seqlens);
-  backward  gdn_backward (the rule's gradients) on 8 sequences of 1024 tokens.
+  backward  gdn_backward (the rule's gradients) on 8 x 1024 and 1 x 8192 tokens.
   latency   the core recurrence at T = 512 (zero state): median and min of
           single launches;
   ceilings  what this device sustains: a 1 GiB device copy and a dense
@@ -275,33 +275,43 @@ def leg_varlen(args, ops, synth, torch):
     return res
 
 
+# fp32 matrix-core products issued per (chunk of 64 tokens, value head) by the
+# chunked backward, 16x16x4 each (2,048 flops), masked blocks included:
+#   per-chunk pass   Q K^T, K K^T: 640 per key head = 640 / 3 per value head
+#   forward chain    K S0^T 128, T R 40, K^T (D U) 128 per 16-channel tile x 8
+#   reverse chain    K dS^T 128, P^T dO 40, T^T dU 40, the dS update 256, x 8
+#   gradient pass    dP and dA 640, the S0 / dS_C products 3,072, the
+#                    (dP o M), W products 1,280, K K^T 320 / 3
+BWD_MFMA_PER_CHUNK_HEAD = 640 / 3 + 8 * 296 + 8 * 464 + 640 + 3072 + 1280 + 320 / 3
+FP32_MFMA_PEAK_TFLOPS = 157.3       # dense fp32 matrix, MI355X
+
+
 def leg_backward(args, ops, synth, torch):
-    """gdn_backward over a training-shaped batch: 8 sequences of 1024 tokens."""
-    N, L = 8, 1024
-    T = N * L
-    log(f"[backward] drawing inputs T={T} N={N}")
-    ci = synth.chunk_inputs_torch(1008, T, lengths=[L] * N, h0_std=0.02)
-    bs = synth.backward_seeds_torch(1009, T, N)
-    d_o, dhT = bs["d_o"], bs["dhT"]
-    ws = torch.empty(ops.gdn_backward_workspace_bytes(N, T, HV), dtype=torch.uint8, device="cuda")
+    """gdn_backward over two training-shaped batches: 8 sequences of 1024
+    tokens, and one sequence of 8192 (the longest chain)."""
+    res = {}
+    for N, L in ((8, 1024), (1, 8192)):
+        T = N * L
+        log(f"[backward] drawing inputs N={N} L={L}")
+        ci = synth.chunk_inputs_torch(1008, T, lengths=[L] * N, h0_std=0.02)
+        bs = synth.backward_seeds_torch(1009, T, N)
+        d_o, dhT = bs["d_o"], bs["dhT"]
+        ws = torch.empty(ops.gdn_backward_workspace_bytes(N, T, HV), dtype=torch.uint8, device="cuda")
 
-    def step():
-        ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], d_o,
-                         initial_state=ci["h0"], grad_final_state=dhT,
-                         cu_seqlens=ci["cu_seqlens"], workspace=ws)
+        def step():
+            ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], d_o,
+                             initial_state=ci["h0"], grad_final_state=dhT,
+                             cu_seqlens=ci["cu_seqlens"], workspace=ws)
 
-    ev, wall = time_leg(step, max(2, args.steps // 4), 1)
-    # algorithmic bytes: q, k, v, g, beta and d_o in; dq, dk, dv, dg, dbeta out;
-    # h0, dhT in and dh0 out
-    per_tok = HK * D * 2 * 2 + HV * D * 2 + HV * 4 * 2 + HV * D * 4 + HK * D * 4 * 2 + HV * D * 4 \
-        + HV * 4 * 2
-    alg = T * per_tok + 3 * N * STATE_BYTES
-    recorded = 2 * (T // 4 + N) * STATE_BYTES   # the checkpointed states, written and read once
-    res = dict(tokens=T, n_seqs=N, event_ms=ev, wall_ms=wall, tokens_per_s=T / (ev * 1e-3),
-               alg_gbps=alg / (ev * 1e-3) / 1e9,
-               with_record_gbps=(alg + recorded) / (ev * 1e-3) / 1e9)
-    log(f"[backward] {ev:.3f} ms/call, {res['tokens_per_s'] / 1e6:.3f} M tok/s, "
-        f"{res['with_record_gbps']:.0f} GB/s counting the checkpoints")
+        ev, wall = time_leg(step, max(2, args.steps // 4), 1)
+        chunk_heads = N * ((L + C - 1) // C) * HV
+        flops = chunk_heads * BWD_MFMA_PER_CHUNK_HEAD * 2048
+        r = dict(tokens=T, n_seqs=N, event_ms=ev, wall_ms=wall, tokens_per_s=T / (ev * 1e-3),
+                 mfma_fp32_tflops=flops / (ev * 1e-3) / 1e12, workspace_bytes=ws.numel())
+        log(f"[backward] {N} x {L}: {ev:.3f} ms/call, {r['tokens_per_s'] / 1e6:.3f} M tok/s, "
+            f"{r['mfma_fp32_tflops']:.1f} TFLOP/s fp32 matrix, workspace {ws.numel() / T / 1024:.0f} KiB/token")
+        res[f"{N}x{L}"] = r
+        del ws, ci, bs, d_o, dhT
     return res
 
 
@@ -546,10 +556,12 @@ def main():
                                     "hbm_frac": round(vl["hbm_gbps"] / HBM_PEAK_GBPS, 4),
                                     "mfma_frac": round(vl["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
     if "backward" in out:
-        bw = out["backward"]
-        line["backward_8x1024"] = {"ms": round(bw["event_ms"], 4),
-                                   "tokens_per_s": round(bw["tokens_per_s"], 1),
-                                   "GBps_with_checkpoints": round(bw["with_record_gbps"], 1)}
+        for key, bw in out["backward"].items():
+            line[f"backward_{key}"] = {
+                "ms": round(bw["event_ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
+                "mfma_fp32_tflops": round(bw["mfma_fp32_tflops"], 2),
+                "mfma_fp32_frac": round(bw["mfma_fp32_tflops"] / FP32_MFMA_PEAK_TFLOPS, 4),
+                "workspace_bytes_per_token": round(bw["workspace_bytes"] / bw["tokens"])}
     if ci is not None and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds, torch)
     print(json.dumps(line), flush=True)

@@ -741,7 +741,7 @@ gdn_status gdn_calib_mfma_loop(int32_t n_iter, int32_t n_blocks, float* out, voi
 
 size_t gdn_backward_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hv) {
   if (n_seqs <= 0 || T_total <= 0 || Hv <= 0) return 0;
-  return gdn::backward_workspace_bytes(n_seqs, T_total, Hv);
+  return gdn::chunked_backward_workspace_bytes(n_seqs, T_total, Hv);
 }
 
 gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t* k,
@@ -810,7 +810,7 @@ gdn_status gdn_backward(const uint16_t* q, int64_t q_tok_stride, const uint16_t*
     const gdn_status s = gdn_validate_cu_seqlens(cu_seqlens, n_seqs, T_total, stream);
     if (s) return s;
   }
-  return hip_status(gdn::launch_backward(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta,
+  return hip_status(gdn::launch_backward_chunked(q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, g, beta,
                                          initial_state, grad_o, grad_final_state, cu_seqlens,
                                          n_seqs, T_total, Hk, Hv, scale, grad_q, grad_k, grad_v,
                                          grad_g, grad_beta, grad_initial_state, workspace,

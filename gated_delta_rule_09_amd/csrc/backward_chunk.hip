@@ -1,0 +1,823 @@
+// backward_chunk.hip -- chunked backward of the gated delta rule: the
+// derivatives of
+//     L = sum(dO * O) + sum(dS_T * S_T)
+// with respect to q, k, v, g, beta and the initial state, for the rule of the
+// "Delta-rule layers" row of the model card's Architecture table,
+//     S <- a S + b (v - a S k) k^T,   o = scale S q,   a = exp(g),
+// taken through the chunk-parallel (WY) form of the same rule that the
+// prefill evaluates (chunks of 64 tokens).  Per chunk, with G the running sum
+// of g inside the chunk, gamma = exp(G), M_ij = exp(G_i - G_j) (j <= i),
+// D_i = exp(G_last - G_i), A = strictly lower (b_i M_ij k_i.k_j), T = (I + A)^-1:
+//     E = V - gamma K S0^T,  U = T (b E),  O = scale (gamma Q S0^T + (M o Q K^T) U),
+//     S_C = gamma_last S0 + U^T D K.
+// Its chain rule, with dS_C the gradient of the chunk's final state:
+//     dU = scale P^T dO + D K dS_C^T,   dR = T^T dU,   dv = b dR,
+//     dS0 = gamma_last dS_C + scale (gamma Q)^T-weighted dO - (b gamma K)-weighted dR
+//     dA = -dR U^T,  dP = scale dO U^T,
+//     dq = scale gamma dO S0 + (dP o M) K,
+//     dk = (dP o M)^T Q + D U dS_C - gamma b dR S0 + W K + W^T K,  W = b o dA o M,
+//     dbeta_i = dR_i . E_i + sum_j dA_ij M_ij k_i.k_j,
+// and the gradient of the log-decays through every gamma, M and D they enter,
+// collected per token as dG_i = q_i . dq_i + k_i . (W K - W^T K - (dP o M)^T Q
+// - gamma b dR S0 - D U dS_C)_i (+ gamma_last <dS_C, S0> + sum_m k_m . (D U dS_C)_m
+// on the last token), then dg = the suffix sum of dG over the chunk.
+//
+// Five launches:
+//   cb_fill/cb_table   chunk slots -> sequence (slot = first token / 64 + sequence)
+//   cb_prep            per (chunk, key head): Q K^T, K K^T (fp32 MFMA), then per
+//                      value head T (forward substitution, one column per lane)
+//                      and P, packed in one 64 x 64 matrix X: T below the
+//                      diagonal, P_ii on it, P_ji above it (T_ii = 1)
+//   cb_fwd             per (sequence, value head, 64 channels): the state chain
+//                      forwards, recording S0, U, E of every chunk
+//   cb_bwd             per (sequence, value head, 64 channels): the gradient
+//                      chain backwards, recording dS_C and dR, writing dv, dh0
+//   cb_grad            per (chunk, key head): dq, dk (summed over the value
+//                      heads in registers), dg, dbeta
+// All contractions run on v_mfma_f32_16x16x4_f32 with fp32 operands: the
+// gradients keep fp32 accuracy at any scale of dO.  In the chains every
+// 64-token x 16-channel intermediate stays in the accumulator layout (lane l:
+// rows 4 (l / 16) + r, column l % 16) and enters the next product as its B
+// operand directly; the A operand then takes its k columns in the same order.
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kC = 64;
+constexpr int kKS = 136;          // bf16 row stride of staged K / Q rows (272 bytes)
+constexpr int kXS = 68;           // fp32 row stride of staged X (272 bytes)
+
+struct CbParams {
+  const uint16_t* q; const uint16_t* k; const uint16_t* v;
+  int64_t qs, ks, vs;
+  const float* g; const float* beta;
+  const float* h0; const float* d_o; const float* dhT;
+  const int32_t* cu;          // nullptr: equal lengths seq_len
+  int n_seqs, seq_len, Hk, Hv, group, n_slots;
+  float scale;
+  int32_t* slot_seq;          // [n_slots]: sequence of the chunk in the slot, -1 for none
+  float* X;                   // [n_slots][Hv][64][64]
+  float* S0;                  // [n_slots][Hv][128][128]: state before the chunk, [dv][dk]
+  float* dSC;                 // [n_slots][Hv][128][128]: dL/dS after the chunk
+  float* U; float* E; float* dR;   // [n_slots][Hv][64][128]
+  float* dq; float* dk; float* dv; float* dg; float* dbeta; float* dh0;
+};
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void cb_seq(const CbParams& p, int n, int& s0, int& s1) {
+  if (p.cu) { s0 = p.cu[n]; s1 = p.cu[n + 1]; }
+  else { s0 = n * p.seq_len; s1 = s0 + p.seq_len; }
+}
+
+// Slot of chunk c of sequence n (first token s0): s0 / 64 + c + n grows by
+// one per chunk of a sequence and by at least one from a sequence's last chunk
+// to the next sequence's first, so slots are distinct and below T / 64 + N.
+__device__ __forceinline__ int cb_slot(int s0, int c, int n) { return (s0 >> 6) + c + n; }
+
+struct SlotChunk { int n, t0, len; };
+__device__ __forceinline__ bool slot_chunk(const CbParams& p, int slot, SlotChunk& sc) {
+  const int n = p.slot_seq[slot];
+  if (n < 0) return false;
+  int s0, s1;
+  cb_seq(p, n, s0, s1);
+  sc.n = n;
+  sc.t0 = s0 + kC * (slot - n - (s0 >> 6));
+  sc.len = min(kC, s1 - sc.t0);
+  return true;
+}
+
+// inclusive prefix sum over the 64 lanes, in lane order
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+// Gates of one chunk and value head, lane i = token i of the chunk (g and
+// beta are 0 past its end, so G_63 = G_last and the padded tokens drop out).
+struct Gates { float G, gam, dec, bet; };
+__device__ __forceinline__ Gates chunk_gates(const CbParams& p, int t0, int len, int h) {
+  const int i = threadIdx.x & 63;
+  const bool ok = i < len;
+  const float gi = ok ? p.g[static_cast<int64_t>(t0 + i) * p.Hv + h] : 0.f;
+  Gates r;
+  r.bet = ok ? p.beta[static_cast<int64_t>(t0 + i) * p.Hv + h] : 0.f;
+  r.G = wave_prefix_sum(gi);
+  const float GL = __shfl(r.G, 63, 64);
+  r.gam = expf(r.G);
+  r.dec = expf(GL - r.G);
+  return r;
+}
+
+// Stage the chunk's 64 rows of bf16 K (or Q) of key head kh into LDS rows of
+// kKS halves, zero past the end; kThr threads, each 8192 / kThr halves of a row
+// (rows 16-byte aligned: the entry point checks the pointers and strides).
+template <int kThr>
+__device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t stride, int t0, int len, int kh,
+                                           uint16_t (*dst)[kKS]) {
+  constexpr int kPer = kC * kD / kThr;          // halves per thread: 32 (256 thr) or 16 (512)
+  const int tid = threadIdx.x;
+  const int row = tid / (kD / kPer);
+  const int c0 = (tid % (kD / kPer)) * kPer;
+  const bool ok = row < len;
+  const uint4* s = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + row) * stride + kh * kD + c0);
+#pragma unroll
+  for (int j = 0; j < kPer / 8; ++j) {
+    const uint4 x = ok ? s[j] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&dst[row][c0 + 8 * j]) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void cb_fill_kernel(int32_t* __restrict__ slot_seq, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) slot_seq[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void cb_table_kernel(CbParams p) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.n_seqs) return;
+  int s0, s1;
+  cb_seq(p, n, s0, s1);
+  const int nc = (s1 - s0 + kC - 1) / kC;
+  for (int c = 0; c < nc; ++c) p.slot_seq[cb_slot(s0, c, n)] = n;
+}
+
+// ---------------------------------------------------------------------------
+// cb_prep: one work-group (4 waves) per (chunk slot, key head).
+constexpr int kSS = 65;           // fp32 row stride of Q K^T, K K^T
+struct PrepLds {
+  uint16_t q[kC][kKS], k[kC][kKS];
+  float qkt[kC][kSS];
+  float kkt[kC][kSS];
+};
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__global__ __launch_bounds__(256) void cb_prep_kernel(CbParams p) {
+  __shared__ __align__(16) PrepLds sm;
+  const int slot = blockIdx.x / p.Hk;
+  const int kh = blockIdx.x - slot * p.Hk;
+  SlotChunk sc;
+  if (!slot_chunk(p, slot, sc)) return;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+
+  stage_rows<256>(p.q, p.qs, sc.t0, sc.len, kh, sm.q);
+  stage_rows<256>(p.k, p.ks, sc.t0, sc.len, kh, sm.k);
+  __syncthreads();
+  // Q K^T and K K^T on and below the diagonal: 2 x 10 blocks of 16 x 16
+  for (int job = w; job < 20; job += 4) {
+    const int kind = job / 10;
+    const int b = job - 10 * kind;
+    const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+    const int jb = b - ib * (ib + 1) / 2;
+    const uint16_t (*A)[kKS] = kind ? sm.k : sm.q;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int kk = 0; kk < kD / 4; ++kk)
+      acc = mfma4(bf16_to_f32(A[ib * 16 + m][4 * kk + g4]), bf16_to_f32(sm.k[jb * 16 + m][4 * kk + g4]), acc);
+    float (*dst)[kSS] = kind ? sm.kkt : sm.qkt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
+  }
+  __syncthreads();
+
+  for (int hv = w; hv < p.group; hv += 4) {
+    const int h = kh * p.group + hv;
+    const Gates gt = chunk_gates(p, sc.t0, sc.len, h);
+    // T = (I + A)^-1 by forward substitution, lane = column c:
+    //   T_ic = delta_ic - sum_{j<i} A_ij T_jc,   A_ij = b_i M_ij k_i.k_j (j < i);
+    // lane j computes A_ij, read by every lane from there
+    float t[kC];
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      const float Gi = lane_value(gt.G, i);
+      const float bi = lane_value(gt.bet, i);
+      const float a = lane < i ? bi * expf(Gi - gt.G) * sm.kkt[i][lane] : 0.f;
+      float acc = lane == i ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) acc = fmaf(-lane_value(a, j), t[j], acc);
+      t[i] = acc;
+    }
+    // X row i: T_ij (j < i), P_ii, P_ji = M_ji q_j.k_i (j > i); lane = column j
+    float* Xh = p.X + (static_cast<int64_t>(slot) * p.Hv + h) * (kC * kC);
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      const float Gi = lane_value(gt.G, i);
+      Xh[i * kC + lane] = lane < i ? t[i] : expf(gt.G - Gi) * sm.qkt[lane][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cb_fwd: one work-group (4 waves) per (sequence, value head, 64 channels);
+// wave w carries channels 16 (4 half + w) .. + 15 of S^T in 8 accumulators
+// (s[db][r] = S^T[16 db + 4 (lane / 16) + r][channel 16 tile + lane % 16]).
+struct ChainLds {
+  uint16_t k[kC][kKS];
+  uint16_t q[kC][kKS];
+  float x[kC][kXS];
+  float gam[kC], dec[kC], bet[kC];
+};
+
+template <int kThr>
+__device__ __forceinline__ void stage_x(const float* Xh, float (*dst)[kXS]) {
+  constexpr int kPer = kC * kC / kThr;       // floats per thread: 16
+  const int tid = threadIdx.x;
+  const int row = tid / (kC / kPer);
+  const int c0 = (tid % (kC / kPer)) * kPer;
+#pragma unroll
+  for (int j = 0; j < kPer / 4; ++j)
+    *reinterpret_cast<floatx4*>(&dst[row][c0 + 4 * j]) = *reinterpret_cast<const floatx4*>(Xh + row * kC + c0 + 4 * j);
+}
+
+__device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
+
+__global__ __launch_bounds__(256) void cb_fwd_kernel(CbParams p) {
+  __shared__ __align__(16) ChainLds sm;
+  const int unit = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
+  const int n = unit / p.Hv;
+  const int h = unit - n * p.Hv;
+  const int kh = h / p.group;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+  const int ch = (4 * half + w) * 16 + m;
+  int s0, s1;
+  cb_seq(p, n, s0, s1);
+  const int nc = (s1 - s0 + kC - 1) / kC;
+
+  floatx4 s[8];
+  const int64_t hrow = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch) * kD + 4 * g4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    s[db] = p.h0 ? *reinterpret_cast<const floatx4*>(p.h0 + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = 0; c < nc; ++c) {
+    const int t0 = s0 + kC * c;
+    const int len = min(kC, s1 - t0);
+    const int slot = cb_slot(s0, c, n);
+    const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
+    stage_rows<256>(p.k, p.ks, t0, len, kh, sm.k);
+    stage_x<256>(p.X + sh * (kC * kC), sm.x);
+    if (w == 0) {
+      const Gates gt = chunk_gates(p, t0, len, h);
+      sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
+    }
+    __syncthreads();
+
+    // the state before the chunk
+    float* S0 = p.S0 + (sh * kD + ch) * kD + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(S0 + 16 * db) = s[db];
+
+    // Z = K S0^T (tokens x channels)
+    floatx4 z[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint2 kx = *reinterpret_cast<const uint2*>(&sm.k[tb * 16 + m][db * 16 + 4 * g4]);
+        z[tb] = mfma4(bf(kx.x & 0xffff), s[db][0], z[tb]);
+        z[tb] = mfma4(bf(kx.x >> 16), s[db][1], z[tb]);
+        z[tb] = mfma4(bf(kx.y & 0xffff), s[db][2], z[tb]);
+        z[tb] = mfma4(bf(kx.y >> 16), s[db][3], z[tb]);
+      }
+    }
+    // E = V - gamma Z, R = b E  (token tb*16 + 4 g4 + r, channel ch)
+    float* Eh = p.E + sh * (kC * kD) + ch;
+    floatx4 R[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tb * 16 + 4 * g4 + r;
+        const float vv = tok < len ? bf(p.v[static_cast<int64_t>(t0 + tok) * p.vs + h * kD + ch]) : 0.f;
+        const float e = vv - sm.gam[tok] * z[tb][r];
+        Eh[tok * kD] = e;
+        R[tb][r] = sm.bet[tok] * e;
+      }
+    // U = T R
+    float* Uh = p.U + sh * (kC * kD) + ch;
+    floatx4 DU[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const int i = ib * 16 + m;
+      floatx4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = 0; jb <= ib; ++jb) {
+        const int j0 = jb * 16 + 4 * g4;
+        const floatx4 xr = *reinterpret_cast<const floatx4*>(&sm.x[i][j0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = j0 + r < i ? xr[r] : j0 + r == i ? 1.f : 0.f;
+          u = mfma4(a, R[jb][r], u);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = ib * 16 + 4 * g4 + r;
+        Uh[tok * kD] = u[r];
+        DU[ib][r] = sm.dec[tok] * u[r];
+      }
+    }
+    // S^T <- gamma_last S^T + K^T (D U)
+    const float gl = sm.gam[kC - 1];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      floatx4 acc = s[db] * gl;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc = mfma4(bf(sm.k[jb * 16 + 4 * g4 + r][db * 16 + m]), DU[jb][r], acc);
+      s[db] = acc;
+    }
+    __syncthreads();   // before the next chunk's staging
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cb_bwd: the gradient chain, chunks in reverse; wave layout as cb_fwd, with
+// ds[db][r] = dS^T[16 db + 4 (lane / 16) + r][channel].
+__global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
+  __shared__ __align__(16) ChainLds sm;
+  const int unit = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
+  const int n = unit / p.Hv;
+  const int h = unit - n * p.Hv;
+  const int kh = h / p.group;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+  const int ch = (4 * half + w) * 16 + m;
+  int s0, s1;
+  cb_seq(p, n, s0, s1);
+  const int nc = (s1 - s0 + kC - 1) / kC;
+
+  floatx4 ds[8];
+  const int64_t hrow = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch) * kD + 4 * g4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    ds[db] = p.dhT ? *reinterpret_cast<const floatx4*>(p.dhT + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = s0 + kC * c;
+    const int len = min(kC, s1 - t0);
+    const int slot = cb_slot(s0, c, n);
+    const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
+    stage_rows<256>(p.k, p.ks, t0, len, kh, sm.k);
+    stage_rows<256>(p.q, p.qs, t0, len, kh, sm.q);
+    stage_x<256>(p.X + sh * (kC * kC), sm.x);
+    if (w == 0) {
+      const Gates gt = chunk_gates(p, t0, len, h);
+      sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
+    }
+    // dO of the chunk in the accumulator layout (token tb*16 + 4 g4 + r)
+    floatx4 dO[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tb * 16 + 4 * g4 + r;
+        dO[tb][r] = tok < len ? p.d_o[(static_cast<int64_t>(t0 + tok) * p.Hv + h) * kD + ch] : 0.f;
+      }
+    __syncthreads();
+
+    // the gradient of the state after the chunk
+    float* dSC = p.dSC + (sh * kD + ch) * kD + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(dSC + 16 * db) = ds[db];
+
+    // Z = K dS^T
+    floatx4 z[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint2 kx = *reinterpret_cast<const uint2*>(&sm.k[tb * 16 + m][db * 16 + 4 * g4]);
+        z[tb] = mfma4(bf(kx.x & 0xffff), ds[db][0], z[tb]);
+        z[tb] = mfma4(bf(kx.x >> 16), ds[db][1], z[tb]);
+        z[tb] = mfma4(bf(kx.y & 0xffff), ds[db][2], z[tb]);
+        z[tb] = mfma4(bf(kx.y >> 16), ds[db][3], z[tb]);
+      }
+    }
+    // dU = scale P^T dO + D Z;  (P^T)_ij = P_ji = X_ij for j > i, X_ii on the diagonal
+    floatx4 dU[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const int i = ib * 16 + m;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = ib; jb < 4; ++jb) {
+        const int j0 = jb * 16 + 4 * g4;
+        const floatx4 xr = *reinterpret_cast<const floatx4*>(&sm.x[i][j0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = mfma4(j0 + r >= i ? xr[r] : 0.f, dO[jb][r], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dU[ib][r] = p.scale * acc[r] + sm.dec[ib * 16 + 4 * g4 + r] * z[ib][r];
+    }
+    // dR = T^T dU;  (T^T)_ij = T_ji = X_ji for j > i, 1 on the diagonal
+    float* dRh = p.dR + sh * (kC * kD) + ch;
+    floatx4 dR[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const int i = ib * 16 + m;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jb = ib; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb * 16 + 4 * g4 + r;
+          acc = mfma4(j > i ? sm.x[j][i] : j == i ? 1.f : 0.f, dU[jb][r], acc);
+        }
+      dR[ib] = acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = ib * 16 + 4 * g4 + r;
+        dRh[tok * kD] = acc[r];
+        if (tok < len) p.dv[(static_cast<int64_t>(t0 + tok) * p.Hv + h) * kD + ch] = sm.bet[tok] * acc[r];
+      }
+    }
+    // dS^T <- gamma_last dS^T + Q^T (scale gamma dO) - K^T (b gamma dR)
+    floatx4 bo[4], br[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = jb * 16 + 4 * g4 + r;
+        bo[jb][r] = p.scale * sm.gam[tok] * dO[jb][r];
+        br[jb][r] = -sm.bet[tok] * sm.gam[tok] * dR[jb][r];
+      }
+    const float gl = sm.gam[kC - 1];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      floatx4 acc = ds[db] * gl;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = jb * 16 + 4 * g4 + r;
+          acc = mfma4(bf(sm.q[tok][db * 16 + m]), bo[jb][r], acc);
+          acc = mfma4(bf(sm.k[tok][db * 16 + m]), br[jb][r], acc);
+        }
+      ds[db] = acc;
+    }
+    __syncthreads();   // before the next chunk's staging
+  }
+  if (p.dh0) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(p.dh0 + hrow + 16 * db) = ds[db];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cb_grad: one work-group (8 waves) per (chunk slot, key head).  Wave w owns
+// columns 16 w .. 16 w + 15 of the 64 x 128 results (dq, dk and their parts),
+// and a share of the 64 x 64 products dP = scale dO U^T, dA = -dR U^T.
+constexpr int kGS = 129;          // fp32 row stride of staged dO, U, dR
+constexpr int kMS = 68;           // fp32 row stride of dP o M, W
+struct GradLds {
+  uint16_t q[kC][kKS], k[kC][kKS];
+  float kkt[kC][kSS];
+  union {
+    struct { float dO[kC][kGS]; float U[kC][kGS]; float dR[kC][kGS]; } in;
+    struct { float dpm[kC][kMS]; float w[kC][kMS]; } mid;
+  } u;
+  float G[kC], gam[kC], dec[kC], bet[kC];
+  float part_q[kC][8], part_y[kC][8], part_s[kC][8];
+  float part_b[kC][4];
+  float dbe[kC];
+  float dss[8];
+};
+
+__global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
+  __shared__ __align__(16) GradLds sm;
+  const int slot = blockIdx.x / p.Hk;
+  const int kh = blockIdx.x - slot * p.Hk;
+  SlotChunk sc;
+  if (!slot_chunk(p, slot, sc)) return;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int g4 = lane >> 4;
+  const int d = w * 16 + m;            // this lane's column of the 64 x 128 results
+
+  stage_rows<512>(p.q, p.qs, sc.t0, sc.len, kh, sm.q);
+  stage_rows<512>(p.k, p.ks, sc.t0, sc.len, kh, sm.k);
+  __syncthreads();
+  // K K^T on and below the diagonal (10 blocks)
+  for (int b = w; b < 10; b += 8) {
+    const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+    const int jb = b - ib * (ib + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int kk = 0; kk < kD / 4; ++kk)
+      acc = mfma4(bf(sm.k[ib * 16 + m][4 * kk + g4]), bf(sm.k[jb * 16 + m][4 * kk + g4]), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.kkt[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
+  }
+
+  // dk summed over the value heads in registers; dq in its output rows (each
+  // element written, then added to, by the one lane that owns it)
+  floatx4 dk_tot[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) dk_tot[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float* dq_out = p.dq + (static_cast<int64_t>(sc.t0) * p.Hk + kh) * kD + d;
+
+  for (int hv = 0; hv < p.group; ++hv) {
+    // the lane indices again from an opaque copy of the thread id: the address
+    // arithmetic of every phase below is then redone per value head rather
+    // than hoisted out of the loop, where it would hold registers throughout
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int lane = tid_v & 63;
+    const int m = lane & 15;
+    const int g4 = lane >> 4;
+    const int d = w * 16 + m;
+    const int h = kh * p.group + hv;
+    const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
+    {  // dO, U, dR rows: thread -> row tid / 8, 16 columns
+      const int row = tid >> 3;
+      const int c0 = (tid & 7) * 16;
+      const bool ok = row < sc.len;
+      const float* so = p.d_o + (static_cast<int64_t>(sc.t0 + row) * p.Hv + h) * kD + c0;
+      const float* su = p.U + (sh * kC + row) * kD + c0;
+      const float* sr = p.dR + (sh * kC + row) * kD + c0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // grad_o is only 4-byte aligned
+        const floatx4 xo = ok ? floatx4{so[4 * j], so[4 * j + 1], so[4 * j + 2], so[4 * j + 3]}
+                              : floatx4{0.f, 0.f, 0.f, 0.f};
+        const floatx4 xu = *reinterpret_cast<const floatx4*>(su + 4 * j);
+        const floatx4 xr = *reinterpret_cast<const floatx4*>(sr + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.u.in.dO[row][c0 + 4 * j + e] = xo[e];
+          sm.u.in.U[row][c0 + 4 * j + e] = xu[e];
+          sm.u.in.dR[row][c0 + 4 * j + e] = xr[e];
+        }
+      }
+    }
+    if (w == 0) {
+      const Gates gt = chunk_gates(p, sc.t0, sc.len, h);
+      sm.G[lane] = gt.G; sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
+    }
+    __syncthreads();
+
+    // products with S0 and dS_C (B operands straight from the workspace):
+    //   dq_h  = (scale gamma dO) S0,  X1 = (-gamma b dR) S0,  dKS = (D U) dS_C
+    floatx4 dqh[4], x1[4], dks[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) dqh[tb] = x1[tb] = dks[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float fq[4], fr[4], fu[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int i = tb * 16 + m;
+      fq[tb] = p.scale * sm.gam[i];
+      fr[tb] = -sm.gam[i] * sm.bet[i];
+      fu[tb] = sm.dec[i];
+    }
+    const float* S0 = p.S0 + sh * (kD * kD) + d;
+    const float* dSC = p.dSC + sh * (kD * kD) + d;
+    float dss = 0.f;
+#pragma unroll 1
+    for (int kk = 0; kk < kD / 4; ++kk) {
+      const int c = 4 * kk + g4;
+      const float b1 = S0[c * kD];
+      const float b2 = dSC[c * kD];
+      dss = fmaf(b1, b2, dss);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int i = tb * 16 + m;
+        dqh[tb] = mfma4(fq[tb] * sm.u.in.dO[i][c], b1, dqh[tb]);
+        x1[tb] = mfma4(fr[tb] * sm.u.in.dR[i][c], b1, x1[tb]);
+        dks[tb] = mfma4(fu[tb] * sm.u.in.U[i][c], b2, dks[tb]);
+      }
+    }
+    dss = wave_sum(dss);
+    if (lane == 0) sm.dss[w] = dss;
+    // k . dKS per token now, and dKS into dk: it is not needed again
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = tb * 16 + 4 * g4 + r;
+        const float ps = sum16(bf(sm.k[i][d]) * dks[tb][r]);
+        if (m == 0) sm.part_s[i][w] = ps;
+      }
+      dk_tot[tb] += dks[tb];
+    }
+    // dbeta's first part: dR_i . E_i, rows 8 w .. 8 w + 7
+    {
+      const float* Eh = p.E + sh * (kC * kD);
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int i = 8 * w + rr;
+        float x = sm.u.in.dR[i][lane] * Eh[i * kD + lane] + sm.u.in.dR[i][lane + 64] * Eh[i * kD + lane + 64];
+        x = wave_sum(x);
+        if (lane == 0) sm.dbe[i] = x;
+      }
+    }
+    // dP o M and W = b o dA o M on and below the diagonal: wave w takes the
+    // 16 x 16 blocks w and w + 8 of the ten (both products share U^T), held in
+    // registers until the staged rows are no longer read
+    floatx4 resP[2], resW[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int b = w + 8 * s2;
+      resP[s2] = resW[s2] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (b >= 10) break;
+      const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+      const int jb = b - ib * (ib + 1) / 2;
+      floatx4 accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kk = 0; kk < kD / 4; ++kk) {
+        const float bu = sm.u.in.U[jb * 16 + m][4 * kk + g4];
+        accP = mfma4(sm.u.in.dO[ib * 16 + m][4 * kk + g4], bu, accP);
+        accA = mfma4(sm.u.in.dR[ib * 16 + m][4 * kk + g4], bu, accA);
+      }
+      const int j = jb * 16 + m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * g4 + r;
+        const float Mij = j <= i ? expf(sm.G[i] - sm.G[j]) : 0.f;
+        const float dA = j < i ? -accA[r] : 0.f;
+        resP[s2][r] = p.scale * accP[r] * Mij;
+        resW[s2][r] = sm.bet[i] * dA * Mij;
+        const float pb = sum16(dA * Mij * sm.kkt[i][j]);
+        if (m == 0) sm.part_b[i][jb] = pb;
+      }
+    }
+    __syncthreads();   // staged rows no longer read: their space takes dP o M and W
+
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int b = w + 8 * s2;
+      if (b >= 10) break;
+      const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+      const int jb = b - ib * (ib + 1) / 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.u.mid.dpm[ib * 16 + 4 * g4 + r][jb * 16 + m] = resP[s2][r];
+        sm.u.mid.w[ib * 16 + 4 * g4 + r][jb * 16 + m] = resW[s2][r];
+      }
+    }
+    __syncthreads();
+
+    // per token block: dq_h += (dP o M) K;  X1 += W K;  X2 = W^T K + (dP o M)^T Q;
+    // then the block's dot products for dG (q . dq_h, k . (X1 - X2); k . dKS is
+    // subtracted in the sum below) and its share of dq, dk
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      floatx4 x2 = {0.f, 0.f, 0.f, 0.f};
+      const int i = tb * 16 + m;
+#pragma unroll 2
+      for (int kk = 0; kk < 4 * (tb + 1); ++kk) {
+        const int j = 4 * kk + g4;
+        const float bk = bf(sm.k[j][d]);
+        dqh[tb] = mfma4(sm.u.mid.dpm[i][j], bk, dqh[tb]);
+        x1[tb] = mfma4(sm.u.mid.w[i][j], bk, x1[tb]);
+      }
+#pragma unroll 2
+      for (int kk = 4 * tb; kk < 16; ++kk) {
+        const int j = 4 * kk + g4;
+        x2 = mfma4(sm.u.mid.w[j][i], bf(sm.k[j][d]), x2);
+        x2 = mfma4(sm.u.mid.dpm[j][i], bf(sm.q[j][d]), x2);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb * 16 + 4 * g4 + r;
+        const float pq = sum16(bf(sm.q[t][d]) * dqh[tb][r]);
+        const float py = sum16(bf(sm.k[t][d]) * (x1[tb][r] - x2[r]));
+        if (m == 0) { sm.part_q[t][w] = pq; sm.part_y[t][w] = py; }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb * 16 + 4 * g4 + r;
+        if (t < sc.len) {
+          float* o = dq_out + static_cast<int64_t>(t) * p.Hk * kD;
+          *o = hv == 0 ? dqh[tb][r] : *o + dqh[tb][r];
+        }
+      }
+      dk_tot[tb] += x1[tb] + x2;
+    }
+    __syncthreads();
+
+    if (w == 0) {
+      const int i = lane;
+      float dG = 0.f, ks = 0.f, dssT = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) {
+        dG += sm.part_q[i][ww] + sm.part_y[i][ww] - sm.part_s[i][ww];
+        ks += sm.part_s[i][ww];
+        dssT += sm.dss[ww];
+      }
+      ks = wave_sum(ks);
+      if (i == kC - 1) dG += sm.gam[kC - 1] * dssT + ks;
+      // dg_i = sum over i' >= i of dG_i'
+      const float tot = wave_sum(dG);
+      const float dg = tot - wave_prefix_sum(dG) + dG;
+      float db = sm.dbe[i];
+      for (int jb = 0; jb <= (i >> 4); ++jb) db += sm.part_b[i][jb];
+      if (i < sc.len) {
+        const int64_t o = static_cast<int64_t>(sc.t0 + i) * p.Hv + h;
+        p.dg[o] = dg;
+        p.dbeta[o] = db;
+      }
+    }
+    __syncthreads();   // before the next value head's staging
+  }
+
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tb * 16 + 4 * g4 + r;
+      if (i < sc.len) p.dk[(static_cast<int64_t>(sc.t0 + i) * p.Hk + kh) * kD + d] = dk_tot[tb][r];
+    }
+}
+
+}  // namespace
+
+size_t chunked_backward_workspace_bytes(int n_seqs, int T_total, int Hv) {
+  const size_t slots = static_cast<size_t>(T_total) / kC + static_cast<size_t>(n_seqs);
+  auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  const size_t sh = slots * static_cast<size_t>(Hv);
+  return up(slots * 4) + up(sh * kC * kC * 4) + 2 * up(sh * kD * kD * 4) + 3 * up(sh * kC * kD * 4);
+}
+
+hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
+                                   const uint16_t* v, int64_t vs, const float* g, const float* beta,
+                                   const float* h0, const float* d_o, const float* dhT,
+                                   const int32_t* cu, int n_seqs, int T_total, int Hk, int Hv,
+                                   float scale, float* dq, float* dk, float* dv, float* dg,
+                                   float* dbeta, float* dh0, void* workspace, hipStream_t stream) {
+  if (n_seqs == 0) return hipSuccess;
+  CbParams p;
+  p.q = q; p.k = k; p.v = v; p.qs = qs; p.ks = ks; p.vs = vs; p.g = g; p.beta = beta;
+  p.h0 = h0; p.d_o = d_o; p.dhT = dhT; p.cu = cu;
+  p.n_seqs = n_seqs; p.seq_len = cu ? 0 : T_total / n_seqs; p.Hk = Hk; p.Hv = Hv;
+  p.group = Hv / Hk; p.scale = scale;
+  const int n_slots = T_total / kC + n_seqs;
+  p.n_slots = n_slots;
+  auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  const size_t sh = static_cast<size_t>(n_slots) * Hv;
+  unsigned char* base = static_cast<unsigned char*>(workspace);
+  p.slot_seq = reinterpret_cast<int32_t*>(base); base += up(static_cast<size_t>(n_slots) * 4);
+  p.X = reinterpret_cast<float*>(base); base += up(sh * kC * kC * 4);
+  p.S0 = reinterpret_cast<float*>(base); base += up(sh * kD * kD * 4);
+  p.dSC = reinterpret_cast<float*>(base); base += up(sh * kD * kD * 4);
+  p.U = reinterpret_cast<float*>(base); base += up(sh * kC * kD * 4);
+  p.E = reinterpret_cast<float*>(base); base += up(sh * kC * kD * 4);
+  p.dR = reinterpret_cast<float*>(base);
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dh0 = dh0;
+
+  const unsigned chains = static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv) * 2u;
+  if (T_total > 0) {
+    hipLaunchKernelGGL(cb_fill_kernel, dim3((n_slots + 255) / 256), dim3(256), 0, stream, p.slot_seq, n_slots);
+    hipLaunchKernelGGL(cb_table_kernel, dim3((n_seqs + 255) / 256), dim3(256), 0, stream, p);
+    const unsigned per_chunk = static_cast<unsigned>(n_slots) * static_cast<unsigned>(Hk);
+    hipLaunchKernelGGL(cb_prep_kernel, dim3(per_chunk), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(cb_grad_kernel, dim3(per_chunk), dim3(512), 0, stream, p);
+  } else if (dh0) {
+    hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

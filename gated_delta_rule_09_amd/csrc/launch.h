@@ -104,16 +104,16 @@ hipError_t launch_conv_state(const uint16_t* x, int64_t xs, uint16_t* conv_state
                              hipStream_t stream, const int32_t* slots = nullptr,
                              int n_slots = 0);
 
-// Backward of the rule (backward.hip): workspace of (T_total / 4 + n_seqs) x
-// Hv x 64 KB of checkpointed states plus the partial dq, dk, dg, dbeta of
-// 1, 2 or 4 row groups per (token, value head).
-size_t backward_workspace_bytes(int n_seqs, int T_total, int Hv);
-hipError_t launch_backward(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
-                           const uint16_t* v, int64_t vs, const float* g, const float* beta,
-                           const float* h0, const float* d_o, const float* dhT, const int32_t* cu,
-                           int n_seqs, int T_total, int Hk, int Hv, float scale, float* dq,
-                           float* dk, float* dv, float* dg, float* dbeta, float* dh0,
-                           void* workspace, hipStream_t stream);
+// The chunked backward (backward_chunk.hip): per chunk slot (T / 64 + n_seqs
+// of them) and value head a 64 x 64 matrix (T and P), the state before and the
+// state gradient after the chunk, and U, E, dR.
+size_t chunked_backward_workspace_bytes(int n_seqs, int T_total, int Hv);
+hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t* k, int64_t ks,
+                                   const uint16_t* v, int64_t vs, const float* g, const float* beta,
+                                   const float* h0, const float* d_o, const float* dhT,
+                                   const int32_t* cu, int n_seqs, int T_total, int Hk, int Hv,
+                                   float scale, float* dq, float* dk, float* dv, float* dg,
+                                   float* dbeta, float* dh0, void* workspace, hipStream_t stream);
 
 // Dense MFMA loop (calib.hip): n_blocks work-groups of 4 waves, each wave
 // n_iter rounds of 8 independent 16x16x32 fp16 products; one float per wave

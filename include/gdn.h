@@ -448,15 +448,16 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  *     L = sum(grad_o * o) + sum(grad_final_state * S_T)
  * (o and S_T as gdn_chunk_fwd computes them from the same inputs) with
  * respect to q, k, v, g, beta and the initial states.  The chain rule is
- * taken through each token's erase-then-write update (the deep-dive page's
- * paragraph on the Gated Delta Rule), in reverse token order, in fp32:
- * one kernel re-runs the recurrence and records the state before every
- * 4th token of each sequence in the workspace, a second walks the tokens
- * backwards holding dL/dS and rebuilding each token's state from the
- * nearest record, a third sums dq and dk over the value heads of each key
- * head.  Small batches split each head's state rows over up to four
- * work-groups.  The workspace holds about 16 KB of states plus 1-4 KB of
- * partial sums per token and value head.
+ * taken through the chunk-parallel form of the erase-then-write update (the
+ * deep-dive page's paragraph on the Gated Delta Rule), chunks of 64 tokens,
+ * in fp32 throughout (fp32 matrix-core products: the gradients keep their
+ * relative accuracy whatever the scale of grad_o): a per-chunk pass forms
+ * (I + A)^-1 and the masked Q K^T of every (chunk, value head), a forward
+ * chain records each chunk's initial state and its U, E, a reverse chain
+ * carries dL/dS through the chunks and records it, and a per-(chunk, key
+ * head) pass forms dq, dk (summed over the key head's value heads), dg and
+ * dbeta.  The workspace holds per chunk slot (T_total / 64 + n_seqs) and value
+ * head about 240 KB: roughly 190 KB per token at 48 value heads.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, n_seqs, T_total, sizes
  *                     as gdn_chunk_fwd (initial_state NULL = zeros)

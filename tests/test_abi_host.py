@@ -270,17 +270,24 @@ def backward(lib, **kw):
                             a["db"], a["dh0"], a["ws"], a["wsb"], a["stream"])
 
 
+def chunked_backward_bytes(n_seqs, T, Hv):
+    """gdn_backward's workspace: per chunk slot (T // 64 + n_seqs of them) a
+    slot -> sequence entry, and per (slot, value head) the 64 x 64 matrix of
+    T and P, the state before and the state gradient after the chunk
+    (128 x 128 each) and U, E, dR (64 x 128 each), fp32, every array
+    256-byte aligned."""
+    up = lambda b: (b + 255) // 256 * 256
+    slots = T // 64 + n_seqs
+    sh = slots * Hv
+    return up(4 * slots) + up(sh * 64 * 64 * 4) + 2 * up(sh * 128 * 128 * 4) + 3 * up(sh * 64 * 128 * 4)
+
+
 def test_backward_validation(lib):
     need = lib.gdn_backward_workspace_bytes(1, 64, 48)
-    # checkpoints + per-(token, head, row group) parts of dq, dk, dg, dbeta; 48 (sequence,
-    # head) pairs get 4 row groups each
-    assert need == (64 // 4 + 1) * 48 * 128 * 128 * 4 + 2 * 64 * 48 * 4 * 129 * 4
+    assert need == chunked_backward_bytes(1, 64, 48) == 23593216
     assert lib.gdn_backward_workspace_bytes(1, 0, 48) == 0
-    # row groups per (sequence, head): 4 up to 128 pairs, 2 up to 3072, then 1
-    for n_seqs, R in ((2, 4), (3, 2), (64, 2), (65, 1)):
-        T = 40 * n_seqs
-        ck = (T // 4 + n_seqs) * 48 * 128 * 128 * 4
-        assert lib.gdn_backward_workspace_bytes(n_seqs, T, 48) == ck + 2 * T * 48 * R * 129 * 4, n_seqs
+    for n_seqs, T in ((2, 80), (3, 1), (64, 2560), (65, 8192), (8, 8192)):
+        assert lib.gdn_backward_workspace_bytes(n_seqs, T, 48) == chunked_backward_bytes(n_seqs, T, 48), n_seqs
     assert backward(lib, do=None) == NULL
     assert backward(lib, dg=None) == NULL
     assert backward(lib, Hv=40) == SHAPE
@@ -342,21 +349,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         ops.lib()
 
 
-def test_backward_checkpoint_slots_fit_the_workspace():
-    """The arithmetic claim behind gdn_backward's checkpoint record: keeping
-    the state before tokens s0, s0 + 4, ... of each sequence (starting at s0)
-    in slot t // 4 + n gives distinct slots below T // 4 + N, the count the
-    workspace holds, over random packings with empty and one-token sequences.
-    (This checks the scheme; the GPU tests run the kernel's own indexing on
-    such packings.)"""
+def test_backward_chunk_slots_fit_the_workspace():
+    """The arithmetic claim behind gdn_backward's per-chunk records: chunk c
+    of sequence n (tokens s0 + 64 c ..) goes to slot (s0 + 64 c) // 64 + n,
+    which gives distinct slots below T // 64 + N, the count the workspace
+    holds, over random packings with empty, one-token and chunk-multiple
+    sequences.  (This checks the scheme; the GPU tests run the kernels' own
+    indexing on such packings.)"""
     import numpy as np
     r = np.random.default_rng(31)
-    for _ in range(200):
-        lens = r.integers(0, 30, size=int(r.integers(1, 12)))
+    for _ in range(300):
+        lens = r.integers(0, 300, size=int(r.integers(1, 12)))
         if r.integers(0, 3) == 0:
             lens[r.integers(0, len(lens))] = 1
+        if r.integers(0, 3) == 0:
+            lens[r.integers(0, len(lens))] = 64 * int(r.integers(1, 4))
         cu = np.concatenate([[0], np.cumsum(lens)])
         T, N = int(cu[-1]), len(lens)
-        slots = [t // 4 + n for n in range(N) for t in range(int(cu[n]), int(cu[n + 1]), 4)]
+        slots = [(int(cu[n]) + 64 * c) // 64 + n for n in range(N)
+                 for c in range((int(lens[n]) + 63) // 64)]
         assert len(set(slots)) == len(slots)
-        assert all(0 <= s < T // 4 + N for s in slots)
+        assert all(0 <= s < T // 64 + N for s in slots)

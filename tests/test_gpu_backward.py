@@ -84,33 +84,56 @@ def test_backward_random_shapes(case):
     _check(got, ref, f"random {case}")
 
 
-def row_groups_of(n_seqs, T, Hv=48):
-    """Row groups per (sequence, head) of a gdn_backward call, read back from
-    its workspace size: checkpoints (T // 4 + N slots of a 128 x 128 state per
-    head) plus two fp32 partial-sum arrays of 129 floats per (token, head,
-    row group)."""
-    need = ops.gdn_backward_workspace_bytes(n_seqs, T, Hv)
-    ck = (T // 4 + n_seqs) * Hv * 128 * 128 * 4
-    R, rem = divmod(need - ck, 2 * T * Hv * 129 * 4)
-    assert rem == 0, (need, ck)
-    return R
+@pytest.mark.parametrize("lens", [[63, 64, 65], [128, 1, 129, 0, 200, 64], [300]],
+                         ids=["around-64", "mixed", "one-300"])
+def test_backward_chunk_edges(lens):
+    """Lengths on either side of the 64-token chunk (63, 64, 65, 128, 129),
+    one-token and empty sequences, several chunks per chain: the chunk slots,
+    the partial last chunk and the chains across chunk boundaries."""
+    log(f"backward chunk edges: lengths {lens}, Hk 2, Hv 6")
+    ci = synth.chunk_inputs(7700 + len(lens), sum(lens), Hk=2, Hv=6, lengths=lens, h0_std=0.05)
+    bs = synth.backward_seeds(7800 + len(lens), sum(lens), len(lens), Hv=6)
+    got, ref = _run(ci, bs, 128 ** -0.5, 2)
+    _check(got, ref, f"lengths {lens}")
 
 
-@pytest.mark.parametrize("n_seqs,R", [(2, 4), (12, 2), (65, 1)])
-def test_backward_row_group_layouts(n_seqs, R):
-    """Each (sequence, value head) is split over 4, 2 or 1 work-groups of rows
-    depending on how many pairs the batch has (at most 128, 129-3072, more):
-    96, 576 and 3120 pairs at 48 heads take the three layouts (checked through
-    the workspace size), each against the oracle."""
+def test_backward_long_chain():
+    """One sequence of 1,000 tokens (16 chunks, the last partial): the state
+    and gradient chains over many chunks."""
+    log("backward: one sequence of 1000 tokens, Hk 1, Hv 2")
+    ci = synth.chunk_inputs(7900, 1000, Hk=1, Hv=2, h0_std=0.05)
+    bs = synth.backward_seeds(7901, 1000, 1, Hv=2)
+    got, ref = _run(ci, bs, 128 ** -0.5, 1)
+    _check(got, ref, "1000 tokens")
+
+
+@pytest.mark.parametrize("n_seqs", [2, 12, 65])
+def test_backward_many_short_sequences(n_seqs):
+    """2, 12 and 65 sequences of 1-11 tokens at 48 value heads (one chunk
+    each, most of it padding), against the oracle."""
     r = np.random.default_rng(9300 + n_seqs)
     lens = [int(x) for x in r.integers(1, 12, size=n_seqs)]
     T = sum(lens)
-    assert row_groups_of(n_seqs, T) == R
-    log(f"backward row groups: {n_seqs} sequences x 48 heads ({R} per pair), lengths {lens}")
+    log(f"backward: {n_seqs} sequences x 48 heads, lengths {lens}")
     ci = synth.chunk_inputs(9400 + n_seqs, T, lengths=lens, h0_std=0.02)
     bs = synth.backward_seeds(9500 + n_seqs, T, n_seqs)
     got, ref = _run(ci, bs, 128 ** -0.5, 16)
     _check(got, ref, f"{n_seqs} sequences")
+
+
+@pytest.mark.parametrize("e", [-40, 30])
+def test_backward_gradient_scale(e):
+    """dO and dS_T scaled by 2^e (e = -40, 30): every gradient is linear in
+    them, and the fp32 products keep their relative accuracy over that range,
+    so the results still meet the bar against the oracle on the scaled seeds."""
+    lens = [100, 37]
+    log(f"backward: upstream gradients scaled by 2^{e}")
+    ci = synth.chunk_inputs(7950, sum(lens), Hk=2, Hv=4, lengths=lens, h0_std=0.05)
+    bs = synth.backward_seeds(7951, sum(lens), len(lens), Hv=4)
+    f = np.float32(2.0 ** e)
+    bs = synth.BackwardSeeds(bs.d_o * f, bs.dhT * f)
+    got, ref = _run(ci, bs, 128 ** -0.5, 2)
+    _check(got, ref, f"2^{e}")
 
 
 def test_backward_full_head_layout():
