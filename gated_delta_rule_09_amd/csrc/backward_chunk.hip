@@ -25,9 +25,11 @@
 // Five launches:
 //   cb_fill/cb_table   chunk slots -> sequence (slot = first token / 64 + sequence)
 //   cb_prep            per (chunk, key head): Q K^T, K K^T (fp32 MFMA), then per
-//                      value head T (forward substitution, one column per lane)
-//                      and P, packed in one 64 x 64 matrix X: T below the
-//                      diagonal, P_ii on it, P_ji above it (T_ii = 1)
+//                      value head one 64 x 64 matrix X: A below the four
+//                      diagonal 16 x 16 blocks, inside them the blocks of
+//                      T_II = (I + A_II)^-1 (forward substitution, one column
+//                      per lane; unit diagonal), P_ii on the diagonal and
+//                      P_ji above it.  The chains solve with (I + A) blockwise.
 //   cb_fwd             per (sequence, value head, 64 channels): the state chain
 //                      forwards, recording S0, U, E of every chunk
 //   cb_bwd             per (sequence, value head, 64 channels): the gradient
@@ -60,7 +62,7 @@ struct CbParams {
   int n_seqs, seq_len, Hk, Hv, group, n_slots;
   float scale;
   int32_t* slot_seq;          // [n_slots]: sequence of the chunk in the slot, -1 for none
-  float* X;                   // [n_slots][Hv][64][64]
+  float* X;                   // [n_slots][Hv][64][64]: A, T_II, P (see cb_prep)
   float* S0;                  // [n_slots][Hv][128][128]: state before the chunk, [dv][dk]
   float* dSC;                 // [n_slots][Hv][128][128]: dL/dS after the chunk
   float* U; float* E; float* dR;   // [n_slots][Hv][64][128]
@@ -116,9 +118,11 @@ struct Gates { float G, gam, dec, bet; };
 __device__ __forceinline__ Gates chunk_gates(const CbParams& p, int t0, int len, int h) {
   const int i = threadIdx.x & 63;
   const bool ok = i < len;
-  const float gi = ok ? p.g[static_cast<int64_t>(t0 + i) * p.Hv + h] : 0.f;
+  const int64_t gi_at = static_cast<int64_t>(t0 + min(i, len - 1)) * p.Hv + h;
+  const float gv = p.g[gi_at], bv = p.beta[gi_at];   // unconditional loads: no branch, no wait
+  const float gi = ok ? gv : 0.f;
   Gates r;
-  r.bet = ok ? p.beta[static_cast<int64_t>(t0 + i) * p.Hv + h] : 0.f;
+  r.bet = ok ? bv : 0.f;
   r.G = wave_prefix_sum(gi);
   const float GL = __shfl(r.G, 63, 64);
   r.gam = expf(r.G);
@@ -137,10 +141,11 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t stride, 
   const int row = tid / (kD / kPer);
   const int c0 = (tid % (kD / kPer)) * kPer;
   const bool ok = row < len;
-  const uint4* s = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + row) * stride + kh * kD + c0);
+  const uint4* s = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + min(row, len - 1)) * stride + kh * kD + c0);
 #pragma unroll
   for (int j = 0; j < kPer / 8; ++j) {
-    const uint4 x = ok ? s[j] : make_uint4(0, 0, 0, 0);
+    const uint4 y = s[j];
+    const uint4 x = ok ? y : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(&dst[row][c0 + 8 * j]) = x;
   }
 }
@@ -206,36 +211,51 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbParams p) {
   __syncthreads();
 
   for (int hv = w; hv < p.group; hv += 4) {
+    // the lane index from an opaque copy: its 64 per-row comparisons below
+    // are then made row by row instead of hoisted out of this loop
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int lane = lane_v;
     const int h = kh * p.group + hv;
     const Gates gt = chunk_gates(p, sc.t0, sc.len, h);
-    // T = (I + A)^-1 by forward substitution, lane = column c:
-    //   T_ic = delta_ic - sum_{j<i} A_ij T_jc,   A_ij = b_i M_ij k_i.k_j (j < i);
-    // lane j computes A_ij, read by every lane from there
-    float t[kC];
+    // The diagonal 16 x 16 blocks of T = (I + A)^-1, T_II = (I + A_II)^-1, by
+    // forward substitution: lane 16 I + c holds column c of T_II (t[ii] = row
+    // ii), A_ij = b_i M_ij k_i.k_j (j < i) comes from the lane of column j in
+    // the same 16-lane group:  T_ic = delta_ic - sum_{j<i} A_ij T_jc.
+    const int blk = lane >> 4;
+    const int c = lane & 15;
+    float t[16];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      const float Gi = lane_value(gt.G, i);
-      const float bi = lane_value(gt.bet, i);
-      const float a = lane < i ? bi * expf(Gi - gt.G) * sm.kkt[i][lane] : 0.f;
-      float acc = lane == i ? 1.f : 0.f;
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = 16 * blk + ii;
+      const float Gi = __shfl(gt.G, i, 64);
+      const float bi = __shfl(gt.bet, i, 64);
+      const float a = c < ii ? bi * expf(Gi - gt.G) * sm.kkt[i][lane] : 0.f;
+      float acc = c == ii ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) acc = fmaf(-lane_value(a, j), t[j], acc);
-      t[i] = acc;
+      for (int jj = 0; jj < ii; ++jj) acc = fmaf(-__shfl(a, 16 * blk + jj, 64), t[jj], acc);
+      t[ii] = acc;
     }
-    // X row i: T_ij (j < i), P_ii, P_ji = M_ji q_j.k_i (j > i); lane = column j
+    // X row i, lane = column j: A_ij below the diagonal blocks, T_II inside
+    // them (below the diagonal), P_ii on the diagonal, P_ji = M_ji q_j.k_i above
     float* Xh = p.X + (static_cast<int64_t>(slot) * p.Hv + h) * (kC * kC);
 #pragma unroll
     for (int i = 0; i < kC; ++i) {
       const float Gi = lane_value(gt.G, i);
-      Xh[i * kC + lane] = lane < i ? t[i] : expf(gt.G - Gi) * sm.qkt[lane][i];
+      const float bi = lane_value(gt.bet, i);
+      const float e = expf(lane < i ? Gi - gt.G : gt.G - Gi);
+      Xh[i * kC + lane] = lane < (i & ~15) ? bi * e * sm.kkt[i][lane]
+                        : lane < i          ? t[i & 15]
+                                            : e * sm.qkt[lane][i];
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// cb_fwd: one work-group (4 waves) per (sequence, value head, 64 channels);
-// wave w carries channels 16 (4 half + w) .. + 15 of S^T in 8 accumulators
-// (s[db][r] = S^T[16 db + 4 (lane / 16) + r][channel 16 tile + lane % 16]).
+// The chains' per-chunk inputs in LDS, and their prefetch: the next chunk's
+// K (and Q) rows, its X and its gates are loaded into registers while the
+// current chunk computes, and written to LDS after it.
 struct ChainLds {
   uint16_t k[kC][kKS];
   uint16_t q[kC][kKS];
@@ -243,20 +263,75 @@ struct ChainLds {
   float gam[kC], dec[kC], bet[kC];
 };
 
-template <int kThr>
-__device__ __forceinline__ void stage_x(const float* Xh, float (*dst)[kXS]) {
-  constexpr int kPer = kC * kC / kThr;       // floats per thread: 16
+template <bool kWithQ>
+struct ChainNext {
+  uint4 k[4];
+  uint4 q[kWithQ ? 4 : 1];
+  floatx4 x[4];
+  float g, b;                 // lane i: token i's g and beta (0 past the end)
+};
+
+template <bool kWithQ>
+__device__ __forceinline__ void chain_load(const CbParams& p, int t0, int len, int h, int kh,
+                                           int64_t sh, ChainNext<kWithQ>& f) {
   const int tid = threadIdx.x;
-  const int row = tid / (kC / kPer);
-  const int c0 = (tid % (kC / kPer)) * kPer;
+  const int lane = tid & 63;
+  const int row = tid >> 2;                   // K / Q: 32 halves, X: 16 floats per thread
+  const bool ok = row < len;
+  const int64_t t = t0 + min(row, len - 1);   // rows past the end load the last, then zero
+  const uint4* sk = reinterpret_cast<const uint4*>(p.k + t * p.ks + kh * kD + (tid & 3) * 32);
 #pragma unroll
-  for (int j = 0; j < kPer / 4; ++j)
-    *reinterpret_cast<floatx4*>(&dst[row][c0 + 4 * j]) = *reinterpret_cast<const floatx4*>(Xh + row * kC + c0 + 4 * j);
+  for (int j = 0; j < 4; ++j) f.k[j] = sk[j];
+  if (kWithQ) {
+    const uint4* sq = reinterpret_cast<const uint4*>(p.q + t * p.qs + kh * kD + (tid & 3) * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.q[j] = sq[j];
+  }
+  if (!ok) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.k[j] = make_uint4(0, 0, 0, 0);
+      if (kWithQ) f.q[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  const float* sx = p.X + sh * (kC * kC) + row * kC + (tid & 3) * 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.x[j] = *reinterpret_cast<const floatx4*>(sx + 4 * j);
+  const bool gok = lane < len;
+  const int64_t gi_at = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
+  f.g = p.g[gi_at];
+  f.b = p.beta[gi_at];
+  if (!gok) f.g = f.b = 0.f;
 }
+
+template <bool kWithQ>
+__device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& sm) {
+  const int tid = threadIdx.x;
+  const int row = tid >> 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint4*>(&sm.k[row][(tid & 3) * 32 + 8 * j]) = f.k[j];
+    if (kWithQ) *reinterpret_cast<uint4*>(&sm.q[row][(tid & 3) * 32 + 8 * j]) = f.q[j];
+    *reinterpret_cast<floatx4*>(&sm.x[row][(tid & 3) * 16 + 4 * j]) = f.x[j];
+  }
+  if ((tid >> 6) == 0) {
+    const int lane = tid & 63;
+    const float G = wave_prefix_sum(f.g);
+    const float GL = __shfl(G, 63, 64);
+    sm.gam[lane] = expf(G);
+    sm.dec[lane] = expf(GL - G);
+    sm.bet[lane] = f.b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cb_fwd: one work-group (4 waves) per (sequence, value head, 64 channels);
+// wave w carries channels 16 (4 half + w) .. + 15 of S^T in 8 accumulators
+// (s[db][r] = S^T[16 db + 4 (lane / 16) + r][channel 16 tile + lane % 16]).
 
 __device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
 
-__global__ __launch_bounds__(256) void cb_fwd_kernel(CbParams p) {
+__global__ __launch_bounds__(256, 2) void cb_fwd_kernel(CbParams p) {
   __shared__ __align__(16) ChainLds sm;
   const int unit = blockIdx.x >> 1;
   const int half = blockIdx.x & 1;
@@ -279,18 +354,29 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbParams p) {
   for (int db = 0; db < 8; ++db)
     s[db] = p.h0 ? *reinterpret_cast<const floatx4*>(p.h0 + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
 
+  ChainNext<false> nx;
+  if (nc > 0) {
+    chain_load(p, s0, min(kC, s1 - s0), h, kh, static_cast<int64_t>(cb_slot(s0, 0, n)) * p.Hv + h, nx);
+    chain_put(nx, sm);
+  }
+  __syncthreads();
   for (int c = 0; c < nc; ++c) {
     const int t0 = s0 + kC * c;
     const int len = min(kC, s1 - t0);
     const int slot = cb_slot(s0, c, n);
     const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
-    stage_rows<256>(p.k, p.ks, t0, len, kh, sm.k);
-    stage_x<256>(p.X + sh * (kC * kC), sm.x);
-    if (w == 0) {
-      const Gates gt = chunk_gates(p, t0, len, h);
-      sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
-    }
-    __syncthreads();
+    // this chunk's V (used after Z), then the next chunk's inputs
+    float vv[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tb * 16 + 4 * g4 + r;
+        const float x = bf(p.v[static_cast<int64_t>(t0 + min(tok, len - 1)) * p.vs + h * kD + ch]);
+        vv[tb][r] = tok < len ? x : 0.f;
+      }
+    if (c + 1 < nc)
+      chain_load(p, t0 + kC, min(kC, s1 - t0 - kC), h, kh, static_cast<int64_t>(slot + 1) * p.Hv + h, nx);
 
     // the state before the chunk
     float* S0 = p.S0 + (sh * kD + ch) * kD + 4 * g4;
@@ -319,28 +405,29 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tb * 16 + 4 * g4 + r;
-        const float vv = tok < len ? bf(p.v[static_cast<int64_t>(t0 + tok) * p.vs + h * kD + ch]) : 0.f;
-        const float e = vv - sm.gam[tok] * z[tb][r];
+        const float e = vv[tb][r] - sm.gam[tok] * z[tb][r];
         Eh[tok * kD] = e;
         R[tb][r] = sm.bet[tok] * e;
       }
-    // U = T R
+    // U = (I + A)^-1 R blockwise: U_I = T_II (R_I - sum_{J<I} A_IJ U_J)
     float* Uh = p.U + sh * (kC * kD) + ch;
-    floatx4 DU[4];
+    floatx4 U[4], DU[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       const int i = ib * 16 + m;
+      floatx4 y = R[ib];
+#pragma unroll
+      for (int jb = 0; jb < ib; ++jb) {
+        const floatx4 xr = *reinterpret_cast<const floatx4*>(&sm.x[i][jb * 16 + 4 * g4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y = mfma4(-xr[r], U[jb][r], y);
+      }
+      const int j0 = ib * 16 + 4 * g4;
+      const floatx4 xr = *reinterpret_cast<const floatx4*>(&sm.x[i][j0]);
       floatx4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jb = 0; jb <= ib; ++jb) {
-        const int j0 = jb * 16 + 4 * g4;
-        const floatx4 xr = *reinterpret_cast<const floatx4*>(&sm.x[i][j0]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = j0 + r < i ? xr[r] : j0 + r == i ? 1.f : 0.f;
-          u = mfma4(a, R[jb][r], u);
-        }
-      }
+      for (int r = 0; r < 4; ++r) u = mfma4(j0 + r < i ? xr[r] : j0 + r == i ? 1.f : 0.f, y[r], u);
+      U[ib] = u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = ib * 16 + 4 * g4 + r;
@@ -360,14 +447,18 @@ __global__ __launch_bounds__(256) void cb_fwd_kernel(CbParams p) {
           acc = mfma4(bf(sm.k[jb * 16 + 4 * g4 + r][db * 16 + m]), DU[jb][r], acc);
       s[db] = acc;
     }
-    __syncthreads();   // before the next chunk's staging
+    __syncthreads();   // every wave is done with this chunk's LDS
+    if (c + 1 < nc) {
+      chain_put(nx, sm);
+      __syncthreads();
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // cb_bwd: the gradient chain, chunks in reverse; wave layout as cb_fwd, with
 // ds[db][r] = dS^T[16 db + 4 (lane / 16) + r][channel].
-__global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
+__global__ __launch_bounds__(256, 2) void cb_bwd_kernel(CbParams p) {
   __shared__ __align__(16) ChainLds sm;
   const int unit = blockIdx.x >> 1;
   const int half = blockIdx.x & 1;
@@ -390,18 +481,18 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
   for (int db = 0; db < 8; ++db)
     ds[db] = p.dhT ? *reinterpret_cast<const floatx4*>(p.dhT + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
 
+  ChainNext<true> nx;
+  if (nc > 0) {
+    const int tl = s0 + kC * (nc - 1);
+    chain_load(p, tl, s1 - tl, h, kh, static_cast<int64_t>(cb_slot(s0, nc - 1, n)) * p.Hv + h, nx);
+    chain_put(nx, sm);
+  }
+  __syncthreads();
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = s0 + kC * c;
     const int len = min(kC, s1 - t0);
     const int slot = cb_slot(s0, c, n);
     const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
-    stage_rows<256>(p.k, p.ks, t0, len, kh, sm.k);
-    stage_rows<256>(p.q, p.qs, t0, len, kh, sm.q);
-    stage_x<256>(p.X + sh * (kC * kC), sm.x);
-    if (w == 0) {
-      const Gates gt = chunk_gates(p, t0, len, h);
-      sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
-    }
     // dO of the chunk in the accumulator layout (token tb*16 + 4 g4 + r)
     floatx4 dO[4];
 #pragma unroll
@@ -409,9 +500,11 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tb * 16 + 4 * g4 + r;
-        dO[tb][r] = tok < len ? p.d_o[(static_cast<int64_t>(t0 + tok) * p.Hv + h) * kD + ch] : 0.f;
+        const float x = p.d_o[(static_cast<int64_t>(t0 + min(tok, len - 1)) * p.Hv + h) * kD + ch];
+        dO[tb][r] = tok < len ? x : 0.f;
       }
-    __syncthreads();
+    // the previous chunk's inputs, written to LDS after this one
+    if (c > 0) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx);
 
     // the gradient of the state after the chunk
     float* dSC = p.dSC + (sh * kD + ch) * kD + 4 * g4;
@@ -448,20 +541,24 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dU[ib][r] = p.scale * acc[r] + sm.dec[ib * 16 + 4 * g4 + r] * z[ib][r];
     }
-    // dR = T^T dU;  (T^T)_ij = T_ji = X_ji for j > i, 1 on the diagonal
+    // dR = (I + A)^-T dU blockwise, last block first:
+    //   dR_I = T_II^T (dU_I - sum_{J>I} A_JI^T dR_J)
     float* dRh = p.dR + sh * (kC * kD) + ch;
     floatx4 dR[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+    for (int ib = 3; ib >= 0; --ib) {
       const int i = ib * 16 + m;
+      floatx4 y = dU[ib];
+#pragma unroll
+      for (int jb = ib + 1; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y = mfma4(-sm.x[jb * 16 + 4 * g4 + r][i], dR[jb][r], y);
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jb = ib; jb < 4; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jb * 16 + 4 * g4 + r;
-          acc = mfma4(j > i ? sm.x[j][i] : j == i ? 1.f : 0.f, dU[jb][r], acc);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int j = ib * 16 + 4 * g4 + r;
+        acc = mfma4(j > i ? sm.x[j][i] : j == i ? 1.f : 0.f, y[r], acc);
+      }
       dR[ib] = acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -470,15 +567,15 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
         if (tok < len) p.dv[(static_cast<int64_t>(t0 + tok) * p.Hv + h) * kD + ch] = sm.bet[tok] * acc[r];
       }
     }
-    // dS^T <- gamma_last dS^T + Q^T (scale gamma dO) - K^T (b gamma dR)
-    floatx4 bo[4], br[4];
+    // dS^T <- gamma_last dS^T + Q^T (scale gamma dO) - K^T (b gamma dR):
+    // dO and dR scaled in place (not needed again)
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = jb * 16 + 4 * g4 + r;
-        bo[jb][r] = p.scale * sm.gam[tok] * dO[jb][r];
-        br[jb][r] = -sm.bet[tok] * sm.gam[tok] * dR[jb][r];
+        dO[jb][r] *= p.scale * sm.gam[tok];
+        dR[jb][r] *= -sm.bet[tok] * sm.gam[tok];
       }
     const float gl = sm.gam[kC - 1];
 #pragma unroll
@@ -489,12 +586,16 @@ __global__ __launch_bounds__(256) void cb_bwd_kernel(CbParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = jb * 16 + 4 * g4 + r;
-          acc = mfma4(bf(sm.q[tok][db * 16 + m]), bo[jb][r], acc);
-          acc = mfma4(bf(sm.k[tok][db * 16 + m]), br[jb][r], acc);
+          acc = mfma4(bf(sm.q[tok][db * 16 + m]), dO[jb][r], acc);
+          acc = mfma4(bf(sm.k[tok][db * 16 + m]), dR[jb][r], acc);
         }
       ds[db] = acc;
     }
-    __syncthreads();   // before the next chunk's staging
+    __syncthreads();   // every wave is done with this chunk's LDS
+    if (c > 0) {
+      chain_put(nx, sm);
+      __syncthreads();
+    }
   }
   if (p.dh0) {
 #pragma unroll
@@ -573,14 +674,14 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       const int row = tid >> 3;
       const int c0 = (tid & 7) * 16;
       const bool ok = row < sc.len;
-      const float* so = p.d_o + (static_cast<int64_t>(sc.t0 + row) * p.Hv + h) * kD + c0;
+      const float* so = p.d_o + (static_cast<int64_t>(sc.t0 + min(row, sc.len - 1)) * p.Hv + h) * kD + c0;
       const float* su = p.U + (sh * kC + row) * kD + c0;
       const float* sr = p.dR + (sh * kC + row) * kD + c0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // grad_o is only 4-byte aligned
-        const floatx4 xo = ok ? floatx4{so[4 * j], so[4 * j + 1], so[4 * j + 2], so[4 * j + 3]}
-                              : floatx4{0.f, 0.f, 0.f, 0.f};
+        const floatx4 yo = {so[4 * j], so[4 * j + 1], so[4 * j + 2], so[4 * j + 3]};
+        const floatx4 xo = ok ? yo : floatx4{0.f, 0.f, 0.f, 0.f};
         const floatx4 xu = *reinterpret_cast<const floatx4*>(su + 4 * j);
         const floatx4 xr = *reinterpret_cast<const floatx4*>(sr + 4 * j);
 #pragma unroll
@@ -613,11 +714,22 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     const float* S0 = p.S0 + sh * (kD * kD) + d;
     const float* dSC = p.dSC + sh * (kD * kD) + d;
     float dss = 0.f;
-#pragma unroll 1
+    // B operands 8 k-steps ahead (the last ones re-read row 127: never used)
+    constexpr int kAhead = 8;
+    float pb1[kAhead], pb2[kAhead];
+#pragma unroll
+    for (int e = 0; e < kAhead; ++e) {
+      pb1[e] = S0[(4 * e + g4) * kD];
+      pb2[e] = dSC[(4 * e + g4) * kD];
+    }
+#pragma unroll kAhead
     for (int kk = 0; kk < kD / 4; ++kk) {
       const int c = 4 * kk + g4;
-      const float b1 = S0[c * kD];
-      const float b2 = dSC[c * kD];
+      const float b1 = pb1[kk % kAhead];
+      const float b2 = pb2[kk % kAhead];
+      const int cn = min(c + 4 * kAhead, kD - 1);
+      pb1[kk % kAhead] = S0[cn * kD];
+      pb2[kk % kAhead] = dSC[cn * kD];
       dss = fmaf(b1, b2, dss);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
