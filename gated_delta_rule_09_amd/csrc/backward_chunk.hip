@@ -22,7 +22,7 @@
 // - gamma b dR S0 - D U dS_C)_i (+ gamma_last <dS_C, S0> + sum_m k_m . (D U dS_C)_m
 // on the last token), then dg = the suffix sum of dG over the chunk.
 //
-// Five launches:
+// Six launches:
 //   cb_fill/cb_table   chunk slots -> sequence (slot = first token / 64 + sequence)
 //   cb_prep            per (chunk, key head): Q K^T, K K^T (fp32 MFMA), then per
 //                      value head one 64 x 64 matrix X: A below the four
@@ -30,10 +30,11 @@
 //                      T_II = (I + A_II)^-1 (forward substitution, one column
 //                      per lane; unit diagonal), P_ii on the diagonal and
 //                      P_ji above it.  The chains solve with (I + A) blockwise.
-//   cb_fwd             per (sequence, value head, 64 channels): the state chain
-//                      forwards, recording S0, U, E of every chunk
-//   cb_bwd             per (sequence, value head, 64 channels): the gradient
-//                      chain backwards, recording dS_C and dR, writing dv, dh0
+//   cb_fwd, cb_bwd     per (sequence, value head, 64 channels): the state chain
+//                      forwards, recording S0, U, E of every chunk, and beside
+//                      it on the library's second stream the gradient chain
+//                      backwards (it needs none of those), recording dS_C and
+//                      dR, writing dv and dh0
 //   cb_grad            per (chunk, key head): dq, dk (summed over the value
 //                      heads in registers), dg, dbeta
 // All contractions run on v_mfma_f32_16x16x4_f32 with fp32 operands: the
@@ -41,6 +42,8 @@
 // 64-token x 16-channel intermediate stays in the accumulator layout (lane l:
 // rows 4 (l / 16) + r, column l % 16) and enters the next product as its B
 // operand directly; the A operand then takes its k columns in the same order.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -106,9 +109,11 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
   return x;
 }
 
+// sum over the 64 lanes: DPP inside the four rows of 16, then across them
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
+  x = sum16(x);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
   return x;
 }
 
@@ -331,10 +336,9 @@ __device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& 
 
 __device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
 
-__global__ __launch_bounds__(256, 2) void cb_fwd_kernel(CbParams p) {
-  __shared__ __align__(16) ChainLds sm;
-  const int unit = blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
+__device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int block) {
+  const int unit = block >> 1;
+  const int half = block & 1;
   const int n = unit / p.Hv;
   const int h = unit - n * p.Hv;
   const int kh = h / p.group;
@@ -458,10 +462,9 @@ __global__ __launch_bounds__(256, 2) void cb_fwd_kernel(CbParams p) {
 // ---------------------------------------------------------------------------
 // cb_bwd: the gradient chain, chunks in reverse; wave layout as cb_fwd, with
 // ds[db][r] = dS^T[16 db + 4 (lane / 16) + r][channel].
-__global__ __launch_bounds__(256, 2) void cb_bwd_kernel(CbParams p) {
-  __shared__ __align__(16) ChainLds sm;
-  const int unit = blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
+__device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int block) {
+  const int unit = block >> 1;
+  const int half = block & 1;
   const int n = unit / p.Hv;
   const int h = unit - n * p.Hv;
   const int kh = h / p.group;
@@ -601,6 +604,16 @@ __global__ __launch_bounds__(256, 2) void cb_bwd_kernel(CbParams p) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(p.dh0 + hrow + 16 * db) = ds[db];
   }
+}
+
+__global__ __launch_bounds__(256, 2) void cb_fwd_kernel(CbParams p) {
+  __shared__ __align__(16) ChainLds sm;
+  fwd_chain(p, sm, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256, 2) void cb_bwd_kernel(CbParams p) {
+  __shared__ __align__(16) ChainLds sm;
+  bwd_chain(p, sm, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -752,14 +765,20 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       }
       dk_tot[tb] += dks[tb];
     }
-    // dbeta's first part: dR_i . E_i, rows 8 w .. 8 w + 7
+    // dbeta's first part: dR_i . E_i, rows 8 w .. 8 w + 7 (the E rows loaded
+    // first, then the sums)
     {
-      const float* Eh = p.E + sh * (kC * kD);
+      const float* Eh = p.E + (sh * kC + 8 * w) * kD + lane;
+      float e0[8], e1[8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        e0[rr] = Eh[rr * kD];
+        e1[rr] = Eh[rr * kD + 64];
+      }
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int i = 8 * w + rr;
-        float x = sm.u.in.dR[i][lane] * Eh[i * kD + lane] + sm.u.in.dR[i][lane + 64] * Eh[i * kD + lane + 64];
-        x = wave_sum(x);
+        const float x = wave_sum(sm.u.in.dR[i][lane] * e0[rr] + sm.u.in.dR[i][lane + 64] * e1[rr]);
         if (lane == 0) sm.dbe[i] = x;
       }
     }
@@ -923,8 +942,24 @@ hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t
     hipLaunchKernelGGL(cb_table_kernel, dim3((n_seqs + 255) / 256), dim3(256), 0, stream, p);
     const unsigned per_chunk = static_cast<unsigned>(n_slots) * static_cast<unsigned>(Hk);
     hipLaunchKernelGGL(cb_prep_kernel, dim3(per_chunk), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+    // the gradient chain needs none of the state chain's records: it runs on
+    // the library's second stream beside it; the gradient pass waits for both
+    Overlap* ov = overlap_of_current_device();
+    if (ov) {
+      std::lock_guard<std::mutex> lock(ov->mu);
+      hipError_t e = hipEventRecord(ov->start, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ov->side, ov->start, 0);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, ov->side, p);
+      hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+      e = hipGetLastError();
+      if (e == hipSuccess) e = hipEventRecord(ov->done[0], ov->side);
+      if (e == hipSuccess) e = hipStreamWaitEvent(stream, ov->done[0], 0);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+    }
     hipLaunchKernelGGL(cb_grad_kernel, dim3(per_chunk), dim3(512), 0, stream, p);
   } else if (dh0) {
     hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, stream, p);

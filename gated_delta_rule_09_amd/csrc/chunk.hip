@@ -1155,15 +1155,21 @@ hipError_t launch_prep(const PrepParams& pp, dim3 grid, bool conv, hipStream_t s
   return hipGetLastError();
 }
 
-// The second stream and the events of the overlapped prefill, one set per
-// device, made on first use (with that device current) and kept until the
-// process ends.  The lock keeps one call's records and waits together.
-struct Overlap {
-  std::mutex mu;
-  hipStream_t side = nullptr;
-  hipEvent_t start = nullptr;
-  hipEvent_t done[2] = {};
-};
+// Compute units of the current device, looked up once per device (calls from
+// several host threads may race to fill an entry; they store the same value).
+int compute_units() {
+  static std::atomic<int> cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace
 
 Overlap* overlap_of_current_device() {
   static Overlap ov[64];
@@ -1181,22 +1187,6 @@ Overlap* overlap_of_current_device() {
   });
   return ok[dev] ? &ov[dev] : nullptr;
 }
-
-// Compute units of the current device, looked up once per device (calls from
-// several host threads may race to fill an entry; they store the same value).
-int compute_units() {
-  static std::atomic<int> cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-}  // namespace
 
 ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, bool conv_v) {
   auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace gdn {
 
 hipError_t launch_decode_step(const uint16_t* q, int64_t q_stride, const uint16_t* k,
@@ -28,6 +30,19 @@ hipError_t launch_conv1d(const uint16_t* x, int64_t xs, const uint16_t* w, const
 hipError_t launch_gated_rmsnorm(const float* o, const uint16_t* z, int64_t zs, const float* w,
                                 void* out, bool out_bf16, int64_t rows, int Hv, float eps,
                                 hipStream_t stream);
+
+// The library's second stream and its events, one set per device, made on
+// first use (with that device current) and kept until the process ends; the
+// overlapped prefill and the backward run work on it beside the caller's
+// stream.  The lock keeps one call's records and waits together.  nullptr if
+// they could not be made.
+struct Overlap {
+  std::mutex mu;
+  hipStream_t side = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t done[2] = {};
+};
+Overlap* overlap_of_current_device();
 
 // Workspace of the chunked prefill (each piece 256-byte aligned):
 //   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]

@@ -164,13 +164,14 @@ def test_empty_batch_is_a_no_op():
     assert out.shape[0] == 0 and torch.equal(pool, pool0) and torch.equal(cs3, cs30)
 
 
-@pytest.mark.parametrize("case", ["varlen", "segmented", "decode"])
+@pytest.mark.parametrize("case", ["varlen", "segmented", "decode", "backward"])
 def test_graph_replay_matches_eager(case):
     """A captured HIP graph of the call (after one eager warm-up), replayed
     three times with eager work and synchronisations between the replays,
     gives the eager call's bits every time.  `segmented` is a B = 1 prefill
     of 32,868 tokens: the overlapped launch, whose second stream joins the
-    capture through its events."""
+    capture through its events; `backward` runs its gradient chain on that
+    stream too (outputs zeroed before each replay)."""
     log(f"graph capture and replay: {case}")
     if case == "varlen":
         lens = [300, 1, 0, 129, 64]
@@ -179,9 +180,29 @@ def test_graph_replay_matches_eager(case):
     elif case == "segmented":
         ci = synth.chunk_inputs_torch(4101, 2 * 16384 + 100, h0_std=0.05)
         n = 1
+    elif case == "backward":
+        lens = [200, 1, 0, 129]
+        ci = synth.chunk_inputs_torch(4103, sum(lens), lengths=lens, h0_std=0.05)
+        bs = synth.backward_seeds_torch(4104, sum(lens), len(lens))
     else:
         di = synth.decode_inputs_torch(4102, 8)
-    if case == "decode":
+    if case == "backward":
+        n, T = len(lens), sum(lens)
+        ws = torch.empty(ops.gdn_backward_workspace_bytes(n, T, 48), dtype=torch.uint8, device="cuda")
+        res = {}
+
+        def call():
+            res["r"] = ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], bs["d_o"],
+                                        initial_state=ci["h0"], grad_final_state=bs["dhT"],
+                                        cu_seqlens=ci["cu_seqlens"], workspace=ws)
+
+        def reset():
+            for v in res.get("r", {}).values():
+                if v is not None:
+                    v.zero_()
+
+        outs = lambda: tuple(res["r"][k].clone() for k in ("dq", "dk", "dv", "dg", "dbeta", "dh0"))
+    elif case == "decode":
         state0 = di["state"].clone()
         o = torch.empty((8, 48, 128), dtype=torch.float32, device="cuda")
         st = state0.clone()
