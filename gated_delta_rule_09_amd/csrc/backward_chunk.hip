@@ -76,6 +76,25 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+// rows[r0 + e][c0 + lane % 16], e = 0..3, of staged bf16 rows: the A operand
+// of a product over tokens with K^T or Q^T, k columns r0 .. r0 + 3 (r0 may
+// differ between the four 16-lane groups).  gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): lane j of a 16-lane group points at row r0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3, and lane i receives column c0 + i of the
+// four rows.
+__device__ __forceinline__ floatx4 col4(const uint16_t (*rows)[kKS], int r0, int c0) {
+  const int j = threadIdx.x & 15;
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(&rows[r0 + (j >> 2)][c0 + 4 * (j & 3)]));
+  return floatx4{bf(static_cast<uint16_t>(v[0])), bf(static_cast<uint16_t>(v[1])),
+                 bf(static_cast<uint16_t>(v[2])), bf(static_cast<uint16_t>(v[3]))};
+}
+
 __device__ __forceinline__ void cb_seq(const CbParams& p, int n, int& s0, int& s1) {
   if (p.cu) { s0 = p.cu[n]; s1 = p.cu[n + 1]; }
   else { s0 = n * p.seq_len; s1 = s0 + p.seq_len; }
@@ -206,9 +225,16 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbParams p) {
     const int jb = b - ib * (ib + 1) / 2;
     const uint16_t (*A)[kKS] = kind ? sm.k : sm.q;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int kk = 0; kk < kD / 4; ++kk)
-      acc = mfma4(bf16_to_f32(A[ib * 16 + m][4 * kk + g4]), bf16_to_f32(sm.k[jb * 16 + m][4 * kk + g4]), acc);
+    // reduction index 16 kb + 4 (lane / 16) + r: four steps per 8-byte read of each row
+#pragma unroll 4
+    for (int kb = 0; kb < kD / 16; ++kb) {
+      const uint2 xa = *reinterpret_cast<const uint2*>(&A[ib * 16 + m][16 * kb + 4 * g4]);
+      const uint2 xb = *reinterpret_cast<const uint2*>(&sm.k[jb * 16 + m][16 * kb + 4 * g4]);
+      acc = mfma4(bf(xa.x & 0xffff), bf(xb.x & 0xffff), acc);
+      acc = mfma4(bf(xa.x >> 16), bf(xb.x >> 16), acc);
+      acc = mfma4(bf(xa.y & 0xffff), bf(xb.y & 0xffff), acc);
+      acc = mfma4(bf(xa.y >> 16), bf(xb.y >> 16), acc);
+    }
     float (*dst)[kSS] = kind ? sm.kkt : sm.qkt;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
@@ -334,7 +360,6 @@ __device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& 
 // wave w carries channels 16 (4 half + w) .. + 15 of S^T in 8 accumulators
 // (s[db][r] = S^T[16 db + 4 (lane / 16) + r][channel 16 tile + lane % 16]).
 
-__device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
 
 __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int block) {
   const int unit = block >> 1;
@@ -445,10 +470,11 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
     for (int db = 0; db < 8; ++db) {
       floatx4 acc = s[db] * gl;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+      for (int jb = 0; jb < 4; ++jb) {
+        const floatx4 kt = col4(sm.k, jb * 16 + 4 * g4, db * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc = mfma4(bf(sm.k[jb * 16 + 4 * g4 + r][db * 16 + m]), DU[jb][r], acc);
+        for (int r = 0; r < 4; ++r) acc = mfma4(kt[r], DU[jb][r], acc);
+      }
       s[db] = acc;
     }
     __syncthreads();   // every wave is done with this chunk's LDS
@@ -585,13 +611,15 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
     for (int db = 0; db < 8; ++db) {
       floatx4 acc = ds[db] * gl;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+      for (int jb = 0; jb < 4; ++jb) {
+        const floatx4 qt = col4(sm.q, jb * 16 + 4 * g4, db * 16);
+        const floatx4 kt = col4(sm.k, jb * 16 + 4 * g4, db * 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tok = jb * 16 + 4 * g4 + r;
-          acc = mfma4(bf(sm.q[tok][db * 16 + m]), dO[jb][r], acc);
-          acc = mfma4(bf(sm.k[tok][db * 16 + m]), dR[jb][r], acc);
+          acc = mfma4(qt[r], dO[jb][r], acc);
+          acc = mfma4(kt[r], dR[jb][r], acc);
         }
+      }
       ds[db] = acc;
     }
     __syncthreads();   // every wave is done with this chunk's LDS
@@ -657,9 +685,16 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
     const int jb = b - ib * (ib + 1) / 2;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int kk = 0; kk < kD / 4; ++kk)
-      acc = mfma4(bf(sm.k[ib * 16 + m][4 * kk + g4]), bf(sm.k[jb * 16 + m][4 * kk + g4]), acc);
+    // reduction index 16 kb + 4 (lane / 16) + r: four steps per 8-byte read of each row
+#pragma unroll 4
+    for (int kb = 0; kb < kD / 16; ++kb) {
+      const uint2 xa = *reinterpret_cast<const uint2*>(&sm.k[ib * 16 + m][16 * kb + 4 * g4]);
+      const uint2 xb = *reinterpret_cast<const uint2*>(&sm.k[jb * 16 + m][16 * kb + 4 * g4]);
+      acc = mfma4(bf(xa.x & 0xffff), bf(xb.x & 0xffff), acc);
+      acc = mfma4(bf(xa.x >> 16), bf(xb.x >> 16), acc);
+      acc = mfma4(bf(xa.y & 0xffff), bf(xb.y & 0xffff), acc);
+      acc = mfma4(bf(xa.y >> 16), bf(xb.y >> 16), acc);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.kkt[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
   }
@@ -835,18 +870,30 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     for (int tb = 0; tb < 4; ++tb) {
       floatx4 x2 = {0.f, 0.f, 0.f, 0.f};
       const int i = tb * 16 + m;
-#pragma unroll 2
-      for (int kk = 0; kk < 4 * (tb + 1); ++kk) {
-        const int j = 4 * kk + g4;
-        const float bk = bf(sm.k[j][d]);
-        dqh[tb] = mfma4(sm.u.mid.dpm[i][j], bk, dqh[tb]);
-        x1[tb] = mfma4(sm.u.mid.w[i][j], bk, x1[tb]);
+      // reduction over tokens j = 16 jb + 4 (lane / 16) + r: K, Q columns by
+      // the transposing read, dP o M and W rows by 16-byte reads
+#pragma unroll 1
+      for (int jb = 0; jb <= tb; ++jb) {
+        const int j0 = 16 * jb + 4 * g4;
+        const floatx4 kt = col4(sm.k, j0, w * 16);
+        const floatx4 ap = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][j0]);
+        const floatx4 aw = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][j0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dqh[tb] = mfma4(ap[r], kt[r], dqh[tb]);
+          x1[tb] = mfma4(aw[r], kt[r], x1[tb]);
+        }
       }
-#pragma unroll 2
-      for (int kk = 4 * tb; kk < 16; ++kk) {
-        const int j = 4 * kk + g4;
-        x2 = mfma4(sm.u.mid.w[j][i], bf(sm.k[j][d]), x2);
-        x2 = mfma4(sm.u.mid.dpm[j][i], bf(sm.q[j][d]), x2);
+#pragma unroll 1
+      for (int jb = tb; jb < 4; ++jb) {
+        const int j0 = 16 * jb + 4 * g4;
+        const floatx4 kt = col4(sm.k, j0, w * 16);
+        const floatx4 qt = col4(sm.q, j0, w * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x2 = mfma4(sm.u.mid.w[j0 + r][i], kt[r], x2);
+          x2 = mfma4(sm.u.mid.dpm[j0 + r][i], qt[r], x2);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

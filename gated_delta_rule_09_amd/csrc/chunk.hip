@@ -659,11 +659,6 @@ struct ScanParams {
   // every sequence, from state h0 to state hT (c_base = 0 and c_count >= the
   // chunks of a sequence: all of it)
   int c_base, c_count;
-  // touch the work-group's own V rows of chunk c + 2 as well (worth it when
-  // every work-group of the launch is resident: the chunk period is then the
-  // latency of the stage copy; with more work-groups than CUs the extra
-  // requests cost more than they save)
-  int touch_v;
 };
 
 // Two stage buffers (the chunk being computed, the one being copied in) and
@@ -694,7 +689,11 @@ __device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
 // 256 VGPRs per wave allow it).  <2, 2, 4>: 64 channels, two tiles per state
 // wave, one work-group per CU: a CU moves the chunk's shared K rows, Q and P
 // fragments and blob once for twice the channels.
-template <int kOutWaves, int kStateWaves, int kTiles = 2>
+// kTouchV: the L2 prefetch also touches the work-group's own V rows of chunk
+// c + 2.  Worth it when every work-group of the launch is resident (the chunk
+// period is then the latency of the stage copy); with more work-groups than
+// CUs the extra requests cost more than they save.
+template <int kOutWaves, int kStateWaves, int kTiles = 2, bool kTouchV = true>
 __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
   using Sh = ScanShape<kTiles>;
   constexpr int kParts = Sh::kParts;
@@ -792,7 +791,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   // work-groups of a key head share its K/Q blob and the blobs of its value
   // heads; member m pulls lines 64 m .. 64 m + 63 of that data (with 64-channel
   // work-groups also the lines 64 members further on), and each work-group
-  // its own V rows when touch_v is set.  One dword per 128-byte line; the
+  // its own V rows with kTouchV.  One dword per 128-byte line; the
   // values go to `sink`, stored only under a condition that never holds.
   const int kq_lines = kKQBytes / 128;
   const int vb_lines = p.group * kVBytes / 128;
@@ -807,7 +806,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
     const unsigned char* b = reinterpret_cast<const unsigned char*>(
         p.v + h * kD + part * kDvPerWg + static_cast<int64_t>(seq_start + ci * kC + r) * p.vs);
     uint32_t x = *reinterpret_cast<const uint32_t*>(line(member * 64 + lane));
-    if (p.touch_v) x ^= *reinterpret_cast<const uint32_t*>(b);
+    if (kTouchV) x ^= *reinterpret_cast<const uint32_t*>(b);
     if (kTiles > 2) x ^= *reinterpret_cast<const uint32_t*>(line((member + members) * 64 + lane));
     return x;
   };
@@ -1260,7 +1259,6 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   const int blocks = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * ScanShape<2>::kParts;
   const int blocks4 = ((sp.n_chain_groups + 7) / 8) * 8 * sp.group * ScanShape<4>::kParts;
   const int cus = compute_units();
-  sp.touch_v = 1;
 
   // Long equal-length sequences whose scan leaves compute units idle (in the
   // 32-channel form, else in the 64-channel form): the prep of segment i + 1
@@ -1317,9 +1315,12 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
   if (blocks <= cus) {
     hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()), 0, stream, sp);
   } else {
-    // more work-groups than CUs: the 64-channel form, half as many
-    sp.touch_v = blocks4 <= cus;
-    hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
+    // more work-groups than CUs: the 64-channel form, half as many; no V
+    // touch once even those outnumber the CUs
+    if (blocks4 <= cus)
+      hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4, true>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
+    else
+      hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4, false>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
   }
   return hipGetLastError();
 }
