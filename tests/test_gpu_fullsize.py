@@ -282,3 +282,24 @@ def test_full_backward_8x1024_every_group():
         for n in (0, N - 1):
             sl = slice(n * L, (n + 1) * L) if name != "dh0" else slice(n, n + 1)
             assert_close(host(got[name][sl]), ref[name][sl], f"{name} sequence {n}")
+
+
+@pytest.mark.timeout(600)
+def test_full_backward_1x8192_every_head():
+    """gdn_backward on the benchmark's long sequence (one sequence of 8192
+    tokens, 128 chunks through both chains, all 48 value heads, h0 and dS_T
+    given): every element of dq, dk, dv, dg, dbeta and dh0 against the oracle."""
+    N, L = 1, 8192
+    log(f"full backward {N} x {L} tokens (benchmark inputs, seeds 1008/1009), every head")
+    ci = synth.chunk_inputs_torch(1008, L, lengths=[L], h0_std=0.02)
+    bs = synth.backward_seeds_torch(1009, L, N)
+    got = ops.gdn_backward(ci["q"], ci["k"], ci["v"], ci["g"], ci["beta"], bs["d_o"],
+                           initial_state=ci["h0"], grad_final_state=bs["dhT"],
+                           cu_seqlens=ci["cu_seqlens"])
+    torch.cuda.synchronize()
+    log("  oracle")
+    ref = oracle.backward(bits(ci["q"]), bits(ci["k"]), bits(ci["v"]), f32(ci["g"]),
+                          f32(ci["beta"]), f32(bs["d_o"]), h0=f32(ci["h0"]), dhT=f32(bs["dhT"]),
+                          cu_seqlens=synth.cu_from_lengths([L]), n_seqs=N)
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert_close(host(got[name]), ref[name], name)
