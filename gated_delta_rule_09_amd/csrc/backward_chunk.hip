@@ -299,7 +299,8 @@ struct ChainNext {
   uint4 k[4];
   uint4 q[kWithQ ? 4 : 1];
   floatx4 x[4];
-  float g, b;                 // lane i: token i's g and beta (0 past the end)
+  float g, b;                 // lane i: token i's g and beta
+  int len;                    // tokens of the chunk: rows and gates past it are zeroed in chain_put
 };
 
 template <bool kWithQ>
@@ -318,40 +319,43 @@ __device__ __forceinline__ void chain_load(const CbParams& p, int t0, int len, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.q[j] = sq[j];
   }
-  if (!ok) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f.k[j] = make_uint4(0, 0, 0, 0);
-      if (kWithQ) f.q[j] = make_uint4(0, 0, 0, 0);
-    }
-  }
+  (void)ok;
+  f.len = len;
   const float* sx = p.X + sh * (kC * kC) + row * kC + (tid & 3) * 16;
 #pragma unroll
   for (int j = 0; j < 4; ++j) f.x[j] = *reinterpret_cast<const floatx4*>(sx + 4 * j);
-  const bool gok = lane < len;
   const int64_t gi_at = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
   f.g = p.g[gi_at];
   f.b = p.beta[gi_at];
-  if (!gok) f.g = f.b = 0.f;
 }
 
 template <bool kWithQ>
+// (the rows and gates past the chunk's end, loaded from its last token, are
+// zeroed here rather than at the load, where the choice would wait for them)
 __device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& sm) {
   const int tid = threadIdx.x;
   const int row = tid >> 2;
+  const uint32_t keep = row < f.len ? 0xffffffffu : 0u;   // a value mask, not a choice of objects
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint4*>(&sm.k[row][(tid & 3) * 32 + 8 * j]) = f.k[j];
-    if (kWithQ) *reinterpret_cast<uint4*>(&sm.q[row][(tid & 3) * 32 + 8 * j]) = f.q[j];
+    const uint4 kv = f.k[j];
+    *reinterpret_cast<uint4*>(&sm.k[row][(tid & 3) * 32 + 8 * j]) =
+        make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
+    if (kWithQ) {
+      const uint4 qv = f.q[j];
+      *reinterpret_cast<uint4*>(&sm.q[row][(tid & 3) * 32 + 8 * j]) =
+          make_uint4(qv.x & keep, qv.y & keep, qv.z & keep, qv.w & keep);
+    }
     *reinterpret_cast<floatx4*>(&sm.x[row][(tid & 3) * 16 + 4 * j]) = f.x[j];
   }
   if ((tid >> 6) == 0) {
     const int lane = tid & 63;
-    const float G = wave_prefix_sum(f.g);
+    const bool gok = lane < f.len;
+    const float G = wave_prefix_sum(gok ? f.g : 0.f);
     const float GL = __shfl(G, 63, 64);
     sm.gam[lane] = expf(G);
     sm.dec[lane] = expf(GL - G);
-    sm.bet[lane] = f.b;
+    sm.bet[lane] = gok ? f.b : 0.f;
   }
 }
 
@@ -401,8 +405,7 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tb * 16 + 4 * g4 + r;
-        const float x = bf(p.v[static_cast<int64_t>(t0 + min(tok, len - 1)) * p.vs + h * kD + ch]);
-        vv[tb][r] = tok < len ? x : 0.f;
+        vv[tb][r] = bf(p.v[static_cast<int64_t>(t0 + min(tok, len - 1)) * p.vs + h * kD + ch]);
       }
     if (c + 1 < nc)
       chain_load(p, t0 + kC, min(kC, s1 - t0 - kC), h, kh, static_cast<int64_t>(slot + 1) * p.Hv + h, nx);
@@ -434,7 +437,8 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tb * 16 + 4 * g4 + r;
-        const float e = vv[tb][r] - sm.gam[tok] * z[tb][r];
+        // V past the chunk's end (loaded from its last token) counts as zero
+        const float e = (tok < len ? vv[tb][r] : 0.f) - sm.gam[tok] * z[tb][r];
         Eh[tok * kD] = e;
         R[tb][r] = sm.bet[tok] * e;
       }
@@ -529,8 +533,7 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = tb * 16 + 4 * g4 + r;
-        const float x = p.d_o[(static_cast<int64_t>(t0 + min(tok, len - 1)) * p.Hv + h) * kD + ch];
-        dO[tb][r] = tok < len ? x : 0.f;
+        dO[tb][r] = p.d_o[(static_cast<int64_t>(t0 + min(tok, len - 1)) * p.Hv + h) * kD + ch];
       }
     // the previous chunk's inputs, written to LDS after this one
     if (c > 0) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx);
