@@ -422,21 +422,33 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   const int grp = lane >> 4;
 
   // g and beta of value head vh, one token per lane
+  // The gate inputs of value head vh, lane = token (tokens past the end read
+  // the last one): loaded here, turned into g, beta (zero past the end) by
+  // finish_gb where they are first needed, since a choice on a freshly
+  // loaded value makes the wave wait for it on the spot.
   auto load_gb = [&](int vh, float& gv, float& bv) {
+    const int64_t t = t0 + min(lane, len - 1);
+    const int h = kh * p.group + vh;
+    if (kGated) {
+      gv = bf16_to_f32(p.ga[t * p.gas + h]);
+      bv = bf16_to_f32(p.gb[t * p.gbs + h]);
+    } else {
+      gv = p.g[t * p.Hv + h];
+      bv = p.beta[t * p.Hv + h];
+    }
+  };
+  auto finish_gb = [&](int vh, float& gv, float& bv) {
     const bool valid = lane < len;
     if (kGated) {
       // softplus(x) = max(x, 0) + log1p(e^-|x|), with the accurate libm forms
-      const int64_t t = t0 + min(lane, len - 1);
       const int h = kh * p.group + vh;
-      const float x = bf16_to_f32(p.ga[t * p.gas + h]) + p.dt_bias[h];
+      const float x = gv + p.dt_bias[h];
       const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-      const float y = bf16_to_f32(p.gb[t * p.gbs + h]);
       gv = valid ? -expf(p.A_log[h]) * sp : 0.f;
-      bv = valid ? 1.f / (1.f + expf(-y)) : 0.f;
+      bv = valid ? 1.f / (1.f + expf(-bv)) : 0.f;
     } else {
-      const int64_t gi = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + kh * p.group + vh;
-      gv = valid ? p.g[gi] : 0.f;
-      bv = valid ? p.beta[gi] : 0.f;
+      gv = valid ? gv : 0.f;
+      bv = valid ? bv : 0.f;
     }
   };
   // decay tables of value head vb0 + w (wave w, lane = token): G = inclusive
@@ -474,7 +486,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     ConvRows cr;
     conv_rows_load(p, cr, p.Hk * kD + kh * kD + g8, t0, r0, len, s0);
     // the first batch's decay tables while the x loads are in flight
-    if (w < nb0) decay(0, gv, bv);
+    if (w < nb0) {
+      finish_gb(w, gv, bv);
+      decay(0, gv, bv);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (m == 1) conv_rows_load(p, cr, kh * kD + g8, t0, r0, len, s0);
@@ -506,7 +521,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
       qraw[j] = uint4{qt[0], qt[1], qt[2], qt[3]};
     }
     // the first batch's decay tables while the K, Q loads are in flight
-    if (w < nb0) decay(0, gv, bv);
+    if (w < nb0) {
+      finish_gb(w, gv, bv);
+      decay(0, gv, bv);
+    }
     // K, Q -> LDS (fp16), rows past the chunk end zeroed
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -574,6 +592,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     if (vb0 > 0) {
       if (w < nb) {
         load_gb(vb0 + w, gv, bv);
+        finish_gb(vb0 + w, gv, bv);
         decay(vb0, gv, bv);
       }
       lds_barrier();   // G, bet of the batch ready
