@@ -575,7 +575,7 @@ size_t gdn_mixer_fwd_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hk
                                      int32_t d, int32_t out_is_bf16) {
   (void)d;
   if (n_seqs < 0 || T_total < 0 || Hk <= 0 || Hv <= 0) return 0;
-  return gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv, true).total +
+  return gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv).total +
          mixer_o_bytes(T_total, Hv, out_is_bf16);
 }
 
@@ -627,7 +627,7 @@ gdn_status gdn_mixer_fwd(const uint16_t* x, int64_t x_stride, const uint16_t* co
   }
   if (static_cast<int64_t>(n_seqs) * Hv * 2 + 16LL * Hv > 0x7fffffffLL)
     return fail(GDN_ERR_SHAPE, "%s: too many (sequence, head) pairs", fn);
-  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv, true);
+  const gdn::ChunkWorkspace ws = gdn::chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
   const size_t need = ws.total + mixer_o_bytes(T_total, Hv, out_is_bf16);
   const int64_t ssz = width * d;
   const Range rx = range_of(x, T_total, x_stride, C, 2);

@@ -63,7 +63,9 @@ constexpr int kThreads = 256;    // prep work-group
 constexpr int kScanLoaderWaves = 2;
 constexpr int kLoaderThreads = 64 * kScanLoaderWaves;
 template <int kOutWaves, int kStateWaves>
-constexpr int scan_threads() { return 64 * (kStateWaves + kOutWaves + kScanLoaderWaves); }
+constexpr int scan_threads(bool conv = false) {   // conv: two conv waves too
+  return 64 * (kStateWaves + kOutWaves + kScanLoaderWaves + (conv ? 2 : 0));
+}
 
 // ---- fragment layout in the workspace -------------------------------------
 // An A32 fragment of a 16 x 32 block holds, for lane l (row l % 16, group
@@ -116,6 +118,15 @@ struct ScanShape {
   static constexpr int kVPiecesPerRow = kDv / 8;
   static constexpr int kU0 = 4 * kTiles;
   static constexpr int kXBytes = 6 * kTiles * kFrag;              // 12 / 24 KB
+  // conv front (kConvV): each loader wave copies the pre-conv rows of its
+  // half of the chunk, 3 rows of history first, and a conv wave forms that
+  // half of the V tile from them
+  static constexpr int kRawRows = kC / 2 + 3;                     // 35
+  static constexpr int kRawBytes = kRawRows * kDv * 2;            // 2240 / 4480
+  static constexpr int kRawPieces = kRawBytes / 16;
+  static constexpr int kRawRounds = (kRawPieces + 63) / 64;
+  static constexpr int kConvTok = kDv / 16;                       // tokens per loader lane
+  static constexpr int kKVBRounds = (kKPieces + kVBPieces + kLoaderThreads - 1) / kLoaderThreads;
   static_assert(kStagePieces == kKPieces + kVBPieces + kVTileBytes / 16, "stage = K rows + value blob + V tile");
   static_assert(kStageBytes % 16 == 0, "stage size");
 };
@@ -176,13 +187,12 @@ struct PrepParams {
   const uint16_t* ga; const uint16_t* gb;
   int64_t gas, gbs;
   const float* A_log; const float* dt_bias;
-  // conv front (kConv): q, k and v come from the causal conv + SiLU (+ L2 for
-  // q, k) of the pre-conv rows x [T, C]; v goes to vout [T, Hv, 128] bf16
+  // conv front (kConv): q and k come from the causal conv + SiLU + L2 of the
+  // pre-conv rows x [T, C] (v is formed by the scan kernel from the same rows)
   const uint16_t* x; int64_t xs;
   const uint16_t* conv_w; const float* conv_bias; const uint16_t* conv_state;
   const int32_t* conv_slots;  // nullptr: sequence n uses conv_state row n
   int conv_n_slots;           // rows of the conv-state pool (with conv_slots)
-  uint16_t* vout;
   float l2_eps;
   const int32_t* cu;          // nullptr: equal lengths seq_len
   const int32_t* chunk_off;   // varlen chunk map (device)
@@ -392,7 +402,7 @@ __device__ __forceinline__ void conv_rows(const PrepParams& p, const ConvRows& c
 }
 
 // kGated: the gates come from the projections (p.ga, p.gb, p.A_log, p.dt_bias).
-// kConv: q, k, v come from the conv front over p.x (v written to p.vout).
+// kConv: q and k come from the conv front over p.x.
 template <bool kGated, bool kConv>
 __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
   __shared__ PrepSmem sm;
@@ -636,25 +646,6 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepParams p) {
     }
     if (vb0 + kHeadBatch < p.group) lds_barrier();   // before the next batch overwrites
   }
-
-  if (kConv) {
-    // v of the key head's value heads: conv + SiLU (no L2), bf16 to vout
-    for (int vh = 0; vh < p.group; ++vh) {
-      const int h = kh * p.group + vh;
-      const int ch0 = 2 * p.Hk * kD + h * kD + g8;
-      ConvRows cv;
-      conv_rows_load(p, cv, ch0, t0, r0, len, s0);
-      float y[4][8];
-      conv_rows(p, cv, ch0, t0, r0, s0, seq, C, false, y);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (r0 + jj < len)
-          __builtin_nontemporal_store(
-              u32x4{pack_bf16x2(y[jj][0], y[jj][1]), pack_bf16x2(y[jj][2], y[jj][3]),
-                    pack_bf16x2(y[jj][4], y[jj][5]), pack_bf16x2(y[jj][6], y[jj][7])},
-              reinterpret_cast<u32x4*>(p.vout + static_cast<int64_t>(t0 + r0 + jj) * (p.Hv * kD) + h * kD + g8));
-    }
-  }
 }
 
 // ---- scan kernel ------------------------------------------------------------
@@ -678,15 +669,30 @@ struct ScanParams {
   // every sequence, from state h0 to state hT (c_base = 0 and c_count >= the
   // chunks of a sequence: all of it)
   int c_base, c_count;
+  // conv front (kConvV): v = silu(causal conv of the pre-conv rows), with v
+  // pointing at the first v column of x and vs its row stride; conv_w [C, 4]
+  // bf16 and conv_bias [C] (or nullptr) of the C = conv_C channels of x,
+  // whose value channels start at conv_v0; history before a sequence from
+  // conv_state [rows, C, 3] (row conv_slots[n], or n) or zeros
+  const uint16_t* conv_w; const float* conv_bias; const uint16_t* conv_state;
+  const int32_t* conv_slots;
+  int conv_n_slots, conv_C, conv_v0;
 };
 
 // Two stage buffers (the chunk being computed, the one being copied in) and
 // two sets of the S0 / U fragments passed from the state wave to the output
 // wave.
-template <int kTiles>
+template <int kTiles, bool kConvV>
 struct __align__(16) ScanSmem {
   unsigned char buf[2][ScanShape<kTiles>::kStageBytes];
   unsigned char xbuf[2][ScanShape<kTiles>::kXBytes];
+};
+// with the conv front also the pre-conv rows, [chunk parity][loader wave]
+template <int kTiles>
+struct __align__(16) ScanSmem<kTiles, true> {
+  unsigned char buf[2][ScanShape<kTiles>::kStageBytes];
+  unsigned char xbuf[2][ScanShape<kTiles>::kXBytes];
+  unsigned char raw[2][2][ScanShape<kTiles>::kRawBytes];
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -712,14 +718,19 @@ __device__ __forceinline__ half4 lds_read_tr(const unsigned char* p) {
 // c + 2.  Worth it when every work-group of the launch is resident (the chunk
 // period is then the latency of the stage copy); with more work-groups than
 // CUs the extra requests cost more than they save.
-template <int kOutWaves, int kStateWaves, int kTiles = 2, bool kTouchV = true>
-__global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
+// kConvV: v is the conv front's output, formed here from the pre-conv rows
+// (p.v, p.vs point into x), so it never goes to HBM: the loader waves also
+// copy those rows into LDS a chunk ahead, and two more waves (conv waves)
+// turn them into the V tile.  On the loader waves themselves the conv held
+// up the copies (T = 8192: 212 us against 179 us for the scan).
+template <int kOutWaves, int kStateWaves, int kTiles = 2, bool kTouchV = true, bool kConvV = false>
+__global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>(kConvV)), kOutWaves == 1 ? 2 : 1) void chunk_scan_kernel(ScanParams p) {
   using Sh = ScanShape<kTiles>;
   constexpr int kParts = Sh::kParts;
   constexpr int kDvPerWg = Sh::kDv;
   constexpr int kScanComputeWaves = kStateWaves + kOutWaves;
   static_assert(kTiles % kStateWaves == 0, "tiles split evenly over the state waves");
-  __shared__ ScanSmem<kTiles> sm;
+  __shared__ ScanSmem<kTiles, kConvV> sm;
 
   // ---- block id -> (sequence rank, value head, value quarter) --------------
   // Chains sharing a key head (group * kParts of them) get block ids that are
@@ -771,7 +782,9 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
 
     // Piece i of the stage is its byte 16 i: the K rows, the value-head blob
     // from T_bb on, then the V tile (token i / kVPiecesPerRow, channels
-    // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDv).
+    // 8 (i % kVPiecesPerRow) .. +7 of this work-group's kDv).  With the conv
+    // front the copy stops before the V tile.
+    constexpr int kRounds = kConvV ? Sh::kKVBRounds : Sh::kStageRounds;
     auto stage = [&](int ci) {
       const int cb = chunk0 + ci;
       const unsigned char* kqb = kq_head + cb * kq_step;
@@ -780,25 +793,144 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
       const int len = min(kC, seq_len - ci * kC);
       const uint16_t* vrow0 = v_head + static_cast<int64_t>(seq_start + ci * kC) * p.vs;
 #pragma unroll
-      for (int j = 0; j < Sh::kStageRounds; ++j) {
+      for (int j = 0; j < kRounds; ++j) {
         const int q = kLoaderThreads * j + lt;
         unsigned char* d = dst + (kLoaderThreads * j + 64 * lw) * 16;
         if (q < kKPieces) {
           lds_dma16(kqb + q * 16, d);
         } else if (q < kKPieces + kVBPieces) {
           lds_dma16(vbb + kOffT + (q - kKPieces) * 16, d);
-        } else if (q < Sh::kStagePieces) {
+        } else if (!kConvV && q < Sh::kStagePieces) {
           const int vp = q - kKPieces - kVBPieces;
           const int r = min(vp / Sh::kVPiecesPerRow, len - 1);   // rows past the end re-read the last
           lds_dma16(vrow0 + static_cast<int64_t>(r) * p.vs + (vp % Sh::kVPiecesPerRow) * 8, d);
         }
       }
     };
-    // Per chunk: the copies of chunk ci + 1.
-    if (n_chunks > 0) stage(0);
-    for (int ci = 0; ci < n_chunks; ++ci) {
-      dma_barrier();
-      if (ci + 1 < n_chunks) stage(ci + 1);
+    if constexpr (!kConvV) {
+      // Per chunk: the copies of chunk ci + 1.
+      if (n_chunks > 0) stage(0);
+      for (int ci = 0; ci < n_chunks; ++ci) {
+        dma_barrier();
+        if (ci + 1 < n_chunks) stage(ci + 1);
+      }
+    } else {
+      // Conv front.  Loader wave `half` copies the pre-conv rows of tokens
+      // 32 half - 3 .. 32 half + 31 of a chunk into raw[chunk & 1][half] two
+      // chunks ahead (row rr is token 32 half - 3 + rr); conv wave `half`
+      // forms tokens 32 half .. 32 half + 31 of the V tile from them a chunk
+      // ahead: its lane (cg, tok0) channels 8 cg .. +7 of tokens tok0 ..
+      // tok0 + kConvTok - 1 of that half, from rows tok0 .. tok0 + kConvTok
+      // + 2.  Tokens before the sequence take the conv state (or zeros); rows
+      // past its end re-read the last.  The operations and their order are
+      // those of conv1d_kernel: v equals what the separate conv call stores.
+      const int half = lw & 1;      // waves lw = 0, 1 copy, lw = 2, 3 convert
+      const int true_start = p.cu ? seq_start : n * p.seq_len;
+      const int seq_end = seq_start + seq_len;
+      const int cg = lane % Sh::kVPiecesPerRow;
+      const int tok0 = Sh::kConvTok * (lane / Sh::kVPiecesPerRow);
+      const int ch = p.conv_v0 + h * kD + part * kDvPerWg + 8 * cg;    // channel of x
+      float wt[32];
+      {
+        const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + static_cast<int64_t>(ch) * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bf16x8_to_f32(wp[q], wt + 8 * q);
+      }
+      float bias[8];
+      if (p.conv_bias) {
+        const float4 b0 = *reinterpret_cast<const float4*>(p.conv_bias + ch);
+        const float4 b1 = *reinterpret_cast<const float4*>(p.conv_bias + ch + 4);
+        bias[0] = b0.x; bias[1] = b0.y; bias[2] = b0.z; bias[3] = b0.w;
+        bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bias[i] = 0.f;
+      }
+      auto raw_copy = [&](int ci) {
+        const int tb = seq_start + ci * kC + 32 * half - 3;     // token of row 0
+        unsigned char* dst = sm.raw[ci & 1][half];
+#pragma unroll
+        for (int j = 0; j < Sh::kRawRounds; ++j) {
+          const int q = 64 * j + lane;
+          if (q < Sh::kRawPieces) {
+            const int t = min(max(tb + q / Sh::kVPiecesPerRow, true_start), seq_end - 1);
+            lds_dma16(v_head + static_cast<int64_t>(t) * p.vs + (q % Sh::kVPiecesPerRow) * 8, dst + j * 1024);
+          }
+        }
+      };
+      // v of chunk ci into its stage buffer; `first`: the sequence's first
+      // chunk, whose rows before token 0 are the history
+      auto conv_tile = [&](int ci, bool first) {
+        const unsigned char* src = sm.raw[ci & 1][half] + tok0 * (kDvPerWg * 2) + cg * 16;
+        float xin[Sh::kConvTok + 3][8];
+#pragma unroll
+        for (int j = 0; j < Sh::kConvTok + 3; ++j)
+          bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + j * (kDvPerWg * 2)), xin[j]);
+        if (first && half == 0 && tok0 < 3) {
+          float st[24];
+          const int64_t row = p.conv_slots ? p.conv_slots[n] : n;
+          // a slot outside the pool reads no history (zeros)
+          const bool has_row = p.conv_state &&
+              (!p.conv_slots || static_cast<uint64_t>(row) < static_cast<uint64_t>(p.conv_n_slots));
+          if (has_row) {
+            const uint4* sp = reinterpret_cast<const uint4*>(p.conv_state + (row * p.conv_C + ch) * 3);
+            bf16x8_to_f32(sp[0], st);
+            bf16x8_to_f32(sp[1], st + 8);
+            bf16x8_to_f32(sp[2], st + 16);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 24; ++i) st[i] = 0.f;
+          }
+          // rows 0, 1, 2 are the tokens 3, 2, 1 before the start: taps 0, 1, 2
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            if (tok0 + j < 3)
+#pragma unroll
+              for (int i = 0; i < 8; ++i) xin[j][i] = st[3 * i + tok0 + j];
+        }
+        unsigned char* dst = sm.buf[ci & 1] + kStageV + (32 * half + tok0) * (kDvPerWg * 2) + cg * 16;
+#pragma unroll
+        for (int jj = 0; jj < Sh::kConvTok; ++jj) {
+          float y[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float acc = fmaf(wt[4 * i], xin[jj][i], bias[i]);
+            acc = fmaf(wt[4 * i + 1], xin[jj + 1][i], acc);
+            acc = fmaf(wt[4 * i + 2], xin[jj + 2][i], acc);
+            acc = fmaf(wt[4 * i + 3], xin[jj + 3][i], acc);
+            y[i] = conv_silu(acc);
+          }
+          *reinterpret_cast<u32x4*>(dst + jj * (kDvPerWg * 2)) =
+              u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                    pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+        }
+      };
+      // One extra barrier before the per-chunk ones: chunk 0's rows in LDS.
+      // Per chunk ci, the loader waves copy the stage of ci + 1 and the rows
+      // of ci + 2 (into the raw buffer of ci, converted a period ago), the
+      // conv waves form v of ci + 1 from its rows (copied a period ago).
+      if (lw < 2) {
+        if (n_chunks > 0) {
+          raw_copy(0);
+          stage(0);
+          if (n_chunks > 1) raw_copy(1);
+        }
+        dma_barrier();                     // rows of chunk 0 in LDS
+        for (int ci = 0; ci < n_chunks; ++ci) {
+          dma_barrier();
+          if (ci + 1 < n_chunks) {
+            stage(ci + 1);
+            if (ci + 2 < n_chunks) raw_copy(ci + 2);
+          }
+        }
+      } else {
+        lds_barrier();
+        if (n_chunks > 0) conv_tile(0, p.cu || p.c_base == 0);
+        for (int ci = 0; ci < n_chunks; ++ci) {
+          dma_barrier();
+          if (ci + 1 < n_chunks) conv_tile(ci + 1, false);
+        }
+      }
     }
     lds_barrier();                         // the compute waves' last two barriers
     lds_barrier();
@@ -839,6 +971,7 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   // chain from one chunk's state to the next holds no output products.
   const int col = lane & 15;
   const int grp = lane >> 4;
+  if constexpr (kConvV) lds_barrier();     // the conv waves' first barrier
 
   // State wave(s): kStateWaves waves share the work-group's two tiles; wave
   // sw carries tiles t0 .. t0 + NT - 1.
@@ -1151,11 +1284,11 @@ __global__ __launch_bounds__((scan_threads<kOutWaves, kStateWaves>()), kOutWaves
   else output_wave(std::integral_constant<int, kOutWaves - 1>{});
 }
 
-static_assert(sizeof(ScanSmem<2>) + kScanLdsPad <= 160 * 1024, "padded scan work-group fits a CU");
-static_assert(sizeof(ScanSmem<2>) + kScanLdsPad + sizeof(PrepSmem) > 160 * 1024,
+static_assert(sizeof(ScanSmem<2, true>) + kScanLdsPad <= 160 * 1024, "padded scan work-group fits a CU");
+static_assert(sizeof(ScanSmem<2, false>) + kScanLdsPad + sizeof(PrepSmem) > 160 * 1024,
               "no prep work-group fits beside a padded scan work-group");
-static_assert(sizeof(ScanSmem<4>) + kScanLdsPad4 <= 160 * 1024, "padded 64-channel work-group fits a CU");
-static_assert(sizeof(ScanSmem<4>) + kScanLdsPad4 + sizeof(PrepSmem) > 160 * 1024,
+static_assert(sizeof(ScanSmem<4, true>) + kScanLdsPad4 <= 160 * 1024, "padded 64-channel work-group fits a CU");
+static_assert(sizeof(ScanSmem<4, false>) + kScanLdsPad4 + sizeof(PrepSmem) > 160 * 1024,
               "no prep work-group fits beside a padded 64-channel scan work-group");
 
 hipError_t launch_prep(const PrepParams& pp, dim3 grid, bool conv, hipStream_t stream) {
@@ -1170,6 +1303,19 @@ hipError_t launch_prep(const PrepParams& pp, dim3 grid, bool conv, hipStream_t s
     else
       hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kThreads), 0, stream, pp);
   }
+  return hipGetLastError();
+}
+
+// One scan launch: the 32- (kTiles = 2) or 64-channel form, with the conv
+// front or without, `lds` bytes of LDS added.
+template <int kTiles, bool kTouchV>
+hipError_t launch_scan(const ScanParams& sp, int blocks, size_t lds, bool conv, hipStream_t stream) {
+  if (conv)
+    hipLaunchKernelGGL((chunk_scan_kernel<2, 2, kTiles, kTouchV, true>), dim3(blocks),
+                       dim3(scan_threads<2, 2>(true)), lds, stream, sp);
+  else
+    hipLaunchKernelGGL((chunk_scan_kernel<2, 2, kTiles, kTouchV, false>), dim3(blocks),
+                       dim3(scan_threads<2, 2>()), lds, stream, sp);
   return hipGetLastError();
 }
 
@@ -1206,7 +1352,7 @@ Overlap* overlap_of_current_device() {
   return ok[dev] ? &ov[dev] : nullptr;
 }
 
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, bool conv_v) {
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv) {
   auto up = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
   ChunkWorkspace ws;
   ws.max_chunks = static_cast<size_t>(T_total) / kC + static_cast<size_t>(n_seqs);
@@ -1215,9 +1361,7 @@ ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, b
   ws.chunk_tab_off = ws.chunk_off_off + up(sizeof(int32_t) * (static_cast<size_t>(n_seqs) + 1));
   ws.kq_off = ws.chunk_tab_off + up(sizeof(int32_t) * 3 * ws.max_chunks);
   ws.v_off = ws.kq_off + up(ws.max_chunks * static_cast<size_t>(Hk) * kKQBytes);
-  ws.conv_v_off = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
-  ws.carry_off = ws.conv_v_off +
-                 (conv_v ? up(static_cast<size_t>(T_total) * static_cast<size_t>(Hv) * kD * 2) : 0);
+  ws.carry_off = ws.v_off + up(ws.max_chunks * static_cast<size_t>(Hv) * kVBytes);
   const bool carry = n_seqs > 0 && T_total / n_seqs >= kSegMinChunks * kC;
   ws.total = ws.carry_off + (carry ? static_cast<size_t>(n_seqs) * Hv * kD * kD * sizeof(float) : 0);
   return ws;
@@ -1230,7 +1374,7 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
                             int n_seqs, int T_total, int Hk, int Hv, float scale,
                             void* workspace, hipStream_t stream, const ConvFront* conv) {
   if (n_seqs == 0) return hipSuccess;
-  const ChunkWorkspace ws = chunk_workspace_layout(n_seqs, T_total, Hk, Hv, conv != nullptr);
+  const ChunkWorkspace ws = chunk_workspace_layout(n_seqs, T_total, Hk, Hv);
   unsigned char* base = static_cast<unsigned char*>(workspace);
   int32_t* order = reinterpret_cast<int32_t*>(base + ws.order_off);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(base + ws.chunk_off_off);
@@ -1253,17 +1397,21 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     pp.x = conv->x; pp.xs = conv->xs; pp.conv_w = conv->w; pp.conv_bias = conv->bias;
     pp.conv_state = conv->state; pp.conv_slots = conv->slots; pp.conv_n_slots = conv->n_slots;
     pp.l2_eps = conv->l2_eps;
-    pp.vout = reinterpret_cast<uint16_t*>(base + ws.conv_v_off);
   }
   pp.cu = cu; pp.chunk_off = chunk_off; pp.chunk_tab = chunk_tab;
   pp.kq = base + ws.kq_off; pp.vb = base + ws.v_off;
   pp.n_seqs = n_seqs; pp.seq_len = seq_len; pp.Hk = Hk; pp.Hv = Hv; pp.group = Hv / Hk;
   pp.scale = scale;
 
-  ScanParams sp;
+  ScanParams sp{};
   if (conv) {
-    v = reinterpret_cast<const uint16_t*>(base + ws.conv_v_off);
-    vs = static_cast<int64_t>(Hv) * kD;
+    // the scan forms v from x's value columns
+    sp.conv_v0 = 2 * Hk * kD;
+    sp.conv_C = (2 * Hk + Hv) * kD;
+    v = conv->x + sp.conv_v0;
+    vs = conv->xs;
+    sp.conv_w = conv->w; sp.conv_bias = conv->bias; sp.conv_state = conv->state;
+    sp.conv_slots = conv->slots; sp.conv_n_slots = conv->n_slots;
   }
   sp.v = v; sp.vs = vs; sp.o = o; sp.o_bf16 = o_bf16 ? 1 : 0; sp.h0 = h0; sp.hT = hT;
   sp.slots = state_slot;
@@ -1313,13 +1461,8 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
         sp.c_count = kSegChunks;
         sp.h0 = s == 0 ? h0 : carry;
         sp.hT = s + 1 == n_seg ? hT : carry;
-        if (seg32)
-          hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()),
-                             kScanLdsPad, stream, sp);
-        else
-          hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4>), dim3(blocks4), dim3(scan_threads<2, 2>()),
-                             kScanLdsPad4, stream, sp);
-        e = hipGetLastError();
+        e = seg32 ? launch_scan<2, true>(sp, blocks, kScanLdsPad, conv != nullptr, stream)
+                  : launch_scan<4, true>(sp, blocks4, kScanLdsPad4, conv != nullptr, stream);
       }
       return e;
     }
@@ -1331,17 +1474,11 @@ hipError_t launch_chunk_fwd(const uint16_t* q, int64_t qs, const uint16_t* k, in
     const hipError_t e = launch_prep(pp, dim3(Hk, n_chunk_slots), conv != nullptr, stream);
     if (e != hipSuccess) return e;
   }
-  if (blocks <= cus) {
-    hipLaunchKernelGGL((chunk_scan_kernel<2, 2>), dim3(blocks), dim3(scan_threads<2, 2>()), 0, stream, sp);
-  } else {
-    // more work-groups than CUs: the 64-channel form, half as many; no V
-    // touch once even those outnumber the CUs
-    if (blocks4 <= cus)
-      hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4, true>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
-    else
-      hipLaunchKernelGGL((chunk_scan_kernel<2, 2, 4, false>), dim3(blocks4), dim3(scan_threads<2, 2>()), 0, stream, sp);
-  }
-  return hipGetLastError();
+  if (blocks <= cus) return launch_scan<2, true>(sp, blocks, 0, conv != nullptr, stream);
+  // more work-groups than CUs: the 64-channel form, half as many; no V
+  // touch once even those outnumber the CUs
+  if (blocks4 <= cus) return launch_scan<4, true>(sp, blocks4, 0, conv != nullptr, stream);
+  return launch_scan<4, false>(sp, blocks4, 0, conv != nullptr, stream);
 }
 
 }  // namespace gdn

@@ -48,14 +48,12 @@ Overlap* overlap_of_current_device();
 //   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]
 //   | K rows + Q fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]
 struct ChunkWorkspace {
-  size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, conv_v_off, carry_off,
-      total;
+  size_t max_chunks, order_off, chunk_off_off, chunk_tab_off, kq_off, v_off, carry_off, total;
 };
-// conv_v: room for the conv front's v [T_total, Hv, 128] bf16 at conv_v_off.
 // Long sequences (T_total / n_seqs >= 32768) also get the state carried from
 // one segment of the overlapped prefill to the next, [n_seqs, Hv, 128, 128]
 // fp32 at carry_off.
-ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv, bool conv_v = false);
+ChunkWorkspace chunk_workspace_layout(int n_seqs, int T_total, int Hk, int Hv);
 
 hipError_t launch_chunk_map(const int32_t* cu, int n_seqs, int T_total, int32_t* order,
                             int32_t* chunk_off, int32_t* chunk_tab, hipStream_t stream);

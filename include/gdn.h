@@ -267,10 +267,9 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  * gdn_mixer_fwd -- the whole token mixer over a prefill in one call (the
  * "Delta-rule layers" row of the model card's Architecture table: causal
  * conv in front, the rule, gated RMS-norm after).  The causal conv (kernel 4)
- * + SiLU + per-head L2 of q and k runs inside the chunk-prep kernel, so no
- * conv output goes to HBM except v, which passes to the scan through the
- * workspace; then the chunked rule, the conv-window update and the gated
- * RMSNorm.  The result equals gdn_conv1d_fwd -> gdn_chunk_fwd ->
+ * + SiLU + per-head L2 of q and k runs inside the chunk-prep kernel and the
+ * conv + SiLU of v inside the scan kernel, so no conv output goes to HBM;
+ * then the conv-window update and the gated RMSNorm.  The result equals gdn_conv1d_fwd -> gdn_chunk_fwd ->
  * gdn_gated_rmsnorm on the same inputs bit for bit (same operations in the
  * same order).
  *   x           [T_total, C] bf16 pre-conv rows [q | k | v], C = (2 Hk + Hv) d,
@@ -298,8 +297,7 @@ gdn_status gdn_chunk_fwd_gated(const uint16_t* q, int64_t q_tok_stride, const ui
  *               rows of out are unspecified
  *   l2_eps, norm_eps  the L2 and RMS epsilons (finite, >= 0)
  *   workspace   gdn_mixer_fwd_workspace_bytes() bytes, 256-byte aligned: the
- *               prefill workspace, v after the conv (T_total x Hv x d bf16)
- *               and, for bf16 out, the fp32 o
+ *               prefill workspace and, for bf16 out, the fp32 o
  * Every pointer 16-byte aligned except g, beta, A_log, dt_bias and
  * cu_seqlens (4 bytes) and a, b (2 bytes).
  * d = 128.  Errors as for gdn_chunk_fwd.

@@ -446,15 +446,20 @@ def _unfused_mixer(x, w, bias, cs, g, beta, z, nw, h0, cu, n_seqs, Hk, Hv, out_b
     return ops.gdn_gated_rmsnorm(o, z, nw, out_bf16=out_bf16), hT
 
 
-@pytest.mark.parametrize("case", ["single", "varlen", "equal_split"])
+@pytest.mark.parametrize("case", ["single", "varlen", "varlen_wide", "equal_split"])
 def test_mixer_fwd_equals_unfused(case):
-    """gdn_mixer_fwd (conv front inside the prep kernel) against the separate
-    conv, prefill and norm calls on the same inputs: out, final states and
-    the conv window identical bit for bit."""
+    """gdn_mixer_fwd (conv front for q, k inside the prep kernel, for v inside
+    the scan kernel) against the separate conv, prefill and norm calls on the
+    same inputs: out, final states and the conv window identical bit for bit.
+    The cases take the scan's three forms: 32 channels per work-group
+    (single, equal_split), 64 channels (varlen), and 64 channels without the
+    L2 touch of the V rows (varlen_wide: 64 (sequence, key head) chains)."""
     if case == "single":
         lens, Hk, Hv, out_bf16, with_cs, with_bias = [200], 16, 48, False, False, False
     elif case == "varlen":
         lens, Hk, Hv, out_bf16, with_cs, with_bias = [70, 0, 1, 130, 3, 64], 4, 12, True, True, True
+    elif case == "varlen_wide":
+        lens, Hk, Hv, out_bf16, with_cs, with_bias = [150, 64, 2, 90], 16, 48, False, True, True
     else:
         lens, Hk, Hv, out_bf16, with_cs, with_bias = [64, 64, 64], 2, 6, False, True, False
     T, N = sum(lens), len(lens)
@@ -463,7 +468,7 @@ def test_mixer_fwd_equals_unfused(case):
     r = np.random.default_rng(37)
     bias = dev_f32((0.1 * r.standard_normal(mi.x.shape[1])).astype(np.float32)) if with_bias else None
     h0 = dev_f32((0.05 * r.standard_normal((N, Hv, 128, 128))).astype(np.float32))
-    cu = dev_i32(synth.cu_from_lengths(lens)) if case == "varlen" else None
+    cu = dev_i32(synth.cu_from_lengths(lens)) if case.startswith("varlen") else None
     x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
     g, b = dev_f32(mi.g), dev_f32(mi.beta)
     cs1 = dev_bf16(mi.conv_state) if with_cs else None
