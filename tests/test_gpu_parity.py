@@ -560,6 +560,39 @@ def test_mixer_fwd_with_state_pools():
     assert torch.equal(cs_pool[others], dev_bf16(mi.conv_state)[others])
 
 
+def test_mixer_fwd_padding_slot():
+    """gdn_mixer_fwd over pools with a padding sequence (slot -1): the real
+    sequences' out rows, states and conv windows equal those of the call on
+    the real sequences alone (bit for bit), and no other pool row changes."""
+    lens, Hk, Hv, n_slots = [40, 70, 1, 129], 2, 6, 7
+    T, N = sum(lens), len(lens)
+    log(f"mixer_fwd with a padding slot, lens={lens}")
+    mi = synth.mixer_inputs(3850, T, Hk=Hk, Hv=Hv, conv_state_seqs=n_slots)
+    pool = (0.05 * np.random.default_rng(43).standard_normal((n_slots, Hv, 128, 128))).astype(np.float32)
+    slots = np.array([2, -1, 6, 4], dtype=np.int32)
+    keep = [0, 2, 3]
+    cu = synth.cu_from_lengths(lens)
+    x, w, z, nw = dev_bf16(mi.x), dev_bf16(mi.conv_w), dev_bf16(mi.z), dev_f32(mi.norm_w)
+    g, b = dev_f32(mi.g), dev_f32(mi.beta)
+    cs_pool, st_pool = dev_bf16(mi.conv_state), dev_f32(pool)
+    out1, _ = ops.gdn_mixer_fwd(x, w, g, b, z, nw, Hk=Hk, conv_state=cs_pool, initial_state=st_pool,
+                                state_slot=dev_i32(slots), cu_seqlens=dev_i32(cu))
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in keep])
+    ridx = torch.from_numpy(rows.astype(np.int64)).cuda()
+    cu2 = np.concatenate([[0], np.cumsum([lens[n] for n in keep])]).astype(np.int32)
+    cs_g, st_g = dev_bf16(mi.conv_state[slots[keep]]), dev_f32(pool[slots[keep]])
+    out2, hT = ops.gdn_mixer_fwd(x[ridx].contiguous(), w, g[ridx].contiguous(), b[ridx].contiguous(),
+                                 z[ridx].contiguous(), nw, Hk=Hk, conv_state=cs_g, initial_state=st_g,
+                                 cu_seqlens=dev_i32(cu2))
+    torch.cuda.synchronize()
+    assert torch.equal(out1[ridx], out2), "out (real sequences)"
+    idx = torch.from_numpy(slots[keep].astype(np.int64)).cuda()
+    assert torch.equal(st_pool[idx], hT) and torch.equal(cs_pool[idx], cs_g)
+    others = [i for i in range(n_slots) if i not in slots[keep]]
+    np.testing.assert_array_equal(host(st_pool)[others], pool[others])
+    assert torch.equal(cs_pool[others], dev_bf16(mi.conv_state)[others])
+
+
 def test_mixer_fwd_against_oracle():
     """The fused mixer against the oracle's conv -> recurrence -> gated norm,
     varlen with conv states, initial states and an empty sequence."""
