@@ -275,8 +275,10 @@ def leg_varlen(args, ops, synth, torch):
     return res
 
 
-# fp32 matrix-core products issued per (chunk of 64 tokens, value head) by the
-# chunked backward, 16x16x4 each (2,048 flops), masked blocks included:
+# matrix products per (chunk of 64 tokens, value head) of the chunked
+# backward, counted as fp32 16x16x4 products (2,048 flops each; the gradient
+# pass's products with S0 and dS_C run as split-bf16 16x16x32 products and are
+# counted by the fp32 work they stand for), masked blocks included:
 #   per-chunk pass   Q K^T, K K^T: 640 per key head = 640 / 3 per value head
 #   forward chain    K S0^T 128, T R 40, K^T (D U) 128 per 16-channel tile x 8
 #   reverse chain    K dS^T 128, P^T dO 40, T^T dU 40, the dS update 256, x 8

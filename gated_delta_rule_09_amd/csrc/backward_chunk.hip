@@ -37,8 +37,11 @@
 //                      dR, writing dv and dh0
 //   cb_grad            per (chunk, key head): dq, dk (summed over the value
 //                      heads in registers), dg, dbeta
-// All contractions run on v_mfma_f32_16x16x4_f32 with fp32 operands: the
-// gradients keep fp32 accuracy at any scale of dO.  In the chains every
+// The contractions run on v_mfma_f32_16x16x4_f32 with fp32 operands, except
+// the gradient pass's three products with S0 and dS_C (60 % of its work),
+// which take fp32 operands split into bf16 hi + lo parts on the bf16 units
+// (three products each, about 2^-17 relative error per product): either way
+// the gradients keep their accuracy at any scale of dO.  In the chains every
 // 64-token x 16-channel intermediate stays in the accumulator layout (lane l:
 // rows 4 (l / 16) + r, column l % 16) and enters the next product as its B
 // operand directly; the A operand then takes its k columns in the same order.
@@ -77,6 +80,39 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 }
 
 __device__ __forceinline__ float bf(uint16_t x) { return bf16_to_f32(x); }
+
+// Products on the bf16 matrix units with fp32-like accuracy: each fp32 operand
+// x is split as x = hi + lo, hi = x rounded to bf16 (nearest even), lo = the
+// remainder x - hi (exact in fp32) rounded to bf16, and a b is taken as
+// hi_a hi_b + hi_a lo_b + lo_a hi_b: the dropped lo_a lo_b and lo's rounding
+// leave a relative error of about 2^-17 per product, with fp32's exponent
+// range (the split needs no scaling at any magnitude of the data).
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {   // nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2v));
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8v& hi, bf16x8v& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = pk_bf16(x[2 * j], x[2 * j + 1]);
+    const float ra = x[2 * j] - __uint_as_float(h[j] << 16);
+    const float rb = x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u);
+    l[j] = pk_bf16(ra, rb);
+  }
+  hi = __builtin_bit_cast(bf16x8v, uint4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8v, uint4{l[0], l[1], l[2], l[3]});
+}
+// acc += a b over k = 32 (16 x 16 x 32: lane l gives A[l % 16][8 (l / 16) + j]
+// and B[8 (l / 16) + j][l % 16]; the result keeps the 16 x 16 x 4 layout)
+__device__ __forceinline__ floatx4 mfma_split(const bf16x8v ah, const bf16x8v al, const bf16x8v bh,
+                                              const bf16x8v bl, floatx4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+}
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
@@ -754,42 +790,68 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     floatx4 dqh[4], x1[4], dks[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) dqh[tb] = x1[tb] = dks[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float fq[4], fr[4], fu[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int i = tb * 16 + m;
-      fq[tb] = p.scale * sm.gam[i];
-      fr[tb] = -sm.gam[i] * sm.bet[i];
-      fu[tb] = sm.dec[i];
-    }
     const float* S0 = p.S0 + sh * (kD * kD) + d;
     const float* dSC = p.dSC + sh * (kD * kD) + d;
     float dss = 0.f;
-    // B operands 8 k-steps ahead (the last ones re-read row 127: never used)
-    constexpr int kAhead = 8;
-    float pb1[kAhead], pb2[kAhead];
+    // split-bf16 products over k-steps of 32 value channels: lane (m, g4)
+    // takes channels c = 32 ks + 8 g4 + j; its B operands (rows c of S0 and
+    // dS_C, column d) are loaded a k-step ahead.  The per-token scales are
+    // applied to the sums afterwards.
+    float nb1[8], nb2[8];
 #pragma unroll
-    for (int e = 0; e < kAhead; ++e) {
-      pb1[e] = S0[(4 * e + g4) * kD];
-      pb2[e] = dSC[(4 * e + g4) * kD];
+    for (int j = 0; j < 8; ++j) {
+      nb1[j] = S0[(8 * g4 + j) * kD];
+      nb2[j] = dSC[(8 * g4 + j) * kD];
     }
-#pragma unroll kAhead
-    for (int kk = 0; kk < kD / 4; ++kk) {
-      const int c = 4 * kk + g4;
-      const float b1 = pb1[kk % kAhead];
-      const float b2 = pb2[kk % kAhead];
-      const int cn = min(c + 4 * kAhead, kD - 1);
-      pb1[kk % kAhead] = S0[cn * kD];
-      pb2[kk % kAhead] = dSC[cn * kD];
-      dss = fmaf(b1, b2, dss);
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      float b1[8], b2[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        b1[j] = nb1[j];
+        b2[j] = nb2[j];
+      }
+      if (ks + 1 < kD / 32) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          nb1[j] = S0[(32 * (ks + 1) + 8 * g4 + j) * kD];
+          nb2[j] = dSC[(32 * (ks + 1) + 8 * g4 + j) * kD];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dss = fmaf(b1[j], b2[j], dss);
+      bf16x8v b1h, b1l, b2h, b2l;
+      split8(b1, b1h, b1l);
+      split8(b2, b2h, b2l);
+      const int c0 = 32 * ks + 8 * g4;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int i = tb * 16 + m;
-        dqh[tb] = mfma4(fq[tb] * sm.u.in.dO[i][c], b1, dqh[tb]);
-        x1[tb] = mfma4(fr[tb] * sm.u.in.dR[i][c], b1, x1[tb]);
-        dks[tb] = mfma4(fu[tb] * sm.u.in.U[i][c], b2, dks[tb]);
+        float a[8];
+        bf16x8v ah, al;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.dO[i][c0 + j];
+        split8(a, ah, al);
+        dqh[tb] = mfma_split(ah, al, b1h, b1l, dqh[tb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.dR[i][c0 + j];
+        split8(a, ah, al);
+        x1[tb] = mfma_split(ah, al, b1h, b1l, x1[tb]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.U[i][c0 + j];
+        split8(a, ah, al);
+        dks[tb] = mfma_split(ah, al, b2h, b2l, dks[tb]);
       }
     }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = tb * 16 + 4 * g4 + r;
+        dqh[tb][r] *= p.scale * sm.gam[i];
+        x1[tb][r] *= -sm.gam[i] * sm.bet[i];
+        dks[tb][r] *= sm.dec[i];
+      }
     dss = wave_sum(dss);
     if (lane == 0) sm.dss[w] = dss;
     // k . dKS per token now, and dKS into dk: it is not needed again
