@@ -54,6 +54,8 @@ SPILL_MARKERS = ("Reload Reuse", "Spill", "Reload")
 
 
 _MFMA = re.compile(r"\s*(v_mfma_\w+)\s+([av]\[\d+:\d+\]),\s*[^,]+,\s*[^,]+,\s*([av]\[\d+:\d+\])")
+# any MFMA's destination, also with an immediate accumulator input (0)
+_MFMA_DEST = re.compile(r"\s*(v_mfma_\w+)\s+([av]\[\d+:\d+\])")
 _DEST = re.compile(r"\s*(v_\w+)\s+([av](?:\d+|\[\d+:\d+\]))")
 
 
@@ -78,7 +80,7 @@ def mixed_mfma_chains(lines, window: int = 24) -> list:
             prev = lines[j].split(";", 1)[0]
             if re.match(r"\s*(\.L|s_cbranch|s_branch|s_setpc)", prev):
                 break
-            pm = _MFMA.match(prev)
+            pm = _MFMA_DEST.match(prev)
             if pm and _regs(pm.group(2)) & srcc:
                 if pm.group(1) != op:
                     found.append(f"{prev.strip()}  ->  {ln.strip()}")

@@ -37,11 +37,15 @@
 //                      dR, writing dv and dh0
 //   cb_grad            per (chunk, key head): dq, dk (summed over the value
 //                      heads in registers), dg, dbeta
-// The contractions run on v_mfma_f32_16x16x4_f32 with fp32 operands, except
-// the gradient pass's three products with S0 and dS_C (60 % of its work),
-// which take fp32 operands split into bf16 hi + lo parts on the bf16 units
-// (three products each, about 2^-17 relative error per product): either way
-// the gradients keep their accuracy at any scale of dO.  In the chains every
+// The large contractions run on the bf16 matrix units with fp32 operands
+// split into bf16 hi + lo parts (about 2^-17 relative error per product,
+// fp32's exponent range): in the chains K S0^T, K dS^T and the state (and
+// state-gradient) updates, whose K and Q operands are bf16 already (two
+// products each), and in the gradient pass the three products with S0 and
+// dS_C (three products each).  The rest (the triangular solves, P^T dO, the
+// gradient pass's other products) run on v_mfma_f32_16x16x4_f32 with fp32
+// operands.  Either way the gradients keep their accuracy at any scale of
+// dO.  In the chains every
 // 64-token x 16-channel intermediate stays in the accumulator layout (lane l:
 // rows 4 (l / 16) + r, column l % 16) and enters the next product as its B
 // operand directly; the A operand then takes its k columns in the same order.
@@ -131,6 +135,38 @@ __device__ __forceinline__ floatx4 col4(const uint16_t (*rows)[kKS], int r0, int
                  bf(static_cast<uint16_t>(v[2])), bf(static_cast<uint16_t>(v[3]))};
 }
 
+// Split-bf16 operands of the chains' 16 x 16 x 32 products.  The reduction
+// index of slot (lane group g, element e) is kappa(g, e) = 4 g + e for e < 4
+// and 16 + 4 g + (e - 4) otherwise, so that two vertically adjacent
+// accumulator tiles (rows 4 g + r of tile a, then of tile b) are a B operand
+// over those 32 rows as they stand.  K and Q are bf16 already: as A operands
+// they need no split, and a product takes two passes (a hi', a lo').
+__device__ __forceinline__ void split_pair(const floatx4 a, const floatx4 b, bf16x8v& hi, bf16x8v& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  split8(x, hi, lo);
+}
+// row `row` of a staged matrix, reduction indices c0 + kappa(g4, e)
+__device__ __forceinline__ bf16x8v row8(const uint16_t (*rows)[kKS], int row, int c0, int g4) {
+  const uint2 a = *reinterpret_cast<const uint2*>(&rows[row][c0 + 4 * g4]);
+  const uint2 b = *reinterpret_cast<const uint2*>(&rows[row][c0 + 16 + 4 * g4]);
+  return __builtin_bit_cast(bf16x8v, uint4{a.x, a.y, b.x, b.y});
+}
+// column c0 + (lane % 16) of a staged matrix, rows r0 + kappa(lane / 16, e):
+// two transposing reads
+__device__ __forceinline__ bf16x8v col8(const uint16_t (*rows)[kKS], int r0, int c0) {
+  const int j = threadIdx.x & 15;
+  const int g4 = (threadIdx.x >> 4) & 3;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(&rows[r0 + 4 * g4 + (j >> 2)][c0 + 4 * (j & 3)]));
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(&rows[r0 + 16 + 4 * g4 + (j >> 2)][c0 + 4 * (j & 3)]));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return __builtin_bit_cast(bf16x8v, uint4{ua.x, ua.y, ub.x, ub.y});
+}
+__device__ __forceinline__ floatx4 mfma_bf(const bf16x8v a, const bf16x8v b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ void cb_seq(const CbParams& p, int n, int& s0, int& s1) {
   if (p.cu) { s0 = p.cu[n]; s1 = p.cu[n + 1]; }
   else { s0 = n * p.seq_len; s1 = s0 + p.seq_len; }
@@ -154,8 +190,7 @@ __device__ __forceinline__ bool slot_chunk(const CbParams& p, int slot, SlotChun
 }
 
 // inclusive prefix sum over the 64 lanes, in lane order
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ float wave_prefix_sum(float x, int lane = threadIdx.x & 63) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const float y = __shfl_up(x, d, 64);
@@ -341,8 +376,8 @@ struct ChainNext {
 
 template <bool kWithQ>
 __device__ __forceinline__ void chain_load(const CbParams& p, int t0, int len, int h, int kh,
-                                           int64_t sh, ChainNext<kWithQ>& f) {
-  const int tid = threadIdx.x;
+                                           int64_t sh, ChainNext<kWithQ>& f,
+                                           int tid = threadIdx.x) {
   const int lane = tid & 63;
   const int row = tid >> 2;                   // K / Q: 32 halves, X: 16 floats per thread
   const bool ok = row < len;
@@ -368,8 +403,8 @@ __device__ __forceinline__ void chain_load(const CbParams& p, int t0, int len, i
 template <bool kWithQ>
 // (the rows and gates past the chunk's end, loaded from its last token, are
 // zeroed here rather than at the load, where the choice would wait for them)
-__device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& sm) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& sm,
+                                          int tid = threadIdx.x) {
   const int row = tid >> 2;
   const uint32_t keep = row < f.len ? 0xffffffffu : 0u;   // a value mask, not a choice of objects
 #pragma unroll
@@ -387,7 +422,7 @@ __device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& 
   if ((tid >> 6) == 0) {
     const int lane = tid & 63;
     const bool gok = lane < f.len;
-    const float G = wave_prefix_sum(gok ? f.g : 0.f);
+    const float G = wave_prefix_sum(gok ? f.g : 0.f, lane);
     const float GL = __shfl(G, 63, 64);
     sm.gam[lane] = expf(G);
     sm.dec[lane] = expf(GL - G);
@@ -430,6 +465,10 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
   }
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
+    // the thread id again from an opaque copy: the prefetch's and LDS writes'
+    // lane arithmetic is then redone per chunk, not held in registers
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
     const int t0 = s0 + kC * c;
     const int len = min(kC, s1 - t0);
     const int slot = cb_slot(s0, c, n);
@@ -444,25 +483,26 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
         vv[tb][r] = bf(p.v[static_cast<int64_t>(t0 + min(tok, len - 1)) * p.vs + h * kD + ch]);
       }
     if (c + 1 < nc)
-      chain_load(p, t0 + kC, min(kC, s1 - t0 - kC), h, kh, static_cast<int64_t>(slot + 1) * p.Hv + h, nx);
+      chain_load(p, t0 + kC, min(kC, s1 - t0 - kC), h, kh, static_cast<int64_t>(slot + 1) * p.Hv + h, nx, tid_c);
 
     // the state before the chunk
     float* S0 = p.S0 + (sh * kD + ch) * kD + 4 * g4;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(S0 + 16 * db) = s[db];
 
-    // Z = K S0^T (tokens x channels)
+    // Z = K S0^T (tokens x channels): split-bf16, 32 state rows a step
     floatx4 z[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 4; ++tb) z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint2 kx = *reinterpret_cast<const uint2*>(&sm.k[tb * 16 + m][db * 16 + 4 * g4]);
-        z[tb] = mfma4(bf(kx.x & 0xffff), s[db][0], z[tb]);
-        z[tb] = mfma4(bf(kx.x >> 16), s[db][1], z[tb]);
-        z[tb] = mfma4(bf(kx.y & 0xffff), s[db][2], z[tb]);
-        z[tb] = mfma4(bf(kx.y >> 16), s[db][3], z[tb]);
+    for (int kp = 0; kp < 4; ++kp) {
+      bf16x8v bh, bl;
+      split_pair(s[2 * kp], s[2 * kp + 1], bh, bl);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const bf16x8v ka = row8(sm.k, tb * 16 + m, 32 * kp, g4);
+        z[tb] = mfma_bf(ka, bh, z[tb]);
+        z[tb] = mfma_bf(ka, bl, z[tb]);
       }
     }
     // E = V - gamma Z, R = b E  (token tb*16 + 4 g4 + r, channel ch)
@@ -504,22 +544,25 @@ __device__ __forceinline__ void fwd_chain(const CbParams& p, ChainLds& sm, int b
         DU[ib][r] = sm.dec[tok] * u[r];
       }
     }
-    // S^T <- gamma_last S^T + K^T (D U)
+    // S^T <- gamma_last S^T + K^T (D U): split-bf16, 32 tokens a step
     const float gl = sm.gam[kC - 1];
+    bf16x8v duh[2], dul[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) split_pair(DU[2 * kp], DU[2 * kp + 1], duh[kp], dul[kp]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       floatx4 acc = s[db] * gl;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const floatx4 kt = col4(sm.k, jb * 16 + 4 * g4, db * 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc = mfma4(kt[r], DU[jb][r], acc);
+      for (int kp = 0; kp < 2; ++kp) {
+        const bf16x8v kt = col8(sm.k, 32 * kp, db * 16);
+        acc = mfma_bf(kt, duh[kp], acc);
+        acc = mfma_bf(kt, dul[kp], acc);
       }
       s[db] = acc;
     }
     __syncthreads();   // every wave is done with this chunk's LDS
     if (c + 1 < nc) {
-      chain_put(nx, sm);
+      chain_put(nx, sm, tid_c);
       __syncthreads();
     }
   }
@@ -558,6 +601,8 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
   }
   __syncthreads();
   for (int c = nc - 1; c >= 0; --c) {
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
     const int t0 = s0 + kC * c;
     const int len = min(kC, s1 - t0);
     const int slot = cb_slot(s0, c, n);
@@ -572,25 +617,26 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
         dO[tb][r] = p.d_o[(static_cast<int64_t>(t0 + min(tok, len - 1)) * p.Hv + h) * kD + ch];
       }
     // the previous chunk's inputs, written to LDS after this one
-    if (c > 0) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx);
+    if (c > 0) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx, tid_c);
 
     // the gradient of the state after the chunk
     float* dSC = p.dSC + (sh * kD + ch) * kD + 4 * g4;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(dSC + 16 * db) = ds[db];
 
-    // Z = K dS^T
+    // Z = K dS^T: split-bf16, 32 state rows a step
     floatx4 z[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < 4; ++tb) z[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint2 kx = *reinterpret_cast<const uint2*>(&sm.k[tb * 16 + m][db * 16 + 4 * g4]);
-        z[tb] = mfma4(bf(kx.x & 0xffff), ds[db][0], z[tb]);
-        z[tb] = mfma4(bf(kx.x >> 16), ds[db][1], z[tb]);
-        z[tb] = mfma4(bf(kx.y & 0xffff), ds[db][2], z[tb]);
-        z[tb] = mfma4(bf(kx.y >> 16), ds[db][3], z[tb]);
+    for (int kp = 0; kp < 4; ++kp) {
+      bf16x8v bh, bl;
+      split_pair(ds[2 * kp], ds[2 * kp + 1], bh, bl);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const bf16x8v ka = row8(sm.k, tb * 16 + m, 32 * kp, g4);
+        z[tb] = mfma_bf(ka, bh, z[tb]);
+        z[tb] = mfma_bf(ka, bl, z[tb]);
       }
     }
     // dU = scale P^T dO + D Z;  (P^T)_ij = P_ji = X_ij for j > i, X_ii on the diagonal
@@ -645,31 +691,40 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
         dO[jb][r] *= p.scale * sm.gam[tok];
         dR[jb][r] *= -sm.bet[tok] * sm.gam[tok];
       }
+    // split-bf16, 32 tokens a step (the step's split operands, then every
+    // row block of dS^T)
     const float gl = sm.gam[kC - 1];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      floatx4 acc = ds[db] * gl;
+    for (int db = 0; db < 8; ++db) ds[db] *= gl;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const floatx4 qt = col4(sm.q, jb * 16 + 4 * g4, db * 16);
-        const floatx4 kt = col4(sm.k, jb * 16 + 4 * g4, db * 16);
+    for (int kp = 0; kp < 2; ++kp) {
+      bf16x8v doh, dol, drh, drl;
+      split_pair(dO[2 * kp], dO[2 * kp + 1], doh, dol);
+      split_pair(dR[2 * kp], dR[2 * kp + 1], drh, drl);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc = mfma4(qt[r], dO[jb][r], acc);
-          acc = mfma4(kt[r], dR[jb][r], acc);
-        }
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8v qt = col8(sm.q, 32 * kp, db * 16);
+        const bf16x8v kt = col8(sm.k, 32 * kp, db * 16);
+        ds[db] = mfma_bf(qt, doh, ds[db]);
+        ds[db] = mfma_bf(qt, dol, ds[db]);
+        ds[db] = mfma_bf(kt, drh, ds[db]);
+        ds[db] = mfma_bf(kt, drl, ds[db]);
       }
-      ds[db] = acc;
     }
     __syncthreads();   // every wave is done with this chunk's LDS
     if (c > 0) {
-      chain_put(nx, sm);
+      chain_put(nx, sm, tid_c);
       __syncthreads();
     }
   }
   if (p.dh0) {
+    // the row offset again from an opaque thread id, not held through the loop
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    const int ch_e = (4 * half + (tid_e >> 6)) * 16 + (tid_e & 15);
+    const int64_t hrow_e = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch_e) * kD + 4 * ((tid_e >> 4) & 3);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(p.dh0 + hrow + 16 * db) = ds[db];
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(p.dh0 + hrow_e + 16 * db) = ds[db];
   }
 }
 

@@ -448,10 +448,10 @@ gdn_status gdn_gated_rmsnorm(const float* o, const uint16_t* z, int64_t z_row_st
  * respect to q, k, v, g, beta and the initial states.  The chain rule is
  * taken through the chunk-parallel form of the erase-then-write update (the
  * deep-dive page's paragraph on the Gated Delta Rule), chunks of 64 tokens,
- * in fp32 (fp32 matrix-core products, and for the products with the recorded
- * states fp32 operands split into bf16 hi + lo parts, about 17 significant
- * bits per product; the gradients keep their relative accuracy whatever the
- * scale of grad_o): a per-chunk pass forms
+ * in fp32 (fp32 matrix-core products, and for the products with the states
+ * and their gradients fp32 operands split into bf16 hi + lo parts, about 17
+ * significant bits per product; the gradients keep their relative accuracy
+ * whatever the scale of grad_o): a per-chunk pass forms
  * (I + A)^-1 and the masked Q K^T of every (chunk, value head), a forward
  * chain records each chunk's initial state and its U, E, a reverse chain
  * carries dL/dS through the chunks and records it, and a per-(chunk, key

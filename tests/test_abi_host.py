@@ -370,3 +370,20 @@ def test_backward_chunk_slots_fit_the_workspace():
                  for c in range((int(lens[n]) + 63) // 64)]
         assert len(set(slots)) == len(slots)
         assert all(0 <= s < T // 64 + N for s in slots)
+
+
+def test_build_flags_mixed_shape_mfma_accumulator_chains():
+    """The build's assembly check: an MFMA whose accumulator input is the
+    result of an MFMA of another shape a few instructions earlier is
+    reported; a result rewritten in between (an LDS read, an MFMA of the same
+    shape, also one with an immediate zero accumulator) is not."""
+    from gated_delta_rule_09_amd import build as B
+    bad = ["\tv_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], v[0:3]",
+           "\tv_add_f32_e32 v20, v21, v22",
+           "\tv_mfma_f32_16x16x16_f16 v[0:3], v[4:5], v[8:9], v[0:3]"]
+    assert len(B.mixed_mfma_chains(bad)) == 1
+    ok = ["\tv_mfma_f32_16x16x4_f32 v[110:113], v84, v238, v[102:105]",
+          "\tds_read2_b64 v[108:111], v149 offset0:32 offset1:36",
+          "\tv_mfma_f32_16x16x32_bf16 v[112:115], v[108:111], v[94:97], 0",
+          "\tv_mfma_f32_16x16x32_bf16 v[108:111], v[108:111], v[100:103], v[112:115]"]
+    assert B.mixed_mfma_chains(ok) == []
