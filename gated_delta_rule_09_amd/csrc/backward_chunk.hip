@@ -77,6 +77,11 @@ struct CbParams {
   float* dSC;                 // [n_slots][Hv][128][128]: dL/dS after the chunk
   float* U; float* E; float* dR;   // [n_slots][Hv][64][128]
   float* dq; float* dk; float* dv; float* dg; float* dbeta; float* dh0;
+  // part 0: every chunk.  Parts 1 and 2: the chunks of each sequence from
+  // mid = nc / 2 on, and those before it.  The gradient chain's part 1 leaves
+  // the state gradient after chunk mid - 1 in that chunk's dSC slot, where
+  // part 2 takes it up; the gradient pass of a part does that part's chunks.
+  int part;
 };
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
@@ -586,21 +591,33 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
   int s0, s1;
   cb_seq(p, n, s0, s1);
   const int nc = (s1 - s0 + kC - 1) / kC;
+  const int mid = nc / 2;
+  const int c_top = p.part == 2 ? mid : nc;     // chunks c_top - 1 .. c_lo
+  const int c_lo = p.part == 1 ? mid : 0;
+  if (p.part == 2 && c_top == 0) return;        // no lower part (the whole work-group)
 
   floatx4 ds[8];
-  const int64_t hrow = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch) * kD + 4 * g4;
+  if (c_top == nc) {
+    const int64_t hrow = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch) * kD + 4 * g4;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    ds[db] = p.dhT ? *reinterpret_cast<const floatx4*>(p.dhT + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 8; ++db)
+      ds[db] = p.dhT ? *reinterpret_cast<const floatx4*>(p.dhT + hrow + 16 * db) : floatx4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    // left by the part above in the slot of chunk c_top - 1
+    const int64_t sh = static_cast<int64_t>(cb_slot(s0, c_top - 1, n)) * p.Hv + h;
+    const float* src = p.dSC + (sh * kD + ch) * kD + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ds[db] = *reinterpret_cast<const floatx4*>(src + 16 * db);
+  }
 
   ChainNext<true> nx;
-  if (nc > 0) {
-    const int tl = s0 + kC * (nc - 1);
-    chain_load(p, tl, s1 - tl, h, kh, static_cast<int64_t>(cb_slot(s0, nc - 1, n)) * p.Hv + h, nx);
+  if (c_top > c_lo) {
+    const int tl = s0 + kC * (c_top - 1);
+    chain_load(p, tl, min(kC, s1 - tl), h, kh, static_cast<int64_t>(cb_slot(s0, c_top - 1, n)) * p.Hv + h, nx);
     chain_put(nx, sm);
   }
   __syncthreads();
-  for (int c = nc - 1; c >= 0; --c) {
+  for (int c = c_top - 1; c >= c_lo; --c) {
     int tid_c = tid;
     asm volatile("" : "+v"(tid_c));
     const int t0 = s0 + kC * c;
@@ -617,7 +634,7 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
         dO[tb][r] = p.d_o[(static_cast<int64_t>(t0 + min(tok, len - 1)) * p.Hv + h) * kD + ch];
       }
     // the previous chunk's inputs, written to LDS after this one
-    if (c > 0) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx, tid_c);
+    if (c > c_lo) chain_load(p, t0 - kC, kC, h, kh, static_cast<int64_t>(slot - 1) * p.Hv + h, nx, tid_c);
 
     // the gradient of the state after the chunk
     float* dSC = p.dSC + (sh * kD + ch) * kD + 4 * g4;
@@ -712,16 +729,22 @@ __device__ __forceinline__ void bwd_chain(const CbParams& p, ChainLds& sm, int b
       }
     }
     __syncthreads();   // every wave is done with this chunk's LDS
-    if (c > 0) {
+    if (c > c_lo) {
       chain_put(nx, sm, tid_c);
       __syncthreads();
     }
   }
-  if (p.dh0) {
-    // the row offset again from an opaque thread id, not held through the loop
-    int tid_e = tid;
-    asm volatile("" : "+v"(tid_e));
-    const int ch_e = (4 * half + (tid_e >> 6)) * 16 + (tid_e & 15);
+  // the row offset again from an opaque thread id, not held through the loop
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int ch_e = (4 * half + (tid_e >> 6)) * 16 + (tid_e & 15);
+  if (c_lo > 0) {
+    // the gradient of the state after chunk c_lo - 1, for the part below
+    const int64_t sh = static_cast<int64_t>(cb_slot(s0, c_lo - 1, n)) * p.Hv + h;
+    float* dst = p.dSC + (sh * kD + ch_e) * kD + 4 * ((tid_e >> 4) & 3);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db) = ds[db];
+  } else if (p.dh0) {
     const int64_t hrow_e = ((static_cast<int64_t>(n) * p.Hv + h) * kD + ch_e) * kD + 4 * ((tid_e >> 4) & 3);
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<floatx4*>(p.dh0 + hrow_e + 16 * db) = ds[db];
@@ -764,6 +787,13 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
   const int kh = blockIdx.x - slot * p.Hk;
   SlotChunk sc;
   if (!slot_chunk(p, slot, sc)) return;
+  if (p.part) {
+    // this part's chunks only: from the sequence's mid = nc / 2 on (1), before it (2)
+    int s0, s1;
+    cb_seq(p, sc.n, s0, s1);
+    const int c = (sc.t0 - s0) / kC;
+    if ((p.part == 1) != (c >= ((s1 - s0 + kC - 1) / kC) / 2)) return;
+  }
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
@@ -1102,6 +1132,7 @@ hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t
   p.E = reinterpret_cast<float*>(base); base += up(sh * kC * kD * 4);
   p.dR = reinterpret_cast<float*>(base);
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta; p.dh0 = dh0;
+  p.part = 0;
 
   const unsigned chains = static_cast<unsigned>(n_seqs) * static_cast<unsigned>(Hv) * 2u;
   if (T_total > 0) {
@@ -1117,6 +1148,33 @@ hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t
       hipError_t e = hipEventRecord(ov->start, stream);
       if (e == hipSuccess) e = hipStreamWaitEvent(ov->side, ov->start, 0);
       if (e != hipSuccess) return e;
+      // Long sequences whose chains leave compute units idle: the gradient
+      // chain in two parts, and the gradient pass over the upper half of each
+      // sequence's chunks (done by the first part and by the state chain,
+      // which ends first) runs beside the second part.
+      if (T_total / n_seqs >= 32 * kC && 4 * n_seqs * Hv <= compute_units()) {
+        CbParams ph = p, pl = p;
+        ph.part = 1;
+        pl.part = 2;
+        hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, ov->side, ph);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(ov->done[0], ov->side);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, ov->side, pl);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(ov->done[1], ov->side);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, ov->done[0], 0);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(cb_grad_kernel, dim3(per_chunk), dim3(512), 0, stream, ph);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, ov->done[1], 0);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(cb_grad_kernel, dim3(per_chunk), dim3(512), 0, stream, pl);
+        return hipGetLastError();
+      }
       hipLaunchKernelGGL(cb_bwd_kernel, dim3(chains), dim3(256), 0, ov->side, p);
       hipLaunchKernelGGL(cb_fwd_kernel, dim3(chains), dim3(256), 0, stream, p);
       e = hipGetLastError();

@@ -1319,6 +1319,8 @@ hipError_t launch_scan(const ScanParams& sp, int blocks, size_t lds, bool conv, 
   return hipGetLastError();
 }
 
+}  // namespace
+
 // Compute units of the current device, looked up once per device (calls from
 // several host threads may race to fill an entry; they store the same value).
 int compute_units() {
@@ -1332,8 +1334,6 @@ int compute_units() {
   }
   return n;
 }
-
-}  // namespace
 
 Overlap* overlap_of_current_device() {
   static Overlap ov[64];

@@ -44,6 +44,9 @@ struct Overlap {
 };
 Overlap* overlap_of_current_device();
 
+// Compute units of the current device (256 if the query fails).
+int compute_units();
+
 // Workspace of the chunked prefill (each piece 256-byte aligned):
 //   order [n_seqs] | chunk_off [n_seqs+1] | chunk_tab [max_chunks][3]
 //   | K rows + Q fragments [max_chunks][Hk] | per-value-head fragments [max_chunks][Hv]

@@ -107,6 +107,28 @@ def test_backward_long_chain():
     _check(got, ref, "1000 tokens")
 
 
+@pytest.mark.parametrize("lens,Hk,Hv,varlen", [([2100], 2, 4, False), ([2048, 2048], 1, 3, False),
+                                               ([4500, 30, 0, 3700], 1, 2, True)])
+def test_backward_long_sequences_in_two_parts(lens, Hk, Hv, varlen):
+    """Long sequences (2,048 tokens or more on average) whose chains leave
+    compute units idle: the gradient chain runs in two parts, each
+    sequence's chunks from nc / 2 on and then those before, the upper half's
+    gradient pass beside the second part, the state gradient handed over
+    through the first part's last chunk slot.  One sequence of 33 chunks (the
+    last partial), two of 32 without cu_seqlens, and a varlen batch with a
+    one-chunk and an empty sequence; against the oracle."""
+    T, N = sum(lens), len(lens)
+    log(f"backward in two parts: lengths {lens}, Hk {Hk}, Hv {Hv}, varlen {varlen}")
+    ci = synth.chunk_inputs(7950 + N, T, Hk=Hk, Hv=Hv, lengths=lens, h0_std=0.05)
+    if not varlen:
+        ci.cu_seqlens = None      # equal split without cu_seqlens
+    bs = synth.backward_seeds(7960 + N, T, N, Hv=Hv)
+    got, ref = _run(ci, bs, 128 ** -0.5, Hk)
+    _check(got, ref, f"{N} sequences of {lens}")
+    if varlen:
+        assert np.all(got["dh0"][2] == ref["dh0"][2])   # the empty sequence passes dS_T through
+
+
 @pytest.mark.parametrize("n_seqs", [2, 12, 65])
 def test_backward_many_short_sequences(n_seqs):
     """2, 12 and 65 sequences of 1-11 tokens at 48 value heads (one chunk
