@@ -16,8 +16,11 @@ resident in HBM.  The same run also times, as extra legs in the same JSON line:
   backward  gdn_backward (the rule's gradients) on 8 x 1024 and 1 x 8192 tokens.
   latency   the core recurrence at T = 512 (zero state): median and min of
           single launches;
-  ceilings  what this device sustains: a 1 GiB device copy and a dense
-          fp16 MFMA loop (gdn_calib_mfma_loop), beside the published peaks.
+  ceilings  what this device sustains: a 1 GiB device copy, a streaming
+          in-place pass over the decode step's 805 MB of states
+          (gdn_calib_stream_inplace: each piece read and written back once)
+          and a dense fp16 MFMA loop (gdn_calib_mfma_loop), beside the
+          published peaks.
 Two more prefill timings, not the headline: o written in bf16
 (`prefill_bf16_o`) and the gates formed from bf16 projections (`prefill_gated`).
 `roofline` covers the prefill launch (one `gdn_chunk_fwd`: the parallel prep
@@ -58,6 +61,7 @@ FLOP_PER_TOKEN = HK * 2 * D * C + HV * (3 * D * (C + 1) + 6 * D * D)      # 6,17
 # bytes per token: q, k, v bf16; g, beta fp32; o fp32
 BYTES_PER_TOKEN = HK * D * 2 * 2 + HV * D * 2 + HV * 4 * 2 + HV * D * 4   # 45,440
 STATE_BYTES = HV * D * D * 4                                              # 3,145,728
+DECODE_N = 256                                                            # sequences of the decode leg
 
 
 def log(*a):
@@ -140,7 +144,7 @@ def leg_prefill(args, ops, synth, torch):
 
 
 def leg_decode(args, ops, synth, torch):
-    N = 256
+    N = DECODE_N
     log(f"[decode] drawing inputs N={N}")
     di = synth.decode_inputs_torch(1003, N)
     o = torch.empty((N, HV, D), dtype=torch.float32, device="cuda")
@@ -374,9 +378,17 @@ def leg_ceilings(args, ops, torch):
     flops = ops.gdn_calib_mfma_loop(n_iter, n_blocks, out)[1]
     ev, _ = time_leg(lambda: ops.gdn_calib_mfma_loop(n_iter, n_blocks, out), 5, 2)
     tflops = flops / (ev * 1e-3) / 1e12
+    # the decode step's states, streamed in place (4 work-groups per CU)
+    buf = torch.zeros(DECODE_N * STATE_BYTES // 4, dtype=torch.float32, device="cuda")
+    sbytes = ops.gdn_calib_stream_inplace(buf, 4 * cus)
+    sev, _ = time_leg(lambda: ops.gdn_calib_stream_inplace(buf, 4 * cus), 10, 3)
+    del buf
+    sgbps = sbytes / (sev * 1e-3) / 1e9
     log(f"[ceilings] copy {cp['bytes'] / (cp['event_ms'] * 1e-3) / 1e9:.0f} GB/s; "
+        f"streaming in place {sgbps:.0f} GB/s ({sbytes / 2e6:.0f} MB); "
         f"MFMA loop {tflops:.0f} TFLOP/s ({n_blocks} x 4 waves x {n_iter} x 8 products)")
     return dict(copy_gbps=cp["bytes"] / (cp["event_ms"] * 1e-3) / 1e9, copy_event_ms=cp["event_ms"],
+                stream_gbps=sgbps, stream_event_ms=sev,
                 mfma_tflops=tflops, mfma_event_ms=ev, mfma_blocks=n_blocks, mfma_iters=n_iter)
 
 
@@ -532,6 +544,8 @@ def main():
         ce = out["ceilings"]
         line["ceilings"] = {"copy_GBps": round(ce["copy_gbps"], 1),
                             "copy_frac_of_peak": round(ce["copy_gbps"] / HBM_PEAK_GBPS, 4),
+                            "stream_inplace_GBps": round(ce["stream_gbps"], 1),
+                            "stream_inplace_frac_of_peak": round(ce["stream_gbps"] / HBM_PEAK_GBPS, 4),
                             "mfma_loop_TFLOPs": round(ce["mfma_tflops"], 1),
                             "mfma_loop_frac_of_peak": round(ce["mfma_tflops"] / MFMA_PEAK_TFLOPS, 4)}
     if "decode" in out:

@@ -739,6 +739,16 @@ gdn_status gdn_calib_mfma_loop(int32_t n_iter, int32_t n_blocks, float* out, voi
                     "gdn_calib_mfma_loop launch");
 }
 
+gdn_status gdn_calib_stream_inplace(void* buf, int64_t bytes, int32_t n_blocks, void* stream) {
+  if (!buf) return fail(GDN_ERR_NULL, "gdn_calib_stream_inplace: buf is NULL");
+  if (bytes <= 0 || bytes % 16 || n_blocks <= 0 || n_blocks > (1 << 20))
+    return fail(GDN_ERR_SHAPE, "gdn_calib_stream_inplace: bytes %lld (a positive multiple of 16) "
+                "and n_blocks %d (1 .. 2^20)", static_cast<long long>(bytes), n_blocks);
+  if (!aligned(buf, 16)) return fail(GDN_ERR_SHAPE, "gdn_calib_stream_inplace: buf misaligned");
+  return hip_status(gdn::launch_stream_inplace(buf, bytes, n_blocks, static_cast<hipStream_t>(stream)),
+                    "gdn_calib_stream_inplace launch");
+}
+
 size_t gdn_backward_workspace_bytes(int32_t n_seqs, int32_t T_total, int32_t Hv) {
   if (n_seqs <= 0 || T_total <= 0 || Hv <= 0) return 0;
   return gdn::chunked_backward_workspace_bytes(n_seqs, T_total, Hv);

@@ -137,5 +137,8 @@ hipError_t launch_backward_chunked(const uint16_t* q, int64_t qs, const uint16_t
 double mfma_loop_flops(int n_iter, int n_blocks);
 int mfma_loop_waves(int n_blocks);
 hipError_t launch_mfma_loop(int n_iter, int n_blocks, float* out, hipStream_t stream);
+// Streaming pass (calib.hip): every 16-byte piece of buf read and written back
+// unchanged, nontemporally, by n_blocks work-groups of 256 threads.
+hipError_t launch_stream_inplace(void* buf, int64_t bytes, int n_blocks, hipStream_t stream);
 
 }  // namespace gdn

@@ -57,6 +57,7 @@ _SIGS = {
     "gdn_validate_cu_seqlens": (_i32, [_vp, _i32, _i32, _vp]),
     "gdn_calib_mfma_loop_flops": (_c.c_double, [_i32, _i32]),
     "gdn_calib_mfma_loop": (_i32, [_i32, _i32, _vp, _vp]),
+    "gdn_calib_stream_inplace": (_i32, [_vp, _i64, _i32, _vp]),
     "gdn_backward_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "gdn_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                             _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -642,6 +643,18 @@ def gdn_calib_mfma_loop(n_iter: int, n_blocks: int,
     h = lib()
     _check(h.gdn_calib_mfma_loop(n_iter, n_blocks, _ptr(out), _stream()), "gdn_calib_mfma_loop")
     return out, float(h.gdn_calib_mfma_loop_flops(n_iter, n_blocks))
+
+
+def gdn_calib_stream_inplace(buf: torch.Tensor, n_blocks: int) -> int:
+    """The streaming pass (a measurement aid): every 16-byte piece of the
+    contiguous CUDA tensor buf read and written back unchanged; returns the
+    HBM bytes of the launch (twice buf's size)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().gdn_calib_stream_inplace(_ptr(buf), nbytes, n_blocks, _stream()),
+           "gdn_calib_stream_inplace")
+    return 2 * nbytes
 
 
 def gdn_backward_workspace_bytes(n_seqs: int, T_total: int, Hv: int) -> int:

@@ -509,6 +509,17 @@ gdn_status gdn_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, in
 double gdn_calib_mfma_loop_flops(int32_t n_iter, int32_t n_blocks);
 gdn_status gdn_calib_mfma_loop(int32_t n_iter, int32_t n_blocks, float* out, void* stream);
 
+/*
+ * gdn_calib_stream_inplace -- a measurement aid, not part of the rule: the
+ * HBM ceiling of the decode step's traffic pattern on the running device.
+ * Every 16-byte piece of buf [bytes] is read and written back unchanged with
+ * nontemporal accesses by n_blocks work-groups of 256 threads (grid-stride),
+ * so 2 * bytes cross HBM per launch; divide by the launch time.  bytes a
+ * positive multiple of 16, buf 16-byte aligned, 1 <= n_blocks <= 2^20;
+ * GDN_ERR_SHAPE / GDN_ERR_NULL otherwise.  The contents are left as they were.
+ */
+gdn_status gdn_calib_stream_inplace(void* buf, int64_t bytes, int32_t n_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

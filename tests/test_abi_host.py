@@ -100,6 +100,15 @@ def test_calib_mfma_loop_validation(lib):
     assert lib.gdn_calib_mfma_loop_flops(0, 4) == 0.0
 
 
+def test_calib_stream_inplace_validation(lib):
+    assert lib.gdn_calib_stream_inplace(None, 1024, 4, None) == NULL
+    assert lib.gdn_calib_stream_inplace(P(0), 0, 4, None) == SHAPE
+    assert lib.gdn_calib_stream_inplace(P(0), 1000, 4, None) == SHAPE      # not a multiple of 16
+    assert lib.gdn_calib_stream_inplace(P(0), 1024, 0, None) == SHAPE
+    assert lib.gdn_calib_stream_inplace(P(0), 1024, (1 << 20) + 1, None) == SHAPE
+    assert lib.gdn_calib_stream_inplace(P(0) + 8, 1024, 4, None) == SHAPE  # misaligned
+
+
 def test_chunk_fwd_bf16o_validation(lib):
     def c16(**kw):
         a = dict(q=P(0), qs=2048, k=P(1), ks=2048, v=P(2), vs=6144, g=P(3), beta=P(4), o=P(5),

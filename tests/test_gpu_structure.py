@@ -254,3 +254,15 @@ def test_graph_replay_matches_eager(case):
             assert torch.equal(a, b), f"replay {r} differs from the eager call"
         junk = torch.randn(1 << 16, device="cuda") * 2.0     # eager work between replays
         del junk
+
+
+def test_calib_stream_inplace_leaves_the_data():
+    """The streaming calibration pass reads and writes every 16-byte piece
+    back unchanged, also for a size that is not a multiple of the grid."""
+    log("calib_stream_inplace: 1 MiB + 48 bytes, 7 work-groups")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    buf = torch.randint(-2**31, 2**31 - 1, ((1 << 18) + 12,), dtype=torch.int32, device="cuda", generator=g)
+    ref = buf.clone()
+    assert ops.gdn_calib_stream_inplace(buf, 7) == 2 * buf.numel() * 4
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
