@@ -301,16 +301,11 @@ __global__ __launch_bounds__(256) void cb_prep_kernel(CbParams p) {
     const int jb = b - ib * (ib + 1) / 2;
     const uint16_t (*A)[kKS] = kind ? sm.k : sm.q;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // reduction index 16 kb + 4 (lane / 16) + r: four steps per 8-byte read of each row
-#pragma unroll 4
-    for (int kb = 0; kb < kD / 16; ++kb) {
-      const uint2 xa = *reinterpret_cast<const uint2*>(&A[ib * 16 + m][16 * kb + 4 * g4]);
-      const uint2 xb = *reinterpret_cast<const uint2*>(&sm.k[jb * 16 + m][16 * kb + 4 * g4]);
-      acc = mfma4(bf(xa.x & 0xffff), bf(xb.x & 0xffff), acc);
-      acc = mfma4(bf(xa.x >> 16), bf(xb.x >> 16), acc);
-      acc = mfma4(bf(xa.y & 0xffff), bf(xb.y & 0xffff), acc);
-      acc = mfma4(bf(xa.y >> 16), bf(xb.y >> 16), acc);
-    }
+    // bf16 operands as they stand (their products are exact in fp32), 32 of
+    // the reduction a step
+#pragma unroll
+    for (int kp = 0; kp < kD / 32; ++kp)
+      acc = mfma_bf(row8(A, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), acc);
     float (*dst)[kSS] = kind ? sm.kkt : sm.qkt;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
@@ -809,16 +804,10 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
     const int jb = b - ib * (ib + 1) / 2;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // reduction index 16 kb + 4 (lane / 16) + r: four steps per 8-byte read of each row
-#pragma unroll 4
-    for (int kb = 0; kb < kD / 16; ++kb) {
-      const uint2 xa = *reinterpret_cast<const uint2*>(&sm.k[ib * 16 + m][16 * kb + 4 * g4]);
-      const uint2 xb = *reinterpret_cast<const uint2*>(&sm.k[jb * 16 + m][16 * kb + 4 * g4]);
-      acc = mfma4(bf(xa.x & 0xffff), bf(xb.x & 0xffff), acc);
-      acc = mfma4(bf(xa.x >> 16), bf(xb.x >> 16), acc);
-      acc = mfma4(bf(xa.y & 0xffff), bf(xb.y & 0xffff), acc);
-      acc = mfma4(bf(xa.y >> 16), bf(xb.y >> 16), acc);
-    }
+    // bf16 operands as they stand (exact products), 32 of the reduction a step
+#pragma unroll
+    for (int kp = 0; kp < kD / 32; ++kp)
+      acc = mfma_bf(row8(sm.k, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.kkt[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
   }
