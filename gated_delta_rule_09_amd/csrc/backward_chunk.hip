@@ -41,11 +41,11 @@
 // split into bf16 hi + lo parts (about 2^-17 relative error per product,
 // fp32's exponent range): in the chains K S0^T, K dS^T and the state (and
 // state-gradient) updates, whose K and Q operands are bf16 already (two
-// products each), and in the gradient pass the three products with S0 and
-// dS_C (three products each).  The rest (the triangular solves, P^T dO, the
-// gradient pass's other products) run on v_mfma_f32_16x16x4_f32 with fp32
-// operands.  Either way the gradients keep their accuracy at any scale of
-// dO.  In the chains every
+// products each), and every product of the gradient pass (three each where
+// both operands are fp32).  Q K^T and K K^T take the bf16 inputs as they
+// stand (exact products).  Only the chains' triangular solves and P^T dO run
+// on v_mfma_f32_16x16x4_f32.  Either way the gradients keep their accuracy
+// at any scale of dO.  In the chains every
 // 64-token x 16-channel intermediate stays in the accumulator layout (lane l:
 // rows 4 (l / 16) + r, column l % 16) and enters the next product as its B
 // operand directly; the A operand then takes its k columns in the same order.
@@ -968,11 +968,23 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
       const int jb = b - ib * (ib + 1) / 2;
       floatx4 accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int kk = 0; kk < kD / 4; ++kk) {
-        const float bu = sm.u.in.U[jb * 16 + m][4 * kk + g4];
-        accP = mfma4(sm.u.in.dO[ib * 16 + m][4 * kk + g4], bu, accP);
-        accA = mfma4(sm.u.in.dR[ib * 16 + m][4 * kk + g4], bu, accA);
+      // split-bf16 over 32 value channels a step (channels 32 ks + 8 g4 + e)
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        const int c0 = 32 * ks + 8 * g4;
+        float a[8];
+        bf16x8v bh, bl, ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.U[jb * 16 + m][c0 + e];
+        split8(a, bh, bl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.dO[ib * 16 + m][c0 + e];
+        split8(a, ah, al);
+        accP = mfma_split(ah, al, bh, bl, accP);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.dR[ib * 16 + m][c0 + e];
+        split8(a, ah, al);
+        accA = mfma_split(ah, al, bh, bl, accA);
       }
       const int j = jb * 16 + m;
 #pragma unroll
@@ -1009,30 +1021,58 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     for (int tb = 0; tb < 4; ++tb) {
       floatx4 x2 = {0.f, 0.f, 0.f, 0.f};
       const int i = tb * 16 + m;
-      // reduction over tokens j = 16 jb + 4 (lane / 16) + r: K, Q columns by
-      // the transposing read, dP o M and W rows by 16-byte reads
-#pragma unroll 1
-      for (int jb = 0; jb <= tb; ++jb) {
-        const int j0 = 16 * jb + 4 * g4;
-        const floatx4 kt = col4(sm.k, j0, w * 16);
-        const floatx4 ap = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][j0]);
-        const floatx4 aw = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][j0]);
+      // reduction over tokens 32 kp + kappa(lane / 16, e) (two 16-token
+      // blocks a step): K, Q columns by the transposing read (bf16 as they
+      // stand), dP o M and W split-bf16; the half of a step outside the
+      // blocks a product covers (left unwritten in LDS) enters as zeros
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dqh[tb] = mfma4(ap[r], kt[r], dqh[tb]);
-          x1[tb] = mfma4(aw[r], kt[r], x1[tb]);
+      for (int kp = 0; 2 * kp <= tb; ++kp) {             // blocks 0 .. tb
+        const bool upper_half = 2 * kp + 1 <= tb;
+        const bf16x8v kt = col8(sm.k, 32 * kp, w * 16);
+        const floatx4 p0 = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][32 * kp + 4 * g4]);
+        const floatx4 p1 = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][32 * kp + 16 + 4 * g4]);
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][32 * kp + 4 * g4]);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][32 * kp + 16 + 4 * g4]);
+        float a[8];
+        bf16x8v ah, al;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = p0[e];
+          a[4 + e] = upper_half ? p1[e] : 0.f;
         }
+        split8(a, ah, al);
+        dqh[tb] = mfma_bf(ah, kt, dqh[tb]);
+        dqh[tb] = mfma_bf(al, kt, dqh[tb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = w0[e];
+          a[4 + e] = upper_half ? w1[e] : 0.f;
+        }
+        split8(a, ah, al);
+        x1[tb] = mfma_bf(ah, kt, x1[tb]);
+        x1[tb] = mfma_bf(al, kt, x1[tb]);
       }
-#pragma unroll 1
-      for (int jb = tb; jb < 4; ++jb) {
-        const int j0 = 16 * jb + 4 * g4;
-        const floatx4 kt = col4(sm.k, j0, w * 16);
-        const floatx4 qt = col4(sm.q, j0, w * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x2 = mfma4(sm.u.mid.w[j0 + r][i], kt[r], x2);
-          x2 = mfma4(sm.u.mid.dpm[j0 + r][i], qt[r], x2);
+      for (int kp = tb / 2; kp < 2; ++kp) {              // blocks tb .. 3
+        const bool lower_half = 2 * kp >= tb;
+        const bf16x8v kt = col8(sm.k, 32 * kp, w * 16);
+        const bf16x8v qt = col8(sm.q, 32 * kp, w * 16);
+        float a[8], b[8];
+        bf16x8v ah, al;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j0 = 32 * kp + 4 * g4 + e, j1 = j0 + 16;
+          a[e] = lower_half ? sm.u.mid.w[j0][i] : 0.f;
+          b[e] = lower_half ? sm.u.mid.dpm[j0][i] : 0.f;
+          a[4 + e] = sm.u.mid.w[j1][i];
+          b[4 + e] = sm.u.mid.dpm[j1][i];
         }
+        split8(a, ah, al);
+        x2 = mfma_bf(ah, kt, x2);
+        x2 = mfma_bf(al, kt, x2);
+        split8(b, ah, al);
+        x2 = mfma_bf(ah, qt, x2);
+        x2 = mfma_bf(al, qt, x2);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
