@@ -126,20 +126,6 @@ __device__ __forceinline__ floatx4 mfma_split(const bf16x8v ah, const bf16x8v al
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// rows[r0 + e][c0 + lane % 16], e = 0..3, of staged bf16 rows: the A operand
-// of a product over tokens with K^T or Q^T, k columns r0 .. r0 + 3 (r0 may
-// differ between the four 16-lane groups).  gfx950's transposing LDS read
-// (ds_read_b64_tr_b16): lane j of a 16-lane group points at row r0 + j / 4,
-// columns c0 + 4 (j % 4) .. + 3, and lane i receives column c0 + i of the
-// four rows.
-__device__ __forceinline__ floatx4 col4(const uint16_t (*rows)[kKS], int r0, int c0) {
-  const int j = threadIdx.x & 15;
-  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4*)(&rows[r0 + (j >> 2)][c0 + 4 * (j & 3)]));
-  return floatx4{bf(static_cast<uint16_t>(v[0])), bf(static_cast<uint16_t>(v[1])),
-                 bf(static_cast<uint16_t>(v[2])), bf(static_cast<uint16_t>(v[3]))};
-}
-
 // Split-bf16 operands of the chains' 16 x 16 x 32 products.  The reduction
 // index of slot (lane group g, element e) is kappa(g, e) = 4 g + e for e < 4
 // and 16 + 4 g + (e - 4) otherwise, so that two vertically adjacent
@@ -769,14 +755,14 @@ __global__ __launch_bounds__(256, 2) void cb_bwd_kernel(CbParams p) {
 // cb_grad: one work-group (8 waves) per (chunk slot, key head).  Wave w owns
 // columns 16 w .. 16 w + 15 of the 64 x 128 results (dq, dk and their parts),
 // and a share of the 64 x 64 products dP = scale dO U^T, dA = -dR U^T.
-constexpr int kGS = 129;          // fp32 row stride of staged dO, U, dR
-constexpr int kMS = 68;           // fp32 row stride of dP o M, W
+// Every wave needs all of dO, U and dR as A operands: they are split into
+// bf16 hi + lo parts once, when staged, and so are dP o M and W, when the
+// waves that form them store them.
 struct GradLds {
   uint16_t q[kC][kKS], k[kC][kKS];
-  float kkt[kC][kSS];
   union {
-    struct { float dO[kC][kGS]; float U[kC][kGS]; float dR[kC][kGS]; } in;
-    struct { float dpm[kC][kMS]; float w[kC][kMS]; } mid;
+    uint16_t in[3][2][kC][kKS];    // dO, U, dR: [array][hi, lo][token][channel]
+    uint16_t mid[2][2][kC][kKS];   // dP o M, W: [matrix][hi, lo][i][j], blocks above the diagonal unwritten
   } u;
   float G[kC], gam[kC], dec[kC], bet[kC];
   float part_q[kC][8], part_y[kC][8], part_s[kC][8];
@@ -784,6 +770,23 @@ struct GradLds {
   float dbe[kC];
   float dss[8];
 };
+
+// 8 contiguous bf16 of a staged row (one 16-byte read), reduction slot j of
+// lane group g4 = channel c0 + j
+__device__ __forceinline__ bf16x8v row8c(const uint16_t (*rows)[kKS], int row, int c0) {
+  return __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&rows[row][c0]));
+}
+// keep elements 0..3 (reduction slots of the first 16-row block), or 4..7
+__device__ __forceinline__ bf16x8v first4(const bf16x8v v) {
+  uint4 u = __builtin_bit_cast(uint4, v);
+  u.z = u.w = 0u;
+  return __builtin_bit_cast(bf16x8v, u);
+}
+__device__ __forceinline__ bf16x8v last4(const bf16x8v v) {
+  uint4 u = __builtin_bit_cast(uint4, v);
+  u.x = u.y = 0u;
+  return __builtin_bit_cast(bf16x8v, u);
+}
 
 __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
   __shared__ __align__(16) GradLds sm;
@@ -808,17 +811,20 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
   stage_rows<512>(p.q, p.qs, sc.t0, sc.len, kh, sm.q);
   stage_rows<512>(p.k, p.ks, sc.t0, sc.len, kh, sm.k);
   __syncthreads();
-  // K K^T on and below the diagonal (10 blocks)
-  for (int b = w; b < 10; b += 8) {
+  // K K^T on and below the diagonal (10 blocks): wave w keeps blocks w and
+  // w + 8, the blocks of dP and dA it forms for every value head
+  floatx4 kkt[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int b = w + 8 * s2;
+    kkt[s2] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (b >= 10) break;
     const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
     const int jb = b - ib * (ib + 1) / 2;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     // bf16 operands as they stand (exact products), 32 of the reduction a step
 #pragma unroll
     for (int kp = 0; kp < kD / 32; ++kp)
-      acc = mfma_bf(row8(sm.k, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.kkt[ib * 16 + 4 * g4 + r][jb * 16 + m] = acc[r];
+      kkt[s2] = mfma_bf(row8(sm.k, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), kkt[s2]);
   }
 
   // dk summed over the value heads in registers; dq in its output rows (each
@@ -840,90 +846,148 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     const int d = w * 16 + m;
     const int h = kh * p.group + hv;
     const int64_t sh = static_cast<int64_t>(slot) * p.Hv + h;
-    {  // dO, U, dR rows: thread -> row tid / 8, 16 columns
-      const int row = tid >> 3;
-      const int c0 = (tid & 7) * 16;
-      const bool ok = row < sc.len;
-      const float* so = p.d_o + (static_cast<int64_t>(sc.t0 + min(row, sc.len - 1)) * p.Hv + h) * kD + c0;
-      const float* su = p.U + (sh * kC + row) * kD + c0;
-      const float* sr = p.dR + (sh * kC + row) * kD + c0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // grad_o is only 4-byte aligned
-        const floatx4 yo = {so[4 * j], so[4 * j + 1], so[4 * j + 2], so[4 * j + 3]};
-        const floatx4 xo = ok ? yo : floatx4{0.f, 0.f, 0.f, 0.f};
-        const floatx4 xu = *reinterpret_cast<const floatx4*>(su + 4 * j);
-        const floatx4 xr = *reinterpret_cast<const floatx4*>(sr + 4 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.u.in.dO[row][c0 + 4 * j + e] = xo[e];
-          sm.u.in.U[row][c0 + 4 * j + e] = xu[e];
-          sm.u.in.dR[row][c0 + 4 * j + e] = xr[e];
-        }
-      }
-    }
+    const float* S0 = p.S0 + sh * (kD * kD) + d;
+    const float* dSC = p.dSC + sh * (kD * kD) + d;
+    // every load of the value head issued up front, so that their latencies
+    // overlap: this thread's dO, U, dR row pieces, the E rows of its dbeta
+    // share (rows 8 w .. + 7), and its B operands of the products with S0 and
+    // dS_C (rows 32 ks + 8 g4 .. + 7, column d), which arrive while the
+    // products of the staged rows alone (dbeta's dR . E, dP and dA) run
+    // the gates first: their loads then precede the others, whose waits
+    // they do not join
     if (w == 0) {
       const Gates gt = chunk_gates(p, sc.t0, sc.len, h);
       sm.G[lane] = gt.G; sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
     }
+    const int srow = tid_v >> 3;
+    const int sc0 = (tid_v & 7) * 16;
+    const bool srow_ok = srow < sc.len;
+    float xo[16], xu[16], xr[16];
+    {
+      const float* so = p.d_o + (static_cast<int64_t>(sc.t0 + min(srow, sc.len - 1)) * p.Hv + h) * kD + sc0;
+      const float* su = p.U + (sh * kC + srow) * kD + sc0;
+      const float* sr = p.dR + (sh * kC + srow) * kD + sc0;
+      // grad_o is only 4-byte aligned; rows past the chunk's end read the last
+      // row (in bounds) and are zeroed after the load
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xo[j] = so[j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(su + 4 * j);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(sr + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { xu[4 * j + e] = a[e]; xr[4 * j + e] = b[e]; }
+      }
+    }
+    // (the scheduler may not move work across these points: every load is
+    // issued, in this order, before any of them is waited for)
+    __builtin_amdgcn_sched_barrier(0);
+    float e0[8], e1[8];
+    {
+      const float* Eh = p.E + (sh * kC + 8 * w) * kD + lane;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        e0[rr] = Eh[rr * kD];
+        e1[rr] = Eh[rr * kD + 64];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float b1[4][8], b2[4][8];
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        b1[ks][j] = S0[(32 * ks + 8 * g4 + j) * kD];
+        b2[ks][j] = dSC[(32 * ks + 8 * g4 + j) * kD];
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    {  // split and stage: thread -> row tid / 8, 16 channels
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float x = xo[j];
+        asm volatile("" : "+v"(x));   // the load stays unconditional
+        xo[j] = srow_ok ? x : 0.f;
+      }
+      const float* src[3] = {xo, xu, xr};
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = src[a][8 * half + j];
+          bf16x8v hi, lo;
+          split8(x, hi, lo);
+          *reinterpret_cast<uint4*>(&sm.u.in[a][0][srow][sc0 + 8 * half]) = __builtin_bit_cast(uint4, hi);
+          *reinterpret_cast<uint4*>(&sm.u.in[a][1][srow][sc0 + 8 * half]) = __builtin_bit_cast(uint4, lo);
+        }
+    }
     __syncthreads();
 
+    // dbeta's first part: dR_i . E_i, rows 8 w .. 8 w + 7 (dR as hi + lo)
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int i = 8 * w + rr;
+      const float r0 = bf(sm.u.in[2][0][i][lane]) + bf(sm.u.in[2][1][i][lane]);
+      const float r1 = bf(sm.u.in[2][0][i][lane + 64]) + bf(sm.u.in[2][1][i][lane + 64]);
+      const float x = wave_sum(r0 * e0[rr] + r1 * e1[rr]);
+      if (lane == 0) sm.dbe[i] = x;
+    }
+    // dP o M and W = b o dA o M on and below the diagonal: wave w takes the
+    // 16 x 16 blocks w and w + 8 of the ten (both products share U^T), held in
+    // registers until the staged rows are no longer read
+    floatx4 resP[2], resW[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int b = w + 8 * s2;
+      resP[s2] = resW[s2] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (b >= 10) break;
+      const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
+      const int jb = b - ib * (ib + 1) / 2;
+      floatx4 accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+      // split-bf16 over 32 value channels a step (channels 32 ks + 8 g4 + e)
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        const int c0 = 32 * ks + 8 * g4;
+        const bf16x8v bh = row8c(sm.u.in[1][0], jb * 16 + m, c0), bl = row8c(sm.u.in[1][1], jb * 16 + m, c0);
+        accP = mfma_split(row8c(sm.u.in[0][0], ib * 16 + m, c0), row8c(sm.u.in[0][1], ib * 16 + m, c0), bh, bl, accP);
+        accA = mfma_split(row8c(sm.u.in[2][0], ib * 16 + m, c0), row8c(sm.u.in[2][1], ib * 16 + m, c0), bh, bl, accA);
+      }
+      const int j = jb * 16 + m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * g4 + r;
+        const float Mij = j <= i ? expf(sm.G[i] - sm.G[j]) : 0.f;
+        const float dA = j < i ? -accA[r] : 0.f;
+        resP[s2][r] = p.scale * accP[r] * Mij;
+        resW[s2][r] = sm.bet[i] * dA * Mij;
+        const float pb = sum16(dA * Mij * kkt[s2][r]);
+        if (m == 0) sm.part_b[i][jb] = pb;
+      }
+    }
     // products with S0 and dS_C (B operands straight from the workspace):
     //   dq_h  = (scale gamma dO) S0,  X1 = (-gamma b dR) S0,  dKS = (D U) dS_C
     floatx4 dqh[4], x1[4], dks[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) dqh[tb] = x1[tb] = dks[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const float* S0 = p.S0 + sh * (kD * kD) + d;
-    const float* dSC = p.dSC + sh * (kD * kD) + d;
     float dss = 0.f;
     // split-bf16 products over k-steps of 32 value channels: lane (m, g4)
-    // takes channels c = 32 ks + 8 g4 + j; its B operands (rows c of S0 and
-    // dS_C, column d) are loaded a k-step ahead.  The per-token scales are
-    // applied to the sums afterwards.
-    float nb1[8], nb2[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      nb1[j] = S0[(8 * g4 + j) * kD];
-      nb2[j] = dSC[(8 * g4 + j) * kD];
-    }
+    // takes channels c = 32 ks + 8 g4 + j.  The per-token scales are applied
+    // to the sums afterwards.
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ++ks) {
-      float b1[8], b2[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        b1[j] = nb1[j];
-        b2[j] = nb2[j];
-      }
-      if (ks + 1 < kD / 32) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          nb1[j] = S0[(32 * (ks + 1) + 8 * g4 + j) * kD];
-          nb2[j] = dSC[(32 * (ks + 1) + 8 * g4 + j) * kD];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dss = fmaf(b1[j], b2[j], dss);
+      for (int j = 0; j < 8; ++j) dss = fmaf(b1[ks][j], b2[ks][j], dss);
       bf16x8v b1h, b1l, b2h, b2l;
-      split8(b1, b1h, b1l);
-      split8(b2, b2h, b2l);
+      split8(b1[ks], b1h, b1l);
+      split8(b2[ks], b2h, b2l);
       const int c0 = 32 * ks + 8 * g4;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int i = tb * 16 + m;
-        float a[8];
-        bf16x8v ah, al;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.dO[i][c0 + j];
-        split8(a, ah, al);
-        dqh[tb] = mfma_split(ah, al, b1h, b1l, dqh[tb]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.dR[i][c0 + j];
-        split8(a, ah, al);
-        x1[tb] = mfma_split(ah, al, b1h, b1l, x1[tb]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = sm.u.in.U[i][c0 + j];
-        split8(a, ah, al);
-        dks[tb] = mfma_split(ah, al, b2h, b2l, dks[tb]);
+        dqh[tb] = mfma_split(row8c(sm.u.in[0][0], i, c0), row8c(sm.u.in[0][1], i, c0), b1h, b1l, dqh[tb]);
+        x1[tb] = mfma_split(row8c(sm.u.in[2][0], i, c0), row8c(sm.u.in[2][1], i, c0), b1h, b1l, x1[tb]);
+        dks[tb] = mfma_split(row8c(sm.u.in[1][0], i, c0), row8c(sm.u.in[1][1], i, c0), b2h, b2l, dks[tb]);
       }
     }
 #pragma unroll
@@ -948,65 +1012,6 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       }
       dk_tot[tb] += dks[tb];
     }
-    // dbeta's first part: dR_i . E_i, rows 8 w .. 8 w + 7 (the E rows loaded
-    // first, then the sums)
-    {
-      const float* Eh = p.E + (sh * kC + 8 * w) * kD + lane;
-      float e0[8], e1[8];
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        e0[rr] = Eh[rr * kD];
-        e1[rr] = Eh[rr * kD + 64];
-      }
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int i = 8 * w + rr;
-        const float x = wave_sum(sm.u.in.dR[i][lane] * e0[rr] + sm.u.in.dR[i][lane + 64] * e1[rr]);
-        if (lane == 0) sm.dbe[i] = x;
-      }
-    }
-    // dP o M and W = b o dA o M on and below the diagonal: wave w takes the
-    // 16 x 16 blocks w and w + 8 of the ten (both products share U^T), held in
-    // registers until the staged rows are no longer read
-    floatx4 resP[2], resW[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int b = w + 8 * s2;
-      resP[s2] = resW[s2] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (b >= 10) break;
-      const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
-      const int jb = b - ib * (ib + 1) / 2;
-      floatx4 accP = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
-      // split-bf16 over 32 value channels a step (channels 32 ks + 8 g4 + e)
-#pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const int c0 = 32 * ks + 8 * g4;
-        float a[8];
-        bf16x8v bh, bl, ah, al;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.U[jb * 16 + m][c0 + e];
-        split8(a, bh, bl);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.dO[ib * 16 + m][c0 + e];
-        split8(a, ah, al);
-        accP = mfma_split(ah, al, bh, bl, accP);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = sm.u.in.dR[ib * 16 + m][c0 + e];
-        split8(a, ah, al);
-        accA = mfma_split(ah, al, bh, bl, accA);
-      }
-      const int j = jb * 16 + m;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ib * 16 + 4 * g4 + r;
-        const float Mij = j <= i ? expf(sm.G[i] - sm.G[j]) : 0.f;
-        const float dA = j < i ? -accA[r] : 0.f;
-        resP[s2][r] = p.scale * accP[r] * Mij;
-        resW[s2][r] = sm.bet[i] * dA * Mij;
-        const float pb = sum16(dA * Mij * sm.kkt[i][j]);
-        if (m == 0) sm.part_b[i][jb] = pb;
-      }
-    }
     __syncthreads();   // staged rows no longer read: their space takes dP o M and W
 
 #pragma unroll
@@ -1016,9 +1021,18 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
       const int jb = b - ib * (ib + 1) / 2;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.u.mid.dpm[ib * 16 + 4 * g4 + r][jb * 16 + m] = resP[s2][r];
-        sm.u.mid.w[ib * 16 + 4 * g4 + r][jb * 16 + m] = resW[s2][r];
+      for (int r = 0; r < 4; r += 2) {
+        const int i = ib * 16 + 4 * g4 + r, j = jb * 16 + m;
+        const uint32_t ph = pk_bf16(resP[s2][r], resP[s2][r + 1]);
+        const uint32_t pl = pk_bf16(resP[s2][r] - __uint_as_float(ph << 16),
+                                    resP[s2][r + 1] - __uint_as_float(ph & 0xffff0000u));
+        const uint32_t wh = pk_bf16(resW[s2][r], resW[s2][r + 1]);
+        const uint32_t wl = pk_bf16(resW[s2][r] - __uint_as_float(wh << 16),
+                                    resW[s2][r + 1] - __uint_as_float(wh & 0xffff0000u));
+        sm.u.mid[0][0][i][j] = static_cast<uint16_t>(ph); sm.u.mid[0][0][i + 1][j] = static_cast<uint16_t>(ph >> 16);
+        sm.u.mid[0][1][i][j] = static_cast<uint16_t>(pl); sm.u.mid[0][1][i + 1][j] = static_cast<uint16_t>(pl >> 16);
+        sm.u.mid[1][0][i][j] = static_cast<uint16_t>(wh); sm.u.mid[1][0][i + 1][j] = static_cast<uint16_t>(wh >> 16);
+        sm.u.mid[1][1][i][j] = static_cast<uint16_t>(wl); sm.u.mid[1][1][i + 1][j] = static_cast<uint16_t>(wl >> 16);
       }
     }
     __syncthreads();
@@ -1031,57 +1045,33 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       floatx4 x2 = {0.f, 0.f, 0.f, 0.f};
       const int i = tb * 16 + m;
       // reduction over tokens 32 kp + kappa(lane / 16, e) (two 16-token
-      // blocks a step): K, Q columns by the transposing read (bf16 as they
-      // stand), dP o M and W split-bf16; the half of a step outside the
-      // blocks a product covers (left unwritten in LDS) enters as zeros
+      // blocks a step), every operand bf16 (K, Q as they stand; dP o M and W
+      // as hi + lo): the half of a step outside the blocks a product covers
+      // (left unwritten in LDS) enters as zeros
 #pragma unroll
       for (int kp = 0; 2 * kp <= tb; ++kp) {             // blocks 0 .. tb
         const bool upper_half = 2 * kp + 1 <= tb;
         const bf16x8v kt = col8(sm.k, 32 * kp, w * 16);
-        const floatx4 p0 = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][32 * kp + 4 * g4]);
-        const floatx4 p1 = *reinterpret_cast<const floatx4*>(&sm.u.mid.dpm[i][32 * kp + 16 + 4 * g4]);
-        const floatx4 w0 = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][32 * kp + 4 * g4]);
-        const floatx4 w1 = *reinterpret_cast<const floatx4*>(&sm.u.mid.w[i][32 * kp + 16 + 4 * g4]);
-        float a[8];
-        bf16x8v ah, al;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = p0[e];
-          a[4 + e] = upper_half ? p1[e] : 0.f;
-        }
-        split8(a, ah, al);
-        dqh[tb] = mfma_bf(ah, kt, dqh[tb]);
-        dqh[tb] = mfma_bf(al, kt, dqh[tb]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = w0[e];
-          a[4 + e] = upper_half ? w1[e] : 0.f;
-        }
-        split8(a, ah, al);
-        x1[tb] = mfma_bf(ah, kt, x1[tb]);
-        x1[tb] = mfma_bf(al, kt, x1[tb]);
+        bf16x8v ph = row8(sm.u.mid[0][0], i, 32 * kp, g4), pl = row8(sm.u.mid[0][1], i, 32 * kp, g4);
+        bf16x8v wh = row8(sm.u.mid[1][0], i, 32 * kp, g4), wl = row8(sm.u.mid[1][1], i, 32 * kp, g4);
+        if (!upper_half) { ph = first4(ph); pl = first4(pl); wh = first4(wh); wl = first4(wl); }
+        dqh[tb] = mfma_bf(ph, kt, dqh[tb]);
+        dqh[tb] = mfma_bf(pl, kt, dqh[tb]);
+        x1[tb] = mfma_bf(wh, kt, x1[tb]);
+        x1[tb] = mfma_bf(wl, kt, x1[tb]);
       }
 #pragma unroll
       for (int kp = tb / 2; kp < 2; ++kp) {              // blocks tb .. 3
         const bool lower_half = 2 * kp >= tb;
         const bf16x8v kt = col8(sm.k, 32 * kp, w * 16);
         const bf16x8v qt = col8(sm.q, 32 * kp, w * 16);
-        float a[8], b[8];
-        bf16x8v ah, al;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j0 = 32 * kp + 4 * g4 + e, j1 = j0 + 16;
-          a[e] = lower_half ? sm.u.mid.w[j0][i] : 0.f;
-          b[e] = lower_half ? sm.u.mid.dpm[j0][i] : 0.f;
-          a[4 + e] = sm.u.mid.w[j1][i];
-          b[4 + e] = sm.u.mid.dpm[j1][i];
-        }
-        split8(a, ah, al);
-        x2 = mfma_bf(ah, kt, x2);
-        x2 = mfma_bf(al, kt, x2);
-        split8(b, ah, al);
-        x2 = mfma_bf(ah, qt, x2);
-        x2 = mfma_bf(al, qt, x2);
+        bf16x8v wh = col8(sm.u.mid[1][0], 32 * kp, tb * 16), wl = col8(sm.u.mid[1][1], 32 * kp, tb * 16);
+        bf16x8v ph = col8(sm.u.mid[0][0], 32 * kp, tb * 16), pl = col8(sm.u.mid[0][1], 32 * kp, tb * 16);
+        if (!lower_half) { ph = last4(ph); pl = last4(pl); wh = last4(wh); wl = last4(wl); }
+        x2 = mfma_bf(wh, kt, x2);
+        x2 = mfma_bf(wl, kt, x2);
+        x2 = mfma_bf(ph, qt, x2);
+        x2 = mfma_bf(pl, qt, x2);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
