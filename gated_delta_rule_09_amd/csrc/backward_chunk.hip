@@ -774,7 +774,10 @@ struct GradLds {
 // 8 contiguous bf16 of a staged row (one 16-byte read), reduction slot j of
 // lane group g4 = channel c0 + j
 __device__ __forceinline__ bf16x8v row8c(const uint16_t (*rows)[kKS], int row, int c0) {
-  return __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&rows[row][c0]));
+  // 24-bit multiply: a 32-bit one is selected as a 64-bit multiply-add whose
+  // unused high input may be a register a load in flight still targets
+  const uint32_t off = __umul24(static_cast<uint32_t>(row), kKS * 2u) + 2u * static_cast<uint32_t>(c0);
+  return __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(rows) + off));
 }
 // keep elements 0..3 (reduction slots of the first 16-row block), or 4..7
 __device__ __forceinline__ bf16x8v first4(const bf16x8v v) {
@@ -802,7 +805,7 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
     if ((p.part == 1) != (c >= ((s1 - s0 + kC - 1) / kC) / 2)) return;
   }
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches on it
   const int lane = tid & 63;
   const int m = lane & 15;
   const int g4 = lane >> 4;
@@ -811,28 +814,10 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
   stage_rows<512>(p.q, p.qs, sc.t0, sc.len, kh, sm.q);
   stage_rows<512>(p.k, p.ks, sc.t0, sc.len, kh, sm.k);
   __syncthreads();
-  // K K^T on and below the diagonal (10 blocks): wave w keeps blocks w and
-  // w + 8, the blocks of dP and dA it forms for every value head
-  floatx4 kkt[2];
+  // dq and dk summed over the value heads in registers
+  floatx4 dq_tot[4], dk_tot[4];
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-    const int b = w + 8 * s2;
-    kkt[s2] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (b >= 10) break;
-    const int ib = b < 1 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3;
-    const int jb = b - ib * (ib + 1) / 2;
-    // bf16 operands as they stand (exact products), 32 of the reduction a step
-#pragma unroll
-    for (int kp = 0; kp < kD / 32; ++kp)
-      kkt[s2] = mfma_bf(row8(sm.k, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), kkt[s2]);
-  }
-
-  // dk summed over the value heads in registers; dq in its output rows (each
-  // element written, then added to, by the one lane that owns it)
-  floatx4 dk_tot[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) dk_tot[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float* dq_out = p.dq + (static_cast<int64_t>(sc.t0) * p.Hk + kh) * kD + d;
+  for (int tb = 0; tb < 4; ++tb) dq_tot[tb] = dk_tot[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int hv = 0; hv < p.group; ++hv) {
     // the lane indices again from an opaque copy of the thread id: the address
@@ -953,6 +938,11 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
         accP = mfma_split(row8c(sm.u.in[0][0], ib * 16 + m, c0), row8c(sm.u.in[0][1], ib * 16 + m, c0), bh, bl, accP);
         accA = mfma_split(row8c(sm.u.in[2][0], ib * 16 + m, c0), row8c(sm.u.in[2][1], ib * 16 + m, c0), bh, bl, accA);
       }
+      // the block of K K^T (bf16 operands as they stand: exact products)
+      floatx4 kkt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kp = 0; kp < kD / 32; ++kp)
+        kkt = mfma_bf(row8(sm.k, ib * 16 + m, 32 * kp, g4), row8(sm.k, jb * 16 + m, 32 * kp, g4), kkt);
       const int j = jb * 16 + m;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -961,10 +951,12 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
         const float dA = j < i ? -accA[r] : 0.f;
         resP[s2][r] = p.scale * accP[r] * Mij;
         resW[s2][r] = sm.bet[i] * dA * Mij;
-        const float pb = sum16(dA * Mij * kkt[s2][r]);
+        const float pb = sum16(dA * Mij * kkt[r]);
         if (m == 0) sm.part_b[i][jb] = pb;
       }
     }
+    // (kept after the products above: they need none of the loads below)
+    __builtin_amdgcn_sched_barrier(0);
     // products with S0 and dS_C (B operands straight from the workspace):
     //   dq_h  = (scale gamma dO) S0,  X1 = (-gamma b dR) S0,  dKS = (D U) dS_C
     floatx4 dqh[4], x1[4], dks[4];
@@ -1080,14 +1072,7 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
         const float py = sum16(bf(sm.k[t][d]) * (x1[tb][r] - x2[r]));
         if (m == 0) { sm.part_q[t][w] = pq; sm.part_y[t][w] = py; }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb * 16 + 4 * g4 + r;
-        if (t < sc.len) {
-          float* o = dq_out + static_cast<int64_t>(t) * p.Hk * kD;
-          *o = hv == 0 ? dqh[tb][r] : *o + dqh[tb][r];
-        }
-      }
+      dq_tot[tb] += dqh[tb];
       dk_tot[tb] += x1[tb] + x2;
     }
     __syncthreads();
@@ -1122,7 +1107,11 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = tb * 16 + 4 * g4 + r;
-      if (i < sc.len) p.dk[(static_cast<int64_t>(sc.t0 + i) * p.Hk + kh) * kD + d] = dk_tot[tb][r];
+      if (i < sc.len) {
+        const int64_t o = (static_cast<int64_t>(sc.t0 + i) * p.Hk + kh) * kD + d;
+        p.dq[o] = dq_tot[tb][r];
+        p.dk[o] = dk_tot[tb][r];
+      }
     }
 }
 
