@@ -223,16 +223,19 @@ template <int kThr>
 __device__ __forceinline__ void stage_rows(const uint16_t* src, int64_t stride, int t0, int len, int kh,
                                            uint16_t (*dst)[kKS]) {
   constexpr int kPer = kC * kD / kThr;          // halves per thread: 32 (256 thr) or 16 (512)
+  constexpr int kRowThr = kD / kPer;            // threads per row
   const int tid = threadIdx.x;
-  const int row = tid / (kD / kPer);
-  const int c0 = (tid % (kD / kPer)) * kPer;
+  const int row = tid / kRowThr;
+  // piece j of a thread: channels 8 (tid % kRowThr + kRowThr j) .. + 7, so
+  // that the threads of a row read contiguous bytes in each load
+  const int c0 = (tid % kRowThr) * 8;
   const bool ok = row < len;
-  const uint4* s = reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + min(row, len - 1)) * stride + kh * kD + c0);
+  const uint16_t* s = src + static_cast<int64_t>(t0 + min(row, len - 1)) * stride + kh * kD + c0;
 #pragma unroll
   for (int j = 0; j < kPer / 8; ++j) {
-    const uint4 y = s[j];
+    const uint4 y = *reinterpret_cast<const uint4*>(s + 8 * kRowThr * j);
     const uint4 x = ok ? y : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&dst[row][c0 + 8 * j]) = x;
+    *reinterpret_cast<uint4*>(&dst[row][c0 + 8 * kRowThr * j]) = x;
   }
 }
 
@@ -371,22 +374,25 @@ __device__ __forceinline__ void chain_load(const CbParams& p, int t0, int len, i
                                            int64_t sh, ChainNext<kWithQ>& f,
                                            int tid = threadIdx.x) {
   const int lane = tid & 63;
-  const int row = tid >> 2;                   // K / Q: 32 halves, X: 16 floats per thread
+  // K / Q: 32 halves, X: 16 floats per thread, in pieces of 16 bytes: piece
+  // j at halves 8 (tid % 4) + 32 j (X: floats 4 (tid % 4) + 16 j), so that
+  // the 4 threads of a row read contiguous bytes in each load
+  const int row = tid >> 2;
   const bool ok = row < len;
   const int64_t t = t0 + min(row, len - 1);   // rows past the end load the last, then zero
-  const uint4* sk = reinterpret_cast<const uint4*>(p.k + t * p.ks + kh * kD + (tid & 3) * 32);
+  const uint16_t* sk = p.k + t * p.ks + kh * kD + (tid & 3) * 8;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.k[j] = sk[j];
+  for (int j = 0; j < 4; ++j) f.k[j] = *reinterpret_cast<const uint4*>(sk + 32 * j);
   if (kWithQ) {
-    const uint4* sq = reinterpret_cast<const uint4*>(p.q + t * p.qs + kh * kD + (tid & 3) * 32);
+    const uint16_t* sq = p.q + t * p.qs + kh * kD + (tid & 3) * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.q[j] = sq[j];
+    for (int j = 0; j < 4; ++j) f.q[j] = *reinterpret_cast<const uint4*>(sq + 32 * j);
   }
   (void)ok;
   f.len = len;
-  const float* sx = p.X + sh * (kC * kC) + row * kC + (tid & 3) * 16;
+  const float* sx = p.X + sh * (kC * kC) + row * kC + (tid & 3) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.x[j] = *reinterpret_cast<const floatx4*>(sx + 4 * j);
+  for (int j = 0; j < 4; ++j) f.x[j] = *reinterpret_cast<const floatx4*>(sx + 16 * j);
   const int64_t gi_at = static_cast<int64_t>(t0 + min(lane, len - 1)) * p.Hv + h;
   f.g = p.g[gi_at];
   f.b = p.beta[gi_at];
@@ -402,14 +408,14 @@ __device__ __forceinline__ void chain_put(const ChainNext<kWithQ>& f, ChainLds& 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint4 kv = f.k[j];
-    *reinterpret_cast<uint4*>(&sm.k[row][(tid & 3) * 32 + 8 * j]) =
+    *reinterpret_cast<uint4*>(&sm.k[row][(tid & 3) * 8 + 32 * j]) =
         make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
     if (kWithQ) {
       const uint4 qv = f.q[j];
-      *reinterpret_cast<uint4*>(&sm.q[row][(tid & 3) * 32 + 8 * j]) =
+      *reinterpret_cast<uint4*>(&sm.q[row][(tid & 3) * 8 + 32 * j]) =
           make_uint4(qv.x & keep, qv.y & keep, qv.z & keep, qv.w & keep);
     }
-    *reinterpret_cast<floatx4*>(&sm.x[row][(tid & 3) * 16 + 4 * j]) = f.x[j];
+    *reinterpret_cast<floatx4*>(&sm.x[row][(tid & 3) * 4 + 16 * j]) = f.x[j];
   }
   if ((tid >> 6) == 0) {
     const int lane = tid & 63;
@@ -844,8 +850,10 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       const Gates gt = chunk_gates(p, sc.t0, sc.len, h);
       sm.G[lane] = gt.G; sm.gam[lane] = gt.gam; sm.dec[lane] = gt.dec; sm.bet[lane] = gt.bet;
     }
+    // thread -> row tid / 8 and channels 32 j + 4 (tid % 8) .. + 3, j = 0..3:
+    // the 8 threads of a row read 128 contiguous bytes per load
     const int srow = tid_v >> 3;
-    const int sc0 = (tid_v & 7) * 16;
+    const int sc0 = (tid_v & 7) * 4;
     const bool srow_ok = srow < sc.len;
     float xo[16], xu[16], xr[16];
     {
@@ -855,11 +863,13 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
       // grad_o is only 4-byte aligned; rows past the chunk's end read the last
       // row (in bounds) and are zeroed after the load
 #pragma unroll
-      for (int j = 0; j < 16; ++j) xo[j] = so[j];
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[4 * j + e] = so[32 * j + e];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(su + 4 * j);
-        const floatx4 b = *reinterpret_cast<const floatx4*>(sr + 4 * j);
+        const floatx4 a = *reinterpret_cast<const floatx4*>(su + 32 * j);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(sr + 32 * j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { xu[4 * j + e] = a[e]; xr[4 * j + e] = b[e]; }
       }
@@ -886,7 +896,7 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
         b2[ks][j] = dSC[(32 * ks + 8 * g4 + j) * kD];
       }
     __builtin_amdgcn_sched_barrier(0);
-    {  // split and stage: thread -> row tid / 8, 16 channels
+    {  // split and stage
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         float x = xo[j];
@@ -897,14 +907,13 @@ __global__ __launch_bounds__(512) void cb_grad_kernel(CbParams p) {
 #pragma unroll
       for (int a = 0; a < 3; ++a)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = src[a][8 * half + j];
-          bf16x8v hi, lo;
-          split8(x, hi, lo);
-          *reinterpret_cast<uint4*>(&sm.u.in[a][0][srow][sc0 + 8 * half]) = __builtin_bit_cast(uint4, hi);
-          *reinterpret_cast<uint4*>(&sm.u.in[a][1][srow][sc0 + 8 * half]) = __builtin_bit_cast(uint4, lo);
+        for (int j = 0; j < 4; ++j) {
+          const float* x = src[a] + 4 * j;
+          const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
+          const uint32_t l0 = pk_bf16(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u));
+          const uint32_t l1 = pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u));
+          *reinterpret_cast<uint2*>(&sm.u.in[a][0][srow][sc0 + 32 * j]) = make_uint2(h0, h1);
+          *reinterpret_cast<uint2*>(&sm.u.in[a][1][srow][sc0 + 32 * j]) = make_uint2(l0, l1);
         }
     }
     __syncthreads();
